@@ -1,0 +1,230 @@
+/*
+ * mok.h — C ABI of the MI355X (gfx950) MoE-layer library.
+ *
+ * One GPU's share of a deterministic mixture-of-experts training layer,
+ * forward and backward: top-k ids -> schedule table -> drop-free permute of
+ * token rows through a fixed ring buffer in mini-batches -> SwiGLU experts as
+ * grouped GEMMs -> weighted combine back to token order; the backward pass
+ * mirrors these steps and computes the router-weight gradient inside the
+ * SwiGLU backward.
+ *
+ * Sources: "Mixture-of-Kittens (MoK)" project summary (Functional API; Key
+ * concepts table), "Cursor Open-Sources Mixture-of-Kittens (MoK)" digest
+ * (English abstract) and "Mixture-of-Kittens(MoK)란?" explainer (sections 1,
+ * 4 ①-③). Each call below names the passage that defines it.
+ *
+ * Conventions for every call:
+ *  - Every buffer is allocated and freed by the caller. The library never
+ *    allocates, frees, synchronises or copies device memory back to the host.
+ *  - Device pointers must be 16-byte aligned. Work is enqueued on `stream`
+ *    (a hipStream_t; NULL = the legacy default stream) and the call returns
+ *    without waiting for it.
+ *  - Host-checkable problems (bad sizes, misaligned or NULL pointers, a buffer
+ *    smaller than mok_query_sizes reports, fewer than 2 ring slots) return a
+ *    non-zero mok_status and enqueue nothing.
+ *  - Data-dependent problems set bits in the device status word (uint32 at
+ *    byte 0 of the schedule buffer): MOK_SCHEDULE_OVERFLOW, MOK_BAD_EXPERT_ID.
+ *    mok_forward / mok_backward then do no work and their outputs are
+ *    undefined. The caller reads the word whenever it synchronises; no
+ *    routed row is ever dropped silently.
+ *  - Calls are re-entrant; concurrent calls need distinct workspaces.
+ *  - bf16 tensors are raw 16-bit patterns; all tensors are dense row-major.
+ */
+#ifndef MOK_H
+#define MOK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mok_status {
+    MOK_OK = 0,
+    MOK_ERROR_INVALID_VALUE = 1,
+    MOK_ERROR_UNSUPPORTED = 2,
+    MOK_ERROR_BUFFER_TOO_SMALL = 3,
+    MOK_ERROR_LAUNCH_FAILED = 4
+} mok_status;
+
+/* precision modes ("Mixture-of-Kittens (MoK)" project summary, Overview) */
+#define MOK_BF16 0
+#define MOK_MXFP8 1
+
+/* device status word bits */
+#define MOK_SCHEDULE_OVERFLOW 1u
+#define MOK_BAD_EXPERT_ID 2u
+
+/* debug_flags: replace every expert by the identity on its rows (forward only;
+   out_t = sum_j g_tj * x_t). Used to test permute followed by unpermute. */
+#define MOK_DEBUG_IDENTITY_EXPERT 1u
+
+/*
+ * Layer knobs ("Mixture-of-Kittens (MoK)" project summary, Key-concepts table:
+ * mini-batch granularity, macro-batch size, schedule capacity multiplier; the
+ * communication-SM knob has no meaning without peers and is not present).
+ * No knob changes any output bit.
+ *   minibatch_rows      rows per mini-batch, a multiple of 16 (default 512)
+ *   macrobatch_tokens   tokens per macro-batch; 0 = one macro-batch
+ *   ring_bytes          size of the ring token buffer; must hold >= 2 mini-batches
+ *   capacity_multiplier schedule capacity relative to the worst case, in (0, 4]
+ *   precision           MOK_BF16 or MOK_MXFP8
+ *   debug_flags         0 in production
+ */
+typedef struct mok_config {
+    int32_t minibatch_rows;
+    int32_t precision;
+    int64_t macrobatch_tokens;
+    int64_t ring_bytes;
+    float capacity_multiplier;
+    uint32_t debug_flags;
+} mok_config;
+
+/*
+ * Layer shape: T rows handed to the layer (tokens; for an expert-parallel
+ * share, the received routed rows with k = 1), hidden size H, expert
+ * intermediate size I, E local experts, k routed rows per token.
+ * H and I are multiples of 64; 1 <= k <= E; T >= 0; T*k < 2^31.
+ */
+typedef struct mok_shape {
+    int64_t T;
+    int32_t H, I, E, k;
+} mok_shape;
+
+/*
+ * Expert weights.
+ * BF16 mode: w_gate, w_up [E,H,I] and w_down [E,I,H], bf16.
+ * MXFP8 mode (weights pre-quantized by mok_mxfp8_quantize; "Mixture-of-Kittens
+ * (MoK)" project summary, Key-concepts table), elements E4M3 bytes and scales
+ * E8M0 bytes, one scale per 32 contiguous elements along the contraction axis:
+ *   for mok_forward : gate/up elems [E,I,H] scales [E,I,H/32]   (W^T, along H)
+ *                     down    elems [E,H,I] scales [E,H,I/32]   (W_down^T, along I)
+ *   for mok_backward: gate/up elems [E,H,I] scales [E,H,I/32]   (along I)
+ *                     down    elems [E,I,H] scales [E,I,H/32]   (along H)
+ * In MXFP8 mode the bf16 pointers are ignored: the weight gradients use
+ * activations only.
+ */
+typedef struct mok_weights {
+    const void *w_gate, *w_up, *w_down;
+    const uint8_t *gate_elems, *gate_scales;
+    const uint8_t *up_elems, *up_scales;
+    const uint8_t *down_elems, *down_scales;
+} mok_weights;
+
+/*
+ * Byte offsets of the schedule table's fields inside the schedule buffer, and
+ * its sizes, for inspection by tests and tools. Fields are int32 arrays:
+ *   counts[E]            rows per expert (sum = T*k: nothing is dropped)
+ *   offsets[E+1]         exclusive scan of counts
+ *   mcounts[NM*E]        rows per (macro-batch, expert)
+ *   moffsets[NM*(E+1)]   first processing position of each (macro-batch, expert)
+ *   perm[R]              processing position q -> routed row f = t*k + j
+ *   inv[R]               routed row f -> processing position q
+ *   canon[R]             position in (expert, f) order -> processing position
+ *   mb_start[G+1]        first processing position of each mini-batch
+ *   segments[cap*4]      (mini-batch g, expert e, first position q0, rows) for
+ *                        each non-empty (mini-batch, expert) intersection
+ * plus uint32 status (byte 0) and int32 n_seg (byte 4).
+ */
+typedef struct mok_schedule_layout {
+    int64_t R, NM, G, cap;
+    size_t status, n_seg, counts, offsets, mcounts, moffsets, perm, inv, canon,
+           mb_start, segments;
+    size_t total_bytes;
+} mok_schedule_layout;
+
+/* Fill *cfg with the defaults: 512-row mini-batches, one macro-batch, a
+   256 MiB ring, capacity multiplier 1, BF16, no debug flags. */
+mok_status mok_config_default(mok_config *cfg);
+
+/*
+ * Host-only size query (the pages' get_workspace sizing, "Mixture-of-Kittens
+ * (MoK)" project summary, Functional API; the workspace is made once and
+ * reused, Key-concepts table). Writes the byte sizes of the workspace
+ * (ring + scratch, reusable across calls), the schedule buffer (one per
+ * routing) and fwd_ctx (forward saves for backward). Any output pointer may
+ * be NULL. Enqueues nothing; needs no GPU.
+ */
+mok_status mok_query_sizes(const mok_config *cfg, const mok_shape *shape,
+                           size_t *workspace_bytes, size_t *schedule_bytes,
+                           size_t *fwd_ctx_bytes);
+
+/* Host-only: the schedule buffer's field offsets for cfg and shape. */
+mok_status mok_schedule_layout_query(const mok_config *cfg, const mok_shape *shape,
+                                     mok_schedule_layout *layout);
+
+/*
+ * Build the schedule table on the device from top-k expert ids
+ * ("Mixture-of-Kittens (MoK)" project summary, Functional API: build_schedule;
+ * "Mixture-of-Kittens(MoK)란?" explainer, section 4 ①: one table drives both
+ * passes; section 4 ③: drop-free, no CPU-GPU synchronisation).
+ *   topk_ids  device int32 [T,k], each in [0,E) (else MOK_BAD_EXPERT_ID)
+ *   schedule  device buffer of schedule_bytes >= mok_query_sizes' value
+ * Processing order sorts routed rows by (macro-batch, expert, row); the table
+ * is a pure function of (topk_ids, shape, config).
+ */
+mok_status mok_build_schedule(const mok_config *cfg, const mok_shape *shape,
+                              const int32_t *topk_ids, void *schedule,
+                              size_t schedule_bytes, void *stream);
+
+/*
+ * Forward pass ("Mixture-of-Kittens (MoK)" project summary, Functional API:
+ * forward -> (out, fwd_ctx); "Mixture-of-Kittens(MoK)란?" explainer, section
+ * 4 ③: ring token buffer consumed in mini-batches).
+ *   x        device bf16 [T,H]
+ *   topk_w   device fp32 [T,k] gate weights
+ *   w        expert weights (see mok_weights)
+ *   out      device bf16 [T,H]: out_t = sum_j topk_w[t,j] * SwiGLU_e(x_t),
+ *            accumulated in fp32 in order j = 0..k-1
+ *   fwd_ctx  device buffer (fwd_ctx_bytes), written; read by mok_backward
+ */
+mok_status mok_forward(const mok_config *cfg, const mok_shape *shape,
+                       const void *schedule, void *workspace, size_t workspace_bytes,
+                       const void *x, const float *topk_w, const mok_weights *w,
+                       void *out, void *fwd_ctx, size_t fwd_ctx_bytes, void *stream);
+
+/*
+ * Backward pass for upstream gradient dy of out ("Mixture-of-Kittens (MoK)"
+ * project summary, Functional API: backward -> grads; "Mixture-of-Kittens(MoK)
+ * 란?" explainer, section 4 ③: the ring is walked in reverse; "Cursor
+ * Open-Sources Mixture-of-Kittens (MoK)" digest, English abstract: the
+ * router-weight gradient is fused into the SwiGLU backward).
+ *   x, topk_w, w, schedule, fwd_ctx   as given to mok_forward
+ *   dy       device bf16 [T,H]
+ *   dx       device bf16 [T,H]
+ *   dw_gate, dw_up [E,H,I] and dw_down [E,I,H], device bf16, overwritten
+ *            (experts that received no rows get zeros)
+ *   dtopk_w  device fp32 [T,k]: d loss / d topk_w[t,j] = <dy_t, y_{t,j}>
+ */
+mok_status mok_backward(const mok_config *cfg, const mok_shape *shape,
+                        const void *schedule, void *workspace, size_t workspace_bytes,
+                        const void *x, const float *topk_w, const mok_weights *w,
+                        const void *fwd_ctx, size_t fwd_ctx_bytes, const void *dy,
+                        void *dx, void *dw_gate, void *dw_up, void *dw_down,
+                        float *dtopk_w, void *stream);
+
+/*
+ * MXFP8 quantization ("Mixture-of-Kittens (MoK)" project summary, Key-concepts
+ * table: weights are pre-quantized before the kernel; block format: OCP MX
+ * v1.0 MXFP8). For each run of 32 contiguous values along K:
+ *   scale byte = clamp(floor(log2 amax) - 8, -127, 127) + 127  (127 if amax = 0)
+ *   element    = E4M3FN(v * 2^-(scale-127)), nearest-even, saturating to +-448
+ *   src            device bf16; [batch, rows, K] if src_is_k_by_rows == 0,
+ *                  [batch, K, rows] if 1 (quantizes the transpose)
+ *   elems          device uint8 [batch, rows, K]
+ *   scales         device uint8 [batch, rows, K/32]
+ * K must be a multiple of 32. NaN/Inf inputs are unsupported.
+ */
+mok_status mok_mxfp8_quantize(const void *src, int64_t batch, int64_t rows, int64_t K,
+                              int32_t src_is_k_by_rows, uint8_t *elems, uint8_t *scales,
+                              void *stream);
+
+/* Static string naming a status code. */
+const char *mok_status_string(mok_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOK_H */

@@ -1,0 +1,288 @@
+"""Python binding of libmok (the MI355X MoE-layer library).
+
+Argument marshalling only: every step of the layer runs in the HIP kernels of
+``libmok.so``; PyTorch provides device memory and the stream. Importing this
+package raises if the library has not been built
+(``python -m mixture_experts_layer_table_amd.build``).
+
+Two levels, after the pages' ops / functional split ("Mixture-of-Kittens (MoK)"
+project summary, Functional API and Key-concepts table):
+
+* ``mok_*`` — one function per C-ABI entry point, same names and arguments;
+  tensors are passed as raw pointers and the caller owns every buffer.
+* ``MoKConfig``, ``get_workspace``, ``build_schedule``, ``forward``,
+  ``backward``, ``mxfp8_quantize`` — allocate the caller-side buffers with
+  torch and call the entry points above.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+
+__version__ = "0.1.0"
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmok.so")
+if not os.path.exists(_LIB_PATH):
+    raise ImportError(f"{_LIB_PATH} is missing: build it with "
+                      "`python -m mixture_experts_layer_table_amd.build` (there is no fallback)")
+_lib = ctypes.CDLL(_LIB_PATH)
+
+MOK_OK, MOK_ERROR_INVALID_VALUE, MOK_ERROR_UNSUPPORTED, MOK_ERROR_BUFFER_TOO_SMALL, \
+    MOK_ERROR_LAUNCH_FAILED = range(5)
+MOK_BF16, MOK_MXFP8 = 0, 1
+MOK_SCHEDULE_OVERFLOW, MOK_BAD_EXPERT_ID = 1, 2
+MOK_DEBUG_IDENTITY_EXPERT = 1
+
+EXPORTS = ("mok_config_default", "mok_query_sizes", "mok_schedule_layout_query",
+           "mok_build_schedule", "mok_forward", "mok_backward", "mok_mxfp8_quantize",
+           "mok_status_string")
+
+
+class mok_config(ctypes.Structure):
+    _fields_ = [("minibatch_rows", ctypes.c_int32), ("precision", ctypes.c_int32),
+                ("macrobatch_tokens", ctypes.c_int64), ("ring_bytes", ctypes.c_int64),
+                ("capacity_multiplier", ctypes.c_float), ("debug_flags", ctypes.c_uint32)]
+
+
+class mok_shape(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int64), ("H", ctypes.c_int32), ("I", ctypes.c_int32),
+                ("E", ctypes.c_int32), ("k", ctypes.c_int32)]
+
+
+class mok_weights(ctypes.Structure):
+    _fields_ = [("w_gate", ctypes.c_void_p), ("w_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p),
+                ("gate_elems", ctypes.c_void_p), ("gate_scales", ctypes.c_void_p),
+                ("up_elems", ctypes.c_void_p), ("up_scales", ctypes.c_void_p),
+                ("down_elems", ctypes.c_void_p), ("down_scales", ctypes.c_void_p)]
+
+
+class mok_schedule_layout(ctypes.Structure):
+    _fields_ = [("R", ctypes.c_int64), ("NM", ctypes.c_int64), ("G", ctypes.c_int64),
+                ("cap", ctypes.c_int64)] + \
+        [(n, ctypes.c_size_t) for n in ("status", "n_seg", "counts", "offsets", "mcounts", "moffsets",
+                                       "perm", "inv", "canon", "mb_start", "segments", "total_bytes")]
+
+
+_P = ctypes.c_void_p
+_sz = ctypes.POINTER(ctypes.c_size_t)
+_sigs = {
+    "mok_config_default": [ctypes.POINTER(mok_config)],
+    "mok_query_sizes": [ctypes.POINTER(mok_config), ctypes.POINTER(mok_shape), _sz, _sz, _sz],
+    "mok_schedule_layout_query": [ctypes.POINTER(mok_config), ctypes.POINTER(mok_shape),
+                                  ctypes.POINTER(mok_schedule_layout)],
+    "mok_build_schedule": [ctypes.POINTER(mok_config), ctypes.POINTER(mok_shape), _P, _P,
+                           ctypes.c_size_t, _P],
+    "mok_forward": [ctypes.POINTER(mok_config), ctypes.POINTER(mok_shape), _P, _P, ctypes.c_size_t,
+                    _P, _P, ctypes.POINTER(mok_weights), _P, _P, ctypes.c_size_t, _P],
+    "mok_backward": [ctypes.POINTER(mok_config), ctypes.POINTER(mok_shape), _P, _P, ctypes.c_size_t,
+                     _P, _P, ctypes.POINTER(mok_weights), _P, ctypes.c_size_t, _P, _P, _P, _P, _P,
+                     _P, _P],
+    "mok_mxfp8_quantize": [_P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
+                           _P, _P, _P],
+}
+for _name, _args in _sigs.items():
+    _f = getattr(_lib, _name)
+    _f.argtypes = _args
+    _f.restype = ctypes.c_int
+_lib.mok_status_string.argtypes = [ctypes.c_int]
+_lib.mok_status_string.restype = ctypes.c_char_p
+
+
+class MokError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {mok_status_string(status)}")
+        self.status = status
+
+
+def _check(status: int, where: str):
+    if status != MOK_OK:
+        raise MokError(status, where)
+
+
+def mok_status_string(status: int) -> str:
+    return _lib.mok_status_string(status).decode()
+
+
+# ----------------------------------------------------------------------------- raw entry points
+
+def mok_config_default(cfg):
+    return _lib.mok_config_default(ctypes.byref(cfg))
+
+
+def mok_query_sizes(cfg, shape, workspace, schedule, fwd_ctx):
+    return _lib.mok_query_sizes(ctypes.byref(cfg), ctypes.byref(shape), workspace, schedule, fwd_ctx)
+
+
+def mok_schedule_layout_query(cfg, shape, layout):
+    return _lib.mok_schedule_layout_query(ctypes.byref(cfg), ctypes.byref(shape), ctypes.byref(layout))
+
+
+def mok_build_schedule(cfg, shape, topk_ids, schedule, schedule_bytes, stream):
+    return _lib.mok_build_schedule(ctypes.byref(cfg), ctypes.byref(shape), topk_ids, schedule,
+                                   schedule_bytes, stream)
+
+
+def mok_forward(cfg, shape, schedule, workspace, workspace_bytes, x, topk_w, weights, out, fwd_ctx,
+                fwd_ctx_bytes, stream):
+    return _lib.mok_forward(ctypes.byref(cfg), ctypes.byref(shape), schedule, workspace, workspace_bytes,
+                            x, topk_w, ctypes.byref(weights), out, fwd_ctx, fwd_ctx_bytes, stream)
+
+
+def mok_backward(cfg, shape, schedule, workspace, workspace_bytes, x, topk_w, weights, fwd_ctx,
+                 fwd_ctx_bytes, dy, dx, dw_gate, dw_up, dw_down, dtopk_w, stream):
+    return _lib.mok_backward(ctypes.byref(cfg), ctypes.byref(shape), schedule, workspace,
+                             workspace_bytes, x, topk_w, ctypes.byref(weights), fwd_ctx, fwd_ctx_bytes,
+                             dy, dx, dw_gate, dw_up, dw_down, dtopk_w, stream)
+
+
+def mok_mxfp8_quantize(src, batch, rows, K, src_is_k_by_rows, elems, scales, stream):
+    return _lib.mok_mxfp8_quantize(src, batch, rows, K, src_is_k_by_rows, elems, scales, stream)
+
+
+# ----------------------------------------------------------------------------- functional layer
+
+@dataclasses.dataclass
+class MoKConfig:
+    """Layer knobs; none of them changes any output bit."""
+    minibatch_rows: int = 512
+    macrobatch_tokens: int = 0
+    ring_bytes: int = 256 << 20
+    capacity_multiplier: float = 1.0
+    precision: int = MOK_BF16
+    debug_flags: int = 0
+
+    def c(self) -> mok_config:
+        return mok_config(self.minibatch_rows, self.precision, self.macrobatch_tokens,
+                          self.ring_bytes, self.capacity_multiplier, self.debug_flags)
+
+
+def _shape(T, H, I, E, k) -> mok_shape:
+    return mok_shape(T, H, I, E, k)
+
+
+def query_sizes(config: MoKConfig, T, H, I, E, k):
+    ws, sc, cx = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    _check(mok_query_sizes(config.c(), _shape(T, H, I, E, k), ctypes.byref(ws), ctypes.byref(sc),
+                           ctypes.byref(cx)), "mok_query_sizes")
+    return ws.value, sc.value, cx.value
+
+
+def schedule_layout(config: MoKConfig, T, H, I, E, k) -> mok_schedule_layout:
+    lay = mok_schedule_layout()
+    _check(mok_schedule_layout_query(config.c(), _shape(T, H, I, E, k), lay), "mok_schedule_layout_query")
+    return lay
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+@dataclasses.dataclass
+class Workspace:
+    """Caller-owned device buffers for one layer shape (made once, reused)."""
+    config: MoKConfig
+    T: int
+    H: int
+    I: int
+    E: int
+    k: int
+    buffer: "object"        # torch.uint8 tensor
+    schedule_bytes: int
+    fwd_ctx_bytes: int
+
+
+def get_workspace(config: MoKConfig, *, device, num_local_tokens: int, hidden_size: int,
+                  intermediate_size: int, num_experts: int, topk: int) -> Workspace:
+    import torch
+    ws, sc, cx = query_sizes(config, num_local_tokens, hidden_size, intermediate_size, num_experts, topk)
+    buf = torch.empty(max(ws, 256), dtype=torch.uint8, device=device)
+    return Workspace(config, num_local_tokens, hidden_size, intermediate_size, num_experts, topk, buf,
+                     sc, cx)
+
+
+def build_schedule(ws: Workspace, topk_ids, schedule=None):
+    """topk_ids: int32 [T,k] on the device. Returns the schedule buffer (uint8 tensor)."""
+    import torch
+    if schedule is None:
+        schedule = torch.empty(max(ws.schedule_bytes, 256), dtype=torch.uint8, device=ws.buffer.device)
+    _check(mok_build_schedule(ws.config.c(), _shape(ws.T, ws.H, ws.I, ws.E, ws.k), _ptr(topk_ids),
+                              _ptr(schedule), schedule.numel(), _stream()), "mok_build_schedule")
+    return schedule
+
+
+def weights_bf16(w_gate, w_up, w_down) -> mok_weights:
+    return mok_weights(w_gate.data_ptr(), w_up.data_ptr(), w_down.data_ptr(), None, None, None, None, None, None)
+
+
+def weights_mxfp8(gate, up, down) -> mok_weights:
+    """Each argument is an (elems, scales) pair of uint8 tensors."""
+    return mok_weights(None, None, None, gate[0].data_ptr(), gate[1].data_ptr(), up[0].data_ptr(),
+                       up[1].data_ptr(), down[0].data_ptr(), down[1].data_ptr())
+
+
+def forward(ws: Workspace, schedule, x, topk_w, weights: mok_weights, out=None, fwd_ctx=None):
+    """Returns (out bf16 [T,H], fwd_ctx uint8)."""
+    import torch
+    if out is None:
+        out = torch.empty((ws.T, ws.H), dtype=torch.bfloat16, device=ws.buffer.device)
+    if fwd_ctx is None:
+        fwd_ctx = torch.empty(max(ws.fwd_ctx_bytes, 256), dtype=torch.uint8, device=ws.buffer.device)
+    _check(mok_forward(ws.config.c(), _shape(ws.T, ws.H, ws.I, ws.E, ws.k), _ptr(schedule),
+                       _ptr(ws.buffer), ws.buffer.numel(), _ptr(x), _ptr(topk_w), weights, _ptr(out),
+                       _ptr(fwd_ctx), fwd_ctx.numel(), _stream()), "mok_forward")
+    return out, fwd_ctx
+
+
+def backward(ws: Workspace, schedule, fwd_ctx, x, topk_w, weights: mok_weights, dy, grads=None):
+    """Returns dict(dx, dw_gate, dw_up, dw_down, dtopk_w)."""
+    import torch
+    dev = ws.buffer.device
+    if grads is None:
+        grads = dict(dx=torch.empty((ws.T, ws.H), dtype=torch.bfloat16, device=dev),
+                     dw_gate=torch.empty((ws.E, ws.H, ws.I), dtype=torch.bfloat16, device=dev),
+                     dw_up=torch.empty((ws.E, ws.H, ws.I), dtype=torch.bfloat16, device=dev),
+                     dw_down=torch.empty((ws.E, ws.I, ws.H), dtype=torch.bfloat16, device=dev),
+                     dtopk_w=torch.empty((ws.T, ws.k), dtype=torch.float32, device=dev))
+    _check(mok_backward(ws.config.c(), _shape(ws.T, ws.H, ws.I, ws.E, ws.k), _ptr(schedule),
+                        _ptr(ws.buffer), ws.buffer.numel(), _ptr(x), _ptr(topk_w), weights,
+                        _ptr(fwd_ctx), fwd_ctx.numel(), _ptr(dy), _ptr(grads["dx"]),
+                        _ptr(grads["dw_gate"]), _ptr(grads["dw_up"]), _ptr(grads["dw_down"]),
+                        _ptr(grads["dtopk_w"]), _stream()), "mok_backward")
+    return grads
+
+
+def mxfp8_quantize(src, src_is_k_by_rows: bool):
+    """src bf16 [B, rows, K] (or [B, K, rows] when src_is_k_by_rows). Returns
+    (elems uint8 [B, rows, K], scales uint8 [B, rows, K/32])."""
+    import torch
+    B = src.shape[0]
+    rows, K = (src.shape[2], src.shape[1]) if src_is_k_by_rows else (src.shape[1], src.shape[2])
+    elems = torch.empty((B, rows, K), dtype=torch.uint8, device=src.device)
+    scales = torch.empty((B, rows, K // 32), dtype=torch.uint8, device=src.device)
+    _check(mok_mxfp8_quantize(_ptr(src), B, rows, K, int(src_is_k_by_rows), _ptr(elems), _ptr(scales),
+                              _stream()), "mok_mxfp8_quantize")
+    return elems, scales
+
+
+def read_schedule(schedule, layout: mok_schedule_layout, E: int):
+    """Copy the schedule table's fields to host numpy arrays (synchronises)."""
+    import numpy as np
+    host = schedule.cpu().numpy()
+
+    def i32(off, n):
+        return host[off: off + 4 * n].view(np.int32).copy()
+    R, NM, G = layout.R, layout.NM, layout.G
+    n_seg = int(i32(layout.n_seg, 1)[0])
+    return dict(status=int(host[layout.status: layout.status + 4].view(np.uint32)[0]), n_seg=n_seg,
+                counts=i32(layout.counts, E), offsets=i32(layout.offsets, E + 1),
+                mcounts=i32(layout.mcounts, NM * E).reshape(NM, E),
+                moffsets=i32(layout.moffsets, NM * (E + 1)).reshape(NM, E + 1),
+                perm=i32(layout.perm, R), inv=i32(layout.inv, R), canon=i32(layout.canon, R),
+                mb_start=i32(layout.mb_start, G + 1),
+                segments=i32(layout.segments, 4 * min(n_seg, layout.cap)).reshape(-1, 4))

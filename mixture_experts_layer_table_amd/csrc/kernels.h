@@ -1,0 +1,23 @@
+// Host-side launchers of the device code (one per C-ABI entry point).
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include "plan.h"
+
+namespace mok {
+
+mok_status launch_build_schedule(const Plan &p, const int32_t *ids, void *schedule, hipStream_t st);
+
+mok_status launch_forward(const Plan &p, const void *schedule, void *workspace, const uint16_t *x,
+                          const float *topk_w, const mok_weights &w, uint16_t *out, void *fwd_ctx,
+                          hipStream_t st);
+
+mok_status launch_backward(const Plan &p, const void *schedule, void *workspace, const uint16_t *x,
+                           const float *topk_w, const mok_weights &w, const void *fwd_ctx,
+                           const uint16_t *dy, uint16_t *dx, uint16_t *dw_gate, uint16_t *dw_up,
+                           uint16_t *dw_down, float *dtopk_w, hipStream_t st);
+
+mok_status launch_mxfp8_quantize(const uint16_t *src, int64_t batch, int64_t rows, int64_t K,
+                                 bool src_is_k_by_rows, uint8_t *elems, uint8_t *scales, hipStream_t st);
+
+}  // namespace mok

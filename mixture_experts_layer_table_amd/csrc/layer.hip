@@ -1,0 +1,794 @@
+// Forward and backward of the MoE layer on gfx950.
+//
+// Forward, per ring round of mini-batches ("Mixture-of-Kittens(MoK)란?"
+// explainer, section 4 ③: a fixed ring buffer consumed in mini-batches):
+//   gather   ring[slot(g)] <- x rows in processing order          (dispatch)
+//   gate/up  h = x W_gate | x W_up per segment, SwiGLU epilogue   (a -> ring-side buffer)
+//   down     y = a W_down, then the weighted combine back to token order
+//            (fused into the epilogue when k = 1; staged per macro-batch and
+//            summed over j = 0..k-1 in fp32 otherwise)
+// Backward walks the rounds in reverse:
+//   gather   ring <- dy rows
+//   dA       G = dy W_down^T with the SwiGLU backward and the router-weight
+//            gradient <G, a> fused into the epilogue ("Cursor Open-Sources
+//            Mixture-of-Kittens (MoK)" digest, English abstract)
+//   dX       dx rows = dh_g W_gate^T + dh_u W_up^T, combined back to tokens
+//   then     router-weight partials summed in ascending order, and the weight
+//            gradients per expert over its rows in (expert, f) order.
+// Every output element is produced by one owner with a fixed reduction order
+// and no floating-point atomics, so results are bitwise reproducible and
+// independent of mini-batch, macro-batch, ring and capacity settings.
+#include <algorithm>
+#include <vector>
+
+#include "gemm.h"
+#include "kernels.h"
+#include "views.h"
+
+namespace mok {
+namespace {
+
+using CfgA = TileCfg<128, 128, 64, 2, 2>;
+
+// ----------------------------------------------------------------------------- tile decode
+
+struct SegTile {
+    MTile mt;
+    int slot;     // ring slot of the tile's mini-batch
+    int rowoff;   // first row of the tile inside that mini-batch
+};
+
+__device__ __forceinline__ bool decode_seg_tile(const SchedView &v, int g0, int g1, int64_t n_slots,
+                                                SegTile &t) {
+    if (*v.status) return false;
+    const int lo = v.mtfirst[g0], hi = v.mtfirst[g1];
+    if ((int)blockIdx.y >= hi - lo) return false;
+    t.mt = v.mtiles[lo + blockIdx.y];
+    t.slot = (int)(t.mt.g % n_slots);
+    t.rowoff = t.mt.q0 - v.mb_start[t.mt.g];
+    return true;
+}
+
+__device__ __forceinline__ void store4_bf16(uint16_t *p, float a, float b, float c, float d) {
+    *reinterpret_cast<uint2 *>(p) = make_uint2(pack_bf16x2(a, b), pack_bf16x2(c, d));
+}
+
+__device__ __forceinline__ float bf16r(float x) { return bf16_to_f32(f32_to_bf16(x)); }
+
+// ----------------------------------------------------------------------------- forward gate/up
+
+struct GateUpArgs {
+    SchedView v;
+    int g0, g1;
+    int64_t n_slots;
+    int MB, H, I;
+    const uint16_t *ring, *wg, *wu;
+    uint16_t *h, *aring;
+};
+
+template <class Cfg>
+struct GateUp {
+    using C = Cfg;
+    using Args = GateUpArgs;
+    RowTile<C, C::BM> xt;
+    TransTile<C, C::BN> wt;
+    SegTile t;
+    int i0, nk, H, I, MB;
+    const uint16_t *wg, *wu;
+    uint16_t *h, *aring;
+
+    __device__ bool setup(const Args &a) {
+        if (!decode_seg_tile(a.v, a.g0, a.g1, a.n_slots, t)) return false;
+        H = a.H;
+        I = a.I;
+        MB = a.MB;
+        i0 = blockIdx.x * (C::BN / 2);
+        const int64_t row0 = (int64_t)t.slot * MB + t.rowoff;
+        const int rows = t.mt.rows;
+        const uint16_t *ring = a.ring;
+        const int Hl = H;
+        xt.init([&](int r) -> const uint16_t * { return r < rows ? ring + (row0 + r) * Hl : nullptr; });
+        wg = a.wg + (int64_t)t.mt.e * H * I;
+        wu = a.wu + (int64_t)t.mt.e * H * I;
+        h = a.h;
+        aring = a.aring;
+        nk = H / C::BK;
+        return true;
+    }
+    __device__ void load(int kt) {
+        const int k0 = kt * C::BK;
+        xt.load(k0);
+        wt.load(
+            [&](int k, int c) -> const uint16_t * {
+                return c < C::BN / 2 ? wg + (int64_t)k * I + i0 + c : wu + (int64_t)k * I + i0 + (c - C::BN / 2);
+            },
+            k0);
+    }
+    __device__ void store(uint16_t *s) const {
+        xt.store(s);
+        wt.store(s + C::BM * C::BK);
+    }
+    // gate block fn pairs with up block fn + FN/2 inside the same wave
+    __device__ int wrow(int wn, int fn) const {
+        return fn < C::FN / 2 ? wn * (C::WN / 2) + fn * 32 : C::BN / 2 + wn * (C::WN / 2) + (fn - C::FN / 2) * 32;
+    }
+    __device__ void epilogue(f32x16_t (&acc)[C::FM][C::FN], int wm, int wn) {
+        const int lane = threadIdx.x & 63;
+#pragma unroll
+        for (int fm = 0; fm < C::FM; ++fm) {
+            const int m = wm * C::WM + fm * 32 + (lane & 31);
+            if (m >= t.mt.rows) continue;
+            const int64_t q = t.mt.q0 + m;
+            uint16_t *hrow = h + q * 2 * I;
+            uint16_t *arow = aring + ((int64_t)t.slot * MB + t.rowoff + m) * I;
+#pragma unroll
+            for (int fn = 0; fn < C::FN / 2; ++fn)
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const int i = i0 + wn * (C::WN / 2) + fn * 32 + g4 * 8 + (lane >> 5) * 4;
+                    float hg[4], hu[4], av[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        hg[j] = acc[fm][fn][g4 * 4 + j];
+                        hu[j] = acc[fm][fn + C::FN / 2][g4 * 4 + j];
+                        av[j] = hg[j] * sigmoidf_(hg[j]) * hu[j];
+                    }
+                    store4_bf16(hrow + i, hg[0], hg[1], hg[2], hg[3]);
+                    store4_bf16(hrow + I + i, hu[0], hu[1], hu[2], hu[3]);
+                    store4_bf16(arow + i, av[0], av[1], av[2], av[3]);
+                }
+        }
+    }
+};
+
+// ----------------------------------------------------------------------------- forward down (+ combine)
+
+struct DownArgs {
+    SchedView v;
+    int g0, g1;
+    int64_t n_slots;
+    int MB, H, I, k, MT, nb_full;
+    const uint16_t *aring, *wd;
+    const float *topk_w;
+    uint16_t *out, *stage;
+};
+
+template <class Cfg>
+struct Down {
+    using C = Cfg;
+    using Args = DownArgs;
+    RowTile<C, C::BM> xt;
+    TransTile<C, C::BN> wt;
+    SegTile t;
+    int n0, nk, H;
+    const uint16_t *wd;
+    Args a;
+
+    __device__ bool setup(const Args &args) {
+        if (!decode_seg_tile(args.v, args.g0, args.g1, args.n_slots, t)) return false;
+        a = args;
+        H = args.H;
+        n0 = blockIdx.x * C::BN;
+        const int64_t row0 = (int64_t)t.slot * args.MB + t.rowoff;
+        const int rows = t.mt.rows, I = args.I;
+        const uint16_t *ar = args.aring;
+        xt.init([&](int r) -> const uint16_t * { return r < rows ? ar + (row0 + r) * I : nullptr; });
+        wd = args.wd + (int64_t)t.mt.e * args.I * H;
+        nk = args.I / C::BK;
+        return true;
+    }
+    __device__ void load(int kt) {
+        const int k0 = kt * C::BK;
+        xt.load(k0);
+        wt.load(
+            [&](int k, int c) -> const uint16_t * {
+                return n0 + c < H ? wd + (int64_t)k * H + n0 + c : nullptr;
+            },
+            k0);
+    }
+    __device__ void store(uint16_t *s) const {
+        xt.store(s);
+        wt.store(s + C::BM * C::BK);
+    }
+    __device__ int wrow(int wn, int fn) const { return wn * C::WN + fn * 32; }
+    __device__ void epilogue(f32x16_t (&acc)[C::FM][C::FN], int wm, int wn) {
+        const int lane = threadIdx.x & 63;
+        const int k = a.k;
+#pragma unroll
+        for (int fm = 0; fm < C::FM; ++fm) {
+            const int m = wm * C::WM + fm * 32 + (lane & 31);
+            if (m >= t.mt.rows) continue;
+            const int q = t.mt.q0 + m;
+            uint16_t *dst;
+            float gw = 1.0f;
+            if (k == 1) {
+                const int tok = a.v.perm[q];
+                gw = a.topk_w[tok];
+                dst = a.out + (int64_t)tok * H;
+            } else {
+                const int64_t base = (int64_t)k * ((t.mt.g / a.nb_full) * (int64_t)a.MT);
+                dst = a.stage + (q - base) * H;
+            }
+#pragma unroll
+            for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const int n = n0 + wn * C::WN + fn * 32 + g4 * 8 + (lane >> 5) * 4;
+                    if (n >= H) continue;
+                    float y[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        y[j] = bf16r(acc[fm][fn][g4 * 4 + j]);   // y rows are bf16
+                        if (k == 1) y[j] = gw * y[j];             // weighted combine, one row per token
+                    }
+                    store4_bf16(dst + n, y[0], y[1], y[2], y[3]);
+                }
+        }
+    }
+};
+
+// ----------------------------------------------------------------------------- backward dA (+ SwiGLU bwd, router grad)
+
+struct DAArgs {
+    SchedView v;
+    int g0, g1;
+    int64_t n_slots;
+    int MB, H, I, S;
+    const uint16_t *ring, *wd, *h;
+    const float *topk_w;
+    uint16_t *dh, *ga;
+    float *dgp;
+};
+
+template <class Cfg>
+struct DA {
+    using C = Cfg;
+    using Args = DAArgs;
+    RowTile<C, C::BM> xt;
+    RowTile<C, C::BN> wt;
+    SegTile t;
+    int i0, nk;
+    Args a;
+
+    __device__ bool setup(const Args &args) {
+        if (!decode_seg_tile(args.v, args.g0, args.g1, args.n_slots, t)) return false;
+        a = args;
+        i0 = blockIdx.x * C::BN;
+        const int H = args.H, I = args.I, rows = t.mt.rows;
+        const int64_t row0 = (int64_t)t.slot * args.MB + t.rowoff;
+        const uint16_t *ring = args.ring;
+        xt.init([&](int r) -> const uint16_t * { return r < rows ? ring + (row0 + r) * H : nullptr; });
+        const uint16_t *wd = args.wd + (int64_t)t.mt.e * I * H;
+        const int i0l = i0;
+        wt.init([&](int r) -> const uint16_t * { return i0l + r < I ? wd + (int64_t)(i0l + r) * H : nullptr; });
+        nk = H / C::BK;
+        return true;
+    }
+    __device__ void load(int kt) {
+        xt.load(kt * C::BK);
+        wt.load(kt * C::BK);
+    }
+    __device__ void store(uint16_t *s) const {
+        xt.store(s);
+        wt.store(s + C::BM * C::BK);
+    }
+    __device__ int wrow(int wn, int fn) const { return wn * C::WN + fn * 32; }
+    __device__ void epilogue(f32x16_t (&acc)[C::FM][C::FN], int wm, int wn) {
+        const int lane = threadIdx.x & 63;
+        const int I = a.I;
+        const int slice = blockIdx.x * C::WAVES_N + wn;
+        const bool slice_ok = i0 + wn * C::WN < I;
+#pragma unroll
+        for (int fm = 0; fm < C::FM; ++fm) {
+            const int m = wm * C::WM + fm * 32 + (lane & 31);
+            const bool ok = m < t.mt.rows;
+            const int q = t.mt.q0 + (ok ? m : 0);
+            const float gw = a.topk_w[a.v.perm[q]];
+            const uint16_t *hrow = a.h + (int64_t)q * 2 * I;
+            uint16_t *dhrow = a.dh + (int64_t)q * 2 * I;
+            uint16_t *garow = a.ga + (int64_t)q * I;
+            float dg = 0.0f;
+#pragma unroll
+            for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const int i = i0 + wn * C::WN + fn * 32 + g4 * 8 + (lane >> 5) * 4;
+                    if (!slice_ok) continue;
+                    const uint2 hg2 = *reinterpret_cast<const uint2 *>(hrow + i);
+                    const uint2 hu2 = *reinterpret_cast<const uint2 *>(hrow + I + i);
+                    const uint32_t hgw[4] = {hg2.x & 0xFFFFu, hg2.x >> 16, hg2.y & 0xFFFFu, hg2.y >> 16};
+                    const uint32_t huw[4] = {hu2.x & 0xFFFFu, hu2.x >> 16, hu2.y & 0xFFFFu, hu2.y >> 16};
+                    float dhg[4], dhu[4], gav[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const float G = acc[fm][fn][g4 * 4 + j];
+                        const float hg = bf16_to_f32(hgw[j]), hu = bf16_to_f32(huw[j]);
+                        const float s = sigmoidf_(hg);
+                        const float sl = hg * s;
+                        const float av = sl * hu;
+                        dg += G * av;
+                        const float da = gw * G;
+                        dhu[j] = da * sl;
+                        dhg[j] = da * hu * s * (1.0f + hg * (1.0f - s));
+                        gav[j] = gw * av;
+                    }
+                    if (ok) {
+                        store4_bf16(dhrow + i, dhg[0], dhg[1], dhg[2], dhg[3]);
+                        store4_bf16(dhrow + I + i, dhu[0], dhu[1], dhu[2], dhu[3]);
+                        store4_bf16(garow + i, gav[0], gav[1], gav[2], gav[3]);
+                    }
+                }
+            // lanes l and l ^ 32 hold the same row: lower half + upper half, fixed order
+            const float other = __shfl_xor(dg, 32);
+            const float tot = (lane < 32) ? dg + other : other + dg;
+            if (ok && lane < 32 && slice_ok) a.dgp[(int64_t)q * a.S + slice] = tot;
+        }
+    }
+};
+
+// ----------------------------------------------------------------------------- backward dX (+ combine)
+
+struct DXArgs {
+    SchedView v;
+    int g0, g1;
+    int64_t n_slots;
+    int H, I, k, MT, nb_full;
+    const uint16_t *dh, *wg, *wu;
+    uint16_t *dx, *stage;
+};
+
+template <class Cfg>
+struct DX {
+    using C = Cfg;
+    using Args = DXArgs;
+    RowTile<C, C::BM> xt;
+    RowTile<C, C::BN> wt;
+    SegTile t;
+    int n0, nk, I;
+    ptrdiff_t delta;
+    Args a;
+
+    __device__ bool setup(const Args &args) {
+        if (!decode_seg_tile(args.v, args.g0, args.g1, args.n_slots, t)) return false;
+        a = args;
+        n0 = blockIdx.x * C::BN;
+        I = args.I;
+        const int H = args.H, rows = t.mt.rows, Il = I;
+        const int64_t q0 = t.mt.q0;
+        const uint16_t *dh = args.dh;
+        xt.init([&](int r) -> const uint16_t * { return r < rows ? dh + (q0 + r) * 2 * Il : nullptr; });
+        const uint16_t *wg = args.wg + (int64_t)t.mt.e * H * I;
+        const uint16_t *wu = args.wu + (int64_t)t.mt.e * H * I;
+        delta = wu - wg;
+        const int n0l = n0;
+        wt.init([&](int r) -> const uint16_t * { return n0l + r < H ? wg + (int64_t)(n0l + r) * Il : nullptr; });
+        nk = 2 * I / C::BK;
+        return true;
+    }
+    __device__ void load(int kt) {
+        xt.load(kt * C::BK);
+        wt.load_split(kt * C::BK, I, delta);
+    }
+    __device__ void store(uint16_t *s) const {
+        xt.store(s);
+        wt.store(s + C::BM * C::BK);
+    }
+    __device__ int wrow(int wn, int fn) const { return wn * C::WN + fn * 32; }
+    __device__ void epilogue(f32x16_t (&acc)[C::FM][C::FN], int wm, int wn) {
+        const int lane = threadIdx.x & 63;
+        const int H = a.H, k = a.k;
+#pragma unroll
+        for (int fm = 0; fm < C::FM; ++fm) {
+            const int m = wm * C::WM + fm * 32 + (lane & 31);
+            if (m >= t.mt.rows) continue;
+            const int q = t.mt.q0 + m;
+            uint16_t *dst;
+            if (k == 1) {
+                dst = a.dx + (int64_t)a.v.perm[q] * H;
+            } else {
+                const int64_t base = (int64_t)k * ((t.mt.g / a.nb_full) * (int64_t)a.MT);
+                dst = a.stage + (q - base) * H;
+            }
+#pragma unroll
+            for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const int n = n0 + wn * C::WN + fn * 32 + g4 * 8 + (lane >> 5) * 4;
+                    if (n >= H) continue;
+                    const f32x16_t &v = acc[fm][fn];
+                    store4_bf16(dst + n, v[g4 * 4], v[g4 * 4 + 1], v[g4 * 4 + 2], v[g4 * 4 + 3]);
+                }
+        }
+    }
+};
+
+// ----------------------------------------------------------------------------- weight gradients
+
+// dW_gate[e] | dW_up[e] = X_e^T [dh_g | dh_u]: M = H, N = 2I, K = rows of e in
+// (expert, f) order, in BK chunks anchored at the expert's first row.
+struct WGUArgs {
+    SchedView v;
+    int H, I;
+    const uint16_t *x, *dh;
+    uint16_t *dwg, *dwu;
+};
+
+template <class Cfg>
+struct WGU {
+    using C = Cfg;
+    using Args = WGUArgs;
+    TransTile<C, C::BM> xt;
+    TransTile<C, C::BN> wt;
+    int e, h0, n0, ne, off, nk;
+    Args a;
+
+    __device__ bool setup(const Args &args) {
+        if (*args.v.status) return false;
+        a = args;
+        e = blockIdx.z;
+        h0 = blockIdx.y * C::BM;
+        n0 = blockIdx.x * C::BN;
+        ne = args.v.counts[e];
+        off = args.v.offsets[e];
+        nk = (ne + C::BK - 1) / C::BK;
+        return true;
+    }
+    __device__ void load(int kt) {
+        const int k0 = kt * C::BK;
+        const int H = a.H, I = a.I;
+        const int32_t *ctok = a.v.ctok + off, *canon = a.v.canon + off;
+        xt.load(
+            [&](int k, int c) -> const uint16_t * {
+                return (k < ne && h0 + c < H) ? a.x + (int64_t)ctok[k] * H + h0 + c : nullptr;
+            },
+            k0);
+        wt.load(
+            [&](int k, int c) -> const uint16_t * {
+                return (k < ne && n0 + c < 2 * I) ? a.dh + (int64_t)canon[k] * 2 * I + n0 + c : nullptr;
+            },
+            k0);
+    }
+    __device__ void store(uint16_t *s) const {
+        xt.store(s);
+        wt.store(s + C::BM * C::BK);
+    }
+    __device__ int wrow(int wn, int fn) const { return wn * C::WN + fn * 32; }
+    __device__ void epilogue(f32x16_t (&acc)[C::FM][C::FN], int wm, int wn) {
+        const int lane = threadIdx.x & 63;
+        const int H = a.H, I = a.I;
+#pragma unroll
+        for (int fm = 0; fm < C::FM; ++fm) {
+            const int hh = h0 + wm * C::WM + fm * 32 + (lane & 31);
+            if (hh >= H) continue;
+#pragma unroll
+            for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const int n = n0 + wn * C::WN + fn * 32 + g4 * 8 + (lane >> 5) * 4;
+                    if (n >= 2 * I) continue;
+                    uint16_t *dst = n < I ? a.dwg + ((int64_t)e * H + hh) * I + n
+                                          : a.dwu + ((int64_t)e * H + hh) * I + (n - I);
+                    const f32x16_t &v = acc[fm][fn];
+                    store4_bf16(dst, v[g4 * 4], v[g4 * 4 + 1], v[g4 * 4 + 2], v[g4 * 4 + 3]);
+                }
+        }
+    }
+};
+
+// dW_down[e] = (g a)_e^T dY_e: M = I, N = H, K as above.
+struct WDArgs {
+    SchedView v;
+    int H, I;
+    const uint16_t *ga, *dy;
+    uint16_t *dwd;
+};
+
+template <class Cfg>
+struct WD {
+    using C = Cfg;
+    using Args = WDArgs;
+    TransTile<C, C::BM> xt;
+    TransTile<C, C::BN> wt;
+    int e, i0, n0, ne, off, nk;
+    Args a;
+
+    __device__ bool setup(const Args &args) {
+        if (*args.v.status) return false;
+        a = args;
+        e = blockIdx.z;
+        i0 = blockIdx.y * C::BM;
+        n0 = blockIdx.x * C::BN;
+        ne = args.v.counts[e];
+        off = args.v.offsets[e];
+        nk = (ne + C::BK - 1) / C::BK;
+        return true;
+    }
+    __device__ void load(int kt) {
+        const int k0 = kt * C::BK;
+        const int H = a.H, I = a.I;
+        const int32_t *ctok = a.v.ctok + off, *canon = a.v.canon + off;
+        xt.load(
+            [&](int k, int c) -> const uint16_t * {
+                return (k < ne && i0 + c < I) ? a.ga + (int64_t)canon[k] * I + i0 + c : nullptr;
+            },
+            k0);
+        wt.load(
+            [&](int k, int c) -> const uint16_t * {
+                return (k < ne && n0 + c < H) ? a.dy + (int64_t)ctok[k] * H + n0 + c : nullptr;
+            },
+            k0);
+    }
+    __device__ void store(uint16_t *s) const {
+        xt.store(s);
+        wt.store(s + C::BM * C::BK);
+    }
+    __device__ int wrow(int wn, int fn) const { return wn * C::WN + fn * 32; }
+    __device__ void epilogue(f32x16_t (&acc)[C::FM][C::FN], int wm, int wn) {
+        const int lane = threadIdx.x & 63;
+        const int H = a.H, I = a.I;
+#pragma unroll
+        for (int fm = 0; fm < C::FM; ++fm) {
+            const int ii = i0 + wm * C::WM + fm * 32 + (lane & 31);
+            if (ii >= I) continue;
+#pragma unroll
+            for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const int n = n0 + wn * C::WN + fn * 32 + g4 * 8 + (lane >> 5) * 4;
+                    if (n >= H) continue;
+                    const f32x16_t &v = acc[fm][fn];
+                    store4_bf16(a.dwd + ((int64_t)e * I + ii) * H + n, v[g4 * 4], v[g4 * 4 + 1], v[g4 * 4 + 2],
+                                v[g4 * 4 + 3]);
+                }
+        }
+    }
+};
+
+// ----------------------------------------------------------------------------- streaming kernels
+
+constexpr int kRowsPerBlock = 4;   // one 64-lane wave per row
+
+// ring[slot(g)][r] = src[token of processing position q] for q in mini-batch g
+__global__ __launch_bounds__(256) void gather_rows(SchedView v, int g0, int64_t n_slots, int MB, int H, int k,
+                                                   const uint16_t *__restrict__ src, uint16_t *__restrict__ ring) {
+    if (*v.status) return;
+    const int g = g0 + blockIdx.y;
+    const int r = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+    const int q = v.mb_start[g] + r;
+    if (q >= v.mb_start[g + 1]) return;
+    const int tok = v.perm[q] / k;
+    const uint4 *s = reinterpret_cast<const uint4 *>(src + (int64_t)tok * H);
+    uint4 *d = reinterpret_cast<uint4 *>(ring + ((g % n_slots) * MB + r) * (int64_t)H);
+    for (int c = threadIdx.x & 63; c < H / 8; c += 64) d[c] = s[c];
+}
+
+// Identity experts (debug): y rows = ring rows, then the same combine as the layer.
+__global__ __launch_bounds__(256) void identity_rows(SchedView v, int g0, int64_t n_slots, int MB, int H, int k,
+                                                     int MT, int nb_full, const float *__restrict__ topk_w,
+                                                     const uint16_t *__restrict__ ring, uint16_t *__restrict__ out,
+                                                     uint16_t *__restrict__ stage) {
+    if (*v.status) return;
+    const int g = g0 + blockIdx.y;
+    const int r = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+    const int q = v.mb_start[g] + r;
+    if (q >= v.mb_start[g + 1]) return;
+    const uint4 *s = reinterpret_cast<const uint4 *>(ring + ((g % n_slots) * MB + r) * (int64_t)H);
+    if (k == 1) {
+        const int tok = v.perm[q];
+        const float gw = topk_w[tok];
+        uint4 *d = reinterpret_cast<uint4 *>(out + (int64_t)tok * H);
+        for (int c = threadIdx.x & 63; c < H / 8; c += 64) {
+            const uint4 x = s[c];
+            const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+            uint32_t o[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                o[j] = pack_bf16x2(gw * bf16_to_f32(w[j] & 0xFFFFu), gw * bf16_to_f32(w[j] >> 16));
+            d[c] = make_uint4(o[0], o[1], o[2], o[3]);
+        }
+    } else {
+        const int64_t base = (int64_t)k * ((g / nb_full) * (int64_t)MT);
+        uint4 *d = reinterpret_cast<uint4 *>(stage + (q - base) * H);
+        for (int c = threadIdx.x & 63; c < H / 8; c += 64) d[c] = s[c];
+    }
+}
+
+// out[t] = sum_{j=0..k-1} g[t,j] * y[t,j] (fp32, fixed order), tokens of one macro-batch;
+// with weighted == false the plain sum (input-gradient combine).
+__global__ __launch_bounds__(256) void combine_rows(SchedView v, int t0, int t1, int H, int k, int64_t base,
+                                                    const float *__restrict__ topk_w, bool weighted,
+                                                    const uint16_t *__restrict__ stage, uint16_t *__restrict__ out) {
+    if (*v.status) return;
+    const int t = t0 + blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+    if (t >= t1) return;
+    for (int c = threadIdx.x & 63; c < H / 8; c += 64) {
+        float acc[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+        for (int j = 0; j < k; ++j) {
+            const int f = t * k + j;
+            const float gw = weighted ? topk_w[f] : 1.0f;
+            const uint4 x = reinterpret_cast<const uint4 *>(stage + (v.inv[f] - base) * H)[c];
+            const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float lo = bf16_to_f32(w[i] & 0xFFFFu), hi = bf16_to_f32(w[i] >> 16);
+                acc[2 * i] = weighted ? __builtin_fmaf(gw, lo, acc[2 * i]) : acc[2 * i] + lo;
+                acc[2 * i + 1] = weighted ? __builtin_fmaf(gw, hi, acc[2 * i + 1]) : acc[2 * i + 1] + hi;
+            }
+        }
+        reinterpret_cast<uint4 *>(out + (int64_t)t * H)[c] =
+            make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]), pack_bf16x2(acc[4], acc[5]),
+                       pack_bf16x2(acc[6], acc[7]));
+    }
+}
+
+// dtopk_w[f] = sum over I-slices s ascending of the partials <G, a> of row inv[f]
+__global__ __launch_bounds__(256) void reduce_router_grad(SchedView v, int S, const float *__restrict__ dgp,
+                                                          float *__restrict__ dtopk_w) {
+    if (*v.status) return;
+    const int f = blockIdx.x * 256 + threadIdx.x;
+    if (f >= v.R) return;
+    const float *p = dgp + (int64_t)v.inv[f] * S;
+    float s = 0.0f;
+    for (int i = 0; i < S; ++i) s += p[i];
+    dtopk_w[f] = s;
+}
+
+// ----------------------------------------------------------------------------- host side
+
+template <class P>
+hipError_t launch_gemm(dim3 grid, const typename P::Args &args, hipStream_t st) {
+    using C = typename P::C;
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void *)gemm_kernel<P>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           (int)C::LDS_BYTES);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    if (grid.x == 0 || grid.y == 0 || grid.z == 0) return hipSuccess;
+    gemm_kernel<P><<<grid, C::NT, C::LDS_BYTES, st>>>(args);
+    return hipGetLastError();
+}
+
+struct Round {
+    int g0, g1;
+};
+
+// Ring rounds: consecutive mini-batches, at most n_slots per round (distinct
+// slots), not crossing a macro-batch boundary when the combine is staged (k > 1).
+std::vector<Round> make_rounds(const Plan &p, bool reverse) {
+    std::vector<Round> out;
+    const int S = (int)std::min<int64_t>(p.n_slots, (int64_t)p.G);
+    auto add_span = [&](int a, int b) {
+        if (!reverse)
+            for (int g = a; g < b; g += S) out.push_back({g, std::min(b, g + S)});
+        else
+            for (int g = b; g > a; g -= S) out.push_back({std::max(a, g - S), g});
+    };
+    if (p.k == 1) {
+        add_span(0, p.G);
+    } else if (!reverse) {
+        for (int m = 0; m < p.NM; ++m) add_span(first_minibatch(p, m), std::min(p.G, first_minibatch(p, m + 1)));
+    } else {
+        for (int m = p.NM - 1; m >= 0; --m) add_span(first_minibatch(p, m), std::min(p.G, first_minibatch(p, m + 1)));
+    }
+    return out;
+}
+
+int64_t mtile_bound(const Plan &p, Round r) {
+    int64_t q0, q1, a, b;
+    minibatch_rows(p, r.g0, &q0, &a);
+    minibatch_rows(p, r.g1 - 1, &b, &q1);
+    const int64_t nmacro = macro_of_minibatch(p, r.g1 - 1) - macro_of_minibatch(p, r.g0) + 1;
+    const int64_t nseg = std::min<int64_t>(p.cap, (int64_t)(r.g1 - r.g0) + (int64_t)(p.E - 1) * nmacro);
+    return (q1 - q0) / p.tile.BM + nseg + 1;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+struct Macro {
+    int m;
+    int t0, t1;
+    int64_t base;
+};
+
+Macro macro_info(const Plan &p, int m) {
+    const int64_t t0 = (int64_t)m * p.MT, t1 = std::min<int64_t>(p.T, t0 + p.MT);
+    return Macro{m, (int)t0, (int)t1, (int64_t)p.k * t0};
+}
+
+}  // namespace
+
+mok_status launch_forward(const Plan &p, const void *schedule, void *workspace, const uint16_t *x,
+                          const float *topk_w, const mok_weights &w, uint16_t *out, void *fwd_ctx,
+                          hipStream_t st) {
+    if (p.R == 0) return MOK_OK;
+    if (p.precision != MOK_BF16) return MOK_ERROR_UNSUPPORTED;
+    const SchedView v = make_sched_view(p, const_cast<void *>(schedule));
+    char *ws = static_cast<char *>(workspace);
+    uint16_t *ring = reinterpret_cast<uint16_t *>(ws + p.w_ring);
+    uint16_t *aring = reinterpret_cast<uint16_t *>(ws + p.w_aring);
+    uint16_t *stage = reinterpret_cast<uint16_t *>(ws + p.w_stage);
+    uint16_t *h = reinterpret_cast<uint16_t *>(static_cast<char *>(fwd_ctx) + p.c_h);
+    const bool identity = p.debug & MOK_DEBUG_IDENTITY_EXPERT;
+    hipError_t err = hipSuccess;
+    for (const Round r : make_rounds(p, false)) {
+        const dim3 sgrid((unsigned)ceil_div(p.MB, kRowsPerBlock), (unsigned)(r.g1 - r.g0));
+        gather_rows<<<sgrid, 256, 0, st>>>(v, r.g0, p.n_slots, p.MB, p.H, p.k, x, ring);
+        if (identity) {
+            identity_rows<<<sgrid, 256, 0, st>>>(v, r.g0, p.n_slots, p.MB, p.H, p.k, (int)p.MT, p.nb_full, topk_w,
+                                                 ring, out, stage);
+        } else {
+            const unsigned mt = (unsigned)mtile_bound(p, r);
+            GateUpArgs ga{v, r.g0, r.g1, p.n_slots, p.MB, p.H, p.I, ring,
+                          static_cast<const uint16_t *>(w.w_gate), static_cast<const uint16_t *>(w.w_up), h, aring};
+            if ((err = launch_gemm<GateUp<CfgA>>(dim3(p.I / (CfgA::BN / 2), mt), ga, st)) != hipSuccess) break;
+            DownArgs da{v, r.g0, r.g1, p.n_slots, p.MB, p.H, p.I, p.k, (int)p.MT, p.nb_full, aring,
+                        static_cast<const uint16_t *>(w.w_down), topk_w, out, stage};
+            if ((err = launch_gemm<Down<CfgA>>(dim3((unsigned)ceil_div(p.H, CfgA::BN), mt), da, st)) != hipSuccess)
+                break;
+        }
+        if (p.k > 1 && (r.g1 == p.G || r.g1 == first_minibatch(p, macro_of_minibatch(p, r.g0) + 1))) {
+            const Macro mc = macro_info(p, macro_of_minibatch(p, r.g0));
+            combine_rows<<<(unsigned)ceil_div(mc.t1 - mc.t0, kRowsPerBlock), 256, 0, st>>>(
+                v, mc.t0, mc.t1, p.H, p.k, mc.base, topk_w, true, stage, out);
+        }
+    }
+    if (err == hipSuccess) err = hipGetLastError();
+    return err == hipSuccess ? MOK_OK : MOK_ERROR_LAUNCH_FAILED;
+}
+
+mok_status launch_backward(const Plan &p, const void *schedule, void *workspace, const uint16_t *x,
+                           const float *topk_w, const mok_weights &w, const void *fwd_ctx, const uint16_t *dy,
+                           uint16_t *dx, uint16_t *dw_gate, uint16_t *dw_up, uint16_t *dw_down, float *dtopk_w,
+                           hipStream_t st) {
+    if (p.precision != MOK_BF16) return MOK_ERROR_UNSUPPORTED;
+    const SchedView v = make_sched_view(p, const_cast<void *>(schedule));
+    char *ws = static_cast<char *>(workspace);
+    uint16_t *ring = reinterpret_cast<uint16_t *>(ws + p.w_ring);
+    uint16_t *stage = reinterpret_cast<uint16_t *>(ws + p.w_stage);
+    uint16_t *dh = reinterpret_cast<uint16_t *>(ws + p.w_dh);
+    uint16_t *ga = reinterpret_cast<uint16_t *>(ws + p.w_ga);
+    float *dgp = reinterpret_cast<float *>(ws + p.w_dgp);
+    const uint16_t *h = reinterpret_cast<const uint16_t *>(static_cast<const char *>(fwd_ctx) + p.c_h);
+    const uint16_t *wg = static_cast<const uint16_t *>(w.w_gate);
+    const uint16_t *wu = static_cast<const uint16_t *>(w.w_up);
+    const uint16_t *wd = static_cast<const uint16_t *>(w.w_down);
+    hipError_t err = hipSuccess;
+    if (p.R > 0) {
+        for (const Round r : make_rounds(p, true)) {
+            const dim3 sgrid((unsigned)ceil_div(p.MB, kRowsPerBlock), (unsigned)(r.g1 - r.g0));
+            gather_rows<<<sgrid, 256, 0, st>>>(v, r.g0, p.n_slots, p.MB, p.H, p.k, dy, ring);
+            const unsigned mt = (unsigned)mtile_bound(p, r);
+            DAArgs aa{v, r.g0, r.g1, p.n_slots, p.MB, p.H, p.I, p.dg_slices, ring, wd, h, topk_w, dh, ga, dgp};
+            if ((err = launch_gemm<DA<CfgA>>(dim3((unsigned)ceil_div(p.I, CfgA::BN), mt), aa, st)) != hipSuccess)
+                break;
+            DXArgs xa{v, r.g0, r.g1, p.n_slots, p.H, p.I, p.k, (int)p.MT, p.nb_full, dh, wg, wu, dx, stage};
+            if ((err = launch_gemm<DX<CfgA>>(dim3((unsigned)ceil_div(p.H, CfgA::BN), mt), xa, st)) != hipSuccess)
+                break;
+            if (p.k > 1 && r.g0 == first_minibatch(p, macro_of_minibatch(p, r.g0))) {
+                const Macro mc = macro_info(p, macro_of_minibatch(p, r.g0));
+                combine_rows<<<(unsigned)ceil_div(mc.t1 - mc.t0, kRowsPerBlock), 256, 0, st>>>(
+                    v, mc.t0, mc.t1, p.H, p.k, mc.base, topk_w, false, stage, dx);
+            }
+        }
+        if (err == hipSuccess)
+            reduce_router_grad<<<(unsigned)ceil_div(p.R, 256), 256, 0, st>>>(v, p.dg_slices, dgp, dtopk_w);
+    }
+    if (err == hipSuccess) {
+        WGUArgs gu{v, p.H, p.I, x, dh, dw_gate, dw_up};
+        err = launch_gemm<WGU<CfgA>>(
+            dim3((unsigned)ceil_div(2 * p.I, CfgA::BN), (unsigned)ceil_div(p.H, CfgA::BM), (unsigned)p.E), gu, st);
+    }
+    if (err == hipSuccess) {
+        WDArgs wda{v, p.H, p.I, ga, dy, dw_down};
+        err = launch_gemm<WD<CfgA>>(
+            dim3((unsigned)ceil_div(p.H, CfgA::BN), (unsigned)ceil_div(p.I, CfgA::BM), (unsigned)p.E), wda, st);
+    }
+    if (err == hipSuccess) err = hipGetLastError();
+    return err == hipSuccess ? MOK_OK : MOK_ERROR_LAUNCH_FAILED;
+}
+
+}  // namespace mok

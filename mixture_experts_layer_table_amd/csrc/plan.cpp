@@ -1,0 +1,123 @@
+// Host-side plan: validation, sizes and buffer layouts (no HIP calls).
+#include "plan.h"
+
+#include <algorithm>
+#include <cmath>
+
+#include "tiles.h"
+
+namespace mok {
+
+namespace {
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+struct Carver {
+    size_t off = 0;
+    size_t take(size_t bytes) {
+        size_t o = off;
+        off = align_up(off + bytes);
+        return o;
+    }
+};
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace
+
+mok_status make_plan(const mok_config *cfg, const mok_shape *shape, Plan *p) {
+    if (!cfg || !shape || !p) return MOK_ERROR_INVALID_VALUE;
+    const mok_shape &s = *shape;
+    if (s.T < 0 || s.H <= 0 || s.I <= 0 || s.E <= 0 || s.k <= 0) return MOK_ERROR_INVALID_VALUE;
+    if (s.H % 64 || s.I % 64) return MOK_ERROR_INVALID_VALUE;
+    if (s.k > s.E || s.E > kMaxExperts) return MOK_ERROR_INVALID_VALUE;
+    if (s.T * (int64_t)s.k >= (int64_t(1) << 31)) return MOK_ERROR_INVALID_VALUE;
+    if (cfg->minibatch_rows < 16 || cfg->minibatch_rows % 16) return MOK_ERROR_INVALID_VALUE;
+    if (cfg->macrobatch_tokens < 0 || cfg->ring_bytes <= 0) return MOK_ERROR_INVALID_VALUE;
+    if (!(cfg->capacity_multiplier > 0.0f && cfg->capacity_multiplier <= 4.0f))
+        return MOK_ERROR_INVALID_VALUE;
+    if (cfg->precision != MOK_BF16 && cfg->precision != MOK_MXFP8) return MOK_ERROR_INVALID_VALUE;
+    if (cfg->debug_flags & ~MOK_DEBUG_IDENTITY_EXPERT) return MOK_ERROR_INVALID_VALUE;
+
+    Plan q;
+    q.T = s.T;
+    q.H = s.H;
+    q.I = s.I;
+    q.E = s.E;
+    q.k = s.k;
+    q.R = s.T * s.k;
+    q.MB = cfg->minibatch_rows;
+    q.precision = cfg->precision;
+    q.debug = cfg->debug_flags;
+    q.MT = (cfg->macrobatch_tokens == 0 || cfg->macrobatch_tokens >= s.T) ? std::max<int64_t>(s.T, 1)
+                                                                            : cfg->macrobatch_tokens;
+    q.NM = s.T == 0 ? 0 : (int)ceil_div(s.T, q.MT);
+    q.nb_full = (int)ceil_div(q.k * q.MT, q.MB);
+    q.G = 0;
+    q.W = 0;
+    if (q.NM > 0) {
+        const int64_t t_last = s.T - (int64_t)(q.NM - 1) * q.MT;
+        const int64_t r_full = q.k * q.MT, r_last = q.k * t_last;
+        q.G = (q.NM - 1) * q.nb_full + (int)ceil_div(r_last, q.MB);
+        q.W = (int64_t)(q.NM - 1) * (q.nb_full + std::min<int64_t>(q.E, r_full) - 1) +
+              (ceil_div(r_last, q.MB) + std::min<int64_t>(q.E, r_last) - 1);
+    }
+    q.cap = (int64_t)std::ceil((double)cfg->capacity_multiplier * (double)q.W);
+    q.ring_row_bytes = q.precision == MOK_BF16 ? (size_t)2 * q.H : (size_t)q.H + q.H / 32;
+    q.n_slots = cfg->ring_bytes / ((int64_t)q.MB * (int64_t)q.ring_row_bytes);
+    if (q.n_slots < 2) return MOK_ERROR_INVALID_VALUE;
+    q.tile = choose_tiles(q.H, q.I, q.E, q.k, q.T, q.precision);
+    q.max_mtiles = q.R / q.tile.BM + q.cap + 1;
+    q.nchunks = (int)ceil_div(q.R, kSchedChunk);
+    q.dg_slices = (int)ceil_div(q.I, q.tile.da_wn);
+    q.stage_rows = q.k > 1 ? q.k * std::min<int64_t>(q.MT, q.T) : 0;
+
+    Carver c;
+    q.s_status = c.take(4);
+    q.s_nseg = 4;
+    q.s_counts = c.take(4 * (size_t)q.E);
+    q.s_offsets = c.take(4 * (size_t)(q.E + 1));
+    q.s_mcounts = c.take(4 * (size_t)q.NM * q.E);
+    q.s_moffsets = c.take(4 * (size_t)q.NM * (q.E + 1));
+    q.s_perm = c.take(4 * (size_t)q.R);
+    q.s_inv = c.take(4 * (size_t)q.R);
+    q.s_canon = c.take(4 * (size_t)q.R);
+    q.s_ctok = c.take(4 * (size_t)q.R);
+    q.s_mbstart = c.take(4 * (size_t)(q.G + 1));
+    q.s_segments = c.take(16 * (size_t)q.cap);
+    q.s_chunk = c.take(4 * (size_t)q.nchunks * q.E);
+    q.s_bound = c.take(4 * (size_t)(q.NM + 1) * q.E);
+    q.s_segfirst = c.take(4 * (size_t)(q.G + 1));
+    q.s_mtfirst = c.take(4 * (size_t)(q.G + 1));
+    q.s_mtiles = c.take(16 * (size_t)q.max_mtiles);
+    q.s_total = c.off;
+
+    Carver w;
+    q.w_ring = w.take((size_t)q.n_slots * q.MB * q.ring_row_bytes);
+    q.w_aring = w.take((size_t)q.n_slots * q.MB * q.I * 2);
+    q.w_stage = w.take((size_t)q.stage_rows * q.H * 2);
+    q.w_dh = w.take((size_t)q.R * 2 * q.I * 2);
+    q.w_ga = w.take((size_t)q.R * q.I * 2);
+    q.w_dgp = w.take((size_t)q.R * q.dg_slices * 4);
+    q.w_total = w.off;
+
+    Carver x;
+    q.c_h = x.take((size_t)q.R * 2 * q.I * 2);
+    q.c_total = x.off;
+    *p = q;
+    return MOK_OK;
+}
+
+void minibatch_rows(const Plan &p, int g, int64_t *q0, int64_t *q1) {
+    const int m = g / p.nb_full, b = g % p.nb_full;
+    const int64_t t0 = (int64_t)m * p.MT;
+    const int64_t rm = p.k * (std::min<int64_t>(p.T, t0 + p.MT) - t0);
+    const int64_t base = p.k * t0;
+    *q0 = base + (int64_t)b * p.MB;
+    *q1 = base + std::min<int64_t>(rm, (int64_t)(b + 1) * p.MB);
+}
+
+int macro_of_minibatch(const Plan &p, int g) { return g / p.nb_full; }
+int first_minibatch(const Plan &p, int m) { return m * p.nb_full; }
+
+}  // namespace mok

@@ -1,0 +1,57 @@
+// Host-side plan: every size and byte offset derived from (config, shape).
+// Pure C++ with no HIP calls, so size queries and argument validation run
+// without a GPU.
+#pragma once
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/mok.h"
+#include "tiles.h"
+
+namespace mok {
+
+constexpr int kSchedChunk = 1024;   // routed rows per block in the schedule kernels
+constexpr size_t kAlign = 256;      // alignment of every sub-buffer
+
+struct Plan {
+    // shape
+    int64_t T = 0, R = 0;
+    int H = 0, I = 0, E = 0, k = 0;
+    // knobs
+    int MB = 0;
+    int64_t MT = 0;          // effective macro-batch tokens (T if 0 or >= T; 1 if T == 0)
+    int precision = MOK_BF16;
+    uint32_t debug = 0;
+    // derived
+    int NM = 0;              // macro-batches
+    int nb_full = 0;         // mini-batches in a full macro-batch
+    int G = 0;               // mini-batches
+    int64_t W = 0, cap = 0;  // worst-case segments, segment capacity
+    int64_t n_slots = 0;     // ring slots (mini-batches the ring holds)
+    size_t ring_row_bytes = 0;
+    TileChoice tile{};
+    int64_t max_mtiles = 0;  // bound on m-tiles over all segments
+    int nchunks = 0;         // schedule chunks of kSchedChunk rows
+    int dg_slices = 0;       // router-grad partial sums per routed row
+    int64_t stage_rows = 0;  // rows of the per-macro-batch combine staging (k > 1)
+
+    // schedule buffer (byte offsets)
+    size_t s_status = 0, s_nseg = 0, s_counts = 0, s_offsets = 0, s_mcounts = 0,
+           s_moffsets = 0, s_perm = 0, s_inv = 0, s_canon = 0, s_ctok = 0, s_mbstart = 0,
+           s_segments = 0, s_chunk = 0, s_bound = 0, s_segfirst = 0, s_mtfirst = 0,
+           s_mtiles = 0, s_total = 0;
+    // workspace (byte offsets)
+    size_t w_ring = 0, w_aring = 0, w_stage = 0, w_dh = 0, w_ga = 0, w_dgp = 0, w_total = 0;
+    // fwd_ctx (byte offsets)
+    size_t c_h = 0, c_total = 0;
+};
+
+mok_status make_plan(const mok_config *cfg, const mok_shape *shape, Plan *p);
+
+// Rows [q0, q1) of mini-batch g: host-computable (depends on sizes only).
+void minibatch_rows(const Plan &p, int g, int64_t *q0, int64_t *q1);
+// Macro-batch of mini-batch g and the first mini-batch of macro-batch m.
+int macro_of_minibatch(const Plan &p, int g);
+int first_minibatch(const Plan &p, int m);
+
+}  // namespace mok

@@ -1,0 +1,267 @@
+// Device-side schedule builder: one table drives every phase of both passes
+// ("Mixture-of-Kittens(MoK)란?" explainer, section 4 ①), built without any
+// device-to-host read and without dropping a routed row (section 4 ③).
+//
+// Processing order sorts routed rows f = t*k + j by (macro-batch, expert, f).
+// With rank_e(f) = #{f' < f : id(f') = e} (a stable counting sort), the
+// position of f in macro-batch m is
+//     q(f) = moffsets[m][e] + rank_e(f) - rank_e(first row of m),
+// and its position in canonical (expert, f) order is offsets[e] + rank_e(f).
+// Only integer atomics are used (order-independent counts).
+#include "kernels.h"
+#include "views.h"
+
+namespace mok {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+__global__ __launch_bounds__(kThreads) void sched_init(SchedView v) {
+    if (threadIdx.x == 0) {
+        *v.status = 0;
+        *v.n_seg = 0;
+    }
+    // defined values for an empty call (T = 0), where the scan does not run
+    for (int e = threadIdx.x; e <= v.E; e += kThreads) {
+        if (e < v.E) v.counts[e] = 0;
+        v.offsets[e] = 0;
+    }
+}
+
+// Per-chunk expert histogram; flags ids outside [0, E).
+__global__ __launch_bounds__(kThreads) void sched_hist(const int32_t *__restrict__ ids, SchedView v) {
+    extern __shared__ int hist[];
+    for (int e = threadIdx.x; e < v.E; e += kThreads) hist[e] = 0;
+    __syncthreads();
+    const int base = blockIdx.x * kSchedChunk;
+    bool bad = false;
+    for (int r = threadIdx.x; r < kSchedChunk; r += kThreads) {
+        const int f = base + r;
+        if (f < v.R) {
+            const int id = ids[f];
+            if ((unsigned)id >= (unsigned)v.E)
+                bad = true;
+            else
+                atomicAdd(&hist[id], 1);
+        }
+    }
+    if (bad) atomicOr(v.status, MOK_BAD_EXPERT_ID);
+    __syncthreads();
+    for (int e = threadIdx.x; e < v.E; e += kThreads) v.chunk[blockIdx.x * v.E + e] = hist[e];
+}
+
+// Exclusive scan of each expert's chunk histogram over chunks; counts, offsets.
+__global__ __launch_bounds__(kThreads) void sched_scan(SchedView v) {
+    if (*v.status) return;
+    for (int e = threadIdx.x; e < v.E; e += kThreads) {
+        int run = 0;
+        for (int c = 0; c < v.nchunks; ++c) {
+            const int t = v.chunk[c * v.E + e];
+            v.chunk[c * v.E + e] = run;
+            run += t;
+        }
+        v.counts[e] = run;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int run = 0;
+        for (int e = 0; e < v.E; ++e) {
+            v.offsets[e] = run;
+            run += v.counts[e];
+        }
+        v.offsets[v.E] = run;
+    }
+}
+
+// rank_e at the first routed row of each macro-batch (and at R).
+__global__ __launch_bounds__(kThreads) void sched_bounds(const int32_t *__restrict__ ids, SchedView v) {
+    if (*v.status) return;
+    extern __shared__ int hist[];
+    const int b = blockIdx.x;
+    const int64_t fb64 = (int64_t)b * v.k * v.MT;
+    const int fb = (int)(fb64 < v.R ? fb64 : v.R);
+    const int c = fb / kSchedChunk;
+    for (int e = threadIdx.x; e < v.E; e += kThreads) hist[e] = 0;
+    __syncthreads();
+    for (int r = c * kSchedChunk + threadIdx.x; r < fb; r += kThreads) atomicAdd(&hist[ids[r]], 1);
+    __syncthreads();
+    for (int e = threadIdx.x; e < v.E; e += kThreads)
+        v.bound[b * v.E + e] = (c < v.nchunks ? v.chunk[c * v.E + e] : v.counts[e]) + hist[e];
+}
+
+struct MbRange {
+    int m, q_lo, q_hi;
+};
+
+__device__ MbRange minibatch_range(const SchedView &v, int g) {
+    const int m = g / v.nb_full, b = g % v.nb_full;
+    const int t0 = m * v.MT;
+    const int t1 = min(v.T, t0 + v.MT);
+    const int base = v.k * t0, rm = v.k * (t1 - t0);
+    return MbRange{m, base + b * v.MB, base + min(rm, (b + 1) * v.MB)};
+}
+
+// Largest e in [0, E) with M[e] <= q (M non-decreasing, M[0] <= q).
+__device__ int expert_at(const int32_t *M, int E, int q) {
+    int lo = 0, hi = E;   // answer in [lo, hi)
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (M[mid] <= q) lo = mid; else hi = mid;
+    }
+    return lo;
+}
+
+constexpr int kTableThreads = 1024;
+
+__device__ void block_exclusive_scan2(int *a, int *b, int G, int &tot_a, int &tot_b) {
+    __shared__ int sa[kTableThreads], sb[kTableThreads];
+    const int tid = threadIdx.x;
+    const int per = (G + kTableThreads - 1) / kTableThreads;
+    const int lo = min(G, tid * per), hi = min(G, lo + per);
+    int xa = 0, xb = 0;
+    for (int i = lo; i < hi; ++i) {
+        xa += a[i];
+        xb += b[i];
+    }
+    sa[tid] = xa;
+    sb[tid] = xb;
+    __syncthreads();
+    for (int d = 1; d < kTableThreads; d <<= 1) {
+        const int ya = tid >= d ? sa[tid - d] : 0, yb = tid >= d ? sb[tid - d] : 0;
+        __syncthreads();
+        sa[tid] += ya;
+        sb[tid] += yb;
+        __syncthreads();
+    }
+    int ra = tid ? sa[tid - 1] : 0, rb = tid ? sb[tid - 1] : 0;
+    for (int i = lo; i < hi; ++i) {
+        const int ta = a[i], tb = b[i];
+        a[i] = ra;
+        b[i] = rb;
+        ra += ta;
+        rb += tb;
+    }
+    tot_a = sa[kTableThreads - 1];
+    tot_b = sb[kTableThreads - 1];
+    __syncthreads();
+}
+
+// Macro-batch offsets, mini-batch ranges, segments and m-tiles (one block).
+__global__ __launch_bounds__(kTableThreads) void sched_table(SchedView v) {
+    if (*v.status) return;
+    const int tid = threadIdx.x;
+    for (int m = tid; m < v.NM; m += kTableThreads) {
+        int run = m * v.MT * v.k;
+        for (int e = 0; e < v.E; ++e) {
+            const int mc = v.bound[(m + 1) * v.E + e] - v.bound[m * v.E + e];
+            v.mcounts[m * v.E + e] = mc;
+            v.moffsets[m * (v.E + 1) + e] = run;
+            run += mc;
+        }
+        v.moffsets[m * (v.E + 1) + v.E] = run;
+    }
+    __syncthreads();
+    for (int g = tid; g < v.G; g += kTableThreads) {
+        const MbRange r = minibatch_range(v, g);
+        const int32_t *M = v.moffsets + r.m * (v.E + 1);
+        int ns = 0, nt = 0;
+        for (int e = expert_at(M, v.E, r.q_lo); e < v.E && M[e] < r.q_hi; ++e) {
+            const int len = min(r.q_hi, M[e + 1]) - max(r.q_lo, M[e]);
+            if (len > 0) {
+                ++ns;
+                nt += (len + v.BM - 1) / v.BM;
+            }
+        }
+        v.segfirst[g] = ns;
+        v.mtfirst[g] = nt;
+    }
+    __syncthreads();
+    int n_seg = 0, n_mt = 0;
+    block_exclusive_scan2(v.segfirst, v.mtfirst, v.G, n_seg, n_mt);
+    const bool overflow = n_seg > v.cap;
+    if (tid == 0) {
+        *v.n_seg = n_seg;
+        if (overflow) atomicOr(v.status, MOK_SCHEDULE_OVERFLOW);
+        v.segfirst[v.G] = n_seg;
+        v.mtfirst[v.G] = n_mt;
+        v.mb_start[v.G] = v.R;
+    }
+    for (int g = tid; g < v.G; g += kTableThreads) {
+        const MbRange r = minibatch_range(v, g);
+        v.mb_start[g] = r.q_lo;
+        const int32_t *M = v.moffsets + r.m * (v.E + 1);
+        int s = v.segfirst[g], t = v.mtfirst[g];
+        for (int e = expert_at(M, v.E, r.q_lo); e < v.E && M[e] < r.q_hi; ++e) {
+            const int a = max(r.q_lo, M[e]);
+            const int len = min(r.q_hi, M[e + 1]) - a;
+            if (len <= 0) continue;
+            if (s < v.cap) {
+                int4 sg = make_int4(g, e, a, len);
+                reinterpret_cast<int4 *>(v.segments)[s] = sg;
+            }
+            ++s;
+            if (!overflow) {
+                for (int j = 0; j * v.BM < len; ++j, ++t) {
+                    if (t < v.max_mtiles) v.mtiles[t] = MTile{a + j * v.BM, min(v.BM, len - j * v.BM), e, g};
+                }
+            }
+        }
+    }
+}
+
+// Stable scatter: perm, inv, canon, ctok.
+__global__ __launch_bounds__(kThreads) void sched_scatter(const int32_t *__restrict__ ids, SchedView v) {
+    if (*v.status) return;
+    __shared__ int s_ids[kSchedChunk];
+    const int base = blockIdx.x * kSchedChunk;
+    const int n = min(kSchedChunk, v.R - base);
+    for (int r = threadIdx.x; r < n; r += kThreads) s_ids[r] = ids[base + r];
+    __syncthreads();
+    const int r0 = threadIdx.x * 4;
+    if (r0 >= n) return;
+    int e4[4], cnt[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) e4[j] = r0 + j < n ? s_ids[r0 + j] : -1;
+    for (int r = 0; r < r0; ++r) {
+        const int x = s_ids[r];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) cnt[j] += (x == e4[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int r = r0 + j;
+        if (r >= n) break;
+        for (int i = 0; i < j; ++i) cnt[j] += (e4[i] == e4[j]);
+        const int e = e4[j];
+        const int f = base + r;
+        const int rank = v.chunk[blockIdx.x * v.E + e] + cnt[j];
+        const int t = f / v.k;
+        const int m = t / v.MT;
+        const int q = v.moffsets[m * (v.E + 1) + e] + rank - v.bound[m * v.E + e];
+        const int c = v.offsets[e] + rank;
+        if ((unsigned)q >= (unsigned)v.R || (unsigned)c >= (unsigned)v.R) continue;  // unreachable
+        v.perm[q] = f;
+        v.inv[f] = q;
+        v.canon[c] = q;
+        v.ctok[c] = t;
+    }
+}
+
+}  // namespace
+
+mok_status launch_build_schedule(const Plan &p, const int32_t *ids, void *schedule, hipStream_t st) {
+    SchedView v = make_sched_view(p, schedule);
+    const size_t hist_lds = sizeof(int) * (size_t)p.E;
+    sched_init<<<1, kThreads, 0, st>>>(v);
+    if (p.nchunks > 0) {
+        sched_hist<<<p.nchunks, kThreads, hist_lds, st>>>(ids, v);
+        sched_scan<<<1, kThreads, 0, st>>>(v);
+        sched_bounds<<<p.NM + 1, kThreads, hist_lds, st>>>(ids, v);
+    }
+    sched_table<<<1, kTableThreads, 0, st>>>(v);
+    if (p.nchunks > 0) sched_scatter<<<p.nchunks, kThreads, 0, st>>>(ids, v);
+    return hipGetLastError() == hipSuccess ? MOK_OK : MOK_ERROR_LAUNCH_FAILED;
+}
+
+}  // namespace mok

@@ -1,0 +1,94 @@
+"""Helpers for the GPU tests: upload seeded inputs, run the layer through the
+C ABI, and compare with the oracle."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import mixture_experts_layer_table_amd as mok
+import synth
+from oracle import layer as L
+
+DEV = "cuda:0"
+TOL_BF16 = 1e-2      # relative Frobenius error, per output tensor (per expert for dW)
+
+
+def dev_bf16(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(DEV).view(torch.bfloat16)
+
+
+def host_f64(t: torch.Tensor) -> np.ndarray:
+    """bf16 / fp32 device tensor -> fp64 numpy (exact)."""
+    if t.dtype == torch.bfloat16:
+        return L.bf16_bits_to_f64(t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16))
+    return t.detach().cpu().numpy().astype(np.float64)
+
+
+def knobs(cfg: synth.LayerConfig, **over) -> mok.MoKConfig:
+    k = dict(minibatch_rows=cfg.minibatch_rows, macrobatch_tokens=cfg.macrobatch_tokens,
+             ring_bytes=cfg.ring_bytes, capacity_multiplier=1.0,
+             precision=mok.MOK_BF16 if cfg.precision == "bf16" else mok.MOK_MXFP8)
+    k.update(over)
+    return mok.MoKConfig(**k)
+
+
+class DeviceInputs:
+    def __init__(self, inp: synth.LayerInputs):
+        self.cfg = inp.cfg
+        self.ids = torch.from_numpy(inp.topk_ids.astype(np.int32)).to(DEV)
+        self.w = torch.from_numpy(inp.topk_w.astype(np.float32)).to(DEV)
+        self.x = dev_bf16(inp.x)
+        self.dy = dev_bf16(inp.dy)
+        self.wg = dev_bf16(inp.w_gate)
+        self.wu = dev_bf16(inp.w_up)
+        self.wd = dev_bf16(inp.w_down)
+
+
+def run_layer(d: DeviceInputs, config: mok.MoKConfig, backward: bool = True):
+    """Schedule + forward (+ backward) on the device. Returns dict of device tensors."""
+    c = d.cfg
+    ws = mok.get_workspace(config, device=DEV, num_local_tokens=c.T, hidden_size=c.H,
+                           intermediate_size=c.I, num_experts=c.E, topk=c.k)
+    sched = mok.build_schedule(ws, d.ids)
+    weights = mok.weights_bf16(d.wg, d.wu, d.wd)
+    out, ctx = mok.forward(ws, sched, d.x, d.w, weights)
+    res = dict(out=out, schedule=sched)
+    if backward:
+        res.update(mok.backward(ws, sched, ctx, d.x, d.w, weights, d.dy))
+    torch.cuda.synchronize()
+    return res
+
+
+def status_word(sched: torch.Tensor) -> int:
+    return int(sched[:4].cpu().numpy().view(np.uint32)[0])
+
+
+def oracle_full(inp: synth.LayerInputs):
+    f = L.bf16_bits_to_f64
+    x, dy = f(inp.x), f(inp.dy)
+    Wg, Wu, Wd = f(inp.w_gate), f(inp.w_up), f(inp.w_down)
+    out, _ = L.forward(x, inp.topk_ids, inp.topk_w, Wg, Wu, Wd)
+    g = L.backward(x, inp.topk_ids, inp.topk_w, Wg, Wu, Wd, dy)
+    return dict(out=out, dx=g["dx"], dw_gate=g["dWg"], dw_up=g["dWu"], dw_down=g["dWd"], dtopk_w=g["dw"])
+
+
+def compare_full(res, ref, E, tol=TOL_BF16):
+    errs = {}
+    for name in ("out", "dx", "dtopk_w"):
+        if name in res:
+            errs[name] = L.rel_frobenius(host_f64(res[name]), ref[name])
+    for name in ("dw_gate", "dw_up", "dw_down"):
+        if name in res:
+            got = host_f64(res[name])
+            for e in range(E):
+                errs[f"{name}[{e}]"] = L.rel_frobenius(got[e], ref[name][e])
+    bad = {k: v for k, v in errs.items() if not v <= tol}
+    assert not bad, f"over tolerance {tol}: {bad}"
+    return errs
+
+
+def same_bits(a: dict, b: dict, names=("out", "dx", "dw_gate", "dw_up", "dw_down", "dtopk_w")):
+    for n in names:
+        if n in a:
+            assert torch.equal(a[n].view(torch.uint8) if a[n].dtype != torch.float32 else a[n].view(torch.int32),
+                               b[n].view(torch.uint8) if b[n].dtype != torch.float32 else b[n].view(torch.int32)), n

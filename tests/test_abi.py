@@ -1,0 +1,100 @@
+"""The C-ABI library loads without a GPU, exports every entry point declared in
+include/mok.h, and rejects bad host-checkable arguments synchronously."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mixture_experts_layer_table_amd as mok
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "mok.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(mok_\w+)\s*\(", text, re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared()
+    assert set(names) == set(mok.EXPORTS)
+    lib = ctypes.CDLL(mok._LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_config_default():
+    c = mok.mok_config()
+    assert mok.mok_config_default(c) == mok.MOK_OK
+    assert (c.minibatch_rows, c.macrobatch_tokens, c.ring_bytes, c.capacity_multiplier, c.precision) == \
+        (512, 0, 256 << 20, 1.0, mok.MOK_BF16)
+
+
+BAD_SHAPES = [dict(T=-1), dict(H=100), dict(I=96), dict(E=0), dict(k=0), dict(k=9), dict(T=1 << 31)]
+
+
+@pytest.mark.parametrize("bad", BAD_SHAPES)
+def test_bad_shapes_rejected(bad):
+    s = dict(T=64, H=128, I=64, E=8, k=2)
+    s.update(bad)
+    with pytest.raises(mok.MokError) as e:
+        mok.query_sizes(mok.MoKConfig(minibatch_rows=32, ring_bytes=1 << 20), **s)
+    assert e.value.status == mok.MOK_ERROR_INVALID_VALUE
+
+
+BAD_CONFIGS = [dict(minibatch_rows=8), dict(minibatch_rows=40), dict(capacity_multiplier=0.0),
+               dict(capacity_multiplier=4.5), dict(precision=7), dict(ring_bytes=32 * 256),
+               dict(macrobatch_tokens=-1), dict(debug_flags=4)]
+
+
+@pytest.mark.parametrize("bad", BAD_CONFIGS)
+def test_bad_configs_rejected(bad):
+    c = dict(minibatch_rows=32, ring_bytes=1 << 20)
+    c.update(bad)
+    with pytest.raises(mok.MokError) as e:
+        mok.query_sizes(mok.MoKConfig(**c), 64, 128, 64, 8, 2)
+    assert e.value.status == mok.MOK_ERROR_INVALID_VALUE
+
+
+def test_schedule_layout_matches_oracle_sizes():
+    from oracle import schedule as S
+    import synth
+    for name in ("tiny", "full_layer", "ep64_share", "stream"):
+        cfg = synth.CONFIGS[name]
+        c = mok.MoKConfig(minibatch_rows=cfg.minibatch_rows, macrobatch_tokens=cfg.macrobatch_tokens,
+                          ring_bytes=cfg.ring_bytes)
+        lay = mok.schedule_layout(c, cfg.T, cfg.H, cfg.I, cfg.E, cfg.k)
+        assert lay.R == cfg.R
+        assert lay.cap == S.capacity(cfg.T, cfg.k, cfg.E, cfg.minibatch_rows, cfg.macrobatch_tokens, 1.0)
+        ids, _, _ = synth.make_routing(cfg)
+        s = S.build(ids, cfg.E, cfg.minibatch_rows, cfg.macrobatch_tokens)
+        assert (lay.NM, lay.G) == (s.NM, s.G)
+        ws, sc, cx = mok.query_sizes(c, cfg.T, cfg.H, cfg.I, cfg.E, cfg.k)
+        assert sc == lay.total_bytes and cx >= cfg.R * 2 * cfg.I * 2
+
+
+def test_ring_slot_count_rule():
+    from oracle import schedule as S
+    # fewer than two mini-batches in the ring is rejected; exactly two is accepted
+    H, MB = 128, 32
+    two = 2 * MB * 2 * H
+    mok.query_sizes(mok.MoKConfig(minibatch_rows=MB, ring_bytes=two), 64, H, 64, 8, 2)
+    assert S.ring_slots(two, MB, 2 * H) == 2
+    with pytest.raises(mok.MokError):
+        mok.query_sizes(mok.MoKConfig(minibatch_rows=MB, ring_bytes=two - 1), 64, H, 64, 8, 2)
+
+
+def test_null_and_misaligned_pointers_rejected_without_device_work():
+    c = mok.MoKConfig(minibatch_rows=32, ring_bytes=1 << 20).c()
+    sh = mok.mok_shape(64, 128, 64, 8, 2)
+    assert mok.mok_build_schedule(c, sh, None, None, 1 << 20, None) == mok.MOK_ERROR_INVALID_VALUE
+    assert mok.mok_build_schedule(c, sh, ctypes.c_void_p(0x1003), ctypes.c_void_p(0x2000), 1 << 20, None) \
+        == mok.MOK_ERROR_INVALID_VALUE
+    assert mok.mok_build_schedule(c, sh, ctypes.c_void_p(0x1000), ctypes.c_void_p(0x2000), 16, None) \
+        == mok.MOK_ERROR_BUFFER_TOO_SMALL
+    w = mok.mok_weights()
+    assert mok.mok_forward(c, sh, None, None, 0, None, None, w, None, None, 0, None) == \
+        mok.MOK_ERROR_INVALID_VALUE
+    assert mok.mok_mxfp8_quantize(None, 1, 1, 33, 0, None, None, None) == mok.MOK_ERROR_INVALID_VALUE
+    assert mok.mok_mxfp8_quantize(None, 1, 1, 32, 2, None, None, None) == mok.MOK_ERROR_INVALID_VALUE

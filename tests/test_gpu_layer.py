@@ -1,0 +1,118 @@
+"""Forward + backward on the GPU against the fp64 oracle at sizes the oracle
+finishes in seconds, plus the method's invariants: permute then unpermute is
+the identity, runs and knob settings are bitwise identical, data-dependent
+errors raise the status word."""
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_layer_table_amd as mok
+import synth
+from gpu_support import (DEV, DeviceInputs, compare_full, knobs, oracle_full, run_layer, same_bits,
+                         status_word)
+
+pytestmark = pytest.mark.gpu
+
+# several tiles in every GEMM dimension, ragged tails, rings smaller than the data
+SMALL = {
+    "tiny": synth.CONFIGS["tiny"],
+    "ragged_k2": synth.small_config("ragged_k2", T=300, H=256, I=192, E=5, k=2, minibatch_rows=48,
+                                    macrobatch_tokens=100, ring_bytes=3 * 48 * 512),
+    "k1_macro": synth.small_config("k1_macro", T=1000, H=384, I=128, E=3, k=1, minibatch_rows=64,
+                                   macrobatch_tokens=300, ring_bytes=4 * 64 * 768, routing="dirichlet"),
+    "k_eq_E": synth.small_config("k_eq_E", T=70, H=128, I=64, E=4, k=4, minibatch_rows=16,
+                                 ring_bytes=2 * 16 * 256),
+    "wide": synth.small_config("wide", T=520, H=640, I=320, E=2, k=1, minibatch_rows=160,
+                               ring_bytes=1 << 22, routing="zipf"),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_parity_small(name):
+    cfg = SMALL[name]
+    print(f"[layer] parity {name}", flush=True)
+    inp = synth.make_inputs(cfg)
+    res = run_layer(DeviceInputs(inp), knobs(cfg))
+    assert status_word(res["schedule"]) == 0
+    errs = compare_full(res, oracle_full(inp), cfg.E)
+    print({k: f"{v:.2e}" for k, v in errs.items() if not k.startswith("dw_")}, flush=True)
+
+
+def test_empty_experts_get_zero_weight_grads():
+    cfg = synth.small_config("sparse", T=200, H=128, I=64, E=6, k=1, minibatch_rows=32, ring_bytes=1 << 20,
+                             routing="zipf")
+    inp = synth.make_inputs(cfg)
+    inp.topk_ids[:] = np.where(inp.topk_ids < 3, inp.topk_ids, 0)   # experts 3..5 receive nothing
+    res = run_layer(DeviceInputs(inp), knobs(cfg))
+    compare_full(res, oracle_full(inp), cfg.E)
+    for n in ("dw_gate", "dw_up", "dw_down"):
+        assert not res[n][3:].float().abs().sum().item()
+
+
+def test_empty_call():
+    cfg = synth.small_config("empty", T=0, H=128, I=64, E=4, k=2, minibatch_rows=16, ring_bytes=1 << 20)
+    inp = synth.make_inputs(cfg)
+    d = DeviceInputs(inp)
+    res = run_layer(d, knobs(cfg))
+    assert res["out"].numel() == 0 and res["dx"].numel() == 0
+    for n in ("dw_gate", "dw_up", "dw_down"):
+        assert not res[n].float().abs().sum().item()
+
+
+def test_permute_unpermute_identity():
+    # identity experts, k = 1, unit gates: out must equal x bit for bit
+    cfg = synth.small_config("perm", T=777, H=256, I=64, E=7, k=1, minibatch_rows=32, macrobatch_tokens=200,
+                             ring_bytes=3 * 32 * 512, routing="dirichlet")
+    inp = synth.make_inputs(cfg)
+    inp.topk_w[:] = 1.0
+    d = DeviceInputs(inp)
+    res = run_layer(d, knobs(cfg, debug_flags=mok.MOK_DEBUG_IDENTITY_EXPERT), backward=False)
+    assert torch.equal(res["out"].view(torch.int16), d.x.view(torch.int16))
+
+
+def test_bitwise_deterministic_ten_runs():
+    cfg = SMALL["ragged_k2"]
+    d = DeviceInputs(synth.make_inputs(cfg))
+    first = run_layer(d, knobs(cfg))
+    for _ in range(9):
+        same_bits(first, run_layer(d, knobs(cfg)))
+
+
+@pytest.mark.parametrize("name", ["ragged_k2", "k1_macro"])
+def test_knobs_do_not_change_bits(name):
+    cfg = SMALL[name]
+    d = DeviceInputs(synth.make_inputs(cfg))
+    base = run_layer(d, knobs(cfg))
+    row = 2 * cfg.H
+    for over in (dict(minibatch_rows=16), dict(minibatch_rows=512, ring_bytes=2 * 512 * row),
+                 dict(macrobatch_tokens=0),
+                 dict(macrobatch_tokens=7), dict(ring_bytes=2 * cfg.minibatch_rows * row),
+                 dict(ring_bytes=1 << 24), dict(capacity_multiplier=4.0)):
+        print(f"[layer] knobs {name} {over}", flush=True)
+        same_bits(base, run_layer(d, knobs(cfg, **over)))
+
+
+def test_status_flags_stop_the_layer():
+    cfg = SMALL["tiny"]
+    inp = synth.make_inputs(cfg)
+    d = DeviceInputs(inp)
+    c = knobs(cfg)
+    ws = mok.get_workspace(c, device=DEV, num_local_tokens=cfg.T, hidden_size=cfg.H, intermediate_size=cfg.I,
+                           num_experts=cfg.E, topk=cfg.k)
+    bad = d.ids.clone()
+    bad[5, 1] = cfg.E
+    sched = mok.build_schedule(ws, bad)
+    out = torch.full((cfg.T, cfg.H), 7.0, dtype=torch.bfloat16, device=DEV)
+    w = mok.weights_bf16(d.wg, d.wu, d.wd)
+    mok.forward(ws, sched, d.x, d.w, w, out=out)
+    torch.cuda.synchronize()
+    assert status_word(sched) == mok.MOK_BAD_EXPERT_ID
+    assert torch.all(out == 7.0)   # no work was done
+    # capacity overflow
+    ws2 = mok.get_workspace(knobs(cfg, capacity_multiplier=0.05), device=DEV, num_local_tokens=cfg.T,
+                            hidden_size=cfg.H, intermediate_size=cfg.I, num_experts=cfg.E, topk=cfg.k)
+    sched2 = mok.build_schedule(ws2, d.ids)
+    mok.forward(ws2, sched2, d.x, d.w, w, out=out)
+    torch.cuda.synchronize()
+    assert status_word(sched2) == mok.MOK_SCHEDULE_OVERFLOW
+    assert torch.all(out == 7.0)
