@@ -1,0 +1,234 @@
+#!/usr/bin/env python3
+"""Throughput of one GPU's share of the MoE training layer (forward + backward).
+
+One step = one pass of the whole hot path on one batch of synthetic input:
+schedule build + forward (ring gather, gate/up GEMM with SwiGLU, down GEMM,
+weighted combine) + backward (dy gather, dA GEMM with SwiGLU backward and
+router-weight gradient, dX GEMM with combine, router-gradient reduction,
+weight-gradient GEMMs). Inputs are resident in HBM before timing starts.
+
+Prints one JSON line. `value` is tokens/s where a token is a pre-routing
+token of the GPU's share (the EP-64 share stands for 2,048 tokens per step).
+Also reports the dominant kernel's roofline (per-kernel durations from HIP
+events recorded by the library on its own stream) and the CPU oracle timed on
+a bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import glob
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+
+WORKLOAD_TEXT = {
+    "ep64_share": "EP-64 one-GPU share: 16,384 routed rows (2,048 tokens x 64 ranks x top-8 / 256 experts x 4), "
+                  "4 local SwiGLU experts, H=7168, I=2048, Zipf(1.2) loads 8658/3769/2317/1640, BF16, "
+                  "ring 256 MiB, mini-batch 512",
+    "full_layer": "single-GPU full layer: T=2048, top-8 of 256 SwiGLU experts, H=7168, I=2048, BF16",
+    "stream": "fine-grained streaming share: 8 x 20,480 rows, 8 experts, H=4096, I=1024, Dirichlet(0.3), "
+              "ring 128 MiB",
+    "tiny": "tiny: T=64, H=128, I=64, E=8, top-2",
+}
+
+
+def flops_per_row(H, I):
+    """Algorithmic flops per routed row, per kernel (recompute and padding not counted)."""
+    return dict(gateup=4 * H * I, down=2 * H * I, dA=2 * H * I, dX=4 * H * I,
+                wgrad_gate_up=4 * H * I, wgrad_down=2 * H * I)
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "mixture_experts_layer_table_amd", "csrc", "*"))):
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` from the committed PMC summary, or None when
+    the summary is missing or the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    m = re.search(r"```json\n(.*?)\n```", open(path).read(), re.S)
+    if not m:
+        return None
+    d = json.loads(m.group(1))
+    if d.get("source_digest") != source_digest():
+        return None
+    k = d.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(inp, tokens_per_step, seconds):
+    """The oracle as it stands, on a bounded sample of routed rows of the same
+    workload: forward and backward of each sampled row, extrapolated to the step."""
+    import numpy as np
+    from oracle import layer as L
+    try:
+        from threadpoolctl import threadpool_info
+        cores = sum(i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas") or 1
+    except Exception:  # pragma: no cover
+        cores = 1
+    cfg = inp.cfg
+    f = L.bf16_bits_to_f64
+    flat = inp.topk_ids.reshape(-1)
+    wflat = inp.topk_w.reshape(-1).astype(np.float64)
+    done, busy, chunk = 0, 0.0, 64
+    for e in range(cfg.E):                       # every row costs the same: any rows are a fair sample
+        rows_e = np.nonzero(flat == e)[0]
+        if rows_e.size == 0:
+            continue
+        Wg, Wu, Wd = f(inp.w_gate[e]), f(inp.w_up[e]), f(inp.w_down[e])   # decoded once, untimed
+        for c0 in range(0, rows_e.size, chunk):
+            rows = rows_e[c0: c0 + chunk]
+            tok = rows // cfg.k
+            t = time.perf_counter()
+            xe, dye = f(inp.x[tok]), f(inp.dy[tok])
+            L.expert_forward(xe, Wg, Wu, Wd)
+            L.expert_backward(xe, dye, wflat[rows][:, None], Wg, Wu, Wd)
+            busy += time.perf_counter() - t
+            done += rows.size
+            if busy >= seconds:
+                break
+        if busy >= seconds:
+            break
+    el = busy
+    step_s = el * cfg.R / max(done, 1)
+    return dict(value=tokens_per_step / step_s, unit="tokens/s", cores=int(cores), kind="oracle",
+                sample=f"{done} of {cfg.R} routed rows (forward + backward, fp64 numpy) in {el:.1f} s, "
+                       f"extrapolated linearly to the step")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=40)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="ep64_share", choices=list(WORKLOAD_TEXT))
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU's share of the layer; --gpus {args.gpus} "
+              f"(WORLD_SIZE={world}) is not supported: run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import mixture_experts_layer_table_amd as mok
+    import synth
+
+    cfg = synth.CONFIGS[args.workload]
+    dev = "cuda:0"
+    inp = synth.make_inputs(cfg)
+
+    def bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    ids = torch.from_numpy(inp.topk_ids).to(dev)
+    tw = torch.from_numpy(inp.topk_w).to(dev)
+    x, dy = bf16(inp.x), bf16(inp.dy)
+    wg, wu, wd = bf16(inp.w_gate), bf16(inp.w_up), bf16(inp.w_down)
+    weights = mok.weights_bf16(wg, wu, wd)
+    config = mok.MoKConfig(minibatch_rows=cfg.minibatch_rows, macrobatch_tokens=cfg.macrobatch_tokens,
+                           ring_bytes=cfg.ring_bytes)
+    ws = mok.get_workspace(config, device=dev, num_local_tokens=cfg.T, hidden_size=cfg.H,
+                           intermediate_size=cfg.I, num_experts=cfg.E, topk=cfg.k)
+    sched = torch.empty(ws.schedule_bytes, dtype=torch.uint8, device=dev)
+    ctx = torch.empty(ws.fwd_ctx_bytes, dtype=torch.uint8, device=dev)
+    out = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device=dev)
+    grads = dict(dx=torch.empty_like(x), dw_gate=torch.empty_like(wg), dw_up=torch.empty_like(wu),
+                 dw_down=torch.empty_like(wd), dtopk_w=torch.empty_like(tw))
+
+    def step():
+        mok.build_schedule(ws, ids, sched)
+        mok.forward(ws, sched, x, tw, weights, out=out, fwd_ctx=ctx)
+        mok.backward(ws, sched, ctx, x, tw, weights, dy, grads=grads)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    assert int(sched[:4].cpu().numpy().view(np.uint32)[0]) == 0, "schedule status word set"
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = e0.elapsed_time(e1)
+    ms_per_step = max(gpu_ms, wall * 1e3) / args.steps
+
+    # per-kernel durations: HIP events recorded by the library around each launch
+    nprof = min(args.steps, 10)
+    mok._check(mok.mok_kernel_timing_enable(1), "timing")
+    for _ in range(nprof):
+        step()
+    torch.cuda.synchronize()
+    ktimes = mok.kernel_times()
+    R, H, I = cfg.R, cfg.H, cfg.I
+    fpr = flops_per_row(H, I)
+    kernels = {}
+    for name, (launches, total_ms, max_ms) in ktimes.items():
+        avg = total_ms / launches
+        entry = dict(launches_per_step=launches / nprof, avg_ms=round(avg, 5), ms_per_step=round(total_ms / nprof, 4))
+        if name in fpr:
+            fl = fpr[name] * R * nprof / launches
+            entry["tflops"] = round(fl / (avg * 1e-3) / 1e12, 1)
+        if name in ("gather", "gather_dy"):
+            by = (2 * cfg.T * H + 2 * R * H + 4 * R) * nprof / launches   # unique reads + writes
+            entry["gbs"] = round(by / (avg * 1e-3) / 1e9, 1)
+        kernels[name] = entry
+    dominant = max((n for n in kernels if n in fpr), key=lambda n: kernels[n]["ms_per_step"])
+    dk = kernels[dominant]
+    ach = dk["tflops"]
+    roofline = dict(bound="mfma", kernel=dominant, achieved=ach, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                    frac=round(ach / PEAK_BF16_TFLOPS, 4),
+                    traffic=read_traffic(args.workload, dominant),
+                    flops_per_launch=fpr[dominant] * R * nprof / ktimes[dominant][0],
+                    avg_launch_ms=dk["avg_ms"])
+
+    total_flops = 18 * R * H * I
+    tokens = cfg.tokens_per_step
+    value = tokens / (ms_per_step * 1e-3)
+    sched_ms = kernels.get("schedule", {}).get("ms_per_step", 0.0)
+    res = dict(
+        metric="MoE layer fwd+bwd tokens/s on 1 GPU; grouped-GEMM MFMA util % of peak",
+        value=round(value, 1), unit="tokens/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
+        ms_per_step=round(ms_per_step, 4), higher_is_better=True, scaling="weak", vs_baseline=None,
+        dtype="bf16", data="synthetic",
+        config=dict(workload=f"{args.workload}: {WORKLOAD_TEXT[args.workload]}", T=cfg.T, H=H, I=I, E=cfg.E,
+                    k=cfg.k, routed_rows=R, tokens_per_step=tokens, minibatch_rows=cfg.minibatch_rows,
+                    macrobatch_tokens=cfg.macrobatch_tokens, ring_bytes=cfg.ring_bytes),
+        rows_per_s=round(R / (ms_per_step * 1e-3), 1),
+        tflops=round(total_flops / (ms_per_step * 1e-3) / 1e12, 1),
+        mfma_util=round(total_flops / (ms_per_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        schedule_share=round(sched_ms / ms_per_step, 4) if sched_ms else None,
+        roofline=roofline, kernels=kernels, source_digest=source_digest(),
+        device=torch.cuda.get_device_name(0),
+    )
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(inp, tokens, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

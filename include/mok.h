@@ -220,6 +220,27 @@ mok_status mok_mxfp8_quantize(const void *src, int64_t batch, int64_t rows, int6
                               int32_t src_is_k_by_rows, uint8_t *elems, uint8_t *scales,
                               void *stream);
 
+/*
+ * Measurement aid, not part of the layer: per-kernel durations for tools such
+ * as benchmarks. While enabled, every kernel launch of the library is
+ * bracketed by two HIP events recorded on the launch's own stream (the
+ * schedule builder's launches count as one "schedule" entry).
+ * mok_kernel_timing_enable(1) discards earlier records and starts recording;
+ * mok_kernel_timing_enable(0) discards records and stops. mok_kernel_timing_read
+ * waits for the recorded events, writes up to `capacity` per-kernel sums in
+ * first-launch order, sets *count to the number of distinct kernels, and
+ * discards the records. Off by default; not meant for production loops.
+ */
+typedef struct mok_kernel_stat {
+    char name[32];
+    int64_t launches;
+    double total_ms;
+    double max_ms;
+} mok_kernel_stat;
+
+mok_status mok_kernel_timing_enable(int32_t enable);
+mok_status mok_kernel_timing_read(mok_kernel_stat *stats, int32_t capacity, int32_t *count);
+
 /* Static string naming a status code. */
 const char *mok_status_string(mok_status status);
 

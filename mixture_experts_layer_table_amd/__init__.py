@@ -3,7 +3,7 @@
 Argument marshalling only: every step of the layer runs in the HIP kernels of
 ``libmok.so``; PyTorch provides device memory and the stream. Importing this
 package raises if the library has not been built
-(``python -m mixture_experts_layer_table_amd.build``).
+(``python mixture_experts_layer_table_amd/build.py``).
 
 Two levels, after the pages' ops / functional split ("Mixture-of-Kittens (MoK)"
 project summary, Functional API and Key-concepts table):
@@ -25,7 +25,7 @@ __version__ = "0.1.0"
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmok.so")
 if not os.path.exists(_LIB_PATH):
     raise ImportError(f"{_LIB_PATH} is missing: build it with "
-                      "`python -m mixture_experts_layer_table_amd.build` (there is no fallback)")
+                      "`python mixture_experts_layer_table_amd/build.py` (there is no fallback)")
 _lib = ctypes.CDLL(_LIB_PATH)
 
 MOK_OK, MOK_ERROR_INVALID_VALUE, MOK_ERROR_UNSUPPORTED, MOK_ERROR_BUFFER_TOO_SMALL, \
@@ -36,7 +36,7 @@ MOK_DEBUG_IDENTITY_EXPERT = 1
 
 EXPORTS = ("mok_config_default", "mok_query_sizes", "mok_schedule_layout_query",
            "mok_build_schedule", "mok_forward", "mok_backward", "mok_mxfp8_quantize",
-           "mok_status_string")
+           "mok_status_string", "mok_kernel_timing_enable", "mok_kernel_timing_read")
 
 
 class mok_config(ctypes.Structure):
@@ -55,6 +55,11 @@ class mok_weights(ctypes.Structure):
                 ("gate_elems", ctypes.c_void_p), ("gate_scales", ctypes.c_void_p),
                 ("up_elems", ctypes.c_void_p), ("up_scales", ctypes.c_void_p),
                 ("down_elems", ctypes.c_void_p), ("down_scales", ctypes.c_void_p)]
+
+
+class mok_kernel_stat(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 32), ("launches", ctypes.c_int64), ("total_ms", ctypes.c_double),
+                ("max_ms", ctypes.c_double)]
 
 
 class mok_schedule_layout(ctypes.Structure):
@@ -80,6 +85,8 @@ _sigs = {
                      _P, _P],
     "mok_mxfp8_quantize": [_P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
                            _P, _P, _P],
+    "mok_kernel_timing_enable": [ctypes.c_int32],
+    "mok_kernel_timing_read": [ctypes.POINTER(mok_kernel_stat), ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)],
 }
 for _name, _args in _sigs.items():
     _f = getattr(_lib, _name)
@@ -138,6 +145,26 @@ def mok_backward(cfg, shape, schedule, workspace, workspace_bytes, x, topk_w, we
 
 def mok_mxfp8_quantize(src, batch, rows, K, src_is_k_by_rows, elems, scales, stream):
     return _lib.mok_mxfp8_quantize(src, batch, rows, K, src_is_k_by_rows, elems, scales, stream)
+
+
+def mok_kernel_timing_enable(enable):
+    return _lib.mok_kernel_timing_enable(enable)
+
+
+def mok_kernel_timing_read(stats, capacity, count):
+    return _lib.mok_kernel_timing_read(stats, capacity, count)
+
+
+def kernel_times(enable_after: bool = False):
+    """Read (and clear) the per-kernel timing records: {name: (launches, total_ms, max_ms)}."""
+    cap = 64
+    arr = (mok_kernel_stat * cap)()
+    n = ctypes.c_int32()
+    _check(mok_kernel_timing_read(arr, cap, ctypes.byref(n)), "mok_kernel_timing_read")
+    out = {arr[i].name.decode(): (arr[i].launches, arr[i].total_ms, arr[i].max_ms) for i in range(min(n.value, cap))}
+    if not enable_after:
+        _check(mok_kernel_timing_enable(0), "mok_kernel_timing_enable")
+    return out
 
 
 # ----------------------------------------------------------------------------- functional layer

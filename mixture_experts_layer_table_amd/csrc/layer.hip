@@ -23,6 +23,7 @@
 
 #include "gemm.h"
 #include "kernels.h"
+#include "timing.h"
 #include "views.h"
 
 namespace mok {
@@ -638,7 +639,7 @@ __global__ __launch_bounds__(256) void reduce_router_grad(SchedView v, int S, co
 // ----------------------------------------------------------------------------- host side
 
 template <class P>
-hipError_t launch_gemm(dim3 grid, const typename P::Args &args, hipStream_t st) {
+hipError_t launch_gemm(const char *name, dim3 grid, const typename P::Args &args, hipStream_t st) {
     using C = typename P::C;
     static bool attr_set = false;
     if (!attr_set) {
@@ -648,6 +649,7 @@ hipError_t launch_gemm(dim3 grid, const typename P::Args &args, hipStream_t st) 
         attr_set = true;
     }
     if (grid.x == 0 || grid.y == 0 || grid.z == 0) return hipSuccess;
+    KernelTimer tm(name, st);
     gemm_kernel<P><<<grid, C::NT, C::LDS_BYTES, st>>>(args);
     return hipGetLastError();
 }
@@ -716,22 +718,27 @@ mok_status launch_forward(const Plan &p, const void *schedule, void *workspace, 
     hipError_t err = hipSuccess;
     for (const Round r : make_rounds(p, false)) {
         const dim3 sgrid((unsigned)ceil_div(p.MB, kRowsPerBlock), (unsigned)(r.g1 - r.g0));
-        gather_rows<<<sgrid, 256, 0, st>>>(v, r.g0, p.n_slots, p.MB, p.H, p.k, x, ring);
+        {
+            KernelTimer tm("gather", st);
+            gather_rows<<<sgrid, 256, 0, st>>>(v, r.g0, p.n_slots, p.MB, p.H, p.k, x, ring);
+        }
         if (identity) {
+            KernelTimer tm("identity", st);
             identity_rows<<<sgrid, 256, 0, st>>>(v, r.g0, p.n_slots, p.MB, p.H, p.k, (int)p.MT, p.nb_full, topk_w,
                                                  ring, out, stage);
         } else {
             const unsigned mt = (unsigned)mtile_bound(p, r);
             GateUpArgs ga{v, r.g0, r.g1, p.n_slots, p.MB, p.H, p.I, ring,
                           static_cast<const uint16_t *>(w.w_gate), static_cast<const uint16_t *>(w.w_up), h, aring};
-            if ((err = launch_gemm<GateUp<CfgA>>(dim3(p.I / (CfgA::BN / 2), mt), ga, st)) != hipSuccess) break;
+            if ((err = launch_gemm<GateUp<CfgA>>("gateup", dim3(p.I / (CfgA::BN / 2), mt), ga, st)) != hipSuccess) break;
             DownArgs da{v, r.g0, r.g1, p.n_slots, p.MB, p.H, p.I, p.k, (int)p.MT, p.nb_full, aring,
                         static_cast<const uint16_t *>(w.w_down), topk_w, out, stage};
-            if ((err = launch_gemm<Down<CfgA>>(dim3((unsigned)ceil_div(p.H, CfgA::BN), mt), da, st)) != hipSuccess)
+            if ((err = launch_gemm<Down<CfgA>>("down", dim3((unsigned)ceil_div(p.H, CfgA::BN), mt), da, st)) != hipSuccess)
                 break;
         }
         if (p.k > 1 && (r.g1 == p.G || r.g1 == first_minibatch(p, macro_of_minibatch(p, r.g0) + 1))) {
             const Macro mc = macro_info(p, macro_of_minibatch(p, r.g0));
+            KernelTimer tm("combine", st);
             combine_rows<<<(unsigned)ceil_div(mc.t1 - mc.t0, kRowsPerBlock), 256, 0, st>>>(
                 v, mc.t0, mc.t1, p.H, p.k, mc.base, topk_w, true, stage, out);
         }
@@ -760,32 +767,38 @@ mok_status launch_backward(const Plan &p, const void *schedule, void *workspace,
     if (p.R > 0) {
         for (const Round r : make_rounds(p, true)) {
             const dim3 sgrid((unsigned)ceil_div(p.MB, kRowsPerBlock), (unsigned)(r.g1 - r.g0));
-            gather_rows<<<sgrid, 256, 0, st>>>(v, r.g0, p.n_slots, p.MB, p.H, p.k, dy, ring);
+            {
+                KernelTimer tm("gather_dy", st);
+                gather_rows<<<sgrid, 256, 0, st>>>(v, r.g0, p.n_slots, p.MB, p.H, p.k, dy, ring);
+            }
             const unsigned mt = (unsigned)mtile_bound(p, r);
             DAArgs aa{v, r.g0, r.g1, p.n_slots, p.MB, p.H, p.I, p.dg_slices, ring, wd, h, topk_w, dh, ga, dgp};
-            if ((err = launch_gemm<DA<CfgA>>(dim3((unsigned)ceil_div(p.I, CfgA::BN), mt), aa, st)) != hipSuccess)
+            if ((err = launch_gemm<DA<CfgA>>("dA", dim3((unsigned)ceil_div(p.I, CfgA::BN), mt), aa, st)) != hipSuccess)
                 break;
             DXArgs xa{v, r.g0, r.g1, p.n_slots, p.H, p.I, p.k, (int)p.MT, p.nb_full, dh, wg, wu, dx, stage};
-            if ((err = launch_gemm<DX<CfgA>>(dim3((unsigned)ceil_div(p.H, CfgA::BN), mt), xa, st)) != hipSuccess)
+            if ((err = launch_gemm<DX<CfgA>>("dX", dim3((unsigned)ceil_div(p.H, CfgA::BN), mt), xa, st)) != hipSuccess)
                 break;
             if (p.k > 1 && r.g0 == first_minibatch(p, macro_of_minibatch(p, r.g0))) {
                 const Macro mc = macro_info(p, macro_of_minibatch(p, r.g0));
+                KernelTimer tm("combine_dx", st);
                 combine_rows<<<(unsigned)ceil_div(mc.t1 - mc.t0, kRowsPerBlock), 256, 0, st>>>(
                     v, mc.t0, mc.t1, p.H, p.k, mc.base, topk_w, false, stage, dx);
             }
         }
-        if (err == hipSuccess)
+        if (err == hipSuccess) {
+            KernelTimer tm("router_grad", st);
             reduce_router_grad<<<(unsigned)ceil_div(p.R, 256), 256, 0, st>>>(v, p.dg_slices, dgp, dtopk_w);
+        }
     }
     if (err == hipSuccess) {
         WGUArgs gu{v, p.H, p.I, x, dh, dw_gate, dw_up};
         err = launch_gemm<WGU<CfgA>>(
-            dim3((unsigned)ceil_div(2 * p.I, CfgA::BN), (unsigned)ceil_div(p.H, CfgA::BM), (unsigned)p.E), gu, st);
+            "wgrad_gate_up",            dim3((unsigned)ceil_div(2 * p.I, CfgA::BN), (unsigned)ceil_div(p.H, CfgA::BM), (unsigned)p.E), gu, st);
     }
     if (err == hipSuccess) {
         WDArgs wda{v, p.H, p.I, ga, dy, dw_down};
         err = launch_gemm<WD<CfgA>>(
-            dim3((unsigned)ceil_div(p.H, CfgA::BN), (unsigned)ceil_div(p.I, CfgA::BM), (unsigned)p.E), wda, st);
+            "wgrad_down",            dim3((unsigned)ceil_div(p.H, CfgA::BN), (unsigned)ceil_div(p.I, CfgA::BM), (unsigned)p.E), wda, st);
     }
     if (err == hipSuccess) err = hipGetLastError();
     return err == hipSuccess ? MOK_OK : MOK_ERROR_LAUNCH_FAILED;

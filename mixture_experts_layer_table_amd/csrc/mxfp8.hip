@@ -13,6 +13,7 @@
 //                sign kept.
 #include "common.h"
 #include "kernels.h"
+#include "timing.h"
 
 namespace mok {
 
@@ -114,6 +115,7 @@ mok_status launch_mxfp8_quantize(const uint16_t *src, int64_t batch, int64_t row
     const int64_t n = batch * rows * (K / 32);
     if (n == 0) return MOK_OK;
     const int64_t blocks = (n + 255) / 256;
+    KernelTimer tm("mxfp8_quantize", st);
     mxfp8_quantize_kernel<<<(unsigned)blocks, 256, 0, st>>>(src, batch, rows, K, src_is_k_by_rows ? 1 : 0, elems,
                                                             scales);
     return hipGetLastError() == hipSuccess ? MOK_OK : MOK_ERROR_LAUNCH_FAILED;

@@ -9,6 +9,7 @@
 // and its position in canonical (expert, f) order is offsets[e] + rank_e(f).
 // Only integer atomics are used (order-independent counts).
 #include "kernels.h"
+#include "timing.h"
 #include "views.h"
 
 namespace mok {
@@ -253,6 +254,7 @@ __global__ __launch_bounds__(kThreads) void sched_scatter(const int32_t *__restr
 mok_status launch_build_schedule(const Plan &p, const int32_t *ids, void *schedule, hipStream_t st) {
     SchedView v = make_sched_view(p, schedule);
     const size_t hist_lds = sizeof(int) * (size_t)p.E;
+    KernelTimer tm("schedule", st);
     sched_init<<<1, kThreads, 0, st>>>(v);
     if (p.nchunks > 0) {
         sched_hist<<<p.nchunks, kThreads, hist_lds, st>>>(ids, v);
