@@ -241,6 +241,10 @@ typedef struct mok_kernel_stat {
 mok_status mok_kernel_timing_enable(int32_t enable);
 mok_status mok_kernel_timing_read(mok_kernel_stat *stats, int32_t capacity, int32_t *count);
 
+/* Text of the calling thread's last HIP error reported as
+   MOK_ERROR_LAUNCH_FAILED ("" if none); valid until the thread's next call. */
+const char *mok_last_error(void);
+
 /* Static string naming a status code. */
 const char *mok_status_string(mok_status status);
 

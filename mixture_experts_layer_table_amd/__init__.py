@@ -22,6 +22,11 @@ import os
 
 __version__ = "0.1.0"
 
+# Device memory and streams come from PyTorch, so the library must run on the
+# HIP runtime torch has loaded: import torch first, so that libmok's dependency
+# on libamdhip64.so.7 resolves to that same copy instead of a second runtime.
+import torch  # noqa: E402,F401
+
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmok.so")
 if not os.path.exists(_LIB_PATH):
     raise ImportError(f"{_LIB_PATH} is missing: build it with "
@@ -36,7 +41,7 @@ MOK_DEBUG_IDENTITY_EXPERT = 1
 
 EXPORTS = ("mok_config_default", "mok_query_sizes", "mok_schedule_layout_query",
            "mok_build_schedule", "mok_forward", "mok_backward", "mok_mxfp8_quantize",
-           "mok_status_string", "mok_kernel_timing_enable", "mok_kernel_timing_read")
+           "mok_status_string", "mok_kernel_timing_enable", "mok_kernel_timing_read", "mok_last_error")
 
 
 class mok_config(ctypes.Structure):
@@ -94,11 +99,14 @@ for _name, _args in _sigs.items():
     _f.restype = ctypes.c_int
 _lib.mok_status_string.argtypes = [ctypes.c_int]
 _lib.mok_status_string.restype = ctypes.c_char_p
+_lib.mok_last_error.argtypes = []
+_lib.mok_last_error.restype = ctypes.c_char_p
 
 
 class MokError(RuntimeError):
     def __init__(self, status: int, where: str):
-        super().__init__(f"{where}: {mok_status_string(status)}")
+        detail = mok_last_error() if status == MOK_ERROR_LAUNCH_FAILED else ""
+        super().__init__(f"{where}: {mok_status_string(status)}" + (f" ({detail})" if detail else ""))
         self.status = status
 
 
@@ -109,6 +117,10 @@ def _check(status: int, where: str):
 
 def mok_status_string(status: int) -> str:
     return _lib.mok_status_string(status).decode()
+
+
+def mok_last_error() -> str:
+    return _lib.mok_last_error().decode()
 
 
 # ----------------------------------------------------------------------------- raw entry points

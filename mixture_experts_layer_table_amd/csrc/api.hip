@@ -68,6 +68,7 @@ mok_status mok_build_schedule(const mok_config *cfg, const mok_shape *shape, con
     if (s != MOK_OK) return s;
     if (!dev_ok(schedule) || (p.R > 0 && !dev_ok(topk_ids))) return MOK_ERROR_INVALID_VALUE;
     if (schedule_bytes < p.s_total) return MOK_ERROR_BUFFER_TOO_SMALL;
+    (void)hipGetLastError();   // drop an earlier, unrelated error of this thread
     return launch_build_schedule(p, topk_ids, schedule, static_cast<hipStream_t>(stream));
 }
 
@@ -93,6 +94,7 @@ mok_status mok_forward(const mok_config *cfg, const mok_shape *shape, const void
     if (!dev_ok(schedule) || !dev_ok(workspace) || !dev_ok(fwd_ctx)) return MOK_ERROR_INVALID_VALUE;
     if (p.R > 0 && (!dev_ok(x) || !dev_ok(topk_w) || !dev_ok(out))) return MOK_ERROR_INVALID_VALUE;
     if (workspace_bytes < p.w_total || fwd_ctx_bytes < p.c_total) return MOK_ERROR_BUFFER_TOO_SMALL;
+    (void)hipGetLastError();
     return launch_forward(p, schedule, workspace, static_cast<const uint16_t *>(x), topk_w, *w,
                           static_cast<uint16_t *>(out), fwd_ctx, static_cast<hipStream_t>(stream));
 }
@@ -111,6 +113,7 @@ mok_status mok_backward(const mok_config *cfg, const mok_shape *shape, const voi
     if (p.R > 0 && (!dev_ok(x) || !dev_ok(topk_w) || !dev_ok(dy) || !dev_ok(dx) || !dev_ok(dtopk_w)))
         return MOK_ERROR_INVALID_VALUE;
     if (workspace_bytes < p.w_total || fwd_ctx_bytes < p.c_total) return MOK_ERROR_BUFFER_TOO_SMALL;
+    (void)hipGetLastError();
     return launch_backward(p, schedule, workspace, static_cast<const uint16_t *>(x), topk_w, *w, fwd_ctx,
                            static_cast<const uint16_t *>(dy), static_cast<uint16_t *>(dx),
                            static_cast<uint16_t *>(dw_gate), static_cast<uint16_t *>(dw_up),
@@ -123,6 +126,7 @@ mok_status mok_mxfp8_quantize(const void *src, int64_t batch, int64_t rows, int6
     if (src_is_k_by_rows != 0 && src_is_k_by_rows != 1) return MOK_ERROR_INVALID_VALUE;
     if (batch * rows * K == 0) return MOK_OK;
     if (!dev_ok(src) || !dev_ok(elems) || !scales) return MOK_ERROR_INVALID_VALUE;
+    (void)hipGetLastError();
     return launch_mxfp8_quantize(static_cast<const uint16_t *>(src), batch, rows, K, src_is_k_by_rows == 1, elems,
                                  scales, static_cast<hipStream_t>(stream));
 }

@@ -6,6 +6,10 @@
 
 namespace mok {
 
+// Records `err` (with the call site) as the calling thread's last error when it
+// is not hipSuccess, and maps it to a status.
+mok_status check_hip(hipError_t err, const char *where);
+
 mok_status launch_build_schedule(const Plan &p, const int32_t *ids, void *schedule, hipStream_t st);
 
 mok_status launch_forward(const Plan &p, const void *schedule, void *workspace, const uint16_t *x,

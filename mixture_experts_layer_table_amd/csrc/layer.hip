@@ -29,7 +29,7 @@
 namespace mok {
 namespace {
 
-using CfgA = TileCfg<128, 128, 64, 2, 2>;
+using CfgA = TileCfg<256, 256, 64, 2, 2>;
 
 // ----------------------------------------------------------------------------- tile decode
 
@@ -72,10 +72,9 @@ struct GateUp {
     using C = Cfg;
     using Args = GateUpArgs;
     RowTile<C, C::BM> xt;
-    TransTile<C, C::BN> wt;
+    TransTileSplit<C, C::BN> wt;
     SegTile t;
     int i0, nk, H, I, MB;
-    const uint16_t *wg, *wu;
     uint16_t *h, *aring;
 
     __device__ bool setup(const Args &a) {
@@ -85,25 +84,17 @@ struct GateUp {
         MB = a.MB;
         i0 = blockIdx.x * (C::BN / 2);
         const int64_t row0 = (int64_t)t.slot * MB + t.rowoff;
-        const int rows = t.mt.rows;
-        const uint16_t *ring = a.ring;
-        const int Hl = H;
-        xt.init([&](int r) -> const uint16_t * { return r < rows ? ring + (row0 + r) * Hl : nullptr; });
-        wg = a.wg + (int64_t)t.mt.e * H * I;
-        wu = a.wu + (int64_t)t.mt.e * H * I;
+        xt.init(a.ring + row0 * H, H, t.mt.rows);
+        const int64_t eoff = (int64_t)t.mt.e * H * I;
+        wt.init(a.wg + eoff + i0, a.wu + eoff + i0, I, H, I - i0);
         h = a.h;
         aring = a.aring;
         nk = H / C::BK;
         return true;
     }
     __device__ void load(int kt) {
-        const int k0 = kt * C::BK;
-        xt.load(k0);
-        wt.load(
-            [&](int k, int c) -> const uint16_t * {
-                return c < C::BN / 2 ? wg + (int64_t)k * I + i0 + c : wu + (int64_t)k * I + i0 + (c - C::BN / 2);
-            },
-            k0);
+        xt.load(kt * C::BK);
+        wt.load(kt * C::BK);
     }
     __device__ void store(uint16_t *s) const {
         xt.store(s);
@@ -127,6 +118,7 @@ struct GateUp {
 #pragma unroll
                 for (int g4 = 0; g4 < 4; ++g4) {
                     const int i = i0 + wn * (C::WN / 2) + fn * 32 + g4 * 8 + (lane >> 5) * 4;
+                    if (i >= I) continue;
                     float hg[4], hu[4], av[4];
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
@@ -162,7 +154,6 @@ struct Down {
     TransTile<C, C::BN> wt;
     SegTile t;
     int n0, nk, H;
-    const uint16_t *wd;
     Args a;
 
     __device__ bool setup(const Args &args) {
@@ -171,21 +162,14 @@ struct Down {
         H = args.H;
         n0 = blockIdx.x * C::BN;
         const int64_t row0 = (int64_t)t.slot * args.MB + t.rowoff;
-        const int rows = t.mt.rows, I = args.I;
-        const uint16_t *ar = args.aring;
-        xt.init([&](int r) -> const uint16_t * { return r < rows ? ar + (row0 + r) * I : nullptr; });
-        wd = args.wd + (int64_t)t.mt.e * args.I * H;
+        xt.init(args.aring + row0 * args.I, args.I, t.mt.rows);
+        wt.init(args.wd + (int64_t)t.mt.e * args.I * H + n0, H, args.I, H - n0);
         nk = args.I / C::BK;
         return true;
     }
     __device__ void load(int kt) {
-        const int k0 = kt * C::BK;
-        xt.load(k0);
-        wt.load(
-            [&](int k, int c) -> const uint16_t * {
-                return n0 + c < H ? wd + (int64_t)k * H + n0 + c : nullptr;
-            },
-            k0);
+        xt.load(kt * C::BK);
+        wt.load(kt * C::BK);
     }
     __device__ void store(uint16_t *s) const {
         xt.store(s);
@@ -255,13 +239,10 @@ struct DA {
         if (!decode_seg_tile(args.v, args.g0, args.g1, args.n_slots, t)) return false;
         a = args;
         i0 = blockIdx.x * C::BN;
-        const int H = args.H, I = args.I, rows = t.mt.rows;
+        const int H = args.H, I = args.I;
         const int64_t row0 = (int64_t)t.slot * args.MB + t.rowoff;
-        const uint16_t *ring = args.ring;
-        xt.init([&](int r) -> const uint16_t * { return r < rows ? ring + (row0 + r) * H : nullptr; });
-        const uint16_t *wd = args.wd + (int64_t)t.mt.e * I * H;
-        const int i0l = i0;
-        wt.init([&](int r) -> const uint16_t * { return i0l + r < I ? wd + (int64_t)(i0l + r) * H : nullptr; });
+        xt.init(args.ring + row0 * H, H, t.mt.rows);
+        wt.init(args.wd + (int64_t)t.mt.e * I * H + (int64_t)i0 * H, H, min(C::BN, I - i0));
         nk = H / C::BK;
         return true;
     }
@@ -284,17 +265,18 @@ struct DA {
             const int m = wm * C::WM + fm * 32 + (lane & 31);
             const bool ok = m < t.mt.rows;
             const int q = t.mt.q0 + (ok ? m : 0);
+            const int64_t c = t.mt.c0 + (ok ? m : 0);   // dh and g*a rows are kept in canonical order
             const float gw = a.topk_w[a.v.perm[q]];
             const uint16_t *hrow = a.h + (int64_t)q * 2 * I;
-            uint16_t *dhrow = a.dh + (int64_t)q * 2 * I;
-            uint16_t *garow = a.ga + (int64_t)q * I;
+            uint16_t *dhrow = a.dh + c * 2 * I;
+            uint16_t *garow = a.ga + c * I;
             float dg = 0.0f;
 #pragma unroll
             for (int fn = 0; fn < C::FN; ++fn)
 #pragma unroll
                 for (int g4 = 0; g4 < 4; ++g4) {
                     const int i = i0 + wn * C::WN + fn * 32 + g4 * 8 + (lane >> 5) * 4;
-                    if (!slice_ok) continue;
+                    if (!slice_ok || i >= I) continue;
                     const uint2 hg2 = *reinterpret_cast<const uint2 *>(hrow + i);
                     const uint2 hu2 = *reinterpret_cast<const uint2 *>(hrow + I + i);
                     const uint32_t hgw[4] = {hg2.x & 0xFFFFu, hg2.x >> 16, hg2.y & 0xFFFFu, hg2.y >> 16};
@@ -346,7 +328,6 @@ struct DX {
     RowTile<C, C::BN> wt;
     SegTile t;
     int n0, nk, I;
-    ptrdiff_t delta;
     Args a;
 
     __device__ bool setup(const Args &args) {
@@ -354,21 +335,16 @@ struct DX {
         a = args;
         n0 = blockIdx.x * C::BN;
         I = args.I;
-        const int H = args.H, rows = t.mt.rows, Il = I;
-        const int64_t q0 = t.mt.q0;
-        const uint16_t *dh = args.dh;
-        xt.init([&](int r) -> const uint16_t * { return r < rows ? dh + (q0 + r) * 2 * Il : nullptr; });
-        const uint16_t *wg = args.wg + (int64_t)t.mt.e * H * I;
-        const uint16_t *wu = args.wu + (int64_t)t.mt.e * H * I;
-        delta = wu - wg;
-        const int n0l = n0;
-        wt.init([&](int r) -> const uint16_t * { return n0l + r < H ? wg + (int64_t)(n0l + r) * Il : nullptr; });
+        const int H = args.H;
+        xt.init(args.dh + (int64_t)t.mt.c0 * 2 * I, 2 * I, t.mt.rows);
+        const int64_t wo = (int64_t)t.mt.e * H * I + (int64_t)n0 * I;
+        wt.init(args.wg + wo, I, min(C::BN, H - n0), args.wu + wo, I);
         nk = 2 * I / C::BK;
         return true;
     }
     __device__ void load(int kt) {
         xt.load(kt * C::BK);
-        wt.load_split(kt * C::BK, I, delta);
+        wt.load(kt * C::BK);
     }
     __device__ void store(uint16_t *s) const {
         xt.store(s);
@@ -418,8 +394,8 @@ template <class Cfg>
 struct WGU {
     using C = Cfg;
     using Args = WGUArgs;
-    TransTile<C, C::BM> xt;
-    TransTile<C, C::BN> wt;
+    TransTileIdx<C, C::BM> xt;   // x rows of the expert's tokens, k = canonical row
+    TransTile<C, C::BN> wt;      // dh rows, stored in canonical order
     int e, h0, n0, ne, off, nk;
     Args a;
 
@@ -432,22 +408,14 @@ struct WGU {
         ne = args.v.counts[e];
         off = args.v.offsets[e];
         nk = (ne + C::BK - 1) / C::BK;
+        xt.init(args.v.ctok + off, ne, args.x, args.H, args.v.T, h0, args.H);
+        const int I2 = 2 * args.I;
+        wt.init(args.dh + (int64_t)off * I2 + n0, I2, ne, I2 - n0);
         return true;
     }
     __device__ void load(int kt) {
-        const int k0 = kt * C::BK;
-        const int H = a.H, I = a.I;
-        const int32_t *ctok = a.v.ctok + off, *canon = a.v.canon + off;
-        xt.load(
-            [&](int k, int c) -> const uint16_t * {
-                return (k < ne && h0 + c < H) ? a.x + (int64_t)ctok[k] * H + h0 + c : nullptr;
-            },
-            k0);
-        wt.load(
-            [&](int k, int c) -> const uint16_t * {
-                return (k < ne && n0 + c < 2 * I) ? a.dh + (int64_t)canon[k] * 2 * I + n0 + c : nullptr;
-            },
-            k0);
+        xt.load(kt * C::BK);
+        wt.load(kt * C::BK);
     }
     __device__ void store(uint16_t *s) const {
         xt.store(s);
@@ -488,8 +456,8 @@ template <class Cfg>
 struct WD {
     using C = Cfg;
     using Args = WDArgs;
-    TransTile<C, C::BM> xt;
-    TransTile<C, C::BN> wt;
+    TransTile<C, C::BM> xt;      // g*a rows, stored in canonical order
+    TransTileIdx<C, C::BN> wt;   // dy rows of the expert's tokens
     int e, i0, n0, ne, off, nk;
     Args a;
 
@@ -502,22 +470,13 @@ struct WD {
         ne = args.v.counts[e];
         off = args.v.offsets[e];
         nk = (ne + C::BK - 1) / C::BK;
+        wt.init(args.v.ctok + off, ne, args.dy, args.H, args.v.T, n0, args.H);
+        xt.init(args.ga + (int64_t)off * args.I + i0, args.I, ne, args.I - i0);
         return true;
     }
     __device__ void load(int kt) {
-        const int k0 = kt * C::BK;
-        const int H = a.H, I = a.I;
-        const int32_t *ctok = a.v.ctok + off, *canon = a.v.canon + off;
-        xt.load(
-            [&](int k, int c) -> const uint16_t * {
-                return (k < ne && i0 + c < I) ? a.ga + (int64_t)canon[k] * I + i0 + c : nullptr;
-            },
-            k0);
-        wt.load(
-            [&](int k, int c) -> const uint16_t * {
-                return (k < ne && n0 + c < H) ? a.dy + (int64_t)ctok[k] * H + n0 + c : nullptr;
-            },
-            k0);
+        xt.load(kt * C::BK);
+        wt.load(kt * C::BK);
     }
     __device__ void store(uint16_t *s) const {
         xt.store(s);
@@ -730,7 +689,9 @@ mok_status launch_forward(const Plan &p, const void *schedule, void *workspace, 
             const unsigned mt = (unsigned)mtile_bound(p, r);
             GateUpArgs ga{v, r.g0, r.g1, p.n_slots, p.MB, p.H, p.I, ring,
                           static_cast<const uint16_t *>(w.w_gate), static_cast<const uint16_t *>(w.w_up), h, aring};
-            if ((err = launch_gemm<GateUp<CfgA>>("gateup", dim3(p.I / (CfgA::BN / 2), mt), ga, st)) != hipSuccess) break;
+            if ((err = launch_gemm<GateUp<CfgA>>("gateup", dim3((unsigned)ceil_div(p.I, CfgA::BN / 2), mt), ga, st)) !=
+                hipSuccess)
+                break;
             DownArgs da{v, r.g0, r.g1, p.n_slots, p.MB, p.H, p.I, p.k, (int)p.MT, p.nb_full, aring,
                         static_cast<const uint16_t *>(w.w_down), topk_w, out, stage};
             if ((err = launch_gemm<Down<CfgA>>("down", dim3((unsigned)ceil_div(p.H, CfgA::BN), mt), da, st)) != hipSuccess)
@@ -744,7 +705,7 @@ mok_status launch_forward(const Plan &p, const void *schedule, void *workspace, 
         }
     }
     if (err == hipSuccess) err = hipGetLastError();
-    return err == hipSuccess ? MOK_OK : MOK_ERROR_LAUNCH_FAILED;
+    return check_hip(err, "mok_forward");
 }
 
 mok_status launch_backward(const Plan &p, const void *schedule, void *workspace, const uint16_t *x,
@@ -801,7 +762,7 @@ mok_status launch_backward(const Plan &p, const void *schedule, void *workspace,
             "wgrad_down",            dim3((unsigned)ceil_div(p.H, CfgA::BN), (unsigned)ceil_div(p.I, CfgA::BM), (unsigned)p.E), wda, st);
     }
     if (err == hipSuccess) err = hipGetLastError();
-    return err == hipSuccess ? MOK_OK : MOK_ERROR_LAUNCH_FAILED;
+    return check_hip(err, "mok_backward");
 }
 
 }  // namespace mok

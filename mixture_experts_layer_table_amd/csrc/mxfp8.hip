@@ -118,7 +118,7 @@ mok_status launch_mxfp8_quantize(const uint16_t *src, int64_t batch, int64_t row
     KernelTimer tm("mxfp8_quantize", st);
     mxfp8_quantize_kernel<<<(unsigned)blocks, 256, 0, st>>>(src, batch, rows, K, src_is_k_by_rows ? 1 : 0, elems,
                                                             scales);
-    return hipGetLastError() == hipSuccess ? MOK_OK : MOK_ERROR_LAUNCH_FAILED;
+    return check_hip(hipGetLastError(), "mok_mxfp8_quantize");
 }
 
 }  // namespace mok

@@ -89,7 +89,7 @@ mok_status make_plan(const mok_config *cfg, const mok_shape *shape, Plan *p) {
     q.s_bound = c.take(4 * (size_t)(q.NM + 1) * q.E);
     q.s_segfirst = c.take(4 * (size_t)(q.G + 1));
     q.s_mtfirst = c.take(4 * (size_t)(q.G + 1));
-    q.s_mtiles = c.take(16 * (size_t)q.max_mtiles);
+    q.s_mtiles = c.take(32 * (size_t)q.max_mtiles);
     q.s_total = c.off;
 
     Carver w;

@@ -203,8 +203,11 @@ __global__ __launch_bounds__(kTableThreads) void sched_table(SchedView v) {
             }
             ++s;
             if (!overflow) {
+                // canonical position of q = a: rows of e in earlier macro-batches come first
+                const int c_a = v.offsets[e] + v.bound[r.m * v.E + e] + (a - M[e]);
                 for (int j = 0; j * v.BM < len; ++j, ++t) {
-                    if (t < v.max_mtiles) v.mtiles[t] = MTile{a + j * v.BM, min(v.BM, len - j * v.BM), e, g};
+                    if (t < v.max_mtiles)
+                        v.mtiles[t] = MTile{a + j * v.BM, min(v.BM, len - j * v.BM), e, g, c_a + j * v.BM, 0, 0, 0};
                 }
             }
         }
@@ -263,7 +266,7 @@ mok_status launch_build_schedule(const Plan &p, const int32_t *ids, void *schedu
     }
     sched_table<<<1, kTableThreads, 0, st>>>(v);
     if (p.nchunks > 0) sched_scatter<<<p.nchunks, kThreads, 0, st>>>(ids, v);
-    return hipGetLastError() == hipSuccess ? MOK_OK : MOK_ERROR_LAUNCH_FAILED;
+    return check_hip(hipGetLastError(), "mok_build_schedule");
 }
 
 }  // namespace mok

@@ -1,7 +1,9 @@
 // Per-launch timing records (see timing.h) and their C-ABI readout.
 #include "timing.h"
+#include "kernels.h"
 
 #include <atomic>
+#include <cstdio>
 #include <cstring>
 #include <map>
 #include <mutex>
@@ -39,9 +41,22 @@ void timing_record(const char *name, hipEvent_t start, hipEvent_t stop) {
     g_recs.push_back(Rec{name, start, stop});
 }
 
+namespace {
+thread_local char g_last_error[256] = "";
+}
+
+mok_status check_hip(hipError_t err, const char *where) {
+    if (err == hipSuccess) return MOK_OK;
+    std::snprintf(g_last_error, sizeof(g_last_error), "%s: %s (%d)", where, hipGetErrorString(err), (int)err);
+    return MOK_ERROR_LAUNCH_FAILED;
+}
+
 }  // namespace mok
 
 extern "C" {
+
+const char *mok_last_error(void) { return mok::g_last_error; }
+
 
 mok_status mok_kernel_timing_enable(int32_t enable) {
     std::lock_guard<std::mutex> lk(mok::g_mu);

@@ -9,9 +9,10 @@
 namespace mok {
 
 // One m-tile of a segment GEMM: up to BM routed rows of one expert inside one
-// mini-batch, starting at processing position q0.
+// mini-batch, starting at processing position q0 and at position c0 of the
+// canonical (expert, routed row) order.
 struct MTile {
-    int32_t q0, rows, e, g;
+    int32_t q0, rows, e, g, c0, pad0, pad1, pad2;
 };
 
 struct SchedView {

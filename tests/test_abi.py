@@ -98,3 +98,10 @@ def test_null_and_misaligned_pointers_rejected_without_device_work():
         mok.MOK_ERROR_INVALID_VALUE
     assert mok.mok_mxfp8_quantize(None, 1, 1, 33, 0, None, None, None) == mok.MOK_ERROR_INVALID_VALUE
     assert mok.mok_mxfp8_quantize(None, 1, 1, 32, 2, None, None, None) == mok.MOK_ERROR_INVALID_VALUE
+
+
+def test_single_hip_runtime_in_process():
+    # the binding shares torch's HIP runtime: only one libamdhip64 is mapped
+    maps = open(f"/proc/{os.getpid()}/maps").read()
+    hip = {l.split()[-1] for l in maps.splitlines() if "libamdhip64" in l}
+    assert len(hip) == 1, hip
