@@ -2,286 +2,336 @@
 // fp32 accumulation on v_mfma_f32_32x32x16_bf16.
 //
 // The MFMA computes transposed 32x32 blocks of C: its A operand is a block of
-// W^T (rows = n), its B operand a block of X (columns = m). With that choice a
-// lane of the accumulator holds one row m of C and four consecutive columns n,
-// so epilogues store 8-byte runs along n and reduce along n inside a lane.
+// W^T (rows = n), its B operand a block of X (columns = m). A lane of the
+// accumulator then holds one row m of C and four consecutive columns n, so
+// epilogues store 8-byte runs along n and reduce along n inside a lane.
 //
-// Both operands are staged in LDS as [rows][BK] bf16 (k contiguous), double
-// buffered, with 16-byte chunks XOR-swizzled per row. Two loaders fill a stage:
-//   RowTile   — tile rows whose k-values are contiguous in memory (activations
-//               in processing order, W^T stored with k contiguous);
-//   TransTile — tile columns contiguous in memory along m or n, k strided
-//               (weights stored [K][N], token rows for the weight gradients):
-//               each thread loads an 8(k) x 8(col) block with 16-byte loads and
-//               transposes it in registers before writing LDS.
+// Data path, per workgroup tile BM x BN and K-step BK = 32:
+//  * global -> LDS with direct loads (buffer_load ... lds, 16 bytes per lane,
+//    lane l lands at the instruction's LDS base + 16*l): no register staging;
+//  * an NSTAGE-deep LDS ring: while the MFMAs consume stage kt, the loads of
+//    k-steps kt+1 .. kt+NSTAGE-1 are in flight;
+//  * two LDS tile layouts, one per operand kind:
+//      Row   — tile rows whose k-values are contiguous in memory (activations,
+//              W^T with k contiguous): [rows][32] bf16, 16-byte chunks swizzled;
+//              fragments read with ds_read_b128;
+//      Trans — tile columns contiguous in memory, k strided (weights stored
+//              [K][N], token rows of the weight gradients): [32][cols] bf16 in
+//              sub-tiles of 128 columns, chunks swizzled by k; fragments read
+//              with two ds_read_b64_tr_b16 (the LDS transpose read), which
+//              deliver 4 consecutive k of one column to each lane.
+//  * buffer loads past a tile's valid range return zeros (hardware range
+//    check), which masks ragged edges without branches.
 #pragma once
 #include "common.h"
 
 namespace mok {
 
-template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_>
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int NSTAGE_>
 struct TileCfg {
-    static constexpr int BM = BM_, BN = BN_, BK = BK_;
+    static constexpr int BM = BM_, BN = BN_, BK = 32;
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
-    static constexpr int NT = 64 * WAVES_M * WAVES_N;
+    static constexpr int NW = WAVES_M * WAVES_N;
+    static constexpr int NT = 64 * NW;
     static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
     static constexpr int FM = WM / 32, FN = WN / 32;
-    static constexpr int KCH = BK / 8;
-    static constexpr int STAGE = (BM + BN) * BK;             // bf16 elements per stage
-    static constexpr size_t LDS_BYTES = 2 * (size_t)STAGE * 2;
+    static constexpr int NSTAGE = NSTAGE_;
+    static constexpr int X_BYTES = BM * BK * 2;   // one stage of the X tile
+    static constexpr int W_BYTES = BN * BK * 2;
+    static constexpr int STAGE_BYTES = X_BYTES + W_BYTES;
+    static constexpr size_t LDS_BYTES = (size_t)NSTAGE * STAGE_BYTES;
     static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must hold whole 32x32 blocks");
-    static_assert(KCH == 8, "LDS swizzle assumes 8 chunks of 16 bytes per row");
+    static_assert(BM % 128 == 0 && BN % 128 == 0, "tiles are made of 128-wide sub-tiles");
+    static_assert(NSTAGE >= 2, "at least double buffered");
 };
 
-// chunk c of row r lives at chunk c ^ swz(r): conflict-free for 8 lanes reading
-// one chunk of 8 consecutive rows, writing 8 chunks of one row, or writing one
-// chunk of rows 8 apart (the transposing loader).
-__device__ __forceinline__ int lds_off(int r, int c, int BK) {
-    return r * BK + ((c ^ ((r ^ (r >> 3)) & 7)) << 3);
-}
+// ----------------------------------------------------------------------------- buffer loads
 
-// Raw buffer loads: base address and size in SGPRs, one 32-bit VGPR offset per
-// thread, plus a uniform scalar offset. Reads at or past `bytes` return zeros
-// (the hardware range check), which masks ragged tile edges without branches.
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-constexpr int kBufWord3 = 0x00020000;   // gfx9 buffer descriptor word 3: 32-bit data format
+// Buffer descriptor (SGPR quad): base address, size in bytes; word 3 selects
+// 32-bit data format, the gfx9 value for raw loads.
+typedef int rsrc_t __attribute__((ext_vector_type(4)));
+constexpr int kBufWord3 = 0x00020000;
+constexpr uint32_t kOutOfRange = 0x80000000u;    // a voffset past any buffer used here (all < 2 GiB)
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, kBufWord3);
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    rsrc_t d;
+    d[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    d[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xFFFFu));
+    d[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+    d[3] = kBufWord3;
+    return d;
 }
-__device__ __forceinline__ uint4 bload(rsrc_t r, uint32_t voff, uint32_t soff) {
-    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
-    return make_uint4(v[0], v[1], v[2], v[3]);
-}
-constexpr uint32_t kOutOfRange = 0x80000000u;   // a voffset past any buffer used here (all < 2 GiB)
 
-// Tile rows [0, nrows) of a row-major array (ld elements per row), k contiguous.
-// An optional second array supplies k >= ksplit (at k - ksplit).
+// 16 bytes per lane from r at voff + soff into LDS at `dst` + 16 * lane
+// (buffer_load_dwordx4 ... lds; M0 holds the LDS base). Issued as inline asm so
+// that the compiler does not track these LDS writes: ordering against LDS
+// reads is explicit (wait_vmcnt + lds_barrier in the kernel loop).
+__device__ __forceinline__ void load_lds16(rsrc_t r, uint32_t voff, uint32_t soff, uint32_t dst) {
+    asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+                 :
+                 : "v"(voff), "s"(r), "s"(soff), "s"(dst)
+                 : "memory", "m0");
+}
+
+// Four consecutive int32 at a uniform address, through the scalar cache
+// (s_load_dwordx4, counted by lgkmcnt rather than vmcnt). The result is not
+// ready until sload_wait() has been passed with the same registers.
+typedef int sgpr4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ sgpr4_t sload4(const int32_t *p) {
+    sgpr4_t v;
+    const uint64_t a = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+    const uint64_t u = ((uint64_t)hi << 32) | lo;
+    asm volatile("s_load_dwordx4 %0, %1, 0x0" : "=s"(v) : "s"(u) : "memory");
+    return v;
+}
+__device__ __forceinline__ void sload_wait(sgpr4_t &v) { asm volatile("s_waitcnt lgkmcnt(0)" : "+s"(v)); }
+
+// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Wave index as a provably uniform value (keeps descriptors and M0 in SGPRs).
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
+
+// Workgroup barrier without the release/acquire fences of __syncthreads():
+// those would wait for every outstanding direct-to-LDS load. Callers first
+// wait (vmcnt) for the loads whose data the barrier publishes; LDS writes by
+// those loads are complete once the counter has passed them.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// ----------------------------------------------------------------------------- LDS layouts (byte offsets)
+
+// Row layout: [rows][32] bf16, 64-byte rows of four 16-byte chunks; chunk c of
+// row r sits at c ^ ((r >> 1) & 3): 8 lanes reading one chunk of 8
+// consecutive rows hit 8 distinct 16-byte bank groups.
+__device__ __forceinline__ uint32_t row_off(int r, int c) {
+    return (uint32_t)(r * 64 + ((c ^ ((r >> 1) & 3)) << 4));
+}
+
+// Trans layout: sub-tiles of 128 columns, each [32 k][128] bf16 with 256-byte
+// k-rows; 16-byte chunk c of k-row k sits at c ^ (2 * (k & 3)): the 16 lanes
+// of a transpose read (4 k-rows x 2 chunks) hit 8 distinct bank groups.
+__device__ __forceinline__ uint32_t trans_off(int k, int col) {
+    return (uint32_t)((col >> 7) * (32 * 256) + k * 256 + (((((col & 127) >> 3) ^ ((k & 3) << 1))) << 4) +
+                      ((col & 7) << 1));
+}
+
+// ----------------------------------------------------------------------------- direct loaders
+
+// Row tile: rows [0, nrows) of a row-major array with ld elements per row
+// starting at `base`, k-step columns [k0, k0 + 32). Optional second array for
+// k >= ksplit (at k - ksplit). Each wave issues ROWS / 16 / NW instructions of
+// 16 rows each.
 template <class C, int ROWS>
-struct RowTile {
-    static constexpr int PER = ROWS * C::KCH / C::NT;
-    static_assert(PER >= 1 && (ROWS * C::KCH) % C::NT == 0, "row tile must split evenly");
-    static constexpr int ROWS_PER_PASS = C::NT / C::KCH;
+struct RowLoader {
+    static constexpr int IPW = ROWS / 16 / C::NW;     // instructions per wave per stage
+    static_assert(IPW >= 1 && ROWS % (16 * C::NW) == 0, "row tile must split over the waves");
     rsrc_t res, res2;
-    uint32_t voff, rowstep;
+    uint32_t voff, ldb, lds0;
     int ksplit;
-    uint4 buf[PER];
-
-    __device__ static int row(int i) { return (int)(threadIdx.x + i * C::NT) / C::KCH; }
-    __device__ static int chunk() { return (int)threadIdx.x % C::KCH; }
 
     __device__ void init(const uint16_t *base, int64_t ld, int nrows, const uint16_t *base2 = nullptr,
                          int ksplit_ = 1 << 30) {
         const uint32_t bytes = (uint32_t)((int64_t)max(nrows, 0) * ld * 2);
         res = make_rsrc(base, bytes);
         res2 = make_rsrc(base2 ? base2 : base, bytes);
-        voff = (uint32_t)((row(0) * ld + chunk() * 8) * 2);
-        rowstep = (uint32_t)(ROWS_PER_PASS * ld * 2);
+        ldb = (uint32_t)(ld * 2);
+        const int wave = wave_id(), L = threadIdx.x & 63;
+        const int r = wave * IPW * 16 + (L >> 2);
+        const int c = (L & 3) ^ ((L >> 3) & 3);      // (r >> 1) & 3 == (L >> 3) & 3
+        voff = (uint32_t)r * ldb + (uint32_t)(c << 4);
+        lds0 = (uint32_t)(wave * IPW * 1024);
         ksplit = ksplit_;
     }
-    __device__ void load(int k0) {
+    __device__ void issue(int k0, uint32_t tile) const {
         const bool second = k0 >= ksplit;
         const rsrc_t r = second ? res2 : res;
         const uint32_t kofs = (uint32_t)((second ? k0 - ksplit : k0) * 2);
 #pragma unroll
-        for (int i = 0; i < PER; ++i) buf[i] = bload(r, voff, kofs + i * rowstep);
-    }
-    __device__ void store(uint16_t *lds) const {
-#pragma unroll
-        for (int i = 0; i < PER; ++i)
-            *reinterpret_cast<uint4 *>(lds + lds_off(row(i), chunk(), C::BK)) = buf[i];
+        for (int i = 0; i < IPW; ++i) load_lds16(r, voff, kofs + (uint32_t)(i * 16) * ldb, tile + lds0 + i * 1024);
     }
 };
 
-// 8 k-rows x 8 columns held by one thread (one uint4 per k-row) -> LDS rows
-// cb*8 + c (one per column), k-chunk kb.
-template <class C>
-__device__ __forceinline__ void trans_block_store(const uint4 (&blk)[8], int kb, int cb, uint16_t *lds) {
-    const uint32_t *in = reinterpret_cast<const uint32_t *>(blk);   // [8 k][4 dwords]
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-        uint4 o;
-        uint32_t *w = reinterpret_cast<uint32_t *>(&o);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint32_t a = in[(2 * j) * 4 + (c >> 1)], b = in[(2 * j + 1) * 4 + (c >> 1)];
-            w[j] = (c & 1) ? pack_hi16(a, b) : pack_lo16(a, b);
-        }
-        *reinterpret_cast<uint4 *>(lds + lds_off(cb * 8 + c, kb, C::BK)) = o;
-    }
-}
-
-// Tile of BK k-rows x COLS columns of a row-major [rows][ld] array whose
-// columns are contiguous (k strided): element (k, c) at base + k*ld + c, k-rows
-// [0, nrows) valid (later k-rows read as zeros). Columns past the array's width
-// read neighbouring data or zeros; they only feed output rows/columns the
-// epilogue discards.
+// Trans tile: k-rows [k0, k0 + 32) x COLS columns of a row-major [K][ld] array
+// whose columns are contiguous; element (k, c) at base + k*ld + c with k-rows
+// [0, nrows) valid (later k-rows read as zeros). With a second base, columns
+// [COLS/2, COLS) come from it instead (the gate | up pairing). Columns past
+// the array's width read neighbouring data or zeros: they only feed output
+// rows/columns the epilogue discards.
 template <class C, int COLS>
-struct TransTile {
-    static constexpr int CB = COLS / 8;
-    static constexpr int NBLK = (C::BK / 8) * CB;
-    static constexpr int PER = (NBLK + C::NT - 1) / C::NT;
-    rsrc_t res;
-    uint32_t voff, ldb;
-    uint4 buf[PER][8];
+struct TransLoader {
+    static constexpr int NINST = COLS / 128 * 8;      // 8 instructions (4 k-rows each) per sub-tile
+    static constexpr int IPW = NINST / C::NW;
+    static_assert(IPW >= 1 && NINST % C::NW == 0, "trans tile must split over the waves");
+    rsrc_t res, res2;
+    uint32_t voff, ldb, lds0;
+    int inst0;
+    bool split;
 
-    __device__ static int blk(int i) { return (int)threadIdx.x + i * C::NT; }
-    __device__ static bool has(int i) { return NBLK % C::NT == 0 || blk(i) < NBLK; }
-
-    __device__ void init(const uint16_t *base, int64_t ld, int nrows, int ncols) {
+    __device__ void init(const uint16_t *base, int64_t ld, int nrows, int ncols, const uint16_t *base2 = nullptr) {
         const int64_t bytes = nrows > 0 ? ((int64_t)(nrows - 1) * ld + ncols) * 2 : 0;
         res = make_rsrc(base, (uint32_t)bytes);
+        res2 = make_rsrc(base2 ? base2 : base, (uint32_t)bytes);
+        split = base2 != nullptr;
         ldb = (uint32_t)(ld * 2);
-        const int b = blk(0);
-        voff = (uint32_t)(((int64_t)(b / CB) * 8 * ld + (b % CB) * 8) * 2);
+        const int wave = wave_id(), L = threadIdx.x & 63;
+        const int c = (L & 15) ^ ((L >> 4) << 1);    // k & 3 == L >> 4
+        voff = (uint32_t)(L >> 4) * ldb + (uint32_t)(c << 4);
+        inst0 = wave * IPW;
+        lds0 = (uint32_t)(inst0 * 1024);
     }
-    __device__ void load(int k0) {
+    __device__ void issue(int k0, uint32_t tile) const {
 #pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            if (!has(i)) continue;
-            const uint32_t v = voff + (uint32_t)(i * C::NT / CB) * 8 * ldb;   // PER > 1 only when NT divides CB
-#pragma unroll
-            for (int r = 0; r < 8; ++r) buf[i][r] = bload(res, v, (uint32_t)(k0 + r) * ldb);
+        for (int i = 0; i < IPW; ++i) {
+            const int inst = inst0 + i, sub = inst >> 3, kq = inst & 7;
+            const bool second = split && sub >= COLS / 256;
+            const uint32_t colb = split ? (uint32_t)((sub % (COLS / 256)) * 256) : (uint32_t)(sub * 256);
+            load_lds16(second ? res2 : res, voff, (uint32_t)(k0 + kq * 4) * ldb + colb, tile + lds0 + i * 1024);
         }
     }
-    __device__ void store(uint16_t *lds) const {
-#pragma unroll
-        for (int i = 0; i < PER; ++i)
-            if (has(i)) trans_block_store<C>(buf[i], blk(i) / CB, blk(i) % CB, lds);
-    }
 };
 
-// TransTile whose first COLS/2 columns come from one array and the rest from
-// another (the gate | up pairing). Each half of the workgroup's waves loads one
-// half, so every wave's buffer descriptor stays uniform.
+// Trans tile whose k-rows are gathered through an index: k-row k lives at
+// base + idx[k]*ld (k >= n: zeros), tile columns start at col0. The indices a
+// wave needs for one issue (4 consecutive k-rows per instruction) are read
+// with scalar loads, whose counter is separate from the vector-memory counter
+// that tracks the direct-to-LDS loads; each lane then picks the index of its
+// own k-row.
 template <class C, int COLS>
-struct TransTileSplit {
-    static constexpr int CB = COLS / 8, HCB = CB / 2;
-    static_assert((C::BK / 8) * CB == C::NT, "one 8x8 block per thread");
+struct TransIdxLoader {
+    static constexpr int NINST = COLS / 128 * 8;
+    static constexpr int IPW = NINST / C::NW;
+    static_assert(IPW >= 1 && NINST % C::NW == 0, "trans tile must split over the waves");
     rsrc_t res;
-    uint32_t voff, ldb;
-    int kb, cb;
-    uint4 buf[8];
-
-    // element (k, c) of half h at base_h + k*ld + c, k-rows [0, nrows), ncols
-    // columns from each base
-    __device__ void init(const uint16_t *base0, const uint16_t *base1, int64_t ld, int nrows, int ncols) {
-        const int half = __builtin_amdgcn_readfirstlane((int)threadIdx.x / (C::NT / 2));
-        const int lt = (int)threadIdx.x % (C::NT / 2);
-        kb = lt / HCB;
-        cb = half * HCB + lt % HCB;
-        const int64_t bytes = nrows > 0 ? ((int64_t)(nrows - 1) * ld + ncols) * 2 : 0;
-        res = make_rsrc(half ? base1 : base0, (uint32_t)bytes);
-        ldb = (uint32_t)(ld * 2);
-        voff = (uint32_t)(((int64_t)kb * 8 * ld + (lt % HCB) * 8) * 2);
-    }
-    __device__ void load(int k0) {
-#pragma unroll
-        for (int r = 0; r < 8; ++r) buf[r] = bload(res, voff, (uint32_t)(k0 + r) * ldb);
-    }
-    __device__ void store(uint16_t *lds) const { trans_block_store<C>(buf, kb, cb, lds); }
-};
-
-// As TransTile, for k-rows gathered through an index: k-row k lives at
-// base + idx[k]*ld (k >= n: zeros). Each thread keeps the row indices of its
-// next tile in registers, fetched one tile ahead so that data loads never wait
-// on an index load.
-template <class C, int COLS>
-struct TransTileIdx {
-    static constexpr int CB = COLS / 8;
-    static constexpr int NBLK = (C::BK / 8) * CB;
-    static constexpr int PER = (NBLK + C::NT - 1) / C::NT;
-    rsrc_t res;
-    uint32_t coloff, ldb;
+    uint32_t coff, ldb, lds0;
     const int32_t *idx;
-    int n;
-    int32_t nid[PER][8];
-    uint4 buf[PER][8];
+    int n, inst0, krow;
+    sgpr4_t nid[IPW];   // indices of the next issue's k-rows, in flight until used
 
-    __device__ static int blk(int i) { return (int)threadIdx.x + i * C::NT; }
-    __device__ static bool has(int i) { return NBLK % C::NT == 0 || blk(i) < NBLK; }
-
-    // base points at column 0 of row 0 of an array of `total_rows` rows; the
-    // tile's columns start at col0 and the array has ncols columns.
     __device__ void init(const int32_t *idx_, int n_, const uint16_t *base, int64_t ld, int64_t total_rows,
-                         int col0, int ncols) {
-        (void)ncols;
+                         int col0) {
         idx = idx_;
         n = n_;
         res = make_rsrc(base, (uint32_t)(total_rows * ld * 2));
         ldb = (uint32_t)(ld * 2);
-        coloff = (uint32_t)((col0 + (blk(0) % CB) * 8) * 2);
+        const int wave = wave_id(), L = threadIdx.x & 63;
+        const int c = (L & 15) ^ ((L >> 4) << 1);
+        coff = (uint32_t)((col0 + c * 8) * 2);
+        krow = L >> 4;
+        inst0 = wave * IPW;
+        lds0 = (uint32_t)(inst0 * 1024);
         fetch(0);
     }
+    // Scalar loads of the indices of k-rows [k0, k0 + 32) this wave issues;
+    // reads at most 3 ints past the expert's rows (inside the index array's buffer).
     __device__ void fetch(int k0) {
 #pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            if (!has(i)) continue;
-            const int kb = blk(i) / CB;
-#pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                const int k = k0 + kb * 8 + r;
-                nid[i][r] = k < n ? idx[k] : -1;
-            }
+        for (int i = 0; i < IPW; ++i) {
+            const int kb = min(k0 + ((inst0 + i) & 7) * 4, max(n - 1, 0));
+            nid[i] = sload4(idx + kb);
         }
     }
-    __device__ void load(int k0) {
+    // issue(k0) uses the indices fetched for k0 (calls follow the fetch order),
+    // then fetches those of k0 + 32.
+    __device__ void issue(int k0, uint32_t tile) {
 #pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            if (!has(i)) continue;
+        for (int i = 0; i < IPW; ++i) sload_wait(nid[i]);
 #pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                const uint32_t v = nid[i][r] >= 0 ? (uint32_t)nid[i][r] * ldb + coloff : kOutOfRange;
-                buf[i][r] = bload(res, v, 0);
-            }
+        for (int i = 0; i < IPW; ++i) {
+            const int inst = inst0 + i, sub = inst >> 3, kb = k0 + (inst & 7) * 4;
+            const int32_t r0 = nid[i][0], r1 = nid[i][1], r2 = nid[i][2], r3 = nid[i][3];
+            const int32_t mine = krow == 0 ? r0 : krow == 1 ? r1 : krow == 2 ? r2 : r3;
+            const uint32_t v = kb + krow < n ? (uint32_t)mine * ldb + coff + (uint32_t)(sub * 256) : kOutOfRange;
+            load_lds16(res, v, 0, tile + lds0 + i * 1024);
         }
-        fetch(k0 + C::BK);
-    }
-    __device__ void store(uint16_t *lds) const {
-#pragma unroll
-        for (int i = 0; i < PER; ++i)
-            if (has(i)) trans_block_store<C>(buf[i], blk(i) / CB, blk(i) % CB, lds);
+        fetch(k0 + 32);
     }
 };
 
-// One BK stage of MFMAs, LDS fragments double buffered across the 16-wide
-// k-steps. wrow(wn, fn) gives the LDS W row of n-block fn of wave wn.
+// ----------------------------------------------------------------------------- fragments
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+
+// MFMA operand for 32 tile rows starting at `row` of a Row tile, k-step kk:
+// lane l holds row + l%32, k = 16*kk + 8*(l/32) + 0..7.
+__device__ __forceinline__ bf16x8_t frag_row(uint32_t tile, int row, int kk) {
+    const int l = threadIdx.x & 63;
+    const uint32_t a = tile + row_off(row + (l & 31), kk * 2 + (l >> 5));
+    return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t *>(
+        (const __attribute__((address_space(3))) char *)(uintptr_t)a);
+}
+
+// MFMA operand for 32 tile columns starting at `col` of a Trans tile, k-step kk:
+// lane l holds column col + l%32, k = 16*kk + 8*(l/32) + 0..7. Within each
+// group of 16 lanes the transpose read hands lane i the 4 values at
+// (k0 + j, c0 + i), j = 0..3, when source lane 4j + q points at (k0 + j, c0 + 4q).
+__device__ __forceinline__ bf16x8_t frag_trans(uint32_t tile, int col, int kk) {
+    const int l = threadIdx.x & 63;
+    const int g = l >> 4, s = l & 15;
+    const int k = kk * 16 + (g >> 1) * 8 + (s >> 2);
+    const int c = col + (g & 1) * 16 + (s & 3) * 4;
+    const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t *)(uintptr_t)(tile + trans_off(k, c)));
+    const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t *)(uintptr_t)(tile + trans_off(k + 4, c)));
+    typedef short v8i16_t __attribute__((ext_vector_type(8)));
+    const v8i16_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8_t, v);
+}
+
+template <bool TRANS>
+__device__ __forceinline__ bf16x8_t frag(uint32_t tile, int rc, int kk) {
+    if constexpr (TRANS)
+        return frag_trans(tile, rc, kk);
+    else
+        return frag_row(tile, rc, kk);
+}
+
+// One BK = 32 stage of MFMAs (two 16-wide k-steps), the second k-step's
+// fragments read ahead of the first k-step's MFMAs.
 template <class C, class P>
-__device__ __forceinline__ void mma_stage(const uint16_t *stage, f32x16_t (&acc)[C::FM][C::FN], int wm,
-                                          int wn, const P &p) {
-    const uint16_t *xs = stage;
-    const uint16_t *ws = stage + C::BM * C::BK;
-    const int lane = threadIdx.x & 63;
-    const int lr = lane & 31, lh = lane >> 5;
-    constexpr int KS = C::BK / 16;
+__device__ __forceinline__ void mma_stage(uint32_t stage, f32x16_t (&acc)[C::FM][C::FN], int wm, int wn, const P &p) {
+    const uint32_t xs = stage, ws = stage + C::X_BYTES;
     bf16x8_t a[2][C::FN], b[2][C::FM];
     auto frags = [&](int kk, int s) {
 #pragma unroll
-        for (int fn = 0; fn < C::FN; ++fn)
-            a[s][fn] = *reinterpret_cast<const bf16x8_t *>(ws + lds_off(p.wrow(wn, fn) + lr, kk * 2 + lh, C::BK));
+        for (int fn = 0; fn < C::FN; ++fn) a[s][fn] = frag<P::W_TRANS>(ws, p.wrow(wn, fn), kk);
 #pragma unroll
-        for (int fm = 0; fm < C::FM; ++fm)
-            b[s][fm] = *reinterpret_cast<const bf16x8_t *>(xs + lds_off(wm * C::WM + fm * 32 + lr, kk * 2 + lh, C::BK));
+        for (int fm = 0; fm < C::FM; ++fm) b[s][fm] = frag<P::X_TRANS>(xs, wm * C::WM + fm * 32, kk);
     };
     frags(0, 0);
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-        if (kk + 1 < KS) frags(kk + 1, (kk + 1) & 1);
+    for (int kk = 0; kk < 2; ++kk) {
+        if (kk + 1 < 2) frags(kk + 1, (kk + 1) & 1);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int fm = 0; fm < C::FM; ++fm)
 #pragma unroll
             for (int fn = 0; fn < C::FN; ++fn)
-                acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk & 1][fn], b[kk & 1][fm], acc[fm][fn], 0, 0, 0);
+                acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk][fn], b[kk][fm], acc[fm][fn], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
     }
 }
 
-// Generic tile kernel body. P provides: setup(args) -> bool, nk, load(kt),
-// store(stage), wrow(wn, fn), epilogue(acc, wm, wn).
+// Generic tile kernel. P provides: C, Args, X_TRANS, W_TRANS, LOADS_PER_STAGE
+// (vector-memory instructions one wave issues per stage, index loads
+// included), setup(args) -> bool, nk, issue(kt, stage_lds_address),
+// wrow(wn, fn), epilogue(acc, wm, wn).
+//
+// Ring discipline: iteration kt waits for its own loads of stage kt (vmcnt
+// counts in issue order), then a barrier makes every wave's loads visible and
+// guarantees stage kt-1 is no longer read; only then are the loads of
+// k-step kt + NSTAGE - 1 issued into that freed stage.
 template <class P>
 __global__ __launch_bounds__(P::C::NT) void gemm_kernel(typename P::Args args) {
     using C = typename P::C;
-    extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+    extern __shared__ __attribute__((aligned(1024))) char lds_raw[];
+    const uint32_t lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)lds_raw;
     P p;
     if (!p.setup(args)) return;
     f32x16_t acc[C::FM][C::FN];
@@ -291,21 +341,21 @@ __global__ __launch_bounds__(P::C::NT) void gemm_kernel(typename P::Args args) {
         for (int fn = 0; fn < C::FN; ++fn)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[fm][fn][r] = 0.0f;
-    const int wave = threadIdx.x >> 6;
+    const int wave = wave_id();
     const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
     const int nk = p.nk;
-    if (nk > 0) {
-        p.load(0);
-        p.store(lds);
-        __syncthreads();
-        for (int kt = 0; kt < nk; ++kt) {
-            const uint16_t *cur = lds + (kt & 1) * C::STAGE;
-            uint16_t *nxt = lds + ((kt + 1) & 1) * C::STAGE;
-            if (kt + 1 < nk) p.load(kt + 1);
-            mma_stage<C>(cur, acc, wm, wn, p);
-            if (kt + 1 < nk) p.store(nxt);
-            __syncthreads();
-        }
+    constexpr int D = C::NSTAGE - 1;   // k-steps in flight
+#pragma unroll
+    for (int s = 0; s < D; ++s)
+        if (s < nk) p.issue(s, lds + s * C::STAGE_BYTES);
+    for (int kt = 0; kt < nk; ++kt) {
+        if (kt + D - 1 < nk)
+            wait_vmcnt<(D - 1) * P::LOADS_PER_STAGE>();   // k-steps kt+1 .. kt+D-1 may stay in flight
+        else
+            wait_vmcnt<0>();
+        lds_barrier();
+        if (kt + D < nk) p.issue(kt + D, lds + ((kt + D) % C::NSTAGE) * C::STAGE_BYTES);
+        mma_stage<C>(lds + (kt % C::NSTAGE) * C::STAGE_BYTES, acc, wm, wn, p);
     }
     p.epilogue(acc, wm, wn);
 }

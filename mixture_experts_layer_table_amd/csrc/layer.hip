@@ -29,22 +29,39 @@
 namespace mok {
 namespace {
 
-using CfgA = TileCfg<256, 256, 64, 2, 2>;
+using CfgA = TileCfg<256, 256, 2, 4, 4>;
 
 // ----------------------------------------------------------------------------- tile decode
 
 struct SegTile {
     MTile mt;
+    int nt;       // n-tile index
     int slot;     // ring slot of the tile's mini-batch
     int rowoff;   // first row of the tile inside that mini-batch
 };
 
-__device__ __forceinline__ bool decode_seg_tile(const SchedView &v, int g0, int g1, int64_t n_slots,
+constexpr int kXcds = 8;       // MI355X: 8 accelerator dies, each with its own L2
+constexpr int kGroupM = 4;     // m-tiles per group of the tile order
+
+// Tile of a segment GEMM for this workgroup. The 1-D grid (a multiple of 8
+// workgroups, at least the number of tiles) is dispatched round-robin over the
+// XCDs; with `per` = ceil(tiles / 8), workgroup b is mapped to tile
+// t = (b % 8) * per + b / 8 so that each XCD walks a contiguous range of
+// tiles, ordered in groups of kGroupM m-tiles x all n-tiles: the tiles an XCD
+// runs together share few operand slices in its L2.
+__device__ __forceinline__ bool decode_seg_tile(const SchedView &v, int g0, int g1, int64_t n_slots, int n_tiles,
                                                 SegTile &t) {
     if (*v.status) return false;
-    const int lo = v.mtfirst[g0], hi = v.mtfirst[g1];
-    if ((int)blockIdx.y >= hi - lo) return false;
-    t.mt = v.mtiles[lo + blockIdx.y];
+    const int lo = v.mtfirst[g0], mtc = v.mtfirst[g1] - lo;
+    const int total = mtc * n_tiles;                      // tiles that exist (device-side count)
+    const int per = (total + kXcds - 1) / kXcds, b = (int)blockIdx.x;
+    if (b / kXcds >= per) return false;                   // the grid is a host-side upper bound
+    const int id = (b % kXcds) * per + b / kXcds;
+    if (id >= total) return false;
+    const int gsize = kGroupM * n_tiles, grp = id / gsize, first = grp * kGroupM;
+    const int gm = min(kGroupM, mtc - first), r = id % gsize;
+    t.mt = v.mtiles[lo + first + r % gm];
+    t.nt = r / gm;
     t.slot = (int)(t.mt.g % n_slots);
     t.rowoff = t.mt.q0 - v.mb_start[t.mt.g];
     return true;
@@ -60,7 +77,7 @@ __device__ __forceinline__ float bf16r(float x) { return bf16_to_f32(f32_to_bf16
 
 struct GateUpArgs {
     SchedView v;
-    int g0, g1;
+    int g0, g1, n_tiles;
     int64_t n_slots;
     int MB, H, I;
     const uint16_t *ring, *wg, *wu;
@@ -71,34 +88,32 @@ template <class Cfg>
 struct GateUp {
     using C = Cfg;
     using Args = GateUpArgs;
-    RowTile<C, C::BM> xt;
-    TransTileSplit<C, C::BN> wt;
+    static constexpr bool X_TRANS = false, W_TRANS = true;
+    RowLoader<C, C::BM> xl;
+    TransLoader<C, C::BN> wl;
+    static constexpr int LOADS_PER_STAGE = RowLoader<C, C::BM>::IPW + TransLoader<C, C::BN>::IPW;
     SegTile t;
     int i0, nk, H, I, MB;
     uint16_t *h, *aring;
 
     __device__ bool setup(const Args &a) {
-        if (!decode_seg_tile(a.v, a.g0, a.g1, a.n_slots, t)) return false;
+        if (!decode_seg_tile(a.v, a.g0, a.g1, a.n_slots, a.n_tiles, t)) return false;
         H = a.H;
         I = a.I;
         MB = a.MB;
-        i0 = blockIdx.x * (C::BN / 2);
+        i0 = t.nt * (C::BN / 2);
         const int64_t row0 = (int64_t)t.slot * MB + t.rowoff;
-        xt.init(a.ring + row0 * H, H, t.mt.rows);
+        xl.init(a.ring + row0 * H, H, t.mt.rows);
         const int64_t eoff = (int64_t)t.mt.e * H * I;
-        wt.init(a.wg + eoff + i0, a.wu + eoff + i0, I, H, I - i0);
+        wl.init(a.wg + eoff + i0, I, H, I - i0, a.wu + eoff + i0);
         h = a.h;
         aring = a.aring;
         nk = H / C::BK;
         return true;
     }
-    __device__ void load(int kt) {
-        xt.load(kt * C::BK);
-        wt.load(kt * C::BK);
-    }
-    __device__ void store(uint16_t *s) const {
-        xt.store(s);
-        wt.store(s + C::BM * C::BK);
+    __device__ void issue(int kt, uint32_t tile) {
+        xl.issue(kt * C::BK, tile);
+        wl.issue(kt * C::BK, tile + C::X_BYTES);
     }
     // gate block fn pairs with up block fn + FN/2 inside the same wave
     __device__ int wrow(int wn, int fn) const {
@@ -138,7 +153,7 @@ struct GateUp {
 
 struct DownArgs {
     SchedView v;
-    int g0, g1;
+    int g0, g1, n_tiles;
     int64_t n_slots;
     int MB, H, I, k, MT, nb_full;
     const uint16_t *aring, *wd;
@@ -150,30 +165,28 @@ template <class Cfg>
 struct Down {
     using C = Cfg;
     using Args = DownArgs;
-    RowTile<C, C::BM> xt;
-    TransTile<C, C::BN> wt;
+    static constexpr bool X_TRANS = false, W_TRANS = true;
+    RowLoader<C, C::BM> xl;
+    TransLoader<C, C::BN> wl;
+    static constexpr int LOADS_PER_STAGE = RowLoader<C, C::BM>::IPW + TransLoader<C, C::BN>::IPW;
     SegTile t;
     int n0, nk, H;
     Args a;
 
     __device__ bool setup(const Args &args) {
-        if (!decode_seg_tile(args.v, args.g0, args.g1, args.n_slots, t)) return false;
+        if (!decode_seg_tile(args.v, args.g0, args.g1, args.n_slots, args.n_tiles, t)) return false;
         a = args;
         H = args.H;
-        n0 = blockIdx.x * C::BN;
+        n0 = t.nt * C::BN;
         const int64_t row0 = (int64_t)t.slot * args.MB + t.rowoff;
-        xt.init(args.aring + row0 * args.I, args.I, t.mt.rows);
-        wt.init(args.wd + (int64_t)t.mt.e * args.I * H + n0, H, args.I, H - n0);
+        xl.init(args.aring + row0 * args.I, args.I, t.mt.rows);
+        wl.init(args.wd + (int64_t)t.mt.e * args.I * H + n0, H, args.I, H - n0);
         nk = args.I / C::BK;
         return true;
     }
-    __device__ void load(int kt) {
-        xt.load(kt * C::BK);
-        wt.load(kt * C::BK);
-    }
-    __device__ void store(uint16_t *s) const {
-        xt.store(s);
-        wt.store(s + C::BM * C::BK);
+    __device__ void issue(int kt, uint32_t tile) {
+        xl.issue(kt * C::BK, tile);
+        wl.issue(kt * C::BK, tile + C::X_BYTES);
     }
     __device__ int wrow(int wn, int fn) const { return wn * C::WN + fn * 32; }
     __device__ void epilogue(f32x16_t (&acc)[C::FM][C::FN], int wm, int wn) {
@@ -216,7 +229,7 @@ struct Down {
 
 struct DAArgs {
     SchedView v;
-    int g0, g1;
+    int g0, g1, n_tiles;
     int64_t n_slots;
     int MB, H, I, S;
     const uint16_t *ring, *wd, *h;
@@ -229,36 +242,34 @@ template <class Cfg>
 struct DA {
     using C = Cfg;
     using Args = DAArgs;
-    RowTile<C, C::BM> xt;
-    RowTile<C, C::BN> wt;
+    static constexpr bool X_TRANS = false, W_TRANS = false;
+    RowLoader<C, C::BM> xl;
+    RowLoader<C, C::BN> wl;
+    static constexpr int LOADS_PER_STAGE = RowLoader<C, C::BM>::IPW + RowLoader<C, C::BN>::IPW;
     SegTile t;
     int i0, nk;
     Args a;
 
     __device__ bool setup(const Args &args) {
-        if (!decode_seg_tile(args.v, args.g0, args.g1, args.n_slots, t)) return false;
+        if (!decode_seg_tile(args.v, args.g0, args.g1, args.n_slots, args.n_tiles, t)) return false;
         a = args;
-        i0 = blockIdx.x * C::BN;
+        i0 = t.nt * C::BN;
         const int H = args.H, I = args.I;
         const int64_t row0 = (int64_t)t.slot * args.MB + t.rowoff;
-        xt.init(args.ring + row0 * H, H, t.mt.rows);
-        wt.init(args.wd + (int64_t)t.mt.e * I * H + (int64_t)i0 * H, H, min(C::BN, I - i0));
+        xl.init(args.ring + row0 * H, H, t.mt.rows);
+        wl.init(args.wd + (int64_t)t.mt.e * I * H + (int64_t)i0 * H, H, min(C::BN, I - i0));
         nk = H / C::BK;
         return true;
     }
-    __device__ void load(int kt) {
-        xt.load(kt * C::BK);
-        wt.load(kt * C::BK);
-    }
-    __device__ void store(uint16_t *s) const {
-        xt.store(s);
-        wt.store(s + C::BM * C::BK);
+    __device__ void issue(int kt, uint32_t tile) {
+        xl.issue(kt * C::BK, tile);
+        wl.issue(kt * C::BK, tile + C::X_BYTES);
     }
     __device__ int wrow(int wn, int fn) const { return wn * C::WN + fn * 32; }
     __device__ void epilogue(f32x16_t (&acc)[C::FM][C::FN], int wm, int wn) {
         const int lane = threadIdx.x & 63;
         const int I = a.I;
-        const int slice = blockIdx.x * C::WAVES_N + wn;
+        const int slice = t.nt * C::WAVES_N + wn;
         const bool slice_ok = i0 + wn * C::WN < I;
 #pragma unroll
         for (int fm = 0; fm < C::FM; ++fm) {
@@ -313,7 +324,7 @@ struct DA {
 
 struct DXArgs {
     SchedView v;
-    int g0, g1;
+    int g0, g1, n_tiles;
     int64_t n_slots;
     int H, I, k, MT, nb_full;
     const uint16_t *dh, *wg, *wu;
@@ -324,31 +335,29 @@ template <class Cfg>
 struct DX {
     using C = Cfg;
     using Args = DXArgs;
-    RowTile<C, C::BM> xt;
-    RowTile<C, C::BN> wt;
+    static constexpr bool X_TRANS = false, W_TRANS = false;
+    RowLoader<C, C::BM> xl;
+    RowLoader<C, C::BN> wl;
+    static constexpr int LOADS_PER_STAGE = RowLoader<C, C::BM>::IPW + RowLoader<C, C::BN>::IPW;
     SegTile t;
     int n0, nk, I;
     Args a;
 
     __device__ bool setup(const Args &args) {
-        if (!decode_seg_tile(args.v, args.g0, args.g1, args.n_slots, t)) return false;
+        if (!decode_seg_tile(args.v, args.g0, args.g1, args.n_slots, args.n_tiles, t)) return false;
         a = args;
-        n0 = blockIdx.x * C::BN;
+        n0 = t.nt * C::BN;
         I = args.I;
         const int H = args.H;
-        xt.init(args.dh + (int64_t)t.mt.c0 * 2 * I, 2 * I, t.mt.rows);
+        xl.init(args.dh + (int64_t)t.mt.c0 * 2 * I, 2 * I, t.mt.rows);
         const int64_t wo = (int64_t)t.mt.e * H * I + (int64_t)n0 * I;
-        wt.init(args.wg + wo, I, min(C::BN, H - n0), args.wu + wo, I);
+        wl.init(args.wg + wo, I, min(C::BN, H - n0), args.wu + wo, I);
         nk = 2 * I / C::BK;
         return true;
     }
-    __device__ void load(int kt) {
-        xt.load(kt * C::BK);
-        wt.load(kt * C::BK);
-    }
-    __device__ void store(uint16_t *s) const {
-        xt.store(s);
-        wt.store(s + C::BM * C::BK);
+    __device__ void issue(int kt, uint32_t tile) {
+        xl.issue(kt * C::BK, tile);
+        wl.issue(kt * C::BK, tile + C::X_BYTES);
     }
     __device__ int wrow(int wn, int fn) const { return wn * C::WN + fn * 32; }
     __device__ void epilogue(f32x16_t (&acc)[C::FM][C::FN], int wm, int wn) {
@@ -394,8 +403,10 @@ template <class Cfg>
 struct WGU {
     using C = Cfg;
     using Args = WGUArgs;
-    TransTileIdx<C, C::BM> xt;   // x rows of the expert's tokens, k = canonical row
-    TransTile<C, C::BN> wt;      // dh rows, stored in canonical order
+    static constexpr bool X_TRANS = true, W_TRANS = true;
+    TransIdxLoader<C, C::BM> xl;   // x rows of the expert's tokens, k = canonical row
+    TransLoader<C, C::BN> wl;      // dh rows, stored in canonical order
+    static constexpr int LOADS_PER_STAGE = TransIdxLoader<C, C::BM>::IPW + TransLoader<C, C::BN>::IPW;
     int e, h0, n0, ne, off, nk;
     Args a;
 
@@ -408,18 +419,14 @@ struct WGU {
         ne = args.v.counts[e];
         off = args.v.offsets[e];
         nk = (ne + C::BK - 1) / C::BK;
-        xt.init(args.v.ctok + off, ne, args.x, args.H, args.v.T, h0, args.H);
+        xl.init(args.v.ctok + off, ne, args.x, args.H, args.v.T, h0);
         const int I2 = 2 * args.I;
-        wt.init(args.dh + (int64_t)off * I2 + n0, I2, ne, I2 - n0);
+        wl.init(args.dh + (int64_t)off * I2 + n0, I2, ne, I2 - n0);
         return true;
     }
-    __device__ void load(int kt) {
-        xt.load(kt * C::BK);
-        wt.load(kt * C::BK);
-    }
-    __device__ void store(uint16_t *s) const {
-        xt.store(s);
-        wt.store(s + C::BM * C::BK);
+    __device__ void issue(int kt, uint32_t tile) {
+        xl.issue(kt * C::BK, tile);
+        wl.issue(kt * C::BK, tile + C::X_BYTES);
     }
     __device__ int wrow(int wn, int fn) const { return wn * C::WN + fn * 32; }
     __device__ void epilogue(f32x16_t (&acc)[C::FM][C::FN], int wm, int wn) {
@@ -456,8 +463,10 @@ template <class Cfg>
 struct WD {
     using C = Cfg;
     using Args = WDArgs;
-    TransTile<C, C::BM> xt;      // g*a rows, stored in canonical order
-    TransTileIdx<C, C::BN> wt;   // dy rows of the expert's tokens
+    static constexpr bool X_TRANS = true, W_TRANS = true;
+    TransLoader<C, C::BM> xl;      // g*a rows, stored in canonical order
+    TransIdxLoader<C, C::BN> wl;   // dy rows of the expert's tokens
+    static constexpr int LOADS_PER_STAGE = TransLoader<C, C::BM>::IPW + TransIdxLoader<C, C::BN>::IPW;
     int e, i0, n0, ne, off, nk;
     Args a;
 
@@ -470,17 +479,13 @@ struct WD {
         ne = args.v.counts[e];
         off = args.v.offsets[e];
         nk = (ne + C::BK - 1) / C::BK;
-        wt.init(args.v.ctok + off, ne, args.dy, args.H, args.v.T, n0, args.H);
-        xt.init(args.ga + (int64_t)off * args.I + i0, args.I, ne, args.I - i0);
+        wl.init(args.v.ctok + off, ne, args.dy, args.H, args.v.T, n0);
+        xl.init(args.ga + (int64_t)off * args.I + i0, args.I, ne, args.I - i0);
         return true;
     }
-    __device__ void load(int kt) {
-        xt.load(kt * C::BK);
-        wt.load(kt * C::BK);
-    }
-    __device__ void store(uint16_t *s) const {
-        xt.store(s);
-        wt.store(s + C::BM * C::BK);
+    __device__ void issue(int kt, uint32_t tile) {
+        xl.issue(kt * C::BK, tile);
+        wl.issue(kt * C::BK, tile + C::X_BYTES);
     }
     __device__ int wrow(int wn, int fn) const { return wn * C::WN + fn * 32; }
     __device__ void epilogue(f32x16_t (&acc)[C::FM][C::FN], int wm, int wn) {
@@ -649,6 +654,11 @@ int64_t mtile_bound(const Plan &p, Round r) {
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// 1-D grid for a segment GEMM: n_tiles x m-tile bound, rounded up to whole XCD rounds.
+dim3 seg_grid(int n_tiles, int64_t mt_bound) {
+    return dim3((unsigned)(ceil_div((int64_t)n_tiles * mt_bound, kXcds) * kXcds));
+}
+
 struct Macro {
     int m;
     int t0, t1;
@@ -686,16 +696,14 @@ mok_status launch_forward(const Plan &p, const void *schedule, void *workspace, 
             identity_rows<<<sgrid, 256, 0, st>>>(v, r.g0, p.n_slots, p.MB, p.H, p.k, (int)p.MT, p.nb_full, topk_w,
                                                  ring, out, stage);
         } else {
-            const unsigned mt = (unsigned)mtile_bound(p, r);
-            GateUpArgs ga{v, r.g0, r.g1, p.n_slots, p.MB, p.H, p.I, ring,
+            const int64_t mt = mtile_bound(p, r);
+            const int ntg = (int)ceil_div(p.I, CfgA::BN / 2), ntd = (int)ceil_div(p.H, CfgA::BN);
+            GateUpArgs ga{v, r.g0, r.g1, ntg, p.n_slots, p.MB, p.H, p.I, ring,
                           static_cast<const uint16_t *>(w.w_gate), static_cast<const uint16_t *>(w.w_up), h, aring};
-            if ((err = launch_gemm<GateUp<CfgA>>("gateup", dim3((unsigned)ceil_div(p.I, CfgA::BN / 2), mt), ga, st)) !=
-                hipSuccess)
-                break;
-            DownArgs da{v, r.g0, r.g1, p.n_slots, p.MB, p.H, p.I, p.k, (int)p.MT, p.nb_full, aring,
+            if ((err = launch_gemm<GateUp<CfgA>>("gateup", seg_grid(ntg, mt), ga, st)) != hipSuccess) break;
+            DownArgs da{v, r.g0, r.g1, ntd, p.n_slots, p.MB, p.H, p.I, p.k, (int)p.MT, p.nb_full, aring,
                         static_cast<const uint16_t *>(w.w_down), topk_w, out, stage};
-            if ((err = launch_gemm<Down<CfgA>>("down", dim3((unsigned)ceil_div(p.H, CfgA::BN), mt), da, st)) != hipSuccess)
-                break;
+            if ((err = launch_gemm<Down<CfgA>>("down", seg_grid(ntd, mt), da, st)) != hipSuccess) break;
         }
         if (p.k > 1 && (r.g1 == p.G || r.g1 == first_minibatch(p, macro_of_minibatch(p, r.g0) + 1))) {
             const Macro mc = macro_info(p, macro_of_minibatch(p, r.g0));
@@ -732,13 +740,12 @@ mok_status launch_backward(const Plan &p, const void *schedule, void *workspace,
                 KernelTimer tm("gather_dy", st);
                 gather_rows<<<sgrid, 256, 0, st>>>(v, r.g0, p.n_slots, p.MB, p.H, p.k, dy, ring);
             }
-            const unsigned mt = (unsigned)mtile_bound(p, r);
-            DAArgs aa{v, r.g0, r.g1, p.n_slots, p.MB, p.H, p.I, p.dg_slices, ring, wd, h, topk_w, dh, ga, dgp};
-            if ((err = launch_gemm<DA<CfgA>>("dA", dim3((unsigned)ceil_div(p.I, CfgA::BN), mt), aa, st)) != hipSuccess)
-                break;
-            DXArgs xa{v, r.g0, r.g1, p.n_slots, p.H, p.I, p.k, (int)p.MT, p.nb_full, dh, wg, wu, dx, stage};
-            if ((err = launch_gemm<DX<CfgA>>("dX", dim3((unsigned)ceil_div(p.H, CfgA::BN), mt), xa, st)) != hipSuccess)
-                break;
+            const int64_t mt = mtile_bound(p, r);
+            const int nta = (int)ceil_div(p.I, CfgA::BN), ntx = (int)ceil_div(p.H, CfgA::BN);
+            DAArgs aa{v, r.g0, r.g1, nta, p.n_slots, p.MB, p.H, p.I, p.dg_slices, ring, wd, h, topk_w, dh, ga, dgp};
+            if ((err = launch_gemm<DA<CfgA>>("dA", seg_grid(nta, mt), aa, st)) != hipSuccess) break;
+            DXArgs xa{v, r.g0, r.g1, ntx, p.n_slots, p.H, p.I, p.k, (int)p.MT, p.nb_full, dh, wg, wu, dx, stage};
+            if ((err = launch_gemm<DX<CfgA>>("dX", seg_grid(ntx, mt), xa, st)) != hipSuccess) break;
             if (p.k > 1 && r.g0 == first_minibatch(p, macro_of_minibatch(p, r.g0))) {
                 const Macro mc = macro_info(p, macro_of_minibatch(p, r.g0));
                 KernelTimer tm("combine_dx", st);

@@ -15,7 +15,7 @@ struct TileChoice {
 
 inline TileChoice choose_tiles(int H, int I, int E, int k, int64_t T, int precision) {
     (void)H; (void)I; (void)E; (void)k; (void)T; (void)precision;
-    return TileChoice{256, 128};
+    return TileChoice{256, 64};
 }
 
 }  // namespace mok
