@@ -67,10 +67,22 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
 // (buffer_load_dwordx4 ... lds; M0 holds the LDS base). Issued as inline asm so
 // that the compiler does not track these LDS writes: ordering against LDS
 // reads is explicit (wait_vmcnt + lds_barrier in the kernel loop).
+// The descriptor is wave-uniform by construction; readfirstlane states it to
+// the compiler (a no-op when the value already sits in scalar registers).
+__device__ __forceinline__ rsrc_t uniform(rsrc_t r) {
+    rsrc_t u;
+    u.x = __builtin_amdgcn_readfirstlane(r.x);
+    u.y = __builtin_amdgcn_readfirstlane(r.y);
+    u.z = __builtin_amdgcn_readfirstlane(r.z);
+    u.w = __builtin_amdgcn_readfirstlane(r.w);
+    return u;
+}
+
 __device__ __forceinline__ void load_lds16(rsrc_t r, uint32_t voff, uint32_t soff, uint32_t dst) {
-    asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+    // one wait state between the SALU write of M0 and the LDS-DMA read of it (GFX9 hazard)
+    asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
                  :
-                 : "v"(voff), "s"(r), "s"(soff), "s"(dst)
+                 : "v"(voff), "s"(uniform(r)), "s"(soff), "s"(dst)
                  : "memory", "m0");
 }
 
@@ -292,41 +304,43 @@ __device__ __forceinline__ bf16x8_t frag(uint32_t tile, int rc, int kk) {
         return frag_row(tile, rc, kk);
 }
 
-// One BK = 32 stage of MFMAs (two 16-wide k-steps), the second k-step's
-// fragments read ahead of the first k-step's MFMAs.
+// Fragments and MFMAs of one 16-wide k-step (kk = 0, 1 of a BK = 32 stage).
 template <class C, class P>
-__device__ __forceinline__ void mma_stage(uint32_t stage, f32x16_t (&acc)[C::FM][C::FN], int wm, int wn, const P &p) {
-    const uint32_t xs = stage, ws = stage + C::X_BYTES;
-    bf16x8_t a[2][C::FN], b[2][C::FM];
-    auto frags = [&](int kk, int s) {
+struct Frags {
+    bf16x8_t a[C::FN], b[C::FM];
+    __device__ __forceinline__ void read(uint32_t stage, int kk, int wm, int wn, const P &p) {
+        const uint32_t xs = stage, ws = stage + C::X_BYTES;
 #pragma unroll
-        for (int fn = 0; fn < C::FN; ++fn) a[s][fn] = frag<P::W_TRANS>(ws, p.wrow(wn, fn), kk);
+        for (int fn = 0; fn < C::FN; ++fn) a[fn] = frag<P::W_TRANS>(ws, p.wrow(wn, fn), kk);
 #pragma unroll
-        for (int fm = 0; fm < C::FM; ++fm) b[s][fm] = frag<P::X_TRANS>(xs, wm * C::WM + fm * 32, kk);
-    };
-    frags(0, 0);
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-        if (kk + 1 < 2) frags(kk + 1, (kk + 1) & 1);
-        __builtin_amdgcn_sched_barrier(0);
+        for (int fm = 0; fm < C::FM; ++fm) b[fm] = frag<P::X_TRANS>(xs, wm * C::WM + fm * 32, kk);
+    }
+    __device__ __forceinline__ void mma(f32x16_t (&acc)[C::FM][C::FN]) const {
 #pragma unroll
         for (int fm = 0; fm < C::FM; ++fm)
 #pragma unroll
             for (int fn = 0; fn < C::FN; ++fn)
-                acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk][fn], b[kk][fm], acc[fm][fn], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
+                acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[fn], b[fm], acc[fm][fn], 0, 0, 0);
     }
-}
+};
+
+__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 // Generic tile kernel. P provides: C, Args, X_TRANS, W_TRANS, LOADS_PER_STAGE
-// (vector-memory instructions one wave issues per stage, index loads
-// included), setup(args) -> bool, nk, issue(kt, stage_lds_address),
-// wrow(wn, fn), epilogue(acc, wm, wn).
+// (vector-memory instructions one wave issues per stage), setup(args) -> bool,
+// nk, issue(kt, stage_lds_address), wrow(wn, fn), epilogue(acc, wm, wn).
 //
-// Ring discipline: iteration kt waits for its own loads of stage kt (vmcnt
-// counts in issue order), then a barrier makes every wave's loads visible and
-// guarantees stage kt-1 is no longer read; only then are the loads of
-// k-step kt + NSTAGE - 1 issued into that freed stage.
+// Pipeline of K-step kt (stage = kt % NSTAGE, D = NSTAGE - 1 steps in flight):
+//   read fragments of half-step 1 of stage kt
+//   issue the direct loads of K-step kt + D into stage (kt - 1) % NSTAGE
+//   MFMAs of half-step 0
+//   wait for this wave's loads of stage kt + 1 (vmcnt counts in issue order)
+//   and for its own LDS reads of stage kt, then barrier: stage kt + 1 is
+//   visible to every wave and stage kt is no longer read by any
+//   read fragments of half-step 0 of stage kt + 1
+//   MFMAs of half-step 1
+// so every LDS read is covered by queued MFMAs, and the barrier sits between
+// two groups of MFMAs (the other wave of the SIMD keeps the matrix core busy).
 template <class P>
 __global__ __launch_bounds__(P::C::NT) void gemm_kernel(typename P::Args args) {
     using C = typename P::C;
@@ -343,19 +357,40 @@ __global__ __launch_bounds__(P::C::NT) void gemm_kernel(typename P::Args args) {
             for (int r = 0; r < 16; ++r) acc[fm][fn][r] = 0.0f;
     const int wave = wave_id();
     const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
-    const int nk = p.nk;
+    const int nk = __builtin_amdgcn_readfirstlane(p.nk);   // wave-uniform loop bound
     constexpr int D = C::NSTAGE - 1;   // k-steps in flight
+    auto stage = [&](int kt) { return lds + (uint32_t)((kt % C::NSTAGE) * C::STAGE_BYTES); };
+    Frags<C, P> f0, f1;
 #pragma unroll
     for (int s = 0; s < D; ++s)
-        if (s < nk) p.issue(s, lds + s * C::STAGE_BYTES);
-    for (int kt = 0; kt < nk; ++kt) {
-        if (kt + D - 1 < nk)
-            wait_vmcnt<(D - 1) * P::LOADS_PER_STAGE>();   // k-steps kt+1 .. kt+D-1 may stay in flight
+        if (s < nk) p.issue(s, stage(s));
+    if (nk > 0) {
+        if (nk >= D)
+            wait_vmcnt<(D - 1) * P::LOADS_PER_STAGE>();
         else
             wait_vmcnt<0>();
         lds_barrier();
-        if (kt + D < nk) p.issue(kt + D, lds + ((kt + D) % C::NSTAGE) * C::STAGE_BYTES);
-        mma_stage<C>(lds + (kt % C::NSTAGE) * C::STAGE_BYTES, acc, wm, wn, p);
+        f0.read(stage(0), 0, wm, wn, p);
+    }
+    for (int kt = 0; kt < nk; ++kt) {
+        f1.read(stage(kt), 1, wm, wn, p);
+        if (kt + D < nk) p.issue(kt + D, stage(kt + D));
+        __builtin_amdgcn_sched_barrier(0);
+        f0.mma(acc);
+        __builtin_amdgcn_sched_barrier(0);
+        // Unconditional, so that the compiler's LDS-counter bookkeeping sees
+        // one straight path (after the last K-step this reads a stale stage
+        // that is never used).
+        if (kt + D < nk)
+            wait_vmcnt<(D - 1) * P::LOADS_PER_STAGE>();   // k-steps kt+2 .. kt+D may stay in flight
+        else
+            wait_vmcnt<0>();
+        wait_lgkm0();
+        lds_barrier();
+        f0.read(stage(kt + 1), 0, wm, wn, p);
+        __builtin_amdgcn_sched_barrier(0);
+        f1.mma(acc);
+        __builtin_amdgcn_sched_barrier(0);
     }
     p.epilogue(acc, wm, wn);
 }
