@@ -51,8 +51,10 @@ def flops_per_row(H, I):
 
 
 def source_digest() -> str:
+    """Digest of the device-code sources (HIP files and the headers they include)."""
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "mixture_experts_layer_table_amd", "csrc", "*"))):
+    csrc = os.path.join(ROOT, "mixture_experts_layer_table_amd", "csrc")
+    for p in sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.h"))):
         h.update(open(p, "rb").read())
     return h.hexdigest()[:16]
 
@@ -121,6 +123,9 @@ def main():
     ap.add_argument("--workload", default="ep64_share", choices=list(WORKLOAD_TEXT))
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="instead of the layer, run a plain device-to-device copy of this many MiB "
+                         "(calibrates the HBM byte counters against a kernel of known traffic)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -133,6 +138,16 @@ def main():
 
     import mixture_experts_layer_table_amd as mok
     import synth
+
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps(dict(copy_probe_bytes=n, launches=args.steps)), flush=True)
+        return
 
     cfg = synth.CONFIGS[args.workload]
     dev = "cuda:0"

@@ -32,6 +32,10 @@ mok_status make_plan(const mok_config *cfg, const mok_shape *shape, Plan *p) {
     if (s.H % 64 || s.I % 64) return MOK_ERROR_INVALID_VALUE;
     if (s.k > s.E || s.E > kMaxExperts) return MOK_ERROR_INVALID_VALUE;
     if (s.T * (int64_t)s.k >= (int64_t(1) << 31)) return MOK_ERROR_INVALID_VALUE;
+    // Activation tensors are addressed through buffer descriptors with 32-bit
+    // byte offsets: x / dy / out / dx [T,H] and h / dh [R,2I] stay below 2 GiB.
+    if (s.T * (int64_t)s.H * 2 >= (int64_t(1) << 31)) return MOK_ERROR_INVALID_VALUE;
+    if (s.T * (int64_t)s.k * s.I * 4 >= (int64_t(1) << 31)) return MOK_ERROR_INVALID_VALUE;
     if (cfg->minibatch_rows < 16 || cfg->minibatch_rows % 16) return MOK_ERROR_INVALID_VALUE;
     if (cfg->macrobatch_tokens < 0 || cfg->ring_bytes <= 0) return MOK_ERROR_INVALID_VALUE;
     if (!(cfg->capacity_multiplier > 0.0f && cfg->capacity_multiplier <= 4.0f))

@@ -31,7 +31,9 @@ def test_config_default():
         (512, 0, 256 << 20, 1.0, mok.MOK_BF16)
 
 
-BAD_SHAPES = [dict(T=-1), dict(H=100), dict(I=96), dict(E=0), dict(k=0), dict(k=9), dict(T=1 << 31)]
+BAD_SHAPES = [dict(T=-1), dict(H=100), dict(I=96), dict(E=0), dict(k=0), dict(k=9), dict(T=1 << 31),
+              dict(T=1 << 17, H=8192),              # x [T,H] bf16 reaches 2 GiB
+              dict(T=1 << 18, I=1024, k=2)]         # h [R,2I] bf16 reaches 2 GiB
 
 
 @pytest.mark.parametrize("bad", BAD_SHAPES)
