@@ -31,12 +31,17 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0
+PEAK_FP8_TFLOPS = 5000.0
 PEAK_HBM_GBS = 8000.0
 
 WORKLOAD_TEXT = {
     "ep64_share": "EP-64 one-GPU share: 16,384 routed rows (2,048 tokens x 64 ranks x top-8 / 256 experts x 4), "
                   "4 local SwiGLU experts, H=7168, I=2048, Zipf(1.2) loads 8658/3769/2317/1640, BF16, "
                   "ring 256 MiB, mini-batch 512",
+    "ep64_share_mxfp8": "EP-64 one-GPU share as ep64_share in MXFP8 (E4M3 elements, E8M0 scale per 32 along K; "
+                        "weights pre-quantized once, activations quantized in-kernel; weight gradients BF16), "
+                        "Zipf(1.2) loads",
+    "ep64_share_mxfp8_uniform": "EP-64 one-GPU share in MXFP8 as ep64_share_mxfp8, uniform loads 4 x 4,096",
     "full_layer": "single-GPU full layer: T=2048, top-8 of 256 SwiGLU experts, H=7168, I=2048, BF16",
     "stream": "fine-grained streaming share: 8 x 20,480 rows, 8 experts, H=4096, I=1024, Dirichlet(0.3), "
               "ring 128 MiB",
@@ -77,9 +82,12 @@ def read_traffic(workload: str, kernel: str):
 
 def cpu_baseline(inp, tokens_per_step, seconds):
     """The oracle as it stands, on a bounded sample of routed rows of the same
-    workload: forward and backward of each sampled row, extrapolated to the step."""
+    workload: forward and backward of each sampled row, extrapolated to the step
+    (with the MXFP8 fake-quant in MXFP8 mode)."""
     import numpy as np
     from oracle import layer as L
+    from oracle import mxfp8 as M
+    fq = M.fake_quant if inp.cfg.precision == "mxfp8" else None
     try:
         from threadpoolctl import threadpool_info
         cores = sum(i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas") or 1
@@ -100,8 +108,8 @@ def cpu_baseline(inp, tokens_per_step, seconds):
             tok = rows // cfg.k
             t = time.perf_counter()
             xe, dye = f(inp.x[tok]), f(inp.dy[tok])
-            L.expert_forward(xe, Wg, Wu, Wd)
-            L.expert_backward(xe, dye, wflat[rows][:, None], Wg, Wu, Wd)
+            L.expert_forward(xe, Wg, Wu, Wd, fq)
+            L.expert_backward(xe, dye, wflat[rows][:, None], Wg, Wu, Wd, fq)
             busy += time.perf_counter() - t
             done += rows.size
             if busy >= seconds:
@@ -160,9 +168,21 @@ def main():
     tw = torch.from_numpy(inp.topk_w).to(dev)
     x, dy = bf16(inp.x), bf16(inp.dy)
     wg, wu, wd = bf16(inp.w_gate), bf16(inp.w_up), bf16(inp.w_down)
-    weights = mok.weights_bf16(wg, wu, wd)
+    mx = cfg.precision == "mxfp8"
+    quant_ms = None
+    if mx:   # weights quantized once per step of a training loop's weight update, outside the layer's time
+        torch.cuda.synchronize()
+        q0, q1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        q0.record()
+        qw = mok.MXFP8Weights(wg, wu, wd)
+        q1.record()
+        torch.cuda.synchronize()
+        quant_ms = q0.elapsed_time(q1)
+        w_fwd, w_bwd = qw.fwd, qw.bwd
+    else:
+        w_fwd = w_bwd = mok.weights_bf16(wg, wu, wd)
     config = mok.MoKConfig(minibatch_rows=cfg.minibatch_rows, macrobatch_tokens=cfg.macrobatch_tokens,
-                           ring_bytes=cfg.ring_bytes)
+                           ring_bytes=cfg.ring_bytes, precision=mok.MOK_MXFP8 if mx else mok.MOK_BF16)
     ws = mok.get_workspace(config, device=dev, num_local_tokens=cfg.T, hidden_size=cfg.H,
                            intermediate_size=cfg.I, num_experts=cfg.E, topk=cfg.k)
     sched = torch.empty(ws.schedule_bytes, dtype=torch.uint8, device=dev)
@@ -173,8 +193,8 @@ def main():
 
     def step():
         mok.build_schedule(ws, ids, sched)
-        mok.forward(ws, sched, x, tw, weights, out=out, fwd_ctx=ctx)
-        mok.backward(ws, sched, ctx, x, tw, weights, dy, grads=grads)
+        mok.forward(ws, sched, x, tw, w_fwd, out=out, fwd_ctx=ctx)
+        mok.backward(ws, sched, ctx, x, tw, w_bwd, dy, grads=grads)
 
     for _ in range(args.warmup):
         step()
@@ -212,16 +232,26 @@ def main():
             by = (2 * cfg.T * H + 2 * R * H + 4 * R) * nprof / launches   # unique reads + writes
             entry["gbs"] = round(by / (avg * 1e-3) / 1e9, 1)
         kernels[name] = entry
+    fp8_kernels = ("gateup", "down", "dA", "dX") if mx else ()
+    for n in kernels:
+        if n in fpr:
+            peak = PEAK_FP8_TFLOPS if n in fp8_kernels else PEAK_BF16_TFLOPS
+            kernels[n]["mfma_dtype"] = "mxfp8" if n in fp8_kernels else "bf16"
+            kernels[n]["frac_of_peak"] = round(kernels[n]["tflops"] / peak, 4)
     dominant = max((n for n in kernels if n in fpr), key=lambda n: kernels[n]["ms_per_step"])
     dk = kernels[dominant]
     ach = dk["tflops"]
-    roofline = dict(bound="mfma", kernel=dominant, achieved=ach, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
-                    frac=round(ach / PEAK_BF16_TFLOPS, 4),
+    dpeak = PEAK_FP8_TFLOPS if dominant in fp8_kernels else PEAK_BF16_TFLOPS
+    roofline = dict(bound="mfma", kernel=dominant, achieved=ach, peak=dpeak, unit="TFLOP/s",
+                    frac=round(ach / dpeak, 4),
                     traffic=read_traffic(args.workload, dominant),
                     flops_per_launch=fpr[dominant] * R * nprof / ktimes[dominant][0],
                     avg_launch_ms=dk["avg_ms"])
 
     total_flops = 18 * R * H * I
+    # time at the MFMA peaks: fwd + dA + dX (12 RHI) on the fp8 peak in MXFP8 mode, the rest bf16
+    peak_time_s = ((12 * R * H * I) / (PEAK_FP8_TFLOPS if mx else PEAK_BF16_TFLOPS)
+                   + (6 * R * H * I) / PEAK_BF16_TFLOPS) / 1e12
     tokens = cfg.tokens_per_step
     value = tokens / (ms_per_step * 1e-3)
     sched_ms = kernels.get("schedule", {}).get("ms_per_step", 0.0)
@@ -229,14 +259,15 @@ def main():
         metric="MoE layer fwd+bwd tokens/s on 1 GPU; grouped-GEMM MFMA util % of peak",
         value=round(value, 1), unit="tokens/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
         ms_per_step=round(ms_per_step, 4), higher_is_better=True, scaling="weak", vs_baseline=None,
-        dtype="bf16", data="synthetic",
+        dtype="mxfp8" if mx else "bf16", data="synthetic",
         config=dict(workload=f"{args.workload}: {WORKLOAD_TEXT[args.workload]}", T=cfg.T, H=H, I=I, E=cfg.E,
                     k=cfg.k, routed_rows=R, tokens_per_step=tokens, minibatch_rows=cfg.minibatch_rows,
                     macrobatch_tokens=cfg.macrobatch_tokens, ring_bytes=cfg.ring_bytes),
         rows_per_s=round(R / (ms_per_step * 1e-3), 1),
         tflops=round(total_flops / (ms_per_step * 1e-3) / 1e12, 1),
-        mfma_util=round(total_flops / (ms_per_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        mfma_util=round(peak_time_s / (ms_per_step * 1e-3), 4),
         schedule_share=round(sched_ms / ms_per_step, 4) if sched_ms else None,
+        weight_quantize_ms=round(quant_ms, 4) if quant_ms is not None else None,
         roofline=roofline, kernels=kernels, source_digest=source_digest(),
         device=torch.cuda.get_device_name(0),
     )

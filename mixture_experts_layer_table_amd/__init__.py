@@ -265,6 +265,24 @@ def weights_mxfp8(gate, up, down) -> mok_weights:
                        up[1].data_ptr(), down[0].data_ptr(), down[1].data_ptr())
 
 
+class MXFP8Weights:
+    """Expert weights quantized once for MXFP8 mode, in both orientations the
+    layer needs (quantized along the contraction axis of each GEMM):
+    ``fwd`` for mok_forward (W_gate^T, W_up^T [E,I,H] along H; W_down^T
+    [E,H,I] along I) and ``bwd`` for mok_backward (W_gate, W_up [E,H,I] along
+    I; W_down [E,I,H] along H). Holds the uint8 tensors the pointers refer to."""
+
+    def __init__(self, w_gate, w_up, w_down):
+        self.fwd_gate = mxfp8_quantize(w_gate, True)
+        self.fwd_up = mxfp8_quantize(w_up, True)
+        self.fwd_down = mxfp8_quantize(w_down, True)
+        self.bwd_gate = mxfp8_quantize(w_gate, False)
+        self.bwd_up = mxfp8_quantize(w_up, False)
+        self.bwd_down = mxfp8_quantize(w_down, False)
+        self.fwd = weights_mxfp8(self.fwd_gate, self.fwd_up, self.fwd_down)
+        self.bwd = weights_mxfp8(self.bwd_gate, self.bwd_up, self.bwd_down)
+
+
 def forward(ws: Workspace, schedule, x, topk_w, weights: mok_weights, out=None, fwd_ctx=None):
     """Returns (out bf16 [T,H], fwd_ctx uint8)."""
     import torch

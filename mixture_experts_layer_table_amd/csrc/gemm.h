@@ -86,6 +86,14 @@ __device__ __forceinline__ void load_lds16(rsrc_t r, uint32_t voff, uint32_t sof
                  : "memory", "m0");
 }
 
+// 4-byte direct-to-LDS load: lane l's dword lands at LDS address dst + 4*l.
+__device__ __forceinline__ void load_lds4(rsrc_t r, uint32_t voff, uint32_t soff, uint32_t dst) {
+    asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dword %0, %1, %2 offen lds"
+                 :
+                 : "v"(voff), "s"(uniform(r)), "s"(soff), "s"(dst)
+                 : "memory", "m0");
+}
+
 // Four consecutive int32 at a uniform address, through the scalar cache
 // (s_load_dwordx4, counted by lgkmcnt rather than vmcnt). The result is not
 // ready until sload_wait() has been passed with the same registers.
@@ -160,6 +168,23 @@ struct RowLoader {
         voff = (uint32_t)r * ldb + (uint32_t)(c << 4);
         lds0 = (uint32_t)(wave * IPW * 1024);
         ksplit = ksplit_;
+    }
+    // Rows [0, ROWS/2) of the tile from `lo`, rows [ROWS/2, ROWS) from `hi`
+    // (nrows_each valid rows in each; every wave's rows lie in one half).
+    __device__ void init_split_rows(const uint16_t *lo, const uint16_t *hi, int64_t ld, int nrows_each) {
+        static_assert((ROWS / 2) % (IPW * 16) == 0, "a wave's rows must lie in one half");
+        const int wave = wave_id();
+        const bool upper = wave * IPW * 16 >= ROWS / 2;
+        const uint32_t bytes = (uint32_t)((int64_t)max(nrows_each, 0) * ld * 2);
+        res = make_rsrc(upper ? hi : lo, bytes);
+        res2 = res;
+        ldb = (uint32_t)(ld * 2);
+        const int L = threadIdx.x & 63;
+        const int r = wave * IPW * 16 + (L >> 2) - (upper ? ROWS / 2 : 0);
+        const int c = (L & 3) ^ ((L >> 3) & 3);
+        voff = (uint32_t)r * ldb + (uint32_t)(c << 4);
+        lds0 = (uint32_t)(wave * IPW * 1024);
+        ksplit = 1 << 30;
     }
     __device__ void issue(int k0, uint32_t tile) const {
         const bool second = k0 >= ksplit;

@@ -18,60 +18,13 @@
 // Every output element is produced by one owner with a fixed reduction order
 // and no floating-point atomics, so results are bitwise reproducible and
 // independent of mini-batch, macro-batch, ring and capacity settings.
-#include <algorithm>
-#include <vector>
-
-#include "gemm.h"
-#include "kernels.h"
-#include "timing.h"
-#include "views.h"
+#include "layer_mx.h"
+#include "layer_parts.h"
 
 namespace mok {
 namespace {
 
 using CfgA = TileCfg<256, 256, 2, 4, 4>;
-
-// ----------------------------------------------------------------------------- tile decode
-
-struct SegTile {
-    MTile mt;
-    int nt;       // n-tile index
-    int slot;     // ring slot of the tile's mini-batch
-    int rowoff;   // first row of the tile inside that mini-batch
-};
-
-constexpr int kXcds = 8;       // MI355X: 8 accelerator dies, each with its own L2
-constexpr int kGroupM = 4;     // m-tiles per group of the tile order
-
-// Tile of a segment GEMM for this workgroup. The 1-D grid (a multiple of 8
-// workgroups, at least the number of tiles) is dispatched round-robin over the
-// XCDs; with `per` = ceil(tiles / 8), workgroup b is mapped to tile
-// t = (b % 8) * per + b / 8 so that each XCD walks a contiguous range of
-// tiles, ordered in groups of kGroupM m-tiles x all n-tiles: the tiles an XCD
-// runs together share few operand slices in its L2.
-__device__ __forceinline__ bool decode_seg_tile(const SchedView &v, int g0, int g1, int64_t n_slots, int n_tiles,
-                                                SegTile &t) {
-    if (*v.status) return false;
-    const int lo = v.mtfirst[g0], mtc = v.mtfirst[g1] - lo;
-    const int total = mtc * n_tiles;                      // tiles that exist (device-side count)
-    const int per = (total + kXcds - 1) / kXcds, b = (int)blockIdx.x;
-    if (b / kXcds >= per) return false;                   // the grid is a host-side upper bound
-    const int id = (b % kXcds) * per + b / kXcds;
-    if (id >= total) return false;
-    const int gsize = kGroupM * n_tiles, grp = id / gsize, first = grp * kGroupM;
-    const int gm = min(kGroupM, mtc - first), r = id % gsize;
-    t.mt = v.mtiles[lo + first + r % gm];
-    t.nt = r / gm;
-    t.slot = (int)(t.mt.g % n_slots);
-    t.rowoff = t.mt.q0 - v.mb_start[t.mt.g];
-    return true;
-}
-
-__device__ __forceinline__ void store4_bf16(uint16_t *p, float a, float b, float c, float d) {
-    *reinterpret_cast<uint2 *>(p) = make_uint2(pack_bf16x2(a, b), pack_bf16x2(c, d));
-}
-
-__device__ __forceinline__ float bf16r(float x) { return bf16_to_f32(f32_to_bf16(x)); }
 
 // ----------------------------------------------------------------------------- forward gate/up
 
@@ -190,38 +143,7 @@ struct Down {
     }
     __device__ int wrow(int wn, int fn) const { return wn * C::WN + fn * 32; }
     __device__ void epilogue(f32x16_t (&acc)[C::FM][C::FN], int wm, int wn) {
-        const int lane = threadIdx.x & 63;
-        const int k = a.k;
-#pragma unroll
-        for (int fm = 0; fm < C::FM; ++fm) {
-            const int m = wm * C::WM + fm * 32 + (lane & 31);
-            if (m >= t.mt.rows) continue;
-            const int q = t.mt.q0 + m;
-            uint16_t *dst;
-            float gw = 1.0f;
-            if (k == 1) {
-                const int tok = a.v.perm[q];
-                gw = a.topk_w[tok];
-                dst = a.out + (int64_t)tok * H;
-            } else {
-                const int64_t base = (int64_t)k * ((t.mt.g / a.nb_full) * (int64_t)a.MT);
-                dst = a.stage + (q - base) * H;
-            }
-#pragma unroll
-            for (int fn = 0; fn < C::FN; ++fn)
-#pragma unroll
-                for (int g4 = 0; g4 < 4; ++g4) {
-                    const int n = n0 + wn * C::WN + fn * 32 + g4 * 8 + (lane >> 5) * 4;
-                    if (n >= H) continue;
-                    float y[4];
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        y[j] = bf16r(acc[fm][fn][g4 * 4 + j]);   // y rows are bf16
-                        if (k == 1) y[j] = gw * y[j];             // weighted combine, one row per token
-                    }
-                    store4_bf16(dst + n, y[0], y[1], y[2], y[3]);
-                }
-        }
+        store_token_rows<C>(acc, t, n0, wm, wn, a.v, H, a.k, a.MT, a.nb_full, a.topk_w, true, a.out, a.stage);
     }
 };
 
@@ -361,30 +283,7 @@ struct DX {
     }
     __device__ int wrow(int wn, int fn) const { return wn * C::WN + fn * 32; }
     __device__ void epilogue(f32x16_t (&acc)[C::FM][C::FN], int wm, int wn) {
-        const int lane = threadIdx.x & 63;
-        const int H = a.H, k = a.k;
-#pragma unroll
-        for (int fm = 0; fm < C::FM; ++fm) {
-            const int m = wm * C::WM + fm * 32 + (lane & 31);
-            if (m >= t.mt.rows) continue;
-            const int q = t.mt.q0 + m;
-            uint16_t *dst;
-            if (k == 1) {
-                dst = a.dx + (int64_t)a.v.perm[q] * H;
-            } else {
-                const int64_t base = (int64_t)k * ((t.mt.g / a.nb_full) * (int64_t)a.MT);
-                dst = a.stage + (q - base) * H;
-            }
-#pragma unroll
-            for (int fn = 0; fn < C::FN; ++fn)
-#pragma unroll
-                for (int g4 = 0; g4 < 4; ++g4) {
-                    const int n = n0 + wn * C::WN + fn * 32 + g4 * 8 + (lane >> 5) * 4;
-                    if (n >= H) continue;
-                    const f32x16_t &v = acc[fm][fn];
-                    store4_bf16(dst + n, v[g4 * 4], v[g4 * 4 + 1], v[g4 * 4 + 2], v[g4 * 4 + 3]);
-                }
-        }
+        store_token_rows<C>(acc, t, n0, wm, wn, a.v, a.H, a.k, a.MT, a.nb_full, nullptr, false, a.dx, a.stage);
     }
 };
 
@@ -511,7 +410,6 @@ struct WD {
 
 // ----------------------------------------------------------------------------- streaming kernels
 
-constexpr int kRowsPerBlock = 4;   // one 64-lane wave per row
 
 // ring[slot(g)][r] = src[token of processing position q] for q in mini-batch g
 __global__ __launch_bounds__(256) void gather_rows(SchedView v, int g0, int64_t n_slots, int MB, int H, int k,
@@ -618,76 +516,30 @@ hipError_t launch_gemm(const char *name, dim3 grid, const typename P::Args &args
     return hipGetLastError();
 }
 
-struct Round {
-    int g0, g1;
-};
-
-// Ring rounds: consecutive mini-batches, at most n_slots per round (distinct
-// slots), not crossing a macro-batch boundary when the combine is staged (k > 1).
-std::vector<Round> make_rounds(const Plan &p, bool reverse) {
-    std::vector<Round> out;
-    const int S = (int)std::min<int64_t>(p.n_slots, (int64_t)p.G);
-    auto add_span = [&](int a, int b) {
-        if (!reverse)
-            for (int g = a; g < b; g += S) out.push_back({g, std::min(b, g + S)});
-        else
-            for (int g = b; g > a; g -= S) out.push_back({std::max(a, g - S), g});
-    };
-    if (p.k == 1) {
-        add_span(0, p.G);
-    } else if (!reverse) {
-        for (int m = 0; m < p.NM; ++m) add_span(first_minibatch(p, m), std::min(p.G, first_minibatch(p, m + 1)));
-    } else {
-        for (int m = p.NM - 1; m >= 0; --m) add_span(first_minibatch(p, m), std::min(p.G, first_minibatch(p, m + 1)));
-    }
-    return out;
-}
-
-int64_t mtile_bound(const Plan &p, Round r) {
-    int64_t q0, q1, a, b;
-    minibatch_rows(p, r.g0, &q0, &a);
-    minibatch_rows(p, r.g1 - 1, &b, &q1);
-    const int64_t nmacro = macro_of_minibatch(p, r.g1 - 1) - macro_of_minibatch(p, r.g0) + 1;
-    const int64_t nseg = std::min<int64_t>(p.cap, (int64_t)(r.g1 - r.g0) + (int64_t)(p.E - 1) * nmacro);
-    return (q1 - q0) / p.tile.BM + nseg + 1;
-}
-
-int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
-
-// 1-D grid for a segment GEMM: n_tiles x m-tile bound, rounded up to whole XCD rounds.
-dim3 seg_grid(int n_tiles, int64_t mt_bound) {
-    return dim3((unsigned)(ceil_div((int64_t)n_tiles * mt_bound, kXcds) * kXcds));
-}
-
-struct Macro {
-    int m;
-    int t0, t1;
-    int64_t base;
-};
-
-Macro macro_info(const Plan &p, int m) {
-    const int64_t t0 = (int64_t)m * p.MT, t1 = std::min<int64_t>(p.T, t0 + p.MT);
-    return Macro{m, (int)t0, (int)t1, (int64_t)p.k * t0};
-}
-
 }  // namespace
 
 mok_status launch_forward(const Plan &p, const void *schedule, void *workspace, const uint16_t *x,
                           const float *topk_w, const mok_weights &w, uint16_t *out, void *fwd_ctx,
                           hipStream_t st) {
     if (p.R == 0) return MOK_OK;
-    if (p.precision != MOK_BF16) return MOK_ERROR_UNSUPPORTED;
+    const bool mx = p.precision == MOK_MXFP8;
+    const bool identity = p.debug & MOK_DEBUG_IDENTITY_EXPERT;
+    if (mx && identity) return MOK_ERROR_UNSUPPORTED;
     const SchedView v = make_sched_view(p, const_cast<void *>(schedule));
     char *ws = static_cast<char *>(workspace);
     uint16_t *ring = reinterpret_cast<uint16_t *>(ws + p.w_ring);
     uint16_t *aring = reinterpret_cast<uint16_t *>(ws + p.w_aring);
     uint16_t *stage = reinterpret_cast<uint16_t *>(ws + p.w_stage);
     uint16_t *h = reinterpret_cast<uint16_t *>(static_cast<char *>(fwd_ctx) + p.c_h);
-    const bool identity = p.debug & MOK_DEBUG_IDENTITY_EXPERT;
     hipError_t err = hipSuccess;
     for (const Round r : make_rounds(p, false)) {
         const dim3 sgrid((unsigned)ceil_div(p.MB, kRowsPerBlock), (unsigned)(r.g1 - r.g0));
-        {
+        if (mx) {
+            if ((err = mx_forward_round(p, v, r.g0, r.g1, mtile_bound(p, r), x, w, ws, h, topk_w, out, stage, st)) !=
+                hipSuccess)
+                break;
+        } else {
+            {
             KernelTimer tm("gather", st);
             gather_rows<<<sgrid, 256, 0, st>>>(v, r.g0, p.n_slots, p.MB, p.H, p.k, x, ring);
         }
@@ -705,6 +557,7 @@ mok_status launch_forward(const Plan &p, const void *schedule, void *workspace, 
                         static_cast<const uint16_t *>(w.w_down), topk_w, out, stage};
             if ((err = launch_gemm<Down<CfgA>>("down", seg_grid(ntd, mt), da, st)) != hipSuccess) break;
         }
+        }
         if (p.k > 1 && (r.g1 == p.G || r.g1 == first_minibatch(p, macro_of_minibatch(p, r.g0) + 1))) {
             const Macro mc = macro_info(p, macro_of_minibatch(p, r.g0));
             KernelTimer tm("combine", st);
@@ -720,7 +573,7 @@ mok_status launch_backward(const Plan &p, const void *schedule, void *workspace,
                            const float *topk_w, const mok_weights &w, const void *fwd_ctx, const uint16_t *dy,
                            uint16_t *dx, uint16_t *dw_gate, uint16_t *dw_up, uint16_t *dw_down, float *dtopk_w,
                            hipStream_t st) {
-    if (p.precision != MOK_BF16) return MOK_ERROR_UNSUPPORTED;
+    const bool mx = p.precision == MOK_MXFP8;
     const SchedView v = make_sched_view(p, const_cast<void *>(schedule));
     char *ws = static_cast<char *>(workspace);
     uint16_t *ring = reinterpret_cast<uint16_t *>(ws + p.w_ring);
@@ -736,6 +589,11 @@ mok_status launch_backward(const Plan &p, const void *schedule, void *workspace,
     if (p.R > 0) {
         for (const Round r : make_rounds(p, true)) {
             const dim3 sgrid((unsigned)ceil_div(p.MB, kRowsPerBlock), (unsigned)(r.g1 - r.g0));
+            if (mx) {
+                if ((err = mx_backward_round(p, v, r.g0, r.g1, mtile_bound(p, r), dy, w, ws, h, topk_w, dx, stage,
+                                             st)) != hipSuccess)
+                    break;
+            } else {
             {
                 KernelTimer tm("gather_dy", st);
                 gather_rows<<<sgrid, 256, 0, st>>>(v, r.g0, p.n_slots, p.MB, p.H, p.k, dy, ring);
@@ -746,6 +604,7 @@ mok_status launch_backward(const Plan &p, const void *schedule, void *workspace,
             if ((err = launch_gemm<DA<CfgA>>("dA", seg_grid(nta, mt), aa, st)) != hipSuccess) break;
             DXArgs xa{v, r.g0, r.g1, ntx, p.n_slots, p.H, p.I, p.k, (int)p.MT, p.nb_full, dh, wg, wu, dx, stage};
             if ((err = launch_gemm<DX<CfgA>>("dX", seg_grid(ntx, mt), xa, st)) != hipSuccess) break;
+            }
             if (p.k > 1 && r.g0 == first_minibatch(p, macro_of_minibatch(p, r.g0))) {
                 const Macro mc = macro_info(p, macro_of_minibatch(p, r.g0));
                 KernelTimer tm("combine_dx", st);

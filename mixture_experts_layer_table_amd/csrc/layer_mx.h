@@ -1,0 +1,24 @@
+// MXFP8 mode of the layer: the per-round launches that differ from BF16
+// (quantizing gathers and the four block-scaled GEMMs). Everything else of a
+// pass (combines, router-gradient reduction, weight gradients) is shared.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include "plan.h"
+#include "views.h"
+
+namespace mok {
+
+// Forward round g0 .. g1-1: gather + quantize x rows into the ring, gate/up
+// GEMM (h -> fwd_ctx, a quantized along I -> the a-ring), down GEMM.
+hipError_t mx_forward_round(const Plan &p, const SchedView &v, int g0, int g1, int64_t mt_bound,
+                            const uint16_t *x, const mok_weights &w, char *ws, uint16_t *h, const float *topk_w,
+                            uint16_t *out, uint16_t *stage, hipStream_t st);
+
+// Backward round g0 .. g1-1: gather + quantize dy rows, dA GEMM with the
+// SwiGLU backward (dh in bf16 and quantized along I), dX GEMM.
+hipError_t mx_backward_round(const Plan &p, const SchedView &v, int g0, int g1, int64_t mt_bound,
+                             const uint16_t *dy, const mok_weights &w, char *ws, const uint16_t *h,
+                             const float *topk_w, uint16_t *dx, uint16_t *stage, hipStream_t st);
+
+}  // namespace mok

@@ -1,0 +1,477 @@
+// MXFP8 mode of the MoE layer ("Mixture-of-Kittens (MoK)" project summary,
+// Overview: BF16 and MXFP8 precision modes; Key-concepts table: MXFP8 weights
+// are pre-quantized). The four input-side GEMMs run on the block-scaled FP8
+// MFMA; every operand is quantized along its contraction axis, 32 values per
+// E8M0 scale:
+//   forward gate/up   x rows (quantized by the ring gather) x W_gate^T | W_up^T
+//   forward down      a (quantized in the gate/up epilogue from its fp32 value) x W_down^T
+//   backward dA       dy rows (quantized by the ring gather) x W_down
+//   backward dX       dh (quantized in the dA epilogue from its fp32 value) x W_gate | W_up
+// h, y, dh (for the weight gradients), dx rows and all outputs stay bf16, and
+// the weight gradients run in BF16 (they have no weight operand).
+//
+// Ring slot (MXFP8): elements [MB][H] then scales [MB][H/32]. a-ring slot
+// (same slot stride as BF16, MB*I*2 bytes): elements [MB][I], scales [MB][I/32].
+// Quantized dh: elements [R][2I], scales [R][2I/32], canonical row order.
+#include "gemm8.h"
+#include "layer_mx.h"
+#include "layer_parts.h"
+#include "mx_codec.h"
+
+namespace mok {
+namespace {
+
+using CfgA = TileCfg<256, 256, 2, 4, 4>;
+using S8 = Fp8Stage<CfgA>;
+
+__device__ __forceinline__ const uint16_t *as_pairs(const uint8_t *p) { return reinterpret_cast<const uint16_t *>(p); }
+
+// ----------------------------------------------------------------------------- quantizing gather
+
+// ring[slot(g)][r] = MXFP8(src[token of processing position q]) along H.
+// One wave per row; lane c handles 8 values, 4 lanes form one 32-block.
+__global__ __launch_bounds__(256) void gather_rows_mx(SchedView v, int g0, int64_t n_slots, int MB, int H, int k,
+                                                      const uint16_t *__restrict__ src, uint8_t *__restrict__ ring) {
+    if (*v.status) return;
+    const int g = g0 + blockIdx.y;
+    const int r = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+    const int q = v.mb_start[g] + r;
+    if (q >= v.mb_start[g + 1]) return;
+    const int tok = v.perm[q] / k;
+    const uint4 *s = reinterpret_cast<const uint4 *>(src + (int64_t)tok * H);
+    uint8_t *slot = ring + (g % n_slots) * (int64_t)MB * (H + H / 32);
+    uint8_t *el = slot + (int64_t)r * H;
+    uint8_t *sc = slot + (int64_t)MB * H + (int64_t)r * (H / 32);
+    for (int c = threadIdx.x & 63; c < H / 8; c += 64) {   // H % 128 == 0: whole 4-lane groups
+        const uint4 xv = s[c];
+        const uint32_t w[4] = {xv.x, xv.y, xv.z, xv.w};
+        uint32_t amax = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) amax = max(amax, max(w[j] & 0x7FFFu, (w[j] >> 16) & 0x7FFFu));
+        amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1));
+        amax = max(amax, (uint32_t)__shfl_xor((int)amax, 2));
+        const uint32_t sb = mx_scale_byte_bf16(amax);
+        const int e = (int)sb - 127;
+        uint32_t o[2];
+#pragma unroll
+        for (int d = 0; d < 2; ++d)
+            o[d] = e4m3_encode_bf16(w[2 * d] & 0xFFFFu, e) | (e4m3_encode_bf16(w[2 * d] >> 16, e) << 8) |
+                   (e4m3_encode_bf16(w[2 * d + 1] & 0xFFFFu, e) << 16) |
+                   (e4m3_encode_bf16(w[2 * d + 1] >> 16, e) << 24);
+        *reinterpret_cast<uint2 *>(el + (int64_t)c * 8) = make_uint2(o[0], o[1]);
+        if ((c & 3) == 0) sc[c >> 2] = (uint8_t)sb;
+    }
+}
+
+// ----------------------------------------------------------------------------- epilogue quantization
+
+// Quantize 16 fp32 values a lane holds of one 32-block (its partner lane
+// l ^ 32 holds the other 16, columns g4*8 + 4*(l/32) + j of the block).
+// Returns the scale byte and, in enc[g4], the 4 codes of columns
+// g4*8 + 4h .. +3. Every lane of the wave must call this (cross-lane
+// exchange). Kept out of line: epilogues call it up to 16 times, and inlining
+// every copy would stop the accumulator loops from unrolling.
+struct Block16 {
+    float v[16];
+};
+struct Enc16 {
+    uint32_t enc[4];
+    uint32_t scale;
+};
+__device__ __attribute__((noinline)) Enc16 quantize_block16(Block16 b) {
+    uint32_t amax = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) amax = max(amax, __float_as_uint(b.v[i]) & 0x7FFFFFFFu);
+    amax = max(amax, (uint32_t)__shfl_xor((int)amax, 32));
+    Enc16 r;
+    r.scale = mx_scale_byte_f32(amax);
+    const int e = (int)r.scale - 127;
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+        uint32_t x = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x |= e4m3_encode_f32(__float_as_uint(b.v[g4 * 4 + j]), e) << (8 * j);
+        r.enc[g4] = x;
+    }
+    return r;
+}
+
+// ----------------------------------------------------------------------------- forward gate/up
+
+struct GateUp8Args {
+    SchedView v;
+    int g0, g1, n_tiles;
+    int64_t n_slots;
+    int MB, H, I;
+    const uint8_t *ring;                       // MXFP8 ring (x rows)
+    const uint8_t *wg, *wgs, *wu, *wus;        // W_gate^T, W_up^T [E][I][H] and scales [E][I][H/32]
+    uint16_t *h;                               // fwd_ctx h [R][2I] bf16, processing order
+    uint8_t *aring;                            // a quantized along I
+};
+
+template <class Cfg>
+struct GateUp8 {
+    using C = Cfg;
+    using Args = GateUp8Args;
+    RowLoader<C, C::BM> xl;
+    RowLoader<C, C::BN> wl;
+    ScaleLoader<C> sl;
+    static constexpr int LOADS_PER_STAGE = RowLoader<C, C::BM>::IPW + RowLoader<C, C::BN>::IPW + 1;
+    SegTile t;
+    int i0, nk;
+    Args a;
+
+    __device__ bool setup(const Args &args) {
+        if (!decode_seg_tile(args.v, args.g0, args.g1, args.n_slots, args.n_tiles, t)) return false;
+        a = args;
+        const int H = args.H, I = args.I;
+        i0 = t.nt * (C::BN / 2);
+        const uint8_t *slot = args.ring + t.slot * (int64_t)args.MB * (H + H / 32);
+        xl.init(as_pairs(slot + (int64_t)t.rowoff * H), H / 2, t.mt.rows);
+        const int64_t eo = (int64_t)t.mt.e * I * H + (int64_t)i0 * H;
+        const int nw = min(C::BN / 2, I - i0);
+        wl.init_split_rows(as_pairs(args.wg + eo), as_pairs(args.wu + eo), H / 2, nw);
+        const int64_t so = (int64_t)t.mt.e * I * (H / 32) + (int64_t)i0 * (H / 32);
+        sl.init(slot + (int64_t)args.MB * H + (int64_t)t.rowoff * (H / 32), t.mt.rows, H / 32, args.wgs + so, nw,
+                H / 32, args.wus + so);
+        nk = H / S8::BK8;
+        return true;
+    }
+    __device__ void issue(int kt, uint32_t stage) {
+        xl.issue(kt * C::BK, stage);
+        wl.issue(kt * C::BK, stage + C::X_BYTES);
+        sl.issue(kt * S8::BK8, stage);
+    }
+    // gate rows of the W tile pair with the up rows BN/2 further inside one wave
+    __device__ int wrow(int wn, int fn) const {
+        return fn < C::FN / 2 ? wn * (C::WN / 2) + fn * 32 : C::BN / 2 + wn * (C::WN / 2) + (fn - C::FN / 2) * 32;
+    }
+    __device__ void epilogue(f32x16_t (&acc)[C::FM][C::FN], int wm, int wn) {
+        const int lane = threadIdx.x & 63, I = a.I;
+        uint8_t *aslot = a.aring + t.slot * (int64_t)a.MB * I * 2;
+#pragma unroll
+        for (int fm = 0; fm < C::FM; ++fm) {
+            const int m = wm * C::WM + fm * 32 + (lane & 31);
+            const bool ok = m < t.mt.rows;   // same for lanes l and l ^ 32
+            const int64_t q = t.mt.q0 + m;
+            uint16_t *hrow = a.h + q * 2 * I;
+            uint8_t *ael = aslot + (int64_t)(t.rowoff + m) * I;
+            uint8_t *asc = aslot + (int64_t)a.MB * I + (int64_t)(t.rowoff + m) * (I / 32);
+#pragma unroll
+            for (int fn = 0; fn < C::FN / 2; ++fn) {
+                const int ib = i0 + wn * (C::WN / 2) + fn * 32;   // one 32-block of i
+                Block16 av;
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const int i = ib + g4 * 8 + (lane >> 5) * 4;
+                    float hg[4], hu[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        hg[j] = acc[fm][fn][g4 * 4 + j];
+                        hu[j] = acc[fm][fn + C::FN / 2][g4 * 4 + j];
+                        av.v[g4 * 4 + j] = hg[j] * sigmoidf_(hg[j]) * hu[j];
+                    }
+                    if (ok) {
+                        store4_bf16(hrow + i, hg[0], hg[1], hg[2], hg[3]);
+                        store4_bf16(hrow + I + i, hu[0], hu[1], hu[2], hu[3]);
+                    }
+                }
+                const Enc16 q8 = quantize_block16(av);
+                if (ok) {
+#pragma unroll
+                    for (int g4 = 0; g4 < 4; ++g4)
+                        *reinterpret_cast<uint32_t *>(ael + ib + g4 * 8 + (lane >> 5) * 4) = q8.enc[g4];
+                    if (lane < 32) asc[ib / 32] = (uint8_t)q8.scale;
+                }
+            }
+        }
+    }
+};
+
+// ----------------------------------------------------------------------------- forward down
+
+struct Down8Args {
+    SchedView v;
+    int g0, g1, n_tiles;
+    int64_t n_slots;
+    int MB, H, I, k, MT, nb_full;
+    const uint8_t *aring;
+    const uint8_t *wd, *wds;                   // W_down^T [E][H][I] and scales [E][H][I/32]
+    const float *topk_w;
+    uint16_t *out, *stage;
+};
+
+template <class Cfg>
+struct Down8 {
+    using C = Cfg;
+    using Args = Down8Args;
+    RowLoader<C, C::BM> xl;
+    RowLoader<C, C::BN> wl;
+    ScaleLoader<C> sl;
+    static constexpr int LOADS_PER_STAGE = RowLoader<C, C::BM>::IPW + RowLoader<C, C::BN>::IPW + 1;
+    SegTile t;
+    int n0, nk;
+    Args a;
+
+    __device__ bool setup(const Args &args) {
+        if (!decode_seg_tile(args.v, args.g0, args.g1, args.n_slots, args.n_tiles, t)) return false;
+        a = args;
+        const int H = args.H, I = args.I;
+        n0 = t.nt * C::BN;
+        const uint8_t *aslot = args.aring + t.slot * (int64_t)args.MB * I * 2;
+        xl.init(as_pairs(aslot + (int64_t)t.rowoff * I), I / 2, t.mt.rows);
+        const int nw = min(C::BN, H - n0);
+        wl.init(as_pairs(args.wd + (int64_t)t.mt.e * H * I + (int64_t)n0 * I), I / 2, nw);
+        sl.init(aslot + (int64_t)args.MB * I + (int64_t)t.rowoff * (I / 32), t.mt.rows, I / 32,
+                args.wds + (int64_t)t.mt.e * H * (I / 32) + (int64_t)n0 * (I / 32), nw, I / 32);
+        nk = I / S8::BK8;
+        return true;
+    }
+    __device__ void issue(int kt, uint32_t stage) {
+        xl.issue(kt * C::BK, stage);
+        wl.issue(kt * C::BK, stage + C::X_BYTES);
+        sl.issue(kt * S8::BK8, stage);
+    }
+    __device__ int wrow(int wn, int fn) const { return wn * C::WN + fn * 32; }
+    __device__ void epilogue(f32x16_t (&acc)[C::FM][C::FN], int wm, int wn) {
+        store_token_rows<C>(acc, t, n0, wm, wn, a.v, a.H, a.k, a.MT, a.nb_full, a.topk_w, true, a.out, a.stage);
+    }
+};
+
+// ----------------------------------------------------------------------------- backward dA
+
+struct DA8Args {
+    SchedView v;
+    int g0, g1, n_tiles;
+    int64_t n_slots;
+    int MB, H, I, S;
+    const uint8_t *ring;                       // MXFP8 ring (dy rows)
+    const uint8_t *wd, *wds;                   // W_down [E][I][H] and scales [E][I][H/32]
+    const uint16_t *h;
+    const float *topk_w;
+    uint16_t *dh, *ga;
+    float *dgp;
+    uint8_t *dhq, *dhqs;
+};
+
+template <class Cfg>
+struct DA8 {
+    using C = Cfg;
+    using Args = DA8Args;
+    RowLoader<C, C::BM> xl;
+    RowLoader<C, C::BN> wl;
+    ScaleLoader<C> sl;
+    static constexpr int LOADS_PER_STAGE = RowLoader<C, C::BM>::IPW + RowLoader<C, C::BN>::IPW + 1;
+    SegTile t;
+    int i0, nk;
+    Args a;
+
+    __device__ bool setup(const Args &args) {
+        if (!decode_seg_tile(args.v, args.g0, args.g1, args.n_slots, args.n_tiles, t)) return false;
+        a = args;
+        const int H = args.H, I = args.I;
+        i0 = t.nt * C::BN;
+        const uint8_t *slot = args.ring + t.slot * (int64_t)args.MB * (H + H / 32);
+        xl.init(as_pairs(slot + (int64_t)t.rowoff * H), H / 2, t.mt.rows);
+        const int nw = min(C::BN, I - i0);
+        wl.init(as_pairs(args.wd + (int64_t)t.mt.e * I * H + (int64_t)i0 * H), H / 2, nw);
+        sl.init(slot + (int64_t)args.MB * H + (int64_t)t.rowoff * (H / 32), t.mt.rows, H / 32,
+                args.wds + (int64_t)t.mt.e * I * (H / 32) + (int64_t)i0 * (H / 32), nw, H / 32);
+        nk = H / S8::BK8;
+        return true;
+    }
+    __device__ void issue(int kt, uint32_t stage) {
+        xl.issue(kt * C::BK, stage);
+        wl.issue(kt * C::BK, stage + C::X_BYTES);
+        sl.issue(kt * S8::BK8, stage);
+    }
+    __device__ int wrow(int wn, int fn) const { return wn * C::WN + fn * 32; }
+    __device__ void epilogue(f32x16_t (&acc)[C::FM][C::FN], int wm, int wn) {
+        const int lane = threadIdx.x & 63;
+        const int I = a.I;
+        const int slice = t.nt * C::WAVES_N + wn;
+        if (i0 + wn * C::WN >= I) return;   // I % 128 == 0: a wave's 64 columns are all valid or none
+#pragma unroll
+        for (int fm = 0; fm < C::FM; ++fm) {
+            const int m = wm * C::WM + fm * 32 + (lane & 31);
+            const bool ok = m < t.mt.rows;
+            const int q = t.mt.q0 + (ok ? m : 0);
+            const int64_t c = t.mt.c0 + (ok ? m : 0);   // dh and g*a rows are kept in canonical order
+            const float gw = a.topk_w[a.v.perm[q]];
+            const uint16_t *hrow = a.h + (int64_t)q * 2 * I;
+            uint16_t *dhrow = a.dh + c * 2 * I;
+            uint16_t *garow = a.ga + c * I;
+            uint8_t *qrow = a.dhq + c * 2 * I;
+            uint8_t *srow = a.dhqs + c * (2 * I / 32);
+            float dg = 0.0f;
+#pragma unroll
+            for (int fn = 0; fn < C::FN; ++fn) {
+                const int ib = i0 + wn * C::WN + fn * 32;   // one 32-block of i
+                Block16 dhg, dhu;
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const int i = ib + g4 * 8 + (lane >> 5) * 4;
+                    const uint2 hg2 = *reinterpret_cast<const uint2 *>(hrow + i);
+                    const uint2 hu2 = *reinterpret_cast<const uint2 *>(hrow + I + i);
+                    const uint32_t hgw[4] = {hg2.x & 0xFFFFu, hg2.x >> 16, hg2.y & 0xFFFFu, hg2.y >> 16};
+                    const uint32_t huw[4] = {hu2.x & 0xFFFFu, hu2.x >> 16, hu2.y & 0xFFFFu, hu2.y >> 16};
+                    float gav[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const float G = acc[fm][fn][g4 * 4 + j];
+                        const float hg = bf16_to_f32(hgw[j]), hu = bf16_to_f32(huw[j]);
+                        const float s = sigmoidf_(hg);
+                        const float sl_ = hg * s;
+                        const float av = sl_ * hu;
+                        dg += G * av;
+                        const float da = gw * G;
+                        dhu.v[g4 * 4 + j] = da * sl_;
+                        dhg.v[g4 * 4 + j] = da * hu * s * (1.0f + hg * (1.0f - s));
+                        gav[j] = gw * av;
+                    }
+                    if (ok) {
+                        store4_bf16(dhrow + i, dhg.v[g4 * 4], dhg.v[g4 * 4 + 1], dhg.v[g4 * 4 + 2], dhg.v[g4 * 4 + 3]);
+                        store4_bf16(dhrow + I + i, dhu.v[g4 * 4], dhu.v[g4 * 4 + 1], dhu.v[g4 * 4 + 2],
+                                    dhu.v[g4 * 4 + 3]);
+                        store4_bf16(garow + i, gav[0], gav[1], gav[2], gav[3]);
+                    }
+                }
+                const Enc16 qg = quantize_block16(dhg);
+                const Enc16 qu = quantize_block16(dhu);
+                if (ok) {
+#pragma unroll
+                    for (int g4 = 0; g4 < 4; ++g4) {
+                        const int i = ib + g4 * 8 + (lane >> 5) * 4;
+                        *reinterpret_cast<uint32_t *>(qrow + i) = qg.enc[g4];
+                        *reinterpret_cast<uint32_t *>(qrow + I + i) = qu.enc[g4];
+                    }
+                    if (lane < 32) {
+                        srow[ib / 32] = (uint8_t)qg.scale;
+                        srow[(I + ib) / 32] = (uint8_t)qu.scale;
+                    }
+                }
+            }
+            // lanes l and l ^ 32 hold the same row: lower half + upper half, fixed order
+            const float other = __shfl_xor(dg, 32);
+            const float tot = (lane < 32) ? dg + other : other + dg;
+            if (ok && lane < 32) a.dgp[(int64_t)q * a.S + slice] = tot;
+        }
+    }
+};
+
+// ----------------------------------------------------------------------------- backward dX
+
+struct DX8Args {
+    SchedView v;
+    int g0, g1, n_tiles;
+    int64_t n_slots;
+    int H, I, k, MT, nb_full;
+    const uint8_t *dhq, *dhqs;
+    const uint8_t *wg, *wgs, *wu, *wus;        // W_gate, W_up [E][H][I] and scales [E][H][I/32]
+    uint16_t *dx, *stage;
+};
+
+template <class Cfg>
+struct DX8 {
+    using C = Cfg;
+    using Args = DX8Args;
+    RowLoader<C, C::BM> xl;
+    RowLoader<C, C::BN> wl;
+    ScaleLoader<C> sl;
+    static constexpr int LOADS_PER_STAGE = RowLoader<C, C::BM>::IPW + RowLoader<C, C::BN>::IPW + 1;
+    SegTile t;
+    int n0, nk;
+    Args a;
+
+    __device__ bool setup(const Args &args) {
+        if (!decode_seg_tile(args.v, args.g0, args.g1, args.n_slots, args.n_tiles, t)) return false;
+        a = args;
+        const int H = args.H, I = args.I;
+        n0 = t.nt * C::BN;
+        xl.init(as_pairs(args.dhq + (int64_t)t.mt.c0 * 2 * I), I, t.mt.rows);   // 2I bytes = I byte pairs
+        const int nw = min(C::BN, H - n0);
+        const int64_t wo = (int64_t)t.mt.e * H * I + (int64_t)n0 * I;
+        wl.init(as_pairs(args.wg + wo), I / 2, nw, as_pairs(args.wu + wo), I / 2);
+        const int64_t so = (int64_t)t.mt.e * H * (I / 32) + (int64_t)n0 * (I / 32);
+        sl.init(args.dhqs + (int64_t)t.mt.c0 * (2 * I / 32), t.mt.rows, 2 * I / 32, args.wgs + so, nw, I / 32, nullptr,
+                args.wus + so, I);
+        nk = 2 * I / S8::BK8;
+        return true;
+    }
+    __device__ void issue(int kt, uint32_t stage) {
+        xl.issue(kt * C::BK, stage);
+        wl.issue(kt * C::BK, stage + C::X_BYTES);
+        sl.issue(kt * S8::BK8, stage);
+    }
+    __device__ int wrow(int wn, int fn) const { return wn * C::WN + fn * 32; }
+    __device__ void epilogue(f32x16_t (&acc)[C::FM][C::FN], int wm, int wn) {
+        store_token_rows<C>(acc, t, n0, wm, wn, a.v, a.H, a.k, a.MT, a.nb_full, nullptr, false, a.dx, a.stage);
+    }
+};
+
+// ----------------------------------------------------------------------------- host side
+
+template <class P>
+hipError_t launch_gemm8(const char *name, dim3 grid, const typename P::Args &args, hipStream_t st) {
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void *)gemm8_kernel<P>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           (int)S8::LDS_BYTES);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    if (grid.x == 0 || grid.y == 0 || grid.z == 0) return hipSuccess;
+    KernelTimer tm(name, st);
+    gemm8_kernel<P><<<grid, CfgA::NT, S8::LDS_BYTES, st>>>(args);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t mx_forward_round(const Plan &p, const SchedView &v, int g0, int g1, int64_t mt_bound,
+                            const uint16_t *x, const mok_weights &w, char *ws, uint16_t *h, const float *topk_w,
+                            uint16_t *out, uint16_t *stage, hipStream_t st) {
+    uint8_t *ring = reinterpret_cast<uint8_t *>(ws + p.w_ring);
+    uint8_t *aring = reinterpret_cast<uint8_t *>(ws + p.w_aring);
+    {
+        const dim3 sgrid((unsigned)ceil_div(p.MB, kRowsPerBlock), (unsigned)(g1 - g0));
+        KernelTimer tm("gather", st);
+        gather_rows_mx<<<sgrid, 256, 0, st>>>(v, g0, p.n_slots, p.MB, p.H, p.k, x, ring);
+    }
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const int ntg = (int)ceil_div(p.I, CfgA::BN / 2), ntd = (int)ceil_div(p.H, CfgA::BN);
+    GateUp8Args ga{v, g0, g1, ntg, p.n_slots, p.MB, p.H, p.I, ring, w.gate_elems, w.gate_scales,
+                   w.up_elems, w.up_scales, h, aring};
+    if ((err = launch_gemm8<GateUp8<CfgA>>("gateup", seg_grid(ntg, mt_bound), ga, st)) != hipSuccess) return err;
+    Down8Args da{v, g0, g1, ntd, p.n_slots, p.MB, p.H, p.I, p.k, (int)p.MT, p.nb_full, aring,
+                 w.down_elems, w.down_scales, topk_w, out, stage};
+    return launch_gemm8<Down8<CfgA>>("down", seg_grid(ntd, mt_bound), da, st);
+}
+
+hipError_t mx_backward_round(const Plan &p, const SchedView &v, int g0, int g1, int64_t mt_bound,
+                             const uint16_t *dy, const mok_weights &w, char *ws, const uint16_t *h,
+                             const float *topk_w, uint16_t *dx, uint16_t *stage, hipStream_t st) {
+    uint8_t *ring = reinterpret_cast<uint8_t *>(ws + p.w_ring);
+    uint16_t *dh = reinterpret_cast<uint16_t *>(ws + p.w_dh);
+    uint16_t *gav = reinterpret_cast<uint16_t *>(ws + p.w_ga);
+    float *dgp = reinterpret_cast<float *>(ws + p.w_dgp);
+    uint8_t *dhq = reinterpret_cast<uint8_t *>(ws + p.w_dhq);
+    uint8_t *dhqs = reinterpret_cast<uint8_t *>(ws + p.w_dhq_scales);
+    {
+        const dim3 sgrid((unsigned)ceil_div(p.MB, kRowsPerBlock), (unsigned)(g1 - g0));
+        KernelTimer tm("gather_dy", st);
+        gather_rows_mx<<<sgrid, 256, 0, st>>>(v, g0, p.n_slots, p.MB, p.H, p.k, dy, ring);
+    }
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const int nta = (int)ceil_div(p.I, CfgA::BN), ntx = (int)ceil_div(p.H, CfgA::BN);
+    DA8Args aa{v, g0, g1, nta, p.n_slots, p.MB, p.H, p.I, p.dg_slices, ring, w.down_elems, w.down_scales, h,
+               topk_w, dh, gav, dgp, dhq, dhqs};
+    if ((err = launch_gemm8<DA8<CfgA>>("dA", seg_grid(nta, mt_bound), aa, st)) != hipSuccess) return err;
+    DX8Args xa{v, g0, g1, ntx, p.n_slots, p.H, p.I, p.k, (int)p.MT, p.nb_full, dhq, dhqs, w.gate_elems,
+               w.gate_scales, w.up_elems, w.up_scales, dx, stage};
+    return launch_gemm8<DX8<CfgA>>("dX", seg_grid(ntx, mt_bound), xa, st);
+}
+
+}  // namespace mok

@@ -42,6 +42,8 @@ struct Plan {
            s_mtiles = 0, s_total = 0;
     // workspace (byte offsets)
     size_t w_ring = 0, w_aring = 0, w_stage = 0, w_dh = 0, w_ga = 0, w_dgp = 0, w_total = 0;
+    // MXFP8 only: dh quantized along I, elements [R][2I] and scales [R][2I/32]
+    size_t w_dhq = 0, w_dhq_scales = 0;
     // fwd_ctx (byte offsets)
     size_t c_h = 0, c_total = 0;
 };

@@ -173,12 +173,18 @@ def token_backward(x_rows, dy_rows, ids_rows, w_rows, expert_w, fq=None):
     return dx, dw
 
 
-def expert_wgrad_columns(xe, dye, g, Wg, Wu, Wd, cols):
+def expert_wgrad_columns(xe, dye, g, Wg, Wu, Wd, cols, fq=None):
     """Columns ``cols`` of dW_gate[e], dW_up[e] ([H, len(cols)]) and rows ``cols`` of
-    dW_down[e] ([len(cols), H]) from all of expert e's rows (xe, dye, g [n,1])."""
-    hg = xe @ Wg[:, cols]
-    hu = xe @ Wu[:, cols]
-    G = dye @ Wd[cols, :].T
+    dW_down[e] ([len(cols), H]) from all of expert e's rows (xe, dye, g [n,1]).
+    ``fq`` as in expert_backward: it reaches the weight gradients only through
+    h (forward product) and G (dA product); the gradient products themselves
+    take unquantized operands. Quantization runs along H, so a column subset
+    of W_gate/W_up or a row subset of W_down quantizes like the whole."""
+    fq = fq or _ident
+    xq = fq(xe, 1)
+    hg = xq @ fq(Wg[:, cols], 0)
+    hu = xq @ fq(Wu[:, cols], 0)
+    G = fq(dye, 1) @ fq(Wd[cols, :], 1).T
     dhg, dhu, _ = swiglu_backward(G, hg, hu, g)
     a = silu(hg) * hu
     return xe.T @ dhg, xe.T @ dhu, (g * a).T @ dye

@@ -11,6 +11,7 @@ from oracle import layer as L
 
 DEV = "cuda:0"
 TOL_BF16 = 1e-2      # relative Frobenius error, per output tensor (per expert for dW)
+TOL_MXFP8 = 6e-2     # same measure, MXFP8 mode against the fake-quant oracle
 
 
 def dev_bf16(bits: np.ndarray) -> torch.Tensor:
@@ -50,11 +51,15 @@ def run_layer(d: DeviceInputs, config: mok.MoKConfig, backward: bool = True):
     ws = mok.get_workspace(config, device=DEV, num_local_tokens=c.T, hidden_size=c.H,
                            intermediate_size=c.I, num_experts=c.E, topk=c.k)
     sched = mok.build_schedule(ws, d.ids)
-    weights = mok.weights_bf16(d.wg, d.wu, d.wd)
-    out, ctx = mok.forward(ws, sched, d.x, d.w, weights)
+    if config.precision == mok.MOK_MXFP8:
+        q = mok.MXFP8Weights(d.wg, d.wu, d.wd)
+        wf, wb = q.fwd, q.bwd
+    else:
+        wf = wb = mok.weights_bf16(d.wg, d.wu, d.wd)
+    out, ctx = mok.forward(ws, sched, d.x, d.w, wf)
     res = dict(out=out, schedule=sched)
     if backward:
-        res.update(mok.backward(ws, sched, ctx, d.x, d.w, weights, d.dy))
+        res.update(mok.backward(ws, sched, ctx, d.x, d.w, wb, d.dy))
     torch.cuda.synchronize()
     return res
 
@@ -63,12 +68,13 @@ def status_word(sched: torch.Tensor) -> int:
     return int(sched[:4].cpu().numpy().view(np.uint32)[0])
 
 
-def oracle_full(inp: synth.LayerInputs):
+def oracle_full(inp: synth.LayerInputs, fq=None):
+    """fp64 oracle of the whole layer; fq = the MXFP8 fake-quant for MXFP8 mode."""
     f = L.bf16_bits_to_f64
     x, dy = f(inp.x), f(inp.dy)
     Wg, Wu, Wd = f(inp.w_gate), f(inp.w_up), f(inp.w_down)
-    out, _ = L.forward(x, inp.topk_ids, inp.topk_w, Wg, Wu, Wd)
-    g = L.backward(x, inp.topk_ids, inp.topk_w, Wg, Wu, Wd, dy)
+    out, _ = L.forward(x, inp.topk_ids, inp.topk_w, Wg, Wu, Wd, fq)
+    g = L.backward(x, inp.topk_ids, inp.topk_w, Wg, Wu, Wd, dy, fq)
     return dict(out=out, dx=g["dx"], dw_gate=g["dWg"], dw_up=g["dWu"], dw_down=g["dWd"], dtopk_w=g["dw"])
 
 

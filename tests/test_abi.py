@@ -107,3 +107,12 @@ def test_single_hip_runtime_in_process():
     maps = open(f"/proc/{os.getpid()}/maps").read()
     hip = {l.split()[-1] for l in maps.splitlines() if "libamdhip64" in l}
     assert len(hip) == 1, hip
+
+
+def test_mxfp8_needs_128_multiples():
+    # the block-scaled GEMMs load four scale bytes (128 values of K) as one aligned dword
+    for H, I in ((128, 64), (192, 128)):
+        with pytest.raises(mok.MokError) as e:
+            mok.query_sizes(mok.MoKConfig(precision=mok.MOK_MXFP8), 64, H, I, 8, 2)
+        assert e.value.status == mok.MOK_ERROR_INVALID_VALUE
+    mok.query_sizes(mok.MoKConfig(precision=mok.MOK_MXFP8), 64, 256, 128, 8, 2)

@@ -7,8 +7,9 @@ import pytest
 import torch
 
 import synth
-from gpu_support import TOL_BF16, DeviceInputs, host_f64, knobs, run_layer, status_word
+from gpu_support import TOL_BF16, TOL_MXFP8, DeviceInputs, host_f64, knobs, run_layer, status_word
 from oracle import layer as L
+from oracle import mxfp8 as M
 
 pytestmark = pytest.mark.gpu
 
@@ -25,6 +26,8 @@ def _sample_tokens(cfg, ids, rng, n=48):
 
 
 def _check(cfg, experts_for_wgrad=2, n_tokens=48):
+    mx = cfg.precision == "mxfp8"
+    fq, tol = (M.fake_quant, TOL_MXFP8) if mx else (None, TOL_BF16)
     print(f"[fullsize] {cfg.name}: generating inputs", flush=True)
     inp = synth.make_inputs(cfg)
     d = DeviceInputs(inp)
@@ -42,8 +45,8 @@ def _check(cfg, experts_for_wgrad=2, n_tokens=48):
         return cache[e]
 
     x, dy = f(inp.x[toks]), f(inp.dy[toks])
-    ref_out = L.token_forward(x, inp.topk_ids[toks], inp.topk_w[toks], ew)
-    ref_dx, ref_dw = L.token_backward(x, dy, inp.topk_ids[toks], inp.topk_w[toks], ew)
+    ref_out = L.token_forward(x, inp.topk_ids[toks], inp.topk_w[toks], ew, fq)
+    ref_dx, ref_dw = L.token_backward(x, dy, inp.topk_ids[toks], inp.topk_w[toks], ew, fq)
     it = torch.from_numpy(toks).to(res["out"].device)
     errs = dict(out=L.rel_frobenius(host_f64(res["out"][it]), ref_out),
                 dx=L.rel_frobenius(host_f64(res["dx"][it]), ref_dx),
@@ -57,13 +60,13 @@ def _check(cfg, experts_for_wgrad=2, n_tokens=48):
         tok = rows // cfg.k
         gw = inp.topk_w.reshape(-1)[rows][:, None].astype(np.float64)
         Wg, Wu, Wd = ew(int(e))
-        a, b, c = L.expert_wgrad_columns(f(inp.x[tok]), f(inp.dy[tok]), gw, Wg, Wu, Wd, cols)
+        a, b, c = L.expert_wgrad_columns(f(inp.x[tok]), f(inp.dy[tok]), gw, Wg, Wu, Wd, cols, fq)
         ic = torch.from_numpy(cols).to(res["out"].device)
         errs[f"dw_gate[{e}]"] = L.rel_frobenius(host_f64(res["dw_gate"][int(e)][:, ic]), a)
         errs[f"dw_up[{e}]"] = L.rel_frobenius(host_f64(res["dw_up"][int(e)][:, ic]), b)
         errs[f"dw_down[{e}]"] = L.rel_frobenius(host_f64(res["dw_down"][int(e)][ic, :]), c)
     print({k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
-    bad = {k: v for k, v in errs.items() if not v <= TOL_BF16}
+    bad = {k: v for k, v in errs.items() if not v <= tol}
     assert not bad, bad
 
 
@@ -78,3 +81,11 @@ def test_stream_macro_batches():
 def test_full_layer():
     # 256 experts: few sampled tokens keep the oracle's weight decoding short
     _check(synth.CONFIGS["full_layer"], n_tokens=6)
+
+
+def test_ep64_share_mxfp8_zipf():
+    _check(synth.CONFIGS["ep64_share_mxfp8"])
+
+
+def test_ep64_share_mxfp8_uniform():
+    _check(synth.CONFIGS["ep64_share_mxfp8_uniform"])

@@ -1,0 +1,59 @@
+"""MXFP8 mode of the layer on the GPU: forward + backward against the fp64
+oracle with the MXFP8 fake-quant at the reading's quantization points
+(relative Frobenius error <= 6e-2), and bitwise reproducibility across runs and
+knob settings."""
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_layer_table_amd as mok
+import synth
+from gpu_support import (TOL_MXFP8, DeviceInputs, compare_full, host_f64, knobs, oracle_full, run_layer,
+                         same_bits, status_word)
+from oracle import layer as L
+from oracle import mxfp8 as M
+
+pytestmark = pytest.mark.gpu
+
+
+def _mx(name, **kw):
+    return synth.small_config(name, precision="mxfp8", **kw)
+
+
+# MXFP8 needs H and I to be multiples of 128; the ring rows are H + H/32 bytes
+SMALL = {
+    "mx_k2_ragged": _mx("mx_k2_ragged", T=300, H=256, I=128, E=5, k=2, minibatch_rows=48, macrobatch_tokens=100,
+                        ring_bytes=3 * 48 * 264),
+    "mx_k1_macro": _mx("mx_k1_macro", T=1000, H=384, I=256, E=3, k=1, minibatch_rows=64, macrobatch_tokens=300,
+                       ring_bytes=4 * 64 * 396, routing="dirichlet"),
+    "mx_wide": _mx("mx_wide", T=520, H=640, I=384, E=2, k=1, minibatch_rows=160, ring_bytes=1 << 22,
+                   routing="zipf"),
+    "mx_k_eq_E": _mx("mx_k_eq_E", T=70, H=128, I=128, E=4, k=4, minibatch_rows=16, ring_bytes=2 * 16 * 132),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_parity_small(name):
+    cfg = SMALL[name]
+    print(f"[mxfp8 layer] parity {name}", flush=True)
+    inp = synth.make_inputs(cfg)
+    res = run_layer(DeviceInputs(inp), knobs(cfg))
+    assert status_word(res["schedule"]) == 0
+    errs = compare_full(res, oracle_full(inp, M.fake_quant), cfg.E, tol=TOL_MXFP8)
+    print("vs fake-quant oracle", {k: f"{v:.2e}" for k, v in errs.items() if not k.startswith("dw_")}, flush=True)
+    plain = oracle_full(inp)                    # reported, not gated: the quantization error itself
+    print("vs unquantized oracle", {n: f"{L.rel_frobenius(host_f64(res[n]), plain[n]):.2e}"
+                                    for n in ("out", "dx", "dtopk_w")}, flush=True)
+
+
+def test_bitwise_deterministic_and_knob_invariant():
+    cfg = SMALL["mx_k2_ragged"]
+    d = DeviceInputs(synth.make_inputs(cfg))
+    first = run_layer(d, knobs(cfg))
+    for _ in range(2):
+        same_bits(first, run_layer(d, knobs(cfg)))
+    for over in (dict(minibatch_rows=16), dict(minibatch_rows=96, ring_bytes=2 * 96 * 264),
+                 dict(macrobatch_tokens=0), dict(ring_bytes=1 << 22), dict(capacity_multiplier=2.0)):
+        print(f"[mxfp8 layer] knobs {over}", flush=True)
+        same_bits(first, run_layer(d, knobs(cfg, **over)))
+

@@ -7,6 +7,7 @@ import torch
 
 import synth
 from oracle import layer as L
+from oracle import mxfp8 as M
 
 
 def _tiny(T=5, H=8, I=4, E=3, k=2, seed=0):
@@ -131,25 +132,26 @@ def test_fused_router_grad_identity():
     assert np.max(np.abs(g["dw"] - g["dw_direct"])) <= 1e-12 * max(1.0, np.max(np.abs(g["dw"])))
 
 
-def test_sampled_forms_match_full():
+@pytest.mark.parametrize("fq", [None, M.fake_quant], ids=["bf16", "mxfp8"])
+def test_sampled_forms_match_full(fq):
     cfg = synth.CONFIGS["tiny"]
     inp = synth.make_inputs(cfg)
     f = L.bf16_bits_to_f64
     x, dy, Wg, Wu, Wd = f(inp.x), f(inp.dy), f(inp.w_gate), f(inp.w_up), f(inp.w_down)
-    out, _ = L.forward(x, inp.topk_ids, inp.topk_w, Wg, Wu, Wd)
-    g = L.backward(x, inp.topk_ids, inp.topk_w, Wg, Wu, Wd, dy)
+    out, _ = L.forward(x, inp.topk_ids, inp.topk_w, Wg, Wu, Wd, fq)
+    g = L.backward(x, inp.topk_ids, inp.topk_w, Wg, Wu, Wd, dy, fq)
     toks = np.array([0, 5, 17, 63])
     ew = lambda e: (Wg[e], Wu[e], Wd[e])
-    o = L.token_forward(x[toks], inp.topk_ids[toks], inp.topk_w[toks], ew)
+    o = L.token_forward(x[toks], inp.topk_ids[toks], inp.topk_w[toks], ew, fq)
     assert np.max(np.abs(o - out[toks])) < 1e-12
-    dx, dw = L.token_backward(x[toks], dy[toks], inp.topk_ids[toks], inp.topk_w[toks], ew)
+    dx, dw = L.token_backward(x[toks], dy[toks], inp.topk_ids[toks], inp.topk_w[toks], ew, fq)
     assert np.max(np.abs(dx - g["dx"][toks])) < 1e-12
     assert np.max(np.abs(dw - g["dw"][toks])) < 1e-12
     e = 3
     rows = np.nonzero(inp.topk_ids.reshape(-1) == e)[0]
     cols = np.array([0, 7, 63])
     gw = inp.topk_w.reshape(-1)[rows][:, None].astype(np.float64)
-    a, b, c = L.expert_wgrad_columns(x[rows // cfg.k], dy[rows // cfg.k], gw, Wg[e], Wu[e], Wd[e], cols)
+    a, b, c = L.expert_wgrad_columns(x[rows // cfg.k], dy[rows // cfg.k], gw, Wg[e], Wu[e], Wd[e], cols, fq)
     assert np.max(np.abs(a - g["dWg"][e][:, cols])) < 1e-12
     assert np.max(np.abs(b - g["dWu"][e][:, cols])) < 1e-12
     assert np.max(np.abs(c - g["dWd"][e][cols, :])) < 1e-12
@@ -160,3 +162,32 @@ def test_bf16_decode():
     v = L.bf16_bits_to_f64(bits)
     assert v[0] == 1.0 and v[1] == -1.0 and v[2] == 0.0 and np.signbit(v[3])
     assert v[4] == (2 - 2 ** -7) * 2.0 ** 127 and v[5] == 2.0 ** -133 and v[6] == 3.140625
+
+
+def test_mxfp8_quantization_points():
+    """The fake-quant hook is applied to exactly the operands the MXFP8 reading
+    names, each along its contraction axis: forward gate/up (x, W_gate, W_up
+    along H), forward down (a, W_down along I), backward dA (dy, W_down along
+    H), backward dX (dh_g, dh_u, W_gate, W_up along I); nothing else."""
+    n, H, I = 3, 64, 32                      # H != I tells the axes apart
+    rng = np.random.default_rng(5)
+    xe, dye = rng.standard_normal((n, H)), rng.standard_normal((n, H))
+    Wg, Wu = rng.standard_normal((H, I)), rng.standard_normal((H, I))
+    Wd = rng.standard_normal((I, H))
+    calls = []
+
+    def spy(a, axis):
+        calls.append((a.shape, a.shape[axis]))
+        return a
+
+    L.expert_forward(xe, Wg, Wu, Wd, spy)
+    fwd = sorted(calls)
+    assert fwd == sorted([((n, H), H), ((H, I), H), ((H, I), H), ((n, I), I), ((I, H), I)])
+    calls.clear()
+    L.expert_backward(xe, dye, np.ones((n, 1)), Wg, Wu, Wd, spy)
+    bwd_only = list(calls)
+    for c in fwd:                            # the recomputed forward quantizes as above
+        bwd_only.remove(c)
+    assert sorted(bwd_only) == sorted([((n, H), H), ((I, H), H),            # dA: dy, W_down along H
+                                       ((n, I), I), ((H, I), I),            # dX: dh_g, W_gate along I
+                                       ((n, I), I), ((H, I), I)])           # dX: dh_u, W_up along I
