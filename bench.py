@@ -52,6 +52,7 @@ WORKLOAD_TEXT = {
 def flops_per_row(H, I):
     """Algorithmic flops per routed row, per kernel (recompute and padding not counted)."""
     return dict(gateup=4 * H * I, down=2 * H * I, dA=2 * H * I, dX=4 * H * I,
+                fwd_gemms=6 * H * I, bwd_gemms=6 * H * I,           # persistent gate/up + down, dA + dX
                 wgrad_gate_up=4 * H * I, wgrad_down=2 * H * I)
 
 
@@ -131,6 +132,8 @@ def main():
     ap.add_argument("--workload", default="ep64_share", choices=list(WORKLOAD_TEXT))
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--separate-launches", action="store_true",
+                    help="one launch per grouped GEMM instead of the persistent pair kernels (per-GEMM timing)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="instead of the layer, run a plain device-to-device copy of this many MiB "
                          "(calibrates the HBM byte counters against a kernel of known traffic)")
@@ -182,7 +185,8 @@ def main():
     else:
         w_fwd = w_bwd = mok.weights_bf16(wg, wu, wd)
     config = mok.MoKConfig(minibatch_rows=cfg.minibatch_rows, macrobatch_tokens=cfg.macrobatch_tokens,
-                           ring_bytes=cfg.ring_bytes, precision=mok.MOK_MXFP8 if mx else mok.MOK_BF16)
+                           ring_bytes=cfg.ring_bytes, precision=mok.MOK_MXFP8 if mx else mok.MOK_BF16,
+                           debug_flags=mok.MOK_DEBUG_SEPARATE_LAUNCHES if args.separate_launches else 0)
     ws = mok.get_workspace(config, device=dev, num_local_tokens=cfg.T, hidden_size=cfg.H,
                            intermediate_size=cfg.I, num_experts=cfg.E, topk=cfg.k)
     sched = torch.empty(ws.schedule_bytes, dtype=torch.uint8, device=dev)
@@ -209,6 +213,7 @@ def main():
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    assert int(sched[:4].cpu().numpy().view(np.uint32)[0]) == 0, "status word set during the timed steps"
     gpu_ms = e0.elapsed_time(e1)
     ms_per_step = max(gpu_ms, wall * 1e3) / args.steps
 
@@ -232,7 +237,7 @@ def main():
             by = (2 * cfg.T * H + 2 * R * H + 4 * R) * nprof / launches   # unique reads + writes
             entry["gbs"] = round(by / (avg * 1e-3) / 1e9, 1)
         kernels[name] = entry
-    fp8_kernels = ("gateup", "down", "dA", "dX") if mx else ()
+    fp8_kernels = ("gateup", "down", "dA", "dX", "fwd_gemms", "bwd_gemms") if mx else ()
     for n in kernels:
         if n in fpr:
             peak = PEAK_FP8_TFLOPS if n in fp8_kernels else PEAK_BF16_TFLOPS

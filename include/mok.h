@@ -55,10 +55,17 @@ typedef enum mok_status {
 /* device status word bits */
 #define MOK_SCHEDULE_OVERFLOW 1u
 #define MOK_BAD_EXPERT_ID 2u
+/* a persistent kernel's work queue made no progress within its spin limit
+   (never expected; outputs are then undefined and the kernel has exited) */
+#define MOK_SCHEDULER_STALLED 4u
 
 /* debug_flags: replace every expert by the identity on its rows (forward only;
    out_t = sum_j g_tj * x_t). Used to test permute followed by unpermute. */
 #define MOK_DEBUG_IDENTITY_EXPERT 1u
+/* debug_flags: run each grouped GEMM of a ring round as its own launch
+   instead of the persistent producer/consumer kernel (same results, bit for
+   bit; used to cross-check the scheduler and to time GEMMs one by one). */
+#define MOK_DEBUG_SEPARATE_LAUNCHES 2u
 
 /*
  * Layer knobs ("Mixture-of-Kittens (MoK)" project summary, Key-concepts table:

@@ -106,7 +106,7 @@ mok_status mok_backward(const mok_config *cfg, const mok_shape *shape, const voi
     Plan p;
     mok_status s = make_plan(cfg, shape, &p);
     if (s != MOK_OK) return s;
-    if (p.debug) return MOK_ERROR_UNSUPPORTED;
+    if (p.debug & MOK_DEBUG_IDENTITY_EXPERT) return MOK_ERROR_UNSUPPORTED;
     if ((s = check_weights(p, w)) != MOK_OK) return s;
     if (!dev_ok(schedule) || !dev_ok(workspace) || !dev_ok(fwd_ctx)) return MOK_ERROR_INVALID_VALUE;
     if (!dev_ok(dw_gate) || !dev_ok(dw_up) || !dev_ok(dw_down)) return MOK_ERROR_INVALID_VALUE;

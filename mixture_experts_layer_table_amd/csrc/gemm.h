@@ -69,6 +69,7 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
 // reads is explicit (wait_vmcnt + lds_barrier in the kernel loop).
 // The descriptor is wave-uniform by construction; readfirstlane states it to
 // the compiler (a no-op when the value already sits in scalar registers).
+__device__ __forceinline__ uint32_t uniform(uint32_t v) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)v); }
 __device__ __forceinline__ rsrc_t uniform(rsrc_t r) {
     rsrc_t u;
     u.x = __builtin_amdgcn_readfirstlane(r.x);
@@ -82,7 +83,7 @@ __device__ __forceinline__ void load_lds16(rsrc_t r, uint32_t voff, uint32_t sof
     // one wait state between the SALU write of M0 and the LDS-DMA read of it (GFX9 hazard)
     asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
                  :
-                 : "v"(voff), "s"(uniform(r)), "s"(soff), "s"(dst)
+                 : "v"(voff), "s"(uniform(r)), "s"(uniform(soff)), "s"(uniform(dst))
                  : "memory", "m0");
 }
 
@@ -90,7 +91,7 @@ __device__ __forceinline__ void load_lds16(rsrc_t r, uint32_t voff, uint32_t sof
 __device__ __forceinline__ void load_lds4(rsrc_t r, uint32_t voff, uint32_t soff, uint32_t dst) {
     asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dword %0, %1, %2 offen lds"
                  :
-                 : "v"(voff), "s"(uniform(r)), "s"(soff), "s"(dst)
+                 : "v"(voff), "s"(uniform(r)), "s"(uniform(soff)), "s"(uniform(dst))
                  : "memory", "m0");
 }
 
@@ -351,9 +352,10 @@ struct Frags {
 
 __device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-// Generic tile kernel. P provides: C, Args, X_TRANS, W_TRANS, LOADS_PER_STAGE
-// (vector-memory instructions one wave issues per stage), setup(args) -> bool,
-// nk, issue(kt, stage_lds_address), wrow(wn, fn), epilogue(acc, wm, wn).
+// One output tile. P provides: C, Args, X_TRANS, W_TRANS, LOADS_PER_STAGE
+// (vector-memory instructions one wave issues per stage), nk,
+// issue(kt, stage_lds_address), wrow(wn, fn), epilogue(acc, wm, wn), and
+// for gemm_kernel setup(args) -> bool.
 //
 // Pipeline of K-step kt (stage = kt % NSTAGE, D = NSTAGE - 1 steps in flight):
 //   read fragments of half-step 1 of stage kt
@@ -367,12 +369,8 @@ __device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0
 // so every LDS read is covered by queued MFMAs, and the barrier sits between
 // two groups of MFMAs (the other wave of the SIMD keeps the matrix core busy).
 template <class P>
-__global__ __launch_bounds__(P::C::NT) void gemm_kernel(typename P::Args args) {
+__device__ __forceinline__ void gemm_tile(P &p, uint32_t lds) {
     using C = typename P::C;
-    extern __shared__ __attribute__((aligned(1024))) char lds_raw[];
-    const uint32_t lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)lds_raw;
-    P p;
-    if (!p.setup(args)) return;
     f32x16_t acc[C::FM][C::FN];
 #pragma unroll
     for (int fm = 0; fm < C::FM; ++fm)
@@ -418,6 +416,16 @@ __global__ __launch_bounds__(P::C::NT) void gemm_kernel(typename P::Args args) {
         __builtin_amdgcn_sched_barrier(0);
     }
     p.epilogue(acc, wm, wn);
+}
+
+// One tile per workgroup; P::setup(args) picks the tile (false: no tile).
+template <class P>
+__global__ __launch_bounds__(P::C::NT) void gemm_kernel(typename P::Args args) {
+    extern __shared__ __attribute__((aligned(1024))) char lds_raw[];
+    const uint32_t lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)lds_raw;
+    P p;
+    if (!p.setup(args)) return;
+    gemm_tile(p, lds);
 }
 
 }  // namespace mok

@@ -115,15 +115,11 @@ __device__ __forceinline__ int scale8(uint32_t area, int row, int kt) {
 //   read W fragments of stage kt + 1 (their latency overlaps the tail of the
 //   MFMAs above and the other wave of the SIMD)
 template <class P>
-__global__ __launch_bounds__(P::C::NT) void gemm8_kernel(typename P::Args args) {
+__device__ __forceinline__ void gemm8_tile(P &p, uint32_t lds) {
     using C = typename P::C;
     using S = Fp8Stage<C>;
     constexpr int FM = C::FM, FN = C::FN, FH = FM / 2;
     static_assert(FM % 2 == 0, "two X halves");
-    extern __shared__ __attribute__((aligned(1024))) char lds_raw[];
-    const uint32_t lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)lds_raw;
-    P p;
-    if (!p.setup(args)) return;
     f32x16_t acc[FM][FN];
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm)
@@ -202,6 +198,15 @@ __global__ __launch_bounds__(P::C::NT) void gemm8_kernel(typename P::Args args) 
         read_w(kt + 1);
     }
     p.epilogue(acc, wm, wn);
+}
+
+template <class P>
+__global__ __launch_bounds__(P::C::NT) void gemm8_kernel(typename P::Args args) {
+    extern __shared__ __attribute__((aligned(1024))) char lds_raw[];
+    const uint32_t lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)lds_raw;
+    P p;
+    if (!p.setup(args)) return;
+    gemm8_tile(p, lds);
 }
 
 }  // namespace mok

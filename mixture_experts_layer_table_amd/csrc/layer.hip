@@ -20,6 +20,7 @@
 // independent of mini-batch, macro-batch, ring and capacity settings.
 #include "layer_mx.h"
 #include "layer_parts.h"
+#include "persist.h"
 
 namespace mok {
 namespace {
@@ -41,6 +42,7 @@ template <class Cfg>
 struct GateUp {
     using C = Cfg;
     using Args = GateUpArgs;
+    static constexpr bool FP8 = false;
     static constexpr bool X_TRANS = false, W_TRANS = true;
     RowLoader<C, C::BM> xl;
     TransLoader<C, C::BN> wl;
@@ -50,7 +52,14 @@ struct GateUp {
     uint16_t *h, *aring;
 
     __device__ bool setup(const Args &a) {
-        if (!decode_seg_tile(a.v, a.g0, a.g1, a.n_slots, a.n_tiles, t)) return false;
+        SegTile tt;
+        if (!decode_seg_tile(a.v, a.g0, a.g1, a.n_slots, a.n_tiles, tt)) return false;
+        init(a, tt);
+        return true;
+    }
+    // the tile's operands, from an m-tile and n-tile chosen by the caller
+    __device__ __forceinline__ void init(const Args &a, const SegTile &tile) {
+        t = tile;
         H = a.H;
         I = a.I;
         MB = a.MB;
@@ -62,7 +71,6 @@ struct GateUp {
         h = a.h;
         aring = a.aring;
         nk = H / C::BK;
-        return true;
     }
     __device__ void issue(int kt, uint32_t tile) {
         xl.issue(kt * C::BK, tile);
@@ -118,6 +126,7 @@ template <class Cfg>
 struct Down {
     using C = Cfg;
     using Args = DownArgs;
+    static constexpr bool FP8 = false;
     static constexpr bool X_TRANS = false, W_TRANS = true;
     RowLoader<C, C::BM> xl;
     TransLoader<C, C::BN> wl;
@@ -127,7 +136,14 @@ struct Down {
     Args a;
 
     __device__ bool setup(const Args &args) {
-        if (!decode_seg_tile(args.v, args.g0, args.g1, args.n_slots, args.n_tiles, t)) return false;
+        SegTile tt;
+        if (!decode_seg_tile(args.v, args.g0, args.g1, args.n_slots, args.n_tiles, tt)) return false;
+        init(args, tt);
+        return true;
+    }
+    // the tile's operands, from an m-tile and n-tile chosen by the caller
+    __device__ __forceinline__ void init(const Args &args, const SegTile &tile) {
+        t = tile;
         a = args;
         H = args.H;
         n0 = t.nt * C::BN;
@@ -135,7 +151,6 @@ struct Down {
         xl.init(args.aring + row0 * args.I, args.I, t.mt.rows);
         wl.init(args.wd + (int64_t)t.mt.e * args.I * H + n0, H, args.I, H - n0);
         nk = args.I / C::BK;
-        return true;
     }
     __device__ void issue(int kt, uint32_t tile) {
         xl.issue(kt * C::BK, tile);
@@ -164,6 +179,7 @@ template <class Cfg>
 struct DA {
     using C = Cfg;
     using Args = DAArgs;
+    static constexpr bool FP8 = false;
     static constexpr bool X_TRANS = false, W_TRANS = false;
     RowLoader<C, C::BM> xl;
     RowLoader<C, C::BN> wl;
@@ -173,7 +189,14 @@ struct DA {
     Args a;
 
     __device__ bool setup(const Args &args) {
-        if (!decode_seg_tile(args.v, args.g0, args.g1, args.n_slots, args.n_tiles, t)) return false;
+        SegTile tt;
+        if (!decode_seg_tile(args.v, args.g0, args.g1, args.n_slots, args.n_tiles, tt)) return false;
+        init(args, tt);
+        return true;
+    }
+    // the tile's operands, from an m-tile and n-tile chosen by the caller
+    __device__ __forceinline__ void init(const Args &args, const SegTile &tile) {
+        t = tile;
         a = args;
         i0 = t.nt * C::BN;
         const int H = args.H, I = args.I;
@@ -181,7 +204,6 @@ struct DA {
         xl.init(args.ring + row0 * H, H, t.mt.rows);
         wl.init(args.wd + (int64_t)t.mt.e * I * H + (int64_t)i0 * H, H, min(C::BN, I - i0));
         nk = H / C::BK;
-        return true;
     }
     __device__ void issue(int kt, uint32_t tile) {
         xl.issue(kt * C::BK, tile);
@@ -257,6 +279,7 @@ template <class Cfg>
 struct DX {
     using C = Cfg;
     using Args = DXArgs;
+    static constexpr bool FP8 = false;
     static constexpr bool X_TRANS = false, W_TRANS = false;
     RowLoader<C, C::BM> xl;
     RowLoader<C, C::BN> wl;
@@ -266,7 +289,14 @@ struct DX {
     Args a;
 
     __device__ bool setup(const Args &args) {
-        if (!decode_seg_tile(args.v, args.g0, args.g1, args.n_slots, args.n_tiles, t)) return false;
+        SegTile tt;
+        if (!decode_seg_tile(args.v, args.g0, args.g1, args.n_slots, args.n_tiles, tt)) return false;
+        init(args, tt);
+        return true;
+    }
+    // the tile's operands, from an m-tile and n-tile chosen by the caller
+    __device__ __forceinline__ void init(const Args &args, const SegTile &tile) {
+        t = tile;
         a = args;
         n0 = t.nt * C::BN;
         I = args.I;
@@ -275,7 +305,6 @@ struct DX {
         const int64_t wo = (int64_t)t.mt.e * H * I + (int64_t)n0 * I;
         wl.init(args.wg + wo, I, min(C::BN, H - n0), args.wu + wo, I);
         nk = 2 * I / C::BK;
-        return true;
     }
     __device__ void issue(int kt, uint32_t tile) {
         xl.issue(kt * C::BK, tile);
@@ -531,6 +560,7 @@ mok_status launch_forward(const Plan &p, const void *schedule, void *workspace, 
     uint16_t *aring = reinterpret_cast<uint16_t *>(ws + p.w_aring);
     uint16_t *stage = reinterpret_cast<uint16_t *>(ws + p.w_stage);
     uint16_t *h = reinterpret_cast<uint16_t *>(static_cast<char *>(fwd_ctx) + p.c_h);
+    int *sync = reinterpret_cast<int *>(ws + p.w_sync);
     hipError_t err = hipSuccess;
     for (const Round r : make_rounds(p, false)) {
         const dim3 sgrid((unsigned)ceil_div(p.MB, kRowsPerBlock), (unsigned)(r.g1 - r.g0));
@@ -552,10 +582,15 @@ mok_status launch_forward(const Plan &p, const void *schedule, void *workspace, 
             const int ntg = (int)ceil_div(p.I, CfgA::BN / 2), ntd = (int)ceil_div(p.H, CfgA::BN);
             GateUpArgs ga{v, r.g0, r.g1, ntg, p.n_slots, p.MB, p.H, p.I, ring,
                           static_cast<const uint16_t *>(w.w_gate), static_cast<const uint16_t *>(w.w_up), h, aring};
-            if ((err = launch_gemm<GateUp<CfgA>>("gateup", seg_grid(ntg, mt), ga, st)) != hipSuccess) break;
             DownArgs da{v, r.g0, r.g1, ntd, p.n_slots, p.MB, p.H, p.I, p.k, (int)p.MT, p.nb_full, aring,
                         static_cast<const uint16_t *>(w.w_down), topk_w, out, stage};
-            if ((err = launch_gemm<Down<CfgA>>("down", seg_grid(ntd, mt), da, st)) != hipSuccess) break;
+            if (p.debug & MOK_DEBUG_SEPARATE_LAUNCHES) {
+                if ((err = launch_gemm<GateUp<CfgA>>("gateup", seg_grid(ntg, mt), ga, st)) != hipSuccess) break;
+                if ((err = launch_gemm<Down<CfgA>>("down", seg_grid(ntd, mt), da, st)) != hipSuccess) break;
+            } else if ((err = launch_pair<GateUp<CfgA>, Down<CfgA>, CfgA::LDS_BYTES>("fwd_gemms", ga, da, sync,
+                                                                                   p.max_mtiles, st)) != hipSuccess) {
+                break;
+            }
         }
         }
         if (p.k > 1 && (r.g1 == p.G || r.g1 == first_minibatch(p, macro_of_minibatch(p, r.g0) + 1))) {
@@ -585,6 +620,7 @@ mok_status launch_backward(const Plan &p, const void *schedule, void *workspace,
     const uint16_t *wg = static_cast<const uint16_t *>(w.w_gate);
     const uint16_t *wu = static_cast<const uint16_t *>(w.w_up);
     const uint16_t *wd = static_cast<const uint16_t *>(w.w_down);
+    int *sync = reinterpret_cast<int *>(ws + p.w_sync);
     hipError_t err = hipSuccess;
     if (p.R > 0) {
         for (const Round r : make_rounds(p, true)) {
@@ -601,9 +637,14 @@ mok_status launch_backward(const Plan &p, const void *schedule, void *workspace,
             const int64_t mt = mtile_bound(p, r);
             const int nta = (int)ceil_div(p.I, CfgA::BN), ntx = (int)ceil_div(p.H, CfgA::BN);
             DAArgs aa{v, r.g0, r.g1, nta, p.n_slots, p.MB, p.H, p.I, p.dg_slices, ring, wd, h, topk_w, dh, ga, dgp};
-            if ((err = launch_gemm<DA<CfgA>>("dA", seg_grid(nta, mt), aa, st)) != hipSuccess) break;
             DXArgs xa{v, r.g0, r.g1, ntx, p.n_slots, p.H, p.I, p.k, (int)p.MT, p.nb_full, dh, wg, wu, dx, stage};
-            if ((err = launch_gemm<DX<CfgA>>("dX", seg_grid(ntx, mt), xa, st)) != hipSuccess) break;
+            if (p.debug & MOK_DEBUG_SEPARATE_LAUNCHES) {
+                if ((err = launch_gemm<DA<CfgA>>("dA", seg_grid(nta, mt), aa, st)) != hipSuccess) break;
+                if ((err = launch_gemm<DX<CfgA>>("dX", seg_grid(ntx, mt), xa, st)) != hipSuccess) break;
+            } else if ((err = launch_pair<DA<CfgA>, DX<CfgA>, CfgA::LDS_BYTES>("bwd_gemms", aa, xa, sync, p.max_mtiles,
+                                                                             st)) != hipSuccess) {
+                break;
+            }
             }
             if (p.k > 1 && r.g0 == first_minibatch(p, macro_of_minibatch(p, r.g0))) {
                 const Macro mc = macro_info(p, macro_of_minibatch(p, r.g0));

@@ -16,6 +16,7 @@
 #include "gemm8.h"
 #include "layer_mx.h"
 #include "layer_parts.h"
+#include "persist.h"
 #include "mx_codec.h"
 
 namespace mok {
@@ -113,6 +114,7 @@ template <class Cfg>
 struct GateUp8 {
     using C = Cfg;
     using Args = GateUp8Args;
+    static constexpr bool FP8 = true;
     RowLoader<C, C::BM> xl;
     RowLoader<C, C::BN> wl;
     ScaleLoader<C> sl;
@@ -122,7 +124,14 @@ struct GateUp8 {
     Args a;
 
     __device__ bool setup(const Args &args) {
-        if (!decode_seg_tile(args.v, args.g0, args.g1, args.n_slots, args.n_tiles, t)) return false;
+        SegTile tt;
+        if (!decode_seg_tile(args.v, args.g0, args.g1, args.n_slots, args.n_tiles, tt)) return false;
+        init(args, tt);
+        return true;
+    }
+    // the tile's operands, from an m-tile and n-tile chosen by the caller
+    __device__ __forceinline__ void init(const Args &args, const SegTile &tile) {
+        t = tile;
         a = args;
         const int H = args.H, I = args.I;
         i0 = t.nt * (C::BN / 2);
@@ -135,7 +144,6 @@ struct GateUp8 {
         sl.init(slot + (int64_t)args.MB * H + (int64_t)t.rowoff * (H / 32), t.mt.rows, H / 32, args.wgs + so, nw,
                 H / 32, args.wus + so);
         nk = H / S8::BK8;
-        return true;
     }
     __device__ void issue(int kt, uint32_t stage) {
         xl.issue(kt * C::BK, stage);
@@ -205,6 +213,7 @@ template <class Cfg>
 struct Down8 {
     using C = Cfg;
     using Args = Down8Args;
+    static constexpr bool FP8 = true;
     RowLoader<C, C::BM> xl;
     RowLoader<C, C::BN> wl;
     ScaleLoader<C> sl;
@@ -214,7 +223,14 @@ struct Down8 {
     Args a;
 
     __device__ bool setup(const Args &args) {
-        if (!decode_seg_tile(args.v, args.g0, args.g1, args.n_slots, args.n_tiles, t)) return false;
+        SegTile tt;
+        if (!decode_seg_tile(args.v, args.g0, args.g1, args.n_slots, args.n_tiles, tt)) return false;
+        init(args, tt);
+        return true;
+    }
+    // the tile's operands, from an m-tile and n-tile chosen by the caller
+    __device__ __forceinline__ void init(const Args &args, const SegTile &tile) {
+        t = tile;
         a = args;
         const int H = args.H, I = args.I;
         n0 = t.nt * C::BN;
@@ -225,7 +241,6 @@ struct Down8 {
         sl.init(aslot + (int64_t)args.MB * I + (int64_t)t.rowoff * (I / 32), t.mt.rows, I / 32,
                 args.wds + (int64_t)t.mt.e * H * (I / 32) + (int64_t)n0 * (I / 32), nw, I / 32);
         nk = I / S8::BK8;
-        return true;
     }
     __device__ void issue(int kt, uint32_t stage) {
         xl.issue(kt * C::BK, stage);
@@ -258,6 +273,7 @@ template <class Cfg>
 struct DA8 {
     using C = Cfg;
     using Args = DA8Args;
+    static constexpr bool FP8 = true;
     RowLoader<C, C::BM> xl;
     RowLoader<C, C::BN> wl;
     ScaleLoader<C> sl;
@@ -267,7 +283,14 @@ struct DA8 {
     Args a;
 
     __device__ bool setup(const Args &args) {
-        if (!decode_seg_tile(args.v, args.g0, args.g1, args.n_slots, args.n_tiles, t)) return false;
+        SegTile tt;
+        if (!decode_seg_tile(args.v, args.g0, args.g1, args.n_slots, args.n_tiles, tt)) return false;
+        init(args, tt);
+        return true;
+    }
+    // the tile's operands, from an m-tile and n-tile chosen by the caller
+    __device__ __forceinline__ void init(const Args &args, const SegTile &tile) {
+        t = tile;
         a = args;
         const int H = args.H, I = args.I;
         i0 = t.nt * C::BN;
@@ -278,7 +301,6 @@ struct DA8 {
         sl.init(slot + (int64_t)args.MB * H + (int64_t)t.rowoff * (H / 32), t.mt.rows, H / 32,
                 args.wds + (int64_t)t.mt.e * I * (H / 32) + (int64_t)i0 * (H / 32), nw, H / 32);
         nk = H / S8::BK8;
-        return true;
     }
     __device__ void issue(int kt, uint32_t stage) {
         xl.issue(kt * C::BK, stage);
@@ -375,6 +397,7 @@ template <class Cfg>
 struct DX8 {
     using C = Cfg;
     using Args = DX8Args;
+    static constexpr bool FP8 = true;
     RowLoader<C, C::BM> xl;
     RowLoader<C, C::BN> wl;
     ScaleLoader<C> sl;
@@ -384,7 +407,14 @@ struct DX8 {
     Args a;
 
     __device__ bool setup(const Args &args) {
-        if (!decode_seg_tile(args.v, args.g0, args.g1, args.n_slots, args.n_tiles, t)) return false;
+        SegTile tt;
+        if (!decode_seg_tile(args.v, args.g0, args.g1, args.n_slots, args.n_tiles, tt)) return false;
+        init(args, tt);
+        return true;
+    }
+    // the tile's operands, from an m-tile and n-tile chosen by the caller
+    __device__ __forceinline__ void init(const Args &args, const SegTile &tile) {
+        t = tile;
         a = args;
         const int H = args.H, I = args.I;
         n0 = t.nt * C::BN;
@@ -396,7 +426,6 @@ struct DX8 {
         sl.init(args.dhqs + (int64_t)t.mt.c0 * (2 * I / 32), t.mt.rows, 2 * I / 32, args.wgs + so, nw, I / 32, nullptr,
                 args.wus + so, I);
         nk = 2 * I / S8::BK8;
-        return true;
     }
     __device__ void issue(int kt, uint32_t stage) {
         xl.issue(kt * C::BK, stage);
@@ -443,9 +472,13 @@ hipError_t mx_forward_round(const Plan &p, const SchedView &v, int g0, int g1, i
     const int ntg = (int)ceil_div(p.I, CfgA::BN / 2), ntd = (int)ceil_div(p.H, CfgA::BN);
     GateUp8Args ga{v, g0, g1, ntg, p.n_slots, p.MB, p.H, p.I, ring, w.gate_elems, w.gate_scales,
                    w.up_elems, w.up_scales, h, aring};
-    if ((err = launch_gemm8<GateUp8<CfgA>>("gateup", seg_grid(ntg, mt_bound), ga, st)) != hipSuccess) return err;
     Down8Args da{v, g0, g1, ntd, p.n_slots, p.MB, p.H, p.I, p.k, (int)p.MT, p.nb_full, aring,
                  w.down_elems, w.down_scales, topk_w, out, stage};
+    if (!(p.debug & MOK_DEBUG_SEPARATE_LAUNCHES))
+        return launch_pair<GateUp8<CfgA>, Down8<CfgA>, S8::LDS_BYTES>("fwd_gemms", ga, da,
+                                                                      reinterpret_cast<int *>(ws + p.w_sync),
+                                                                      p.max_mtiles, st);
+    if ((err = launch_gemm8<GateUp8<CfgA>>("gateup", seg_grid(ntg, mt_bound), ga, st)) != hipSuccess) return err;
     return launch_gemm8<Down8<CfgA>>("down", seg_grid(ntd, mt_bound), da, st);
 }
 
@@ -468,9 +501,13 @@ hipError_t mx_backward_round(const Plan &p, const SchedView &v, int g0, int g1, 
     const int nta = (int)ceil_div(p.I, CfgA::BN), ntx = (int)ceil_div(p.H, CfgA::BN);
     DA8Args aa{v, g0, g1, nta, p.n_slots, p.MB, p.H, p.I, p.dg_slices, ring, w.down_elems, w.down_scales, h,
                topk_w, dh, gav, dgp, dhq, dhqs};
-    if ((err = launch_gemm8<DA8<CfgA>>("dA", seg_grid(nta, mt_bound), aa, st)) != hipSuccess) return err;
     DX8Args xa{v, g0, g1, ntx, p.n_slots, p.H, p.I, p.k, (int)p.MT, p.nb_full, dhq, dhqs, w.gate_elems,
                w.gate_scales, w.up_elems, w.up_scales, dx, stage};
+    if (!(p.debug & MOK_DEBUG_SEPARATE_LAUNCHES))
+        return launch_pair<DA8<CfgA>, DX8<CfgA>, S8::LDS_BYTES>("bwd_gemms", aa, xa,
+                                                                reinterpret_cast<int *>(ws + p.w_sync), p.max_mtiles,
+                                                                st);
+    if ((err = launch_gemm8<DA8<CfgA>>("dA", seg_grid(nta, mt_bound), aa, st)) != hipSuccess) return err;
     return launch_gemm8<DX8<CfgA>>("dX", seg_grid(ntx, mt_bound), xa, st);
 }
 

@@ -1,0 +1,202 @@
+// Persistent producer/consumer scheduling of the two grouped GEMMs of a ring
+// round (forward: gate/up -> down; backward: dA -> dX), in one launch of one
+// workgroup per compute unit.
+//
+// Why ("Mixture-of-Kittens(MoK)란?" explainer, section 4 ②: overlap granularity
+// is chosen per workload; "technical foundation": scheduling inside the kernel
+// rather than by the host): with 256 x 256 tiles a GEMM of the EP-64 share is
+// 2 to 7 waves of tiles over 256 compute units, so a stream of separate
+// launches idles most of the chip during the last partial wave of every
+// GEMM. Here consumer tiles of an m-tile start as soon as that m-tile's
+// producer tiles are done, filling those tails.
+//
+// Work queue. Items of class 1 (producer tiles) and class 2 (consumer tiles)
+// are numbered in the XCD-aware group order of the separate launches and cut
+// into 8 contiguous chunks, one per XCD; a workgroup claims from its own
+// XCD's chunk first and then from the others, producers before consumers.
+// Claim counters are integers in the workspace, taken with atomic add.
+// Completion of a producer tile is published with a release increment of its
+// m-tile's counter (device scope: the write-back of this XCD's L2); a consumer
+// waits until its m-tile's counter is complete, then takes an acquire fence
+// (invalidate of its L2 and L1) before reading what the producers wrote.
+//
+// Deadlock freedom: producers depend on nothing inside the launch, and a
+// consumer tile is claimed only after every producer tile has been claimed,
+// i.e. is running on a resident workgroup that will finish it; a workgroup
+// waiting for its consumer tile's m-tile therefore always waits for work in
+// progress, whatever number of workgroups is resident. (Claiming consumers by
+// fetch-and-add and then waiting, rather than polling for a ready one, keeps
+// the claim itself one atomic per tile.) A poll budget bounds the wait anyway:
+// exhausting it sets MOK_SCHEDULER_STALLED and exits.
+//
+// Results equal those of separate launches bit for bit: every output tile is
+// computed by one workgroup in the same order.
+#pragma once
+#include "gemm8.h"
+#include "layer_parts.h"
+
+namespace mok {
+namespace {
+
+constexpr int kSpinLimit = 1 << 20;   // polls without a claim before giving up
+
+struct PairSync {
+    int *head;   // [2 * kXcds] claimed items of class 1 / 2 per XCD chunk (relative to the chunk start)
+    int *done;   // [m-tiles of the round] finished producer tiles per m-tile
+};
+
+__device__ __forceinline__ int load_relaxed(const int *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// item id -> (m-tile j, n-tile n) in the group order of decode_seg_tile
+__device__ __forceinline__ void item_tile(int id, int nt, int mtc, int &j, int &n) {
+    const int gsize = kGroupM * nt, grp = id / gsize, first = grp * kGroupM;
+    const int gm = min(kGroupM, mtc - first), r = id % gsize;
+    j = first + r % gm;
+    n = r / gm;
+}
+
+struct QueueShape {
+    int mtc, nt1, nt2, n1, n2, per1, per2;
+};
+
+// Thread 0 of a workgroup: claim the next item. Returns its class (0: queue
+// drained or stalled) and sets id. Producer tiles go first, so that the tiles
+// an XCD runs together stay in the lockstep order of a separate launch (their
+// shared operand slices are then read from L2, not HBM); consumer tiles fill
+// the compute units that the producers' last partial wave leaves idle.
+__device__ int claim_item(const PairSync &s, const QueueShape &q, int xcd, uint32_t *status, int &id) {
+    for (int i = 0; i < kXcds; ++i) {
+        const int x = (xcd + i) % kXcds, start = x * q.per1, len = min(q.n1 - start, q.per1);
+        if (load_relaxed(&s.head[x]) >= len) continue;
+        const int h = atomicAdd(&s.head[x], 1);
+        if (h < len) {
+            id = start + h;
+            return 1;
+        }
+    }
+    // Every producer tile is claimed, and each is running on a resident
+    // workgroup: take the next consumer tile and wait for its m-tile.
+    for (int i = 0; i < kXcds; ++i) {
+        const int x = (xcd + i) % kXcds, start = x * q.per2, len = min(q.n2 - start, q.per2);
+        if (load_relaxed(&s.head[kXcds + x]) >= len) continue;
+        const int h = atomicAdd(&s.head[kXcds + x], 1);
+        if (h >= len) continue;
+        int j, n;
+        item_tile(start + h, q.nt2, q.mtc, j, n);
+        int polls = 0;
+        while (load_relaxed(&s.done[j]) < q.nt1) {
+            if (++polls > kSpinLimit) {
+                atomicOr(status, MOK_SCHEDULER_STALLED);
+                return 0;
+            }
+            __builtin_amdgcn_s_sleep(8);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        id = start + h;
+        return 2;
+    }
+    return 0;
+}
+
+template <class P>
+__device__ __forceinline__ void run_tile(P &p, uint32_t lds) {
+    if constexpr (P::FP8)
+        gemm8_tile(p, lds);
+    else
+        gemm_tile(p, lds);
+}
+
+template <class P>
+__device__ __forceinline__ SegTile seg_tile(const SchedView &v, int lo, int j, int n, int64_t n_slots) {
+    SegTile t;
+    t.mt = v.mtiles[lo + j];
+    t.nt = n;
+    t.slot = (int)(t.mt.g % n_slots);
+    t.rowoff = t.mt.q0 - v.mb_start[t.mt.g];
+    return t;
+}
+
+// P1 tiles of m-tile j write what P2 tiles of m-tile j read (all of P1's
+// n-tiles). TILE_LDS: LDS bytes of the larger tile pipeline; two ints after it
+// broadcast the claimed item.
+template <class P1, class P2, size_t TILE_LDS>
+__global__ __launch_bounds__(P1::C::NT) void persist_pair_kernel(typename P1::Args a1, typename P2::Args a2,
+                                                                 PairSync s) {
+    extern __shared__ __attribute__((aligned(1024))) char lds_raw[];
+    const uint32_t lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)lds_raw;
+    int *bcast = reinterpret_cast<int *>(lds_raw + TILE_LDS);
+    const SchedView &v = a1.v;
+    if (*v.status) return;
+    const int lo = v.mtfirst[a1.g0];
+    QueueShape q;
+    q.mtc = v.mtfirst[a1.g1] - lo;
+    q.nt1 = a1.n_tiles;
+    q.nt2 = a2.n_tiles;
+    q.n1 = q.mtc * q.nt1;
+    q.n2 = q.mtc * q.nt2;
+    q.per1 = (q.n1 + kXcds - 1) / kXcds;
+    q.per2 = (q.n2 + kXcds - 1) / kXcds;
+    const int xcd = (int)(blockIdx.x % kXcds);   // workgroups are dispatched round-robin over the XCDs
+    for (;;) {
+        if (threadIdx.x == 0) {
+            int id = 0;
+            const int cls = claim_item(s, q, xcd, v.status, id);
+            bcast[0] = cls;
+            bcast[1] = id;
+        }
+        __syncthreads();
+        const int cls = bcast[0], id = bcast[1];
+        if (cls == 0) return;
+        int j, n;
+        if (cls == 1) {
+            item_tile(id, q.nt1, q.mtc, j, n);
+            P1 p;
+            p.init(a1, seg_tile<P1>(v, lo, j, n, a1.n_slots));
+            run_tile(p, lds);
+        } else {
+            item_tile(id, q.nt2, q.mtc, j, n);
+            P2 p;
+            p.init(a2, seg_tile<P2>(v, lo, j, n, a2.n_slots));
+            run_tile(p, lds);
+        }
+        __syncthreads();   // every wave's stores issued and complete, LDS free for the next tile
+        if (cls == 1 && threadIdx.x == 0) __hip_atomic_fetch_add(&s.done[j], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// Clears the claim and completion counters (a kernel, so that a captured
+// graph replays it).
+__global__ __launch_bounds__(256) void sync_clear(int *p, int n) {
+    for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) p[i] = 0;
+}
+
+inline int device_cu_count() {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        n = 256;
+    return n;
+}
+
+template <class P1, class P2, size_t TILE_LDS>
+hipError_t launch_pair(const char *name, const typename P1::Args &a1, const typename P2::Args &a2, int *sync,
+                       int64_t max_mtiles, hipStream_t st) {
+    constexpr size_t lds_bytes = TILE_LDS + 64;
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void *)persist_pair_kernel<P1, P2, TILE_LDS>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    const int n = kSyncHeads + (int)max_mtiles;
+    sync_clear<<<(unsigned)std::min<int64_t>((n + 255) / 256, 1024), 256, 0, st>>>(sync, n);
+    KernelTimer tm(name, st);
+    persist_pair_kernel<P1, P2, TILE_LDS>
+        <<<(unsigned)device_cu_count(), P1::C::NT, lds_bytes, st>>>(a1, a2, PairSync{sync, sync + kSyncHeads});
+    return hipGetLastError();
+}
+
+}  // namespace
+}  // namespace mok

@@ -41,7 +41,7 @@ mok_status make_plan(const mok_config *cfg, const mok_shape *shape, Plan *p) {
     if (!(cfg->capacity_multiplier > 0.0f && cfg->capacity_multiplier <= 4.0f))
         return MOK_ERROR_INVALID_VALUE;
     if (cfg->precision != MOK_BF16 && cfg->precision != MOK_MXFP8) return MOK_ERROR_INVALID_VALUE;
-    if (cfg->debug_flags & ~MOK_DEBUG_IDENTITY_EXPERT) return MOK_ERROR_INVALID_VALUE;
+    if (cfg->debug_flags & ~(MOK_DEBUG_IDENTITY_EXPERT | MOK_DEBUG_SEPARATE_LAUNCHES)) return MOK_ERROR_INVALID_VALUE;
     // MXFP8 GEMMs load the scale bytes of four 32-blocks as one aligned dword
     if (cfg->precision == MOK_MXFP8 && (s.H % 128 || s.I % 128)) return MOK_ERROR_INVALID_VALUE;
 
@@ -105,6 +105,7 @@ mok_status make_plan(const mok_config *cfg, const mok_shape *shape, Plan *p) {
     q.w_dh = w.take((size_t)q.R * 2 * q.I * 2);
     q.w_ga = w.take((size_t)q.R * q.I * 2);
     q.w_dgp = w.take((size_t)q.R * q.dg_slices * 4);
+    q.w_sync = w.take(4 * (size_t)(kSyncHeads + q.max_mtiles));
     if (q.precision == MOK_MXFP8) {
         q.w_dhq = w.take((size_t)q.R * 2 * q.I);
         q.w_dhq_scales = w.take((size_t)q.R * 2 * q.I / 32);

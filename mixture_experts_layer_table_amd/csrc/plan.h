@@ -12,6 +12,7 @@ namespace mok {
 
 constexpr int kSchedChunk = 1024;   // routed rows per block in the schedule kernels
 constexpr size_t kAlign = 256;      // alignment of every sub-buffer
+constexpr int kSyncHeads = 16;      // claim counters of a persistent kernel: 2 item classes x 8 XCDs
 
 struct Plan {
     // shape
@@ -42,6 +43,9 @@ struct Plan {
            s_mtiles = 0, s_total = 0;
     // workspace (byte offsets)
     size_t w_ring = 0, w_aring = 0, w_stage = 0, w_dh = 0, w_ga = 0, w_dgp = 0, w_total = 0;
+    // persistent-kernel work queues: kSyncHeads claim counters, then one
+    // completion counter per m-tile of a ring round
+    size_t w_sync = 0;
     // MXFP8 only: dh quantized along I, elements [R][2I] and scales [R][2I/32]
     size_t w_dhq = 0, w_dhq_scales = 0;
     // fwd_ctx (byte offsets)

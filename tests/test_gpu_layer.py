@@ -33,7 +33,7 @@ def test_parity_small(name):
     print(f"[layer] parity {name}", flush=True)
     inp = synth.make_inputs(cfg)
     res = run_layer(DeviceInputs(inp), knobs(cfg))
-    assert status_word(res["schedule"]) == 0
+    assert status_word(res["schedule"]) == 0          # includes: the persistent queues never stalled
     errs = compare_full(res, oracle_full(inp), cfg.E)
     print({k: f"{v:.2e}" for k, v in errs.items() if not k.startswith("dw_")}, flush=True)
 
@@ -87,7 +87,8 @@ def test_knobs_do_not_change_bits(name):
     for over in (dict(minibatch_rows=16), dict(minibatch_rows=512, ring_bytes=2 * 512 * row),
                  dict(macrobatch_tokens=0),
                  dict(macrobatch_tokens=7), dict(ring_bytes=2 * cfg.minibatch_rows * row),
-                 dict(ring_bytes=1 << 24), dict(capacity_multiplier=4.0)):
+                 dict(ring_bytes=1 << 24), dict(capacity_multiplier=4.0),
+                 dict(debug_flags=mok.MOK_DEBUG_SEPARATE_LAUNCHES)):
         print(f"[layer] knobs {name} {over}", flush=True)
         same_bits(base, run_layer(d, knobs(cfg, **over)))
 

@@ -53,7 +53,8 @@ def test_bitwise_deterministic_and_knob_invariant():
     for _ in range(2):
         same_bits(first, run_layer(d, knobs(cfg)))
     for over in (dict(minibatch_rows=16), dict(minibatch_rows=96, ring_bytes=2 * 96 * 264),
-                 dict(macrobatch_tokens=0), dict(ring_bytes=1 << 22), dict(capacity_multiplier=2.0)):
+                 dict(macrobatch_tokens=0), dict(ring_bytes=1 << 22), dict(capacity_multiplier=2.0),
+                 dict(debug_flags=mok.MOK_DEBUG_SEPARATE_LAUNCHES)):
         print(f"[mxfp8 layer] knobs {over}", flush=True)
         same_bits(first, run_layer(d, knobs(cfg, **over)))
 
