@@ -53,6 +53,7 @@ def flops_per_row(H, I):
     """Algorithmic flops per routed row, per kernel (recompute and padding not counted)."""
     return dict(gateup=4 * H * I, down=2 * H * I, dA=2 * H * I, dX=4 * H * I,
                 fwd_gemms=6 * H * I, bwd_gemms=6 * H * I,           # persistent gate/up + down, dA + dX
+                fwd_pass=6 * H * I, bwd_pass=6 * H * I,             # whole-pass persistent (gather + both GEMMs)
                 wgrad_gate_up=4 * H * I, wgrad_down=2 * H * I)
 
 
@@ -134,6 +135,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--separate-launches", action="store_true",
                     help="one launch per grouped GEMM instead of the persistent pair kernels (per-GEMM timing)")
+    ap.add_argument("--whole-pass", action="store_true",
+                    help="k == 1: one persistent launch per pass with the in-kernel ring protocol")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="instead of the layer, run a plain device-to-device copy of this many MiB "
                          "(calibrates the HBM byte counters against a kernel of known traffic)")
@@ -186,7 +189,8 @@ def main():
         w_fwd = w_bwd = mok.weights_bf16(wg, wu, wd)
     config = mok.MoKConfig(minibatch_rows=cfg.minibatch_rows, macrobatch_tokens=cfg.macrobatch_tokens,
                            ring_bytes=cfg.ring_bytes, precision=mok.MOK_MXFP8 if mx else mok.MOK_BF16,
-                           debug_flags=mok.MOK_DEBUG_SEPARATE_LAUNCHES if args.separate_launches else 0)
+                           debug_flags=(mok.MOK_DEBUG_SEPARATE_LAUNCHES if args.separate_launches else 0)
+                           | (mok.MOK_DEBUG_WHOLE_PASS if args.whole_pass else 0))
     ws = mok.get_workspace(config, device=dev, num_local_tokens=cfg.T, hidden_size=cfg.H,
                            intermediate_size=cfg.I, num_experts=cfg.E, topk=cfg.k)
     sched = torch.empty(ws.schedule_bytes, dtype=torch.uint8, device=dev)
@@ -237,7 +241,7 @@ def main():
             by = (2 * cfg.T * H + 2 * R * H + 4 * R) * nprof / launches   # unique reads + writes
             entry["gbs"] = round(by / (avg * 1e-3) / 1e9, 1)
         kernels[name] = entry
-    fp8_kernels = ("gateup", "down", "dA", "dX", "fwd_gemms", "bwd_gemms") if mx else ()
+    fp8_kernels = ("gateup", "down", "dA", "dX", "fwd_gemms", "bwd_gemms", "fwd_pass", "bwd_pass") if mx else ()
     for n in kernels:
         if n in fpr:
             peak = PEAK_FP8_TFLOPS if n in fp8_kernels else PEAK_BF16_TFLOPS

@@ -66,6 +66,14 @@ typedef enum mok_status {
    instead of the persistent producer/consumer kernel (same results, bit for
    bit; used to cross-check the scheduler and to time GEMMs one by one). */
 #define MOK_DEBUG_SEPARATE_LAUNCHES 2u
+/* debug_flags (k == 1 only): run each whole forward / dgrad pass as one
+   persistent launch in which gathers and both GEMMs of every ring round
+   follow the in-kernel ring protocol (slot full / release counters) instead
+   of stream order between rounds. Same results, bit for bit. Not the
+   default: on this GPU every cross-XCD handoff inside a kernel costs a
+   device-scope L2 write-back / invalidate, and the measured pass is slower
+   than the gather kernel plus the persistent GEMM pair. */
+#define MOK_DEBUG_WHOLE_PASS 4u
 
 /*
  * Layer knobs ("Mixture-of-Kittens (MoK)" project summary, Key-concepts table:

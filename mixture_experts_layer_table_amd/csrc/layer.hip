@@ -441,17 +441,12 @@ struct WD {
 
 
 // ring[slot(g)][r] = src[token of processing position q] for q in mini-batch g
-__global__ __launch_bounds__(256) void gather_rows(SchedView v, int g0, int64_t n_slots, int MB, int H, int k,
-                                                   const uint16_t *__restrict__ src, uint16_t *__restrict__ ring) {
-    if (*v.status) return;
+__global__ __launch_bounds__(256) void gather_rows(GatherBf16 ga, int g0) {
+    if (*ga.v.status) return;
     const int g = g0 + blockIdx.y;
     const int r = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
-    const int q = v.mb_start[g] + r;
-    if (q >= v.mb_start[g + 1]) return;
-    const int tok = v.perm[q] / k;
-    const uint4 *s = reinterpret_cast<const uint4 *>(src + (int64_t)tok * H);
-    uint4 *d = reinterpret_cast<uint4 *>(ring + ((g % n_slots) * MB + r) * (int64_t)H);
-    for (int c = threadIdx.x & 63; c < H / 8; c += 64) d[c] = s[c];
+    if (ga.v.mb_start[g] + r >= ga.v.mb_start[g + 1]) return;
+    ga.row(g, r);
 }
 
 // Identity experts (debug): y rows = ring rows, then the same combine as the layer.
@@ -545,6 +540,10 @@ hipError_t launch_gemm(const char *name, dim3 grid, const typename P::Args &args
     return hipGetLastError();
 }
 
+bool whole_pass(const Plan &p) {
+    return p.k == 1 && (p.debug & MOK_DEBUG_WHOLE_PASS) && !(p.debug & MOK_DEBUG_SEPARATE_LAUNCHES);
+}
+
 }  // namespace
 
 mok_status launch_forward(const Plan &p, const void *schedule, void *workspace, const uint16_t *x,
@@ -562,6 +561,21 @@ mok_status launch_forward(const Plan &p, const void *schedule, void *workspace, 
     uint16_t *h = reinterpret_cast<uint16_t *>(static_cast<char *>(fwd_ctx) + p.c_h);
     int *sync = reinterpret_cast<int *>(ws + p.w_sync);
     hipError_t err = hipSuccess;
+    if (whole_pass(p) && !identity) {   // one launch for the pass, ring protocol in the kernel
+        if (mx) {
+            err = mx_forward_pass(p, v, x, w, ws, h, topk_w, out, st);
+        } else {
+            const int ntg = (int)ceil_div(p.I, CfgA::BN / 2), ntd = (int)ceil_div(p.H, CfgA::BN);
+            GateUpArgs ga{v, 0, p.G, ntg, p.n_slots, p.MB, p.H, p.I, ring,
+                          static_cast<const uint16_t *>(w.w_gate), static_cast<const uint16_t *>(w.w_up), h, aring};
+            DownArgs da{v, 0, p.G, ntd, p.n_slots, p.MB, p.H, p.I, p.k, (int)p.MT, p.nb_full, aring,
+                        static_cast<const uint16_t *>(w.w_down), topk_w, out, stage};
+            err = launch_pass<GatherBf16, GateUp<CfgA>, Down<CfgA>, 3, CfgA::LDS_BYTES>(
+                "fwd_pass", p, GatherBf16{v, p.n_slots, p.MB, p.H, p.k, x, ring}, ga, da, false, sync, st);
+        }
+        if (err == hipSuccess) err = hipGetLastError();
+        return check_hip(err, "mok_forward");
+    }
     for (const Round r : make_rounds(p, false)) {
         const dim3 sgrid((unsigned)ceil_div(p.MB, kRowsPerBlock), (unsigned)(r.g1 - r.g0));
         if (mx) {
@@ -571,7 +585,7 @@ mok_status launch_forward(const Plan &p, const void *schedule, void *workspace, 
         } else {
             {
             KernelTimer tm("gather", st);
-            gather_rows<<<sgrid, 256, 0, st>>>(v, r.g0, p.n_slots, p.MB, p.H, p.k, x, ring);
+            gather_rows<<<sgrid, 256, 0, st>>>(GatherBf16{v, p.n_slots, p.MB, p.H, p.k, x, ring}, r.g0);
         }
         if (identity) {
             KernelTimer tm("identity", st);
@@ -622,7 +636,21 @@ mok_status launch_backward(const Plan &p, const void *schedule, void *workspace,
     const uint16_t *wd = static_cast<const uint16_t *>(w.w_down);
     int *sync = reinterpret_cast<int *>(ws + p.w_sync);
     hipError_t err = hipSuccess;
-    if (p.R > 0) {
+    if (p.R > 0 && whole_pass(p)) {   // one launch for the dgrad pass
+        if (mx) {
+            err = mx_backward_pass(p, v, dy, w, ws, h, topk_w, dx, st);
+        } else {
+            const int nta = (int)ceil_div(p.I, CfgA::BN), ntx = (int)ceil_div(p.H, CfgA::BN);
+            DAArgs aa{v, 0, p.G, nta, p.n_slots, p.MB, p.H, p.I, p.dg_slices, ring, wd, h, topk_w, dh, ga, dgp};
+            DXArgs xa{v, 0, p.G, ntx, p.n_slots, p.H, p.I, p.k, (int)p.MT, p.nb_full, dh, wg, wu, dx, stage};
+            err = launch_pass<GatherBf16, DA<CfgA>, DX<CfgA>, 2, CfgA::LDS_BYTES>(
+                "bwd_pass", p, GatherBf16{v, p.n_slots, p.MB, p.H, p.k, dy, ring}, aa, xa, true, sync, st);
+        }
+        if (err == hipSuccess) {
+            KernelTimer tm("router_grad", st);
+            reduce_router_grad<<<(unsigned)ceil_div(p.R, 256), 256, 0, st>>>(v, p.dg_slices, dgp, dtopk_w);
+        }
+    } else if (p.R > 0) {
         for (const Round r : make_rounds(p, true)) {
             const dim3 sgrid((unsigned)ceil_div(p.MB, kRowsPerBlock), (unsigned)(r.g1 - r.g0));
             if (mx) {
@@ -632,7 +660,7 @@ mok_status launch_backward(const Plan &p, const void *schedule, void *workspace,
             } else {
             {
                 KernelTimer tm("gather_dy", st);
-                gather_rows<<<sgrid, 256, 0, st>>>(v, r.g0, p.n_slots, p.MB, p.H, p.k, dy, ring);
+                gather_rows<<<sgrid, 256, 0, st>>>(GatherBf16{v, p.n_slots, p.MB, p.H, p.k, dy, ring}, r.g0);
             }
             const int64_t mt = mtile_bound(p, r);
             const int nta = (int)ceil_div(p.I, CfgA::BN), ntx = (int)ceil_div(p.H, CfgA::BN);

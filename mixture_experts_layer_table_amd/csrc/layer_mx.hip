@@ -29,39 +29,117 @@ __device__ __forceinline__ const uint16_t *as_pairs(const uint8_t *p) { return r
 
 // ----------------------------------------------------------------------------- quantizing gather
 
-// ring[slot(g)][r] = MXFP8(src[token of processing position q]) along H.
-// One wave per row; lane c handles 8 values, 4 lanes form one 32-block.
-__global__ __launch_bounds__(256) void gather_rows_mx(SchedView v, int g0, int64_t n_slots, int MB, int H, int k,
-                                                      const uint16_t *__restrict__ src, uint8_t *__restrict__ ring) {
-    if (*v.status) return;
+// Dispatch copy of one row into the MXFP8 ring: one wave quantizes the row of
+// processing position q = mb_start[g] + r along H into ring slot g % n_slots;
+// lane c handles 8 values, 4 lanes form one 32-block.
+struct GatherMx;
+template <int NT>
+__device__ void gather_mx_rows(const GatherMx &ga, int g, int r0, int nrows, const int *tok);
+
+struct GatherMx {
+    SchedView v;
+    int64_t n_slots;
+    int MB, H, k;
+    const uint16_t *src;
+    uint8_t *ring;
+
+    template <int NT>
+    __device__ __forceinline__ void rows(int g, int r0, int nrows, const int *tok) const {
+        gather_mx_rows<NT>(*this, g, r0, nrows, tok);
+    }
+
+    __device__ __forceinline__ void row(int g, int r) const {
+        const int tok = v.perm[v.mb_start[g] + r] / k;
+        const uint4 *s = reinterpret_cast<const uint4 *>(src + (int64_t)tok * H);
+        uint8_t *slot = ring + (g % n_slots) * (int64_t)MB * (H + H / 32);
+        uint8_t *el = slot + (int64_t)r * H;
+        uint8_t *sc = slot + (int64_t)MB * H + (int64_t)r * (H / 32);
+        // H % 128 == 0: whole 4-lane groups; 4 loads in flight per lane before encoding
+        const int n = H / 8, lane = threadIdx.x & 63;
+        for (int c0 = 0; c0 < n; c0 += 64 * 4) {
+            uint4 t[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int c = c0 + i * 64 + lane;
+                t[i] = c < n ? s[c] : make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int c = c0 + i * 64 + lane;
+                if (c0 + i * 64 >= n) break;   // wave-uniform
+                const uint32_t w[4] = {t[i].x, t[i].y, t[i].z, t[i].w};
+                uint32_t amax = 0;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) amax = max(amax, max(w[j] & 0x7FFFu, (w[j] >> 16) & 0x7FFFu));
+                amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1));   // the 4 lanes of a 32-block
+                amax = max(amax, (uint32_t)__shfl_xor((int)amax, 2));
+                const uint32_t sb = mx_scale_byte_bf16(amax);
+                const int e = (int)sb - 127;
+                uint32_t o[2];
+#pragma unroll
+                for (int d = 0; d < 2; ++d)
+                    o[d] = e4m3_encode_bf16(w[2 * d] & 0xFFFFu, e) | (e4m3_encode_bf16(w[2 * d] >> 16, e) << 8) |
+                           (e4m3_encode_bf16(w[2 * d + 1] & 0xFFFFu, e) << 16) |
+                           (e4m3_encode_bf16(w[2 * d + 1] >> 16, e) << 24);
+                if (c < n) {
+                    *reinterpret_cast<uint2 *>(el + (int64_t)c * 8) = make_uint2(o[0], o[1]);
+                    if ((c & 3) == 0) sc[c >> 2] = (uint8_t)sb;
+                }
+            }
+        }
+    }
+};
+
+// Rows [r0, r0 + nrows) of mini-batch g by the whole workgroup (NT threads,
+// a multiple of 64): one flat pass over (row, 8-value chunk) with 8 loads in
+// flight per thread; n = H/8 is a multiple of 16, so the 4 lanes of a
+// 32-block always share a row. tok: the rows' token indices, in LDS.
+template <int NT>
+__device__ void gather_mx_rows(const GatherMx &ga, int g, int r0, int nrows, const int *tok) {
+    const int H = ga.H, n = H / 8, total = nrows * n;
+    uint8_t *slot = ga.ring + (g % ga.n_slots) * (int64_t)ga.MB * (H + H / 32);
+    uint8_t *el = slot + (int64_t)r0 * H;                         // rows are contiguous: chunk e at byte 8e
+    uint8_t *sc = slot + (int64_t)ga.MB * H + (int64_t)r0 * (H / 32);   // block e/4 at byte e/4
+    for (int e0 = 0; e0 < total; e0 += NT * 8) {
+        uint4 t[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int e = e0 + i * NT + (int)threadIdx.x;
+            t[i] = e < total ? reinterpret_cast<const uint4 *>(ga.src + (int64_t)tok[e / n] * H)[e % n]
+                             : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int e = e0 + i * NT + (int)threadIdx.x;
+            if (e0 + i * NT >= total) break;   // workgroup-uniform
+            const uint32_t w[4] = {t[i].x, t[i].y, t[i].z, t[i].w};
+            uint32_t amax = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) amax = max(amax, max(w[j] & 0x7FFFu, (w[j] >> 16) & 0x7FFFu));
+            amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1));
+            amax = max(amax, (uint32_t)__shfl_xor((int)amax, 2));
+            const uint32_t sb = mx_scale_byte_bf16(amax);
+            const int ex = (int)sb - 127;
+            uint32_t o[2];
+#pragma unroll
+            for (int d = 0; d < 2; ++d)
+                o[d] = e4m3_encode_bf16(w[2 * d] & 0xFFFFu, ex) | (e4m3_encode_bf16(w[2 * d] >> 16, ex) << 8) |
+                       (e4m3_encode_bf16(w[2 * d + 1] & 0xFFFFu, ex) << 16) |
+                       (e4m3_encode_bf16(w[2 * d + 1] >> 16, ex) << 24);
+            if (e < total) {
+                *reinterpret_cast<uint2 *>(el + (int64_t)e * 8) = make_uint2(o[0], o[1]);
+                if ((e & 3) == 0) sc[e >> 2] = (uint8_t)sb;
+            }
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void gather_rows_mx(GatherMx ga, int g0) {
+    if (*ga.v.status) return;
     const int g = g0 + blockIdx.y;
     const int r = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
-    const int q = v.mb_start[g] + r;
-    if (q >= v.mb_start[g + 1]) return;
-    const int tok = v.perm[q] / k;
-    const uint4 *s = reinterpret_cast<const uint4 *>(src + (int64_t)tok * H);
-    uint8_t *slot = ring + (g % n_slots) * (int64_t)MB * (H + H / 32);
-    uint8_t *el = slot + (int64_t)r * H;
-    uint8_t *sc = slot + (int64_t)MB * H + (int64_t)r * (H / 32);
-    for (int c = threadIdx.x & 63; c < H / 8; c += 64) {   // H % 128 == 0: whole 4-lane groups
-        const uint4 xv = s[c];
-        const uint32_t w[4] = {xv.x, xv.y, xv.z, xv.w};
-        uint32_t amax = 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) amax = max(amax, max(w[j] & 0x7FFFu, (w[j] >> 16) & 0x7FFFu));
-        amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1));
-        amax = max(amax, (uint32_t)__shfl_xor((int)amax, 2));
-        const uint32_t sb = mx_scale_byte_bf16(amax);
-        const int e = (int)sb - 127;
-        uint32_t o[2];
-#pragma unroll
-        for (int d = 0; d < 2; ++d)
-            o[d] = e4m3_encode_bf16(w[2 * d] & 0xFFFFu, e) | (e4m3_encode_bf16(w[2 * d] >> 16, e) << 8) |
-                   (e4m3_encode_bf16(w[2 * d + 1] & 0xFFFFu, e) << 16) |
-                   (e4m3_encode_bf16(w[2 * d + 1] >> 16, e) << 24);
-        *reinterpret_cast<uint2 *>(el + (int64_t)c * 8) = make_uint2(o[0], o[1]);
-        if ((c & 3) == 0) sc[c >> 2] = (uint8_t)sb;
-    }
+    if (ga.v.mb_start[g] + r >= ga.v.mb_start[g + 1]) return;
+    ga.row(g, r);
 }
 
 // ----------------------------------------------------------------------------- epilogue quantization
@@ -465,7 +543,7 @@ hipError_t mx_forward_round(const Plan &p, const SchedView &v, int g0, int g1, i
     {
         const dim3 sgrid((unsigned)ceil_div(p.MB, kRowsPerBlock), (unsigned)(g1 - g0));
         KernelTimer tm("gather", st);
-        gather_rows_mx<<<sgrid, 256, 0, st>>>(v, g0, p.n_slots, p.MB, p.H, p.k, x, ring);
+        gather_rows_mx<<<sgrid, 256, 0, st>>>(GatherMx{v, p.n_slots, p.MB, p.H, p.k, x, ring}, g0);
     }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
@@ -494,7 +572,7 @@ hipError_t mx_backward_round(const Plan &p, const SchedView &v, int g0, int g1, 
     {
         const dim3 sgrid((unsigned)ceil_div(p.MB, kRowsPerBlock), (unsigned)(g1 - g0));
         KernelTimer tm("gather_dy", st);
-        gather_rows_mx<<<sgrid, 256, 0, st>>>(v, g0, p.n_slots, p.MB, p.H, p.k, dy, ring);
+        gather_rows_mx<<<sgrid, 256, 0, st>>>(GatherMx{v, p.n_slots, p.MB, p.H, p.k, dy, ring}, g0);
     }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
@@ -509,6 +587,36 @@ hipError_t mx_backward_round(const Plan &p, const SchedView &v, int g0, int g1, 
                                                                 st);
     if ((err = launch_gemm8<DA8<CfgA>>("dA", seg_grid(nta, mt_bound), aa, st)) != hipSuccess) return err;
     return launch_gemm8<DX8<CfgA>>("dX", seg_grid(ntx, mt_bound), xa, st);
+}
+
+hipError_t mx_forward_pass(const Plan &p, const SchedView &v, const uint16_t *x, const mok_weights &w, char *ws,
+                           uint16_t *h, const float *topk_w, uint16_t *out, hipStream_t st) {
+    uint8_t *ring = reinterpret_cast<uint8_t *>(ws + p.w_ring);
+    uint8_t *aring = reinterpret_cast<uint8_t *>(ws + p.w_aring);
+    const int ntg = (int)ceil_div(p.I, CfgA::BN / 2), ntd = (int)ceil_div(p.H, CfgA::BN);
+    GateUp8Args ga{v, 0, p.G, ntg, p.n_slots, p.MB, p.H, p.I, ring, w.gate_elems, w.gate_scales,
+                   w.up_elems, w.up_scales, h, aring};
+    Down8Args da{v, 0, p.G, ntd, p.n_slots, p.MB, p.H, p.I, p.k, (int)p.MT, p.nb_full, aring,
+                 w.down_elems, w.down_scales, topk_w, out, nullptr};
+    return launch_pass<GatherMx, GateUp8<CfgA>, Down8<CfgA>, 3, S8::LDS_BYTES>(
+        "fwd_pass", p, GatherMx{v, p.n_slots, p.MB, p.H, p.k, x, ring}, ga, da, false,
+        reinterpret_cast<int *>(ws + p.w_sync), st);
+}
+
+hipError_t mx_backward_pass(const Plan &p, const SchedView &v, const uint16_t *dy, const mok_weights &w, char *ws,
+                            const uint16_t *h, const float *topk_w, uint16_t *dx, hipStream_t st) {
+    uint8_t *ring = reinterpret_cast<uint8_t *>(ws + p.w_ring);
+    const int nta = (int)ceil_div(p.I, CfgA::BN), ntx = (int)ceil_div(p.H, CfgA::BN);
+    DA8Args aa{v, 0, p.G, nta, p.n_slots, p.MB, p.H, p.I, p.dg_slices, ring, w.down_elems, w.down_scales, h,
+               topk_w, reinterpret_cast<uint16_t *>(ws + p.w_dh), reinterpret_cast<uint16_t *>(ws + p.w_ga),
+               reinterpret_cast<float *>(ws + p.w_dgp), reinterpret_cast<uint8_t *>(ws + p.w_dhq),
+               reinterpret_cast<uint8_t *>(ws + p.w_dhq_scales)};
+    DX8Args xa{v, 0, p.G, ntx, p.n_slots, p.H, p.I, p.k, (int)p.MT, p.nb_full,
+               reinterpret_cast<uint8_t *>(ws + p.w_dhq), reinterpret_cast<uint8_t *>(ws + p.w_dhq_scales),
+               w.gate_elems, w.gate_scales, w.up_elems, w.up_scales, dx, nullptr};
+    return launch_pass<GatherMx, DA8<CfgA>, DX8<CfgA>, 2, S8::LDS_BYTES>(
+        "bwd_pass", p, GatherMx{v, p.n_slots, p.MB, p.H, p.k, dy, ring}, aa, xa, true,
+        reinterpret_cast<int *>(ws + p.w_sync), st);
 }
 
 }  // namespace mok

@@ -99,6 +99,61 @@ __device__ __forceinline__ void store_token_rows(const f32x16_t (&acc)[C::FM][C:
 
 constexpr int kRowsPerBlock = 4;   // one 64-lane wave per row
 
+// Dispatch copy of one row (bf16 ring): one wave moves the row of processing
+// position q = mb_start[g] + r from token order into ring slot g % n_slots.
+struct GatherBf16 {
+    SchedView v;
+    int64_t n_slots;
+    int MB, H, k;
+    const uint16_t *src;
+    uint16_t *ring;
+
+    // 8 loads in flight per lane before the stores: a wave moving rows one
+    // after the other is otherwise bound by one memory round trip per 1 KiB.
+    __device__ __forceinline__ void row(int g, int r) const {
+        const int tok = v.perm[v.mb_start[g] + r] / k;
+        const uint4 *s = reinterpret_cast<const uint4 *>(src + (int64_t)tok * H);
+        uint4 *d = reinterpret_cast<uint4 *>(ring + ((g % n_slots) * MB + r) * (int64_t)H);
+        const int n = H / 8, lane = threadIdx.x & 63;
+        for (int c0 = 0; c0 < n; c0 += 64 * 8) {
+            uint4 t[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int c = c0 + i * 64 + lane;
+                t[i] = c < n ? s[c] : make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int c = c0 + i * 64 + lane;
+                if (c < n) d[c] = t[i];
+            }
+        }
+    }
+
+    // Rows [r0, r0 + nrows) of mini-batch g by the whole workgroup (nt threads):
+    // one flat pass over (row, 16-byte chunk) with 16 loads in flight per
+    // thread. tok: the rows' token indices, already in LDS.
+    template <int NT>
+    __device__ __forceinline__ void rows(int g, int r0, int nrows, const int *tok) const {
+        const int n = H / 8, total = nrows * n;
+        uint4 *dslot = reinterpret_cast<uint4 *>(ring + ((g % n_slots) * MB + r0) * (int64_t)H);
+        for (int e0 = 0; e0 < total; e0 += NT * 16) {
+            uint4 t[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int e = e0 + i * NT + (int)threadIdx.x;
+                t[i] = e < total ? reinterpret_cast<const uint4 *>(src + (int64_t)tok[e / n] * H)[e % n]
+                                 : make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int e = e0 + i * NT + (int)threadIdx.x;
+                if (e < total) dslot[e] = t[i];   // slot rows are contiguous: element e at row e / n, chunk e % n
+            }
+        }
+    }
+};
+
 struct Round {
     int g0, g1;
 };

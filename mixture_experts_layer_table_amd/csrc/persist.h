@@ -166,6 +166,186 @@ __global__ __launch_bounds__(P1::C::NT) void persist_pair_kernel(typename P1::Ar
     }
 }
 
+// ----------------------------------------------------------------------------- whole pass (k == 1)
+
+// One launch for a whole pass when every token has one routed row: the ring
+// rounds run back to back through the ring protocol instead of stream order
+// ("Mixture-of-Kittens(MoK)란?" explainer, section 4 ③: a fixed ring of
+// mini-batch slots, reused without the host).
+//
+// Items, in one global order (round r = 0 .. NR-1, rounds of S mini-batches
+// ascending in the forward pass and descending in the backward pass):
+//   segment 3r     gather items: 64 rows of one mini-batch g into slot g % n_slots
+//   segment 3r + 1 producer tiles of the round's m-tiles (gate/up, or dA)
+//   segment 3r + 2 consumer tiles of the round's m-tiles (down, or dX)
+// Ring protocol, integers in the workspace:
+//   full[r]      gather items of round r done  (producer tiles of round r wait
+//                for all of them, so that a workgroup takes one acquire fence
+//                per round instead of one per tile: each fence empties its
+//                XCD's L2, which the tiles running there share)
+//   done[m]      producer tiles of m-tile m done (its consumer tiles wait for all)
+//   used[g]      slot-reading tiles of g done  (the last one releases the slot)
+//   released[s]  mini-batches that have left slot s; a gather item of round r
+//                waits until released[s] >= r (each earlier round held one
+//                mini-batch in every slot)
+// The slot-reading tiles are the consumers in the forward pass (down reads the
+// a-ring) and the producers in the backward pass (dA reads the dy ring).
+//
+// A workgroup claims from segment s only after it has seen every item of the
+// segments before s claimed; every item depends only on items of earlier
+// segments, which are therefore running on resident workgroups or done, so
+// every wait ends (by induction over the order), whatever number of
+// workgroups is resident.
+struct PassSync {
+    int *head;       // [3 * NR * kXcds] claimed items per segment and XCD chunk
+    int *full;       // [NR]
+    int *used;       // [G]
+    int *released;   // [min(n_slots, G)]
+    int *done;       // [m-tiles]
+};
+
+struct PassShape {
+    int G, S, NR, cpm;   // mini-batches, per round, rounds, gather items per mini-batch
+    bool reverse;
+};
+
+constexpr int kGatherRows = 64;   // rows per gather item (8 waves x 8 rows)
+
+__device__ __forceinline__ void round_span(const PassShape &ps, int r, int &a, int &b) {
+    if (!ps.reverse) {
+        a = r * ps.S;
+        b = min(ps.G, a + ps.S);
+    } else {
+        b = ps.G - r * ps.S;
+        a = max(0, b - ps.S);
+    }
+}
+
+struct PassItem {
+    int kind;   // 0 none, 1 gather, 2 producer, 3 consumer
+    int a, b;   // (gather) mini-batch, row chunk; (tiles) m-tile (global index), n-tile
+    int round;
+};
+
+__device__ __forceinline__ bool wait_at_least(const int *p, int target, uint32_t *status) {
+    int polls = 0;
+    while (load_relaxed(p) < target) {
+        if (++polls > kSpinLimit) {
+            atomicOr(status, MOK_SCHEDULER_STALLED);
+            return false;
+        }
+        __builtin_amdgcn_s_sleep(8);
+    }
+    return true;
+}
+
+// Thread 0: claim the next item at or after segment `seg` and wait for its inputs.
+__device__ PassItem claim_pass_item(const PassSync &s, const PassShape &ps, const SchedView &v, int nt1, int nt2,
+                                    int64_t n_slots, int xcd, int &seg, int &acq_round) {
+    PassItem it{0, 0, 0, 0};
+    for (; seg < 3 * ps.NR; ++seg) {
+        const int r = seg / 3, c = seg % 3;
+        int a, b;
+        round_span(ps, r, a, b);
+        int *head = s.head + seg * kXcds;
+        if (c == 0) {
+            const int n = (b - a) * ps.cpm;
+            if (load_relaxed(head) >= n) continue;
+            const int h = atomicAdd(head, 1);
+            if (h >= n) continue;
+            const int g = a + h / ps.cpm;
+            if (!wait_at_least(&s.released[g % n_slots], r, v.status)) return it;
+            it = PassItem{1, g, h % ps.cpm, r};
+            return it;
+        }
+        const int lo = v.mtfirst[a], mtc = v.mtfirst[b] - lo, nt = c == 1 ? nt1 : nt2;
+        const int n = mtc * nt, per = (n + kXcds - 1) / kXcds;
+        for (int i = 0; i < kXcds; ++i) {
+            const int x = (xcd + i) % kXcds, start = x * per, len = min(n - start, per);
+            if (load_relaxed(&head[x]) >= len) continue;
+            const int h = atomicAdd(&head[x], 1);
+            if (h >= len) continue;
+            int j, nn;
+            item_tile(start + h, nt, mtc, j, nn);
+            if (c == 1) {
+                if (acq_round < r) {   // first producer tile of this round on this workgroup
+                    if (!wait_at_least(&s.full[r], (b - a) * ps.cpm, v.status)) return it;
+                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+                    acq_round = r;
+                }
+            } else {
+                if (!wait_at_least(&s.done[lo + j], nt1, v.status)) return it;
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            }
+            it = PassItem{c == 1 ? 2 : 3, lo + j, nn, r};
+            return it;
+        }
+    }
+    return it;
+}
+
+// GA: the dispatch copy (row(g, r) by one wave); P1 -> P2 as in persist_pair_kernel;
+// RELEASE: the class (2 producer, 3 consumer) whose tiles are the last readers of a slot.
+template <class GA, class P1, class P2, int RELEASE, size_t TILE_LDS>
+__global__ __launch_bounds__(P1::C::NT) void persist_pass_kernel(GA ga, typename P1::Args a1, typename P2::Args a2,
+                                                                 PassSync s, PassShape ps) {
+    extern __shared__ __attribute__((aligned(1024))) char lds_raw[];
+    const uint32_t lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)lds_raw;
+    int *bcast = reinterpret_cast<int *>(lds_raw + TILE_LDS);
+    const SchedView &v = a1.v;
+    if (*v.status) return;
+    const int xcd = (int)(blockIdx.x % kXcds);
+    const int64_t n_slots = a1.n_slots;
+    int seg = 0;          // thread 0's claim cursor
+    int acq_round = -1;   // last round whose gathers thread 0 has acquired
+    for (;;) {
+        if (threadIdx.x == 0) {
+            const PassItem it = claim_pass_item(s, ps, v, a1.n_tiles, a2.n_tiles, n_slots, xcd, seg, acq_round);
+            bcast[0] = it.kind;
+            bcast[1] = it.a;
+            bcast[2] = it.b;
+            bcast[3] = it.round;
+        }
+        __syncthreads();
+        const int kind = bcast[0], ia = bcast[1], ib = bcast[2];
+        if (kind == 0) return;
+        if (kind == 1) {
+            const int r0 = ib * kGatherRows;
+            const int nrows = max(0, min(kGatherRows, v.mb_start[ia + 1] - v.mb_start[ia] - r0));
+            int *tok = bcast + 16;   // kGatherRows token indices
+            if ((int)threadIdx.x < nrows) tok[threadIdx.x] = v.perm[v.mb_start[ia] + r0 + threadIdx.x] / ga.k;
+            __syncthreads();
+            ga.template rows<P1::C::NT>(ia, r0, nrows, tok);
+        } else if (kind == 2) {
+            P1 p;
+            const MTile mt = v.mtiles[ia];
+            p.init(a1, SegTile{mt, ib, (int)(mt.g % n_slots), mt.q0 - v.mb_start[mt.g]});
+            run_tile(p, lds);
+        } else {
+            P2 p;
+            const MTile mt = v.mtiles[ia];
+            p.init(a2, SegTile{mt, ib, (int)(mt.g % n_slots), mt.q0 - v.mb_start[mt.g]});
+            run_tile(p, lds);
+        }
+        __syncthreads();   // every wave's stores complete, LDS free for the next item
+        if (threadIdx.x == 0) {
+            if (kind == 1) {
+                __hip_atomic_fetch_add(&s.full[bcast[3]], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            } else {
+                if (kind == 2) __hip_atomic_fetch_add(&s.done[ia], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+                if (kind == RELEASE) {
+                    const int g = v.mtiles[ia].g;
+                    const int expect = (v.mtfirst[g + 1] - v.mtfirst[g]) * (kind == 2 ? a1.n_tiles : a2.n_tiles);
+                    const int prev = __hip_atomic_fetch_add(&s.used[g], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+                    if (prev + 1 == expect)
+                        __hip_atomic_fetch_add(&s.released[g % n_slots], 1, __ATOMIC_RELEASE,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+                }
+            }
+        }
+    }
+}
+
 // Clears the claim and completion counters (a kernel, so that a captured
 // graph replays it).
 __global__ __launch_bounds__(256) void sync_clear(int *p, int n) {
@@ -177,6 +357,47 @@ inline int device_cu_count() {
     if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
         n = 256;
     return n;
+}
+
+// Sync-area layout of the whole-pass kernel, in ints.
+struct PassLayout {
+    int NR, S, cpm, slots, total;
+    int head, full, used, released, done;
+};
+inline PassLayout pass_layout(const Plan &p) {
+    PassLayout l;
+    l.S = (int)std::min<int64_t>(p.n_slots, (int64_t)p.G);
+    l.NR = p.G == 0 ? 0 : (p.G + l.S - 1) / l.S;
+    l.cpm = (p.MB + kGatherRows - 1) / kGatherRows;
+    l.slots = l.S;
+    l.head = 0;
+    l.full = l.head + 3 * l.NR * kXcds;
+    l.used = l.full + l.NR;
+    l.released = l.used + p.G;
+    l.done = l.released + l.slots;
+    l.total = l.done + (int)p.max_mtiles;
+    return l;
+}
+
+template <class GA, class P1, class P2, int RELEASE, size_t TILE_LDS>
+hipError_t launch_pass(const char *name, const Plan &p, const GA &ga, const typename P1::Args &a1,
+                       const typename P2::Args &a2, bool reverse, int *sync, hipStream_t st) {
+    constexpr size_t lds_bytes = TILE_LDS + 64 + 4 * kGatherRows;   // claim broadcast, gather token ids
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void *)persist_pass_kernel<GA, P1, P2, RELEASE, TILE_LDS>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    const PassLayout l = pass_layout(p);
+    sync_clear<<<(unsigned)std::min<int64_t>((l.total + 255) / 256, 1024), 256, 0, st>>>(sync, l.total);
+    const PassSync s{sync + l.head, sync + l.full, sync + l.used, sync + l.released, sync + l.done};
+    const PassShape ps{p.G, l.S, l.NR, l.cpm, reverse};
+    KernelTimer tm(name, st);
+    persist_pass_kernel<GA, P1, P2, RELEASE, TILE_LDS>
+        <<<(unsigned)device_cu_count(), P1::C::NT, lds_bytes, st>>>(ga, a1, a2, s, ps);
+    return hipGetLastError();
 }
 
 template <class P1, class P2, size_t TILE_LDS>

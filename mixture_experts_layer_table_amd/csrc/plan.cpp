@@ -41,7 +41,8 @@ mok_status make_plan(const mok_config *cfg, const mok_shape *shape, Plan *p) {
     if (!(cfg->capacity_multiplier > 0.0f && cfg->capacity_multiplier <= 4.0f))
         return MOK_ERROR_INVALID_VALUE;
     if (cfg->precision != MOK_BF16 && cfg->precision != MOK_MXFP8) return MOK_ERROR_INVALID_VALUE;
-    if (cfg->debug_flags & ~(MOK_DEBUG_IDENTITY_EXPERT | MOK_DEBUG_SEPARATE_LAUNCHES)) return MOK_ERROR_INVALID_VALUE;
+    if (cfg->debug_flags & ~(MOK_DEBUG_IDENTITY_EXPERT | MOK_DEBUG_SEPARATE_LAUNCHES | MOK_DEBUG_WHOLE_PASS))
+        return MOK_ERROR_INVALID_VALUE;
     // MXFP8 GEMMs load the scale bytes of four 32-blocks as one aligned dword
     if (cfg->precision == MOK_MXFP8 && (s.H % 128 || s.I % 128)) return MOK_ERROR_INVALID_VALUE;
 
@@ -105,7 +106,12 @@ mok_status make_plan(const mok_config *cfg, const mok_shape *shape, Plan *p) {
     q.w_dh = w.take((size_t)q.R * 2 * q.I * 2);
     q.w_ga = w.take((size_t)q.R * q.I * 2);
     q.w_dgp = w.take((size_t)q.R * q.dg_slices * 4);
-    q.w_sync = w.take(4 * (size_t)(kSyncHeads + q.max_mtiles));
+    {   // persistent-kernel counters: the larger of the pair layout and the whole-pass layout
+        const int64_t S = std::max<int64_t>(1, std::min<int64_t>(q.n_slots, (int64_t)q.G));
+        const int64_t NR = (q.G + S - 1) / S;
+        const int64_t pass = 3 * NR * 8 + 2 * (int64_t)q.G + S + q.max_mtiles;
+        q.w_sync = w.take(4 * (size_t)std::max<int64_t>(kSyncHeads + q.max_mtiles, pass));
+    }
     if (q.precision == MOK_MXFP8) {
         q.w_dhq = w.take((size_t)q.R * 2 * q.I);
         q.w_dhq_scales = w.take((size_t)q.R * 2 * q.I / 32);

@@ -88,7 +88,8 @@ def test_knobs_do_not_change_bits(name):
                  dict(macrobatch_tokens=0),
                  dict(macrobatch_tokens=7), dict(ring_bytes=2 * cfg.minibatch_rows * row),
                  dict(ring_bytes=1 << 24), dict(capacity_multiplier=4.0),
-                 dict(debug_flags=mok.MOK_DEBUG_SEPARATE_LAUNCHES)):
+                 dict(debug_flags=mok.MOK_DEBUG_SEPARATE_LAUNCHES),
+                 dict(debug_flags=mok.MOK_DEBUG_WHOLE_PASS), dict(debug_flags=mok.MOK_DEBUG_WHOLE_PASS, ring_bytes=2 * cfg.minibatch_rows * row)):
         print(f"[layer] knobs {name} {over}", flush=True)
         same_bits(base, run_layer(d, knobs(cfg, **over)))
 

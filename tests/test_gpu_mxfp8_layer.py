@@ -46,15 +46,18 @@ def test_parity_small(name):
                                     for n in ("out", "dx", "dtopk_w")}, flush=True)
 
 
-def test_bitwise_deterministic_and_knob_invariant():
-    cfg = SMALL["mx_k2_ragged"]
+@pytest.mark.parametrize("name", ["mx_k2_ragged", "mx_k1_macro"])
+def test_bitwise_deterministic_and_knob_invariant(name):
+    cfg = SMALL[name]
+    row = cfg.H + cfg.H // 32                  # MXFP8 ring row bytes
     d = DeviceInputs(synth.make_inputs(cfg))
     first = run_layer(d, knobs(cfg))
     for _ in range(2):
         same_bits(first, run_layer(d, knobs(cfg)))
-    for over in (dict(minibatch_rows=16), dict(minibatch_rows=96, ring_bytes=2 * 96 * 264),
+    for over in (dict(minibatch_rows=16), dict(minibatch_rows=96, ring_bytes=2 * 96 * row),
                  dict(macrobatch_tokens=0), dict(ring_bytes=1 << 22), dict(capacity_multiplier=2.0),
-                 dict(debug_flags=mok.MOK_DEBUG_SEPARATE_LAUNCHES)):
-        print(f"[mxfp8 layer] knobs {over}", flush=True)
+                 dict(debug_flags=mok.MOK_DEBUG_SEPARATE_LAUNCHES),
+                 dict(debug_flags=mok.MOK_DEBUG_WHOLE_PASS), dict(debug_flags=mok.MOK_DEBUG_WHOLE_PASS, ring_bytes=2 * cfg.minibatch_rows * row)):
+        print(f"[mxfp8 layer] knobs {name} {over}", flush=True)
         same_bits(first, run_layer(d, knobs(cfg, **over)))
 
