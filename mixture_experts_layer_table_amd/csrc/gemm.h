@@ -129,17 +129,21 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "me
 // ----------------------------------------------------------------------------- LDS layouts (byte offsets)
 
 // Row layout: [rows][32] bf16, 64-byte rows of four 16-byte chunks; chunk c of
-// row r sits at c ^ ((r >> 1) & 3): 8 lanes reading one chunk of 8
-// consecutive rows hit 8 distinct 16-byte bank groups.
+// row r sits at c ^ ((r >> 2) & 3). The LDS serves 256 bytes (64 banks) per
+// cycle, 16 lanes of a 16-byte read: 16 lanes reading one chunk of 16
+// consecutive rows then hit 16 distinct 16-byte bank groups (r % 4 picks the
+// 64-byte quarter, (r >> 2) & 3 the group inside it).
 __device__ __forceinline__ uint32_t row_off(int r, int c) {
-    return (uint32_t)(r * 64 + ((c ^ ((r >> 1) & 3)) << 4));
+    return (uint32_t)(r * 64 + ((c ^ ((r >> 2) & 3)) << 4));
 }
 
 // Trans layout: sub-tiles of 128 columns, each [32 k][128] bf16 with 256-byte
-// k-rows; 16-byte chunk c of k-row k sits at c ^ (2 * (k & 3)): the 16 lanes
-// of a transpose read (4 k-rows x 2 chunks) hit 8 distinct bank groups.
+// k-rows; 16-byte chunk c of k-row k sits at c ^ (4 * (k & 3)). The 32 lanes
+// the LDS serves per cycle of a transpose read cover 4 consecutive k-rows x 4
+// chunks of one 32-column block: the XOR moves each k-row's 4 chunks to its
+// own quarter of the 256-byte bank window, so they hit 16 distinct groups.
 __device__ __forceinline__ uint32_t trans_off(int k, int col) {
-    return (uint32_t)((col >> 7) * (32 * 256) + k * 256 + (((((col & 127) >> 3) ^ ((k & 3) << 1))) << 4) +
+    return (uint32_t)((col >> 7) * (32 * 256) + k * 256 + (((((col & 127) >> 3) ^ ((k & 3) << 2))) << 4) +
                       ((col & 7) << 1));
 }
 
@@ -165,7 +169,7 @@ struct RowLoader {
         ldb = (uint32_t)(ld * 2);
         const int wave = wave_id(), L = threadIdx.x & 63;
         const int r = wave * IPW * 16 + (L >> 2);
-        const int c = (L & 3) ^ ((L >> 3) & 3);      // (r >> 1) & 3 == (L >> 3) & 3
+        const int c = (L & 3) ^ ((L >> 4) & 3);      // (r >> 2) & 3 == (L >> 4) & 3 (16-row blocks)
         voff = (uint32_t)r * ldb + (uint32_t)(c << 4);
         lds0 = (uint32_t)(wave * IPW * 1024);
         ksplit = ksplit_;
@@ -182,7 +186,7 @@ struct RowLoader {
         ldb = (uint32_t)(ld * 2);
         const int L = threadIdx.x & 63;
         const int r = wave * IPW * 16 + (L >> 2) - (upper ? ROWS / 2 : 0);
-        const int c = (L & 3) ^ ((L >> 3) & 3);
+        const int c = (L & 3) ^ ((L >> 4) & 3);
         voff = (uint32_t)r * ldb + (uint32_t)(c << 4);
         lds0 = (uint32_t)(wave * IPW * 1024);
         ksplit = 1 << 30;
@@ -219,7 +223,7 @@ struct TransLoader {
         split = base2 != nullptr;
         ldb = (uint32_t)(ld * 2);
         const int wave = wave_id(), L = threadIdx.x & 63;
-        const int c = (L & 15) ^ ((L >> 4) << 1);    // k & 3 == L >> 4
+        const int c = (L & 15) ^ ((L >> 4) << 2);    // k & 3 == L >> 4
         voff = (uint32_t)(L >> 4) * ldb + (uint32_t)(c << 4);
         inst0 = wave * IPW;
         lds0 = (uint32_t)(inst0 * 1024);
@@ -259,7 +263,7 @@ struct TransIdxLoader {
         res = make_rsrc(base, (uint32_t)(total_rows * ld * 2));
         ldb = (uint32_t)(ld * 2);
         const int wave = wave_id(), L = threadIdx.x & 63;
-        const int c = (L & 15) ^ ((L >> 4) << 1);
+        const int c = (L & 15) ^ ((L >> 4) << 2);
         coff = (uint32_t)((col0 + c * 8) * 2);
         krow = L >> 4;
         inst0 = wave * IPW;
