@@ -64,7 +64,8 @@ typedef enum mok_status {
 #define MOK_DEBUG_IDENTITY_EXPERT 1u
 /* debug_flags: run each grouped GEMM of a ring round as its own launch
    instead of the persistent producer/consumer kernel (same results, bit for
-   bit; used to cross-check the scheduler and to time GEMMs one by one). */
+   bit; used to cross-check the scheduler and to time GEMMs one by one).
+   BF16 only: MXFP8 rounds always launch their GEMMs one by one. */
 #define MOK_DEBUG_SEPARATE_LAUNCHES 2u
 /* debug_flags (k == 1 only): run each whole forward / dgrad pass as one
    persistent launch in which gathers and both GEMMs of every ring round

@@ -95,20 +95,22 @@ __device__ __forceinline__ void load_lds4(rsrc_t r, uint32_t voff, uint32_t soff
                  : "memory", "m0");
 }
 
-// Four consecutive int32 at a uniform address, through the scalar cache
-// (s_load_dwordx4, counted by lgkmcnt rather than vmcnt). The result is not
-// ready until sload_wait() has been passed with the same registers.
-typedef int sgpr4_t __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ sgpr4_t sload4(const int32_t *p) {
-    sgpr4_t v;
+// Four consecutive int32 at a uniform address, read through the constant
+// address space so that the compiler emits a scalar load (s_load_dwordx4,
+// counted by lgkmcnt rather than vmcnt) and places its wait before the first
+// use itself. (A load written as inline asm would not do: the compiler takes
+// an asm output as ready when the statement ends and may copy the registers
+// before the data has arrived.)
+struct sidx4_t {
+    int32_t v[4];
+};
+__device__ __forceinline__ sidx4_t sload4(const int32_t *p) {
     const uint64_t a = reinterpret_cast<uint64_t>(p);
     const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
     const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
-    const uint64_t u = ((uint64_t)hi << 32) | lo;
-    asm volatile("s_load_dwordx4 %0, %1, 0x0" : "=s"(v) : "s"(u) : "memory");
-    return v;
+    const auto *c = reinterpret_cast<const __attribute__((address_space(4))) int32_t *>(((uint64_t)hi << 32) | lo);
+    return sidx4_t{{c[0], c[1], c[2], c[3]}};
 }
-__device__ __forceinline__ void sload_wait(sgpr4_t &v) { asm volatile("s_waitcnt lgkmcnt(0)" : "+s"(v)); }
 
 // s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding).
 template <int N>
@@ -254,7 +256,7 @@ struct TransIdxLoader {
     uint32_t coff, ldb, lds0;
     const int32_t *idx;
     int n, inst0, krow;
-    sgpr4_t nid[IPW];   // indices of the next issue's k-rows, in flight until used
+    sidx4_t nid[IPW];   // indices of the next issue's k-rows (loaded one issue ahead)
 
     __device__ void init(const int32_t *idx_, int n_, const uint16_t *base, int64_t ld, int64_t total_rows,
                          int col0) {
@@ -283,11 +285,9 @@ struct TransIdxLoader {
     // then fetches those of k0 + 32.
     __device__ void issue(int k0, uint32_t tile) {
 #pragma unroll
-        for (int i = 0; i < IPW; ++i) sload_wait(nid[i]);
-#pragma unroll
         for (int i = 0; i < IPW; ++i) {
             const int inst = inst0 + i, sub = inst >> 3, kb = k0 + (inst & 7) * 4;
-            const int32_t r0 = nid[i][0], r1 = nid[i][1], r2 = nid[i][2], r3 = nid[i][3];
+            const int32_t r0 = nid[i].v[0], r1 = nid[i].v[1], r2 = nid[i].v[2], r3 = nid[i].v[3];
             const int32_t mine = krow == 0 ? r0 : krow == 1 ? r1 : krow == 2 ? r2 : r3;
             const uint32_t v = kb + krow < n ? (uint32_t)mine * ldb + coff + (uint32_t)(sub * 256) : kOutOfRange;
             load_lds16(res, v, 0, tile + lds0 + i * 1024);
@@ -361,20 +361,25 @@ __device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0
 // issue(kt, stage_lds_address), wrow(wn, fn), epilogue(acc, wm, wn), and
 // for gemm_kernel setup(args) -> bool.
 //
-// Pipeline of K-step kt (stage = kt % NSTAGE, D = NSTAGE - 1 steps in flight):
-//   read fragments of half-step 1 of stage kt
-//   issue the direct loads of K-step kt + D into stage (kt - 1) % NSTAGE
-//   MFMAs of half-step 0
-//   wait for this wave's loads of stage kt + 1 (vmcnt counts in issue order)
-//   and for its own LDS reads of stage kt, then barrier: stage kt + 1 is
-//   visible to every wave and stage kt is no longer read by any
-//   read fragments of half-step 0 of stage kt + 1
-//   MFMAs of half-step 1
-// so every LDS read is covered by queued MFMAs, and the barrier sits between
-// two groups of MFMAs (the other wave of the SIMD keeps the matrix core busy).
+// Ping-pong schedule. The two waves that share a SIMD belong to different
+// groups (wm = 0 and wm = 1) and run half a stage apart around one barrier
+// per stage (stage = kt % NSTAGE; loads run 3 stages ahead):
+//   group 0: MFMAs(stage kt) | wait own loads of kt+1 | barrier | issue kt+3, read fragments(kt+1)
+//   group 1: issue kt+3, read fragments(kt) | wait own loads of kt+1 | barrier | MFMAs(stage kt)
+// While one group waits at the barrier or for its fragment reads, the other
+// group's MFMAs keep the SIMD's matrix core busy.
+// Ordering: every wave waits for its own loads of stage kt+1 before barrier
+// kt, so stage kt+1 is visible after it (group 0 reads it right away, group 1
+// in its next iteration). Slot kt-1 is refilled (with stage kt+3) after
+// barrier kt-1 by group 1 and after barrier kt by group 0; every read of stage
+// kt-1 has landed before barrier kt-1: group 0 consumed its fragments in the
+// MFMAs before that barrier, and group 1 waits for its reads (lgkmcnt) right
+// before it.
 template <class P>
 __device__ __forceinline__ void gemm_tile(P &p, uint32_t lds) {
     using C = typename P::C;
+    static_assert(C::WAVES_M == 2 && C::NSTAGE == 4, "two wave groups, 4-stage ring");
+    constexpr int L = P::LOADS_PER_STAGE;
     f32x16_t acc[C::FM][C::FN];
 #pragma unroll
     for (int fm = 0; fm < C::FM; ++fm)
@@ -384,40 +389,53 @@ __device__ __forceinline__ void gemm_tile(P &p, uint32_t lds) {
             for (int r = 0; r < 16; ++r) acc[fm][fn][r] = 0.0f;
     const int wave = wave_id();
     const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
-    const int nk = __builtin_amdgcn_readfirstlane(p.nk);   // wave-uniform loop bound
-    constexpr int D = C::NSTAGE - 1;   // k-steps in flight
+    const int nk = __builtin_amdgcn_readfirstlane(p.nk);
     auto stage = [&](int kt) { return lds + (uint32_t)((kt % C::NSTAGE) * C::STAGE_BYTES); };
     Frags<C, P> f0, f1;
+    auto read_stage = [&](int kt) {
+        f0.read(stage(kt), 0, wm, wn, p);
+        f1.read(stage(kt), 1, wm, wn, p);
+    };
+    auto mma_stage = [&]() {
+        f0.mma(acc);
+        f1.mma(acc);
+    };
 #pragma unroll
-    for (int s = 0; s < D; ++s)
+    for (int s = 0; s < 3; ++s)
         if (s < nk) p.issue(s, stage(s));
     if (nk > 0) {
-        if (nk >= D)
-            wait_vmcnt<(D - 1) * P::LOADS_PER_STAGE>();
-        else
-            wait_vmcnt<0>();
+        if (nk >= 3) wait_vmcnt<2 * L>();
+        else if (nk == 2) wait_vmcnt<L>();
+        else wait_vmcnt<0>();
         lds_barrier();
-        f0.read(stage(0), 0, wm, wn, p);
     }
-    for (int kt = 0; kt < nk; ++kt) {
-        f1.read(stage(kt), 1, wm, wn, p);
-        if (kt + D < nk) p.issue(kt + D, stage(kt + D));
-        __builtin_amdgcn_sched_barrier(0);
-        f0.mma(acc);
-        __builtin_amdgcn_sched_barrier(0);
-        // Unconditional, so that the compiler's LDS-counter bookkeeping sees
-        // one straight path (after the last K-step this reads a stale stage
-        // that is never used).
-        if (kt + D < nk)
-            wait_vmcnt<(D - 1) * P::LOADS_PER_STAGE>();   // k-steps kt+2 .. kt+D may stay in flight
-        else
-            wait_vmcnt<0>();
-        wait_lgkm0();
-        lds_barrier();
-        f0.read(stage(kt + 1), 0, wm, wn, p);
-        __builtin_amdgcn_sched_barrier(0);
-        f1.mma(acc);
-        __builtin_amdgcn_sched_barrier(0);
+    if (wm == 0) {
+        if (nk > 0) read_stage(0);
+        for (int kt = 0; kt < nk; ++kt) {
+            __builtin_amdgcn_sched_barrier(0);
+            mma_stage();
+            __builtin_amdgcn_sched_barrier(0);
+            // own loads issued so far: up to stage kt + 2; stage kt + 1 must have landed
+            if (kt + 2 < nk) wait_vmcnt<L>();
+            else wait_vmcnt<0>();
+            lds_barrier();
+            if (kt + 3 < nk) p.issue(kt + 3, stage(kt + 3));
+            if (kt + 1 < nk) read_stage(kt + 1);
+        }
+    } else {
+        for (int kt = 0; kt < nk; ++kt) {
+            if (kt + 3 < nk) p.issue(kt + 3, stage(kt + 3));
+            read_stage(kt);
+            // own loads issued so far: up to stage kt + 3; stage kt + 1 must have landed
+            if (kt + 3 < nk) wait_vmcnt<2 * L>();
+            else if (kt + 2 < nk) wait_vmcnt<L>();
+            else wait_vmcnt<0>();
+            wait_lgkm0();   // fragment reads of stage kt landed: the slot is refilled right after this barrier
+            lds_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            mma_stage();
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
     p.epilogue(acc, wm, wn);
 }

@@ -98,28 +98,18 @@ __device__ __forceinline__ int scale8(uint32_t area, int row, int kt) {
     return (int)*(const __attribute__((address_space(3))) uint8_t *)(uintptr_t)a;
 }
 
-// Generic block-scaled tile kernel. P provides what gemm_kernel's problems
-// provide (C, Args, setup, nk counted in 64-wide stages, issue(kt, stage)
-// which also issues the scale loads, wrow, epilogue), with
-// LOADS_PER_STAGE counting the scale load.
-//
-// Pipeline of stage kt (D = NSTAGE - 1 stages in flight), MFMAs split by the
-// X fragments: half 0 = fm in [0, FM/2), half 1 = fm in [FM/2, FM):
-//   read X fragments (and scales) of half 1 of stage kt
-//   issue the loads of stage kt + D
-//   MFMAs of half 0
-//   wait for this wave's loads of stage kt + 1 and its LDS reads of stage kt;
-//   barrier (stage kt + 1 visible, stage kt free)
-//   read X fragments of half 0 of stage kt + 1
-//   MFMAs of half 1
-//   read W fragments of stage kt + 1 (their latency overlaps the tail of the
-//   MFMAs above and the other wave of the SIMD)
+// Block-scaled tile. P provides what gemm_tile's problems provide (C, Args,
+// nk counted in 64-wide stages, issue(kt, stage) which also issues the scale
+// load, wrow, epilogue), with LOADS_PER_STAGE counting the scale load.
+// Same ping-pong schedule as gemm_tile: the two waves of a SIMD (wm = 0, 1)
+// run half a stage apart around one barrier per stage, so one group's MFMAs
+// cover the other's barrier wait and fragment reads.
 template <class P>
 __device__ __forceinline__ void gemm8_tile(P &p, uint32_t lds) {
     using C = typename P::C;
     using S = Fp8Stage<C>;
-    constexpr int FM = C::FM, FN = C::FN, FH = FM / 2;
-    static_assert(FM % 2 == 0, "two X halves");
+    constexpr int FM = C::FM, FN = C::FN, L = P::LOADS_PER_STAGE;
+    static_assert(C::WAVES_M == 2 && C::NSTAGE == 4, "two wave groups, 4-stage ring");
     f32x16_t acc[FM][FN];
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm)
@@ -130,72 +120,65 @@ __device__ __forceinline__ void gemm8_tile(P &p, uint32_t lds) {
     const int wave = wave_id();
     const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
     const int nk = __builtin_amdgcn_readfirstlane(p.nk);
-    constexpr int D = C::NSTAGE - 1;
     auto stage = [&](int kt) { return lds + (uint32_t)((kt % C::NSTAGE) * S::BYTES); };
 
     i32x8_t wa[FN], xb[FM];
     int swa[FN], sxb[FM];
-    auto read_w = [&](int kt) {
+    auto read_stage = [&](int kt) {
         const uint32_t st = stage(kt);
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
             wa[fn] = frag8(st + C::X_BYTES, p.wrow(wn, fn));
             swa[fn] = scale8(st + S::SC_OFF + C::BM * 4, p.wrow(wn, fn), kt);
         }
-    };
-    // the half index is a compile-time constant (integral_constant)
-    auto read_x = [&](auto halfc, int kt) {
-        constexpr int half = decltype(halfc)::value;
-        const uint32_t st = stage(kt);
 #pragma unroll
-        for (int i = 0; i < FH; ++i) {
-            const int fm = half * FH + i;
+        for (int fm = 0; fm < FM; ++fm) {
             xb[fm] = frag8(st, wm * C::WM + fm * 32);
             sxb[fm] = scale8(st + S::SC_OFF, wm * C::WM + fm * 32, kt);
         }
     };
-    auto mma = [&](auto halfc) {
-        constexpr int half = decltype(halfc)::value;
+    auto mma_stage = [&]() {
 #pragma unroll
-        for (int i = 0; i < FH; ++i) {
-            const int fm = half * FH + i;
+        for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn)
                 acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wa[fn], xb[fm], acc[fm][fn], 0, 0, 0,
                                                                               swa[fn], 0, sxb[fm]);
-        }
     };
-    using I0 = std::integral_constant<int, 0>;
-    using I1 = std::integral_constant<int, 1>;
 #pragma unroll
-    for (int s = 0; s < D; ++s)
+    for (int s = 0; s < 3; ++s)
         if (s < nk) p.issue(s, stage(s));
     if (nk > 0) {
-        if (nk >= D)
-            wait_vmcnt<(D - 1) * P::LOADS_PER_STAGE>();
-        else
-            wait_vmcnt<0>();
+        if (nk >= 3) wait_vmcnt<2 * L>();
+        else if (nk == 2) wait_vmcnt<L>();
+        else wait_vmcnt<0>();
         lds_barrier();
-        read_w(0);
-        read_x(I0{}, 0);
     }
-    for (int kt = 0; kt < nk; ++kt) {
-        read_x(I1{}, kt);
-        if (kt + D < nk) p.issue(kt + D, stage(kt + D));
-        __builtin_amdgcn_sched_barrier(0);
-        mma(I0{});
-        __builtin_amdgcn_sched_barrier(0);
-        if (kt + D < nk)
-            wait_vmcnt<(D - 1) * P::LOADS_PER_STAGE>();
-        else
-            wait_vmcnt<0>();
-        wait_lgkm0();
-        lds_barrier();
-        read_x(I0{}, kt + 1);   // after the last stage these read a stale stage, never used
-        __builtin_amdgcn_sched_barrier(0);
-        mma(I1{});
-        __builtin_amdgcn_sched_barrier(0);
-        read_w(kt + 1);
+    if (wm == 0) {
+        if (nk > 0) read_stage(0);
+        for (int kt = 0; kt < nk; ++kt) {
+            __builtin_amdgcn_sched_barrier(0);
+            mma_stage();
+            __builtin_amdgcn_sched_barrier(0);
+            if (kt + 2 < nk) wait_vmcnt<L>();
+            else wait_vmcnt<0>();
+            lds_barrier();
+            if (kt + 3 < nk) p.issue(kt + 3, stage(kt + 3));
+            if (kt + 1 < nk) read_stage(kt + 1);
+        }
+    } else {
+        for (int kt = 0; kt < nk; ++kt) {
+            if (kt + 3 < nk) p.issue(kt + 3, stage(kt + 3));
+            read_stage(kt);
+            if (kt + 3 < nk) wait_vmcnt<2 * L>();
+            else if (kt + 2 < nk) wait_vmcnt<L>();
+            else wait_vmcnt<0>();
+            wait_lgkm0();   // fragment reads of stage kt landed: the slot is refilled right after this barrier
+            lds_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            mma_stage();
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
     p.epilogue(acc, wm, wn);
 }

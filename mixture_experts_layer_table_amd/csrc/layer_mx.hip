@@ -552,10 +552,8 @@ hipError_t mx_forward_round(const Plan &p, const SchedView &v, int g0, int g1, i
                    w.up_elems, w.up_scales, h, aring};
     Down8Args da{v, g0, g1, ntd, p.n_slots, p.MB, p.H, p.I, p.k, (int)p.MT, p.nb_full, aring,
                  w.down_elems, w.down_scales, topk_w, out, stage};
-    if (!(p.debug & MOK_DEBUG_SEPARATE_LAUNCHES))
-        return launch_pair<GateUp8<CfgA>, Down8<CfgA>, S8::LDS_BYTES>("fwd_gemms", ga, da,
-                                                                      reinterpret_cast<int *>(ws + p.w_sync),
-                                                                      p.max_mtiles, st);
+    // One launch per GEMM: the two block-scaled tiles do not fit one persistent
+    // kernel's register budget (two waves per SIMD) without spilling.
     if ((err = launch_gemm8<GateUp8<CfgA>>("gateup", seg_grid(ntg, mt_bound), ga, st)) != hipSuccess) return err;
     return launch_gemm8<Down8<CfgA>>("down", seg_grid(ntd, mt_bound), da, st);
 }
@@ -581,10 +579,6 @@ hipError_t mx_backward_round(const Plan &p, const SchedView &v, int g0, int g1, 
                topk_w, dh, gav, dgp, dhq, dhqs};
     DX8Args xa{v, g0, g1, ntx, p.n_slots, p.H, p.I, p.k, (int)p.MT, p.nb_full, dhq, dhqs, w.gate_elems,
                w.gate_scales, w.up_elems, w.up_scales, dx, stage};
-    if (!(p.debug & MOK_DEBUG_SEPARATE_LAUNCHES))
-        return launch_pair<DA8<CfgA>, DX8<CfgA>, S8::LDS_BYTES>("bwd_gemms", aa, xa,
-                                                                reinterpret_cast<int *>(ws + p.w_sync), p.max_mtiles,
-                                                                st);
     if ((err = launch_gemm8<DA8<CfgA>>("dA", seg_grid(nta, mt_bound), aa, st)) != hipSuccess) return err;
     return launch_gemm8<DX8<CfgA>>("dX", seg_grid(ntx, mt_bound), xa, st);
 }

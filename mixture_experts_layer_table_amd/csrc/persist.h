@@ -100,6 +100,17 @@ __device__ int claim_item(const PairSync &s, const QueueShape &q, int xcd, uint3
     return 0;
 }
 
+// End of a work item: every wave waits for its own global stores to be
+// acknowledged by the L2 before the workgroup barrier. The barrier alone waits
+// for LDS traffic only, and the agent-scope release that thread 0 performs
+// afterwards (L2 write-back, then the flag) covers its own wave's stores; with
+// this wait it covers the whole workgroup's. The barrier also frees the LDS
+// for the next item.
+__device__ __forceinline__ void item_done_barrier() {
+    wait_vmcnt<0>();
+    __syncthreads();
+}
+
 template <class P>
 __device__ __forceinline__ void run_tile(P &p, uint32_t lds) {
     if constexpr (P::FP8)
@@ -161,7 +172,7 @@ __global__ __launch_bounds__(P1::C::NT) void persist_pair_kernel(typename P1::Ar
             p.init(a2, seg_tile<P2>(v, lo, j, n, a2.n_slots));
             run_tile(p, lds);
         }
-        __syncthreads();   // every wave's stores issued and complete, LDS free for the next tile
+        item_done_barrier();
         if (cls == 1 && threadIdx.x == 0) __hip_atomic_fetch_add(&s.done[j], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
@@ -225,6 +236,7 @@ struct PassItem {
     int kind;   // 0 none, 1 gather, 2 producer, 3 consumer
     int a, b;   // (gather) mini-batch, row chunk; (tiles) m-tile (global index), n-tile
     int round;
+    int acquire;   // the item's inputs were published by other workgroups since this one last acquired
 };
 
 __device__ __forceinline__ bool wait_at_least(const int *p, int target, uint32_t *status) {
@@ -242,7 +254,7 @@ __device__ __forceinline__ bool wait_at_least(const int *p, int target, uint32_t
 // Thread 0: claim the next item at or after segment `seg` and wait for its inputs.
 __device__ PassItem claim_pass_item(const PassSync &s, const PassShape &ps, const SchedView &v, int nt1, int nt2,
                                     int64_t n_slots, int xcd, int &seg, int &acq_round) {
-    PassItem it{0, 0, 0, 0};
+    PassItem it{0, 0, 0, 0, 0};
     for (; seg < 3 * ps.NR; ++seg) {
         const int r = seg / 3, c = seg % 3;
         int a, b;
@@ -255,7 +267,7 @@ __device__ PassItem claim_pass_item(const PassSync &s, const PassShape &ps, cons
             if (h >= n) continue;
             const int g = a + h / ps.cpm;
             if (!wait_at_least(&s.released[g % n_slots], r, v.status)) return it;
-            it = PassItem{1, g, h % ps.cpm, r};
+            it = PassItem{1, g, h % ps.cpm, r, 0};
             return it;
         }
         const int lo = v.mtfirst[a], mtc = v.mtfirst[b] - lo, nt = c == 1 ? nt1 : nt2;
@@ -267,17 +279,18 @@ __device__ PassItem claim_pass_item(const PassSync &s, const PassShape &ps, cons
             if (h >= len) continue;
             int j, nn;
             item_tile(start + h, nt, mtc, j, nn);
+            int acquire = 1;
             if (c == 1) {
                 if (acq_round < r) {   // first producer tile of this round on this workgroup
                     if (!wait_at_least(&s.full[r], (b - a) * ps.cpm, v.status)) return it;
-                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
                     acq_round = r;
+                } else {
+                    acquire = 0;
                 }
             } else {
                 if (!wait_at_least(&s.done[lo + j], nt1, v.status)) return it;
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
             }
-            it = PassItem{c == 1 ? 2 : 3, lo + j, nn, r};
+            it = PassItem{c == 1 ? 2 : 3, lo + j, nn, r, acquire};
             return it;
         }
     }
@@ -305,10 +318,16 @@ __global__ __launch_bounds__(P1::C::NT) void persist_pass_kernel(GA ga, typename
             bcast[1] = it.a;
             bcast[2] = it.b;
             bcast[3] = it.round;
+            bcast[4] = it.acquire;
         }
         __syncthreads();
         const int kind = bcast[0], ia = bcast[1], ib = bcast[2];
         if (kind == 0) return;
+        // Every wave takes the acquire itself, so that its own loads are
+        // ordered after its own L1/L2 invalidate. Ring slots are reused within
+        // this launch: this XCD's L2 and this CU's L1 may hold a slot's lines
+        // from an earlier round.
+        if (bcast[4]) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         if (kind == 1) {
             const int r0 = ib * kGatherRows;
             const int nrows = max(0, min(kGatherRows, v.mb_start[ia + 1] - v.mb_start[ia] - r0));
@@ -327,7 +346,10 @@ __global__ __launch_bounds__(P1::C::NT) void persist_pass_kernel(GA ga, typename
             p.init(a2, SegTile{mt, ib, (int)(mt.g % n_slots), mt.q0 - v.mb_start[mt.g]});
             run_tile(p, lds);
         }
-        __syncthreads();   // every wave's stores complete, LDS free for the next item
+        // Every wave writes its own stores back to where other XCDs read them
+        // before the workgroup publishes the item.
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        item_done_barrier();
         if (threadIdx.x == 0) {
             if (kind == 1) {
                 __hip_atomic_fetch_add(&s.full[bcast[3]], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
