@@ -70,10 +70,11 @@ typedef enum mok_status {
 /* debug_flags (k == 1 only): run each whole forward / dgrad pass as one
    persistent launch in which gathers and both GEMMs of every ring round
    follow the in-kernel ring protocol (slot full / release counters) instead
-   of stream order between rounds. Same results, bit for bit. Not the
-   default: on this GPU every cross-XCD handoff inside a kernel costs a
-   device-scope L2 write-back / invalidate, and the measured pass is slower
-   than the gather kernel plus the persistent GEMM pair. */
+   of stream order between rounds. Same results, bit for bit. BF16 only:
+   MXFP8 mode ignores the flag. Not the default: on this GPU every cross-XCD
+   handoff inside a kernel costs a device-scope L2 write-back / invalidate,
+   and the measured pass is slower than the gather kernel plus the
+   persistent GEMM pair. */
 #define MOK_DEBUG_WHOLE_PASS 4u
 
 /*

@@ -80,32 +80,47 @@ struct GateUp {
     __device__ int wrow(int wn, int fn) const {
         return fn < C::FN / 2 ? wn * (C::WN / 2) + fn * 32 : C::BN / 2 + wn * (C::WN / 2) + (fn - C::FN / 2) * 32;
     }
+    // h = [x W_gate | x W_up] rows and a = silu(h_gate) * h_up rows, staged
+    // through LDS (FragStage): the wave's columns are 32 gate then 32 up
+    // columns of the same 32 values of i.
     __device__ void epilogue(f32x16_t (&acc)[C::FM][C::FN], int wm, int wn) {
+        const int ib = i0 + wn * (C::WN / 2);
+        if (ib >= I) return;   // I % 64 == 0: the wave's i are all valid or all past I
         const int lane = threadIdx.x & 63;
+        staged_rows<C>([&](int fm, int fn, int g4, int j) { return acc[fm][fn][g4 * 4 + j]; },
+                       [&](int fm, int r) -> uint16_t * {
+                           const int m = wm * C::WM + fm * 32 + r;
+                           if (m >= t.mt.rows) return nullptr;
+                           // gate columns go to h[.., i], up columns to h[.., I + i]
+                           const bool up = FragStage<C>::pass_col(lane) >= C::WN / 2;
+                           return h + (int64_t)(t.mt.q0 + m) * 2 * I + ib + (up ? I - C::WN / 2 : 0);
+                       });
+        // a: the first half of each staged row holds the 32 values of i
+        using FS = FragStage<C>;
+        const uint32_t area = FS::area(wave_id(), 1);
 #pragma unroll
         for (int fm = 0; fm < C::FM; ++fm) {
-            const int m = wm * C::WM + fm * 32 + (lane & 31);
-            if (m >= t.mt.rows) continue;
-            const int64_t q = t.mt.q0 + m;
-            uint16_t *hrow = h + q * 2 * I;
-            uint16_t *arow = aring + ((int64_t)t.slot * MB + t.rowoff + m) * I;
 #pragma unroll
             for (int fn = 0; fn < C::FN / 2; ++fn)
 #pragma unroll
                 for (int g4 = 0; g4 < 4; ++g4) {
-                    const int i = i0 + wn * (C::WN / 2) + fn * 32 + g4 * 8 + (lane >> 5) * 4;
-                    if (i >= I) continue;
-                    float hg[4], hu[4], av[4];
+                    float av[4];
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        hg[j] = acc[fm][fn][g4 * 4 + j];
-                        hu[j] = acc[fm][fn + C::FN / 2][g4 * 4 + j];
-                        av[j] = hg[j] * sigmoidf_(hg[j]) * hu[j];
+                        const float hg = acc[fm][fn][g4 * 4 + j], hu = acc[fm][fn + C::FN / 2][g4 * 4 + j];
+                        av[j] = hg * sigmoidf_(hg) * hu;
                     }
-                    store4_bf16(hrow + i, hg[0], hg[1], hg[2], hg[3]);
-                    store4_bf16(hrow + I + i, hu[0], hu[1], hu[2], hu[3]);
-                    store4_bf16(arow + i, av[0], av[1], av[2], av[3]);
+                    FS::put(area + FS::frag_off(fn, g4, lane),
+                            make_uint2(pack_bf16x2(av[0], av[1]), pack_bf16x2(av[2], av[3])));
                 }
+#pragma unroll
+            for (int p = 0; p < FS::PASSES; ++p) {
+                const int m = wm * C::WM + fm * 32 + FS::pass_row(p, lane);
+                const int cc = FS::pass_col(lane);
+                if (m < t.mt.rows && cc < C::WN / 2)
+                    *reinterpret_cast<uint2 *>(aring + ((int64_t)t.slot * MB + t.rowoff + m) * I + ib + cc) =
+                        FS::get(area + FS::pass_off(p, lane));
+            }
         }
     }
 };
@@ -210,56 +225,84 @@ struct DA {
         wl.issue(kt * C::BK, tile + C::X_BYTES);
     }
     __device__ int wrow(int wn, int fn) const { return wn * C::WN + fn * 32; }
+    // SwiGLU backward of the tile, staged through LDS per 32-row fragment
+    // (FragStage): h rows come in and dh, g*a rows leave as whole row runs.
     __device__ void epilogue(f32x16_t (&acc)[C::FM][C::FN], int wm, int wn) {
+        using FS = FragStage<C>;
         const int lane = threadIdx.x & 63;
         const int I = a.I;
         const int slice = t.nt * C::WAVES_N + wn;
-        const bool slice_ok = i0 + wn * C::WN < I;
+        const int ib = i0 + wn * C::WN;
+        if (ib >= I) return;   // I % 64 == 0: this wave's columns are all valid or all past I
+        const uint32_t sg = FS::area(wave_id(), 3), su = sg + FS::BYTES, sa = su + FS::BYTES;
+        const int cc = FS::pass_col(lane);
+        uint2 hg[FS::PASSES], hu[FS::PASSES];
+        auto load_h = [&](int fm, uint2 (&g)[FS::PASSES], uint2 (&u)[FS::PASSES]) {
+#pragma unroll
+            for (int p = 0; p < FS::PASSES; ++p) {
+                const int m = wm * C::WM + fm * 32 + FS::pass_row(p, lane);
+                const uint16_t *hrow = a.h + (int64_t)(t.mt.q0 + (m < t.mt.rows ? m : 0)) * 2 * I + ib + cc;
+                g[p] = *reinterpret_cast<const uint2 *>(hrow);
+                u[p] = *reinterpret_cast<const uint2 *>(hrow + I);
+            }
+        };
+        load_h(0, hg, hu);
 #pragma unroll
         for (int fm = 0; fm < C::FM; ++fm) {
-            const int m = wm * C::WM + fm * 32 + (lane & 31);
-            const bool ok = m < t.mt.rows;
-            const int q = t.mt.q0 + (ok ? m : 0);
-            const int64_t c = t.mt.c0 + (ok ? m : 0);   // dh and g*a rows are kept in canonical order
+#pragma unroll
+            for (int p = 0; p < FS::PASSES; ++p) {
+                FS::put(sg + FS::pass_off(p, lane), hg[p]);
+                FS::put(su + FS::pass_off(p, lane), hu[p]);
+            }
+            __builtin_amdgcn_sched_barrier(0);   // phases stay in order: keeps live ranges short
+            const int mrow = wm * C::WM + fm * 32 + (lane & 31);
+            const bool ok = mrow < t.mt.rows;
+            const int q = t.mt.q0 + (ok ? mrow : 0);
             const float gw = a.topk_w[a.v.perm[q]];
-            const uint16_t *hrow = a.h + (int64_t)q * 2 * I;
-            uint16_t *dhrow = a.dh + c * 2 * I;
-            uint16_t *garow = a.ga + c * I;
             float dg = 0.0f;
 #pragma unroll
             for (int fn = 0; fn < C::FN; ++fn)
 #pragma unroll
                 for (int g4 = 0; g4 < 4; ++g4) {
-                    const int i = i0 + wn * C::WN + fn * 32 + g4 * 8 + (lane >> 5) * 4;
-                    if (!slice_ok || i >= I) continue;
-                    const uint2 hg2 = *reinterpret_cast<const uint2 *>(hrow + i);
-                    const uint2 hu2 = *reinterpret_cast<const uint2 *>(hrow + I + i);
-                    const uint32_t hgw[4] = {hg2.x & 0xFFFFu, hg2.x >> 16, hg2.y & 0xFFFFu, hg2.y >> 16};
-                    const uint32_t huw[4] = {hu2.x & 0xFFFFu, hu2.x >> 16, hu2.y & 0xFFFFu, hu2.y >> 16};
+                    const uint32_t o = FS::frag_off(fn, g4, lane);
+                    const uint2 hg2 = FS::get(sg + o), hu2 = FS::get(su + o);
                     float dhg[4], dhu[4], gav[4];
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const float G = acc[fm][fn][g4 * 4 + j];
-                        const float hg = bf16_to_f32(hgw[j]), hu = bf16_to_f32(huw[j]);
-                        const float s = sigmoidf_(hg);
-                        const float sl = hg * s;
-                        const float av = sl * hu;
+                        const float hgv = bf16_at(hg2, j), huv = bf16_at(hu2, j);
+                        const float s = sigmoidf_(hgv);
+                        const float sl = hgv * s;
+                        const float av = sl * huv;
                         dg += G * av;
                         const float da = gw * G;
                         dhu[j] = da * sl;
-                        dhg[j] = da * hu * s * (1.0f + hg * (1.0f - s));
+                        dhg[j] = da * huv * s * (1.0f + hgv * (1.0f - s));
                         gav[j] = gw * av;
                     }
-                    if (ok) {
-                        store4_bf16(dhrow + i, dhg[0], dhg[1], dhg[2], dhg[3]);
-                        store4_bf16(dhrow + I + i, dhu[0], dhu[1], dhu[2], dhu[3]);
-                        store4_bf16(garow + i, gav[0], gav[1], gav[2], gav[3]);
-                    }
+                    FS::put(sg + o, make_uint2(pack_bf16x2(dhg[0], dhg[1]), pack_bf16x2(dhg[2], dhg[3])));
+                    FS::put(su + o, make_uint2(pack_bf16x2(dhu[0], dhu[1]), pack_bf16x2(dhu[2], dhu[3])));
+                    FS::put(sa + o, make_uint2(pack_bf16x2(gav[0], gav[1]), pack_bf16x2(gav[2], gav[3])));
                 }
+            __builtin_amdgcn_sched_barrier(0);
+            // next fragment's h in flight while this one's rows are stored (its accumulators are dead now)
+            if (fm + 1 < C::FM) load_h(fm + 1, hg, hu);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int p = 0; p < FS::PASSES; ++p) {
+                const int m = wm * C::WM + fm * 32 + FS::pass_row(p, lane);
+                if (m < t.mt.rows) {
+                    const int64_t c = t.mt.c0 + m;   // dh and g*a rows are kept in canonical order
+                    const uint32_t o = FS::pass_off(p, lane);
+                    *reinterpret_cast<uint2 *>(a.dh + c * 2 * I + ib + cc) = FS::get(sg + o);
+                    *reinterpret_cast<uint2 *>(a.dh + c * 2 * I + I + ib + cc) = FS::get(su + o);
+                    *reinterpret_cast<uint2 *>(a.ga + c * I + ib + cc) = FS::get(sa + o);
+                }
+            }
             // lanes l and l ^ 32 hold the same row: lower half + upper half, fixed order
             const float other = __shfl_xor(dg, 32);
             const float tot = (lane < 32) ? dg + other : other + dg;
-            if (ok && lane < 32 && slice_ok) a.dgp[(int64_t)q * a.S + slice] = tot;
+            if (ok && lane < 32) a.dgp[(int64_t)q * a.S + slice] = tot;
         }
     }
 };
@@ -358,24 +401,15 @@ struct WGU {
     }
     __device__ int wrow(int wn, int fn) const { return wn * C::WN + fn * 32; }
     __device__ void epilogue(f32x16_t (&acc)[C::FM][C::FN], int wm, int wn) {
-        const int lane = threadIdx.x & 63;
         const int H = a.H, I = a.I;
-#pragma unroll
-        for (int fm = 0; fm < C::FM; ++fm) {
-            const int hh = h0 + wm * C::WM + fm * 32 + (lane & 31);
-            if (hh >= H) continue;
-#pragma unroll
-            for (int fn = 0; fn < C::FN; ++fn)
-#pragma unroll
-                for (int g4 = 0; g4 < 4; ++g4) {
-                    const int n = n0 + wn * C::WN + fn * 32 + g4 * 8 + (lane >> 5) * 4;
-                    if (n >= 2 * I) continue;
-                    uint16_t *dst = n < I ? a.dwg + ((int64_t)e * H + hh) * I + n
-                                          : a.dwu + ((int64_t)e * H + hh) * I + (n - I);
-                    const f32x16_t &v = acc[fm][fn];
-                    store4_bf16(dst, v[g4 * 4], v[g4 * 4 + 1], v[g4 * 4 + 2], v[g4 * 4 + 3]);
-                }
-        }
+        const int nb = n0 + wn * C::WN;
+        if (nb >= 2 * I) return;   // I % 64 == 0: the wave's columns are all gate, all up or all past 2I
+        uint16_t *base = nb < I ? a.dwg + nb : a.dwu + (nb - I);
+        staged_rows<C>([&](int fm, int fn, int g4, int j) { return acc[fm][fn][g4 * 4 + j]; },
+                       [&](int fm, int r) -> uint16_t * {
+                           const int hh = h0 + wm * C::WM + fm * 32 + r;
+                           return hh < H ? base + ((int64_t)e * H + hh) * I : nullptr;
+                       });
     }
 };
 
@@ -417,23 +451,14 @@ struct WD {
     }
     __device__ int wrow(int wn, int fn) const { return wn * C::WN + fn * 32; }
     __device__ void epilogue(f32x16_t (&acc)[C::FM][C::FN], int wm, int wn) {
-        const int lane = threadIdx.x & 63;
         const int H = a.H, I = a.I;
-#pragma unroll
-        for (int fm = 0; fm < C::FM; ++fm) {
-            const int ii = i0 + wm * C::WM + fm * 32 + (lane & 31);
-            if (ii >= I) continue;
-#pragma unroll
-            for (int fn = 0; fn < C::FN; ++fn)
-#pragma unroll
-                for (int g4 = 0; g4 < 4; ++g4) {
-                    const int n = n0 + wn * C::WN + fn * 32 + g4 * 8 + (lane >> 5) * 4;
-                    if (n >= H) continue;
-                    const f32x16_t &v = acc[fm][fn];
-                    store4_bf16(a.dwd + ((int64_t)e * I + ii) * H + n, v[g4 * 4], v[g4 * 4 + 1], v[g4 * 4 + 2],
-                                v[g4 * 4 + 3]);
-                }
-        }
+        const int nb = n0 + wn * C::WN;
+        if (nb >= H) return;   // H % 64 == 0
+        staged_rows<C>([&](int fm, int fn, int g4, int j) { return acc[fm][fn][g4 * 4 + j]; },
+                       [&](int fm, int r) -> uint16_t * {
+                           const int ii = i0 + wm * C::WM + fm * 32 + r;
+                           return ii < I ? a.dwd + ((int64_t)e * I + ii) * H + nb : nullptr;
+                       });
     }
 };
 
@@ -540,8 +565,10 @@ hipError_t launch_gemm(const char *name, dim3 grid, const typename P::Args &args
     return hipGetLastError();
 }
 
+// BF16 only: MXFP8 runs its rounds as separate launches whatever the flag.
 bool whole_pass(const Plan &p) {
-    return p.k == 1 && (p.debug & MOK_DEBUG_WHOLE_PASS) && !(p.debug & MOK_DEBUG_SEPARATE_LAUNCHES);
+    return p.k == 1 && p.precision == MOK_BF16 && (p.debug & MOK_DEBUG_WHOLE_PASS) &&
+           !(p.debug & MOK_DEBUG_SEPARATE_LAUNCHES);
 }
 
 }  // namespace
@@ -562,17 +589,13 @@ mok_status launch_forward(const Plan &p, const void *schedule, void *workspace, 
     int *sync = reinterpret_cast<int *>(ws + p.w_sync);
     hipError_t err = hipSuccess;
     if (whole_pass(p) && !identity) {   // one launch for the pass, ring protocol in the kernel
-        if (mx) {
-            err = mx_forward_pass(p, v, x, w, ws, h, topk_w, out, st);
-        } else {
-            const int ntg = (int)ceil_div(p.I, CfgA::BN / 2), ntd = (int)ceil_div(p.H, CfgA::BN);
-            GateUpArgs ga{v, 0, p.G, ntg, p.n_slots, p.MB, p.H, p.I, ring,
-                          static_cast<const uint16_t *>(w.w_gate), static_cast<const uint16_t *>(w.w_up), h, aring};
-            DownArgs da{v, 0, p.G, ntd, p.n_slots, p.MB, p.H, p.I, p.k, (int)p.MT, p.nb_full, aring,
-                        static_cast<const uint16_t *>(w.w_down), topk_w, out, stage};
-            err = launch_pass<GatherBf16, GateUp<CfgA>, Down<CfgA>, 3, CfgA::LDS_BYTES>(
-                "fwd_pass", p, GatherBf16{v, p.n_slots, p.MB, p.H, p.k, x, ring}, ga, da, false, sync, st);
-        }
+        const int ntg = (int)ceil_div(p.I, CfgA::BN / 2), ntd = (int)ceil_div(p.H, CfgA::BN);
+        GateUpArgs ga{v, 0, p.G, ntg, p.n_slots, p.MB, p.H, p.I, ring,
+                      static_cast<const uint16_t *>(w.w_gate), static_cast<const uint16_t *>(w.w_up), h, aring};
+        DownArgs da{v, 0, p.G, ntd, p.n_slots, p.MB, p.H, p.I, p.k, (int)p.MT, p.nb_full, aring,
+                    static_cast<const uint16_t *>(w.w_down), topk_w, out, stage};
+        err = launch_pass<GatherBf16, GateUp<CfgA>, Down<CfgA>, 3, CfgA::LDS_BYTES>(
+            "fwd_pass", p, GatherBf16{v, p.n_slots, p.MB, p.H, p.k, x, ring}, ga, da, false, sync, st);
         if (err == hipSuccess) err = hipGetLastError();
         return check_hip(err, "mok_forward");
     }
@@ -637,15 +660,11 @@ mok_status launch_backward(const Plan &p, const void *schedule, void *workspace,
     int *sync = reinterpret_cast<int *>(ws + p.w_sync);
     hipError_t err = hipSuccess;
     if (p.R > 0 && whole_pass(p)) {   // one launch for the dgrad pass
-        if (mx) {
-            err = mx_backward_pass(p, v, dy, w, ws, h, topk_w, dx, st);
-        } else {
-            const int nta = (int)ceil_div(p.I, CfgA::BN), ntx = (int)ceil_div(p.H, CfgA::BN);
-            DAArgs aa{v, 0, p.G, nta, p.n_slots, p.MB, p.H, p.I, p.dg_slices, ring, wd, h, topk_w, dh, ga, dgp};
-            DXArgs xa{v, 0, p.G, ntx, p.n_slots, p.H, p.I, p.k, (int)p.MT, p.nb_full, dh, wg, wu, dx, stage};
-            err = launch_pass<GatherBf16, DA<CfgA>, DX<CfgA>, 2, CfgA::LDS_BYTES>(
-                "bwd_pass", p, GatherBf16{v, p.n_slots, p.MB, p.H, p.k, dy, ring}, aa, xa, true, sync, st);
-        }
+        const int nta = (int)ceil_div(p.I, CfgA::BN), ntx = (int)ceil_div(p.H, CfgA::BN);
+        DAArgs aa{v, 0, p.G, nta, p.n_slots, p.MB, p.H, p.I, p.dg_slices, ring, wd, h, topk_w, dh, ga, dgp};
+        DXArgs xa{v, 0, p.G, ntx, p.n_slots, p.H, p.I, p.k, (int)p.MT, p.nb_full, dh, wg, wu, dx, stage};
+        err = launch_pass<GatherBf16, DA<CfgA>, DX<CfgA>, 2, CfgA::LDS_BYTES>(
+            "bwd_pass", p, GatherBf16{v, p.n_slots, p.MB, p.H, p.k, dy, ring}, aa, xa, true, sync, st);
         if (err == hipSuccess) {
             KernelTimer tm("router_grad", st);
             reduce_router_grad<<<(unsigned)ceil_div(p.R, 256), 256, 0, st>>>(v, p.dg_slices, dgp, dtopk_w);

@@ -21,11 +21,4 @@ hipError_t mx_backward_round(const Plan &p, const SchedView &v, int g0, int g1, 
                              const uint16_t *dy, const mok_weights &w, char *ws, const uint16_t *h,
                              const float *topk_w, uint16_t *dx, uint16_t *stage, hipStream_t st);
 
-// Whole forward / dgrad pass in one persistent launch (k == 1): gathers and
-// both GEMMs of every ring round, ring slots reused through in-kernel flags.
-hipError_t mx_forward_pass(const Plan &p, const SchedView &v, const uint16_t *x, const mok_weights &w, char *ws,
-                           uint16_t *h, const float *topk_w, uint16_t *out, hipStream_t st);
-hipError_t mx_backward_pass(const Plan &p, const SchedView &v, const uint16_t *dy, const mok_weights &w, char *ws,
-                            const uint16_t *h, const float *topk_w, uint16_t *dx, hipStream_t st);
-
 }  // namespace mok

@@ -16,7 +16,6 @@
 #include "gemm8.h"
 #include "layer_mx.h"
 #include "layer_parts.h"
-#include "persist.h"
 #include "mx_codec.h"
 
 namespace mok {
@@ -32,21 +31,12 @@ __device__ __forceinline__ const uint16_t *as_pairs(const uint8_t *p) { return r
 // Dispatch copy of one row into the MXFP8 ring: one wave quantizes the row of
 // processing position q = mb_start[g] + r along H into ring slot g % n_slots;
 // lane c handles 8 values, 4 lanes form one 32-block.
-struct GatherMx;
-template <int NT>
-__device__ void gather_mx_rows(const GatherMx &ga, int g, int r0, int nrows, const int *tok);
-
 struct GatherMx {
     SchedView v;
     int64_t n_slots;
     int MB, H, k;
     const uint16_t *src;
     uint8_t *ring;
-
-    template <int NT>
-    __device__ __forceinline__ void rows(int g, int r0, int nrows, const int *tok) const {
-        gather_mx_rows<NT>(*this, g, r0, nrows, tok);
-    }
 
     __device__ __forceinline__ void row(int g, int r) const {
         const int tok = v.perm[v.mb_start[g] + r] / k;
@@ -89,50 +79,6 @@ struct GatherMx {
         }
     }
 };
-
-// Rows [r0, r0 + nrows) of mini-batch g by the whole workgroup (NT threads,
-// a multiple of 64): one flat pass over (row, 8-value chunk) with 8 loads in
-// flight per thread; n = H/8 is a multiple of 16, so the 4 lanes of a
-// 32-block always share a row. tok: the rows' token indices, in LDS.
-template <int NT>
-__device__ void gather_mx_rows(const GatherMx &ga, int g, int r0, int nrows, const int *tok) {
-    const int H = ga.H, n = H / 8, total = nrows * n;
-    uint8_t *slot = ga.ring + (g % ga.n_slots) * (int64_t)ga.MB * (H + H / 32);
-    uint8_t *el = slot + (int64_t)r0 * H;                         // rows are contiguous: chunk e at byte 8e
-    uint8_t *sc = slot + (int64_t)ga.MB * H + (int64_t)r0 * (H / 32);   // block e/4 at byte e/4
-    for (int e0 = 0; e0 < total; e0 += NT * 8) {
-        uint4 t[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int e = e0 + i * NT + (int)threadIdx.x;
-            t[i] = e < total ? reinterpret_cast<const uint4 *>(ga.src + (int64_t)tok[e / n] * H)[e % n]
-                             : make_uint4(0, 0, 0, 0);
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int e = e0 + i * NT + (int)threadIdx.x;
-            if (e0 + i * NT >= total) break;   // workgroup-uniform
-            const uint32_t w[4] = {t[i].x, t[i].y, t[i].z, t[i].w};
-            uint32_t amax = 0;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) amax = max(amax, max(w[j] & 0x7FFFu, (w[j] >> 16) & 0x7FFFu));
-            amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1));
-            amax = max(amax, (uint32_t)__shfl_xor((int)amax, 2));
-            const uint32_t sb = mx_scale_byte_bf16(amax);
-            const int ex = (int)sb - 127;
-            uint32_t o[2];
-#pragma unroll
-            for (int d = 0; d < 2; ++d)
-                o[d] = e4m3_encode_bf16(w[2 * d] & 0xFFFFu, ex) | (e4m3_encode_bf16(w[2 * d] >> 16, ex) << 8) |
-                       (e4m3_encode_bf16(w[2 * d + 1] & 0xFFFFu, ex) << 16) |
-                       (e4m3_encode_bf16(w[2 * d + 1] >> 16, ex) << 24);
-            if (e < total) {
-                *reinterpret_cast<uint2 *>(el + (int64_t)e * 8) = make_uint2(o[0], o[1]);
-                if ((e & 3) == 0) sc[e >> 2] = (uint8_t)sb;
-            }
-        }
-    }
-}
 
 __global__ __launch_bounds__(256) void gather_rows_mx(GatherMx ga, int g0) {
     if (*ga.v.status) return;
@@ -390,15 +336,26 @@ struct DA8 {
         const int lane = threadIdx.x & 63;
         const int I = a.I;
         const int slice = t.nt * C::WAVES_N + wn;
-        if (i0 + wn * C::WN >= I) return;   // I % 128 == 0: a wave's 64 columns are all valid or none
+        const int ib0 = i0 + wn * C::WN;
+        if (ib0 >= I) return;   // I % 128 == 0: a wave's 64 columns are all valid or none
+        int q[C::FM];
+        bool ok[C::FM];
+        float gw[C::FM];
 #pragma unroll
         for (int fm = 0; fm < C::FM; ++fm) {
             const int m = wm * C::WM + fm * 32 + (lane & 31);
-            const bool ok = m < t.mt.rows;
-            const int q = t.mt.q0 + (ok ? m : 0);
-            const int64_t c = t.mt.c0 + (ok ? m : 0);   // dh and g*a rows are kept in canonical order
-            const float gw = a.topk_w[a.v.perm[q]];
-            const uint16_t *hrow = a.h + (int64_t)q * 2 * I;
+            ok[fm] = m < t.mt.rows;
+            q[fm] = t.mt.q0 + (ok[fm] ? m : 0);
+        }
+#pragma unroll
+        for (int fm = 0; fm < C::FM; ++fm) gw[fm] = a.topk_w[a.v.perm[q[fm]]];
+#pragma unroll
+        for (int fm = 0; fm < C::FM; ++fm) {
+            // one batch per fragment (the quantizer's staging leaves no room to prefetch the next)
+            HBatch<C> h;
+            h.load(a.h + (int64_t)q[fm] * 2 * I, I, ib0, lane);
+            const int m = wm * C::WM + fm * 32 + (lane & 31);
+            const int64_t c = t.mt.c0 + (ok[fm] ? m : 0);   // dh and g*a rows are kept in canonical order
             uint16_t *dhrow = a.dh + c * 2 * I;
             uint16_t *garow = a.ga + c * I;
             uint8_t *qrow = a.dhq + c * 2 * I;
@@ -406,30 +363,26 @@ struct DA8 {
             float dg = 0.0f;
 #pragma unroll
             for (int fn = 0; fn < C::FN; ++fn) {
-                const int ib = i0 + wn * C::WN + fn * 32;   // one 32-block of i
+                const int ib = ib0 + fn * 32;   // one 32-block of i
                 Block16 dhg, dhu;
 #pragma unroll
                 for (int g4 = 0; g4 < 4; ++g4) {
                     const int i = ib + g4 * 8 + (lane >> 5) * 4;
-                    const uint2 hg2 = *reinterpret_cast<const uint2 *>(hrow + i);
-                    const uint2 hu2 = *reinterpret_cast<const uint2 *>(hrow + I + i);
-                    const uint32_t hgw[4] = {hg2.x & 0xFFFFu, hg2.x >> 16, hg2.y & 0xFFFFu, hg2.y >> 16};
-                    const uint32_t huw[4] = {hu2.x & 0xFFFFu, hu2.x >> 16, hu2.y & 0xFFFFu, hu2.y >> 16};
                     float gav[4];
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const float G = acc[fm][fn][g4 * 4 + j];
-                        const float hg = bf16_to_f32(hgw[j]), hu = bf16_to_f32(huw[j]);
+                        const float hg = bf16_at(h.g[fn][g4], j), hu = bf16_at(h.u[fn][g4], j);
                         const float s = sigmoidf_(hg);
                         const float sl_ = hg * s;
                         const float av = sl_ * hu;
                         dg += G * av;
-                        const float da = gw * G;
+                        const float da = gw[fm] * G;
                         dhu.v[g4 * 4 + j] = da * sl_;
                         dhg.v[g4 * 4 + j] = da * hu * s * (1.0f + hg * (1.0f - s));
-                        gav[j] = gw * av;
+                        gav[j] = gw[fm] * av;
                     }
-                    if (ok) {
+                    if (ok[fm]) {
                         store4_bf16(dhrow + i, dhg.v[g4 * 4], dhg.v[g4 * 4 + 1], dhg.v[g4 * 4 + 2], dhg.v[g4 * 4 + 3]);
                         store4_bf16(dhrow + I + i, dhu.v[g4 * 4], dhu.v[g4 * 4 + 1], dhu.v[g4 * 4 + 2],
                                     dhu.v[g4 * 4 + 3]);
@@ -438,7 +391,7 @@ struct DA8 {
                 }
                 const Enc16 qg = quantize_block16(dhg);
                 const Enc16 qu = quantize_block16(dhu);
-                if (ok) {
+                if (ok[fm]) {
 #pragma unroll
                     for (int g4 = 0; g4 < 4; ++g4) {
                         const int i = ib + g4 * 8 + (lane >> 5) * 4;
@@ -454,7 +407,7 @@ struct DA8 {
             // lanes l and l ^ 32 hold the same row: lower half + upper half, fixed order
             const float other = __shfl_xor(dg, 32);
             const float tot = (lane < 32) ? dg + other : other + dg;
-            if (ok && lane < 32) a.dgp[(int64_t)q * a.S + slice] = tot;
+            if (ok[fm] && lane < 32) a.dgp[(int64_t)q[fm] * a.S + slice] = tot;
         }
     }
 };
@@ -581,36 +534,6 @@ hipError_t mx_backward_round(const Plan &p, const SchedView &v, int g0, int g1, 
                w.gate_scales, w.up_elems, w.up_scales, dx, stage};
     if ((err = launch_gemm8<DA8<CfgA>>("dA", seg_grid(nta, mt_bound), aa, st)) != hipSuccess) return err;
     return launch_gemm8<DX8<CfgA>>("dX", seg_grid(ntx, mt_bound), xa, st);
-}
-
-hipError_t mx_forward_pass(const Plan &p, const SchedView &v, const uint16_t *x, const mok_weights &w, char *ws,
-                           uint16_t *h, const float *topk_w, uint16_t *out, hipStream_t st) {
-    uint8_t *ring = reinterpret_cast<uint8_t *>(ws + p.w_ring);
-    uint8_t *aring = reinterpret_cast<uint8_t *>(ws + p.w_aring);
-    const int ntg = (int)ceil_div(p.I, CfgA::BN / 2), ntd = (int)ceil_div(p.H, CfgA::BN);
-    GateUp8Args ga{v, 0, p.G, ntg, p.n_slots, p.MB, p.H, p.I, ring, w.gate_elems, w.gate_scales,
-                   w.up_elems, w.up_scales, h, aring};
-    Down8Args da{v, 0, p.G, ntd, p.n_slots, p.MB, p.H, p.I, p.k, (int)p.MT, p.nb_full, aring,
-                 w.down_elems, w.down_scales, topk_w, out, nullptr};
-    return launch_pass<GatherMx, GateUp8<CfgA>, Down8<CfgA>, 3, S8::LDS_BYTES>(
-        "fwd_pass", p, GatherMx{v, p.n_slots, p.MB, p.H, p.k, x, ring}, ga, da, false,
-        reinterpret_cast<int *>(ws + p.w_sync), st);
-}
-
-hipError_t mx_backward_pass(const Plan &p, const SchedView &v, const uint16_t *dy, const mok_weights &w, char *ws,
-                            const uint16_t *h, const float *topk_w, uint16_t *dx, hipStream_t st) {
-    uint8_t *ring = reinterpret_cast<uint8_t *>(ws + p.w_ring);
-    const int nta = (int)ceil_div(p.I, CfgA::BN), ntx = (int)ceil_div(p.H, CfgA::BN);
-    DA8Args aa{v, 0, p.G, nta, p.n_slots, p.MB, p.H, p.I, p.dg_slices, ring, w.down_elems, w.down_scales, h,
-               topk_w, reinterpret_cast<uint16_t *>(ws + p.w_dh), reinterpret_cast<uint16_t *>(ws + p.w_ga),
-               reinterpret_cast<float *>(ws + p.w_dgp), reinterpret_cast<uint8_t *>(ws + p.w_dhq),
-               reinterpret_cast<uint8_t *>(ws + p.w_dhq_scales)};
-    DX8Args xa{v, 0, p.G, ntx, p.n_slots, p.H, p.I, p.k, (int)p.MT, p.nb_full,
-               reinterpret_cast<uint8_t *>(ws + p.w_dhq), reinterpret_cast<uint8_t *>(ws + p.w_dhq_scales),
-               w.gate_elems, w.gate_scales, w.up_elems, w.up_scales, dx, nullptr};
-    return launch_pass<GatherMx, DA8<CfgA>, DX8<CfgA>, 2, S8::LDS_BYTES>(
-        "bwd_pass", p, GatherMx{v, p.n_slots, p.MB, p.H, p.k, dy, ring}, aa, xa, true,
-        reinterpret_cast<int *>(ws + p.w_sync), st);
 }
 
 }  // namespace mok

@@ -55,6 +55,117 @@ __device__ __forceinline__ void store4_bf16(uint16_t *p, float a, float b, float
 
 __device__ __forceinline__ float bf16r(float x) { return bf16_to_f32(f32_to_bf16(x)); }
 
+// The saved pre-activations one lane needs for one 32-row fragment of the dA
+// epilogue: for each (fn, g4) block, 4 consecutive columns i of the gate half
+// and of the up half of its row (columns >= I read as zeros). The epilogue
+// loads the next fragment's batch before it stores the current one's
+// results: its stores may alias these loads for all the compiler knows, so
+// loads written after them would wait for every store before them.
+template <class C>
+struct HBatch {
+    uint2 g[C::FN][4], u[C::FN][4];
+    __device__ __forceinline__ void load(const uint16_t *hrow, int I, int ib, int lane) {
+#pragma unroll
+        for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const int i = ib + fn * 32 + g4 * 8 + (lane >> 5) * 4;
+                if (i < I) {
+                    g[fn][g4] = *reinterpret_cast<const uint2 *>(hrow + i);
+                    u[fn][g4] = *reinterpret_cast<const uint2 *>(hrow + I + i);
+                } else {
+                    g[fn][g4] = make_uint2(0, 0);
+                    u[fn][g4] = make_uint2(0, 0);
+                }
+            }
+    }
+};
+
+// ----------------------------------------------------------------------------- LDS-staged epilogue rows
+
+// Epilogue output and input pass through LDS one 32-row fragment at a time,
+// so that global memory sees whole 128-byte row runs: a fragment's
+// accumulators hold 32 rows x 4 columns per lane, and storing them directly
+// writes 8-byte pieces of 32 rows per instruction. Each wave uses its own
+// area of the tile's LDS, which is free once every wave has passed the last
+// barrier of the K loop (no stage is read or loaded after it); no barrier is
+// needed because a wave's LDS accesses complete in order. Rows are padded to
+// WN*2 + 8 bytes: the 32 lanes that hold one column group of 32 rows then
+// fall on 32 distinct bank pairs.
+template <class C>
+struct FragStage {
+    static constexpr int STRIDE = C::WN * 2 + 8;      // bytes per staged row
+    static constexpr int BYTES = 32 * STRIDE;         // one 32-row array
+    static constexpr int LPR = C::WN / 4;             // lanes per row in a row pass (8 bytes each)
+    static constexpr int RPP = 64 / LPR;              // rows per row pass
+    static constexpr int PASSES = 32 / RPP;
+    static_assert(64 % LPR == 0 && 32 % RPP == 0, "row passes must tile the fragment");
+
+    // dynamic LDS starts at offset 0 in every kernel that runs these tiles
+    static __device__ __forceinline__ uint32_t area(int wave, int narrays) {
+        extern __shared__ __attribute__((aligned(1024))) char lds_raw[];
+        return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)lds_raw +
+               (uint32_t)(wave * narrays * BYTES);
+    }
+    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+    static __device__ __forceinline__ void put(uint32_t a, uint2 v) {
+        u32x2_t w;
+        w.x = v.x;
+        w.y = v.y;
+        *reinterpret_cast<__attribute__((address_space(3))) u32x2_t *>((uintptr_t)a) = w;
+    }
+    static __device__ __forceinline__ uint2 get(uint32_t a) {
+        const u32x2_t w = *reinterpret_cast<const __attribute__((address_space(3))) u32x2_t *>((uintptr_t)a);
+        return make_uint2(w.x, w.y);
+    }
+    // fragment layout: 4 columns (fn, g4) of row lane % 32
+    static __device__ __forceinline__ uint32_t frag_off(int fn, int g4, int lane) {
+        return (uint32_t)((lane & 31) * STRIDE + (fn * 32 + g4 * 8 + (lane >> 5) * 4) * 2);
+    }
+    // row-pass layout: pass p covers rows p*RPP .. p*RPP+RPP-1, 4 columns per lane
+    static __device__ __forceinline__ int pass_row(int p, int lane) { return p * RPP + lane / LPR; }
+    static __device__ __forceinline__ int pass_col(int lane) { return (lane % LPR) * 4; }
+    static __device__ __forceinline__ uint32_t pass_off(int p, int lane) {
+        return (uint32_t)(pass_row(p, lane) * STRIDE + pass_col(lane) * 2);
+    }
+};
+
+// One wave's share of a tile leaves as rows, through its FragStage area:
+// for each 32-row fragment fm, value(fm, fn, g4, j) is the element of
+// fragment row lane % 32 at wave column fn*32 + g4*8 + 4*(lane/32) + j, and
+// row_dst(fm, r) the destination of wave column 0 of fragment row r (nullptr:
+// row not stored). Every column of the wave is stored (callers return early
+// for waves whose columns lie past the output's width).
+template <class C, class Val, class Dst>
+__device__ __forceinline__ void staged_rows(Val value, Dst row_dst) {
+    using FS = FragStage<C>;
+    const int lane = threadIdx.x & 63;
+    const uint32_t area = FS::area(wave_id(), 1);
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm) {
+#pragma unroll
+        for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                float y[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) y[j] = value(fm, fn, g4, j);
+                FS::put(area + FS::frag_off(fn, g4, lane), make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])));
+            }
+#pragma unroll
+        for (int p = 0; p < FS::PASSES; ++p) {
+            uint16_t *d = row_dst(fm, FS::pass_row(p, lane));
+            if (d) *reinterpret_cast<uint2 *>(d + FS::pass_col(lane)) = FS::get(area + FS::pass_off(p, lane));
+        }
+    }
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return bf16_to_f32(w & 0xFFFFu); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return bf16_to_f32(w >> 16); }
+__device__ __forceinline__ float bf16_at(const uint2 &v, int j) {
+    return j == 0 ? bf16_lo(v.x) : j == 1 ? bf16_hi(v.x) : j == 2 ? bf16_lo(v.y) : bf16_hi(v.y);
+}
+
 // Rows of y (forward down GEMM) or of dx (backward dX GEMM) leave the GEMM
 // towards token order. k == 1: straight to the token's row, the forward one
 // scaled by its gate weight after rounding y to bf16 (the weighted combine);
@@ -65,36 +176,26 @@ __device__ __forceinline__ void store_token_rows(const f32x16_t (&acc)[C::FM][C:
                                                  int nb_full, const float *topk_w, bool weighted, uint16_t *dst_k1,
                                                  uint16_t *stage) {
     const int lane = threadIdx.x & 63;
+    const int nb = n0 + wn * C::WN;
+    if (nb >= H) return;   // H % 64 == 0: the wave's columns are all valid or all past H
+    float gw[C::FM];
 #pragma unroll
     for (int fm = 0; fm < C::FM; ++fm) {
         const int m = wm * C::WM + fm * 32 + (lane & 31);
-        if (m >= t.mt.rows) continue;
-        const int q = t.mt.q0 + m;
-        uint16_t *dst;
-        float gw = 1.0f;
-        if (k == 1) {
-            const int tok = v.perm[q];
-            if (weighted) gw = topk_w[tok];
-            dst = dst_k1 + (int64_t)tok * H;
-        } else {
-            const int64_t base = (int64_t)k * ((t.mt.g / nb_full) * (int64_t)MT);
-            dst = stage + (q - base) * H;
-        }
-#pragma unroll
-        for (int fn = 0; fn < C::FN; ++fn)
-#pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                const int n = n0 + wn * C::WN + fn * 32 + g4 * 8 + (lane >> 5) * 4;
-                if (n >= H) continue;
-                float y[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    y[j] = acc[fm][fn][g4 * 4 + j];
-                    if (weighted && k == 1) y[j] = gw * bf16r(y[j]);   // y rows are bf16
-                }
-                store4_bf16(dst + n, y[0], y[1], y[2], y[3]);
-            }
+        gw[fm] = (weighted && k == 1 && m < t.mt.rows) ? topk_w[v.perm[t.mt.q0 + m]] : 1.0f;
     }
+    const int64_t sbase = (int64_t)k * ((t.mt.g / nb_full) * (int64_t)MT);
+    staged_rows<C>(
+        [&](int fm, int fn, int g4, int j) {
+            const float y = acc[fm][fn][g4 * 4 + j];
+            return (weighted && k == 1) ? gw[fm] * bf16r(y) : y;   // y rows are bf16
+        },
+        [&](int fm, int r) -> uint16_t * {
+            const int m = wm * C::WM + fm * 32 + r;
+            if (m >= t.mt.rows) return nullptr;
+            const int q = t.mt.q0 + m;
+            return (k == 1 ? dst_k1 + (int64_t)v.perm[q] * H : stage + (q - sbase) * H) + nb;
+        });
 }
 
 constexpr int kRowsPerBlock = 4;   // one 64-lane wave per row

@@ -49,6 +49,25 @@ __device__ __forceinline__ int load_relaxed(const int *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Thread 0: wait until *p >= target. Gives up (and flags the stall) after
+// kSpinLimit polls, or as soon as another workgroup has flagged one, so that a
+// stalled launch ends in about one poll budget instead of one budget per
+// remaining item.
+__device__ __forceinline__ bool wait_at_least(const int *p, int target, uint32_t *status) {
+    int polls = 0;
+    while (load_relaxed(p) < target) {
+        if (++polls > kSpinLimit) {
+            atomicOr(status, MOK_SCHEDULER_STALLED);
+            return false;
+        }
+        if ((polls & 255) == 0 &&
+            (__hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & MOK_SCHEDULER_STALLED))
+            return false;
+        __builtin_amdgcn_s_sleep(8);
+    }
+    return true;
+}
+
 // item id -> (m-tile j, n-tile n) in the group order of decode_seg_tile
 __device__ __forceinline__ void item_tile(int id, int nt, int mtc, int &j, int &n) {
     const int gsize = kGroupM * nt, grp = id / gsize, first = grp * kGroupM;
@@ -85,14 +104,7 @@ __device__ int claim_item(const PairSync &s, const QueueShape &q, int xcd, uint3
         if (h >= len) continue;
         int j, n;
         item_tile(start + h, q.nt2, q.mtc, j, n);
-        int polls = 0;
-        while (load_relaxed(&s.done[j]) < q.nt1) {
-            if (++polls > kSpinLimit) {
-                atomicOr(status, MOK_SCHEDULER_STALLED);
-                return 0;
-            }
-            __builtin_amdgcn_s_sleep(8);
-        }
+        if (!wait_at_least(&s.done[j], q.nt1, status)) return 0;
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         id = start + h;
         return 2;
@@ -239,17 +251,6 @@ struct PassItem {
     int acquire;   // the item's inputs were published by other workgroups since this one last acquired
 };
 
-__device__ __forceinline__ bool wait_at_least(const int *p, int target, uint32_t *status) {
-    int polls = 0;
-    while (load_relaxed(p) < target) {
-        if (++polls > kSpinLimit) {
-            atomicOr(status, MOK_SCHEDULER_STALLED);
-            return false;
-        }
-        __builtin_amdgcn_s_sleep(8);
-    }
-    return true;
-}
 
 // Thread 0: claim the next item at or after segment `seg` and wait for its inputs.
 __device__ PassItem claim_pass_item(const PassSync &s, const PassShape &ps, const SchedView &v, int nt1, int nt2,
