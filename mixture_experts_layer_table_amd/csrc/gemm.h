@@ -375,12 +375,18 @@ __device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0
 // kt-1 has landed before barrier kt-1: group 0 consumed its fragments in the
 // MFMAs before that barrier, and group 1 waits for its reads (lgkmcnt) right
 // before it.
+// Block coordinates of a tile (the launch grid's, or a persistent kernel's
+// virtual grid).
+struct Blk {
+    int x, y, z;
+};
+
+// K loop of one tile into acc.
 template <class P>
-__device__ __forceinline__ void gemm_tile(P &p, uint32_t lds) {
+__device__ __forceinline__ void gemm_mainloop(P &p, uint32_t lds, f32x16_t (&acc)[P::C::FM][P::C::FN]) {
     using C = typename P::C;
     static_assert(C::WAVES_M == 2 && C::NSTAGE == 4, "two wave groups, 4-stage ring");
     constexpr int L = P::LOADS_PER_STAGE;
-    f32x16_t acc[C::FM][C::FN];
 #pragma unroll
     for (int fm = 0; fm < C::FM; ++fm)
 #pragma unroll
@@ -437,16 +443,25 @@ __device__ __forceinline__ void gemm_tile(P &p, uint32_t lds) {
             __builtin_amdgcn_sched_barrier(0);
         }
     }
-    p.epilogue(acc, wm, wn);
 }
 
-// One tile per workgroup; P::setup(args) picks the tile (false: no tile).
+// One tile: prologue, K loop, epilogue.
+template <class P>
+__device__ __forceinline__ void gemm_tile(P &p, uint32_t lds) {
+    using C = typename P::C;
+    f32x16_t acc[C::FM][C::FN];
+    gemm_mainloop(p, lds, acc);
+    const int wave = wave_id();
+    p.epilogue(acc, wave / C::WAVES_N, wave % C::WAVES_N);
+}
+
+// One tile per workgroup; P::setup(args, block) picks the tile (false: no tile).
 template <class P>
 __global__ __launch_bounds__(P::C::NT) void gemm_kernel(typename P::Args args) {
     extern __shared__ __attribute__((aligned(1024))) char lds_raw[];
     const uint32_t lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)lds_raw;
     P p;
-    if (!p.setup(args)) return;
+    if (!p.setup(args, Blk{(int)blockIdx.x, (int)blockIdx.y, (int)blockIdx.z})) return;
     gemm_tile(p, lds);
 }
 

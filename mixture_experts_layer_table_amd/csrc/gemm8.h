@@ -188,7 +188,7 @@ __global__ __launch_bounds__(P::C::NT) void gemm8_kernel(typename P::Args args) 
     extern __shared__ __attribute__((aligned(1024))) char lds_raw[];
     const uint32_t lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)lds_raw;
     P p;
-    if (!p.setup(args)) return;
+    if (!p.setup(args, Blk{(int)blockIdx.x, (int)blockIdx.y, (int)blockIdx.z})) return;
     gemm8_tile(p, lds);
 }
 

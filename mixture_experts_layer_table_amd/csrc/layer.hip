@@ -51,9 +51,9 @@ struct GateUp {
     int i0, nk, H, I, MB;
     uint16_t *h, *aring;
 
-    __device__ bool setup(const Args &a) {
+    __device__ bool setup(const Args &a, Blk b) {
         SegTile tt;
-        if (!decode_seg_tile(a.v, a.g0, a.g1, a.n_slots, a.n_tiles, tt)) return false;
+        if (!decode_seg_tile(a.v, a.g0, a.g1, a.n_slots, a.n_tiles, b.x, tt)) return false;
         init(a, tt);
         return true;
     }
@@ -86,17 +86,17 @@ struct GateUp {
     __device__ void epilogue(f32x16_t (&acc)[C::FM][C::FN], int wm, int wn) {
         const int ib = i0 + wn * (C::WN / 2);
         if (ib >= I) return;   // I % 64 == 0: the wave's i are all valid or all past I
-        const int lane = threadIdx.x & 63;
-        staged_rows<C>([&](int fm, int fn, int g4, int j) { return acc[fm][fn][g4 * 4 + j]; },
+        const int lane = epi_lane();
+        staged_rows<C, C::LDS_BYTES>([&](int fm, int fn, int g4, int j) { return acc[fm][fn][g4 * 4 + j]; },
                        [&](int fm, int r) -> uint16_t * {
                            const int m = wm * C::WM + fm * 32 + r;
                            if (m >= t.mt.rows) return nullptr;
                            // gate columns go to h[.., i], up columns to h[.., I + i]
-                           const bool up = FragStage<C>::pass_col(lane) >= C::WN / 2;
+                           const bool up = FragStage<C, C::LDS_BYTES>::pass_col(lane) >= C::WN / 2;
                            return h + (int64_t)(t.mt.q0 + m) * 2 * I + ib + (up ? I - C::WN / 2 : 0);
                        });
         // a: the first half of each staged row holds the 32 values of i
-        using FS = FragStage<C>;
+        using FS = FragStage<C, C::LDS_BYTES>;
         const uint32_t area = FS::area(wave_id(), 1);
 #pragma unroll
         for (int fm = 0; fm < C::FM; ++fm) {
@@ -118,8 +118,8 @@ struct GateUp {
                 const int m = wm * C::WM + fm * 32 + FS::pass_row(p, lane);
                 const int cc = FS::pass_col(lane);
                 if (m < t.mt.rows && cc < C::WN / 2)
-                    *reinterpret_cast<uint2 *>(aring + ((int64_t)t.slot * MB + t.rowoff + m) * I + ib + cc) =
-                        FS::get(area + FS::pass_off(p, lane));
+                    store8_nt(aring + ((int64_t)t.slot * MB + t.rowoff + m) * I + ib + cc,
+                              FS::get(area + FS::pass_off(p, lane)));
             }
         }
     }
@@ -150,9 +150,9 @@ struct Down {
     int n0, nk, H;
     Args a;
 
-    __device__ bool setup(const Args &args) {
+    __device__ bool setup(const Args &args, Blk b) {
         SegTile tt;
-        if (!decode_seg_tile(args.v, args.g0, args.g1, args.n_slots, args.n_tiles, tt)) return false;
+        if (!decode_seg_tile(args.v, args.g0, args.g1, args.n_slots, args.n_tiles, b.x, tt)) return false;
         init(args, tt);
         return true;
     }
@@ -173,7 +173,7 @@ struct Down {
     }
     __device__ int wrow(int wn, int fn) const { return wn * C::WN + fn * 32; }
     __device__ void epilogue(f32x16_t (&acc)[C::FM][C::FN], int wm, int wn) {
-        store_token_rows<C>(acc, t, n0, wm, wn, a.v, H, a.k, a.MT, a.nb_full, a.topk_w, true, a.out, a.stage);
+        store_token_rows<C, C::LDS_BYTES>(acc, t, n0, wm, wn, a.v, H, a.k, a.MT, a.nb_full, a.topk_w, true, a.out, a.stage);
     }
 };
 
@@ -203,9 +203,9 @@ struct DA {
     int i0, nk;
     Args a;
 
-    __device__ bool setup(const Args &args) {
+    __device__ bool setup(const Args &args, Blk b) {
         SegTile tt;
-        if (!decode_seg_tile(args.v, args.g0, args.g1, args.n_slots, args.n_tiles, tt)) return false;
+        if (!decode_seg_tile(args.v, args.g0, args.g1, args.n_slots, args.n_tiles, b.x, tt)) return false;
         init(args, tt);
         return true;
     }
@@ -228,8 +228,8 @@ struct DA {
     // SwiGLU backward of the tile, staged through LDS per 32-row fragment
     // (FragStage): h rows come in and dh, g*a rows leave as whole row runs.
     __device__ void epilogue(f32x16_t (&acc)[C::FM][C::FN], int wm, int wn) {
-        using FS = FragStage<C>;
-        const int lane = threadIdx.x & 63;
+        using FS = FragStage<C, C::LDS_BYTES>;
+        const int lane = epi_lane();
         const int I = a.I;
         const int slice = t.nt * C::WAVES_N + wn;
         const int ib = i0 + wn * C::WN;
@@ -294,9 +294,9 @@ struct DA {
                 if (m < t.mt.rows) {
                     const int64_t c = t.mt.c0 + m;   // dh and g*a rows are kept in canonical order
                     const uint32_t o = FS::pass_off(p, lane);
-                    *reinterpret_cast<uint2 *>(a.dh + c * 2 * I + ib + cc) = FS::get(sg + o);
-                    *reinterpret_cast<uint2 *>(a.dh + c * 2 * I + I + ib + cc) = FS::get(su + o);
-                    *reinterpret_cast<uint2 *>(a.ga + c * I + ib + cc) = FS::get(sa + o);
+                    store8_nt(a.dh + c * 2 * I + ib + cc, FS::get(sg + o));
+                    store8_nt(a.dh + c * 2 * I + I + ib + cc, FS::get(su + o));
+                    store8_nt(a.ga + c * I + ib + cc, FS::get(sa + o));
                 }
             }
             // lanes l and l ^ 32 hold the same row: lower half + upper half, fixed order
@@ -331,9 +331,9 @@ struct DX {
     int n0, nk, I;
     Args a;
 
-    __device__ bool setup(const Args &args) {
+    __device__ bool setup(const Args &args, Blk b) {
         SegTile tt;
-        if (!decode_seg_tile(args.v, args.g0, args.g1, args.n_slots, args.n_tiles, tt)) return false;
+        if (!decode_seg_tile(args.v, args.g0, args.g1, args.n_slots, args.n_tiles, b.x, tt)) return false;
         init(args, tt);
         return true;
     }
@@ -355,7 +355,7 @@ struct DX {
     }
     __device__ int wrow(int wn, int fn) const { return wn * C::WN + fn * 32; }
     __device__ void epilogue(f32x16_t (&acc)[C::FM][C::FN], int wm, int wn) {
-        store_token_rows<C>(acc, t, n0, wm, wn, a.v, a.H, a.k, a.MT, a.nb_full, nullptr, false, a.dx, a.stage);
+        store_token_rows<C, C::LDS_BYTES>(acc, t, n0, wm, wn, a.v, a.H, a.k, a.MT, a.nb_full, nullptr, false, a.dx, a.stage);
     }
 };
 
@@ -381,12 +381,12 @@ struct WGU {
     int e, h0, n0, ne, off, nk;
     Args a;
 
-    __device__ bool setup(const Args &args) {
+    __device__ bool setup(const Args &args, Blk b) {
         if (*args.v.status) return false;
         a = args;
-        e = blockIdx.z;
-        h0 = blockIdx.y * C::BM;
-        n0 = blockIdx.x * C::BN;
+        e = b.z;
+        h0 = b.y * C::BM;
+        n0 = b.x * C::BN;
         ne = args.v.counts[e];
         off = args.v.offsets[e];
         nk = (ne + C::BK - 1) / C::BK;
@@ -405,7 +405,7 @@ struct WGU {
         const int nb = n0 + wn * C::WN;
         if (nb >= 2 * I) return;   // I % 64 == 0: the wave's columns are all gate, all up or all past 2I
         uint16_t *base = nb < I ? a.dwg + nb : a.dwu + (nb - I);
-        staged_rows<C>([&](int fm, int fn, int g4, int j) { return acc[fm][fn][g4 * 4 + j]; },
+        staged_rows<C, C::LDS_BYTES>([&](int fm, int fn, int g4, int j) { return acc[fm][fn][g4 * 4 + j]; },
                        [&](int fm, int r) -> uint16_t * {
                            const int hh = h0 + wm * C::WM + fm * 32 + r;
                            return hh < H ? base + ((int64_t)e * H + hh) * I : nullptr;
@@ -432,12 +432,12 @@ struct WD {
     int e, i0, n0, ne, off, nk;
     Args a;
 
-    __device__ bool setup(const Args &args) {
+    __device__ bool setup(const Args &args, Blk b) {
         if (*args.v.status) return false;
         a = args;
-        e = blockIdx.z;
-        i0 = blockIdx.y * C::BM;
-        n0 = blockIdx.x * C::BN;
+        e = b.z;
+        i0 = b.y * C::BM;
+        n0 = b.x * C::BN;
         ne = args.v.counts[e];
         off = args.v.offsets[e];
         nk = (ne + C::BK - 1) / C::BK;
@@ -454,7 +454,7 @@ struct WD {
         const int H = a.H, I = a.I;
         const int nb = n0 + wn * C::WN;
         if (nb >= H) return;   // H % 64 == 0
-        staged_rows<C>([&](int fm, int fn, int g4, int j) { return acc[fm][fn][g4 * 4 + j]; },
+        staged_rows<C, C::LDS_BYTES>([&](int fm, int fn, int g4, int j) { return acc[fm][fn][g4 * 4 + j]; },
                        [&](int fm, int r) -> uint16_t * {
                            const int ii = i0 + wm * C::WM + fm * 32 + r;
                            return ii < I ? a.dwd + ((int64_t)e * I + ii) * H + nb : nullptr;

@@ -147,9 +147,9 @@ struct GateUp8 {
     int i0, nk;
     Args a;
 
-    __device__ bool setup(const Args &args) {
+    __device__ bool setup(const Args &args, Blk b) {
         SegTile tt;
-        if (!decode_seg_tile(args.v, args.g0, args.g1, args.n_slots, args.n_tiles, tt)) return false;
+        if (!decode_seg_tile(args.v, args.g0, args.g1, args.n_slots, args.n_tiles, b.x, tt)) return false;
         init(args, tt);
         return true;
     }
@@ -246,9 +246,9 @@ struct Down8 {
     int n0, nk;
     Args a;
 
-    __device__ bool setup(const Args &args) {
+    __device__ bool setup(const Args &args, Blk b) {
         SegTile tt;
-        if (!decode_seg_tile(args.v, args.g0, args.g1, args.n_slots, args.n_tiles, tt)) return false;
+        if (!decode_seg_tile(args.v, args.g0, args.g1, args.n_slots, args.n_tiles, b.x, tt)) return false;
         init(args, tt);
         return true;
     }
@@ -273,7 +273,7 @@ struct Down8 {
     }
     __device__ int wrow(int wn, int fn) const { return wn * C::WN + fn * 32; }
     __device__ void epilogue(f32x16_t (&acc)[C::FM][C::FN], int wm, int wn) {
-        store_token_rows<C>(acc, t, n0, wm, wn, a.v, a.H, a.k, a.MT, a.nb_full, a.topk_w, true, a.out, a.stage);
+        store_token_rows<C, Fp8Stage<C>::LDS_BYTES>(acc, t, n0, wm, wn, a.v, a.H, a.k, a.MT, a.nb_full, a.topk_w, true, a.out, a.stage);
     }
 };
 
@@ -306,9 +306,9 @@ struct DA8 {
     int i0, nk;
     Args a;
 
-    __device__ bool setup(const Args &args) {
+    __device__ bool setup(const Args &args, Blk b) {
         SegTile tt;
-        if (!decode_seg_tile(args.v, args.g0, args.g1, args.n_slots, args.n_tiles, tt)) return false;
+        if (!decode_seg_tile(args.v, args.g0, args.g1, args.n_slots, args.n_tiles, b.x, tt)) return false;
         init(args, tt);
         return true;
     }
@@ -437,9 +437,9 @@ struct DX8 {
     int n0, nk;
     Args a;
 
-    __device__ bool setup(const Args &args) {
+    __device__ bool setup(const Args &args, Blk b) {
         SegTile tt;
-        if (!decode_seg_tile(args.v, args.g0, args.g1, args.n_slots, args.n_tiles, tt)) return false;
+        if (!decode_seg_tile(args.v, args.g0, args.g1, args.n_slots, args.n_tiles, b.x, tt)) return false;
         init(args, tt);
         return true;
     }
@@ -465,7 +465,7 @@ struct DX8 {
     }
     __device__ int wrow(int wn, int fn) const { return wn * C::WN + fn * 32; }
     __device__ void epilogue(f32x16_t (&acc)[C::FM][C::FN], int wm, int wn) {
-        store_token_rows<C>(acc, t, n0, wm, wn, a.v, a.H, a.k, a.MT, a.nb_full, nullptr, false, a.dx, a.stage);
+        store_token_rows<C, Fp8Stage<C>::LDS_BYTES>(acc, t, n0, wm, wn, a.v, a.H, a.k, a.MT, a.nb_full, nullptr, false, a.dx, a.stage);
     }
 };
 

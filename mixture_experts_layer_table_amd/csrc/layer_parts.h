@@ -32,11 +32,11 @@ constexpr int kGroupM = 4;     // m-tiles per group of the tile order
 // tiles, ordered in groups of kGroupM m-tiles x all n-tiles: the tiles an XCD
 // runs together share few operand slices in its L2.
 __device__ __forceinline__ bool decode_seg_tile(const SchedView &v, int g0, int g1, int64_t n_slots, int n_tiles,
-                                                SegTile &t) {
+                                                int b, SegTile &t) {
     if (*v.status) return false;
     const int lo = v.mtfirst[g0], mtc = v.mtfirst[g1] - lo;
     const int total = mtc * n_tiles;                      // tiles that exist (device-side count)
-    const int per = (total + kXcds - 1) / kXcds, b = (int)blockIdx.x;
+    const int per = (total + kXcds - 1) / kXcds;
     if (b / kXcds >= per) return false;                   // the grid is a host-side upper bound
     const int id = (b % kXcds) * per + b / kXcds;
     if (id >= total) return false;
@@ -86,26 +86,38 @@ struct HBatch {
 // Epilogue output and input pass through LDS one 32-row fragment at a time,
 // so that global memory sees whole 128-byte row runs: a fragment's
 // accumulators hold 32 rows x 4 columns per lane, and storing them directly
-// writes 8-byte pieces of 32 rows per instruction. Each wave uses its own
-// area of the tile's LDS, which is free once every wave has passed the last
-// barrier of the K loop (no stage is read or loaded after it); no barrier is
-// needed because a wave's LDS accesses complete in order. Rows are padded to
-// WN*2 + 8 bytes: the 32 lanes that hold one column group of 32 rows then
-// fall on 32 distinct bank pairs.
-template <class C>
+// writes 8-byte pieces of 32 rows per instruction. Each wave has its own
+// 4 KiB area per array ([32 rows][64 columns] bf16); the areas of all waves
+// sit at the end of the tile's LDS (LDS_END), inside the last pipeline
+// stage(s), which no load targets once every wave has passed the last
+// barrier of the K loop. A wave's LDS accesses complete in order, so no
+// barrier is needed inside the epilogue. The 8-byte unit u of row r is kept
+// at unit u ^ (r % 16): the 32 lanes that hold one column group of 32 rows
+// then fall on distinct bank pairs (two rows per pair).
+// Lane index as a value the compiler cannot see through: epilogue offsets
+// derived from it are computed where they are used instead of being hoisted
+// out of a persistent kernel's tile loop and kept live across the K loop.
+__device__ __forceinline__ int epi_lane() {
+    int l = (int)(threadIdx.x & 63);
+    asm volatile("" : "+v"(l));
+    return l;
+}
+
+template <class C, size_t LDS_END>
 struct FragStage {
-    static constexpr int STRIDE = C::WN * 2 + 8;      // bytes per staged row
-    static constexpr int BYTES = 32 * STRIDE;         // one 32-row array
-    static constexpr int LPR = C::WN / 4;             // lanes per row in a row pass (8 bytes each)
+    static_assert(C::WN == 64, "one staged row is 128 bytes");
+    static constexpr int ROW = 128;                   // bytes per staged row
+    static constexpr int BYTES = 32 * ROW;            // one array of one wave
+    static constexpr int LPR = 16;                    // lanes per row in a row pass (8 bytes each)
     static constexpr int RPP = 64 / LPR;              // rows per row pass
     static constexpr int PASSES = 32 / RPP;
-    static_assert(64 % LPR == 0 && 32 % RPP == 0, "row passes must tile the fragment");
 
     // dynamic LDS starts at offset 0 in every kernel that runs these tiles
     static __device__ __forceinline__ uint32_t area(int wave, int narrays) {
+        static_assert(LDS_END >= (size_t)C::NT / 64 * BYTES, "staging must fit the tile's LDS");
         extern __shared__ __attribute__((aligned(1024))) char lds_raw[];
-        return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)lds_raw +
-               (uint32_t)(wave * narrays * BYTES);
+        return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)lds_raw + (uint32_t)LDS_END -
+               (uint32_t)((C::NT / 64 - wave) * narrays * BYTES);
     }
     typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
     static __device__ __forceinline__ void put(uint32_t a, uint2 v) {
@@ -118,16 +130,15 @@ struct FragStage {
         const u32x2_t w = *reinterpret_cast<const __attribute__((address_space(3))) u32x2_t *>((uintptr_t)a);
         return make_uint2(w.x, w.y);
     }
+    static __device__ __forceinline__ uint32_t at(int r, int u) { return (uint32_t)(r * ROW + ((u ^ (r & 15)) << 3)); }
     // fragment layout: 4 columns (fn, g4) of row lane % 32
     static __device__ __forceinline__ uint32_t frag_off(int fn, int g4, int lane) {
-        return (uint32_t)((lane & 31) * STRIDE + (fn * 32 + g4 * 8 + (lane >> 5) * 4) * 2);
+        return at(lane & 31, fn * 8 + g4 * 2 + (lane >> 5));
     }
     // row-pass layout: pass p covers rows p*RPP .. p*RPP+RPP-1, 4 columns per lane
     static __device__ __forceinline__ int pass_row(int p, int lane) { return p * RPP + lane / LPR; }
     static __device__ __forceinline__ int pass_col(int lane) { return (lane % LPR) * 4; }
-    static __device__ __forceinline__ uint32_t pass_off(int p, int lane) {
-        return (uint32_t)(pass_row(p, lane) * STRIDE + pass_col(lane) * 2);
-    }
+    static __device__ __forceinline__ uint32_t pass_off(int p, int lane) { return at(pass_row(p, lane), lane % LPR); }
 };
 
 // One wave's share of a tile leaves as rows, through its FragStage area:
@@ -136,10 +147,21 @@ struct FragStage {
 // row_dst(fm, r) the destination of wave column 0 of fragment row r (nullptr:
 // row not stored). Every column of the wave is stored (callers return early
 // for waves whose columns lie past the output's width).
-template <class C, class Val, class Dst>
+// 8-byte row-run store of epilogue output with the non-temporal hint: output
+// rows are not read again by this kernel, and keeping them out of the L2's
+// retained lines leaves room for the operand slices that tiles share.
+__device__ __forceinline__ void store8_nt(uint16_t *p, uint2 v) {
+    typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+    v2u w;
+    w.x = v.x;
+    w.y = v.y;
+    __builtin_nontemporal_store(w, reinterpret_cast<v2u *>(p));
+}
+
+template <class C, size_t LDS_END, class Val, class Dst>
 __device__ __forceinline__ void staged_rows(Val value, Dst row_dst) {
-    using FS = FragStage<C>;
-    const int lane = threadIdx.x & 63;
+    using FS = FragStage<C, LDS_END>;
+    const int lane = epi_lane();
     const uint32_t area = FS::area(wave_id(), 1);
 #pragma unroll
     for (int fm = 0; fm < C::FM; ++fm) {
@@ -155,7 +177,7 @@ __device__ __forceinline__ void staged_rows(Val value, Dst row_dst) {
 #pragma unroll
         for (int p = 0; p < FS::PASSES; ++p) {
             uint16_t *d = row_dst(fm, FS::pass_row(p, lane));
-            if (d) *reinterpret_cast<uint2 *>(d + FS::pass_col(lane)) = FS::get(area + FS::pass_off(p, lane));
+            if (d) store8_nt(d + FS::pass_col(lane), FS::get(area + FS::pass_off(p, lane)));
         }
     }
 }
@@ -170,12 +192,12 @@ __device__ __forceinline__ float bf16_at(const uint2 &v, int j) {
 // towards token order. k == 1: straight to the token's row, the forward one
 // scaled by its gate weight after rounding y to bf16 (the weighted combine);
 // k > 1: into the macro-batch's staging rows, combined later in j order.
-template <class C>
+template <class C, size_t LDS_END>
 __device__ __forceinline__ void store_token_rows(const f32x16_t (&acc)[C::FM][C::FN], const SegTile &t, int n0,
                                                  int wm, int wn, const SchedView &v, int H, int k, int MT,
                                                  int nb_full, const float *topk_w, bool weighted, uint16_t *dst_k1,
                                                  uint16_t *stage) {
-    const int lane = threadIdx.x & 63;
+    const int lane = epi_lane();
     const int nb = n0 + wn * C::WN;
     if (nb >= H) return;   // H % 64 == 0: the wave's columns are all valid or all past H
     float gw[C::FM];
@@ -185,7 +207,7 @@ __device__ __forceinline__ void store_token_rows(const f32x16_t (&acc)[C::FM][C:
         gw[fm] = (weighted && k == 1 && m < t.mt.rows) ? topk_w[v.perm[t.mt.q0 + m]] : 1.0f;
     }
     const int64_t sbase = (int64_t)k * ((t.mt.g / nb_full) * (int64_t)MT);
-    staged_rows<C>(
+    staged_rows<C, LDS_END>(
         [&](int fm, int fn, int g4, int j) {
             const float y = acc[fm][fn][g4 * 4 + j];
             return (weighted && k == 1) ? gw[fm] * bf16r(y) : y;   // y rows are bf16
