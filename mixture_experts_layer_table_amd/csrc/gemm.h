@@ -356,37 +356,51 @@ struct Frags {
 
 __device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-// One output tile. P provides: C, Args, X_TRANS, W_TRANS, LOADS_PER_STAGE
-// (vector-memory instructions one wave issues per stage), nk,
-// issue(kt, stage_lds_address), wrow(wn, fn), epilogue(acc, wm, wn), and
-// for gemm_kernel setup(args) -> bool.
-//
-// Ping-pong schedule. The two waves that share a SIMD belong to different
-// groups (wm = 0 and wm = 1) and run half a stage apart around one barrier
-// per stage (stage = kt % NSTAGE; loads run 3 stages ahead):
-//   group 0: MFMAs(stage kt) | wait own loads of kt+1 | barrier | issue kt+3, read fragments(kt+1)
-//   group 1: issue kt+3, read fragments(kt) | wait own loads of kt+1 | barrier | MFMAs(stage kt)
-// While one group waits at the barrier or for its fragment reads, the other
-// group's MFMAs keep the SIMD's matrix core busy.
-// Ordering: every wave waits for its own loads of stage kt+1 before barrier
-// kt, so stage kt+1 is visible after it (group 0 reads it right away, group 1
-// in its next iteration). Slot kt-1 is refilled (with stage kt+3) after
-// barrier kt-1 by group 1 and after barrier kt by group 0; every read of stage
-// kt-1 has landed before barrier kt-1: group 0 consumed its fragments in the
-// MFMAs before that barrier, and group 1 waits for its reads (lgkmcnt) right
-// before it.
 // Block coordinates of a tile (the launch grid's, or a persistent kernel's
 // virtual grid).
 struct Blk {
     int x, y, z;
 };
 
+// One output tile. P provides: C, Args, X_TRANS, W_TRANS, LOADS_PER_STAGE
+// (vector-memory instructions one wave issues per stage), nk,
+// issue(kt, stage_lds_address), wrow(wn, fn), epilogue(acc, wm, wn), and
+// for gemm_kernel setup(args) -> bool.
+//
+// Ping-pong schedule. The two wave groups (wm = 0 and wm = 1) run half a
+// stage apart around one barrier per stage (stage = kt % NSTAGE; loads run
+// D = NSTAGE - 1 stages ahead):
+//   group 0: MFMAs(stage kt) | wait own loads of kt+1 | barrier | issue kt+D, read fragments(kt+1)
+//   group 1: issue kt+D, read fragments(kt) | wait own loads of kt+1 | barrier | MFMAs(stage kt)
+// While one group waits at the barrier or for its fragment reads, the other
+// group's MFMAs keep the matrix cores busy.
+// Ordering: every wave waits for its own loads of stage kt+1 before barrier
+// kt, so stage kt+1 is visible after it (group 0 reads it right away, group 1
+// in its next iteration). Slot kt-1 is refilled (with stage kt+D) after
+// barrier kt-1 by group 1 and after barrier kt by group 0; every read of stage
+// kt-1 has landed before barrier kt-1: group 0 consumed its fragments in the
+// MFMAs before that barrier, and group 1 waits for its reads (lgkmcnt) right
+// before it.
+// s_waitcnt for "at most n stages of L loads still in flight" (n wave-uniform, 0 <= n).
+template <int L, int MAXN>
+__device__ __forceinline__ void wait_stages(int n) {
+    if constexpr (MAXN > 0) {
+        if (n >= MAXN) {
+            wait_vmcnt<MAXN * L>();
+            return;
+        }
+        wait_stages<L, MAXN - 1>(n);
+    } else {
+        wait_vmcnt<0>();
+    }
+}
+
 // K loop of one tile into acc.
 template <class P>
 __device__ __forceinline__ void gemm_mainloop(P &p, uint32_t lds, f32x16_t (&acc)[P::C::FM][P::C::FN]) {
     using C = typename P::C;
-    static_assert(C::WAVES_M == 2 && C::NSTAGE == 4, "two wave groups, 4-stage ring");
-    constexpr int L = P::LOADS_PER_STAGE;
+    static_assert(C::WAVES_M == 2, "two wave groups");
+    constexpr int L = P::LOADS_PER_STAGE, D = C::NSTAGE - 1;
 #pragma unroll
     for (int fm = 0; fm < C::FM; ++fm)
 #pragma unroll
@@ -407,12 +421,10 @@ __device__ __forceinline__ void gemm_mainloop(P &p, uint32_t lds, f32x16_t (&acc
         f1.mma(acc);
     };
 #pragma unroll
-    for (int s = 0; s < 3; ++s)
+    for (int s = 0; s < D; ++s)
         if (s < nk) p.issue(s, stage(s));
     if (nk > 0) {
-        if (nk >= 3) wait_vmcnt<2 * L>();
-        else if (nk == 2) wait_vmcnt<L>();
-        else wait_vmcnt<0>();
+        wait_stages<L, D - 1>(min(D, nk) - 1);   // stage 0 landed
         lds_barrier();
     }
     if (wm == 0) {
@@ -421,21 +433,19 @@ __device__ __forceinline__ void gemm_mainloop(P &p, uint32_t lds, f32x16_t (&acc
             __builtin_amdgcn_sched_barrier(0);
             mma_stage();
             __builtin_amdgcn_sched_barrier(0);
-            // own loads issued so far: up to stage kt + 2; stage kt + 1 must have landed
-            if (kt + 2 < nk) wait_vmcnt<L>();
+            // own loads issued so far: up to stage kt + D - 1; stage kt + 1 must have landed
+            if constexpr (D >= 2) wait_stages<L, D - 2>(max(0, min(D - 2, nk - 2 - kt)));
             else wait_vmcnt<0>();
             lds_barrier();
-            if (kt + 3 < nk) p.issue(kt + 3, stage(kt + 3));
+            if (kt + D < nk) p.issue(kt + D, stage(kt + D));
             if (kt + 1 < nk) read_stage(kt + 1);
         }
     } else {
         for (int kt = 0; kt < nk; ++kt) {
-            if (kt + 3 < nk) p.issue(kt + 3, stage(kt + 3));
+            if (kt + D < nk) p.issue(kt + D, stage(kt + D));
             read_stage(kt);
-            // own loads issued so far: up to stage kt + 3; stage kt + 1 must have landed
-            if (kt + 3 < nk) wait_vmcnt<2 * L>();
-            else if (kt + 2 < nk) wait_vmcnt<L>();
-            else wait_vmcnt<0>();
+            // own loads issued so far: up to stage kt + D; stage kt + 1 must have landed
+            wait_stages<L, D - 1>(max(0, min(D - 1, nk - 2 - kt)));
             wait_lgkm0();   // fragment reads of stage kt landed: the slot is refilled right after this barrier
             lds_barrier();
             __builtin_amdgcn_sched_barrier(0);
@@ -456,8 +466,10 @@ __device__ __forceinline__ void gemm_tile(P &p, uint32_t lds) {
 }
 
 // One tile per workgroup; P::setup(args, block) picks the tile (false: no tile).
+// Two waves per SIMD (at most 256 registers each): two 4-wave workgroups, or
+// one 8-wave workgroup, per compute unit.
 template <class P>
-__global__ __launch_bounds__(P::C::NT) void gemm_kernel(typename P::Args args) {
+__global__ __launch_bounds__(P::C::NT, 2) void gemm_kernel(typename P::Args args) {
     extern __shared__ __attribute__((aligned(1024))) char lds_raw[];
     const uint32_t lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)lds_raw;
     P p;
