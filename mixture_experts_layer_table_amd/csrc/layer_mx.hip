@@ -179,35 +179,38 @@ struct GateUp8 {
         return fn < C::FN / 2 ? wn * (C::WN / 2) + fn * 32 : C::BN / 2 + wn * (C::WN / 2) + (fn - C::FN / 2) * 32;
     }
     __device__ void epilogue(f32x16_t (&acc)[C::FM][C::FN], int wm, int wn) {
-        const int lane = threadIdx.x & 63, I = a.I;
+        constexpr size_t END = Fp8Stage<C>::LDS_BYTES;
+        const int I = a.I;
+        const int ib0 = i0 + wn * (C::WN / 2);
+        if (ib0 >= I) return;   // I % 128 == 0: the wave's i are all valid or all past I
+        // h rows (gate columns to h[.., i], up columns to h[.., I + i]) through LDS
+        staged_rows<C, END>([&](int fm, int fn, int g4, int j) { return acc[fm][fn][g4 * 4 + j]; },
+                            [&](int fm, int r) -> uint16_t * {
+                                const int m = wm * C::WM + fm * 32 + r;
+                                if (m >= t.mt.rows) return nullptr;
+                                const bool up = FragStage<C, END>::pass_col(epi_lane()) >= C::WN / 2;
+                                return a.h + (int64_t)(t.mt.q0 + m) * 2 * I + ib0 + (up ? I - C::WN / 2 : 0);
+                            });
+        // a, quantized along i: fp8 codes and one scale per 32-block, stored directly
+        const int lane = epi_lane();
         uint8_t *aslot = a.aring + t.slot * (int64_t)a.MB * I * 2;
 #pragma unroll
         for (int fm = 0; fm < C::FM; ++fm) {
             const int m = wm * C::WM + fm * 32 + (lane & 31);
             const bool ok = m < t.mt.rows;   // same for lanes l and l ^ 32
-            const int64_t q = t.mt.q0 + m;
-            uint16_t *hrow = a.h + q * 2 * I;
             uint8_t *ael = aslot + (int64_t)(t.rowoff + m) * I;
             uint8_t *asc = aslot + (int64_t)a.MB * I + (int64_t)(t.rowoff + m) * (I / 32);
 #pragma unroll
             for (int fn = 0; fn < C::FN / 2; ++fn) {
-                const int ib = i0 + wn * (C::WN / 2) + fn * 32;   // one 32-block of i
+                const int ib = ib0 + fn * 32;   // one 32-block of i
                 Block16 av;
 #pragma unroll
-                for (int g4 = 0; g4 < 4; ++g4) {
-                    const int i = ib + g4 * 8 + (lane >> 5) * 4;
-                    float hg[4], hu[4];
+                for (int g4 = 0; g4 < 4; ++g4)
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        hg[j] = acc[fm][fn][g4 * 4 + j];
-                        hu[j] = acc[fm][fn + C::FN / 2][g4 * 4 + j];
-                        av.v[g4 * 4 + j] = hg[j] * sigmoidf_(hg[j]) * hu[j];
+                        const float hg = acc[fm][fn][g4 * 4 + j], hu = acc[fm][fn + C::FN / 2][g4 * 4 + j];
+                        av.v[g4 * 4 + j] = hg * sigmoidf_(hg) * hu;
                     }
-                    if (ok) {
-                        store4_bf16(hrow + i, hg[0], hg[1], hg[2], hg[3]);
-                        store4_bf16(hrow + I + i, hu[0], hu[1], hu[2], hu[3]);
-                    }
-                }
                 const Enc16 q8 = quantize_block16(av);
                 if (ok) {
 #pragma unroll
