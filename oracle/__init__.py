@@ -22,10 +22,12 @@ Modules:
   schedule  — O1, the schedule table (integer result, compared bit-exactly)
   layer     — O2/O3, forward and backward in fp64
   mxfp8     — O4, the MXFP8 codec and fake-quant
+  router    — O5, the router front-end (softmax, top-k, renormalisation) and
+              its logit gradient
 
 Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 against values fixed outside the oracle (closed forms, brute force, finite
 differences, an independent autograd formulation, library casts); none is
 "parity unpinned".
 """
-from . import schedule, layer, mxfp8  # noqa: F401
+from . import schedule, layer, mxfp8, router  # noqa: F401
