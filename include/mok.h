@@ -238,6 +238,35 @@ mok_status mok_mxfp8_quantize(const void *src, int64_t batch, int64_t rows, int6
                               void *stream);
 
 /*
+ * Router front-end: the step before schedule building, which takes the top-k
+ * expert choice as input ("Mixture-of-Kittens (MoK)" project summary,
+ * Functional API; "Mixture-of-Kittens(MoK)란?" explainer, section 1: each
+ * token activates a few experts). The pages leave the router's formula open;
+ * this is softmax over all E experts, the k largest logits, and weights
+ * renormalised over the chosen k:
+ *   topk_ids[t, j]  the j-th largest logit of row t (the lower expert index
+ *                   first among equal logits)
+ *   topk_w[t, j]    exp(l_j - m) / sum_i exp(l_i - m) over the chosen i,
+ *                   m = the row's largest logit (fp32)
+ *   logits          device fp32 [T, E], row-major, finite
+ *   topk_ids        device int32 [T, k];  topk_w  device fp32 [T, k]
+ * 1 <= k <= min(E, 64), E <= 1024; T == 0 is a no-op. Bitwise deterministic.
+ */
+mok_status mok_route(const float *logits, int64_t T, int32_t E, int32_t k, int32_t *topk_ids,
+                     float *topk_w, void *stream);
+
+/*
+ * Logit gradient of mok_route (the choice is piecewise constant):
+ *   dlogits[t, e] = w_e * (dtopk_w_e - sum_j w_j * dtopk_w_j)  for chosen e,
+ *                   0 for every other expert
+ * topk_ids and topk_w as mok_route returned them, dtopk_w device fp32 [T, k]
+ * (for instance mok_backward's dtopk_w); dlogits device fp32 [T, E], every
+ * entry written. Same limits as mok_route.
+ */
+mok_status mok_route_backward(const int32_t *topk_ids, const float *topk_w, const float *dtopk_w,
+                              int64_t T, int32_t E, int32_t k, float *dlogits, void *stream);
+
+/*
  * Measurement aid, not part of the layer: per-kernel durations for tools such
  * as benchmarks. While enabled, every kernel launch of the library is
  * bracketed by two HIP events recorded on the launch's own stream (the

@@ -40,8 +40,9 @@ MOK_SCHEDULE_OVERFLOW, MOK_BAD_EXPERT_ID, MOK_SCHEDULER_STALLED = 1, 2, 4
 MOK_DEBUG_IDENTITY_EXPERT, MOK_DEBUG_SEPARATE_LAUNCHES, MOK_DEBUG_WHOLE_PASS = 1, 2, 4
 
 EXPORTS = ("mok_config_default", "mok_query_sizes", "mok_schedule_layout_query",
-           "mok_build_schedule", "mok_forward", "mok_backward", "mok_mxfp8_quantize",
-           "mok_status_string", "mok_kernel_timing_enable", "mok_kernel_timing_read", "mok_last_error")
+           "mok_build_schedule", "mok_forward", "mok_backward", "mok_mxfp8_quantize", "mok_route",
+           "mok_route_backward", "mok_status_string", "mok_kernel_timing_enable", "mok_kernel_timing_read",
+           "mok_last_error")
 
 
 class mok_config(ctypes.Structure):
@@ -90,6 +91,8 @@ _sigs = {
                      _P, _P],
     "mok_mxfp8_quantize": [_P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
                            _P, _P, _P],
+    "mok_route": [_P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _P, _P, _P],
+    "mok_route_backward": [_P, _P, _P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _P, _P],
     "mok_kernel_timing_enable": [ctypes.c_int32],
     "mok_kernel_timing_read": [ctypes.POINTER(mok_kernel_stat), ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)],
 }
@@ -157,6 +160,14 @@ def mok_backward(cfg, shape, schedule, workspace, workspace_bytes, x, topk_w, we
 
 def mok_mxfp8_quantize(src, batch, rows, K, src_is_k_by_rows, elems, scales, stream):
     return _lib.mok_mxfp8_quantize(src, batch, rows, K, src_is_k_by_rows, elems, scales, stream)
+
+
+def mok_route(logits, T, E, k, topk_ids, topk_w, stream):
+    return _lib.mok_route(logits, T, E, k, topk_ids, topk_w, stream)
+
+
+def mok_route_backward(topk_ids, topk_w, dtopk_w, T, E, k, dlogits, stream):
+    return _lib.mok_route_backward(topk_ids, topk_w, dtopk_w, T, E, k, dlogits, stream)
 
 
 def mok_kernel_timing_enable(enable):
@@ -325,6 +336,28 @@ def mxfp8_quantize(src, src_is_k_by_rows: bool):
     _check(mok_mxfp8_quantize(_ptr(src), B, rows, K, int(src_is_k_by_rows), _ptr(elems), _ptr(scales),
                               _stream()), "mok_mxfp8_quantize")
     return elems, scales
+
+
+def route(logits, k: int):
+    """logits fp32 [T, E] on the device. Returns (topk_ids int32 [T, k],
+    topk_w fp32 [T, k]): the k largest logits per row and their softmax weights
+    renormalised over the chosen k."""
+    import torch
+    T, E = logits.shape
+    ids = torch.empty((T, k), dtype=torch.int32, device=logits.device)
+    w = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+    _check(mok_route(_ptr(logits), T, E, k, _ptr(ids), _ptr(w), _stream()), "mok_route")
+    return ids, w
+
+
+def route_backward(topk_ids, topk_w, dtopk_w, E: int):
+    """Logit gradient fp32 [T, E] of route() for the upstream gradient dtopk_w [T, k]."""
+    import torch
+    T, k = topk_ids.shape
+    dl = torch.empty((T, E), dtype=torch.float32, device=topk_ids.device)
+    _check(mok_route_backward(_ptr(topk_ids), _ptr(topk_w), _ptr(dtopk_w), T, E, k, _ptr(dl), _stream()),
+           "mok_route_backward")
+    return dl
 
 
 def read_schedule(schedule, layout: mok_schedule_layout, E: int):

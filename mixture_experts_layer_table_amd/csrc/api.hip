@@ -9,6 +9,7 @@ using namespace mok;
 namespace {
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void *p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 bool dev_ok(const void *p) { return p != nullptr && aligned16(p); }
 
 }  // namespace
@@ -129,6 +130,25 @@ mok_status mok_mxfp8_quantize(const void *src, int64_t batch, int64_t rows, int6
     (void)hipGetLastError();
     return launch_mxfp8_quantize(static_cast<const uint16_t *>(src), batch, rows, K, src_is_k_by_rows == 1, elems,
                                  scales, static_cast<hipStream_t>(stream));
+}
+
+mok_status mok_route(const float *logits, int64_t T, int32_t E, int32_t k, int32_t *topk_ids, float *topk_w,
+                     void *stream) {
+    if (T < 0 || E < 1 || E > 1024 || k < 1 || k > E || k > 64) return MOK_ERROR_INVALID_VALUE;
+    if (T == 0) return MOK_OK;
+    if (!aligned4(logits) || !aligned4(topk_ids) || !aligned4(topk_w)) return MOK_ERROR_INVALID_VALUE;
+    (void)hipGetLastError();
+    return launch_route(logits, T, E, k, topk_ids, topk_w, static_cast<hipStream_t>(stream));
+}
+
+mok_status mok_route_backward(const int32_t *topk_ids, const float *topk_w, const float *dtopk_w, int64_t T,
+                              int32_t E, int32_t k, float *dlogits, void *stream) {
+    if (T < 0 || E < 1 || E > 1024 || k < 1 || k > E || k > 64) return MOK_ERROR_INVALID_VALUE;
+    if (T == 0) return MOK_OK;
+    if (!aligned4(topk_ids) || !aligned4(topk_w) || !aligned4(dtopk_w) || !aligned4(dlogits))
+        return MOK_ERROR_INVALID_VALUE;
+    (void)hipGetLastError();
+    return launch_route_backward(topk_ids, topk_w, dtopk_w, T, E, k, dlogits, static_cast<hipStream_t>(stream));
 }
 
 const char *mok_status_string(mok_status status) {

@@ -24,4 +24,9 @@ mok_status launch_backward(const Plan &p, const void *schedule, void *workspace,
 mok_status launch_mxfp8_quantize(const uint16_t *src, int64_t batch, int64_t rows, int64_t K,
                                  bool src_is_k_by_rows, uint8_t *elems, uint8_t *scales, hipStream_t st);
 
+mok_status launch_route(const float *logits, int64_t T, int E, int k, int32_t *ids, float *w, hipStream_t st);
+
+mok_status launch_route_backward(const int32_t *ids, const float *w, const float *dw, int64_t T, int E, int k,
+                                 float *dl, hipStream_t st);
+
 }  // namespace mok

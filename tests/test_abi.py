@@ -116,3 +116,14 @@ def test_mxfp8_needs_128_multiples():
             mok.query_sizes(mok.MoKConfig(precision=mok.MOK_MXFP8), 64, H, I, 8, 2)
         assert e.value.status == mok.MOK_ERROR_INVALID_VALUE
     mok.query_sizes(mok.MoKConfig(precision=mok.MOK_MXFP8), 64, 256, 128, 8, 2)
+
+
+def test_route_argument_checks():
+    # validation happens before any device call
+    bad = [(-1, 8, 2), (4, 0, 1), (4, 1025, 2), (4, 8, 0), (4, 8, 9), (4, 100, 65)]
+    for T, E, k in bad:
+        assert mok.mok_route(None, T, E, k, None, None, None) == mok.MOK_ERROR_INVALID_VALUE, (T, E, k)
+        assert mok.mok_route_backward(None, None, None, T, E, k, None, None) == mok.MOK_ERROR_INVALID_VALUE
+    assert mok.mok_route(None, 0, 8, 2, None, None, None) == mok.MOK_OK          # empty call
+    assert mok.mok_route(None, 3, 8, 2, None, None, None) == mok.MOK_ERROR_INVALID_VALUE   # null pointers
+    assert mok.mok_route_backward(None, None, None, 0, 8, 2, None, None) == mok.MOK_OK
