@@ -76,6 +76,12 @@ typedef enum mok_status {
    and the measured pass is slower than the gather kernel plus the
    persistent GEMM pair. */
 #define MOK_DEBUG_WHOLE_PASS 4u
+/* debug_flags: every wait inside the persistent kernels gives up at once, as
+   if its poll budget were spent. The call then ends with
+   MOK_SCHEDULER_STALLED in the status word, leaving the outputs that depend
+   on the abandoned waits unwritten. Tests the stall exit path; never for
+   production use. */
+#define MOK_DEBUG_FORCE_STALL 8u
 
 /*
  * Layer knobs ("Mixture-of-Kittens (MoK)" project summary, Key-concepts table:

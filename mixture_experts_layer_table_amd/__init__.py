@@ -37,7 +37,7 @@ MOK_OK, MOK_ERROR_INVALID_VALUE, MOK_ERROR_UNSUPPORTED, MOK_ERROR_BUFFER_TOO_SMA
     MOK_ERROR_LAUNCH_FAILED = range(5)
 MOK_BF16, MOK_MXFP8 = 0, 1
 MOK_SCHEDULE_OVERFLOW, MOK_BAD_EXPERT_ID, MOK_SCHEDULER_STALLED = 1, 2, 4
-MOK_DEBUG_IDENTITY_EXPERT, MOK_DEBUG_SEPARATE_LAUNCHES, MOK_DEBUG_WHOLE_PASS = 1, 2, 4
+MOK_DEBUG_IDENTITY_EXPERT, MOK_DEBUG_SEPARATE_LAUNCHES, MOK_DEBUG_WHOLE_PASS, MOK_DEBUG_FORCE_STALL = 1, 2, 4, 8
 
 EXPORTS = ("mok_config_default", "mok_query_sizes", "mok_schedule_layout_query",
            "mok_build_schedule", "mok_forward", "mok_backward", "mok_mxfp8_quantize", "mok_route",

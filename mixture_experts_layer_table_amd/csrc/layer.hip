@@ -625,7 +625,7 @@ mok_status launch_forward(const Plan &p, const void *schedule, void *workspace, 
                 if ((err = launch_gemm<GateUp<CfgA>>("gateup", seg_grid(ntg, mt), ga, st)) != hipSuccess) break;
                 if ((err = launch_gemm<Down<CfgA>>("down", seg_grid(ntd, mt), da, st)) != hipSuccess) break;
             } else if ((err = launch_pair<GateUp<CfgA>, Down<CfgA>, CfgA::LDS_BYTES>("fwd_gemms", ga, da, sync,
-                                                                                   p.max_mtiles, st)) != hipSuccess) {
+                                                                                   p.max_mtiles, spin_limit(p), st)) != hipSuccess) {
                 break;
             }
         }
@@ -689,7 +689,7 @@ mok_status launch_backward(const Plan &p, const void *schedule, void *workspace,
                 if ((err = launch_gemm<DA<CfgA>>("dA", seg_grid(nta, mt), aa, st)) != hipSuccess) break;
                 if ((err = launch_gemm<DX<CfgA>>("dX", seg_grid(ntx, mt), xa, st)) != hipSuccess) break;
             } else if ((err = launch_pair<DA<CfgA>, DX<CfgA>, CfgA::LDS_BYTES>("bwd_gemms", aa, xa, sync, p.max_mtiles,
-                                                                             st)) != hipSuccess) {
+                                                                             spin_limit(p), st)) != hipSuccess) {
                 break;
             }
             }

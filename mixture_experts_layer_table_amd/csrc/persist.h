@@ -43,6 +43,7 @@ constexpr int kSpinLimit = 1 << 20;   // polls without a claim before giving up
 struct PairSync {
     int *head;   // [2 * kXcds] claimed items of class 1 / 2 per XCD chunk (relative to the chunk start)
     int *done;   // [m-tiles of the round] finished producer tiles per m-tile
+    int spin_limit;   // poll budget of a wait; < 0: every wait gives up at once (stall-path test)
 };
 
 __device__ __forceinline__ int load_relaxed(const int *p) {
@@ -50,13 +51,18 @@ __device__ __forceinline__ int load_relaxed(const int *p) {
 }
 
 // Thread 0: wait until *p >= target. Gives up (and flags the stall) after
-// kSpinLimit polls, or as soon as another workgroup has flagged one, so that a
+// `limit` polls, or as soon as another workgroup has flagged one, so that a
 // stalled launch ends in about one poll budget instead of one budget per
-// remaining item.
-__device__ __forceinline__ bool wait_at_least(const int *p, int target, uint32_t *status) {
+// remaining item. limit < 0 gives up at once (forced from the host to test
+// this exit path).
+__device__ __forceinline__ bool wait_at_least(const int *p, int target, uint32_t *status, int limit) {
+    if (limit < 0) {
+        atomicOr(status, MOK_SCHEDULER_STALLED);
+        return false;
+    }
     int polls = 0;
     while (load_relaxed(p) < target) {
-        if (++polls > kSpinLimit) {
+        if (++polls > limit) {
             atomicOr(status, MOK_SCHEDULER_STALLED);
             return false;
         }
@@ -104,7 +110,7 @@ __device__ int claim_item(const PairSync &s, const QueueShape &q, int xcd, uint3
         if (h >= len) continue;
         int j, n;
         item_tile(start + h, q.nt2, q.mtc, j, n);
-        if (!wait_at_least(&s.done[j], q.nt1, status)) return 0;
+        if (!wait_at_least(&s.done[j], q.nt1, status, s.spin_limit)) return 0;
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         id = start + h;
         return 2;
@@ -225,6 +231,7 @@ struct PassSync {
     int *used;       // [G]
     int *released;   // [min(n_slots, G)]
     int *done;       // [m-tiles]
+    int spin_limit;  // as in PairSync
 };
 
 struct PassShape {
@@ -267,7 +274,7 @@ __device__ PassItem claim_pass_item(const PassSync &s, const PassShape &ps, cons
             const int h = atomicAdd(head, 1);
             if (h >= n) continue;
             const int g = a + h / ps.cpm;
-            if (!wait_at_least(&s.released[g % n_slots], r, v.status)) return it;
+            if (!wait_at_least(&s.released[g % n_slots], r, v.status, s.spin_limit)) return it;
             it = PassItem{1, g, h % ps.cpm, r, 0};
             return it;
         }
@@ -283,13 +290,13 @@ __device__ PassItem claim_pass_item(const PassSync &s, const PassShape &ps, cons
             int acquire = 1;
             if (c == 1) {
                 if (acq_round < r) {   // first producer tile of this round on this workgroup
-                    if (!wait_at_least(&s.full[r], (b - a) * ps.cpm, v.status)) return it;
+                    if (!wait_at_least(&s.full[r], (b - a) * ps.cpm, v.status, s.spin_limit)) return it;
                     acq_round = r;
                 } else {
                     acquire = 0;
                 }
             } else {
-                if (!wait_at_least(&s.done[lo + j], nt1, v.status)) return it;
+                if (!wait_at_least(&s.done[lo + j], nt1, v.status, s.spin_limit)) return it;
             }
             it = PassItem{c == 1 ? 2 : 3, lo + j, nn, r, acquire};
             return it;
@@ -402,6 +409,9 @@ inline PassLayout pass_layout(const Plan &p) {
     return l;
 }
 
+// Poll budget of the persistent kernels' waits (MOK_DEBUG_FORCE_STALL: none).
+inline int spin_limit(const Plan &p) { return (p.debug & MOK_DEBUG_FORCE_STALL) ? -1 : kSpinLimit; }
+
 template <class GA, class P1, class P2, int RELEASE, size_t TILE_LDS>
 hipError_t launch_pass(const char *name, const Plan &p, const GA &ga, const typename P1::Args &a1,
                        const typename P2::Args &a2, bool reverse, int *sync, hipStream_t st) {
@@ -415,7 +425,7 @@ hipError_t launch_pass(const char *name, const Plan &p, const GA &ga, const type
     }
     const PassLayout l = pass_layout(p);
     sync_clear<<<(unsigned)std::min<int64_t>((l.total + 255) / 256, 1024), 256, 0, st>>>(sync, l.total);
-    const PassSync s{sync + l.head, sync + l.full, sync + l.used, sync + l.released, sync + l.done};
+    const PassSync s{sync + l.head, sync + l.full, sync + l.used, sync + l.released, sync + l.done, spin_limit(p)};
     const PassShape ps{p.G, l.S, l.NR, l.cpm, reverse};
     KernelTimer tm(name, st);
     persist_pass_kernel<GA, P1, P2, RELEASE, TILE_LDS>
@@ -425,7 +435,7 @@ hipError_t launch_pass(const char *name, const Plan &p, const GA &ga, const type
 
 template <class P1, class P2, size_t TILE_LDS>
 hipError_t launch_pair(const char *name, const typename P1::Args &a1, const typename P2::Args &a2, int *sync,
-                       int64_t max_mtiles, hipStream_t st) {
+                       int64_t max_mtiles, int spin, hipStream_t st) {
     constexpr size_t lds_bytes = TILE_LDS + 64;
     static bool attr_set = false;
     if (!attr_set) {
@@ -438,7 +448,7 @@ hipError_t launch_pair(const char *name, const typename P1::Args &a1, const type
     sync_clear<<<(unsigned)std::min<int64_t>((n + 255) / 256, 1024), 256, 0, st>>>(sync, n);
     KernelTimer tm(name, st);
     persist_pair_kernel<P1, P2, TILE_LDS>
-        <<<(unsigned)device_cu_count(), P1::C::NT, lds_bytes, st>>>(a1, a2, PairSync{sync, sync + kSyncHeads});
+        <<<(unsigned)device_cu_count(), P1::C::NT, lds_bytes, st>>>(a1, a2, PairSync{sync, sync + kSyncHeads, spin});
     return hipGetLastError();
 }
 

@@ -41,7 +41,8 @@ mok_status make_plan(const mok_config *cfg, const mok_shape *shape, Plan *p) {
     if (!(cfg->capacity_multiplier > 0.0f && cfg->capacity_multiplier <= 4.0f))
         return MOK_ERROR_INVALID_VALUE;
     if (cfg->precision != MOK_BF16 && cfg->precision != MOK_MXFP8) return MOK_ERROR_INVALID_VALUE;
-    if (cfg->debug_flags & ~(MOK_DEBUG_IDENTITY_EXPERT | MOK_DEBUG_SEPARATE_LAUNCHES | MOK_DEBUG_WHOLE_PASS))
+    if (cfg->debug_flags &
+        ~(MOK_DEBUG_IDENTITY_EXPERT | MOK_DEBUG_SEPARATE_LAUNCHES | MOK_DEBUG_WHOLE_PASS | MOK_DEBUG_FORCE_STALL))
         return MOK_ERROR_INVALID_VALUE;
     // MXFP8 GEMMs load the scale bytes of four 32-blocks as one aligned dword
     if (cfg->precision == MOK_MXFP8 && (s.H % 128 || s.I % 128)) return MOK_ERROR_INVALID_VALUE;

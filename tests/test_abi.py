@@ -47,7 +47,7 @@ def test_bad_shapes_rejected(bad):
 
 BAD_CONFIGS = [dict(minibatch_rows=8), dict(minibatch_rows=40), dict(capacity_multiplier=0.0),
                dict(capacity_multiplier=4.5), dict(precision=7), dict(ring_bytes=32 * 256),
-               dict(macrobatch_tokens=-1), dict(debug_flags=8)]
+               dict(macrobatch_tokens=-1), dict(debug_flags=16)]
 
 
 @pytest.mark.parametrize("bad", BAD_CONFIGS)

@@ -118,3 +118,34 @@ def test_status_flags_stop_the_layer():
     torch.cuda.synchronize()
     assert status_word(sched2) == mok.MOK_SCHEDULE_OVERFLOW
     assert torch.all(out == 7.0)
+
+
+@pytest.mark.parametrize("flags", [0, mok.MOK_DEBUG_WHOLE_PASS])
+def test_forced_stall_ends_the_call(flags):
+    # every in-kernel wait gives up at once: the launch must end, flag the
+    # stall, and leave the outputs that depend on the waits unwritten
+    cfg = SMALL["k1_macro"]
+    d = DeviceInputs(synth.make_inputs(cfg))
+    w = mok.weights_bf16(d.wg, d.wu, d.wd)
+    c = knobs(cfg, debug_flags=flags | mok.MOK_DEBUG_FORCE_STALL)
+    ws = mok.get_workspace(c, device=DEV, num_local_tokens=cfg.T, hidden_size=cfg.H, intermediate_size=cfg.I,
+                           num_experts=cfg.E, topk=cfg.k)
+    sched = mok.build_schedule(ws, d.ids)
+    out = torch.full((cfg.T, cfg.H), 7.0, dtype=torch.bfloat16, device=DEV)
+    mok.forward(ws, sched, d.x, d.w, w, out=out)
+    torch.cuda.synchronize()
+    assert status_word(sched) == mok.MOK_SCHEDULER_STALLED
+    assert torch.all(out == 7.0)
+    # backward after a normal forward: the dgrad waits give up
+    ok = knobs(cfg, debug_flags=flags)
+    ws2 = mok.get_workspace(ok, device=DEV, num_local_tokens=cfg.T, hidden_size=cfg.H, intermediate_size=cfg.I,
+                            num_experts=cfg.E, topk=cfg.k)
+    sched2 = mok.build_schedule(ws2, d.ids)
+    _, ctx = mok.forward(ws2, sched2, d.x, d.w, w)
+    torch.cuda.synchronize()
+    assert status_word(sched2) == 0
+    ws2.config = c
+    grads = mok.backward(ws2, sched2, ctx, d.x, d.w, w, d.dy)
+    torch.cuda.synchronize()
+    assert status_word(sched2) == mok.MOK_SCHEDULER_STALLED
+    del grads
