@@ -275,6 +275,8 @@ def main():
         rows_per_s=round(R / (ms_per_step * 1e-3), 1),
         tflops=round(total_flops / (ms_per_step * 1e-3) / 1e12, 1),
         mfma_util=round(peak_time_s / (ms_per_step * 1e-3), 4),
+        # the grouped GEMMs alone: the same flops at peak over their summed kernel time
+        gemm_mfma_util=round(peak_time_s / (sum(kernels[n]["ms_per_step"] for n in kernels if n in fpr) * 1e-3), 4),
         schedule_share=round(sched_ms / ms_per_step, 4) if sched_ms else None,
         weight_quantize_ms=round(quant_ms, 4) if quant_ms is not None else None,
         roofline=roofline, kernels=kernels, source_digest=source_digest(),
