@@ -240,6 +240,9 @@ def main():
         if name in ("gather", "gather_dy"):
             by = (2 * cfg.T * H + 2 * R * H + 4 * R) * nprof / launches   # unique reads + writes
             entry["gbs"] = round(by / (avg * 1e-3) / 1e9, 1)
+        if name in ("combine", "combine_dx"):   # k > 1: staged rows read, token rows written
+            by = (2 * R * H + 2 * cfg.T * H + 8 * R) * nprof / launches
+            entry["gbs"] = round(by / (avg * 1e-3) / 1e9, 1)
         kernels[name] = entry
     fp8_kernels = ("gateup", "down", "dA", "dX", "fwd_gemms", "bwd_gemms", "fwd_pass", "bwd_pass") if mx else ()
     for n in kernels:

@@ -505,28 +505,49 @@ __global__ __launch_bounds__(256) void identity_rows(SchedView v, int g0, int64_
     }
 }
 
-// out[t] = sum_{j=0..k-1} g[t,j] * y[t,j] (fp32, fixed order), tokens of one macro-batch;
-// with weighted == false the plain sum (input-gradient combine).
-__global__ __launch_bounds__(256) void combine_rows(SchedView v, int t0, int t1, int H, int k, int64_t base,
+// out[t] = sum_{j=0..k-1} g[t,j] * y[t,j] (fp32, j ascending), tokens of one macro-batch;
+// with weighted == false the plain sum (input-gradient combine). One workgroup
+// per token: the token's k staged-row indices and gate weights go to LDS once,
+// and every thread keeps kCombineBatch rows' 16-byte chunks in flight before it
+// adds them, in j order. LDS: k ints, then k floats (8 k bytes, dynamic).
+constexpr int kCombineBatch = 8;
+__global__ __launch_bounds__(256) void combine_rows(SchedView v, int t0, int H, int k, int64_t base,
                                                     const float *__restrict__ topk_w, bool weighted,
                                                     const uint16_t *__restrict__ stage, uint16_t *__restrict__ out) {
+    extern __shared__ int comb_lds[];
     if (*v.status) return;
-    const int t = t0 + blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
-    if (t >= t1) return;
-    for (int c = threadIdx.x & 63; c < H / 8; c += 64) {
+    const int t = t0 + blockIdx.x;
+    int *row = comb_lds;
+    float *gw = reinterpret_cast<float *>(comb_lds + k);
+    for (int j = threadIdx.x; j < k; j += 256) {
+        const int f = t * k + j;
+        row[j] = (int)(v.inv[f] - base);
+        gw[j] = weighted ? topk_w[f] : 1.0f;
+    }
+    __syncthreads();
+    const int n = H / 8;
+    typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+    const u32x4_t *src = reinterpret_cast<const u32x4_t *>(stage);   // each staged row is read once
+    for (int c = threadIdx.x; c < n; c += 256) {
         float acc[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-        for (int j = 0; j < k; ++j) {
-            const int f = t * k + j;
-            const float gw = weighted ? topk_w[f] : 1.0f;
-            const uint4 x = reinterpret_cast<const uint4 *>(stage + (v.inv[f] - base) * H)[c];
-            const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+        for (int j0 = 0; j0 < k; j0 += kCombineBatch) {
+            u32x4_t x[kCombineBatch];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float lo = bf16_to_f32(w[i] & 0xFFFFu), hi = bf16_to_f32(w[i] >> 16);
-                acc[2 * i] = weighted ? __builtin_fmaf(gw, lo, acc[2 * i]) : acc[2 * i] + lo;
-                acc[2 * i + 1] = weighted ? __builtin_fmaf(gw, hi, acc[2 * i + 1]) : acc[2 * i + 1] + hi;
+            for (int b = 0; b < kCombineBatch; ++b)
+                x[b] = j0 + b < k ? __builtin_nontemporal_load(src + (int64_t)row[j0 + b] * n + c) : u32x4_t{0, 0, 0, 0};
+#pragma unroll
+            for (int b = 0; b < kCombineBatch; ++b) {
+                if (j0 + b >= k) break;
+                const float g = gw[j0 + b];
+                const uint32_t w[4] = {x[b].x, x[b].y, x[b].z, x[b].w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float lo = bf16_to_f32(w[i] & 0xFFFFu), hi = bf16_to_f32(w[i] >> 16);
+                    acc[2 * i] = weighted ? __builtin_fmaf(g, lo, acc[2 * i]) : acc[2 * i] + lo;
+                    acc[2 * i + 1] = weighted ? __builtin_fmaf(g, hi, acc[2 * i + 1]) : acc[2 * i + 1] + hi;
+                }
             }
         }
         reinterpret_cast<uint4 *>(out + (int64_t)t * H)[c] =
@@ -633,8 +654,9 @@ mok_status launch_forward(const Plan &p, const void *schedule, void *workspace, 
         if (p.k > 1 && (r.g1 == p.G || r.g1 == first_minibatch(p, macro_of_minibatch(p, r.g0) + 1))) {
             const Macro mc = macro_info(p, macro_of_minibatch(p, r.g0));
             KernelTimer tm("combine", st);
-            combine_rows<<<(unsigned)ceil_div(mc.t1 - mc.t0, kRowsPerBlock), 256, 0, st>>>(
-                v, mc.t0, mc.t1, p.H, p.k, mc.base, topk_w, true, stage, out);
+            if (mc.t1 > mc.t0)
+                combine_rows<<<(unsigned)(mc.t1 - mc.t0), 256, 8 * p.k, st>>>(v, mc.t0, p.H, p.k, mc.base, topk_w,
+                                                                              true, stage, out);
         }
     }
     if (err == hipSuccess) err = hipGetLastError();
@@ -696,8 +718,9 @@ mok_status launch_backward(const Plan &p, const void *schedule, void *workspace,
             if (p.k > 1 && r.g0 == first_minibatch(p, macro_of_minibatch(p, r.g0))) {
                 const Macro mc = macro_info(p, macro_of_minibatch(p, r.g0));
                 KernelTimer tm("combine_dx", st);
-                combine_rows<<<(unsigned)ceil_div(mc.t1 - mc.t0, kRowsPerBlock), 256, 0, st>>>(
-                    v, mc.t0, mc.t1, p.H, p.k, mc.base, topk_w, false, stage, dx);
+                if (mc.t1 > mc.t0)
+                    combine_rows<<<(unsigned)(mc.t1 - mc.t0), 256, 8 * p.k, st>>>(v, mc.t0, p.H, p.k, mc.base,
+                                                                                  topk_w, false, stage, dx);
             }
         }
         if (err == hipSuccess) {
