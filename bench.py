@@ -20,6 +20,7 @@ from __future__ import annotations
 import argparse
 import ctypes
 import glob
+import dataclasses
 import hashlib
 import json
 import os
@@ -133,6 +134,8 @@ def main():
     ap.add_argument("--workload", default="ep64_share", choices=list(WORKLOAD_TEXT))
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--minibatch-rows", type=int, default=0,
+                    help="override the workload's mini-batch size (results do not depend on it)")
     ap.add_argument("--separate-launches", action="store_true",
                     help="one launch per grouped GEMM instead of the persistent pair kernels (per-GEMM timing)")
     ap.add_argument("--whole-pass", action="store_true",
@@ -164,6 +167,8 @@ def main():
         return
 
     cfg = synth.CONFIGS[args.workload]
+    if args.minibatch_rows:
+        cfg = dataclasses.replace(cfg, minibatch_rows=args.minibatch_rows)
     dev = "cuda:0"
     inp = synth.make_inputs(cfg)
 

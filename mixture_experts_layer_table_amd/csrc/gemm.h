@@ -27,9 +27,11 @@
 
 namespace mok {
 
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int NSTAGE_>
+// OCC: waves per SIMD the kernel is built for (2: up to 256 registers per
+// lane; 4: up to 128, two 8-wave workgroups per compute unit).
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int NSTAGE_, int OCC_ = 2>
 struct TileCfg {
-    static constexpr int BM = BM_, BN = BN_, BK = 32;
+    static constexpr int BM = BM_, BN = BN_, BK = 32, OCC = OCC_;
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
     static constexpr int NW = WAVES_M * WAVES_N;
     static constexpr int NT = 64 * NW;
@@ -42,7 +44,12 @@ struct TileCfg {
     static constexpr size_t LDS_BYTES = (size_t)NSTAGE * STAGE_BYTES;
     static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must hold whole 32x32 blocks");
     static_assert(BM % 128 == 0 && BN % 128 == 0, "tiles are made of 128-wide sub-tiles");
-    static_assert(NSTAGE >= 2, "at least double buffered");
+    // The ping-pong K loop needs loads D = NSTAGE - 1 >= 2 stages ahead: wave
+    // group 0 reads stage kt+1 right after barrier kt, and group 1 reads stage
+    // kt+1 before barrier kt+1, so every load of stage kt+1 must have been
+    // issued, and waited for by its wave, before barrier kt. With D = 1 stage
+    // kt+1 would be issued only after barrier kt.
+    static_assert(NSTAGE >= 3, "loads must run at least two stages ahead");
 };
 
 // ----------------------------------------------------------------------------- buffer loads
@@ -335,22 +342,28 @@ __device__ __forceinline__ bf16x8_t frag(uint32_t tile, int rc, int kk) {
 }
 
 // Fragments and MFMAs of one 16-wide k-step (kk = 0, 1 of a BK = 32 stage).
-template <class C, class P>
+// FULL: every 32-row block of the wave's rows holds valid rows; otherwise only
+// the first `live` blocks do, and the others (zeros from the range-checked
+// loads, discarded by the epilogue) are neither read nor multiplied.
+template <class C, class P, bool FULL>
 struct Frags {
     bf16x8_t a[C::FN], b[C::FM];
-    __device__ __forceinline__ void read(uint32_t stage, int kk, int wm, int wn, const P &p) {
+    __device__ __forceinline__ void read(uint32_t stage, int kk, int wm, int wn, const P &p, int live) {
+        if (!FULL && live == 0) return;
         const uint32_t xs = stage, ws = stage + C::X_BYTES;
 #pragma unroll
         for (int fn = 0; fn < C::FN; ++fn) a[fn] = frag<P::W_TRANS>(ws, p.wrow(wn, fn), kk);
 #pragma unroll
-        for (int fm = 0; fm < C::FM; ++fm) b[fm] = frag<P::X_TRANS>(xs, wm * C::WM + fm * 32, kk);
+        for (int fm = 0; fm < C::FM; ++fm)
+            if (FULL || fm < live) b[fm] = frag<P::X_TRANS>(xs, wm * C::WM + fm * 32, kk);
     }
-    __device__ __forceinline__ void mma(f32x16_t (&acc)[C::FM][C::FN]) const {
+    __device__ __forceinline__ void mma(f32x16_t (&acc)[C::FM][C::FN], int live) const {
 #pragma unroll
         for (int fm = 0; fm < C::FM; ++fm)
+            if (FULL || fm < live)
 #pragma unroll
-            for (int fn = 0; fn < C::FN; ++fn)
-                acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[fn], b[fm], acc[fm][fn], 0, 0, 0);
+                for (int fn = 0; fn < C::FN; ++fn)
+                    acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[fn], b[fm], acc[fm][fn], 0, 0, 0);
     }
 };
 
@@ -363,7 +376,8 @@ struct Blk {
 };
 
 // One output tile. P provides: C, Args, X_TRANS, W_TRANS, LOADS_PER_STAGE
-// (vector-memory instructions one wave issues per stage), nk,
+// (vector-memory instructions one wave issues per stage), nk, mvalid() (valid
+// rows of the X tile),
 // issue(kt, stage_lds_address), wrow(wn, fn), epilogue(acc, wm, wn), and
 // for gemm_kernel setup(args) -> bool.
 //
@@ -395,30 +409,24 @@ __device__ __forceinline__ void wait_stages(int n) {
     }
 }
 
-// K loop of one tile into acc.
-template <class P>
-__device__ __forceinline__ void gemm_mainloop(P &p, uint32_t lds, f32x16_t (&acc)[P::C::FM][P::C::FN]) {
+// K loop of one tile into acc (acc zeroed by the caller). live: the wave's
+// 32-row blocks that hold valid rows (FM when FULL).
+template <class P, bool FULL>
+__device__ __forceinline__ void gemm_kloop(P &p, uint32_t lds, f32x16_t (&acc)[P::C::FM][P::C::FN], int live) {
     using C = typename P::C;
-    static_assert(C::WAVES_M == 2, "two wave groups");
     constexpr int L = P::LOADS_PER_STAGE, D = C::NSTAGE - 1;
-#pragma unroll
-    for (int fm = 0; fm < C::FM; ++fm)
-#pragma unroll
-        for (int fn = 0; fn < C::FN; ++fn)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[fm][fn][r] = 0.0f;
     const int wave = wave_id();
     const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
     const int nk = __builtin_amdgcn_readfirstlane(p.nk);
     auto stage = [&](int kt) { return lds + (uint32_t)((kt % C::NSTAGE) * C::STAGE_BYTES); };
-    Frags<C, P> f0, f1;
+    Frags<C, P, FULL> f0, f1;
     auto read_stage = [&](int kt) {
-        f0.read(stage(kt), 0, wm, wn, p);
-        f1.read(stage(kt), 1, wm, wn, p);
+        f0.read(stage(kt), 0, wm, wn, p, live);
+        f1.read(stage(kt), 1, wm, wn, p, live);
     };
     auto mma_stage = [&]() {
-        f0.mma(acc);
-        f1.mma(acc);
+        f0.mma(acc, live);
+        f1.mma(acc, live);
     };
 #pragma unroll
     for (int s = 0; s < D; ++s)
@@ -455,6 +463,30 @@ __device__ __forceinline__ void gemm_mainloop(P &p, uint32_t lds, f32x16_t (&acc
     }
 }
 
+// K loop of one tile into acc. P::mvalid() gives the tile's valid X rows: a
+// wave whose rows are partly or wholly past them takes the K loop that skips
+// the empty 32-row blocks (both loops run the same barriers). Grouped GEMMs
+// whose groups hold fewer rows than the tile (many small experts) then spend
+// matrix-core time on real rows only.
+template <class P>
+__device__ __forceinline__ void gemm_mainloop(P &p, uint32_t lds, f32x16_t (&acc)[P::C::FM][P::C::FN]) {
+    using C = typename P::C;
+    static_assert(C::WAVES_M == 2, "two wave groups");
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[fm][fn][r] = 0.0f;
+    const int wm = wave_id() / C::WAVES_N;
+    const int d = __builtin_amdgcn_readfirstlane(p.mvalid() - wm * C::WM);
+    const int live = d <= 0 ? 0 : min(C::FM, (d + 31) / 32);
+    if (live == C::FM)
+        gemm_kloop<P, true>(p, lds, acc, C::FM);
+    else
+        gemm_kloop<P, false>(p, lds, acc, live);
+}
+
 // One tile: prologue, K loop, epilogue.
 template <class P>
 __device__ __forceinline__ void gemm_tile(P &p, uint32_t lds) {
@@ -466,10 +498,10 @@ __device__ __forceinline__ void gemm_tile(P &p, uint32_t lds) {
 }
 
 // One tile per workgroup; P::setup(args, block) picks the tile (false: no tile).
-// Two waves per SIMD (at most 256 registers each): two 4-wave workgroups, or
-// one 8-wave workgroup, per compute unit.
+// C::OCC waves per SIMD: with OCC = 2, one 8-wave workgroup per compute unit;
+// with OCC = 4 (and at most 80 KiB of LDS), two.
 template <class P>
-__global__ __launch_bounds__(P::C::NT, 2) void gemm_kernel(typename P::Args args) {
+__global__ __launch_bounds__(P::C::NT, P::C::OCC) void gemm_kernel(typename P::Args args) {
     extern __shared__ __attribute__((aligned(1024))) char lds_raw[];
     const uint32_t lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)lds_raw;
     P p;

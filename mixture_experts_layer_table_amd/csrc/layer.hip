@@ -25,7 +25,13 @@
 namespace mok {
 namespace {
 
-using CfgA = TileCfg<256, 256, 2, 4, 4>;
+using CfgA = TileCfg<256, 256, 2, 4, 4>;   // 4 stages of 32 KiB: 3 in flight while one is multiplied
+using CfgS = TileCfg<128, 256, 2, 4, 6>;   // small groups: 6 stages of 24 KiB, 80 KiB of weights in flight
+// Weight gradients of small groups: K (the expert's rows) is a few k-steps, so
+// a tile is mostly its loads and its output stores; two workgroups per compute
+// unit (72 KiB of LDS each, at most 128 registers) overlap one's stores with
+// the other's loads.
+using CfgW = TileCfg<128, 256, 2, 4, 3, 4>;
 
 // ----------------------------------------------------------------------------- forward gate/up
 
@@ -48,6 +54,7 @@ struct GateUp {
     TransLoader<C, C::BN> wl;
     static constexpr int LOADS_PER_STAGE = RowLoader<C, C::BM>::IPW + TransLoader<C, C::BN>::IPW;
     SegTile t;
+    __device__ int mvalid() const { return t.mt.rows; }
     int i0, nk, H, I, MB;
     uint16_t *h, *aring;
 
@@ -147,6 +154,7 @@ struct Down {
     TransLoader<C, C::BN> wl;
     static constexpr int LOADS_PER_STAGE = RowLoader<C, C::BM>::IPW + TransLoader<C, C::BN>::IPW;
     SegTile t;
+    __device__ int mvalid() const { return t.mt.rows; }
     int n0, nk, H;
     Args a;
 
@@ -200,6 +208,7 @@ struct DA {
     RowLoader<C, C::BN> wl;
     static constexpr int LOADS_PER_STAGE = RowLoader<C, C::BM>::IPW + RowLoader<C, C::BN>::IPW;
     SegTile t;
+    __device__ int mvalid() const { return t.mt.rows; }
     int i0, nk;
     Args a;
 
@@ -328,6 +337,7 @@ struct DX {
     RowLoader<C, C::BN> wl;
     static constexpr int LOADS_PER_STAGE = RowLoader<C, C::BM>::IPW + RowLoader<C, C::BN>::IPW;
     SegTile t;
+    __device__ int mvalid() const { return t.mt.rows; }
     int n0, nk, I;
     Args a;
 
@@ -380,6 +390,7 @@ struct WGU {
     static constexpr int LOADS_PER_STAGE = TransIdxLoader<C, C::BM>::IPW + TransLoader<C, C::BN>::IPW;
     int e, h0, n0, ne, off, nk;
     Args a;
+    __device__ int mvalid() const { return a.H - h0; }
 
     __device__ bool setup(const Args &args, Blk b) {
         if (*args.v.status) return false;
@@ -431,6 +442,7 @@ struct WD {
     static constexpr int LOADS_PER_STAGE = TransLoader<C, C::BM>::IPW + TransIdxLoader<C, C::BN>::IPW;
     int e, i0, n0, ne, off, nk;
     Args a;
+    __device__ int mvalid() const { return a.I - i0; }
 
     __device__ bool setup(const Args &args, Blk b) {
         if (*args.v.status) return false;
@@ -586,10 +598,44 @@ hipError_t launch_gemm(const char *name, dim3 grid, const typename P::Args &args
     return hipGetLastError();
 }
 
-// BF16 only: MXFP8 runs its rounds as separate launches whatever the flag.
+// BF16 with 256-row tiles only: MXFP8 runs its rounds as separate launches
+// whatever the flag, and small-group layers (128-row tiles) run ring rounds.
 bool whole_pass(const Plan &p) {
-    return p.k == 1 && p.precision == MOK_BF16 && (p.debug & MOK_DEBUG_WHOLE_PASS) &&
+    return p.k == 1 && p.precision == MOK_BF16 && p.tile.BM == CfgA::BM && (p.debug & MOK_DEBUG_WHOLE_PASS) &&
            !(p.debug & MOK_DEBUG_SEPARATE_LAUNCHES);
+}
+
+// The two grouped GEMMs of one forward ring round (gate/up, then down), in
+// the tile family C.
+template <class C>
+hipError_t fwd_round_gemms(const Plan &p, const GateUpArgs &ga, const DownArgs &da, int64_t mt, int *sync,
+                           hipStream_t st) {
+    if (p.debug & MOK_DEBUG_SEPARATE_LAUNCHES) {
+        const hipError_t e = launch_gemm<GateUp<C>>("gateup", seg_grid(ga.n_tiles, mt), ga, st);
+        return e != hipSuccess ? e : launch_gemm<Down<C>>("down", seg_grid(da.n_tiles, mt), da, st);
+    }
+    return launch_pair<GateUp<C>, Down<C>, C::LDS_BYTES>("fwd_gemms", ga, da, sync, p.max_mtiles, spin_limit(p), st);
+}
+
+// The two grouped GEMMs of one backward ring round (dA, then dX).
+template <class C>
+hipError_t bwd_round_gemms(const Plan &p, const DAArgs &aa, const DXArgs &xa, int64_t mt, int *sync,
+                           hipStream_t st) {
+    if (p.debug & MOK_DEBUG_SEPARATE_LAUNCHES) {
+        const hipError_t e = launch_gemm<DA<C>>("dA", seg_grid(aa.n_tiles, mt), aa, st);
+        return e != hipSuccess ? e : launch_gemm<DX<C>>("dX", seg_grid(xa.n_tiles, mt), xa, st);
+    }
+    return launch_pair<DA<C>, DX<C>, C::LDS_BYTES>("bwd_gemms", aa, xa, sync, p.max_mtiles, spin_limit(p), st);
+}
+
+// The weight-gradient GEMMs (dW_gate | dW_up, then dW_down), in the tile family C.
+template <class C>
+hipError_t wgrad_gemms(const Plan &p, const WGUArgs &gu, const WDArgs &wda, hipStream_t st) {
+    const hipError_t e = launch_gemm<WGU<C>>(
+        "wgrad_gate_up", dim3((unsigned)ceil_div(2 * p.I, C::BN), (unsigned)ceil_div(p.H, C::BM), (unsigned)p.E), gu, st);
+    if (e != hipSuccess) return e;
+    return launch_gemm<WD<C>>(
+        "wgrad_down", dim3((unsigned)ceil_div(p.H, C::BN), (unsigned)ceil_div(p.I, C::BM), (unsigned)p.E), wda, st);
 }
 
 }  // namespace
@@ -642,13 +688,9 @@ mok_status launch_forward(const Plan &p, const void *schedule, void *workspace, 
                           static_cast<const uint16_t *>(w.w_gate), static_cast<const uint16_t *>(w.w_up), h, aring};
             DownArgs da{v, r.g0, r.g1, ntd, p.n_slots, p.MB, p.H, p.I, p.k, (int)p.MT, p.nb_full, aring,
                         static_cast<const uint16_t *>(w.w_down), topk_w, out, stage};
-            if (p.debug & MOK_DEBUG_SEPARATE_LAUNCHES) {
-                if ((err = launch_gemm<GateUp<CfgA>>("gateup", seg_grid(ntg, mt), ga, st)) != hipSuccess) break;
-                if ((err = launch_gemm<Down<CfgA>>("down", seg_grid(ntd, mt), da, st)) != hipSuccess) break;
-            } else if ((err = launch_pair<GateUp<CfgA>, Down<CfgA>, CfgA::LDS_BYTES>("fwd_gemms", ga, da, sync,
-                                                                                   p.max_mtiles, spin_limit(p), st)) != hipSuccess) {
-                break;
-            }
+            err = p.tile.BM == CfgS::BM ? fwd_round_gemms<CfgS>(p, ga, da, mt, sync, st)
+                                        : fwd_round_gemms<CfgA>(p, ga, da, mt, sync, st);
+            if (err != hipSuccess) break;
         }
         }
         if (p.k > 1 && (r.g1 == p.G || r.g1 == first_minibatch(p, macro_of_minibatch(p, r.g0) + 1))) {
@@ -707,13 +749,9 @@ mok_status launch_backward(const Plan &p, const void *schedule, void *workspace,
             const int nta = (int)ceil_div(p.I, CfgA::BN), ntx = (int)ceil_div(p.H, CfgA::BN);
             DAArgs aa{v, r.g0, r.g1, nta, p.n_slots, p.MB, p.H, p.I, p.dg_slices, ring, wd, h, topk_w, dh, ga, dgp};
             DXArgs xa{v, r.g0, r.g1, ntx, p.n_slots, p.H, p.I, p.k, (int)p.MT, p.nb_full, dh, wg, wu, dx, stage};
-            if (p.debug & MOK_DEBUG_SEPARATE_LAUNCHES) {
-                if ((err = launch_gemm<DA<CfgA>>("dA", seg_grid(nta, mt), aa, st)) != hipSuccess) break;
-                if ((err = launch_gemm<DX<CfgA>>("dX", seg_grid(ntx, mt), xa, st)) != hipSuccess) break;
-            } else if ((err = launch_pair<DA<CfgA>, DX<CfgA>, CfgA::LDS_BYTES>("bwd_gemms", aa, xa, sync, p.max_mtiles,
-                                                                             spin_limit(p), st)) != hipSuccess) {
-                break;
-            }
+            err = p.tile.BM == CfgS::BM ? bwd_round_gemms<CfgS>(p, aa, xa, mt, sync, st)
+                                        : bwd_round_gemms<CfgA>(p, aa, xa, mt, sync, st);
+            if (err != hipSuccess) break;
             }
             if (p.k > 1 && r.g0 == first_minibatch(p, macro_of_minibatch(p, r.g0))) {
                 const Macro mc = macro_info(p, macro_of_minibatch(p, r.g0));
@@ -729,14 +767,9 @@ mok_status launch_backward(const Plan &p, const void *schedule, void *workspace,
         }
     }
     if (err == hipSuccess) {
-        WGUArgs gu{v, p.H, p.I, x, dh, dw_gate, dw_up};
-        err = launch_gemm<WGU<CfgA>>(
-            "wgrad_gate_up",            dim3((unsigned)ceil_div(2 * p.I, CfgA::BN), (unsigned)ceil_div(p.H, CfgA::BM), (unsigned)p.E), gu, st);
-    }
-    if (err == hipSuccess) {
-        WDArgs wda{v, p.H, p.I, ga, dy, dw_down};
-        err = launch_gemm<WD<CfgA>>(
-            "wgrad_down",            dim3((unsigned)ceil_div(p.H, CfgA::BN), (unsigned)ceil_div(p.I, CfgA::BM), (unsigned)p.E), wda, st);
+        const WGUArgs gu{v, p.H, p.I, x, dh, dw_gate, dw_up};
+        const WDArgs wda{v, p.H, p.I, ga, dy, dw_down};
+        err = p.tile.BM == CfgS::BM ? wgrad_gemms<CfgW>(p, gu, wda, st) : wgrad_gemms<CfgA>(p, gu, wda, st);
     }
     if (err == hipSuccess) err = hipGetLastError();
     return check_hip(err, "mok_backward");
