@@ -255,6 +255,14 @@ struct DA {
                 u[p] = *reinterpret_cast<const uint2 *>(hrow + I);
             }
         };
+        // gate weights of the lane's fragment rows (row lane % 32 of each fm), in
+        // flight together with the first fragment's h rows
+        float gws[C::FM];
+#pragma unroll
+        for (int fm = 0; fm < C::FM; ++fm) {
+            const int mrow = wm * C::WM + fm * 32 + (lane & 31);
+            gws[fm] = a.topk_w[a.v.perm[t.mt.q0 + (mrow < t.mt.rows ? mrow : 0)]];
+        }
         load_h(0, hg, hu);
 #pragma unroll
         for (int fm = 0; fm < C::FM; ++fm) {
@@ -267,7 +275,7 @@ struct DA {
             const int mrow = wm * C::WM + fm * 32 + (lane & 31);
             const bool ok = mrow < t.mt.rows;
             const int q = t.mt.q0 + (ok ? mrow : 0);
-            const float gw = a.topk_w[a.v.perm[q]];
+            const float gw = gws[fm];
             float dg = 0.0f;
 #pragma unroll
             for (int fn = 0; fn < C::FN; ++fn)

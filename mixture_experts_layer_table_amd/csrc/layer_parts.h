@@ -200,12 +200,19 @@ __device__ __forceinline__ void store_token_rows(const f32x16_t (&acc)[C::FM][C:
     const int lane = epi_lane();
     const int nb = n0 + wn * C::WN;
     if (nb >= H) return;   // H % 64 == 0: the wave's columns are all valid or all past H
+    // k == 1: token (and gate weight) of the lane's fragment rows, row lane % 32
+    // of each fm, all loaded up front; the row passes take a row's token from
+    // the lane that holds it. (Loaded per pass, each fragment's index loads
+    // would wait behind the previous fragment's stores.)
+    int tok[C::FM];
     float gw[C::FM];
 #pragma unroll
     for (int fm = 0; fm < C::FM; ++fm) {
         const int m = wm * C::WM + fm * 32 + (lane & 31);
-        gw[fm] = (weighted && k == 1 && m < t.mt.rows) ? topk_w[v.perm[t.mt.q0 + m]] : 1.0f;
+        tok[fm] = k == 1 ? v.perm[t.mt.q0 + (m < t.mt.rows ? m : 0)] : 0;
     }
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm) gw[fm] = (weighted && k == 1) ? topk_w[tok[fm]] : 1.0f;
     const int64_t sbase = (int64_t)k * ((t.mt.g / nb_full) * (int64_t)MT);
     staged_rows<C, LDS_END>(
         [&](int fm, int fn, int g4, int j) {
@@ -213,10 +220,12 @@ __device__ __forceinline__ void store_token_rows(const f32x16_t (&acc)[C::FM][C:
             return (weighted && k == 1) ? gw[fm] * bf16r(y) : y;   // y rows are bf16
         },
         [&](int fm, int r) -> uint16_t * {
+            // every lane takes part in the shuffle (before any lane leaves): lane r holds row r's token
+            const int tok_r = k == 1 ? __shfl(tok[fm], r) : 0;
             const int m = wm * C::WM + fm * 32 + r;
             if (m >= t.mt.rows) return nullptr;
             const int q = t.mt.q0 + m;
-            return (k == 1 ? dst_k1 + (int64_t)v.perm[q] * H : stage + (q - sbase) * H) + nb;
+            return (k == 1 ? dst_k1 + (int64_t)tok_r * H : stage + (q - sbase) * H) + nb;
         });
 }
 

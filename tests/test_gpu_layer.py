@@ -70,6 +70,23 @@ def test_permute_unpermute_identity():
     assert torch.equal(res["out"].view(torch.int16), d.x.view(torch.int16))
 
 
+def test_weighted_identity_rounds_to_nearest_even():
+    # identity experts, k = 1, gates in (0, 1): out = bf16(fp32(g) * fp32(x)), one
+    # fp32 product rounded to bf16 to nearest even; torch's CPU cast gives the
+    # expected bits, so any other rounding of the kernels' bf16 stores shows
+    cfg = synth.small_config("perm_w", T=517, H=256, I=64, E=5, k=1, minibatch_rows=32, ring_bytes=3 * 32 * 512,
+                             routing="zipf")
+    inp = synth.make_inputs(cfg)
+    d = DeviceInputs(inp)
+    res = run_layer(d, knobs(cfg, debug_flags=mok.MOK_DEBUG_IDENTITY_EXPERT), backward=False)
+    g = torch.from_numpy(np.ascontiguousarray(inp.topk_w, dtype=np.float32)).reshape(-1, 1)
+    want = (g * d.x.cpu().float()).to(torch.bfloat16)
+    got = res["out"].cpu()
+    assert torch.equal(got.view(torch.int16), want.view(torch.int16))
+    assert not torch.equal(got.view(torch.int16), (g * d.x.cpu().float()).view(torch.int32).bitwise_right_shift(16)
+                           .to(torch.int16))   # the products do need rounding (truncation differs)
+
+
 def test_bitwise_deterministic_ten_runs():
     cfg = SMALL["ragged_k2"]
     d = DeviceInputs(synth.make_inputs(cfg))
