@@ -126,6 +126,32 @@ def cpu_baseline(inp, tokens_per_step, seconds):
                        f"extrapolated linearly to the step")
 
 
+def library_gemm_rates(cfg, steps):
+    """hipBLASLt bf16 rates (torch.matmul, fp32 accumulation) for the dense GEMMs
+    with the shapes of the layer's grouped GEMMs over all R routed rows: gate/up
+    [R,H]x[H,2I], down [R,I]x[I,H], dA [R,H]x[H,I], dX [R,2I]x[2I,H]."""
+    import torch
+    torch.backends.cuda.preferred_blas_library("hipblaslt")
+    R, H, I = cfg.R, cfg.H, cfg.I
+    out = dict(kind="library_gemm", library="hipblaslt via torch.matmul", dtype="bf16", rows=R, shapes={})
+    for name, (m, k, n) in dict(gateup=(R, H, 2 * I), down=(R, I, H), dA=(R, H, I), dX=(R, 2 * I, H)).items():
+        a = torch.randn(m, k, device="cuda:0").to(torch.bfloat16)
+        b = torch.randn(k, n, device="cuda:0").to(torch.bfloat16)
+        for _ in range(3):
+            c = a @ b
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            c = a @ b
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        out["shapes"][name] = dict(m=m, k=k, n=n, ms=round(ms, 4), tflops=round(2 * m * k * n / ms / 1e9, 1))
+        del a, b, c
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -143,6 +169,10 @@ def main():
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="instead of the layer, run a plain device-to-device copy of this many MiB "
                          "(calibrates the HBM byte counters against a kernel of known traffic)")
+    ap.add_argument("--library-gemm", action="store_true",
+                    help="instead of the layer, time the vendor library's dense bf16 GEMM (torch.matmul on "
+                         "hipBLASLt) at the workload's four grouped-GEMM shapes taken as single dense GEMMs: "
+                         "a reference rate for the grouped GEMMs on this GPU, not part of the layer")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -164,6 +194,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps(dict(copy_probe_bytes=n, launches=args.steps)), flush=True)
+        return
+
+    if args.library_gemm:
+        print(json.dumps(library_gemm_rates(synth.CONFIGS[args.workload], args.steps)), flush=True)
         return
 
     cfg = synth.CONFIGS[args.workload]
