@@ -23,6 +23,9 @@
 //  * buffer loads past a tile's valid range return zeros (hardware range
 //    check), which masks ragged edges without branches.
 #pragma once
+#include <type_traits>
+#include <utility>
+
 #include "common.h"
 
 namespace mok {
@@ -253,7 +256,10 @@ struct TransLoader {
 // wave needs for one issue (4 consecutive k-rows per instruction) are read
 // with scalar loads, whose counter is separate from the vector-memory counter
 // that tracks the direct-to-LDS loads; each lane then picks the index of its
-// own k-row.
+// own k-row. fetch(k0) must precede issue(k0), in k order; the K loop places
+// each fetch where no wait on LDS reads follows soon: scalar loads return out
+// of order, so while one is in flight every wait for an LDS fragment becomes
+// a wait for all of them, the scalar load's memory round trip included.
 template <class C, int COLS>
 struct TransIdxLoader {
     static constexpr int NINST = COLS / 128 * 8;
@@ -288,8 +294,7 @@ struct TransIdxLoader {
             nid[i] = sload4(idx + kb);
         }
     }
-    // issue(k0) uses the indices fetched for k0 (calls follow the fetch order),
-    // then fetches those of k0 + 32.
+    // issue(k0) uses the indices fetched for k0 (init fetches those of k0 = 0).
     __device__ void issue(int k0, uint32_t tile) {
 #pragma unroll
         for (int i = 0; i < IPW; ++i) {
@@ -299,7 +304,6 @@ struct TransIdxLoader {
             const uint32_t v = kb + krow < n ? (uint32_t)mine * ldb + coff + (uint32_t)(sub * 256) : kOutOfRange;
             load_lds16(res, v, 0, tile + lds0 + i * 1024);
         }
-        fetch(k0 + 32);
     }
 };
 
@@ -367,7 +371,15 @@ struct Frags {
     }
 };
 
-__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+// Wait for every LDS read (and scalar load) of this wave. The asm form keeps
+// memory accesses from moving across it; the builtin that follows tells the
+// compiler's own wait tracking that nothing is pending any more, so that it
+// does not wait again (then also for scalar loads issued later) before the
+// next use of the fragments.
+__device__ __forceinline__ void wait_lgkm0() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0), vmcnt and expcnt left at their maxima (gfx9 encoding)
+}
 
 // Block coordinates of a tile (the launch grid's, or a persistent kernel's
 // virtual grid).
@@ -409,6 +421,17 @@ __device__ __forceinline__ void wait_stages(int n) {
     }
 }
 
+// P::fetch(kt), where a problem has it, prepares what issue(kt) needs (the
+// scalar index loads of a gathered operand); fetch(0) is part of setup.
+template <class P, class = void>
+struct has_fetch : std::false_type {};
+template <class P>
+struct has_fetch<P, std::void_t<decltype(std::declval<P &>().fetch(0))>> : std::true_type {};
+template <class P>
+__device__ __forceinline__ void fetch_stage(P &p, int kt) {
+    if constexpr (has_fetch<P>::value) p.fetch(kt);
+}
+
 // K loop of one tile into acc (acc zeroed by the caller). live: the wave's
 // 32-row blocks that hold valid rows (FM when FULL).
 template <class P, bool FULL>
@@ -430,17 +453,24 @@ __device__ __forceinline__ void gemm_kloop(P &p, uint32_t lds, f32x16_t (&acc)[P
     };
 #pragma unroll
     for (int s = 0; s < D; ++s)
-        if (s < nk) p.issue(s, stage(s));
+        if (s < nk) {
+            if (s > 0) fetch_stage(p, s);
+            p.issue(s, stage(s));
+        }
     if (nk > 0) {
         wait_stages<L, D - 1>(min(D, nk) - 1);   // stage 0 landed
         lds_barrier();
     }
+    // Index fetches (fetch_stage) go where no LDS wait follows soon: group 0
+    // right after issuing its MFMAs (the next LDS wait is after the barrier),
+    // group 1 right after the barrier (its MFMA phase reads no LDS).
     if (wm == 0) {
         if (nk > 0) read_stage(0);
         for (int kt = 0; kt < nk; ++kt) {
             __builtin_amdgcn_sched_barrier(0);
             mma_stage();
             __builtin_amdgcn_sched_barrier(0);
+            if (kt + D < nk) fetch_stage(p, kt + D);
             // own loads issued so far: up to stage kt + D - 1; stage kt + 1 must have landed
             if constexpr (D >= 2) wait_stages<L, D - 2>(max(0, min(D - 2, nk - 2 - kt)));
             else wait_vmcnt<0>();
@@ -449,6 +479,7 @@ __device__ __forceinline__ void gemm_kloop(P &p, uint32_t lds, f32x16_t (&acc)[P
             if (kt + 1 < nk) read_stage(kt + 1);
         }
     } else {
+        if (D < nk) fetch_stage(p, D);
         for (int kt = 0; kt < nk; ++kt) {
             if (kt + D < nk) p.issue(kt + D, stage(kt + D));
             read_stage(kt);
@@ -457,6 +488,7 @@ __device__ __forceinline__ void gemm_kloop(P &p, uint32_t lds, f32x16_t (&acc)[P
             wait_lgkm0();   // fragment reads of stage kt landed: the slot is refilled right after this barrier
             lds_barrier();
             __builtin_amdgcn_sched_barrier(0);
+            if (kt + D + 1 < nk) fetch_stage(p, kt + D + 1);
             mma_stage();
             __builtin_amdgcn_sched_barrier(0);
         }

@@ -414,6 +414,7 @@ struct WGU {
         wl.init(args.dh + (int64_t)off * I2 + n0, I2, ne, I2 - n0);
         return true;
     }
+    __device__ void fetch(int kt) { xl.fetch(kt * C::BK); }
     __device__ void issue(int kt, uint32_t tile) {
         xl.issue(kt * C::BK, tile);
         wl.issue(kt * C::BK, tile + C::X_BYTES);
@@ -465,6 +466,7 @@ struct WD {
         xl.init(args.ga + (int64_t)off * args.I + i0, args.I, ne, args.I - i0);
         return true;
     }
+    __device__ void fetch(int kt) { wl.fetch(kt * C::BK); }
     __device__ void issue(int kt, uint32_t tile) {
         xl.issue(kt * C::BK, tile);
         wl.issue(kt * C::BK, tile + C::X_BYTES);
