@@ -381,6 +381,24 @@ struct DX {
 
 // dW_gate[e] | dW_up[e] = X_e^T [dh_g | dh_u]: M = H, N = 2I, K = rows of e in
 // (expert, f) order, in BK chunks anchored at the expert's first row.
+// Tile of a weight-gradient GEMM for workgroup b of the 1-D grid (gx n-tiles
+// x gy m-tiles per expert, experts in order): b is read as an index into the
+// group order of the segment GEMMs, groups of kGroupM m-tiles x all n-tiles.
+// Workgroups are dispatched round-robin over the 8 XCDs, so each XCD takes
+// every 8th tile of every group: with kGroupM = 4 one m-tile of each group
+// and half of its n-tiles, i.e. the 32 tiles an XCD runs together read
+// 4 m-slices and 8 n-slices of operands (instead of 2 n-slices and 16
+// m-slices in n-fastest order), and every XCD gets the same share of each
+// expert's tiles, whose K is the expert's row count.
+__device__ __forceinline__ void wgrad_tile(int b, int gx, int gy, int &e, int &m, int &n) {
+    const int per_e = gx * gy;
+    e = b / per_e;
+    const int o = b - e * per_e, gsize = kGroupM * gx, g = o / gsize, first = g * kGroupM;
+    const int gm = min(kGroupM, gy - first), r = o - g * gsize;
+    m = first + r % gm;
+    n = r / gm;
+}
+
 struct WGUArgs {
     SchedView v;
     int H, I;
@@ -403,9 +421,9 @@ struct WGU {
     __device__ bool setup(const Args &args, Blk b) {
         if (*args.v.status) return false;
         a = args;
-        e = b.z;
-        h0 = b.y * C::BM;
-        n0 = b.x * C::BN;
+        wgrad_tile(b.x, (2 * args.I + C::BN - 1) / C::BN, (args.H + C::BM - 1) / C::BM, e, h0, n0);
+        h0 *= C::BM;
+        n0 *= C::BN;
         ne = args.v.counts[e];
         off = args.v.offsets[e];
         nk = (ne + C::BK - 1) / C::BK;
@@ -456,9 +474,9 @@ struct WD {
     __device__ bool setup(const Args &args, Blk b) {
         if (*args.v.status) return false;
         a = args;
-        e = b.z;
-        i0 = b.y * C::BM;
-        n0 = b.x * C::BN;
+        wgrad_tile(b.x, (args.H + C::BN - 1) / C::BN, (args.I + C::BM - 1) / C::BM, e, i0, n0);
+        i0 *= C::BM;
+        n0 *= C::BN;
         ne = args.v.counts[e];
         off = args.v.offsets[e];
         nk = (ne + C::BK - 1) / C::BK;
@@ -642,10 +660,10 @@ hipError_t bwd_round_gemms(const Plan &p, const DAArgs &aa, const DXArgs &xa, in
 template <class C>
 hipError_t wgrad_gemms(const Plan &p, const WGUArgs &gu, const WDArgs &wda, hipStream_t st) {
     const hipError_t e = launch_gemm<WGU<C>>(
-        "wgrad_gate_up", dim3((unsigned)ceil_div(2 * p.I, C::BN), (unsigned)ceil_div(p.H, C::BM), (unsigned)p.E), gu, st);
+        "wgrad_gate_up", dim3((unsigned)(ceil_div(2 * p.I, C::BN) * ceil_div(p.H, C::BM) * p.E)), gu, st);
     if (e != hipSuccess) return e;
     return launch_gemm<WD<C>>(
-        "wgrad_down", dim3((unsigned)ceil_div(p.H, C::BN), (unsigned)ceil_div(p.I, C::BM), (unsigned)p.E), wda, st);
+        "wgrad_down", dim3((unsigned)(ceil_div(p.H, C::BN) * ceil_div(p.I, C::BM) * p.E)), wda, st);
 }
 
 }  // namespace
