@@ -382,7 +382,7 @@ struct DX {
 // dW_gate[e] | dW_up[e] = X_e^T [dh_g | dh_u]: M = H, N = 2I, K = rows of e in
 // (expert, f) order, in BK chunks anchored at the expert's first row.
 // Tile of a weight-gradient GEMM for workgroup b of the 1-D grid (gx n-tiles
-// x gy m-tiles per expert, experts in order): b is read as an index into the
+// x gy m-tiles per expert, experts in the order below): b is read as an index into the
 // group order of the segment GEMMs, groups of kGroupM m-tiles x all n-tiles.
 // Workgroups are dispatched round-robin over the 8 XCDs, so each XCD takes
 // every 8th tile of every group: with kGroupM = 4 one m-tile of each group
@@ -390,10 +390,34 @@ struct DX {
 // 4 m-slices and 8 n-slices of operands (instead of 2 n-slices and 16
 // m-slices in n-fastest order), and every XCD gets the same share of each
 // expert's tiles, whose K is the expert's row count.
-__device__ __forceinline__ void wgrad_tile(int b, int gx, int gy, int &e, int &m, int &n) {
+//
+// Experts go in descending order of their row count (ties: lower index
+// first) when there are at most kLptExperts of them, so that the longest
+// tiles start first and the short ones fill the end (longest-processing-time
+// order; the loads of the streaming share are Dirichlet-skewed, and the
+// heaviest expert's tiles starting last left half the compute units idle for
+// a third of the kernel). With more experts each group is small and the
+// order stays by index. Each tile's arithmetic is the same in either order.
+constexpr int kLptExperts = 32;
+__device__ __forceinline__ int expert_by_rank(const SchedView &v, int r) {
+    if (v.E > kLptExperts) return r;
+    for (int e = 0; e < v.E; ++e) {
+        const int ce = v.counts[e];
+        int rank = 0;
+        for (int f = 0; f < v.E; ++f) {
+            const int cf = v.counts[f];
+            rank += (cf > ce || (cf == ce && f < e)) ? 1 : 0;
+        }
+        if (rank == r) return e;
+    }
+    return r;   // not reached: the ranks are a permutation of 0 .. E-1
+}
+
+__device__ __forceinline__ void wgrad_tile(const SchedView &v, int b, int gx, int gy, int &e, int &m, int &n) {
     const int per_e = gx * gy;
-    e = b / per_e;
-    const int o = b - e * per_e, gsize = kGroupM * gx, g = o / gsize, first = g * kGroupM;
+    const int rank = b / per_e;
+    e = expert_by_rank(v, rank);
+    const int o = b - rank * per_e, gsize = kGroupM * gx, g = o / gsize, first = g * kGroupM;
     const int gm = min(kGroupM, gy - first), r = o - g * gsize;
     m = first + r % gm;
     n = r / gm;
@@ -421,7 +445,7 @@ struct WGU {
     __device__ bool setup(const Args &args, Blk b) {
         if (*args.v.status) return false;
         a = args;
-        wgrad_tile(b.x, (2 * args.I + C::BN - 1) / C::BN, (args.H + C::BM - 1) / C::BM, e, h0, n0);
+        wgrad_tile(args.v, b.x, (2 * args.I + C::BN - 1) / C::BN, (args.H + C::BM - 1) / C::BM, e, h0, n0);
         h0 *= C::BM;
         n0 *= C::BN;
         ne = args.v.counts[e];
@@ -474,7 +498,7 @@ struct WD {
     __device__ bool setup(const Args &args, Blk b) {
         if (*args.v.status) return false;
         a = args;
-        wgrad_tile(b.x, (args.H + C::BN - 1) / C::BN, (args.I + C::BM - 1) / C::BM, e, i0, n0);
+        wgrad_tile(args.v, b.x, (args.H + C::BN - 1) / C::BN, (args.I + C::BM - 1) / C::BM, e, i0, n0);
         i0 *= C::BM;
         n0 *= C::BN;
         ne = args.v.counts[e];
