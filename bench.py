@@ -152,6 +152,81 @@ def library_gemm_rates(cfg, steps):
     return out
 
 
+def sweep(args, cfg, base, n_cu, ids, tw, x, dy, wg, wu, wd, w_fwd, w_bwd, dev):
+    """Step time over mini-batch rows x ring size; no knob changes a result bit, so the
+    outputs of every point are compared with the first point's, byte for byte."""
+    import numpy as np
+    import torch
+
+    import mixture_experts_layer_table_amd as mok
+    row_bytes = 2 * cfg.H if base.precision == mok.MOK_BF16 else cfg.H + cfg.H // 32
+    pick = mok.autosize_config(base, cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, n_cu)
+    macro_rows = cfg.k * (cfg.T if cfg.macrobatch_tokens in (0,) or cfg.macrobatch_tokens >= cfg.T
+                          else cfg.macrobatch_tokens)
+    points = []
+    for mb in (256, 512, 1024, 2048, 4096, 8192, 16384, 32768):
+        if mb > max(2 * macro_rows, 256):
+            continue
+        for ring in sorted({2 * mb * row_bytes, max(cfg.ring_bytes, 2 * mb * row_bytes)}):
+            points.append((mb, ring))
+    if (pick.minibatch_rows, pick.ring_bytes) not in points:
+        points.append((pick.minibatch_rows, pick.ring_bytes))
+    out = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device=dev)
+    grads = dict(dx=torch.empty_like(x), dw_gate=torch.empty_like(wg), dw_up=torch.empty_like(wu),
+                 dw_down=torch.empty_like(wd), dtopk_w=torch.empty_like(tw))
+    first = None
+    results = []
+    for mb, ring in points:
+        c = dataclasses.replace(base, minibatch_rows=mb, ring_bytes=ring)
+        ws = mok.get_workspace(c, device=dev, num_local_tokens=cfg.T, hidden_size=cfg.H,
+                               intermediate_size=cfg.I, num_experts=cfg.E, topk=cfg.k)
+        sched = torch.empty(ws.schedule_bytes, dtype=torch.uint8, device=dev)
+        ctx = torch.empty(ws.fwd_ctx_bytes, dtype=torch.uint8, device=dev)
+
+        def step():
+            mok.build_schedule(ws, ids, sched)
+            mok.forward(ws, sched, x, tw, w_fwd, out=out, fwd_ctx=ctx)
+            mok.backward(ws, sched, ctx, x, tw, w_bwd, dy, grads=grads)
+
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+        status = int(sched[:4].cpu().numpy().view(np.uint32)[0])
+        digest = [out.clone()] + [grads[n].clone() for n in ("dx", "dw_gate", "dw_up", "dw_down", "dtopk_w")]
+        if first is None:
+            first = digest
+        same = all(torch.equal(a.view(torch.uint8) if a.dtype != torch.float32 else a.view(torch.int32),
+                               b.view(torch.uint8) if b.dtype != torch.float32 else b.view(torch.int32))
+                   for a, b in zip(digest, first))
+        ms = e0.elapsed_time(e1) / args.steps
+        n_slots = ring // (mb * row_bytes)
+        rec = dict(sweep=args.workload, minibatch_rows=mb, ring_bytes=ring, ring_slots=n_slots,
+                   rows_per_round=min(n_slots * mb, cfg.R), ms_per_step=round(ms, 4),
+                   tokens_per_s=round(cfg.tokens_per_step / (ms * 1e-3), 1), status=status,
+                   bitwise_equal_to_first=bool(same),
+                   two_wave_pick=(mb, ring) == (pick.minibatch_rows, pick.ring_bytes))
+        results.append(rec)
+        print(json.dumps(rec), flush=True)
+        del ws, sched, ctx
+        torch.cuda.empty_cache()
+    best = min(results, key=lambda r: r["ms_per_step"])
+    pick_rec = next(r for r in results if r["two_wave_pick"])
+    print(json.dumps(dict(sweep_summary=args.workload, n_cu=n_cu,
+                          pick=dict(minibatch_rows=pick.minibatch_rows, ring_bytes=pick.ring_bytes,
+                                    ms_per_step=pick_rec["ms_per_step"]),
+                          best=dict(minibatch_rows=best["minibatch_rows"], ring_bytes=best["ring_bytes"],
+                                    ms_per_step=best["ms_per_step"]),
+                          pick_over_best=round(pick_rec["ms_per_step"] / best["ms_per_step"], 4),
+                          all_bitwise_equal=all(r["bitwise_equal_to_first"] for r in results),
+                          all_status_clear=all(r["status"] == 0 for r in results))), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -169,6 +244,12 @@ def main():
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="instead of the layer, run a plain device-to-device copy of this many MiB "
                          "(calibrates the HBM byte counters against a kernel of known traffic)")
+    ap.add_argument("--autosize", action="store_true",
+                    help="size the mini-batch by the two-wave rule (mok_config_autosize) instead of the "
+                         "workload's setting")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of one bench line, time the step over a grid of mini-batch sizes and ring "
+                         "sizes (plus the two-wave pick) and print one JSON line per point, then a summary")
     ap.add_argument("--library-gemm", action="store_true",
                     help="instead of the layer, time the vendor library's dense bf16 GEMM (torch.matmul on "
                          "hipBLASLt) at the workload's four grouped-GEMM shapes taken as single dense GEMMs: "
@@ -230,6 +311,13 @@ def main():
                            ring_bytes=cfg.ring_bytes, precision=mok.MOK_MXFP8 if mx else mok.MOK_BF16,
                            debug_flags=(mok.MOK_DEBUG_SEPARATE_LAUNCHES if args.separate_launches else 0)
                            | (mok.MOK_DEBUG_WHOLE_PASS if args.whole_pass else 0))
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    if args.autosize:
+        config = mok.autosize_config(config, cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, n_cu)
+        cfg = dataclasses.replace(cfg, minibatch_rows=config.minibatch_rows, ring_bytes=config.ring_bytes)
+    if args.sweep:
+        sweep(args, cfg, config, n_cu, ids, tw, x, dy, wg, wu, wd, w_fwd, w_bwd, dev)
+        return
     ws = mok.get_workspace(config, device=dev, num_local_tokens=cfg.T, hidden_size=cfg.H,
                            intermediate_size=cfg.I, num_experts=cfg.E, topk=cfg.k)
     sched = torch.empty(ws.schedule_bytes, dtype=torch.uint8, device=dev)

@@ -162,6 +162,27 @@ typedef struct mok_schedule_layout {
 mok_status mok_config_default(mok_config *cfg);
 
 /*
+ * Host-only: size the mini-batch by the two-wave rule ("Mixture-of-Kittens(MoK)
+ * 란?" explainer, section 4 ②: the overlap unit is the smallest that still
+ * gives every expert-grouped GEMM at least two full waves of compute units;
+ * its worked example is 2,368 tokens for a Kimi 2.5-shaped layer).
+ * The gate/up GEMM of r rows has r*2I/(BM*256) output tiles counted
+ * fractionally, BM being the layer's m-tile rows (256, or 128 for BF16 layers
+ * of many small groups) and 256 the n-tile width; two waves over n_cu compute
+ * units need r >= 2*n_cu*BM*256/(2I). minibatch_rows becomes that minimum
+ * rounded up to whole m-tiles (m-tiles are cut at mini-batch boundaries),
+ * capped at one macro-batch's routed rows rounded up to 16; ring_bytes is
+ * raised to two slots of that size if it holds fewer and otherwise kept (it is
+ * the caller's memory budget). Every other field is kept.
+ *   cfg    in/out: the caller's knobs; written only on MOK_OK
+ *   shape  the layer shape, validated as by mok_query_sizes
+ *   n_cu   compute units to fill; <= 0 means 256 (one MI355X)
+ * Returns MOK_ERROR_INVALID_VALUE for a null pointer or a shape or knob
+ * mok_query_sizes would reject. Results never depend on the knobs it sets.
+ */
+mok_status mok_config_autosize(mok_config *cfg, const mok_shape *shape, int32_t n_cu);
+
+/*
  * Host-only size query (the pages' get_workspace sizing, "Mixture-of-Kittens
  * (MoK)" project summary, Functional API; the workspace is made once and
  * reused, Key-concepts table). Writes the byte sizes of the workspace

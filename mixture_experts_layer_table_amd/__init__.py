@@ -39,7 +39,7 @@ MOK_BF16, MOK_MXFP8 = 0, 1
 MOK_SCHEDULE_OVERFLOW, MOK_BAD_EXPERT_ID, MOK_SCHEDULER_STALLED = 1, 2, 4
 MOK_DEBUG_IDENTITY_EXPERT, MOK_DEBUG_SEPARATE_LAUNCHES, MOK_DEBUG_WHOLE_PASS, MOK_DEBUG_FORCE_STALL = 1, 2, 4, 8
 
-EXPORTS = ("mok_config_default", "mok_query_sizes", "mok_schedule_layout_query",
+EXPORTS = ("mok_config_default", "mok_config_autosize", "mok_query_sizes", "mok_schedule_layout_query",
            "mok_build_schedule", "mok_forward", "mok_backward", "mok_mxfp8_quantize", "mok_route",
            "mok_route_backward", "mok_status_string", "mok_kernel_timing_enable", "mok_kernel_timing_read",
            "mok_last_error")
@@ -79,6 +79,7 @@ _P = ctypes.c_void_p
 _sz = ctypes.POINTER(ctypes.c_size_t)
 _sigs = {
     "mok_config_default": [ctypes.POINTER(mok_config)],
+    "mok_config_autosize": [ctypes.POINTER(mok_config), ctypes.POINTER(mok_shape), ctypes.c_int32],
     "mok_query_sizes": [ctypes.POINTER(mok_config), ctypes.POINTER(mok_shape), _sz, _sz, _sz],
     "mok_schedule_layout_query": [ctypes.POINTER(mok_config), ctypes.POINTER(mok_shape),
                                   ctypes.POINTER(mok_schedule_layout)],
@@ -130,6 +131,10 @@ def mok_last_error() -> str:
 
 def mok_config_default(cfg):
     return _lib.mok_config_default(ctypes.byref(cfg))
+
+
+def mok_config_autosize(cfg, shape, n_cu):
+    return _lib.mok_config_autosize(ctypes.byref(cfg), ctypes.byref(shape), n_cu)
 
 
 def mok_query_sizes(cfg, shape, workspace, schedule, fwd_ctx):
@@ -209,6 +214,13 @@ class MoKConfig:
 
 def _shape(T, H, I, E, k) -> mok_shape:
     return mok_shape(T, H, I, E, k)
+
+
+def autosize_config(config: MoKConfig, T, H, I, E, k, n_cu: int = 0) -> MoKConfig:
+    """Copy of ``config`` with the mini-batch sized by the two-wave rule (mok_config_autosize)."""
+    c = config.c()
+    _check(mok_config_autosize(c, _shape(T, H, I, E, k), n_cu), "mok_config_autosize")
+    return dataclasses.replace(config, minibatch_rows=c.minibatch_rows, ring_bytes=c.ring_bytes)
 
 
 def query_sizes(config: MoKConfig, T, H, I, E, k):

@@ -1,4 +1,5 @@
 // C ABI entry points: argument validation on the host, then launches.
+#include <algorithm>
 #include <cstdint>
 
 #include "kernels.h"
@@ -24,6 +25,33 @@ mok_status mok_config_default(mok_config *cfg) {
     cfg->ring_bytes = int64_t(256) << 20;
     cfg->capacity_multiplier = 1.0f;
     cfg->debug_flags = 0;
+    return MOK_OK;
+}
+
+mok_status mok_config_autosize(mok_config *cfg, const mok_shape *shape, int32_t n_cu) {
+    if (!cfg || !shape) return MOK_ERROR_INVALID_VALUE;
+    const int64_t units = n_cu > 0 ? n_cu : 256;
+    // Validate the shape and the other knobs with the smallest mini-batch and
+    // an unbounded ring; the plan also gives the tile rows and the row bytes.
+    mok_config probe = *cfg;
+    probe.minibatch_rows = 16;
+    probe.ring_bytes = int64_t(1) << 50;
+    Plan p;
+    mok_status s = make_plan(&probe, shape, &p);
+    if (s != MOK_OK) return s;
+    const int64_t BM = p.tile.BM;
+    const int64_t rows = (2 * units * BM * kTileN + 2 * (int64_t)p.I - 1) / (2 * (int64_t)p.I);
+    int64_t mb = (rows + BM - 1) / BM * BM;
+    const int64_t macro_rows = ((int64_t)p.k * p.MT + 15) / 16 * 16;
+    mb = std::max<int64_t>(16, std::min(mb, macro_rows));
+    if (mb > (int64_t(1) << 30)) return MOK_ERROR_INVALID_VALUE;
+    mok_config out = *cfg;
+    out.minibatch_rows = (int32_t)mb;
+    const int64_t two_slots = 2 * mb * (int64_t)p.ring_row_bytes;
+    if (out.ring_bytes < two_slots) out.ring_bytes = two_slots;
+    s = make_plan(&out, shape, &p);
+    if (s != MOK_OK) return s;
+    *cfg = out;
     return MOK_OK;
 }
 

@@ -32,6 +32,7 @@ using CfgS = TileCfg<128, 256, 2, 4, 6>;   // small groups: 6 stages of 24 KiB, 
 // unit (72 KiB of LDS each, at most 128 registers) overlap one's stores with
 // the other's loads.
 using CfgW = TileCfg<128, 256, 2, 4, 3, 4>;
+static_assert(CfgA::BN == kTileN && CfgS::BN == kTileN, "host sizing assumes kTileN-column tiles");
 
 // ----------------------------------------------------------------------------- forward gate/up
 

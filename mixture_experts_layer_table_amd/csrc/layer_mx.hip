@@ -22,6 +22,7 @@ namespace mok {
 namespace {
 
 using CfgA = TileCfg<256, 256, 2, 4, 4>;
+static_assert(CfgA::BN == kTileN, "host sizing assumes kTileN-column tiles");
 using S8 = Fp8Stage<CfgA>;
 
 __device__ __forceinline__ const uint16_t *as_pairs(const uint8_t *p) { return reinterpret_cast<const uint16_t *>(p); }

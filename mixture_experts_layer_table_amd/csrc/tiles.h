@@ -7,6 +7,8 @@
 namespace mok {
 
 constexpr int kMaxExperts = 4096;
+// Output columns per tile of every segment GEMM (BF16 and MXFP8 alike).
+constexpr int kTileN = 256;
 
 struct TileChoice {
     int BM;      // routed rows per m-tile of the segment GEMMs

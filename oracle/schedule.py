@@ -136,3 +136,34 @@ def build(topk_ids: np.ndarray, E: int, MB: int, MT: int = 0,
 def ring_slots(ring_bytes: int, MB: int, row_bytes: int) -> int:
     """Number of whole mini-batch slots a ring of ``ring_bytes`` holds."""
     return ring_bytes // (MB * row_bytes)
+
+
+def two_wave_min_rows(n_units: int, tile_m: int, tile_n: int, I: int) -> int:
+    """Fewest routed rows whose gate/up grouped GEMM fills two full waves.
+
+    "Mixture-of-Kittens(MoK)란?" explainer, section 4 ②: the overlap unit is
+    sized so that each expert-grouped GEMM runs at least two full waves of the
+    GPU's compute units. The gate/up GEMM of r rows has N = 2I output columns,
+    so it holds r*2I / (tile_m*tile_n) output tiles counted fractionally; two
+    waves over n_units units need r >= 2*n_units*tile_m*tile_n / (2I).
+    Reading: tiles are counted fractionally (the pages' worked example, 2,368
+    tokens for the Kimi 2.5 shape, is 2 * 148 * 128*256 / 4096 exactly).
+    """
+    return -(-(2 * n_units * tile_m * tile_n) // (2 * I))
+
+
+def autosize_minibatch(T: int, k: int, I: int, MT: int, n_units: int, tile_m: int,
+                       tile_n: int) -> int:
+    """Mini-batch rows under the two-wave rule, in whole m-tiles.
+
+    Reading (the pages give the minimum, not the rounding): m-tiles are cut at
+    mini-batch boundaries, so the two-wave minimum is rounded up to a whole
+    number of tile_m-row tiles; a mini-batch never holds more rows than one
+    macro-batch routes (k * MT, MT = 0 meaning all T tokens), rounded up to the
+    16-row granule of the mini-batch size, and is at least 16 rows.
+    """
+    rows = two_wave_min_rows(n_units, tile_m, tile_n, I)
+    mb = -(-rows // tile_m) * tile_m
+    mt = T if (MT == 0 or MT >= T) else MT
+    cap = -(-(k * max(mt, 1)) // 16) * 16
+    return max(16, min(mb, cap))

@@ -127,3 +127,41 @@ def test_route_argument_checks():
     assert mok.mok_route(None, 0, 8, 2, None, None, None) == mok.MOK_OK          # empty call
     assert mok.mok_route(None, 3, 8, 2, None, None, None) == mok.MOK_ERROR_INVALID_VALUE   # null pointers
     assert mok.mok_route_backward(None, None, None, 0, 8, 2, None, None) == mok.MOK_OK
+
+
+def _tile_rows(cfg):
+    # the kernels' documented m-tile: 128 rows for BF16 layers averaging at most 128 rows per expert
+    return 128 if cfg.precision == "bf16" and cfg.T * cfg.k <= 128 * cfg.E else 256
+
+
+@pytest.mark.parametrize("name", ["tiny", "full_layer", "ep64_share", "ep64_share_mxfp8", "stream"])
+@pytest.mark.parametrize("n_cu", [0, 8, 256, 304])
+def test_autosize_matches_the_two_wave_rule(name, n_cu):
+    from oracle import schedule as S
+    import synth
+    cfg = synth.CONFIGS[name]
+    prec = mok.MOK_MXFP8 if cfg.precision == "mxfp8" else mok.MOK_BF16
+    base = mok.MoKConfig(macrobatch_tokens=cfg.macrobatch_tokens, ring_bytes=cfg.ring_bytes, precision=prec,
+                         capacity_multiplier=1.5)
+    out = mok.autosize_config(base, cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, n_cu)
+    units = n_cu if n_cu > 0 else 256
+    want = S.autosize_minibatch(cfg.T, cfg.k, cfg.I, cfg.macrobatch_tokens, units, _tile_rows(cfg), 256)
+    assert out.minibatch_rows == want
+    row_bytes = 2 * cfg.H if prec == mok.MOK_BF16 else cfg.H + cfg.H // 32
+    assert out.ring_bytes == max(cfg.ring_bytes, 2 * want * row_bytes)
+    assert (out.macrobatch_tokens, out.precision, out.capacity_multiplier) == \
+        (base.macrobatch_tokens, base.precision, base.capacity_multiplier)
+    mok.query_sizes(out, cfg.T, cfg.H, cfg.I, cfg.E, cfg.k)   # the result is a valid config
+
+
+def test_autosize_rejects_bad_arguments():
+    c = mok.mok_config()
+    mok.mok_config_default(c)
+    before = (c.minibatch_rows, c.ring_bytes)
+    assert mok.mok_config_autosize(c, mok.mok_shape(64, 100, 64, 8, 2), 0) == mok.MOK_ERROR_INVALID_VALUE
+    assert (c.minibatch_rows, c.ring_bytes) == before           # untouched on error
+    c.capacity_multiplier = 0.0
+    assert mok.mok_config_autosize(c, mok.mok_shape(64, 128, 64, 8, 2), 0) == mok.MOK_ERROR_INVALID_VALUE
+    lib = ctypes.CDLL(mok._LIB_PATH)
+    lib.mok_config_autosize.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32]
+    assert lib.mok_config_autosize(None, None, 0) == mok.MOK_ERROR_INVALID_VALUE

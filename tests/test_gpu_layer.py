@@ -111,6 +111,19 @@ def test_knobs_do_not_change_bits(name):
         same_bits(base, run_layer(d, knobs(cfg, **over)))
 
 
+@pytest.mark.parametrize("name", ["ragged_k2", "k1_macro"])
+def test_autosized_config_gives_the_same_bits(name):
+    # the two-wave mini-batch changes no output bit (at these sizes it is one
+    # macro-batch's rows; the full-size step compares every point of a sweep)
+    cfg = SMALL[name]
+    d = DeviceInputs(synth.make_inputs(cfg))
+    base = run_layer(d, knobs(cfg))
+    for n_cu in (0, 1):
+        c = mok.autosize_config(knobs(cfg), cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, n_cu)
+        print(f"[layer] autosize {name} n_cu={n_cu} mb={c.minibatch_rows} ring={c.ring_bytes}", flush=True)
+        same_bits(base, run_layer(d, c))
+
+
 def test_status_flags_stop_the_layer():
     cfg = SMALL["tiny"]
     inp = synth.make_inputs(cfg)

@@ -137,3 +137,42 @@ def test_named_workloads_invariants(name):
         assert s.G == 32 and s.n_seg <= 35
     if name == "stream":
         assert s.NM == 8 and s.G == 320
+
+
+def _read_two_wave(path):
+    rows = []
+    for line in open(path):
+        line = line.strip()
+        if line and not line.startswith("#"):
+            rows.append(tuple(int(v) for v in line.split()))
+    return rows
+
+
+def test_two_wave_rule_worked_example(golden_dir):
+    for units, tm, tn, I, rows in _read_two_wave(os.path.join(golden_dir, "two_wave_rule.txt")):
+        assert S.two_wave_min_rows(units, tm, tn, I) == rows
+
+
+@pytest.mark.parametrize("units,tm,tn,I", [(1, 16, 16, 64), (3, 32, 64, 96), (7, 128, 256, 320),
+                                           (256, 256, 256, 1024), (5, 48, 80, 2048)])
+def test_two_wave_rule_is_the_least_row_count(units, tm, tn, I):
+    # brute force: the fewest rows r with r*2I/(tm*tn) >= 2*units output tiles
+    r = 0
+    while r * 2 * I < 2 * units * tm * tn:
+        r += 1
+    assert S.two_wave_min_rows(units, tm, tn, I) == r
+
+
+@pytest.mark.parametrize("T,k,I,MT,units,tm", [(16384, 1, 2048, 0, 256, 256), (2048, 8, 2048, 0, 256, 128),
+                                                (163840, 1, 1024, 20480, 256, 256), (64, 2, 64, 0, 256, 128),
+                                                (1000, 3, 512, 100, 8, 256), (0, 1, 64, 0, 256, 256)])
+def test_autosize_minibatch_by_enumeration(T, k, I, MT, units, tm):
+    mb = S.autosize_minibatch(T, k, I, MT, units, tm, 256)
+    mt = T if (MT == 0 or MT >= T) else MT
+    macro_rows = k * max(mt, 1)
+    # the smallest whole number of m-tiles that reaches two waves, unless one macro-batch is smaller
+    n = 1
+    while n * tm * 2 * I < 2 * units * tm * 256:
+        n += 1
+    want = n * tm if n * tm <= macro_rows else -(-macro_rows // 16) * 16
+    assert mb == max(16, want) and mb % 16 == 0
