@@ -28,7 +28,10 @@ MXFP8 weights are pre-quantized): ``fq`` is a fake-quant callable
 ``fq(array, axis)`` applied to both operands of the forward gate/up and down
 products and the backward input-gradient products, along their contraction
 axis; weight gradients stay unquantized (reading: MXFP8 is a weight format and
-the weight-gradient products have no weight operand).
+the weight-gradient products have no weight operand). The MXFP8 weight-gradient
+variant (``wgrad_fq``) also quantizes the weight-gradient products' operands
+along the contraction axis, the expert's rows: blocks of 32 rows in canonical
+order per column, the last block of each expert zero-padded.
 """
 from __future__ import annotations
 
@@ -79,18 +82,35 @@ def swiglu_backward(G, hg, hu, g):
     return dhg, dhu, dw
 
 
-def expert_backward(xe, dye, g, Wg, Wu, Wd, fq=None):
+def rows_fq(fq, a):
+    """fq along the row (token) axis of a [n, c], the rows zero-padded to a
+    multiple of 32 first: a group's last block holds its tail rows and zeros,
+    which leave the block's largest magnitude, and every product, unchanged."""
+    n = a.shape[0]
+    pad = -n % 32
+    ap = np.concatenate([a, np.zeros((pad,) + a.shape[1:])], axis=0) if pad else a
+    return fq(ap, 0)[:n]
+
+
+def expert_backward(xe, dye, g, Wg, Wu, Wd, fq=None, wgrad_fq=None):
     """Backward of one expert for its rows. g is [n,1]. Returns a dict with the
     per-row input gradient dxr, router-weight gradient (fused and direct) and
-    this expert's weight gradients."""
+    this expert's weight gradients. wgrad_fq (MXFP8 weight gradients) quantizes
+    both operands of each weight-gradient product along their contraction
+    axis, the expert's rows in canonical order: x and dh for dW_gate / dW_up,
+    g*a and dy for dW_down."""
     fq = fq or _ident
     hg, hu, a, y = expert_forward(xe, Wg, Wu, Wd, fq)
     G = fq(dye, 1) @ fq(Wd, 1).T
     dhg, dhu, dw = swiglu_backward(G, hg, hu, g)
     dw_direct = np.sum(dye * y, axis=1)
     dxr = fq(dhg, 1) @ fq(Wg, 1).T + fq(dhu, 1) @ fq(Wu, 1).T
-    return dict(dxr=dxr, dw=dw, dw_direct=dw_direct,
-                dWg=xe.T @ dhg, dWu=xe.T @ dhu, dWd=(g * a).T @ dye,
+    if wgrad_fq is None:
+        dWg, dWu, dWd = xe.T @ dhg, xe.T @ dhu, (g * a).T @ dye
+    else:
+        q = lambda v: rows_fq(wgrad_fq, v)
+        dWg, dWu, dWd = q(xe).T @ q(dhg), q(xe).T @ q(dhu), q(g * a).T @ q(dye)
+    return dict(dxr=dxr, dw=dw, dw_direct=dw_direct, dWg=dWg, dWu=dWu, dWd=dWd,
                 hg=hg, hu=hu, dhg=dhg, dhu=dhu)
 
 
@@ -117,7 +137,7 @@ def forward(x, topk_ids, topk_w, Wg, Wu, Wd, fq=None):
     return out, Y
 
 
-def backward(x, topk_ids, topk_w, Wg, Wu, Wd, dy, fq=None):
+def backward(x, topk_ids, topk_w, Wg, Wu, Wd, dy, fq=None, wgrad_fq=None):
     """Gradients of L = <dy, out>. Returns dict with dx [T,H], dWg, dWu [E,H,I],
     dWd [E,I,H], dw [T,k] (fused form), dw_direct [T,k]."""
     T, k = topk_ids.shape
@@ -132,7 +152,7 @@ def backward(x, topk_ids, topk_w, Wg, Wu, Wd, dy, fq=None):
         if rows.size == 0:
             continue
         tok = rows // k
-        r = expert_backward(x[tok], dy[tok], wflat[rows][:, None], Wg[e], Wu[e], Wd[e], fq)
+        r = expert_backward(x[tok], dy[tok], wflat[rows][:, None], Wg[e], Wu[e], Wd[e], fq, wgrad_fq)
         np.add.at(dx, tok, r["dxr"])
         dWg[e], dWu[e], dWd[e] = r["dWg"], r["dWu"], r["dWd"]
         dw[rows] = r["dw"]

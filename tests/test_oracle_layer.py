@@ -191,3 +191,62 @@ def test_mxfp8_quantization_points():
     assert sorted(bwd_only) == sorted([((n, H), H), ((I, H), H),            # dA: dy, W_down along H
                                        ((n, I), I), ((H, I), I),            # dX: dh_g, W_gate along I
                                        ((n, I), I), ((H, I), I)])           # dX: dh_u, W_up along I
+
+
+def test_mxfp8_wgrad_quantization_points():
+    """The weight-gradient hook quantizes exactly x, dh_g, dh_u, g*a and dy,
+    each along the row (token) axis, zero-padded to whole 32-row blocks."""
+    n, H, I = 37, 64, 32
+    rng = np.random.default_rng(6)
+    xe, dye = rng.standard_normal((n, H)), rng.standard_normal((n, H))
+    Wg, Wu, Wd = rng.standard_normal((H, I)), rng.standard_normal((H, I)), rng.standard_normal((I, H))
+    calls = []
+
+    def spy(a, axis):
+        calls.append((a.shape, axis))
+        return a
+
+    plain = L.expert_backward(xe, dye, np.full((n, 1), 0.5), Wg, Wu, Wd)
+    r = L.expert_backward(xe, dye, np.full((n, 1), 0.5), Wg, Wu, Wd, wgrad_fq=spy)
+    assert sorted(calls) == sorted([((64, H), 0), ((64, I), 0), ((64, H), 0), ((64, I), 0),
+                                    ((64, I), 0), ((64, H), 0)])
+    for k in ("dWg", "dWu", "dWd"):          # the identity hook reduces to the unquantized products
+        np.testing.assert_allclose(r[k], plain[k], rtol=1e-13, atol=1e-12)
+
+
+def test_mxfp8_wgrad_blocks_by_hand():
+    """rows_fq on 40 rows: rows 0-31 form one block per column, rows 32-39 a
+    block of their own (its scale from those 8 rows alone), checked against the
+    codec applied to each column's blocks one by one."""
+    rng = np.random.default_rng(7)
+    a = rng.standard_normal((40, 3)) * np.array([1.0, 300.0, 1e-3])
+    a[35:, 1] *= 1000.0                       # the tail block's amax differs from the first block's
+    got = L.rows_fq(M.fake_quant, a)
+    want = np.zeros_like(a)
+    for c in range(3):
+        for r0, r1 in ((0, 32), (32, 40)):
+            blk = np.zeros(32)
+            blk[:r1 - r0] = a[r0:r1, c]
+            el, sc = M.quantize(blk[None, :])
+            want[r0:r1, c] = M.dequantize(el, sc)[0, :r1 - r0]
+    np.testing.assert_array_equal(got, want)
+
+
+def test_mxfp8_wgrad_error_bound():
+    """Each quantized operand is within 2^-4 relative of its value (E4M3 keeps 3
+    mantissa bits, so half an ulp is 2^-4 of the value's binade), so every
+    product term, and the sum, moves by at most (2*2^-4 + 2^-8) sum |x||dh|."""
+    n, H, I = 70, 64, 32
+    rng = np.random.default_rng(8)
+    xe, dye = rng.standard_normal((n, H)), rng.standard_normal((n, H))
+    Wg, Wu, Wd = rng.standard_normal((H, I)), rng.standard_normal((H, I)), rng.standard_normal((I, H))
+    g = rng.uniform(0.1, 1.0, (n, 1))
+    plain = L.expert_backward(xe, dye, g, Wg, Wu, Wd)
+    q = L.expert_backward(xe, dye, g, Wg, Wu, Wd, wgrad_fq=M.fake_quant)
+    eps = 2 * 2.0 ** -4 + 2.0 ** -8
+    bounds = dict(dWg=np.abs(xe).T @ np.abs(plain["dhg"]), dWu=np.abs(xe).T @ np.abs(plain["dhu"]))
+    _, _, a, _ = L.expert_forward(xe, Wg, Wu, Wd)
+    bounds["dWd"] = np.abs(g * a).T @ np.abs(dye)
+    for k, b in bounds.items():
+        assert np.all(np.abs(q[k] - plain[k]) <= eps * b + 1e-12), k
+        assert not np.allclose(q[k], plain[k], rtol=1e-6), k   # the hook did quantize
