@@ -247,6 +247,8 @@ def main():
     ap.add_argument("--autosize", action="store_true",
                     help="size the mini-batch by the two-wave rule (mok_config_autosize) instead of the "
                          "workload's setting")
+    ap.add_argument("--mx-wgrad", action="store_true",
+                    help="MXFP8 workloads: weight gradients on the block-scaled MFMA too (MOK_MXFP8_WGRAD)")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of one bench line, time the step over a grid of mini-batch sizes and ring "
                          "sizes (plus the two-wave pick) and print one JSON line per point, then a summary")
@@ -308,7 +310,8 @@ def main():
     else:
         w_fwd = w_bwd = mok.weights_bf16(wg, wu, wd)
     config = mok.MoKConfig(minibatch_rows=cfg.minibatch_rows, macrobatch_tokens=cfg.macrobatch_tokens,
-                           ring_bytes=cfg.ring_bytes, precision=mok.MOK_MXFP8 if mx else mok.MOK_BF16,
+                           ring_bytes=cfg.ring_bytes,
+                           precision=(mok.MOK_MXFP8_WGRAD if args.mx_wgrad else mok.MOK_MXFP8) if mx else mok.MOK_BF16,
                            debug_flags=(mok.MOK_DEBUG_SEPARATE_LAUNCHES if args.separate_launches else 0)
                            | (mok.MOK_DEBUG_WHOLE_PASS if args.whole_pass else 0))
     n_cu = torch.cuda.get_device_properties(0).multi_processor_count
@@ -372,6 +375,8 @@ def main():
             entry["gbs"] = round(by / (avg * 1e-3) / 1e9, 1)
         kernels[name] = entry
     fp8_kernels = ("gateup", "down", "dA", "dX", "fwd_gemms", "bwd_gemms", "fwd_pass", "bwd_pass") if mx else ()
+    if mx and args.mx_wgrad:
+        fp8_kernels += ("wgrad_gate_up", "wgrad_down")
     for n in kernels:
         if n in fpr:
             peak = PEAK_FP8_TFLOPS if n in fp8_kernels else PEAK_BF16_TFLOPS
@@ -390,7 +395,7 @@ def main():
     total_flops = 18 * R * H * I
     # time at the MFMA peaks: fwd + dA + dX (12 RHI) on the fp8 peak in MXFP8 mode, the rest bf16
     peak_time_s = ((12 * R * H * I) / (PEAK_FP8_TFLOPS if mx else PEAK_BF16_TFLOPS)
-                   + (6 * R * H * I) / PEAK_BF16_TFLOPS) / 1e12
+                   + (6 * R * H * I) / (PEAK_FP8_TFLOPS if mx and args.mx_wgrad else PEAK_BF16_TFLOPS)) / 1e12
     tokens = cfg.tokens_per_step
     value = tokens / (ms_per_step * 1e-3)
     sched_ms = kernels.get("schedule", {}).get("ms_per_step", 0.0)

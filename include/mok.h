@@ -51,6 +51,12 @@ typedef enum mok_status {
 /* precision modes ("Mixture-of-Kittens (MoK)" project summary, Overview) */
 #define MOK_BF16 0
 #define MOK_MXFP8 1
+/* MXFP8 with the weight gradients on the block-scaled MFMA as well: their
+   operands (x, dh, g*a, dy) are quantized along the token axis, 32 rows of one
+   expert per E8M0 scale in canonical order, each expert's rows zero-padded to
+   a multiple of 128 ("Mixture-of-Kittens (MoK)" project summary, Key-concepts
+   table: MXFP8 mode; the pages leave the weight-gradient precision open). */
+#define MOK_MXFP8_WGRAD 2
 
 /* device status word bits */
 #define MOK_SCHEDULE_OVERFLOW 1u
@@ -92,7 +98,7 @@ typedef enum mok_status {
  *   macrobatch_tokens   tokens per macro-batch; 0 = one macro-batch
  *   ring_bytes          size of the ring token buffer; must hold >= 2 mini-batches
  *   capacity_multiplier schedule capacity relative to the worst case, in (0, 4]
- *   precision           MOK_BF16 or MOK_MXFP8
+ *   precision           MOK_BF16, MOK_MXFP8 or MOK_MXFP8_WGRAD
  *   debug_flags         0 in production
  */
 typedef struct mok_config {

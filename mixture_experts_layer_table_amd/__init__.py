@@ -35,7 +35,7 @@ _lib = ctypes.CDLL(_LIB_PATH)
 
 MOK_OK, MOK_ERROR_INVALID_VALUE, MOK_ERROR_UNSUPPORTED, MOK_ERROR_BUFFER_TOO_SMALL, \
     MOK_ERROR_LAUNCH_FAILED = range(5)
-MOK_BF16, MOK_MXFP8 = 0, 1
+MOK_BF16, MOK_MXFP8, MOK_MXFP8_WGRAD = 0, 1, 2
 MOK_SCHEDULE_OVERFLOW, MOK_BAD_EXPERT_ID, MOK_SCHEDULER_STALLED = 1, 2, 4
 MOK_DEBUG_IDENTITY_EXPERT, MOK_DEBUG_SEPARATE_LAUNCHES, MOK_DEBUG_WHOLE_PASS, MOK_DEBUG_FORCE_STALL = 1, 2, 4, 8
 

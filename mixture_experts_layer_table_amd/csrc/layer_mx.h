@@ -21,4 +21,11 @@ hipError_t mx_backward_round(const Plan &p, const SchedView &v, int g0, int g1, 
                              const uint16_t *dy, const mok_weights &w, char *ws, const uint16_t *h,
                              const float *topk_w, uint16_t *dx, uint16_t *stage, hipStream_t st);
 
+// MXFP8 weight gradients (MOK_MXFP8_WGRAD), after the backward rounds: the
+// padded expert offsets, the four operands quantized along the token axis
+// (x and dy rows by token, dh and g*a in canonical order, all in the
+// workspace), then the two block-scaled weight-gradient GEMMs.
+hipError_t mx_wgrad(const Plan &p, const SchedView &v, char *ws, const uint16_t *x, const uint16_t *dy,
+                    uint16_t *dw_gate, uint16_t *dw_up, uint16_t *dw_down, hipStream_t st);
+
 }  // namespace mok

@@ -473,6 +473,248 @@ struct DX8 {
     }
 };
 
+// ----------------------------------------------------------------------------- MXFP8 weight gradients
+//
+// dW_gate | dW_up [e] = X_e^T [dh_g | dh_u] and dW_down[e] = (g a)_e^T dY_e contract
+// over the expert's rows, so both operands are quantized along that axis:
+// 32 consecutive rows of one expert (canonical order) per column share one
+// E8M0 scale. The quantizer writes them transposed, [column][Kp] (K = rows
+// contiguous, as the block-scaled tile reads both operands), expert e's rows
+// at [po[e], po[e] + count) and zeros up to po[e+1] = po[e] + count rounded
+// up to 128 (the tile's K step for whole scale dwords).
+
+// po[e] = sum over f < e of counts[f] rounded up to 128; one workgroup.
+__global__ __launch_bounds__(256) void wq_offsets(SchedView v, int32_t *po) {
+    if (*v.status) return;
+    __shared__ int32_t part[256];
+    const int E = v.E, per = (E + 255) / 256, t = threadIdx.x;
+    const int e0 = min(E, t * per), e1 = min(E, e0 + per);
+    int32_t sum = 0;
+    for (int e = e0; e < e1; ++e) sum += (v.counts[e] + 127) / 128 * 128;
+    part[t] = sum;
+    __syncthreads();
+    if (t == 0) {   // 256 partial sums, serially: fixed order
+        int32_t run = 0;
+        for (int i = 0; i < 256; ++i) {
+            const int32_t x = part[i];
+            part[i] = run;
+            run += x;
+        }
+    }
+    __syncthreads();
+    int32_t run = part[t];
+    for (int e = e0; e < e1; ++e) {
+        po[e] = run;
+        run += (v.counts[e] + 127) / 128 * 128;
+    }
+    if (e1 == E && e0 < e1) po[E] = run;   // the thread holding the last expert
+}
+
+struct QuantCols {
+    SchedView v;
+    const int32_t *po;
+    const uint16_t *src;   // bf16 rows: token rows (by_token) or canonical rows
+    int64_t ld;            // elements per source row
+    int ncols;
+    bool by_token;
+    int64_t Kp;
+    uint8_t *el, *sc;      // [ncols][Kp] codes, [ncols][Kp/32] scale bytes
+};
+
+// Workgroup (j, column chunk): padded positions [128j, 128j + 128) (one
+// expert's, as po is a multiple of 128) of 64 columns. The 128 x 64 source
+// tile is read in 16-byte chunks (4 loads in flight per thread) into LDS;
+// thread (c, b) then quantizes column c's 32-row block b and leaves its 32
+// code bytes in an LDS row of 33 dwords per column (conflict-free); last,
+// every 8 consecutive threads write one column's 128 code bytes as 16-byte
+// stores.
+constexpr int kQRows = 128, kQCols = 64;
+__global__ __launch_bounds__(256) void quantize_cols(QuantCols q) {
+    if (*q.v.status) return;
+    __shared__ int32_t rows[kQRows];
+    __shared__ __attribute__((aligned(16))) uint16_t tile[kQRows][kQCols];
+    __shared__ uint32_t codes[kQCols][33];
+    const int64_t p0 = (int64_t)blockIdx.x * kQRows;
+    const int E = q.v.E;
+    if (p0 >= q.po[E]) return;   // past every expert's padded rows: never read
+    int lo = 0, hi = E;          // the expert e with po[e] <= p0 < po[e+1]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (q.po[mid] <= p0) lo = mid;
+        else hi = mid;
+    }
+    const int e = lo;
+    const int r0 = (int)(p0 - q.po[e]), n = q.v.counts[e] - r0;   // valid rows here: min(128, n)
+    const int t = threadIdx.x;
+    if (t < kQRows) {
+        int row = -1;
+        if (t < n) {
+            const int c = q.v.offsets[e] + r0 + t;
+            row = q.by_token ? q.v.ctok[c] : c;
+        }
+        rows[t] = row;
+    }
+    __syncthreads();
+    const int col0 = blockIdx.y * kQCols;
+    constexpr int CPR = kQCols / 8;           // 16-byte chunks per tile row
+    constexpr int RPP = 256 / CPR;            // rows per pass
+    uint4 v[kQRows / RPP];
+#pragma unroll
+    for (int pass = 0; pass < kQRows / RPP; ++pass) {
+        const int r = pass * RPP + t / CPR, ch = (t % CPR) * 8;
+        const int row = rows[r];
+        v[pass] = make_uint4(0, 0, 0, 0);
+        if (row >= 0 && col0 + ch < q.ncols)   // ncols % 128 == 0: whole chunks
+            v[pass] = *reinterpret_cast<const uint4 *>(q.src + (int64_t)row * q.ld + col0 + ch);
+    }
+#pragma unroll
+    for (int pass = 0; pass < kQRows / RPP; ++pass)
+        *reinterpret_cast<uint4 *>(&tile[pass * RPP + t / CPR][(t % CPR) * 8]) = v[pass];
+    __syncthreads();
+#pragma unroll
+    for (int cb = t; cb < kQCols * 4; cb += 256) {
+        const int c = cb % kQCols, b = cb / kQCols;
+        uint32_t x[32];
+        uint32_t amax = 0;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            x[i] = tile[b * 32 + i][c];
+            amax = max(amax, x[i] & 0x7FFFu);
+        }
+        const uint32_t sb = mx_scale_byte_bf16(amax);
+        const int ex = (int)sb - 127;
+#pragma unroll
+        for (int d = 0; d < 8; ++d)
+            codes[c][b * 8 + d] = e4m3_encode_bf16(x[4 * d], ex) | (e4m3_encode_bf16(x[4 * d + 1], ex) << 8) |
+                                  (e4m3_encode_bf16(x[4 * d + 2], ex) << 16) |
+                                  (e4m3_encode_bf16(x[4 * d + 3], ex) << 24);
+        if (col0 + c < q.ncols) q.sc[(int64_t)(col0 + c) * (q.Kp / 32) + p0 / 32 + b] = (uint8_t)sb;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = t; i < kQCols * 8; i += 256) {
+        const int c = i >> 3, ch = i & 7;
+        if (col0 + c < q.ncols) {
+            const uint4 w = make_uint4(codes[c][ch * 4], codes[c][ch * 4 + 1], codes[c][ch * 4 + 2],
+                                       codes[c][ch * 4 + 3]);
+            *reinterpret_cast<uint4 *>(q.el + (int64_t)(col0 + c) * q.Kp + p0 + ch * 16) = w;
+        }
+    }
+}
+
+// dW_gate | dW_up [e]: M = H (x columns), N = 2I (dh columns), K = the expert's padded rows.
+struct WGU8Args {
+    SchedView v;
+    int H, I;
+    int64_t Kp;
+    const int32_t *po;
+    const uint8_t *qx, *qxs, *qdh, *qdhs;
+    uint16_t *dwg, *dwu;
+};
+
+template <class Cfg>
+struct WGU8 {
+    using C = Cfg;
+    using Args = WGU8Args;
+    static constexpr bool FP8 = true;
+    RowLoader<C, C::BM> xl;
+    RowLoader<C, C::BN> wl;
+    ScaleLoader<C> sl;
+    static constexpr int LOADS_PER_STAGE = RowLoader<C, C::BM>::IPW + RowLoader<C, C::BN>::IPW + 1;
+    int e, h0, n0, nk;
+    Args a;
+
+    __device__ bool setup(const Args &args, Blk b) {
+        if (*args.v.status) return false;
+        a = args;
+        wgrad_tile(args.v, b.x, (2 * args.I + C::BN - 1) / C::BN, (args.H + C::BM - 1) / C::BM, e, h0, n0);
+        h0 *= C::BM;
+        n0 *= C::BN;
+        const int pe = args.po[e], kpe = args.po[e + 1] - pe;   // a multiple of 128
+        nk = kpe / Fp8Stage<C>::BK8;
+        const int64_t Kp = args.Kp, kb = Kp / 32;
+        const int mx = min(C::BM, args.H - h0), mw = min(C::BN, 2 * args.I - n0);
+        xl.init(as_pairs(args.qx + (int64_t)h0 * Kp + pe), Kp / 2, mx);
+        wl.init(as_pairs(args.qdh + (int64_t)n0 * Kp + pe), Kp / 2, mw);
+        sl.init(args.qxs + (int64_t)h0 * kb + pe / 32, mx, (int)kb, args.qdhs + (int64_t)n0 * kb + pe / 32, mw,
+                (int)kb);
+        return true;
+    }
+    __device__ void issue(int kt, uint32_t stage) {
+        xl.issue(kt * C::BK, stage);
+        wl.issue(kt * C::BK, stage + C::X_BYTES);
+        sl.issue(kt * Fp8Stage<C>::BK8, stage);
+    }
+    __device__ int wrow(int wn, int fn) const { return wn * C::WN + fn * 32; }
+    __device__ void epilogue(f32x16_t (&acc)[C::FM][C::FN], int wm, int wn) {
+        const int H = a.H, I = a.I;
+        const int nb = n0 + wn * C::WN;
+        if (nb >= 2 * I) return;   // I % 128 == 0: the wave's columns are all gate, all up or all past 2I
+        uint16_t *base = nb < I ? a.dwg + nb : a.dwu + (nb - I);
+        staged_rows<C, Fp8Stage<C>::LDS_BYTES>([&](int fm, int fn, int g4, int j) { return acc[fm][fn][g4 * 4 + j]; },
+                                               [&](int fm, int r) -> uint16_t * {
+                                                   const int hh = h0 + wm * C::WM + fm * 32 + r;
+                                                   return hh < H ? base + ((int64_t)e * H + hh) * I : nullptr;
+                                               });
+    }
+};
+
+// dW_down[e]: M = I (g*a columns), N = H (dy columns), K as above.
+struct WD8Args {
+    SchedView v;
+    int H, I;
+    int64_t Kp;
+    const int32_t *po;
+    const uint8_t *qga, *qgas, *qdy, *qdys;
+    uint16_t *dwd;
+};
+
+template <class Cfg>
+struct WD8 {
+    using C = Cfg;
+    using Args = WD8Args;
+    static constexpr bool FP8 = true;
+    RowLoader<C, C::BM> xl;
+    RowLoader<C, C::BN> wl;
+    ScaleLoader<C> sl;
+    static constexpr int LOADS_PER_STAGE = RowLoader<C, C::BM>::IPW + RowLoader<C, C::BN>::IPW + 1;
+    int e, i0, n0, nk;
+    Args a;
+
+    __device__ bool setup(const Args &args, Blk b) {
+        if (*args.v.status) return false;
+        a = args;
+        wgrad_tile(args.v, b.x, (args.H + C::BN - 1) / C::BN, (args.I + C::BM - 1) / C::BM, e, i0, n0);
+        i0 *= C::BM;
+        n0 *= C::BN;
+        const int pe = args.po[e], kpe = args.po[e + 1] - pe;
+        nk = kpe / Fp8Stage<C>::BK8;
+        const int64_t Kp = args.Kp, kb = Kp / 32;
+        const int mx = min(C::BM, args.I - i0), mw = min(C::BN, args.H - n0);
+        xl.init(as_pairs(args.qga + (int64_t)i0 * Kp + pe), Kp / 2, mx);
+        wl.init(as_pairs(args.qdy + (int64_t)n0 * Kp + pe), Kp / 2, mw);
+        sl.init(args.qgas + (int64_t)i0 * kb + pe / 32, mx, (int)kb, args.qdys + (int64_t)n0 * kb + pe / 32, mw,
+                (int)kb);
+        return true;
+    }
+    __device__ void issue(int kt, uint32_t stage) {
+        xl.issue(kt * C::BK, stage);
+        wl.issue(kt * C::BK, stage + C::X_BYTES);
+        sl.issue(kt * Fp8Stage<C>::BK8, stage);
+    }
+    __device__ int wrow(int wn, int fn) const { return wn * C::WN + fn * 32; }
+    __device__ void epilogue(f32x16_t (&acc)[C::FM][C::FN], int wm, int wn) {
+        const int H = a.H, I = a.I;
+        const int nb = n0 + wn * C::WN;
+        if (nb >= H) return;   // H % 128 == 0
+        staged_rows<C, Fp8Stage<C>::LDS_BYTES>([&](int fm, int fn, int g4, int j) { return acc[fm][fn][g4 * 4 + j]; },
+                                               [&](int fm, int r) -> uint16_t * {
+                                                   const int ii = i0 + wm * C::WM + fm * 32 + r;
+                                                   return ii < I ? a.dwd + ((int64_t)e * I + ii) * H + nb : nullptr;
+                                               });
+    }
+};
+
 // ----------------------------------------------------------------------------- host side
 
 template <class P>
@@ -538,6 +780,40 @@ hipError_t mx_backward_round(const Plan &p, const SchedView &v, int g0, int g1, 
                w.gate_scales, w.up_elems, w.up_scales, dx, stage};
     if ((err = launch_gemm8<DA8<CfgA>>("dA", seg_grid(nta, mt_bound), aa, st)) != hipSuccess) return err;
     return launch_gemm8<DX8<CfgA>>("dX", seg_grid(ntx, mt_bound), xa, st);
+}
+
+hipError_t mx_wgrad(const Plan &p, const SchedView &v, char *ws, const uint16_t *x, const uint16_t *dy,
+                    uint16_t *dw_gate, uint16_t *dw_up, uint16_t *dw_down, hipStream_t st) {
+    int32_t *po = reinterpret_cast<int32_t *>(ws + p.w_po);
+    auto B = [&](size_t off) { return reinterpret_cast<uint8_t *>(ws + off); };
+    const uint16_t *dh = reinterpret_cast<const uint16_t *>(ws + p.w_dh);
+    const uint16_t *gav = reinterpret_cast<const uint16_t *>(ws + p.w_ga);
+    {
+        KernelTimer tm("wq_offsets", st);
+        wq_offsets<<<1, 256, 0, st>>>(v, po);
+    }
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const unsigned nb = (unsigned)(p.Kp / kQRows);
+    const QuantCols qs[4] = {
+        {v, po, x, p.H, p.H, true, p.Kp, B(p.w_qx), B(p.w_qxs)},
+        {v, po, dh, 2 * (int64_t)p.I, 2 * p.I, false, p.Kp, B(p.w_qdh), B(p.w_qdhs)},
+        {v, po, gav, p.I, p.I, false, p.Kp, B(p.w_qga), B(p.w_qgas)},
+        {v, po, dy, p.H, p.H, true, p.Kp, B(p.w_qdy), B(p.w_qdys)},
+    };
+    if (p.R > 0) {
+        KernelTimer tm("wgrad_quantize", st);
+        for (const QuantCols &q : qs)
+            quantize_cols<<<dim3(nb, (unsigned)ceil_div(q.ncols, kQCols)), 256, 0, st>>>(q);
+    }
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    const WGU8Args gu{v, p.H, p.I, p.Kp, po, B(p.w_qx), B(p.w_qxs), B(p.w_qdh), B(p.w_qdhs), dw_gate, dw_up};
+    const WD8Args wd{v, p.H, p.I, p.Kp, po, B(p.w_qga), B(p.w_qgas), B(p.w_qdy), B(p.w_qdys), dw_down};
+    err = launch_gemm8<WGU8<CfgA>>(
+        "wgrad_gate_up", dim3((unsigned)(ceil_div(2 * p.I, CfgA::BN) * ceil_div(p.H, CfgA::BM) * p.E)), gu, st);
+    if (err != hipSuccess) return err;
+    return launch_gemm8<WD8<CfgA>>(
+        "wgrad_down", dim3((unsigned)(ceil_div(p.H, CfgA::BN) * ceil_div(p.I, CfgA::BM) * p.E)), wd, st);
 }
 
 }  // namespace mok

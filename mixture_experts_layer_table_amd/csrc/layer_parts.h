@@ -25,6 +25,48 @@ struct SegTile {
 constexpr int kXcds = 8;       // MI355X: 8 accelerator dies, each with its own L2
 constexpr int kGroupM = 4;     // m-tiles per group of the tile order
 
+// Tile of a weight-gradient GEMM for workgroup b of the 1-D grid (gx n-tiles
+// x gy m-tiles per expert, experts in the order below): b is read as an index into the
+// group order of the segment GEMMs, groups of kGroupM m-tiles x all n-tiles.
+// Workgroups are dispatched round-robin over the 8 XCDs, so each XCD takes
+// every 8th tile of every group: with kGroupM = 4 one m-tile of each group
+// and half of its n-tiles, i.e. the 32 tiles an XCD runs together read
+// 4 m-slices and 8 n-slices of operands (instead of 2 n-slices and 16
+// m-slices in n-fastest order), and every XCD gets the same share of each
+// expert's tiles, whose K is the expert's row count.
+//
+// Experts go in descending order of their row count (ties: lower index
+// first) when there are at most kLptExperts of them, so that the longest
+// tiles start first and the short ones fill the end (longest-processing-time
+// order; the loads of the streaming share are Dirichlet-skewed, and the
+// heaviest expert's tiles starting last left half the compute units idle for
+// a third of the kernel). With more experts each group is small and the
+// order stays by index. Each tile's arithmetic is the same in either order.
+constexpr int kLptExperts = 32;
+__device__ __forceinline__ int expert_by_rank(const SchedView &v, int r) {
+    if (v.E > kLptExperts) return r;
+    for (int e = 0; e < v.E; ++e) {
+        const int ce = v.counts[e];
+        int rank = 0;
+        for (int f = 0; f < v.E; ++f) {
+            const int cf = v.counts[f];
+            rank += (cf > ce || (cf == ce && f < e)) ? 1 : 0;
+        }
+        if (rank == r) return e;
+    }
+    return r;   // not reached: the ranks are a permutation of 0 .. E-1
+}
+
+__device__ __forceinline__ void wgrad_tile(const SchedView &v, int b, int gx, int gy, int &e, int &m, int &n) {
+    const int per_e = gx * gy;
+    const int rank = b / per_e;
+    e = expert_by_rank(v, rank);
+    const int o = b - rank * per_e, gsize = kGroupM * gx, g = o / gsize, first = g * kGroupM;
+    const int gm = min(kGroupM, gy - first), r = o - g * gsize;
+    m = first + r % gm;
+    n = r / gm;
+}
+
 // Tile of a segment GEMM for this workgroup. The 1-D grid (a multiple of 8
 // workgroups, at least the number of tiles) is dispatched round-robin over the
 // XCDs; with `per` = ceil(tiles / 8), workgroup b is mapped to tile

@@ -40,12 +40,13 @@ mok_status make_plan(const mok_config *cfg, const mok_shape *shape, Plan *p) {
     if (cfg->macrobatch_tokens < 0 || cfg->ring_bytes <= 0) return MOK_ERROR_INVALID_VALUE;
     if (!(cfg->capacity_multiplier > 0.0f && cfg->capacity_multiplier <= 4.0f))
         return MOK_ERROR_INVALID_VALUE;
-    if (cfg->precision != MOK_BF16 && cfg->precision != MOK_MXFP8) return MOK_ERROR_INVALID_VALUE;
+    if (cfg->precision != MOK_BF16 && cfg->precision != MOK_MXFP8 && cfg->precision != MOK_MXFP8_WGRAD)
+        return MOK_ERROR_INVALID_VALUE;
     if (cfg->debug_flags &
         ~(MOK_DEBUG_IDENTITY_EXPERT | MOK_DEBUG_SEPARATE_LAUNCHES | MOK_DEBUG_WHOLE_PASS | MOK_DEBUG_FORCE_STALL))
         return MOK_ERROR_INVALID_VALUE;
     // MXFP8 GEMMs load the scale bytes of four 32-blocks as one aligned dword
-    if (cfg->precision == MOK_MXFP8 && (s.H % 128 || s.I % 128)) return MOK_ERROR_INVALID_VALUE;
+    if (cfg->precision != MOK_BF16 && (s.H % 128 || s.I % 128)) return MOK_ERROR_INVALID_VALUE;
 
     Plan q;
     q.T = s.T;
@@ -55,7 +56,8 @@ mok_status make_plan(const mok_config *cfg, const mok_shape *shape, Plan *p) {
     q.k = s.k;
     q.R = s.T * s.k;
     q.MB = cfg->minibatch_rows;
-    q.precision = cfg->precision;
+    q.precision = cfg->precision == MOK_BF16 ? MOK_BF16 : MOK_MXFP8;
+    q.mx_wgrad = cfg->precision == MOK_MXFP8_WGRAD;
     q.debug = cfg->debug_flags;
     q.MT = (cfg->macrobatch_tokens == 0 || cfg->macrobatch_tokens >= s.T) ? std::max<int64_t>(s.T, 1)
                                                                             : cfg->macrobatch_tokens;
@@ -116,6 +118,20 @@ mok_status make_plan(const mok_config *cfg, const mok_shape *shape, Plan *p) {
     if (q.precision == MOK_MXFP8) {
         q.w_dhq = w.take((size_t)q.R * 2 * q.I);
         q.w_dhq_scales = w.take((size_t)q.R * 2 * q.I / 32);
+    }
+    if (q.mx_wgrad) {
+        // every non-empty expert adds at most 127 rows of padding
+        q.Kp = (q.R + 127 * std::min<int64_t>(q.E, q.R) + 127) / 128 * 128;
+        const size_t kp = (size_t)q.Kp;
+        q.w_qx = w.take((size_t)q.H * kp);
+        q.w_qxs = w.take((size_t)q.H * kp / 32);
+        q.w_qdh = w.take((size_t)2 * q.I * kp);
+        q.w_qdhs = w.take((size_t)2 * q.I * kp / 32);
+        q.w_qga = w.take((size_t)q.I * kp);
+        q.w_qgas = w.take((size_t)q.I * kp / 32);
+        q.w_qdy = w.take((size_t)q.H * kp);
+        q.w_qdys = w.take((size_t)q.H * kp / 32);
+        q.w_po = w.take(4 * (size_t)(q.E + 1));
     }
     q.w_total = w.off;
 

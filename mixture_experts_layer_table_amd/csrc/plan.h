@@ -21,7 +21,8 @@ struct Plan {
     // knobs
     int MB = 0;
     int64_t MT = 0;          // effective macro-batch tokens (T if 0 or >= T; 1 if T == 0)
-    int precision = MOK_BF16;
+    int precision = MOK_BF16;   // MOK_BF16 or MOK_MXFP8 (MOK_MXFP8_WGRAD sets MOK_MXFP8 and mx_wgrad)
+    bool mx_wgrad = false;      // weight gradients on the block-scaled MFMA
     uint32_t debug = 0;
     // derived
     int NM = 0;              // macro-batches
@@ -48,6 +49,12 @@ struct Plan {
     size_t w_sync = 0;
     // MXFP8 only: dh quantized along I, elements [R][2I] and scales [R][2I/32]
     size_t w_dhq = 0, w_dhq_scales = 0;
+    // MXFP8 weight gradients only: operands quantized along the token axis,
+    // transposed: [cols][Kp] elements and [cols][Kp/32] scales for x (H cols),
+    // dh (2I), g*a (I) and dy (H), expert e's rows at [po[e], po[e+1]) of Kp,
+    // po[e+1] - po[e] = its row count rounded up to 128; po [E+1] int32.
+    int64_t Kp = 0;
+    size_t w_qx = 0, w_qxs = 0, w_qdh = 0, w_qdhs = 0, w_qga = 0, w_qgas = 0, w_qdy = 0, w_qdys = 0, w_po = 0;
     // fwd_ctx (byte offsets)
     size_t c_h = 0, c_total = 0;
 };

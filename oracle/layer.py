@@ -193,13 +193,15 @@ def token_backward(x_rows, dy_rows, ids_rows, w_rows, expert_w, fq=None):
     return dx, dw
 
 
-def expert_wgrad_columns(xe, dye, g, Wg, Wu, Wd, cols, fq=None):
+def expert_wgrad_columns(xe, dye, g, Wg, Wu, Wd, cols, fq=None, wgrad_fq=None):
     """Columns ``cols`` of dW_gate[e], dW_up[e] ([H, len(cols)]) and rows ``cols`` of
     dW_down[e] ([len(cols), H]) from all of expert e's rows (xe, dye, g [n,1]).
     ``fq`` as in expert_backward: it reaches the weight gradients only through
     h (forward product) and G (dA product); the gradient products themselves
     take unquantized operands. Quantization runs along H, so a column subset
-    of W_gate/W_up or a row subset of W_down quantizes like the whole."""
+    of W_gate/W_up or a row subset of W_down quantizes like the whole.
+    ``wgrad_fq`` as in expert_backward: blocks run along the rows, one column
+    at a time, so a column subset also quantizes like the whole."""
     fq = fq or _ident
     xq = fq(xe, 1)
     hg = xq @ fq(Wg[:, cols], 0)
@@ -207,7 +209,10 @@ def expert_wgrad_columns(xe, dye, g, Wg, Wu, Wd, cols, fq=None):
     G = fq(dye, 1) @ fq(Wd[cols, :], 1).T
     dhg, dhu, _ = swiglu_backward(G, hg, hu, g)
     a = silu(hg) * hu
-    return xe.T @ dhg, xe.T @ dhu, (g * a).T @ dye
+    if wgrad_fq is None:
+        return xe.T @ dhg, xe.T @ dhu, (g * a).T @ dye
+    q = lambda v: rows_fq(wgrad_fq, v)
+    return q(xe).T @ q(dhg), q(xe).T @ q(dhu), q(g * a).T @ q(dye)
 
 
 def rel_frobenius(got, ref) -> float:

@@ -51,7 +51,7 @@ def run_layer(d: DeviceInputs, config: mok.MoKConfig, backward: bool = True):
     ws = mok.get_workspace(config, device=DEV, num_local_tokens=c.T, hidden_size=c.H,
                            intermediate_size=c.I, num_experts=c.E, topk=c.k)
     sched = mok.build_schedule(ws, d.ids)
-    if config.precision == mok.MOK_MXFP8:
+    if config.precision in (mok.MOK_MXFP8, mok.MOK_MXFP8_WGRAD):
         q = mok.MXFP8Weights(d.wg, d.wu, d.wd)
         wf, wb = q.fwd, q.bwd
     else:
@@ -68,13 +68,14 @@ def status_word(sched: torch.Tensor) -> int:
     return int(sched[:4].cpu().numpy().view(np.uint32)[0])
 
 
-def oracle_full(inp: synth.LayerInputs, fq=None):
-    """fp64 oracle of the whole layer; fq = the MXFP8 fake-quant for MXFP8 mode."""
+def oracle_full(inp: synth.LayerInputs, fq=None, wgrad_fq=None):
+    """fp64 oracle of the whole layer; fq = the MXFP8 fake-quant for MXFP8 mode,
+    wgrad_fq the same for the MXFP8 weight gradients."""
     f = L.bf16_bits_to_f64
     x, dy = f(inp.x), f(inp.dy)
     Wg, Wu, Wd = f(inp.w_gate), f(inp.w_up), f(inp.w_down)
     out, _ = L.forward(x, inp.topk_ids, inp.topk_w, Wg, Wu, Wd, fq)
-    g = L.backward(x, inp.topk_ids, inp.topk_w, Wg, Wu, Wd, dy, fq)
+    g = L.backward(x, inp.topk_ids, inp.topk_w, Wg, Wu, Wd, dy, fq, wgrad_fq)
     return dict(out=out, dx=g["dx"], dw_gate=g["dWg"], dw_up=g["dWu"], dw_down=g["dWd"], dtopk_w=g["dw"])
 
 

@@ -6,6 +6,7 @@ import numpy as np
 import pytest
 import torch
 
+import mixture_experts_layer_table_amd as mok
 import synth
 from gpu_support import TOL_BF16, TOL_MXFP8, DeviceInputs, host_f64, knobs, run_layer, status_word
 from oracle import layer as L
@@ -25,14 +26,15 @@ def _sample_tokens(cfg, ids, rng, n=48):
     return np.array(sorted(picks))
 
 
-def _check(cfg, experts_for_wgrad=2, n_tokens=48):
+def _check(cfg, experts_for_wgrad=2, n_tokens=48, mx_wgrad=False):
     mx = cfg.precision == "mxfp8"
     fq, tol = (M.fake_quant, TOL_MXFP8) if mx else (None, TOL_BF16)
+    wfq = M.fake_quant if mx_wgrad else None
     print(f"[fullsize] {cfg.name}: generating inputs", flush=True)
     inp = synth.make_inputs(cfg)
     d = DeviceInputs(inp)
     print(f"[fullsize] {cfg.name}: running layer", flush=True)
-    res = run_layer(d, knobs(cfg))
+    res = run_layer(d, knobs(cfg, precision=mok.MOK_MXFP8_WGRAD) if mx_wgrad else knobs(cfg))
     assert status_word(res["schedule"]) == 0
     rng = np.random.default_rng(1)
     f = L.bf16_bits_to_f64
@@ -60,7 +62,7 @@ def _check(cfg, experts_for_wgrad=2, n_tokens=48):
         tok = rows // cfg.k
         gw = inp.topk_w.reshape(-1)[rows][:, None].astype(np.float64)
         Wg, Wu, Wd = ew(int(e))
-        a, b, c = L.expert_wgrad_columns(f(inp.x[tok]), f(inp.dy[tok]), gw, Wg, Wu, Wd, cols, fq)
+        a, b, c = L.expert_wgrad_columns(f(inp.x[tok]), f(inp.dy[tok]), gw, Wg, Wu, Wd, cols, fq, wfq)
         ic = torch.from_numpy(cols).to(res["out"].device)
         errs[f"dw_gate[{e}]"] = L.rel_frobenius(host_f64(res["dw_gate"][int(e)][:, ic]), a)
         errs[f"dw_up[{e}]"] = L.rel_frobenius(host_f64(res["dw_up"][int(e)][:, ic]), b)
@@ -89,3 +91,7 @@ def test_ep64_share_mxfp8_zipf():
 
 def test_ep64_share_mxfp8_uniform():
     _check(synth.CONFIGS["ep64_share_mxfp8_uniform"])
+
+
+def test_ep64_share_mxfp8_wgrad():
+    _check(synth.CONFIGS["ep64_share_mxfp8"], mx_wgrad=True)

@@ -132,14 +132,15 @@ def test_fused_router_grad_identity():
     assert np.max(np.abs(g["dw"] - g["dw_direct"])) <= 1e-12 * max(1.0, np.max(np.abs(g["dw"])))
 
 
-@pytest.mark.parametrize("fq", [None, M.fake_quant], ids=["bf16", "mxfp8"])
-def test_sampled_forms_match_full(fq):
+@pytest.mark.parametrize("fq,wfq", [(None, None), (M.fake_quant, None), (M.fake_quant, M.fake_quant)],
+                         ids=["bf16", "mxfp8", "mxfp8_wgrad"])
+def test_sampled_forms_match_full(fq, wfq):
     cfg = synth.CONFIGS["tiny"]
     inp = synth.make_inputs(cfg)
     f = L.bf16_bits_to_f64
     x, dy, Wg, Wu, Wd = f(inp.x), f(inp.dy), f(inp.w_gate), f(inp.w_up), f(inp.w_down)
     out, _ = L.forward(x, inp.topk_ids, inp.topk_w, Wg, Wu, Wd, fq)
-    g = L.backward(x, inp.topk_ids, inp.topk_w, Wg, Wu, Wd, dy, fq)
+    g = L.backward(x, inp.topk_ids, inp.topk_w, Wg, Wu, Wd, dy, fq, wfq)
     toks = np.array([0, 5, 17, 63])
     ew = lambda e: (Wg[e], Wu[e], Wd[e])
     o = L.token_forward(x[toks], inp.topk_ids[toks], inp.topk_w[toks], ew, fq)
@@ -151,7 +152,7 @@ def test_sampled_forms_match_full(fq):
     rows = np.nonzero(inp.topk_ids.reshape(-1) == e)[0]
     cols = np.array([0, 7, 63])
     gw = inp.topk_w.reshape(-1)[rows][:, None].astype(np.float64)
-    a, b, c = L.expert_wgrad_columns(x[rows // cfg.k], dy[rows // cfg.k], gw, Wg[e], Wu[e], Wd[e], cols, fq)
+    a, b, c = L.expert_wgrad_columns(x[rows // cfg.k], dy[rows // cfg.k], gw, Wg[e], Wu[e], Wd[e], cols, fq, wfq)
     assert np.max(np.abs(a - g["dWg"][e][:, cols])) < 1e-12
     assert np.max(np.abs(b - g["dWu"][e][:, cols])) < 1e-12
     assert np.max(np.abs(c - g["dWd"][e][cols, :])) < 1e-12
