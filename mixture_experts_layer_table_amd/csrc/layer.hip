@@ -734,7 +734,10 @@ mok_status launch_backward(const Plan &p, const void *schedule, void *workspace,
     const uint16_t *wd = static_cast<const uint16_t *>(w.w_down);
     int *sync = reinterpret_cast<int *>(ws + p.w_sync);
     hipError_t err = hipSuccess;
-    if (p.R > 0 && whole_pass(p)) {   // one launch for the dgrad pass
+    bool wq_joined = false;   // MXFP8 weight gradients: x and dy quantizers forked to a side stream
+    if (p.mx_wgrad) err = mx_wgrad_begin(p, v, ws, x, dy, st, &wq_joined);
+    if (err != hipSuccess) {
+    } else if (p.R > 0 && whole_pass(p)) {   // one launch for the dgrad pass
         const int nta = (int)ceil_div(p.I, CfgA::BN), ntx = (int)ceil_div(p.H, CfgA::BN);
         DAArgs aa{v, 0, p.G, nta, p.n_slots, p.MB, p.H, p.I, p.dg_slices, ring, wd, h, topk_w, dh, ga, dgp};
         DXArgs xa{v, 0, p.G, ntx, p.n_slots, p.H, p.I, p.k, (int)p.MT, p.nb_full, dh, wg, wu, dx, stage};
@@ -777,8 +780,10 @@ mok_status launch_backward(const Plan &p, const void *schedule, void *workspace,
             reduce_router_grad<<<(unsigned)ceil_div(p.R, 256), 256, 0, st>>>(v, p.dg_slices, dgp, dtopk_w);
         }
     }
-    if (err == hipSuccess && p.mx_wgrad) {
-        err = mx_wgrad(p, v, ws, x, dy, dw_gate, dw_up, dw_down, st);
+    if (p.mx_wgrad) {
+        // after an error only the join: no fork is left open
+        const hipError_t e2 = mx_wgrad_finish(p, v, ws, wq_joined, err == hipSuccess, dw_gate, dw_up, dw_down, st);
+        if (err == hipSuccess) err = e2;
     } else if (err == hipSuccess) {
         const WGUArgs gu{v, p.H, p.I, x, dh, dw_gate, dw_up};
         const WDArgs wda{v, p.H, p.I, ga, dy, dw_down};

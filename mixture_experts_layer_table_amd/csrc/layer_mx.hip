@@ -13,6 +13,8 @@
 // Ring slot (MXFP8): elements [MB][H] then scales [MB][H/32]. a-ring slot
 // (same slot stride as BF16, MB*I*2 bytes): elements [MB][I], scales [MB][I/32].
 // Quantized dh: elements [R][2I], scales [R][2I/32], canonical row order.
+#include <mutex>
+
 #include "gemm8.h"
 #include "layer_mx.h"
 #include "layer_parts.h"
@@ -782,31 +784,95 @@ hipError_t mx_backward_round(const Plan &p, const SchedView &v, int g0, int g1, 
     return launch_gemm8<DX8<CfgA>>("dX", seg_grid(ntx, mt_bound), xa, st);
 }
 
-hipError_t mx_wgrad(const Plan &p, const SchedView &v, char *ws, const uint16_t *x, const uint16_t *dy,
-                    uint16_t *dw_gate, uint16_t *dw_up, uint16_t *dw_down, hipStream_t st) {
+namespace {
+
+// Side stream and fork/join events of one device, made on first use. The x
+// and dy quantizers run there, beside the backward rounds, which are bound by
+// the matrix cores while the quantizers are bound by memory.
+struct SideStream {
+    hipStream_t s = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+    bool tried = false;
+};
+std::mutex g_side_mu;
+SideStream g_side[64];
+
+// Call with g_side_mu held. Null stream: unavailable, run on the caller's stream.
+SideStream *side_stream() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    SideStream &ss = g_side[dev];
+    if (!ss.tried) {
+        ss.tried = true;
+        if (hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) != hipSuccess ||
+            hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess ||
+            hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess)
+            ss.s = nullptr;
+    }
+    return ss.s ? &ss : nullptr;
+}
+
+QuantCols quant_cols(const Plan &p, const SchedView &v, char *ws, int which, const uint16_t *x,
+                     const uint16_t *dy) {
     int32_t *po = reinterpret_cast<int32_t *>(ws + p.w_po);
     auto B = [&](size_t off) { return reinterpret_cast<uint8_t *>(ws + off); };
-    const uint16_t *dh = reinterpret_cast<const uint16_t *>(ws + p.w_dh);
-    const uint16_t *gav = reinterpret_cast<const uint16_t *>(ws + p.w_ga);
-    {
-        KernelTimer tm("wq_offsets", st);
-        wq_offsets<<<1, 256, 0, st>>>(v, po);
+    switch (which) {
+    case 0: return QuantCols{v, po, x, p.H, p.H, true, p.Kp, B(p.w_qx), B(p.w_qxs)};
+    case 1: return QuantCols{v, po, reinterpret_cast<const uint16_t *>(ws + p.w_dh), 2 * (int64_t)p.I, 2 * p.I,
+                             false, p.Kp, B(p.w_qdh), B(p.w_qdhs)};
+    case 2: return QuantCols{v, po, reinterpret_cast<const uint16_t *>(ws + p.w_ga), p.I, p.I, false, p.Kp,
+                             B(p.w_qga), B(p.w_qgas)};
+    default: return QuantCols{v, po, dy, p.H, p.H, true, p.Kp, B(p.w_qdy), B(p.w_qdys)};
     }
+}
+
+void launch_quant(const QuantCols &q, const Plan &p, const char *name, hipStream_t st) {
+    KernelTimer tm(name, st);
+    quantize_cols<<<dim3((unsigned)(p.Kp / kQRows), (unsigned)ceil_div(q.ncols, kQCols)), 256, 0, st>>>(q);
+}
+
+}  // namespace
+
+hipError_t mx_wgrad_begin(const Plan &p, const SchedView &v, char *ws, const uint16_t *x, const uint16_t *dy,
+                          hipStream_t st, bool *joined) {
+    *joined = false;
+    if (p.R == 0) return hipSuccess;
+    std::lock_guard<std::mutex> lock(g_side_mu);
+    SideStream *ss = side_stream();
+    hipStream_t q = st;
+    if (ss && hipEventRecord(ss->fork, st) == hipSuccess && hipStreamWaitEvent(ss->s, ss->fork, 0) == hipSuccess)
+        q = ss->s;
+    {
+        KernelTimer tm("wq_offsets", q);
+        wq_offsets<<<1, 256, 0, q>>>(v, reinterpret_cast<int32_t *>(ws + p.w_po));
+    }
+    launch_quant(quant_cols(p, v, ws, 0, x, dy), p, "wgrad_quantize_x_dy", q);
+    launch_quant(quant_cols(p, v, ws, 3, x, dy), p, "wgrad_quantize_x_dy", q);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    const unsigned nb = (unsigned)(p.Kp / kQRows);
-    const QuantCols qs[4] = {
-        {v, po, x, p.H, p.H, true, p.Kp, B(p.w_qx), B(p.w_qxs)},
-        {v, po, dh, 2 * (int64_t)p.I, 2 * p.I, false, p.Kp, B(p.w_qdh), B(p.w_qdhs)},
-        {v, po, gav, p.I, p.I, false, p.Kp, B(p.w_qga), B(p.w_qgas)},
-        {v, po, dy, p.H, p.H, true, p.Kp, B(p.w_qdy), B(p.w_qdys)},
-    };
+    if (q != st) {
+        if ((err = hipEventRecord(ss->join, q)) != hipSuccess) return err;
+        *joined = true;
+    }
+    return hipSuccess;
+}
+
+hipError_t mx_wgrad_finish(const Plan &p, const SchedView &v, char *ws, bool joined, bool compute,
+                           uint16_t *dw_gate, uint16_t *dw_up, uint16_t *dw_down, hipStream_t st) {
+    hipError_t err = hipSuccess;
+    if (joined) {
+        std::lock_guard<std::mutex> lock(g_side_mu);
+        // a later record of the same event on the in-order side stream also covers this call's work
+        if ((err = hipStreamWaitEvent(st, side_stream()->join, 0)) != hipSuccess) return err;
+    }
+    if (!compute) return hipSuccess;
     if (p.R > 0) {
-        KernelTimer tm("wgrad_quantize", st);
-        for (const QuantCols &q : qs)
-            quantize_cols<<<dim3(nb, (unsigned)ceil_div(q.ncols, kQCols)), 256, 0, st>>>(q);
+        launch_quant(quant_cols(p, v, ws, 1, nullptr, nullptr), p, "wgrad_quantize_dh_ga", st);
+        launch_quant(quant_cols(p, v, ws, 2, nullptr, nullptr), p, "wgrad_quantize_dh_ga", st);
     }
     if ((err = hipGetLastError()) != hipSuccess) return err;
+    auto B = [&](size_t off) { return reinterpret_cast<uint8_t *>(ws + off); };
+    const int32_t *po = reinterpret_cast<const int32_t *>(ws + p.w_po);
     const WGU8Args gu{v, p.H, p.I, p.Kp, po, B(p.w_qx), B(p.w_qxs), B(p.w_qdh), B(p.w_qdhs), dw_gate, dw_up};
     const WD8Args wd{v, p.H, p.I, p.Kp, po, B(p.w_qga), B(p.w_qgas), B(p.w_qdy), B(p.w_qdys), dw_down};
     err = launch_gemm8<WGU8<CfgA>>(
