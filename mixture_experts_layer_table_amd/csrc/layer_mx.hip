@@ -836,7 +836,11 @@ void launch_quant(const QuantCols &q, const Plan &p, const char *name, hipStream
 hipError_t mx_wgrad_begin(const Plan &p, const SchedView &v, char *ws, const uint16_t *x, const uint16_t *dy,
                           hipStream_t st, bool *joined) {
     *joined = false;
-    if (p.R == 0) return hipSuccess;
+    if (p.R == 0) {   // every count is 0: po all 0, so each weight-gradient tile has K = 0 and writes zeros
+        KernelTimer tm("wq_offsets", st);
+        wq_offsets<<<1, 256, 0, st>>>(v, reinterpret_cast<int32_t *>(ws + p.w_po));
+        return hipGetLastError();
+    }
     std::lock_guard<std::mutex> lock(g_side_mu);
     SideStream *ss = side_stream();
     hipStream_t q = st;

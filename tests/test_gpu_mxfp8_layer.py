@@ -102,3 +102,14 @@ def test_wgrad_deterministic_knob_invariant_and_empty_experts():
                  dict(debug_flags=mok.MOK_DEBUG_SEPARATE_LAUNCHES)):
         print(f"[mxfp8 wgrad] knobs {over}", flush=True)
         same_bits(first, run_layer(d, knobs(cfg, precision=mok.MOK_MXFP8_WGRAD, **over)))
+
+
+def test_wgrad_empty_call():
+    # T = 0: every expert is empty, so the weight gradients are zeros
+    cfg = _mx("mx_empty", T=0, H=128, I=128, E=4, k=2, minibatch_rows=16, ring_bytes=1 << 20)
+    d = DeviceInputs(synth.make_inputs(cfg))
+    res = run_layer(d, knobs(cfg, precision=mok.MOK_MXFP8_WGRAD))
+    assert res["out"].numel() == 0 and res["dx"].numel() == 0
+    for n in ("dw_gate", "dw_up", "dw_down"):
+        assert not res[n].float().abs().sum().item()
+
