@@ -279,13 +279,18 @@ def build_schedule(ws: Workspace, topk_ids, schedule=None):
 
 
 def weights_bf16(w_gate, w_up, w_down) -> mok_weights:
-    return mok_weights(w_gate.data_ptr(), w_up.data_ptr(), w_down.data_ptr(), None, None, None, None, None, None)
+    """The struct keeps references to the tensors, so their memory lives as long as it does."""
+    w = mok_weights(w_gate.data_ptr(), w_up.data_ptr(), w_down.data_ptr(), None, None, None, None, None, None)
+    w._tensors = (w_gate, w_up, w_down)
+    return w
 
 
 def weights_mxfp8(gate, up, down) -> mok_weights:
-    """Each argument is an (elems, scales) pair of uint8 tensors."""
-    return mok_weights(None, None, None, gate[0].data_ptr(), gate[1].data_ptr(), up[0].data_ptr(),
-                       up[1].data_ptr(), down[0].data_ptr(), down[1].data_ptr())
+    """Each argument is an (elems, scales) pair of uint8 tensors (kept referenced by the struct)."""
+    w = mok_weights(None, None, None, gate[0].data_ptr(), gate[1].data_ptr(), up[0].data_ptr(),
+                    up[1].data_ptr(), down[0].data_ptr(), down[1].data_ptr())
+    w._tensors = (gate, up, down)
+    return w
 
 
 class MXFP8Weights:

@@ -165,3 +165,26 @@ def test_autosize_rejects_bad_arguments():
     lib = ctypes.CDLL(mok._LIB_PATH)
     lib.mok_config_autosize.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32]
     assert lib.mok_config_autosize(None, None, 0) == mok.MOK_ERROR_INVALID_VALUE
+
+
+def test_weight_structs_keep_their_tensors_alive():
+    # the structs hold raw pointers; the binding keeps the tensors referenced so
+    # that temporaries passed in are not freed (and their memory reused) before the call
+    import gc
+    import weakref
+    import torch
+    t = torch.ones(8)
+    r = weakref.ref(t)
+    w = mok.weights_bf16(t, torch.ones(2), torch.ones(2))
+    del t
+    gc.collect()
+    assert r() is not None
+    pair = (torch.ones(4, dtype=torch.uint8), torch.ones(1, dtype=torch.uint8))
+    r2 = weakref.ref(pair[0])
+    w8 = mok.weights_mxfp8(pair, pair, pair)
+    del pair
+    gc.collect()
+    assert r2() is not None
+    del w, w8
+    gc.collect()
+    assert r() is None and r2() is None
