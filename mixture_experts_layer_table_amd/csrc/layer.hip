@@ -640,6 +640,7 @@ hipError_t bwd_round_gemms(const Plan &p, const DAArgs &aa, const DXArgs &xa, in
 }
 
 // The weight-gradient GEMMs (dW_gate | dW_up, then dW_down), in the tile family C.
+// (Running dW_down beside dW_gate | dW_up on a second stream measured no faster.)
 template <class C>
 hipError_t wgrad_gemms(const Plan &p, const WGUArgs &gu, const WDArgs &wda, hipStream_t st) {
     const hipError_t e = launch_gemm<WGU<C>>(
@@ -734,8 +735,8 @@ mok_status launch_backward(const Plan &p, const void *schedule, void *workspace,
     const uint16_t *wd = static_cast<const uint16_t *>(w.w_down);
     int *sync = reinterpret_cast<int *>(ws + p.w_sync);
     hipError_t err = hipSuccess;
-    bool wq_joined = false;   // MXFP8 weight gradients: x and dy quantizers forked to a side stream
-    if (p.mx_wgrad) err = mx_wgrad_begin(p, v, ws, x, dy, st, &wq_joined);
+    hipStream_t wq_side = st;   // MXFP8 weight gradients: x and dy quantizers forked to a side stream
+    if (p.mx_wgrad) err = mx_wgrad_begin(p, v, ws, x, dy, st, &wq_side);
     if (err != hipSuccess) {
     } else if (p.R > 0 && whole_pass(p)) {   // one launch for the dgrad pass
         const int nta = (int)ceil_div(p.I, CfgA::BN), ntx = (int)ceil_div(p.H, CfgA::BN);
@@ -782,7 +783,7 @@ mok_status launch_backward(const Plan &p, const void *schedule, void *workspace,
     }
     if (p.mx_wgrad) {
         // after an error only the join: no fork is left open
-        const hipError_t e2 = mx_wgrad_finish(p, v, ws, wq_joined, err == hipSuccess, dw_gate, dw_up, dw_down, st);
+        const hipError_t e2 = mx_wgrad_finish(p, v, ws, wq_side, err == hipSuccess, dw_gate, dw_up, dw_down, st);
         if (err == hipSuccess) err = e2;
     } else if (err == hipSuccess) {
         const WGUArgs gu{v, p.H, p.I, x, dh, dw_gate, dw_up};

@@ -23,14 +23,14 @@ hipError_t mx_backward_round(const Plan &p, const SchedView &v, int g0, int g1, 
 
 // MXFP8 weight gradients (MOK_MXFP8_WGRAD). begin, before the backward
 // rounds: the padded expert offsets and x and dy quantized along the token
-// axis, on a side stream forked from st when one is available (*joined then
-// says finish must join it). finish, after the rounds: dh and g*a quantized
+// axis, on the side stream forked from st (*side; st itself when none is
+// available). finish, after the rounds: joins *side, then dh and g*a quantized
 // the same way (canonical order), then the two block-scaled weight-gradient
 // GEMMs on st (compute = false: only the join, after an error). All
 // operands live in the workspace.
 hipError_t mx_wgrad_begin(const Plan &p, const SchedView &v, char *ws, const uint16_t *x, const uint16_t *dy,
-                          hipStream_t st, bool *joined);
-hipError_t mx_wgrad_finish(const Plan &p, const SchedView &v, char *ws, bool joined, bool compute,
+                          hipStream_t st, hipStream_t *side);
+hipError_t mx_wgrad_finish(const Plan &p, const SchedView &v, char *ws, hipStream_t side, bool compute,
                            uint16_t *dw_gate, uint16_t *dw_up, uint16_t *dw_down, hipStream_t st);
 
 }  // namespace mok

@@ -13,12 +13,11 @@
 // Ring slot (MXFP8): elements [MB][H] then scales [MB][H/32]. a-ring slot
 // (same slot stride as BF16, MB*I*2 bytes): elements [MB][I], scales [MB][I/32].
 // Quantized dh: elements [R][2I], scales [R][2I/32], canonical row order.
-#include <mutex>
-
 #include "gemm8.h"
 #include "layer_mx.h"
 #include "layer_parts.h"
 #include "mx_codec.h"
+#include "streams.h"
 
 namespace mok {
 namespace {
@@ -786,32 +785,6 @@ hipError_t mx_backward_round(const Plan &p, const SchedView &v, int g0, int g1, 
 
 namespace {
 
-// Side stream and fork/join events of one device, made on first use. The x
-// and dy quantizers run there, beside the backward rounds, which are bound by
-// the matrix cores while the quantizers are bound by memory.
-struct SideStream {
-    hipStream_t s = nullptr;
-    hipEvent_t fork = nullptr, join = nullptr;
-    bool tried = false;
-};
-std::mutex g_side_mu;
-SideStream g_side[64];
-
-// Call with g_side_mu held. Null stream: unavailable, run on the caller's stream.
-SideStream *side_stream() {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
-    SideStream &ss = g_side[dev];
-    if (!ss.tried) {
-        ss.tried = true;
-        if (hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) != hipSuccess ||
-            hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess ||
-            hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess)
-            ss.s = nullptr;
-    }
-    return ss.s ? &ss : nullptr;
-}
-
 QuantCols quant_cols(const Plan &p, const SchedView &v, char *ws, int which, const uint16_t *x,
                      const uint16_t *dy) {
     int32_t *po = reinterpret_cast<int32_t *>(ws + p.w_po);
@@ -834,42 +807,30 @@ void launch_quant(const QuantCols &q, const Plan &p, const char *name, hipStream
 }  // namespace
 
 hipError_t mx_wgrad_begin(const Plan &p, const SchedView &v, char *ws, const uint16_t *x, const uint16_t *dy,
-                          hipStream_t st, bool *joined) {
-    *joined = false;
+                          hipStream_t st, hipStream_t *side) {
+    *side = st;
     if (p.R == 0) {   // every count is 0: po all 0, so each weight-gradient tile has K = 0 and writes zeros
         KernelTimer tm("wq_offsets", st);
         wq_offsets<<<1, 256, 0, st>>>(v, reinterpret_cast<int32_t *>(ws + p.w_po));
         return hipGetLastError();
     }
-    std::lock_guard<std::mutex> lock(g_side_mu);
-    SideStream *ss = side_stream();
-    hipStream_t q = st;
-    if (ss && hipEventRecord(ss->fork, st) == hipSuccess && hipStreamWaitEvent(ss->s, ss->fork, 0) == hipSuccess)
-        q = ss->s;
+    // x and dy are inputs: their quantizers run beside the backward rounds,
+    // which are bound by the matrix cores while the quantizers are bound by memory
+    const hipStream_t q = side_fork(st);
+    *side = q;
     {
         KernelTimer tm("wq_offsets", q);
         wq_offsets<<<1, 256, 0, q>>>(v, reinterpret_cast<int32_t *>(ws + p.w_po));
     }
     launch_quant(quant_cols(p, v, ws, 0, x, dy), p, "wgrad_quantize_x_dy", q);
     launch_quant(quant_cols(p, v, ws, 3, x, dy), p, "wgrad_quantize_x_dy", q);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    if (q != st) {
-        if ((err = hipEventRecord(ss->join, q)) != hipSuccess) return err;
-        *joined = true;
-    }
-    return hipSuccess;
+    return hipGetLastError();
 }
 
-hipError_t mx_wgrad_finish(const Plan &p, const SchedView &v, char *ws, bool joined, bool compute,
+hipError_t mx_wgrad_finish(const Plan &p, const SchedView &v, char *ws, hipStream_t side, bool compute,
                            uint16_t *dw_gate, uint16_t *dw_up, uint16_t *dw_down, hipStream_t st) {
-    hipError_t err = hipSuccess;
-    if (joined) {
-        std::lock_guard<std::mutex> lock(g_side_mu);
-        // a later record of the same event on the in-order side stream also covers this call's work
-        if ((err = hipStreamWaitEvent(st, side_stream()->join, 0)) != hipSuccess) return err;
-    }
-    if (!compute) return hipSuccess;
+    hipError_t err = side_join(st, side);
+    if (err != hipSuccess || !compute) return err;
     if (p.R > 0) {
         launch_quant(quant_cols(p, v, ws, 1, nullptr, nullptr), p, "wgrad_quantize_dh_ga", st);
         launch_quant(quant_cols(p, v, ws, 2, nullptr, nullptr), p, "wgrad_quantize_dh_ga", st);
