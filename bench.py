@@ -58,12 +58,21 @@ def flops_per_row(H, I):
                 wgrad_gate_up=4 * H * I, wgrad_down=2 * H * I)
 
 
-def source_digest() -> str:
-    """Digest of the device-code sources (HIP files and the headers they include)."""
+def _code_only(text: str) -> str:
+    """Source text without // and /* */ comments and blank lines (string literals
+    holding comment markers are not expected in these sources)."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = (re.sub(r"//.*", "", l).rstrip() for l in text.splitlines())
+    return "\n".join(l for l in lines if l)
+
+
+def source_digest(csrc: str = "") -> str:
+    """Digest of the device-code sources (HIP files and the headers they include),
+    comments excluded, so that a comment edit does not retire the counters."""
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "mixture_experts_layer_table_amd", "csrc")
+    csrc = csrc or os.path.join(ROOT, "mixture_experts_layer_table_amd", "csrc")
     for p in sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.h"))):
-        h.update(open(p, "rb").read())
+        h.update(_code_only(open(p, encoding="utf-8").read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -7,8 +7,9 @@
 //   forward down      a (quantized in the gate/up epilogue from its fp32 value) x W_down^T
 //   backward dA       dy rows (quantized by the ring gather) x W_down
 //   backward dX       dh (quantized in the dA epilogue from its fp32 value) x W_gate | W_up
-// h, y, dh (for the weight gradients), dx rows and all outputs stay bf16, and
-// the weight gradients run in BF16 (they have no weight operand).
+// h, y, dh (for the weight gradients), dx rows and all outputs stay bf16. The
+// weight gradients run in BF16 (they have no weight operand), or, with
+// MOK_MXFP8_WGRAD, on operands quantized along the token axis (below).
 //
 // Ring slot (MXFP8): elements [MB][H] then scales [MB][H/32]. a-ring slot
 // (same slot stride as BF16, MB*I*2 bytes): elements [MB][I], scales [MB][I/32].
