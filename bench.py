@@ -66,13 +66,26 @@ def _code_only(text: str) -> str:
     return "\n".join(l for l in lines if l)
 
 
-def source_digest(csrc: str = "") -> str:
-    """Digest of the device-code sources (HIP files and the headers they include),
-    comments excluded, so that a comment edit does not retire the counters."""
+def build_flags(build_py: str = "") -> str:
+    """The compiler command-line pieces of the library's build script (its COMMON
+    flag list and the source list), as text: a flag change alters the kernels."""
+    build_py = build_py or os.path.join(ROOT, "mixture_experts_layer_table_amd", "build.py")
+    text = open(build_py, encoding="utf-8").read()
+    parts = re.findall(r"^(SOURCES|COMMON)\s*=\s*(\[.*?\])", text, re.M | re.S)
+    return "\n".join(f"{k}=" + re.sub(r"\s+", "", re.sub(r"#.*", "", v)) for k, v in parts)
+
+
+def source_digest(csrc: str = "", build_py: str = "") -> str:
+    """Digest of everything that decides the kernels' code and launches: the HIP
+    files, the headers they include, the host sources (plan, streams, timing:
+    slot counts, workspace layout, launch shapes) and the build flags, comments
+    excluded, so that a comment edit does not retire the counters."""
     h = hashlib.sha256()
     csrc = csrc or os.path.join(ROOT, "mixture_experts_layer_table_amd", "csrc")
-    for p in sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.h"))):
+    for p in sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.h")) +
+                    glob.glob(os.path.join(csrc, "*.cpp"))):
         h.update(_code_only(open(p, encoding="utf-8").read()).encode())
+    h.update(build_flags(build_py).encode())
     return h.hexdigest()[:16]
 
 

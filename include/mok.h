@@ -64,6 +64,12 @@ typedef enum mok_status {
 /* a persistent kernel's work queue made no progress within its spin limit
    (never expected; outputs are then undefined and the kernel has exited) */
 #define MOK_SCHEDULER_STALLED 4u
+/* mok_forward / mok_backward got a schedule table built for another layout:
+   a different shape, minibatch_rows, macrobatch_tokens, capacity_multiplier
+   or m-tile height (set by the precision). The builder writes a fingerprint of
+   these into the table and each reader checks it before reading anything
+   else; no work is done after a mismatch. */
+#define MOK_SCHEDULE_MISMATCH 8u
 
 /* debug_flags: replace every expert by the identity on its rows (forward only;
    out_t = sum_j g_tj * x_t). Used to test permute followed by unpermute. */
@@ -76,11 +82,9 @@ typedef enum mok_status {
 /* debug_flags (k == 1 only): run each whole forward / dgrad pass as one
    persistent launch in which gathers and both GEMMs of every ring round
    follow the in-kernel ring protocol (slot full / release counters) instead
-   of stream order between rounds. Same results, bit for bit. BF16 only:
-   MXFP8 mode ignores the flag. Not the default: on this GPU every cross-XCD
-   handoff inside a kernel costs a device-scope L2 write-back / invalidate,
-   and the measured pass is slower than the gather kernel plus the
-   persistent GEMM pair. */
+   of stream order between rounds. Currently switched off: every call that
+   sets it returns MOK_ERROR_UNSUPPORTED and enqueues nothing, because runs
+   that included this mode hung twice without a shown cause. */
 #define MOK_DEBUG_WHOLE_PASS 4u
 /* debug_flags: every wait inside the persistent kernels gives up at once, as
    if its poll budget were spent. The call then ends with
@@ -100,6 +104,11 @@ typedef enum mok_status {
  *   capacity_multiplier schedule capacity relative to the worst case, in (0, 4]
  *   precision           MOK_BF16, MOK_MXFP8 or MOK_MXFP8_WGRAD
  *   debug_flags         0 in production
+ *   persistent_workgroups  workgroups of each persistent-kernel launch, in
+ *                       [0, 65535]; 0 (the default) = one per compute unit.
+ *                       Fewer leave units idle, more wait behind the resident
+ *                       ones; the work queues give every value the same bits
+ *                       (a grid-size sweep is part of the race tests).
  */
 typedef struct mok_config {
     int32_t minibatch_rows;
@@ -108,6 +117,7 @@ typedef struct mok_config {
     int64_t ring_bytes;
     float capacity_multiplier;
     uint32_t debug_flags;
+    int32_t persistent_workgroups;
 } mok_config;
 
 /*
@@ -164,7 +174,8 @@ typedef struct mok_schedule_layout {
 } mok_schedule_layout;
 
 /* Fill *cfg with the defaults: 512-row mini-batches, one macro-batch, a
-   256 MiB ring, capacity multiplier 1, BF16, no debug flags. */
+   256 MiB ring, capacity multiplier 1, BF16, no debug flags, one persistent
+   workgroup per compute unit. */
 mok_status mok_config_default(mok_config *cfg);
 
 /*
@@ -222,6 +233,10 @@ mok_status mok_build_schedule(const mok_config *cfg, const mok_shape *shape,
  * Forward pass ("Mixture-of-Kittens (MoK)" project summary, Functional API:
  * forward -> (out, fwd_ctx); "Mixture-of-Kittens(MoK)란?" explainer, section
  * 4 ③: ring token buffer consumed in mini-batches).
+ *   schedule the table mok_build_schedule wrote (schedule_bytes long) for
+ *            the same shape, minibatch_rows, macrobatch_tokens,
+ *            capacity_multiplier and precision; checked against a layout
+ *            fingerprint before use (MOK_SCHEDULE_MISMATCH)
  *   x        device bf16 [T,H]
  *   topk_w   device fp32 [T,k] gate weights
  *   w        expert weights (see mok_weights)
@@ -230,7 +245,8 @@ mok_status mok_build_schedule(const mok_config *cfg, const mok_shape *shape,
  *   fwd_ctx  device buffer (fwd_ctx_bytes), written; read by mok_backward
  */
 mok_status mok_forward(const mok_config *cfg, const mok_shape *shape,
-                       const void *schedule, void *workspace, size_t workspace_bytes,
+                       const void *schedule, size_t schedule_bytes,
+                       void *workspace, size_t workspace_bytes,
                        const void *x, const float *topk_w, const mok_weights *w,
                        void *out, void *fwd_ctx, size_t fwd_ctx_bytes, void *stream);
 
@@ -240,7 +256,8 @@ mok_status mok_forward(const mok_config *cfg, const mok_shape *shape,
  * 란?" explainer, section 4 ③: the ring is walked in reverse; "Cursor
  * Open-Sources Mixture-of-Kittens (MoK)" digest, English abstract: the
  * router-weight gradient is fused into the SwiGLU backward).
- *   x, topk_w, w, schedule, fwd_ctx   as given to mok_forward
+ *   x, topk_w, w, schedule, fwd_ctx   as given to mok_forward (the schedule
+ *            is checked as there)
  *   dy       device bf16 [T,H]
  *   dx       device bf16 [T,H]
  *   dw_gate, dw_up [E,H,I] and dw_down [E,I,H], device bf16, overwritten
@@ -248,7 +265,8 @@ mok_status mok_forward(const mok_config *cfg, const mok_shape *shape,
  *   dtopk_w  device fp32 [T,k]: d loss / d topk_w[t,j] = <dy_t, y_{t,j}>
  */
 mok_status mok_backward(const mok_config *cfg, const mok_shape *shape,
-                        const void *schedule, void *workspace, size_t workspace_bytes,
+                        const void *schedule, size_t schedule_bytes,
+                        void *workspace, size_t workspace_bytes,
                         const void *x, const float *topk_w, const mok_weights *w,
                         const void *fwd_ctx, size_t fwd_ctx_bytes, const void *dy,
                         void *dx, void *dw_gate, void *dw_up, void *dw_down,

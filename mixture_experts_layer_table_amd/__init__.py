@@ -36,7 +36,7 @@ _lib = ctypes.CDLL(_LIB_PATH)
 MOK_OK, MOK_ERROR_INVALID_VALUE, MOK_ERROR_UNSUPPORTED, MOK_ERROR_BUFFER_TOO_SMALL, \
     MOK_ERROR_LAUNCH_FAILED = range(5)
 MOK_BF16, MOK_MXFP8, MOK_MXFP8_WGRAD = 0, 1, 2
-MOK_SCHEDULE_OVERFLOW, MOK_BAD_EXPERT_ID, MOK_SCHEDULER_STALLED = 1, 2, 4
+MOK_SCHEDULE_OVERFLOW, MOK_BAD_EXPERT_ID, MOK_SCHEDULER_STALLED, MOK_SCHEDULE_MISMATCH = 1, 2, 4, 8
 MOK_DEBUG_IDENTITY_EXPERT, MOK_DEBUG_SEPARATE_LAUNCHES, MOK_DEBUG_WHOLE_PASS, MOK_DEBUG_FORCE_STALL = 1, 2, 4, 8
 
 EXPORTS = ("mok_config_default", "mok_config_autosize", "mok_query_sizes", "mok_schedule_layout_query",
@@ -48,7 +48,8 @@ EXPORTS = ("mok_config_default", "mok_config_autosize", "mok_query_sizes", "mok_
 class mok_config(ctypes.Structure):
     _fields_ = [("minibatch_rows", ctypes.c_int32), ("precision", ctypes.c_int32),
                 ("macrobatch_tokens", ctypes.c_int64), ("ring_bytes", ctypes.c_int64),
-                ("capacity_multiplier", ctypes.c_float), ("debug_flags", ctypes.c_uint32)]
+                ("capacity_multiplier", ctypes.c_float), ("debug_flags", ctypes.c_uint32),
+                ("persistent_workgroups", ctypes.c_int32)]
 
 
 class mok_shape(ctypes.Structure):
@@ -85,11 +86,11 @@ _sigs = {
                                   ctypes.POINTER(mok_schedule_layout)],
     "mok_build_schedule": [ctypes.POINTER(mok_config), ctypes.POINTER(mok_shape), _P, _P,
                            ctypes.c_size_t, _P],
-    "mok_forward": [ctypes.POINTER(mok_config), ctypes.POINTER(mok_shape), _P, _P, ctypes.c_size_t,
-                    _P, _P, ctypes.POINTER(mok_weights), _P, _P, ctypes.c_size_t, _P],
-    "mok_backward": [ctypes.POINTER(mok_config), ctypes.POINTER(mok_shape), _P, _P, ctypes.c_size_t,
-                     _P, _P, ctypes.POINTER(mok_weights), _P, ctypes.c_size_t, _P, _P, _P, _P, _P,
-                     _P, _P],
+    "mok_forward": [ctypes.POINTER(mok_config), ctypes.POINTER(mok_shape), _P, ctypes.c_size_t, _P,
+                    ctypes.c_size_t, _P, _P, ctypes.POINTER(mok_weights), _P, _P, ctypes.c_size_t, _P],
+    "mok_backward": [ctypes.POINTER(mok_config), ctypes.POINTER(mok_shape), _P, ctypes.c_size_t, _P,
+                     ctypes.c_size_t, _P, _P, ctypes.POINTER(mok_weights), _P, ctypes.c_size_t, _P, _P, _P,
+                     _P, _P, _P, _P],
     "mok_mxfp8_quantize": [_P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
                            _P, _P, _P],
     "mok_route": [_P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _P, _P, _P],
@@ -150,15 +151,16 @@ def mok_build_schedule(cfg, shape, topk_ids, schedule, schedule_bytes, stream):
                                    schedule_bytes, stream)
 
 
-def mok_forward(cfg, shape, schedule, workspace, workspace_bytes, x, topk_w, weights, out, fwd_ctx,
-                fwd_ctx_bytes, stream):
-    return _lib.mok_forward(ctypes.byref(cfg), ctypes.byref(shape), schedule, workspace, workspace_bytes,
-                            x, topk_w, ctypes.byref(weights), out, fwd_ctx, fwd_ctx_bytes, stream)
+def mok_forward(cfg, shape, schedule, schedule_bytes, workspace, workspace_bytes, x, topk_w, weights, out,
+                fwd_ctx, fwd_ctx_bytes, stream):
+    return _lib.mok_forward(ctypes.byref(cfg), ctypes.byref(shape), schedule, schedule_bytes, workspace,
+                            workspace_bytes, x, topk_w, ctypes.byref(weights), out, fwd_ctx, fwd_ctx_bytes,
+                            stream)
 
 
-def mok_backward(cfg, shape, schedule, workspace, workspace_bytes, x, topk_w, weights, fwd_ctx,
-                 fwd_ctx_bytes, dy, dx, dw_gate, dw_up, dw_down, dtopk_w, stream):
-    return _lib.mok_backward(ctypes.byref(cfg), ctypes.byref(shape), schedule, workspace,
+def mok_backward(cfg, shape, schedule, schedule_bytes, workspace, workspace_bytes, x, topk_w, weights,
+                 fwd_ctx, fwd_ctx_bytes, dy, dx, dw_gate, dw_up, dw_down, dtopk_w, stream):
+    return _lib.mok_backward(ctypes.byref(cfg), ctypes.byref(shape), schedule, schedule_bytes, workspace,
                              workspace_bytes, x, topk_w, ctypes.byref(weights), fwd_ctx, fwd_ctx_bytes,
                              dy, dx, dw_gate, dw_up, dw_down, dtopk_w, stream)
 
@@ -206,10 +208,12 @@ class MoKConfig:
     capacity_multiplier: float = 1.0
     precision: int = MOK_BF16
     debug_flags: int = 0
+    persistent_workgroups: int = 0      # 0: one per compute unit
 
     def c(self) -> mok_config:
         return mok_config(self.minibatch_rows, self.precision, self.macrobatch_tokens,
-                          self.ring_bytes, self.capacity_multiplier, self.debug_flags)
+                          self.ring_bytes, self.capacity_multiplier, self.debug_flags,
+                          self.persistent_workgroups)
 
 
 def _shape(T, H, I, E, k) -> mok_shape:
@@ -238,6 +242,35 @@ def schedule_layout(config: MoKConfig, T, H, I, E, k) -> mok_schedule_layout:
 
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _require(t, name, dtype, shape, device=None):
+    """The C ABI receives raw pointers and no sizes for most tensors, so every
+    tensor is checked here before a call: dtype (an int64 id tensor read as
+    int32 would route silently wrong), exact shape (a short output would be
+    written past its end), contiguity and device."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor, got {type(t).__name__}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if device is not None and t.device != torch.device(device):
+        raise ValueError(f"{name}: on {t.device}, expected {device}")
+
+
+def _require_bytes(t, name, nbytes, device=None):
+    """A caller-given uint8 buffer of at least nbytes (workspace, schedule, fwd_ctx)."""
+    import torch
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.uint8 or t.dim() != 1 or not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous 1-D uint8 tensor")
+    if t.numel() < nbytes:
+        raise ValueError(f"{name}: {t.numel()} bytes, need {nbytes}")
+    if device is not None and t.device != torch.device(device):
+        raise ValueError(f"{name}: on {t.device}, expected {device}")
 
 
 def _stream():
@@ -271,8 +304,11 @@ def get_workspace(config: MoKConfig, *, device, num_local_tokens: int, hidden_si
 def build_schedule(ws: Workspace, topk_ids, schedule=None):
     """topk_ids: int32 [T,k] on the device. Returns the schedule buffer (uint8 tensor)."""
     import torch
+    dev = ws.buffer.device
+    _require(topk_ids, "topk_ids", torch.int32, (ws.T, ws.k), dev)
     if schedule is None:
-        schedule = torch.empty(max(ws.schedule_bytes, 256), dtype=torch.uint8, device=ws.buffer.device)
+        schedule = torch.empty(max(ws.schedule_bytes, 256), dtype=torch.uint8, device=dev)
+    _require_bytes(schedule, "schedule", ws.schedule_bytes, dev)
     _check(mok_build_schedule(ws.config.c(), _shape(ws.T, ws.H, ws.I, ws.E, ws.k), _ptr(topk_ids),
                               _ptr(schedule), schedule.numel(), _stream()), "mok_build_schedule")
     return schedule
@@ -282,15 +318,47 @@ def weights_bf16(w_gate, w_up, w_down) -> mok_weights:
     """The struct keeps references to the tensors, so their memory lives as long as it does."""
     w = mok_weights(w_gate.data_ptr(), w_up.data_ptr(), w_down.data_ptr(), None, None, None, None, None, None)
     w._tensors = (w_gate, w_up, w_down)
+    w._kind = "bf16"
     return w
 
 
-def weights_mxfp8(gate, up, down) -> mok_weights:
-    """Each argument is an (elems, scales) pair of uint8 tensors (kept referenced by the struct)."""
+def weights_mxfp8(gate, up, down, orientation: str = "") -> mok_weights:
+    """Each argument is an (elems, scales) pair of uint8 tensors (kept referenced
+    by the struct); orientation "fwd" or "bwd" when known (MXFP8Weights sets it)."""
     w = mok_weights(None, None, None, gate[0].data_ptr(), gate[1].data_ptr(), up[0].data_ptr(),
                     up[1].data_ptr(), down[0].data_ptr(), down[1].data_ptr())
     w._tensors = (gate, up, down)
+    w._kind = "mxfp8" + (":" + orientation if orientation else "")
     return w
+
+
+def _check_weights(ws: "Workspace", weights: mok_weights, orientation: str):
+    """Shapes, dtypes and devices of the tensors a weight struct refers to."""
+    import torch
+    tensors = getattr(weights, "_tensors", None)
+    if tensors is None:          # a hand-made struct: nothing to check against
+        return
+    dev = ws.buffer.device
+    E, H, I = ws.E, ws.H, ws.I
+    mx = ws.config.precision in (MOK_MXFP8, MOK_MXFP8_WGRAD)
+    kind = getattr(weights, "_kind", "")
+    if not mx:
+        if not kind.startswith("bf16"):
+            raise ValueError("BF16 mode needs bf16 weights (weights_bf16)")
+        for t, n, sh in zip(tensors, ("w_gate", "w_up", "w_down"), ((E, H, I), (E, H, I), (E, I, H))):
+            _require(t, n, torch.bfloat16, sh, dev)
+        return
+    if not kind.startswith("mxfp8"):
+        raise ValueError("MXFP8 mode needs quantized weights (MXFP8Weights)")
+    if ":" in kind and kind.split(":")[1] != orientation:
+        raise ValueError(f"MXFP8 weights quantized for {kind.split(':')[1]}, used in {orientation}")
+    if orientation == "fwd":        # quantized along the forward contraction axes
+        shapes = ((E, I, H), (E, I, H), (E, H, I))
+    else:
+        shapes = ((E, H, I), (E, H, I), (E, I, H))
+    for (el, sc), n, sh in zip(tensors, ("gate", "up", "down"), shapes):
+        _require(el, n + " elements", torch.uint8, sh, dev)
+        _require(sc, n + " scales", torch.uint8, sh[:2] + (sh[2] // 32,), dev)
 
 
 class MXFP8Weights:
@@ -307,19 +375,26 @@ class MXFP8Weights:
         self.bwd_gate = mxfp8_quantize(w_gate, False)
         self.bwd_up = mxfp8_quantize(w_up, False)
         self.bwd_down = mxfp8_quantize(w_down, False)
-        self.fwd = weights_mxfp8(self.fwd_gate, self.fwd_up, self.fwd_down)
-        self.bwd = weights_mxfp8(self.bwd_gate, self.bwd_up, self.bwd_down)
+        self.fwd = weights_mxfp8(self.fwd_gate, self.fwd_up, self.fwd_down, "fwd")
+        self.bwd = weights_mxfp8(self.bwd_gate, self.bwd_up, self.bwd_down, "bwd")
 
 
 def forward(ws: Workspace, schedule, x, topk_w, weights: mok_weights, out=None, fwd_ctx=None):
     """Returns (out bf16 [T,H], fwd_ctx uint8)."""
     import torch
+    dev = ws.buffer.device
     if out is None:
-        out = torch.empty((ws.T, ws.H), dtype=torch.bfloat16, device=ws.buffer.device)
+        out = torch.empty((ws.T, ws.H), dtype=torch.bfloat16, device=dev)
     if fwd_ctx is None:
-        fwd_ctx = torch.empty(max(ws.fwd_ctx_bytes, 256), dtype=torch.uint8, device=ws.buffer.device)
+        fwd_ctx = torch.empty(max(ws.fwd_ctx_bytes, 256), dtype=torch.uint8, device=dev)
+    _require_bytes(schedule, "schedule", ws.schedule_bytes, dev)
+    _require(x, "x", torch.bfloat16, (ws.T, ws.H), dev)
+    _require(topk_w, "topk_w", torch.float32, (ws.T, ws.k), dev)
+    _require(out, "out", torch.bfloat16, (ws.T, ws.H), dev)
+    _require_bytes(fwd_ctx, "fwd_ctx", ws.fwd_ctx_bytes, dev)
+    _check_weights(ws, weights, "fwd")
     _check(mok_forward(ws.config.c(), _shape(ws.T, ws.H, ws.I, ws.E, ws.k), _ptr(schedule),
-                       _ptr(ws.buffer), ws.buffer.numel(), _ptr(x), _ptr(topk_w), weights, _ptr(out),
+                       schedule.numel(), _ptr(ws.buffer), ws.buffer.numel(), _ptr(x), _ptr(topk_w), weights, _ptr(out),
                        _ptr(fwd_ctx), fwd_ctx.numel(), _stream()), "mok_forward")
     return out, fwd_ctx
 
@@ -328,14 +403,21 @@ def backward(ws: Workspace, schedule, fwd_ctx, x, topk_w, weights: mok_weights, 
     """Returns dict(dx, dw_gate, dw_up, dw_down, dtopk_w)."""
     import torch
     dev = ws.buffer.device
+    shapes = dict(dx=((ws.T, ws.H), torch.bfloat16), dw_gate=((ws.E, ws.H, ws.I), torch.bfloat16),
+                  dw_up=((ws.E, ws.H, ws.I), torch.bfloat16), dw_down=((ws.E, ws.I, ws.H), torch.bfloat16),
+                  dtopk_w=((ws.T, ws.k), torch.float32))
     if grads is None:
-        grads = dict(dx=torch.empty((ws.T, ws.H), dtype=torch.bfloat16, device=dev),
-                     dw_gate=torch.empty((ws.E, ws.H, ws.I), dtype=torch.bfloat16, device=dev),
-                     dw_up=torch.empty((ws.E, ws.H, ws.I), dtype=torch.bfloat16, device=dev),
-                     dw_down=torch.empty((ws.E, ws.I, ws.H), dtype=torch.bfloat16, device=dev),
-                     dtopk_w=torch.empty((ws.T, ws.k), dtype=torch.float32, device=dev))
+        grads = {n: torch.empty(sh, dtype=dt, device=dev) for n, (sh, dt) in shapes.items()}
+    for n, (sh, dt) in shapes.items():
+        _require(grads[n], n, dt, sh, dev)
+    _require_bytes(schedule, "schedule", ws.schedule_bytes, dev)
+    _require_bytes(fwd_ctx, "fwd_ctx", ws.fwd_ctx_bytes, dev)
+    _require(x, "x", torch.bfloat16, (ws.T, ws.H), dev)
+    _require(topk_w, "topk_w", torch.float32, (ws.T, ws.k), dev)
+    _require(dy, "dy", torch.bfloat16, (ws.T, ws.H), dev)
+    _check_weights(ws, weights, "bwd")
     _check(mok_backward(ws.config.c(), _shape(ws.T, ws.H, ws.I, ws.E, ws.k), _ptr(schedule),
-                        _ptr(ws.buffer), ws.buffer.numel(), _ptr(x), _ptr(topk_w), weights,
+                        schedule.numel(), _ptr(ws.buffer), ws.buffer.numel(), _ptr(x), _ptr(topk_w), weights,
                         _ptr(fwd_ctx), fwd_ctx.numel(), _ptr(dy), _ptr(grads["dx"]),
                         _ptr(grads["dw_gate"]), _ptr(grads["dw_up"]), _ptr(grads["dw_down"]),
                         _ptr(grads["dtopk_w"]), _stream()), "mok_backward")
@@ -346,6 +428,9 @@ def mxfp8_quantize(src, src_is_k_by_rows: bool):
     """src bf16 [B, rows, K] (or [B, K, rows] when src_is_k_by_rows). Returns
     (elems uint8 [B, rows, K], scales uint8 [B, rows, K/32])."""
     import torch
+    if src.dim() != 3:
+        raise ValueError(f"src: expected [B, rows, K] or [B, K, rows], got shape {tuple(src.shape)}")
+    _require(src, "src", torch.bfloat16, tuple(src.shape))
     B = src.shape[0]
     rows, K = (src.shape[2], src.shape[1]) if src_is_k_by_rows else (src.shape[1], src.shape[2])
     elems = torch.empty((B, rows, K), dtype=torch.uint8, device=src.device)
@@ -361,6 +446,7 @@ def route(logits, k: int):
     renormalised over the chosen k."""
     import torch
     T, E = logits.shape
+    _require(logits, "logits", torch.float32, (T, E))
     ids = torch.empty((T, k), dtype=torch.int32, device=logits.device)
     w = torch.empty((T, k), dtype=torch.float32, device=logits.device)
     _check(mok_route(_ptr(logits), T, E, k, _ptr(ids), _ptr(w), _stream()), "mok_route")
@@ -371,6 +457,9 @@ def route_backward(topk_ids, topk_w, dtopk_w, E: int):
     """Logit gradient fp32 [T, E] of route() for the upstream gradient dtopk_w [T, k]."""
     import torch
     T, k = topk_ids.shape
+    _require(topk_ids, "topk_ids", torch.int32, (T, k))
+    _require(topk_w, "topk_w", torch.float32, (T, k), topk_ids.device)
+    _require(dtopk_w, "dtopk_w", torch.float32, (T, k), topk_ids.device)
     dl = torch.empty((T, E), dtype=torch.float32, device=topk_ids.device)
     _check(mok_route_backward(_ptr(topk_ids), _ptr(topk_w), _ptr(dtopk_w), T, E, k, _ptr(dl), _stream()),
            "mok_route_backward")

@@ -25,6 +25,7 @@ mok_status mok_config_default(mok_config *cfg) {
     cfg->ring_bytes = int64_t(256) << 20;
     cfg->capacity_multiplier = 1.0f;
     cfg->debug_flags = 0;
+    cfg->persistent_workgroups = 0;
     return MOK_OK;
 }
 
@@ -113,23 +114,26 @@ static mok_status check_weights(const Plan &p, const mok_weights *w) {
     return MOK_OK;
 }
 
-mok_status mok_forward(const mok_config *cfg, const mok_shape *shape, const void *schedule, void *workspace,
-                       size_t workspace_bytes, const void *x, const float *topk_w, const mok_weights *w,
-                       void *out, void *fwd_ctx, size_t fwd_ctx_bytes, void *stream) {
+mok_status mok_forward(const mok_config *cfg, const mok_shape *shape, const void *schedule, size_t schedule_bytes,
+                       void *workspace, size_t workspace_bytes, const void *x, const float *topk_w,
+                       const mok_weights *w, void *out, void *fwd_ctx, size_t fwd_ctx_bytes, void *stream) {
     Plan p;
     mok_status s = make_plan(cfg, shape, &p);
     if (s != MOK_OK) return s;
     if ((s = check_weights(p, w)) != MOK_OK && !(p.debug & MOK_DEBUG_IDENTITY_EXPERT)) return s;
     if (!dev_ok(schedule) || !dev_ok(workspace) || !dev_ok(fwd_ctx)) return MOK_ERROR_INVALID_VALUE;
     if (p.R > 0 && (!dev_ok(x) || !dev_ok(topk_w) || !dev_ok(out))) return MOK_ERROR_INVALID_VALUE;
-    if (workspace_bytes < p.w_total || fwd_ctx_bytes < p.c_total) return MOK_ERROR_BUFFER_TOO_SMALL;
+    if (schedule_bytes < p.s_total || workspace_bytes < p.w_total || fwd_ctx_bytes < p.c_total)
+        return MOK_ERROR_BUFFER_TOO_SMALL;
     (void)hipGetLastError();
+    if ((s = launch_schedule_check(p, schedule, static_cast<hipStream_t>(stream))) != MOK_OK) return s;
     return launch_forward(p, schedule, workspace, static_cast<const uint16_t *>(x), topk_w, *w,
                           static_cast<uint16_t *>(out), fwd_ctx, static_cast<hipStream_t>(stream));
 }
 
-mok_status mok_backward(const mok_config *cfg, const mok_shape *shape, const void *schedule, void *workspace,
-                        size_t workspace_bytes, const void *x, const float *topk_w, const mok_weights *w,
+mok_status mok_backward(const mok_config *cfg, const mok_shape *shape, const void *schedule, size_t schedule_bytes,
+                        void *workspace, size_t workspace_bytes, const void *x, const float *topk_w,
+                        const mok_weights *w,
                         const void *fwd_ctx, size_t fwd_ctx_bytes, const void *dy, void *dx, void *dw_gate,
                         void *dw_up, void *dw_down, float *dtopk_w, void *stream) {
     Plan p;
@@ -141,8 +145,10 @@ mok_status mok_backward(const mok_config *cfg, const mok_shape *shape, const voi
     if (!dev_ok(dw_gate) || !dev_ok(dw_up) || !dev_ok(dw_down)) return MOK_ERROR_INVALID_VALUE;
     if (p.R > 0 && (!dev_ok(x) || !dev_ok(topk_w) || !dev_ok(dy) || !dev_ok(dx) || !dev_ok(dtopk_w)))
         return MOK_ERROR_INVALID_VALUE;
-    if (workspace_bytes < p.w_total || fwd_ctx_bytes < p.c_total) return MOK_ERROR_BUFFER_TOO_SMALL;
+    if (schedule_bytes < p.s_total || workspace_bytes < p.w_total || fwd_ctx_bytes < p.c_total)
+        return MOK_ERROR_BUFFER_TOO_SMALL;
     (void)hipGetLastError();
+    if ((s = launch_schedule_check(p, schedule, static_cast<hipStream_t>(stream))) != MOK_OK) return s;
     return launch_backward(p, schedule, workspace, static_cast<const uint16_t *>(x), topk_w, *w, fwd_ctx,
                            static_cast<const uint16_t *>(dy), static_cast<uint16_t *>(dx),
                            static_cast<uint16_t *>(dw_gate), static_cast<uint16_t *>(dw_up),

@@ -12,6 +12,10 @@ mok_status check_hip(hipError_t err, const char *where);
 
 mok_status launch_build_schedule(const Plan &p, const int32_t *ids, void *schedule, hipStream_t st);
 
+// Enqueues the fingerprint check of a schedule table against the plan of the
+// call that is about to read it (sets MOK_SCHEDULE_MISMATCH on a mismatch).
+mok_status launch_schedule_check(const Plan &p, const void *schedule, hipStream_t st);
+
 mok_status launch_forward(const Plan &p, const void *schedule, void *workspace, const uint16_t *x,
                           const float *topk_w, const mok_weights &w, uint16_t *out, void *fwd_ctx,
                           hipStream_t st);

@@ -625,7 +625,8 @@ hipError_t fwd_round_gemms(const Plan &p, const GateUpArgs &ga, const DownArgs &
         const hipError_t e = launch_gemm<GateUp<C>>("gateup", seg_grid(ga.n_tiles, mt), ga, st);
         return e != hipSuccess ? e : launch_gemm<Down<C>>("down", seg_grid(da.n_tiles, mt), da, st);
     }
-    return launch_pair<GateUp<C>, Down<C>, C::LDS_BYTES>("fwd_gemms", ga, da, sync, p.max_mtiles, spin_limit(p), st);
+    return launch_pair<GateUp<C>, Down<C>, C::LDS_BYTES>("fwd_gemms", ga, da, sync, p.max_mtiles, spin_limit(p),
+                                                         persistent_grid(p), st);
 }
 
 // The two grouped GEMMs of one backward ring round (dA, then dX).
@@ -636,7 +637,8 @@ hipError_t bwd_round_gemms(const Plan &p, const DAArgs &aa, const DXArgs &xa, in
         const hipError_t e = launch_gemm<DA<C>>("dA", seg_grid(aa.n_tiles, mt), aa, st);
         return e != hipSuccess ? e : launch_gemm<DX<C>>("dX", seg_grid(xa.n_tiles, mt), xa, st);
     }
-    return launch_pair<DA<C>, DX<C>, C::LDS_BYTES>("bwd_gemms", aa, xa, sync, p.max_mtiles, spin_limit(p), st);
+    return launch_pair<DA<C>, DX<C>, C::LDS_BYTES>("bwd_gemms", aa, xa, sync, p.max_mtiles, spin_limit(p),
+                                                   persistent_grid(p), st);
 }
 
 // The weight-gradient GEMMs (dW_gate | dW_up, then dW_down), in the tile family C.

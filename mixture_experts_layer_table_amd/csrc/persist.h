@@ -406,6 +406,9 @@ inline int device_cu_count() {
     return n;
 }
 
+// Workgroups of a persistent launch: the plan's cap, else one per compute unit.
+inline unsigned persistent_grid(const Plan &p) { return (unsigned)(p.grid > 0 ? p.grid : device_cu_count()); }
+
 // Sync-area layout of the whole-pass kernel, in ints.
 struct PassLayout {
     int NR, S, cpm, slots, total;
@@ -446,13 +449,13 @@ hipError_t launch_pass(const char *name, const Plan &p, const GA &ga, const type
     const PassShape ps{p.G, l.S, l.NR, l.cpm, reverse};
     KernelTimer tm(name, st);
     persist_pass_kernel<GA, P1, P2, RELEASE, TILE_LDS>
-        <<<(unsigned)device_cu_count(), P1::C::NT, lds_bytes, st>>>(ga, a1, a2, s, ps);
+        <<<persistent_grid(p), P1::C::NT, lds_bytes, st>>>(ga, a1, a2, s, ps);
     return hipGetLastError();
 }
 
 template <class P1, class P2, size_t TILE_LDS>
 hipError_t launch_pair(const char *name, const typename P1::Args &a1, const typename P2::Args &a2, int *sync,
-                       int64_t max_mtiles, int spin, hipStream_t st) {
+                       int64_t max_mtiles, int spin, unsigned grid, hipStream_t st) {
     constexpr size_t lds_bytes = TILE_LDS + 64;
     static bool attr_set = false;
     if (!attr_set) {
@@ -465,7 +468,7 @@ hipError_t launch_pair(const char *name, const typename P1::Args &a1, const type
     sync_clear<<<(unsigned)std::min<int64_t>((n + 255) / 256, 1024), 256, 0, st>>>(sync, n);
     KernelTimer tm(name, st);
     persist_pair_kernel<P1, P2, TILE_LDS>
-        <<<(unsigned)device_cu_count(), P1::C::NT, lds_bytes, st>>>(a1, a2, PairSync{sync, sync + kSyncHeads, spin});
+        <<<grid, P1::C::NT, lds_bytes, st>>>(a1, a2, PairSync{sync, sync + kSyncHeads, spin});
     return hipGetLastError();
 }
 

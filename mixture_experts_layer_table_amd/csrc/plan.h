@@ -24,6 +24,7 @@ struct Plan {
     int precision = MOK_BF16;   // MOK_BF16 or MOK_MXFP8 (MOK_MXFP8_WGRAD sets MOK_MXFP8 and mx_wgrad)
     bool mx_wgrad = false;      // weight gradients on the block-scaled MFMA
     uint32_t debug = 0;
+    int grid = 0;            // persistent-kernel workgroups (0: one per compute unit)
     // derived
     int NM = 0;              // macro-batches
     int nb_full = 0;         // mini-batches in a full macro-batch
@@ -38,7 +39,10 @@ struct Plan {
     int64_t stage_rows = 0;  // rows of the per-macro-batch combine staging (k > 1)
 
     // schedule buffer (byte offsets)
-    size_t s_status = 0, s_nseg = 0, s_counts = 0, s_offsets = 0, s_mcounts = 0,
+    // layout fingerprint: a hash of every size the schedule's layout depends
+    // on, written into the table by its builder and checked by its readers
+    uint32_t fingerprint = 0;
+    size_t s_status = 0, s_nseg = 0, s_fprint = 0, s_counts = 0, s_offsets = 0, s_mcounts = 0,
            s_moffsets = 0, s_perm = 0, s_inv = 0, s_canon = 0, s_ctok = 0, s_mbstart = 0,
            s_segments = 0, s_chunk = 0, s_bound = 0, s_segfirst = 0, s_mtfirst = 0,
            s_mtiles = 0, s_total = 0;

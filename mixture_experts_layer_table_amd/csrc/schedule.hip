@@ -22,6 +22,7 @@ __global__ __launch_bounds__(kThreads) void sched_init(SchedView v) {
     if (threadIdx.x == 0) {
         *v.status = 0;
         *v.n_seg = 0;
+        *v.fprint = v.fingerprint;
     }
     // defined values for an empty call (T = 0), where the scan does not run
     for (int e = threadIdx.x; e <= v.E; e += kThreads) {
@@ -252,7 +253,23 @@ __global__ __launch_bounds__(kThreads) void sched_scatter(const int32_t *__restr
     }
 }
 
+// A reader's check of the table before anything else reads it: a table whose
+// fingerprint differs from the reader's plan (built under other knobs or
+// another shape) raises MOK_SCHEDULE_MISMATCH, and every later kernel of the
+// call exits on the status word.
+__global__ __launch_bounds__(64) void sched_check(uint32_t *status, const uint32_t *fprint, uint32_t expect) {
+    if (threadIdx.x == 0 && *fprint != expect) atomicOr(status, MOK_SCHEDULE_MISMATCH);
+}
+
 }  // namespace
+
+mok_status launch_schedule_check(const Plan &p, const void *schedule, hipStream_t st) {
+    char *b = static_cast<char *>(const_cast<void *>(schedule));
+    KernelTimer tm("sched_check", st);
+    sched_check<<<1, 64, 0, st>>>(reinterpret_cast<uint32_t *>(b + p.s_status),
+                                  reinterpret_cast<const uint32_t *>(b + p.s_fprint), p.fingerprint);
+    return check_hip(hipGetLastError(), "schedule check");
+}
 
 mok_status launch_build_schedule(const Plan &p, const int32_t *ids, void *schedule, hipStream_t st) {
     SchedView v = make_sched_view(p, schedule);

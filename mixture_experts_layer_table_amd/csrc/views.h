@@ -18,10 +18,12 @@ struct MTile {
 struct SchedView {
     uint32_t *status;
     int32_t *n_seg;
+    uint32_t *fprint;
     int32_t *counts, *offsets, *mcounts, *moffsets, *perm, *inv, *canon, *ctok, *mb_start,
         *segments, *chunk, *bound, *segfirst, *mtfirst;
     MTile *mtiles;
     int32_t R, T, k, E, MB, MT, NM, nb_full, G, cap, BM, nchunks, max_mtiles;
+    uint32_t fingerprint;   // the plan's: what sched_init writes and sched_check expects
 };
 
 inline SchedView make_sched_view(const Plan &p, void *buf) {
@@ -29,6 +31,7 @@ inline SchedView make_sched_view(const Plan &p, void *buf) {
     SchedView v;
     v.status = reinterpret_cast<uint32_t *>(b + p.s_status);
     v.n_seg = reinterpret_cast<int32_t *>(b + p.s_nseg);
+    v.fprint = reinterpret_cast<uint32_t *>(b + p.s_fprint);
     auto I32 = [&](size_t off) { return reinterpret_cast<int32_t *>(b + off); };
     v.counts = I32(p.s_counts);
     v.offsets = I32(p.s_offsets);
@@ -58,6 +61,7 @@ inline SchedView make_sched_view(const Plan &p, void *buf) {
     v.BM = p.tile.BM;
     v.nchunks = p.nchunks;
     v.max_mtiles = (int32_t)p.max_mtiles;
+    v.fingerprint = p.fingerprint;
     return v;
 }
 

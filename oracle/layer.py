@@ -216,7 +216,9 @@ def expert_wgrad_columns(xe, dye, g, Wg, Wu, Wd, cols, fq=None, wgrad_fq=None):
 
 
 def rel_frobenius(got, ref) -> float:
-    """||got - ref||_F / ||ref||_F (0 when both are exactly zero)."""
+    """||got - ref||_F / ||ref||_F (0 when both are exactly zero, infinite when
+    only ref is). The tolerance measure for floating-point outputs: one number
+    per output tensor (per expert for the weight gradients)."""
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     nr = np.linalg.norm(ref)
@@ -224,3 +226,23 @@ def rel_frobenius(got, ref) -> float:
     if nr == 0:
         return 0.0 if nd == 0 else float("inf")
     return float(nd / nr)
+
+
+def rel_rows(got, ref) -> np.ndarray:
+    """Per-row form of rel_frobenius: ||got[r] - ref[r]|| / ||ref[r]|| for every
+    row r of the leading axis (trailing axes flattened into the row); 0 where
+    both rows are exactly zero, infinite where only ref's is. A row that is
+    wrong as a whole (another row's values, zeros, a wrong expert) scores about
+    1 or more, however many correct rows surround it."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape
+    n = ref.shape[0] if ref.ndim else 1
+    g2, r2 = got.reshape(n, -1), ref.reshape(n, -1)
+    nr = np.linalg.norm(r2, axis=1)
+    nd = np.linalg.norm(g2 - r2, axis=1)
+    out = np.empty(n)
+    zero = nr == 0
+    out[~zero] = nd[~zero] / nr[~zero]
+    out[zero] = np.where(nd[zero] == 0, 0.0, np.inf)
+    return out

@@ -264,3 +264,48 @@ def small_config(name="small", *, T, H, I, E, k, minibatch_rows=32, macrobatch_t
     return LayerConfig(name, T=T, H=H, I=I, E=E, k=k, routing=routing,
                        minibatch_rows=minibatch_rows, macrobatch_tokens=macrobatch_tokens,
                        ring_bytes=ring_bytes, precision=precision, tokens_per_step=T, seed=seed)
+
+
+# ----------------------------------------------------------------------------- MXFP8-lossless inputs
+
+def lossless_mxfp8_inputs(cfg: LayerConfig) -> LayerInputs:
+    """Inputs on which every MXFP8 quantization point of the layer is exact.
+
+    Every operand the MXFP8 mode quantizes (x, dy, the three weights, and the
+    activations a and dh the layer derives from them) then holds values n * 2^p
+    with an integer 1 <= n <= 14: four significant bits at most, and a block
+    maximum whose leading digits are at most 1.75, so that scaling by the E8M0
+    block exponent never saturates past 448. The construction:
+
+      x[:, :H/2]  integers 1..14        x[:, H/2:]  +-2^(0..3)
+      W_gate[e][pg(i), i] = 32          (pg into the first half of H)
+      W_up[e][pu(i), i]   = +-2^(0..2)  (pu into the second half of H)
+      W_down[e][i, pd(i)] = +-2^(-3..0) (pd injective: one entry per row and column)
+      dy = +-2^(0..3);   gate weights 1/2 or 1
+
+    so that h_gate = 32 n >= 32 (where silu is the identity to within
+    exp(-32)), h_up and G = dy W_down^T are single terms, and a, dh, y and the
+    combine are exact in fp32 and bf16. Requires k <= 2, I <= H/2, H even.
+    Routing (ids) follows ``cfg.routing``; these are draws only, like every
+    other input here.
+    """
+    T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
+    assert k <= 2 and H % 2 == 0 and I <= H // 2
+    ids, _, logits = make_routing(cfg)
+    rng = seq(cfg.seed, STREAM_X, 1 << 20)
+    half = H // 2
+    x = np.empty((T, H), dtype=np.float32)
+    x[:, :half] = rng.integers(1, 15, size=(T, half))
+    x[:, half:] = rng.choice([-1.0, 1.0], size=(T, H - half)) * 2.0 ** rng.integers(0, 4, size=(T, H - half))
+    wg = np.zeros((E, H, I), dtype=np.float32)
+    wu = np.zeros((E, H, I), dtype=np.float32)
+    wd = np.zeros((E, I, H), dtype=np.float32)
+    cols = np.arange(I)
+    for e in range(E):
+        wg[e, rng.integers(0, half, size=I), cols] = 32.0
+        wu[e, rng.integers(half, H, size=I), cols] = rng.choice([-1.0, 1.0], size=I) * 2.0 ** rng.integers(0, 3, size=I)
+        wd[e, cols, rng.permutation(H)[:I]] = rng.choice([-1.0, 1.0], size=I) * 2.0 ** -rng.integers(0, 4, size=I)
+    dy = rng.choice([-1.0, 1.0], size=(T, H)) * 2.0 ** rng.integers(0, 4, size=(T, H))
+    w = rng.choice([0.5, 1.0], size=(T, k)).astype(np.float32)
+    b = f32_to_bf16_bits
+    return LayerInputs(cfg, ids, w, b(x), b(wg), b(wu), b(wd), b(dy.astype(np.float32)), logits)

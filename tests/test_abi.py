@@ -5,6 +5,7 @@ import os
 import re
 
 import pytest
+import torch
 
 import mixture_experts_layer_table_amd as mok
 
@@ -27,8 +28,9 @@ def test_every_declared_symbol_is_exported():
 def test_config_default():
     c = mok.mok_config()
     assert mok.mok_config_default(c) == mok.MOK_OK
-    assert (c.minibatch_rows, c.macrobatch_tokens, c.ring_bytes, c.capacity_multiplier, c.precision) == \
-        (512, 0, 256 << 20, 1.0, mok.MOK_BF16)
+    assert (c.minibatch_rows, c.macrobatch_tokens, c.ring_bytes, c.capacity_multiplier, c.precision,
+            c.persistent_workgroups) == (512, 0, 256 << 20, 1.0, mok.MOK_BF16, 0)
+    assert ctypes.sizeof(mok.mok_config) == 40
 
 
 BAD_SHAPES = [dict(T=-1), dict(H=100), dict(I=96), dict(E=0), dict(k=0), dict(k=9), dict(T=1 << 31),
@@ -47,7 +49,8 @@ def test_bad_shapes_rejected(bad):
 
 BAD_CONFIGS = [dict(minibatch_rows=8), dict(minibatch_rows=40), dict(capacity_multiplier=0.0),
                dict(capacity_multiplier=4.5), dict(precision=7), dict(ring_bytes=32 * 256),
-               dict(macrobatch_tokens=-1), dict(debug_flags=16)]
+               dict(macrobatch_tokens=-1), dict(debug_flags=16), dict(persistent_workgroups=-1),
+               dict(persistent_workgroups=65536)]
 
 
 @pytest.mark.parametrize("bad", BAD_CONFIGS)
@@ -96,7 +99,7 @@ def test_null_and_misaligned_pointers_rejected_without_device_work():
     assert mok.mok_build_schedule(c, sh, ctypes.c_void_p(0x1000), ctypes.c_void_p(0x2000), 16, None) \
         == mok.MOK_ERROR_BUFFER_TOO_SMALL
     w = mok.mok_weights()
-    assert mok.mok_forward(c, sh, None, None, 0, None, None, w, None, None, 0, None) == \
+    assert mok.mok_forward(c, sh, None, 0, None, 0, None, None, w, None, None, 0, None) == \
         mok.MOK_ERROR_INVALID_VALUE
     assert mok.mok_mxfp8_quantize(None, 1, 1, 33, 0, None, None, None) == mok.MOK_ERROR_INVALID_VALUE
     assert mok.mok_mxfp8_quantize(None, 1, 1, 32, 2, None, None, None) == mok.MOK_ERROR_INVALID_VALUE
@@ -188,3 +191,80 @@ def test_weight_structs_keep_their_tensors_alive():
     del w, w8
     gc.collect()
     assert r() is None and r2() is None
+
+
+def test_whole_pass_mode_is_switched_off():
+    # every entry point that takes a config rejects the flag before any device work
+    for prec in (mok.MOK_BF16, mok.MOK_MXFP8):
+        cfg = mok.MoKConfig(minibatch_rows=32, ring_bytes=1 << 20, precision=prec,
+                            debug_flags=mok.MOK_DEBUG_WHOLE_PASS)
+        with pytest.raises(mok.MokError) as e:
+            mok.query_sizes(cfg, 64, 256, 128, 8, 1)
+        assert e.value.status == mok.MOK_ERROR_UNSUPPORTED
+    c = mok.MoKConfig(minibatch_rows=32, ring_bytes=1 << 20, debug_flags=mok.MOK_DEBUG_WHOLE_PASS).c()
+    sh = mok.mok_shape(64, 128, 64, 8, 1)
+    p = ctypes.c_void_p(0x1000)
+    assert mok.mok_build_schedule(c, sh, p, p, 1 << 20, None) == mok.MOK_ERROR_UNSUPPORTED
+    w = mok.mok_weights(0x1000, 0x1000, 0x1000)
+    assert mok.mok_forward(c, sh, p, 1 << 30, p, 1 << 30, p, p, w, p, p, 1 << 30, None) == \
+        mok.MOK_ERROR_UNSUPPORTED
+    assert mok.mok_backward(c, sh, p, 1 << 30, p, 1 << 30, p, p, w, p, 1 << 30, p, p, p, p, p, p, None) == \
+        mok.MOK_ERROR_UNSUPPORTED
+
+
+def _cpu_workspace(I=64, **over):
+    # a workspace on the host: enough for the binding's checks, which run
+    # before any call into the library
+    c = mok.MoKConfig(minibatch_rows=32, ring_bytes=1 << 20, **over)
+    return mok.get_workspace(c, device="cpu", num_local_tokens=64, hidden_size=128, intermediate_size=I,
+                             num_experts=8, topk=2)
+
+
+def test_binding_rejects_int64_ids():
+    # int64 ids read as int32 would put every id in range and route silently wrong
+    ws = _cpu_workspace()
+    with pytest.raises(ValueError, match="dtype"):
+        mok.build_schedule(ws, torch.zeros((64, 2), dtype=torch.int64))
+    with pytest.raises(ValueError, match="shape"):
+        mok.build_schedule(ws, torch.zeros((64, 3), dtype=torch.int32))
+    with pytest.raises(ValueError, match="contiguous"):
+        mok.build_schedule(ws, torch.zeros((2, 64), dtype=torch.int32).t())
+
+
+def test_binding_rejects_wrong_outputs_and_inputs():
+    ws = _cpu_workspace()
+    sched = torch.zeros(ws.schedule_bytes, dtype=torch.uint8)
+    x = torch.zeros((64, 128), dtype=torch.bfloat16)
+    tw = torch.zeros((64, 2), dtype=torch.float32)
+    w = mok.weights_bf16(torch.zeros((8, 128, 64), dtype=torch.bfloat16),
+                         torch.zeros((8, 128, 64), dtype=torch.bfloat16),
+                         torch.zeros((8, 64, 128), dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="out: shape"):
+        mok.forward(ws, sched, x, tw, w, out=torch.zeros((63, 128), dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="x: dtype"):
+        mok.forward(ws, sched, x.float(), tw, w)
+    with pytest.raises(ValueError, match="schedule"):
+        mok.forward(ws, sched[:16], x, tw, w)
+    bad_w = mok.weights_bf16(torch.zeros((8, 64, 128), dtype=torch.bfloat16),
+                             torch.zeros((8, 128, 64), dtype=torch.bfloat16),
+                             torch.zeros((8, 64, 128), dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="w_gate: shape"):
+        mok.forward(ws, sched, x, tw, bad_w)
+    ctx = torch.zeros(ws.fwd_ctx_bytes, dtype=torch.uint8)
+    grads = dict(dx=torch.zeros((64, 128), dtype=torch.bfloat16),
+                 dw_gate=torch.zeros((8, 128, 64), dtype=torch.bfloat16),
+                 dw_up=torch.zeros((8, 128, 64), dtype=torch.bfloat16),
+                 dw_down=torch.zeros((8, 128, 64), dtype=torch.bfloat16),       # transposed: wrong
+                 dtopk_w=torch.zeros((64, 2), dtype=torch.float32))
+    with pytest.raises(ValueError, match="dw_down: shape"):
+        mok.backward(ws, sched, ctx, x, tw, w, x, grads=grads)
+
+
+def test_binding_rejects_weights_of_the_wrong_mode():
+    ws = _cpu_workspace(I=128, precision=mok.MOK_MXFP8)
+    sched = torch.zeros(ws.schedule_bytes, dtype=torch.uint8)
+    w = mok.weights_bf16(torch.zeros((8, 128, 128), dtype=torch.bfloat16),
+                         torch.zeros((8, 128, 128), dtype=torch.bfloat16),
+                         torch.zeros((8, 128, 128), dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="MXFP8 mode"):
+        mok.forward(ws, sched, torch.zeros((64, 128), dtype=torch.bfloat16), torch.zeros((64, 2)), w)

@@ -95,20 +95,46 @@ def test_bitwise_deterministic_ten_runs():
         same_bits(first, run_layer(d, knobs(cfg)))
 
 
-@pytest.mark.parametrize("name", ["ragged_k2", "k1_macro"])
-def test_knobs_do_not_change_bits(name):
+# The whole-pass mode was present in both runs that hung without a shown
+# cause; the library now rejects it (MOK_ERROR_UNSUPPORTED) and its cases stay
+# off the GPU until a cause is shown and fixed.
+WHOLE_PASS_OFF = "whole-pass mode switched off: it was present in two hangs whose cause was not shown"
+
+
+def _knob_sweep(name, overrides):
     cfg = SMALL[name]
     d = DeviceInputs(synth.make_inputs(cfg))
     base = run_layer(d, knobs(cfg))
     row = 2 * cfg.H
-    for over in (dict(minibatch_rows=16), dict(minibatch_rows=512, ring_bytes=2 * 512 * row),
-                 dict(macrobatch_tokens=0),
-                 dict(macrobatch_tokens=7), dict(ring_bytes=2 * cfg.minibatch_rows * row),
-                 dict(ring_bytes=1 << 24), dict(capacity_multiplier=4.0),
-                 dict(debug_flags=mok.MOK_DEBUG_SEPARATE_LAUNCHES),
-                 dict(debug_flags=mok.MOK_DEBUG_WHOLE_PASS), dict(debug_flags=mok.MOK_DEBUG_WHOLE_PASS, ring_bytes=2 * cfg.minibatch_rows * row)):
+    for over in overrides(cfg, row):
         print(f"[layer] knobs {name} {over}", flush=True)
         same_bits(base, run_layer(d, knobs(cfg, **over)))
+
+
+@pytest.mark.parametrize("name", ["ragged_k2", "k1_macro"])
+def test_knobs_do_not_change_bits(name):
+    _knob_sweep(name, lambda cfg, row: (
+        dict(minibatch_rows=16), dict(minibatch_rows=512, ring_bytes=2 * 512 * row),
+        dict(macrobatch_tokens=0), dict(macrobatch_tokens=7), dict(ring_bytes=2 * cfg.minibatch_rows * row),
+        dict(ring_bytes=1 << 24), dict(capacity_multiplier=4.0),
+        dict(debug_flags=mok.MOK_DEBUG_SEPARATE_LAUNCHES)))
+
+
+@pytest.mark.parametrize("name", ["ragged_k2", "k1_macro"])
+def test_persistent_grid_size_does_not_change_bits(name):
+    # race check of the persistent work queues: one workgroup runs every tile
+    # in claim order, a few contend for them, more than the compute units
+    # queue behind the resident ones; every grid gives the same bits
+    _knob_sweep(name, lambda cfg, row: tuple(dict(persistent_workgroups=n) for n in (1, 2, 3, 7, 64, 300, 1024)) +
+                (dict(persistent_workgroups=5, ring_bytes=2 * cfg.minibatch_rows * row),))
+
+
+@pytest.mark.skip(reason=WHOLE_PASS_OFF)
+@pytest.mark.parametrize("name", ["ragged_k2", "k1_macro"])
+def test_whole_pass_mode_gives_the_same_bits(name):
+    _knob_sweep(name, lambda cfg, row: (
+        dict(debug_flags=mok.MOK_DEBUG_WHOLE_PASS),
+        dict(debug_flags=mok.MOK_DEBUG_WHOLE_PASS, ring_bytes=2 * cfg.minibatch_rows * row)))
 
 
 @pytest.mark.parametrize("name", ["ragged_k2", "k1_macro"])
@@ -150,7 +176,33 @@ def test_status_flags_stop_the_layer():
     assert torch.all(out == 7.0)
 
 
-@pytest.mark.parametrize("flags", [0, mok.MOK_DEBUG_WHOLE_PASS])
+def test_schedule_built_for_other_knobs_is_refused():
+    # a table built under another capacity multiplier (or mini-batch size) has
+    # another layout: the readers' fingerprint check flags it before any work
+    cfg = SMALL["tiny"]
+    d = DeviceInputs(synth.make_inputs(cfg))
+    w = mok.weights_bf16(d.wg, d.wu, d.wd)
+    big = mok.get_workspace(knobs(cfg, capacity_multiplier=4.0), device=DEV, num_local_tokens=cfg.T,
+                            hidden_size=cfg.H, intermediate_size=cfg.I, num_experts=cfg.E, topk=cfg.k)
+    sched = mok.build_schedule(big, d.ids)
+    torch.cuda.synchronize()
+    assert status_word(sched) == 0
+    ws = mok.get_workspace(knobs(cfg), device=DEV, num_local_tokens=cfg.T, hidden_size=cfg.H,
+                           intermediate_size=cfg.I, num_experts=cfg.E, topk=cfg.k)
+    assert ws.schedule_bytes <= sched.numel()
+    out = torch.full((cfg.T, cfg.H), 7.0, dtype=torch.bfloat16, device=DEV)
+    mok.forward(ws, sched, d.x, d.w, w, out=out)
+    torch.cuda.synchronize()
+    assert status_word(sched) == mok.MOK_SCHEDULE_MISMATCH
+    assert torch.all(out == 7.0)
+    # the matching reader runs normally on a fresh table
+    sched2 = mok.build_schedule(big, d.ids)
+    mok.forward(big, sched2, d.x, d.w, w, out=out)
+    torch.cuda.synchronize()
+    assert status_word(sched2) == 0 and not torch.all(out == 7.0)
+
+
+@pytest.mark.parametrize("flags", [0, pytest.param(mok.MOK_DEBUG_WHOLE_PASS, marks=pytest.mark.skip(reason=WHOLE_PASS_OFF))])
 def test_forced_stall_ends_the_call(flags):
     # every in-kernel wait gives up at once: the launch must end, flag the
     # stall, and leave the outputs that depend on the waits unwritten

@@ -62,9 +62,21 @@ def test_bitwise_deterministic_and_knob_invariant(name):
         same_bits(first, run_layer(d, knobs(cfg)))
     for over in (dict(minibatch_rows=16), dict(minibatch_rows=96, ring_bytes=2 * 96 * row),
                  dict(macrobatch_tokens=0), dict(ring_bytes=1 << 22), dict(capacity_multiplier=2.0),
-                 dict(debug_flags=mok.MOK_DEBUG_SEPARATE_LAUNCHES),
-                 dict(debug_flags=mok.MOK_DEBUG_WHOLE_PASS), dict(debug_flags=mok.MOK_DEBUG_WHOLE_PASS, ring_bytes=2 * cfg.minibatch_rows * row)):
+                 dict(debug_flags=mok.MOK_DEBUG_SEPARATE_LAUNCHES)):
         print(f"[mxfp8 layer] knobs {name} {over}", flush=True)
+        same_bits(first, run_layer(d, knobs(cfg, **over)))
+
+
+@pytest.mark.skip(reason="the whole-pass mode is switched off (MOK_ERROR_UNSUPPORTED): it was present in two "
+                         "hangs whose cause was not shown")
+@pytest.mark.parametrize("name", ["mx_k2_ragged", "mx_k1_macro"])
+def test_whole_pass_flag_in_mxfp8_mode(name):
+    cfg = SMALL[name]
+    row = cfg.H + cfg.H // 32
+    d = DeviceInputs(synth.make_inputs(cfg))
+    first = run_layer(d, knobs(cfg))
+    for over in (dict(debug_flags=mok.MOK_DEBUG_WHOLE_PASS),
+                 dict(debug_flags=mok.MOK_DEBUG_WHOLE_PASS, ring_bytes=2 * cfg.minibatch_rows * row)):
         same_bits(first, run_layer(d, knobs(cfg, **over)))
 
 
@@ -113,3 +125,30 @@ def test_wgrad_empty_call():
     for n in ("dw_gate", "dw_up", "dw_down"):
         assert not res[n].float().abs().sum().item()
 
+
+
+# ----------------------------------------------------------------------------- lossless inputs
+
+LOSSLESS = [_mx("ll_k1", T=160, H=256, I=128, E=3, k=1, routing="zipf", minibatch_rows=32),
+            _mx("ll_k2", T=96, H=384, I=128, E=4, k=2, minibatch_rows=48, macrobatch_tokens=40)]
+
+
+@pytest.mark.parametrize("cfg", LOSSLESS, ids=lambda c: c.name)
+def test_lossless_inputs_mxfp8_matches_bf16(cfg):
+    """On inputs whose every quantization point is exact (integers times powers
+    of two; synth.lossless_mxfp8_inputs), the MXFP8 path must give the BF16
+    path's results (BF16 tolerance), in both MXFP8 modes, and the BF16 path
+    must match the oracle."""
+    inp = synth.lossless_mxfp8_inputs(cfg)
+    d = DeviceInputs(inp)
+    bf = run_layer(d, knobs(cfg, precision=mok.MOK_BF16))
+    assert status_word(bf["schedule"]) == 0
+    compare_full(bf, oracle_full(inp), cfg.E)
+    ref = {n: host_f64(bf[n]) for n in ("out", "dx", "dw_gate", "dw_up", "dw_down", "dtopk_w")}
+    for prec in (mok.MOK_MXFP8, mok.MOK_MXFP8_WGRAD):
+        mx = run_layer(d, knobs(cfg, precision=prec))
+        assert status_word(mx["schedule"]) == 0
+        errs = compare_full(mx, ref, cfg.E)             # against the BF16 path, at the BF16 tolerance
+        exact = [n for n in ref if torch.equal(mx[n].view(torch.uint8), bf[n].view(torch.uint8))]
+        print(f"[mxfp8 lossless] {cfg.name} precision {prec}: worst {max(errs.values()):.2e}; "
+              f"bit-identical to BF16: {exact}", flush=True)
