@@ -54,7 +54,6 @@ def flops_per_row(H, I):
     """Algorithmic flops per routed row, per kernel (recompute and padding not counted)."""
     return dict(gateup=4 * H * I, down=2 * H * I, dA=2 * H * I, dX=4 * H * I,
                 fwd_gemms=6 * H * I, bwd_gemms=6 * H * I,           # persistent gate/up + down, dA + dX
-                fwd_pass=6 * H * I, bwd_pass=6 * H * I,             # whole-pass persistent (gather + both GEMMs)
                 wgrad_gate_up=4 * H * I, wgrad_down=2 * H * I)
 
 
@@ -261,8 +260,6 @@ def main():
                     help="override the workload's mini-batch size (results do not depend on it)")
     ap.add_argument("--separate-launches", action="store_true",
                     help="one launch per grouped GEMM instead of the persistent pair kernels (per-GEMM timing)")
-    ap.add_argument("--whole-pass", action="store_true",
-                    help="k == 1: one persistent launch per pass with the in-kernel ring protocol")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="instead of the layer, run a plain device-to-device copy of this many MiB "
                          "(calibrates the HBM byte counters against a kernel of known traffic)")
@@ -334,8 +331,7 @@ def main():
     config = mok.MoKConfig(minibatch_rows=cfg.minibatch_rows, macrobatch_tokens=cfg.macrobatch_tokens,
                            ring_bytes=cfg.ring_bytes,
                            precision=(mok.MOK_MXFP8_WGRAD if args.mx_wgrad else mok.MOK_MXFP8) if mx else mok.MOK_BF16,
-                           debug_flags=(mok.MOK_DEBUG_SEPARATE_LAUNCHES if args.separate_launches else 0)
-                           | (mok.MOK_DEBUG_WHOLE_PASS if args.whole_pass else 0))
+                           debug_flags=mok.MOK_DEBUG_SEPARATE_LAUNCHES if args.separate_launches else 0)
     n_cu = torch.cuda.get_device_properties(0).multi_processor_count
     if args.autosize:
         config = mok.autosize_config(config, cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, n_cu)
@@ -396,7 +392,7 @@ def main():
             by = (2 * R * H + 2 * cfg.T * H + 8 * R) * nprof / launches
             entry["gbs"] = round(by / (avg * 1e-3) / 1e9, 1)
         kernels[name] = entry
-    fp8_kernels = ("gateup", "down", "dA", "dX", "fwd_gemms", "bwd_gemms", "fwd_pass", "bwd_pass") if mx else ()
+    fp8_kernels = ("gateup", "down", "dA", "dX", "fwd_gemms", "bwd_gemms") if mx else ()
     if mx and args.mx_wgrad:
         fp8_kernels += ("wgrad_gate_up", "wgrad_down")
     for n in kernels:
@@ -412,7 +408,10 @@ def main():
                     frac=round(ach / dpeak, 4),
                     traffic=read_traffic(args.workload, dominant),
                     flops_per_launch=fpr[dominant] * R * nprof / ktimes[dominant][0],
-                    avg_launch_ms=dk["avg_ms"])
+                    avg_launch_ms=dk["avg_ms"],
+                    timing_source=f"HIP events the library records around each launch on the launch's own "
+                                  f"stream, over {nprof} steps after the timed region (the rocprofv3 kernel "
+                                  f"trace of the same command is the cross-check)")
 
     total_flops = 18 * R * H * I
     # time at the MFMA peaks: fwd + dA + dX (12 RHI) on the fp8 peak in MXFP8 mode, the rest bf16

@@ -152,3 +152,5 @@ def test_lossless_inputs_mxfp8_matches_bf16(cfg):
         exact = [n for n in ref if torch.equal(mx[n].view(torch.uint8), bf[n].view(torch.uint8))]
         print(f"[mxfp8 lossless] {cfg.name} precision {prec}: worst {max(errs.values()):.2e}; "
               f"bit-identical to BF16: {exact}", flush=True)
+        # every value on the path is exact in both modes, so the bits agree too
+        assert sorted(exact) == sorted(ref), f"not bit-identical: {sorted(set(ref) - set(exact))}"
