@@ -273,6 +273,28 @@ mok_status mok_backward(const mok_config *cfg, const mok_shape *shape,
                         float *dtopk_w, void *stream);
 
 /*
+ * mok_forward without a workspace argument: the forward pass's scratch (ring,
+ * a-ring, combine staging, work-queue counters) lives in a static device array
+ * of MOK_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held until the
+ * process ends. For callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * The call itself allocates nothing (no hipMalloc, hipFree or allocating
+ * library routine); its first call on a device looks up that device's copy
+ * of the array. Arguments and results are mok_forward's, bit for bit.
+ * A layer whose forward needs more scratch than the array holds (about
+ * ring_bytes + ring_bytes * I / H + the k > 1 combine staging) returns
+ * MOK_ERROR_BUFFER_TOO_SMALL, with the sizes in mok_last_error(); a smaller
+ * ring_bytes knob changes no output bit. Every call on one GPU shares that
+ * GPU's array and leaves its contents behind: calls that overlap on one GPU
+ * (concurrent streams or threads) race and must be serialised by the caller.
+ */
+#define MOK_NOALLOC_SCRATCH_BYTES (64u << 20)
+mok_status mok_forward_noalloc(const mok_config *cfg, const mok_shape *shape,
+                               const void *schedule, size_t schedule_bytes,
+                               const void *x, const float *topk_w, const mok_weights *w,
+                               void *out, void *fwd_ctx, size_t fwd_ctx_bytes, void *stream);
+
+/*
  * MXFP8 quantization ("Mixture-of-Kittens (MoK)" project summary, Key-concepts
  * table: weights are pre-quantized before the kernel; block format: OCP MX
  * v1.0 MXFP8). For each run of 32 contiguous values along K:

@@ -42,7 +42,8 @@ MOK_DEBUG_IDENTITY_EXPERT, MOK_DEBUG_SEPARATE_LAUNCHES, MOK_DEBUG_WHOLE_PASS, MO
 EXPORTS = ("mok_config_default", "mok_config_autosize", "mok_query_sizes", "mok_schedule_layout_query",
            "mok_build_schedule", "mok_forward", "mok_backward", "mok_mxfp8_quantize", "mok_route",
            "mok_route_backward", "mok_status_string", "mok_kernel_timing_enable", "mok_kernel_timing_read",
-           "mok_last_error")
+           "mok_last_error", "mok_forward_noalloc")
+MOK_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class mok_config(ctypes.Structure):
@@ -91,6 +92,8 @@ _sigs = {
     "mok_backward": [ctypes.POINTER(mok_config), ctypes.POINTER(mok_shape), _P, ctypes.c_size_t, _P,
                      ctypes.c_size_t, _P, _P, ctypes.POINTER(mok_weights), _P, ctypes.c_size_t, _P, _P, _P,
                      _P, _P, _P, _P],
+    "mok_forward_noalloc": [ctypes.POINTER(mok_config), ctypes.POINTER(mok_shape), _P, ctypes.c_size_t, _P, _P,
+                            ctypes.POINTER(mok_weights), _P, _P, ctypes.c_size_t, _P],
     "mok_mxfp8_quantize": [_P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
                            _P, _P, _P],
     "mok_route": [_P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _P, _P, _P],
@@ -163,6 +166,12 @@ def mok_backward(cfg, shape, schedule, schedule_bytes, workspace, workspace_byte
     return _lib.mok_backward(ctypes.byref(cfg), ctypes.byref(shape), schedule, schedule_bytes, workspace,
                              workspace_bytes, x, topk_w, ctypes.byref(weights), fwd_ctx, fwd_ctx_bytes,
                              dy, dx, dw_gate, dw_up, dw_down, dtopk_w, stream)
+
+
+def mok_forward_noalloc(cfg, shape, schedule, schedule_bytes, x, topk_w, weights, out, fwd_ctx, fwd_ctx_bytes,
+                        stream):
+    return _lib.mok_forward_noalloc(ctypes.byref(cfg), ctypes.byref(shape), schedule, schedule_bytes, x, topk_w,
+                                    ctypes.byref(weights), out, fwd_ctx, fwd_ctx_bytes, stream)
 
 
 def mok_mxfp8_quantize(src, batch, rows, K, src_is_k_by_rows, elems, scales, stream):
@@ -396,6 +405,24 @@ def forward(ws: Workspace, schedule, x, topk_w, weights: mok_weights, out=None, 
     _check(mok_forward(ws.config.c(), _shape(ws.T, ws.H, ws.I, ws.E, ws.k), _ptr(schedule),
                        schedule.numel(), _ptr(ws.buffer), ws.buffer.numel(), _ptr(x), _ptr(topk_w), weights, _ptr(out),
                        _ptr(fwd_ctx), fwd_ctx.numel(), _stream()), "mok_forward")
+    return out, fwd_ctx
+
+
+def forward_noalloc(ws: Workspace, schedule, x, topk_w, weights: mok_weights, out, fwd_ctx):
+    """forward() through mok_forward_noalloc: the library's static scratch
+    instead of ws.buffer (ws supplies the config and shape only). out and
+    fwd_ctx are caller-given; nothing is allocated here or in the call."""
+    import torch
+    dev = ws.buffer.device
+    _require_bytes(schedule, "schedule", ws.schedule_bytes, dev)
+    _require(x, "x", torch.bfloat16, (ws.T, ws.H), dev)
+    _require(topk_w, "topk_w", torch.float32, (ws.T, ws.k), dev)
+    _require(out, "out", torch.bfloat16, (ws.T, ws.H), dev)
+    _require_bytes(fwd_ctx, "fwd_ctx", ws.fwd_ctx_bytes, dev)
+    _check_weights(ws, weights, "fwd")
+    _check(mok_forward_noalloc(ws.config.c(), _shape(ws.T, ws.H, ws.I, ws.E, ws.k), _ptr(schedule),
+                               schedule.numel(), _ptr(x), _ptr(topk_w), weights, _ptr(out), _ptr(fwd_ctx),
+                               fwd_ctx.numel(), _stream()), "mok_forward_noalloc")
     return out, fwd_ctx
 
 

@@ -16,7 +16,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmok.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["plan.cpp", "timing.cpp", "streams.cpp", "schedule.hip", "layer.hip", "layer_mx.hip", "mxfp8.hip", "router.hip", "api.hip"]
+SOURCES = ["plan.cpp", "timing.cpp", "streams.cpp", "schedule.hip", "layer.hip", "layer_mx.hip", "mxfp8.hip", "router.hip", "api.hip", "noalloc.hip"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
           # packed fp32 vector ops stay off (v_pk_*_f32 are not generated)
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

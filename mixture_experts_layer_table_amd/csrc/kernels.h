@@ -9,6 +9,8 @@ namespace mok {
 // Records `err` (with the call site) as the calling thread's last error when it
 // is not hipSuccess, and maps it to a status.
 mok_status check_hip(hipError_t err, const char *where);
+// Sets the calling thread's mok_last_error text.
+void set_last_error(const char *text);
 
 mok_status launch_build_schedule(const Plan &p, const int32_t *ids, void *schedule, hipStream_t st);
 

@@ -165,6 +165,21 @@ mok_status make_plan(const mok_config *cfg, const mok_shape *shape, Plan *p) {
     return MOK_OK;
 }
 
+Plan forward_only_workspace(const Plan &p, size_t *bytes) {
+    Plan q = p;
+    Carver w;
+    q.w_ring = w.take((size_t)q.n_slots * q.MB * q.ring_row_bytes);
+    q.w_aring = w.take((size_t)q.n_slots * q.MB * q.I * 2);
+    q.w_stage = w.take((size_t)q.stage_rows * q.H * 2);
+    q.w_sync = w.take(4 * (size_t)(kSyncHeads + q.max_mtiles));
+    // backward-only regions: none in this layout (a forward never touches them)
+    q.w_dh = q.w_ga = q.w_dgp = q.w_dhq = q.w_dhq_scales = 0;
+    q.w_qx = q.w_qxs = q.w_qdh = q.w_qdhs = q.w_qga = q.w_qgas = q.w_qdy = q.w_qdys = q.w_po = 0;
+    q.w_total = w.off;
+    *bytes = w.off;
+    return q;
+}
+
 void minibatch_rows(const Plan &p, int g, int64_t *q0, int64_t *q1) {
     const int m = g / p.nb_full, b = g % p.nb_full;
     const int64_t t0 = (int64_t)m * p.MT;

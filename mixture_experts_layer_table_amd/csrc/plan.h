@@ -65,6 +65,11 @@ struct Plan {
 
 mok_status make_plan(const mok_config *cfg, const mok_shape *shape, Plan *p);
 
+// The forward pass reads and writes only the ring, the a-ring, the combine
+// staging and the persistent queues' counters of the workspace. Returns a copy
+// of p whose workspace holds just those, packed from offset 0, and its size.
+Plan forward_only_workspace(const Plan &p, size_t *bytes);
+
 // Rows [q0, q1) of mini-batch g: host-computable (depends on sizes only).
 void minibatch_rows(const Plan &p, int g, int64_t *q0, int64_t *q1);
 // Macro-batch of mini-batch g and the first mini-batch of macro-batch m.

@@ -45,6 +45,8 @@ namespace {
 thread_local char g_last_error[256] = "";
 }
 
+void set_last_error(const char *text) { std::snprintf(g_last_error, sizeof(g_last_error), "%s", text); }
+
 mok_status check_hip(hipError_t err, const char *where) {
     if (err == hipSuccess) return MOK_OK;
     std::snprintf(g_last_error, sizeof(g_last_error), "%s: %s (%d)", where, hipGetErrorString(err), (int)err);

@@ -268,3 +268,15 @@ def test_binding_rejects_weights_of_the_wrong_mode():
                          torch.zeros((8, 128, 128), dtype=torch.bfloat16))
     with pytest.raises(ValueError, match="MXFP8 mode"):
         mok.forward(ws, sched, torch.zeros((64, 128), dtype=torch.bfloat16), torch.zeros((64, 2)), w)
+
+
+def test_noalloc_forward_rejects_oversized_scratch_without_device_work():
+    # the EP-64 share's default 256 MiB ring needs more than the static scratch;
+    # the size check comes before any device call
+    c = mok.MoKConfig(minibatch_rows=512, ring_bytes=256 << 20).c()
+    sh = mok.mok_shape(16384, 7168, 2048, 4, 1)
+    p = ctypes.c_void_p(0x1000)
+    w = mok.mok_weights(0x1000, 0x1000, 0x1000)
+    assert mok.mok_forward_noalloc(c, sh, p, 1 << 40, p, p, w, p, p, 1 << 40, None) == \
+        mok.MOK_ERROR_BUFFER_TOO_SMALL
+    assert "scratch" in mok.mok_last_error()
