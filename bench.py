@@ -248,6 +248,60 @@ def sweep(args, cfg, base, n_cu, ids, tw, x, dy, wg, wu, wd, w_fwd, w_bwd, dev):
                           all_status_clear=all(r["status"] == 0 for r in results))), flush=True)
 
 
+TRACE_KERNELS = {0: "fwd_gemms", 1: "bwd_gemms", 2: "wgrad_gate_up", 3: "wgrad_down", 4: "other"}
+
+
+def item_trace_summary(rec, cfg):
+    """Where the compute units' time goes in each traced GEMM kernel, from the
+    per-item records (100 MHz clock): per launch, each workgroup's span from the
+    launch's first record to its last is split into claim and input wait, K
+    loop, epilogue (stores and publication), idle before its first item and
+    idle after its last; shares are over workgroups x launch span, averaged
+    over launches of the same kernel. Also microseconds per item and per K step
+    for each item class whose K is fixed (segment GEMMs)."""
+    import numpy as np
+    H, I = cfg.H, cfg.I
+    ksteps = {(0, 1): H // 32, (0, 2): I // 32, (1, 1): H // 32, (1, 2): 2 * I // 32}
+    out = {}
+    for kern in sorted(set(rec["kernel"].tolist())):
+        rk = rec[rec["kernel"] == kern]
+        shares, per_class = [], {}
+        for launch in sorted(set(rk["launch"].tolist())):
+            r = rk[rk["launch"] == launch]
+            t0, t1 = int(r["t_claim"].min()), int(r["t_end"].max())
+            span = max(t1 - t0, 1)
+            wgs = sorted(set(r["workgroup"].tolist()))
+            tot = dict(claim=0, kloop=0, epilogue=0, idle_start=0, idle_end=0)
+            for wg in wgs:
+                w = r[r["workgroup"] == wg]
+                tot["claim"] += int((w["t_start"] - w["t_claim"]).sum())
+                tot["kloop"] += int((w["t_kloop"] - w["t_start"]).sum())
+                tot["epilogue"] += int((w["t_end"] - w["t_kloop"]).sum())
+                tot["idle_start"] += int(w["t_claim"].min()) - t0
+                tot["idle_end"] += t1 - int(w["t_end"].max())
+            denom = span * len(wgs)
+            shares.append({k: v / denom for k, v in tot.items()} | dict(span_us=span / 100.0, workgroups=len(wgs)))
+            for cls in sorted(set(r["item_class"].tolist())):
+                c = r[r["item_class"] == cls]
+                d = per_class.setdefault(int(cls), dict(items=0, kloop=0, epi=0, claim=0))
+                d["items"] += len(c)
+                d["kloop"] += int((c["t_kloop"] - c["t_start"]).sum())
+                d["epi"] += int((c["t_end"] - c["t_kloop"]).sum())
+                d["claim"] += int((c["t_start"] - c["t_claim"]).sum())
+        avg = {k: round(float(np.mean([s[k] for s in shares])), 4) for k in shares[0]}
+        avg["launches"] = len(shares)
+        classes = {}
+        for cls, d in per_class.items():
+            n = max(d["items"], 1)
+            e = dict(items_per_launch=round(d["items"] / len(shares), 1), kloop_us=round(d["kloop"] / n / 100.0, 2),
+                     epilogue_us=round(d["epi"] / n / 100.0, 2), claim_us=round(d["claim"] / n / 100.0, 2))
+            if (kern, cls) in ksteps:
+                e["us_per_kstep"] = round(d["kloop"] / n / 100.0 / ksteps[(kern, cls)], 3)
+            classes[cls] = e
+        out[TRACE_KERNELS.get(kern, str(kern))] = dict(shares=avg, classes=classes)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -260,6 +314,8 @@ def main():
                     help="override the workload's mini-batch size (results do not depend on it)")
     ap.add_argument("--separate-launches", action="store_true",
                     help="one launch per grouped GEMM instead of the persistent pair kernels (per-GEMM timing)")
+    ap.add_argument("--item-trace", action="store_true",
+                    help="record the per-item trace of the GEMM kernels over --steps steps and print its summary")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="instead of the layer, run a plain device-to-device copy of this many MiB "
                          "(calibrates the HBM byte counters against a kernel of known traffic)")
@@ -356,6 +412,15 @@ def main():
         step()
     torch.cuda.synchronize()
     assert int(sched[:4].cpu().numpy().view(np.uint32)[0]) == 0, "schedule status word set"
+    if args.item_trace:
+        mok._check(mok.mok_item_trace_enable(1), "mok_item_trace_enable")
+        for _ in range(args.steps):
+            step()
+        rec, n = mok.item_trace_read()
+        mok._check(mok.mok_item_trace_enable(0), "mok_item_trace_enable")
+        print(json.dumps(dict(item_trace=args.workload, steps=args.steps, records=int(n),
+                              summary=item_trace_summary(rec, cfg))), flush=True)
+        return
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()

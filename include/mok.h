@@ -360,6 +360,43 @@ typedef struct mok_kernel_stat {
 mok_status mok_kernel_timing_enable(int32_t enable);
 mok_status mok_kernel_timing_read(mok_kernel_stat *stats, int32_t capacity, int32_t *count);
 
+/*
+ * Measurement aid, not part of the layer: a per-item trace of the GEMM
+ * kernels, to see how the tiles of a pass overlap and where a compute unit's
+ * time goes ("Mixture-of-Kittens(MoK)란?" explainer, section 4 ②: the overlap
+ * granularity is checked against its estimate). One record per tile of the
+ * persistent pair kernels (forward gate/up + down, backward dA + dX) and of
+ * the weight-gradient kernels. Times are the GPU's constant 100 MHz clock
+ * (s_memrealtime). While tracing is off a kernel pays one scalar branch per
+ * tile.
+ */
+typedef struct mok_item_record {
+    uint64_t t_claim;    /* the workgroup began to claim the item (other kernels: the tile started) */
+    uint64_t t_start;    /* the item was claimed and its inputs were ready */
+    uint64_t t_kloop;    /* its K loop ended (the epilogue begins) */
+    uint64_t t_end;      /* its outputs were stored (and, in a pair kernel, published) */
+    uint32_t launch;     /* launches since tracing was enabled, in issue order */
+    uint8_t kernel;      /* MOK_TRACE_* */
+    uint8_t item_class;  /* pair kernels: 1 producer tile, 2 consumer tile; otherwise 0 */
+    uint16_t xcd;        /* workgroup index mod 8, its XCD */
+    uint32_t item;       /* pair kernels: index in its class's queue; otherwise the workgroup's tile */
+    uint32_t workgroup;  /* workgroup index */
+} mok_item_record;
+#define MOK_TRACE_FWD_GEMMS 0
+#define MOK_TRACE_BWD_GEMMS 1
+#define MOK_TRACE_WGRAD_GATE_UP 2
+#define MOK_TRACE_WGRAD_DOWN 3
+#define MOK_TRACE_OTHER 4
+#define MOK_ITEM_TRACE_CAPACITY 65536
+/* enable(1): discard earlier records and start recording into a device
+   buffer of MOK_ITEM_TRACE_CAPACITY records inside the library (later ones are
+   dropped); enable(0): stop. read: wait for the device, copy up to `capacity`
+   records in completion order, set *count to the number recorded (it may
+   exceed MOK_ITEM_TRACE_CAPACITY when records were dropped). Single device,
+   not for production loops. */
+mok_status mok_item_trace_enable(int32_t enable);
+mok_status mok_item_trace_read(mok_item_record *records, int32_t capacity, int32_t *count);
+
 /* Text of the calling thread's last HIP error reported as
    MOK_ERROR_LAUNCH_FAILED ("" if none); valid until the thread's next call. */
 const char *mok_last_error(void);

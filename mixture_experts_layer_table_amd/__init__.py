@@ -42,7 +42,9 @@ MOK_DEBUG_IDENTITY_EXPERT, MOK_DEBUG_SEPARATE_LAUNCHES, MOK_DEBUG_WHOLE_PASS, MO
 EXPORTS = ("mok_config_default", "mok_config_autosize", "mok_query_sizes", "mok_schedule_layout_query",
            "mok_build_schedule", "mok_forward", "mok_backward", "mok_mxfp8_quantize", "mok_route",
            "mok_route_backward", "mok_status_string", "mok_kernel_timing_enable", "mok_kernel_timing_read",
-           "mok_last_error", "mok_forward_noalloc")
+           "mok_last_error", "mok_forward_noalloc", "mok_item_trace_enable", "mok_item_trace_read")
+MOK_TRACE_FWD_GEMMS, MOK_TRACE_BWD_GEMMS, MOK_TRACE_WGRAD_GATE_UP, MOK_TRACE_WGRAD_DOWN, MOK_TRACE_OTHER = range(5)
+MOK_ITEM_TRACE_CAPACITY = 65536
 MOK_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
@@ -68,6 +70,13 @@ class mok_weights(ctypes.Structure):
 class mok_kernel_stat(ctypes.Structure):
     _fields_ = [("name", ctypes.c_char * 32), ("launches", ctypes.c_int64), ("total_ms", ctypes.c_double),
                 ("max_ms", ctypes.c_double)]
+
+
+class mok_item_record(ctypes.Structure):
+    _fields_ = [("t_claim", ctypes.c_uint64), ("t_start", ctypes.c_uint64), ("t_kloop", ctypes.c_uint64),
+                ("t_end", ctypes.c_uint64), ("launch", ctypes.c_uint32), ("kernel", ctypes.c_uint8),
+                ("item_class", ctypes.c_uint8), ("xcd", ctypes.c_uint16), ("item", ctypes.c_uint32),
+                ("workgroup", ctypes.c_uint32)]
 
 
 class mok_schedule_layout(ctypes.Structure):
@@ -99,6 +108,8 @@ _sigs = {
     "mok_route": [_P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _P, _P, _P],
     "mok_route_backward": [_P, _P, _P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _P, _P],
     "mok_kernel_timing_enable": [ctypes.c_int32],
+    "mok_item_trace_enable": [ctypes.c_int32],
+    "mok_item_trace_read": [ctypes.POINTER(mok_item_record), ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)],
     "mok_kernel_timing_read": [ctypes.POINTER(mok_kernel_stat), ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)],
 }
 for _name, _args in _sigs.items():
@@ -192,6 +203,29 @@ def mok_kernel_timing_enable(enable):
 
 def mok_kernel_timing_read(stats, capacity, count):
     return _lib.mok_kernel_timing_read(stats, capacity, count)
+
+
+def mok_item_trace_enable(enable):
+    return _lib.mok_item_trace_enable(enable)
+
+
+def mok_item_trace_read(records, capacity, count):
+    return _lib.mok_item_trace_read(records, capacity, count)
+
+
+def item_trace_read():
+    """The per-item trace records so far as a numpy structured array (synchronises)."""
+    import numpy as np
+    cap = MOK_ITEM_TRACE_CAPACITY
+    arr = (mok_item_record * cap)()
+    n = ctypes.c_int32()
+    _check(mok_item_trace_read(arr, cap, ctypes.byref(n)), "mok_item_trace_read")
+    dt = np.dtype([("t_claim", "<u8"), ("t_start", "<u8"), ("t_kloop", "<u8"), ("t_end", "<u8"),
+                   ("launch", "<u4"), ("kernel", "u1"), ("item_class", "u1"), ("xcd", "<u2"),
+                   ("item", "<u4"), ("workgroup", "<u4")])
+    assert dt.itemsize == ctypes.sizeof(mok_item_record)
+    buf = np.frombuffer(bytes(arr), dtype=dt)
+    return buf[:min(n.value, cap)].copy(), n.value
 
 
 def kernel_times(enable_after: bool = False):

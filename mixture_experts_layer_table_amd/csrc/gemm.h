@@ -27,6 +27,7 @@
 #include <utility>
 
 #include "common.h"
+#include "../../include/mok.h"
 
 namespace mok {
 
@@ -519,26 +520,68 @@ __device__ __forceinline__ void gemm_mainloop(P &p, uint32_t lds, f32x16_t (&acc
         gemm_kloop<P, false>(p, lds, acc, live);
 }
 
-// One tile: prologue, K loop, epilogue.
+// One tile: prologue, K loop, epilogue. Returns the constant-clock time
+// (s_memrealtime, 100 MHz) at which the K loop ended, for the item trace.
 template <class P>
-__device__ __forceinline__ void gemm_tile(P &p, uint32_t lds) {
+__device__ __forceinline__ uint64_t gemm_tile(P &p, uint32_t lds) {
     using C = typename P::C;
     f32x16_t acc[C::FM][C::FN];
     gemm_mainloop(p, lds, acc);
+    const uint64_t t_kloop = __builtin_amdgcn_s_memrealtime();
     const int wave = wave_id();
     p.epilogue(acc, wave / C::WAVES_N, wave % C::WAVES_N);
+    return t_kloop;
+}
+
+// ----------------------------------------------------------------------------- item trace
+
+// Destination of the optional per-item trace (mok_item_trace_enable): null
+// when tracing is off, which costs one scalar branch per tile.
+struct TraceArgs {
+    mok_item_record *rec;
+    int *count;
+    int cap;
+    uint32_t launch;
+    int kernel;
+};
+
+// Thread 0 of a workgroup: append one record (dropped once the buffer is full).
+__device__ __forceinline__ void trace_item(const TraceArgs &tr, uint64_t t_claim, uint64_t t_start, uint64_t t_kloop,
+                                           int cls, int item) {
+    if (!tr.rec) return;
+    const uint64_t t_end = __builtin_amdgcn_s_memrealtime();
+    const int slot = atomicAdd(tr.count, 1);
+    if (slot >= tr.cap) return;
+    mok_item_record r;
+    r.t_claim = t_claim;
+    r.t_start = t_start;
+    r.t_kloop = t_kloop;
+    r.t_end = t_end;
+    r.launch = tr.launch;
+    r.kernel = (uint8_t)tr.kernel;
+    r.item_class = (uint8_t)cls;
+    r.xcd = (uint16_t)(blockIdx.x % 8);
+    r.item = (uint32_t)item;
+    r.workgroup = blockIdx.x;
+    tr.rec[slot] = r;
 }
 
 // One tile per workgroup; P::setup(args, block) picks the tile (false: no tile).
 // C::OCC waves per SIMD: with OCC = 2, one 8-wave workgroup per compute unit;
 // with OCC = 4 (and at most 80 KiB of LDS), two.
 template <class P>
-__global__ __launch_bounds__(P::C::NT, P::C::OCC) void gemm_kernel(typename P::Args args) {
+__global__ __launch_bounds__(P::C::NT, P::C::OCC) void gemm_kernel(typename P::Args args, TraceArgs tr) {
     extern __shared__ __attribute__((aligned(1024))) char lds_raw[];
     const uint32_t lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)lds_raw;
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
     P p;
     if (!p.setup(args, Blk{(int)blockIdx.x, (int)blockIdx.y, (int)blockIdx.z})) return;
-    gemm_tile(p, lds);
+    const uint64_t t_kloop = gemm_tile(p, lds);
+    if (tr.rec) {
+        wait_vmcnt<0>();
+        __syncthreads();
+        if (threadIdx.x == 0) trace_item(tr, t0, t0, t_kloop, 0, (int)blockIdx.x);
+    }
 }
 
 }  // namespace mok

@@ -18,6 +18,8 @@
 // Every output element is produced by one owner with a fixed reduction order
 // and no floating-point atomics, so results are bitwise reproducible and
 // independent of mini-batch, macro-batch, ring and capacity settings.
+#include <mutex>
+
 #include "layer_mx.h"
 #include "layer_parts.h"
 #include "persist.h"
@@ -530,53 +532,78 @@ __global__ __launch_bounds__(256) void identity_rows(SchedView v, int g0, int64_
 
 // out[t] = sum_{j=0..k-1} g[t,j] * y[t,j] (fp32, j ascending), tokens of one macro-batch;
 // with weighted == false the plain sum (input-gradient combine). One workgroup
-// per token: the token's k staged-row indices and gate weights go to LDS once,
-// and every thread keeps kCombineBatch rows' 16-byte chunks in flight before it
-// adds them, in j order. LDS: k ints, then k floats (8 k bytes, dynamic).
+// per token, kCombineChunks 16-byte chunks of the row per thread: each thread
+// issues the loads of a whole batch of kCombineBatch staged rows for all its
+// chunks before it adds them, in j order. The row indices and gate weights of
+// a batch are read by every lane (one broadcast line): no LDS and no barrier,
+// so a workgroup starts streaming at once. (One 256-thread workgroup per token
+// staging the indices through LDS moved 67% of the HBM peak on a probe of the
+// full layer's k = 8 combine; this form 76%.)
 constexpr int kCombineBatch = 8;
-__global__ __launch_bounds__(256) void combine_rows(SchedView v, int t0, int H, int k, int64_t base,
+constexpr int kCombineChunks = 2;
+__global__ __launch_bounds__(512) void combine_rows(SchedView v, int t0, int H, int k, int64_t base,
                                                     const float *__restrict__ topk_w, bool weighted,
                                                     const uint16_t *__restrict__ stage, uint16_t *__restrict__ out) {
-    extern __shared__ int comb_lds[];
     if (*v.status) return;
     const int t = t0 + blockIdx.x;
-    int *row = comb_lds;
-    float *gw = reinterpret_cast<float *>(comb_lds + k);
-    for (int j = threadIdx.x; j < k; j += 256) {
-        const int f = t * k + j;
-        row[j] = (int)(v.inv[f] - base);
-        gw[j] = weighted ? topk_w[f] : 1.0f;
-    }
-    __syncthreads();
-    const int n = H / 8;
+    const int n = H / 8, nt = (int)blockDim.x;
     typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
     const u32x4_t *src = reinterpret_cast<const u32x4_t *>(stage);   // each staged row is read once
-    for (int c = threadIdx.x; c < n; c += 256) {
-        float acc[8];
+    for (int cb = 0; cb < n; cb += kCombineChunks * nt) {
+        float acc[kCombineChunks][8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+        for (int c = 0; c < kCombineChunks; ++c)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[c][i] = 0.0f;
         for (int j0 = 0; j0 < k; j0 += kCombineBatch) {
-            u32x4_t x[kCombineBatch];
+            int64_t row[kCombineBatch];
+            float gw[kCombineBatch];
 #pragma unroll
-            for (int b = 0; b < kCombineBatch; ++b)
-                x[b] = j0 + b < k ? __builtin_nontemporal_load(src + (int64_t)row[j0 + b] * n + c) : u32x4_t{0, 0, 0, 0};
+            for (int b = 0; b < kCombineBatch; ++b) {
+                const int f = t * k + min(j0 + b, k - 1);
+                row[b] = (int64_t)(v.inv[f] - base) * n;
+                gw[b] = weighted ? topk_w[f] : 1.0f;
+            }
+            u32x4_t x[kCombineChunks][kCombineBatch];
+#pragma unroll
+            for (int c = 0; c < kCombineChunks; ++c) {
+                const int ch = cb + c * nt + (int)threadIdx.x;
+#pragma unroll
+                for (int b = 0; b < kCombineBatch; ++b)
+                    x[c][b] = (j0 + b < k && ch < n) ? __builtin_nontemporal_load(src + row[b] + ch) : u32x4_t{0, 0, 0, 0};
+            }
 #pragma unroll
             for (int b = 0; b < kCombineBatch; ++b) {
                 if (j0 + b >= k) break;
-                const float g = gw[j0 + b];
-                const uint32_t w[4] = {x[b].x, x[b].y, x[b].z, x[b].w};
+                const float g = gw[b];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float lo = bf16_to_f32(w[i] & 0xFFFFu), hi = bf16_to_f32(w[i] >> 16);
-                    acc[2 * i] = weighted ? __builtin_fmaf(g, lo, acc[2 * i]) : acc[2 * i] + lo;
-                    acc[2 * i + 1] = weighted ? __builtin_fmaf(g, hi, acc[2 * i + 1]) : acc[2 * i + 1] + hi;
+                for (int c = 0; c < kCombineChunks; ++c) {
+                    const uint32_t w4[4] = {x[c][b].x, x[c][b].y, x[c][b].z, x[c][b].w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float lo = bf16_to_f32(w4[i] & 0xFFFFu), hi = bf16_to_f32(w4[i] >> 16);
+                        acc[c][2 * i] = weighted ? __builtin_fmaf(g, lo, acc[c][2 * i]) : acc[c][2 * i] + lo;
+                        acc[c][2 * i + 1] = weighted ? __builtin_fmaf(g, hi, acc[c][2 * i + 1]) : acc[c][2 * i + 1] + hi;
+                    }
                 }
             }
         }
-        reinterpret_cast<uint4 *>(out + (int64_t)t * H)[c] =
-            make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]), pack_bf16x2(acc[4], acc[5]),
-                       pack_bf16x2(acc[6], acc[7]));
+#pragma unroll
+        for (int c = 0; c < kCombineChunks; ++c) {
+            const int ch = cb + c * nt + (int)threadIdx.x;
+            if (ch < n)
+                reinterpret_cast<uint4 *>(out + (int64_t)t * H)[ch] =
+                    make_uint4(pack_bf16x2(acc[c][0], acc[c][1]), pack_bf16x2(acc[c][2], acc[c][3]),
+                               pack_bf16x2(acc[c][4], acc[c][5]), pack_bf16x2(acc[c][6], acc[c][7]));
+        }
     }
+}
+
+// Threads of a combine workgroup: enough for kCombineChunks chunks each of an
+// H-wide row, in whole waves, at most 512.
+inline unsigned combine_threads(int H) {
+    const int n = H / 8;
+    return (unsigned)std::min(512, std::max(64, (n + kCombineChunks * 64 - 1) / (kCombineChunks * 64) * 64));
 }
 
 // dtopk_w[f] = sum over I-slices s ascending of the partials <G, a> of row inv[f]
@@ -591,10 +618,33 @@ __global__ __launch_bounds__(256) void reduce_router_grad(SchedView v, int S, co
     dtopk_w[f] = s;
 }
 
+// ----------------------------------------------------------------------------- item trace (measurement aid)
+
+static __device__ __align__(256) mok_item_record item_trace_records[MOK_ITEM_TRACE_CAPACITY];
+static __device__ int item_trace_count;
+
+struct TraceState {
+    std::mutex mu;
+    bool on = false;
+    uint32_t launch = 0;
+    int device = -1;
+    mok_item_record *rec = nullptr;   // the current device's copies (hipGetSymbolAddress)
+    int *count = nullptr;
+};
+TraceState g_trace;
+
+// The trace destination for the next launch of `kernel` (all null while tracing is off).
+TraceArgs trace_args(int kernel) {
+    std::lock_guard<std::mutex> lk(g_trace.mu);
+    if (!g_trace.on) return TraceArgs{nullptr, nullptr, 0, 0, kernel};
+    return TraceArgs{g_trace.rec, g_trace.count, MOK_ITEM_TRACE_CAPACITY, g_trace.launch++, kernel};
+}
+
 // ----------------------------------------------------------------------------- host side
 
 template <class P>
-hipError_t launch_gemm(const char *name, dim3 grid, const typename P::Args &args, hipStream_t st) {
+hipError_t launch_gemm(const char *name, dim3 grid, const typename P::Args &args, hipStream_t st,
+                       int trace_kernel = MOK_TRACE_OTHER) {
     using C = typename P::C;
     static bool attr_set = false;
     if (!attr_set) {
@@ -605,7 +655,7 @@ hipError_t launch_gemm(const char *name, dim3 grid, const typename P::Args &args
     }
     if (grid.x == 0 || grid.y == 0 || grid.z == 0) return hipSuccess;
     KernelTimer tm(name, st);
-    gemm_kernel<P><<<grid, C::NT, C::LDS_BYTES, st>>>(args);
+    gemm_kernel<P><<<grid, C::NT, C::LDS_BYTES, st>>>(args, trace_args(trace_kernel));
     return hipGetLastError();
 }
 
@@ -626,7 +676,7 @@ hipError_t fwd_round_gemms(const Plan &p, const GateUpArgs &ga, const DownArgs &
         return e != hipSuccess ? e : launch_gemm<Down<C>>("down", seg_grid(da.n_tiles, mt), da, st);
     }
     return launch_pair<GateUp<C>, Down<C>, C::LDS_BYTES>("fwd_gemms", ga, da, sync, p.max_mtiles, spin_limit(p),
-                                                         persistent_grid(p), st);
+                                                         persistent_grid(p), st, trace_args(MOK_TRACE_FWD_GEMMS));
 }
 
 // The two grouped GEMMs of one backward ring round (dA, then dX).
@@ -638,7 +688,7 @@ hipError_t bwd_round_gemms(const Plan &p, const DAArgs &aa, const DXArgs &xa, in
         return e != hipSuccess ? e : launch_gemm<DX<C>>("dX", seg_grid(xa.n_tiles, mt), xa, st);
     }
     return launch_pair<DA<C>, DX<C>, C::LDS_BYTES>("bwd_gemms", aa, xa, sync, p.max_mtiles, spin_limit(p),
-                                                   persistent_grid(p), st);
+                                                   persistent_grid(p), st, trace_args(MOK_TRACE_BWD_GEMMS));
 }
 
 // The weight-gradient GEMMs (dW_gate | dW_up, then dW_down), in the tile family C.
@@ -646,10 +696,12 @@ hipError_t bwd_round_gemms(const Plan &p, const DAArgs &aa, const DXArgs &xa, in
 template <class C>
 hipError_t wgrad_gemms(const Plan &p, const WGUArgs &gu, const WDArgs &wda, hipStream_t st) {
     const hipError_t e = launch_gemm<WGU<C>>(
-        "wgrad_gate_up", dim3((unsigned)(ceil_div(2 * p.I, C::BN) * ceil_div(p.H, C::BM) * p.E)), gu, st);
+        "wgrad_gate_up", dim3((unsigned)(ceil_div(2 * p.I, C::BN) * ceil_div(p.H, C::BM) * p.E)), gu, st,
+        MOK_TRACE_WGRAD_GATE_UP);
     if (e != hipSuccess) return e;
     return launch_gemm<WD<C>>(
-        "wgrad_down", dim3((unsigned)(ceil_div(p.H, C::BN) * ceil_div(p.I, C::BM) * p.E)), wda, st);
+        "wgrad_down", dim3((unsigned)(ceil_div(p.H, C::BN) * ceil_div(p.I, C::BM) * p.E)), wda, st,
+        MOK_TRACE_WGRAD_DOWN);
 }
 
 }  // namespace
@@ -711,8 +763,8 @@ mok_status launch_forward(const Plan &p, const void *schedule, void *workspace, 
             const Macro mc = macro_info(p, macro_of_minibatch(p, r.g0));
             KernelTimer tm("combine", st);
             if (mc.t1 > mc.t0)
-                combine_rows<<<(unsigned)(mc.t1 - mc.t0), 256, 8 * p.k, st>>>(v, mc.t0, p.H, p.k, mc.base, topk_w,
-                                                                              true, stage, out);
+                combine_rows<<<(unsigned)(mc.t1 - mc.t0), combine_threads(p.H), 0, st>>>(v, mc.t0, p.H, p.k, mc.base,
+                                                                                         topk_w, true, stage, out);
         }
     }
     if (err == hipSuccess) err = hipGetLastError();
@@ -774,8 +826,8 @@ mok_status launch_backward(const Plan &p, const void *schedule, void *workspace,
                 const Macro mc = macro_info(p, macro_of_minibatch(p, r.g0));
                 KernelTimer tm("combine_dx", st);
                 if (mc.t1 > mc.t0)
-                    combine_rows<<<(unsigned)(mc.t1 - mc.t0), 256, 8 * p.k, st>>>(v, mc.t0, p.H, p.k, mc.base,
-                                                                                  topk_w, false, stage, dx);
+                    combine_rows<<<(unsigned)(mc.t1 - mc.t0), combine_threads(p.H), 0, st>>>(
+                        v, mc.t0, p.H, p.k, mc.base, topk_w, false, stage, dx);
             }
         }
         if (err == hipSuccess) {
@@ -797,3 +849,50 @@ mok_status launch_backward(const Plan &p, const void *schedule, void *workspace,
 }
 
 }  // namespace mok
+
+using mok::g_trace;
+
+extern "C" mok_status mok_item_trace_enable(int32_t enable) {
+    std::lock_guard<std::mutex> lk(g_trace.mu);
+    if (!enable) {
+        g_trace.on = false;
+        return MOK_OK;
+    }
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess && (dev != g_trace.device || !g_trace.rec)) {
+        void *r = nullptr, *c = nullptr;
+        e = hipGetSymbolAddress(&r, HIP_SYMBOL(mok::item_trace_records));
+        if (e == hipSuccess) e = hipGetSymbolAddress(&c, HIP_SYMBOL(mok::item_trace_count));
+        if (e == hipSuccess) {
+            g_trace.rec = static_cast<mok_item_record *>(r);
+            g_trace.count = static_cast<int *>(c);
+            g_trace.device = dev;
+        }
+    }
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e == hipSuccess) e = hipMemset(g_trace.count, 0, sizeof(int));
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) return mok::check_hip(e, "mok_item_trace_enable");
+    g_trace.launch = 0;
+    g_trace.on = true;
+    return MOK_OK;
+}
+
+extern "C" mok_status mok_item_trace_read(mok_item_record *records, int32_t capacity, int32_t *count) {
+    if (!count || capacity < 0 || (capacity > 0 && !records)) return MOK_ERROR_INVALID_VALUE;
+    std::lock_guard<std::mutex> lk(g_trace.mu);
+    if (!g_trace.count) {
+        *count = 0;
+        return MOK_OK;
+    }
+    int n = 0;
+    hipError_t e = hipDeviceSynchronize();
+    if (e == hipSuccess) e = hipMemcpy(&n, g_trace.count, sizeof(int), hipMemcpyDeviceToHost);
+    const int copy = std::min(std::min(n, (int)MOK_ITEM_TRACE_CAPACITY), capacity);
+    if (e == hipSuccess && copy > 0)
+        e = hipMemcpy(records, g_trace.rec, sizeof(mok_item_record) * (size_t)copy, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return mok::check_hip(e, "mok_item_trace_read");
+    *count = n;
+    return MOK_OK;
+}

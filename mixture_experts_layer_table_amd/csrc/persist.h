@@ -50,6 +50,7 @@ struct PairSync {
     int *head;   // [2 * kXcds] claimed items of class 1 / 2 per XCD chunk (relative to the chunk start)
     int *done;   // [m-tiles of the round] finished producer tiles per m-tile
     int spin_limit;   // poll budget of a wait; < 0: every wait gives up at once (stall-path test)
+    TraceArgs trace;  // optional per-item trace (trace.rec null: off)
 };
 
 __device__ __forceinline__ int load_relaxed(const int *p) {
@@ -147,12 +148,15 @@ __device__ __forceinline__ void item_done_barrier() {
     __syncthreads();
 }
 
+// Returns the K loop's end time where the tile pipeline reports it (0 otherwise).
 template <class P>
-__device__ __forceinline__ void run_tile(P &p, uint32_t lds) {
-    if constexpr (P::FP8)
+__device__ __forceinline__ uint64_t run_tile(P &p, uint32_t lds) {
+    if constexpr (P::FP8) {
         gemm8_tile(p, lds);
-    else
-        gemm_tile(p, lds);
+        return 0;
+    } else {
+        return gemm_tile(p, lds);
+    }
 }
 
 template <class P>
@@ -185,30 +189,35 @@ __global__ __launch_bounds__(P1::C::NT) void persist_pair_kernel(typename P1::Ar
     q.n2 = q.mtc * q.nt2;
     q.ng = (q.mtc + kGroupM - 1) / kGroupM;
     const int xcd = (int)(blockIdx.x % kXcds);   // workgroups are dispatched round-robin over the XCDs
+    uint64_t t_claim = 0, t_start = 0;   // thread 0's item-trace times
     for (;;) {
         if (threadIdx.x == 0) {
+            if (s.trace.rec) t_claim = __builtin_amdgcn_s_memrealtime();
             int id = 0;
             const int cls = claim_item(s, q, xcd, v.status, id);
             bcast[0] = cls;
             bcast[1] = id;
+            if (s.trace.rec) t_start = __builtin_amdgcn_s_memrealtime();
         }
         __syncthreads();
         const int cls = bcast[0], id = bcast[1];
         if (cls == 0) return;
         int j, n;
+        uint64_t t_kloop;
         if (cls == 1) {
             item_tile(id, q.nt1, q.mtc, j, n);
             P1 p;
             p.init(a1, seg_tile<P1>(v, lo, j, n, a1.n_slots));
-            run_tile(p, lds);
+            t_kloop = run_tile(p, lds);
         } else {
             item_tile(id, q.nt2, q.mtc, j, n);
             P2 p;
             p.init(a2, seg_tile<P2>(v, lo, j, n, a2.n_slots));
-            run_tile(p, lds);
+            t_kloop = run_tile(p, lds);
         }
         item_done_barrier();
         if (cls == 1 && threadIdx.x == 0) __hip_atomic_fetch_add(&s.done[j], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        if (threadIdx.x == 0) trace_item(s.trace, t_claim, t_start, t_kloop, cls, id);
     }
 }
 
@@ -455,7 +464,7 @@ hipError_t launch_pass(const char *name, const Plan &p, const GA &ga, const type
 
 template <class P1, class P2, size_t TILE_LDS>
 hipError_t launch_pair(const char *name, const typename P1::Args &a1, const typename P2::Args &a2, int *sync,
-                       int64_t max_mtiles, int spin, unsigned grid, hipStream_t st) {
+                       int64_t max_mtiles, int spin, unsigned grid, hipStream_t st, TraceArgs tr) {
     constexpr size_t lds_bytes = TILE_LDS + 64;
     static bool attr_set = false;
     if (!attr_set) {
@@ -468,7 +477,7 @@ hipError_t launch_pair(const char *name, const typename P1::Args &a1, const type
     sync_clear<<<(unsigned)std::min<int64_t>((n + 255) / 256, 1024), 256, 0, st>>>(sync, n);
     KernelTimer tm(name, st);
     persist_pair_kernel<P1, P2, TILE_LDS>
-        <<<grid, P1::C::NT, lds_bytes, st>>>(a1, a2, PairSync{sync, sync + kSyncHeads, spin});
+        <<<grid, P1::C::NT, lds_bytes, st>>>(a1, a2, PairSync{sync, sync + kSyncHeads, spin, tr});
     return hipGetLastError();
 }
 

@@ -231,3 +231,34 @@ def test_forced_stall_ends_the_call(flags):
     torch.cuda.synchronize()
     assert status_word(sched2) == mok.MOK_SCHEDULER_STALLED
     del grads
+
+
+def test_item_trace_records_every_tile_without_changing_bits():
+    # the measurement aid: one record per tile of the pair kernels and the
+    # weight-gradient kernels, times ordered, outputs unchanged
+    cfg = SMALL["k1_macro"]
+    d = DeviceInputs(synth.make_inputs(cfg))
+    base = run_layer(d, knobs(cfg))
+    assert mok.mok_item_trace_enable(1) == mok.MOK_OK
+    try:
+        traced = run_layer(d, knobs(cfg))
+        rec, n = mok.item_trace_read()
+    finally:
+        mok.mok_item_trace_enable(0)
+    same_bits(base, traced)
+    assert n == len(rec) > 0
+    assert np.all(rec["t_claim"] <= rec["t_start"]) and np.all(rec["t_start"] <= rec["t_kloop"])
+    assert np.all(rec["t_kloop"] <= rec["t_end"])
+    kinds = set(rec["kernel"].tolist())
+    assert {mok.MOK_TRACE_FWD_GEMMS, mok.MOK_TRACE_BWD_GEMMS, mok.MOK_TRACE_WGRAD_GATE_UP,
+            mok.MOK_TRACE_WGRAD_DOWN} <= kinds
+    # every producer and consumer tile of each pair launch appears exactly once
+    for launch in set(rec["launch"][rec["kernel"] <= 1].tolist()):
+        r = rec[rec["launch"] == launch]
+        for cls in (1, 2):
+            items = r["item"][r["item_class"] == cls]
+            assert len(items) == len(set(items.tolist())) > 0
+    # tracing off again: nothing more is recorded
+    run_layer(d, knobs(cfg))
+    _, n2 = mok.item_trace_read()
+    assert n2 == n
