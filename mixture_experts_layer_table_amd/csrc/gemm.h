@@ -469,7 +469,9 @@ __device__ __forceinline__ void gemm_kloop(P &p, uint32_t lds, f32x16_t (&acc)[P
         if (nk > 0) read_stage(0);
         for (int kt = 0; kt < nk; ++kt) {
             __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_setprio(1);
             mma_stage();
+            __builtin_amdgcn_s_setprio(0);
             __builtin_amdgcn_sched_barrier(0);
             if (kt + D < nk) fetch_stage(p, kt + D);
             // own loads issued so far: up to stage kt + D - 1; stage kt + 1 must have landed
@@ -490,7 +492,9 @@ __device__ __forceinline__ void gemm_kloop(P &p, uint32_t lds, f32x16_t (&acc)[P
             lds_barrier();
             __builtin_amdgcn_sched_barrier(0);
             if (kt + D + 1 < nk) fetch_stage(p, kt + D + 1);
+            __builtin_amdgcn_s_setprio(1);
             mma_stage();
+            __builtin_amdgcn_s_setprio(0);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -520,17 +524,23 @@ __device__ __forceinline__ void gemm_mainloop(P &p, uint32_t lds, f32x16_t (&acc
         gemm_kloop<P, false>(p, lds, acc, live);
 }
 
-// One tile: prologue, K loop, epilogue. Returns the constant-clock time
+// One tile: prologue, K loop, `between()` (e.g. a persistent workgroup's
+// claim of its next item), epilogue. Returns the constant-clock time
 // (s_memrealtime, 100 MHz) at which the K loop ended, for the item trace.
-template <class P>
-__device__ __forceinline__ uint64_t gemm_tile(P &p, uint32_t lds) {
+template <class P, class F>
+__device__ __forceinline__ uint64_t gemm_tile(P &p, uint32_t lds, F &&between) {
     using C = typename P::C;
     f32x16_t acc[C::FM][C::FN];
     gemm_mainloop(p, lds, acc);
     const uint64_t t_kloop = __builtin_amdgcn_s_memrealtime();
+    between();
     const int wave = wave_id();
     p.epilogue(acc, wave / C::WAVES_N, wave % C::WAVES_N);
     return t_kloop;
+}
+template <class P>
+__device__ __forceinline__ uint64_t gemm_tile(P &p, uint32_t lds) {
+    return gemm_tile(p, lds, [] {});
 }
 
 // ----------------------------------------------------------------------------- item trace

@@ -19,6 +19,7 @@
 // and no floating-point atomics, so results are bitwise reproducible and
 // independent of mini-batch, macro-batch, ring and capacity settings.
 #include <mutex>
+#include <type_traits>
 
 #include "layer_mx.h"
 #include "layer_parts.h"
@@ -387,18 +388,23 @@ struct DX {
 struct WGUArgs {
     SchedView v;
     int H, I;
-    const uint16_t *x, *dh;
+    const uint16_t *x;    // x [T][H], token order (read through the token index)
+    const uint16_t *xc;   // x rows in canonical order [R][H] (CANON), else unused
+    const uint16_t *dh;   // dh rows in canonical order
     uint16_t *dwg, *dwu;
 };
 
-template <class Cfg>
+// CANON: the x rows come from their canonical-order copy as contiguous rows;
+// otherwise they are gathered from x through the token index (ctok).
+template <class Cfg, bool CANON>
 struct WGU {
     using C = Cfg;
     using Args = WGUArgs;
     static constexpr bool X_TRANS = true, W_TRANS = true;
-    TransIdxLoader<C, C::BM> xl;   // x rows of the expert's tokens, k = canonical row
-    TransLoader<C, C::BN> wl;      // dh rows, stored in canonical order
-    static constexpr int LOADS_PER_STAGE = TransIdxLoader<C, C::BM>::IPW + TransLoader<C, C::BN>::IPW;
+    using XL = std::conditional_t<CANON, TransLoader<C, C::BM>, TransIdxLoader<C, C::BM>>;
+    XL xl;                      // x rows of the expert's tokens, k = canonical row
+    TransLoader<C, C::BN> wl;   // dh rows of the expert
+    static constexpr int LOADS_PER_STAGE = XL::IPW + TransLoader<C, C::BN>::IPW;
     int e, h0, n0, ne, off, nk;
     Args a;
     __device__ int mvalid() const { return a.H - h0; }
@@ -412,12 +418,17 @@ struct WGU {
         ne = args.v.counts[e];
         off = args.v.offsets[e];
         nk = (ne + C::BK - 1) / C::BK;
-        xl.init(args.v.ctok + off, ne, args.x, args.H, args.v.T, h0);
+        if constexpr (CANON)
+            xl.init(args.xc + (int64_t)off * args.H + h0, args.H, ne, args.H - h0);
+        else
+            xl.init(args.v.ctok + off, ne, args.x, args.H, args.v.T, h0);
         const int I2 = 2 * args.I;
         wl.init(args.dh + (int64_t)off * I2 + n0, I2, ne, I2 - n0);
         return true;
     }
-    __device__ void fetch(int kt) { xl.fetch(kt * C::BK); }
+    __device__ void fetch(int kt) {
+        if constexpr (!CANON) xl.fetch(kt * C::BK);
+    }
     __device__ void issue(int kt, uint32_t tile) {
         xl.issue(kt * C::BK, tile);
         wl.issue(kt * C::BK, tile + C::X_BYTES);
@@ -440,18 +451,21 @@ struct WGU {
 struct WDArgs {
     SchedView v;
     int H, I;
-    const uint16_t *ga, *dy;
+    const uint16_t *ga;    // g*a rows in canonical order
+    const uint16_t *dy;    // dy [T][H], token order (read through the token index)
+    const uint16_t *dyc;   // dy rows in canonical order [R][H] (CANON), else unused
     uint16_t *dwd;
 };
 
-template <class Cfg>
+template <class Cfg, bool CANON>
 struct WD {
     using C = Cfg;
     using Args = WDArgs;
     static constexpr bool X_TRANS = true, W_TRANS = true;
-    TransLoader<C, C::BM> xl;      // g*a rows, stored in canonical order
-    TransIdxLoader<C, C::BN> wl;   // dy rows of the expert's tokens
-    static constexpr int LOADS_PER_STAGE = TransLoader<C, C::BM>::IPW + TransIdxLoader<C, C::BN>::IPW;
+    using WL = std::conditional_t<CANON, TransLoader<C, C::BN>, TransIdxLoader<C, C::BN>>;
+    TransLoader<C, C::BM> xl;   // g*a rows of the expert
+    WL wl;                      // dy rows of the expert's tokens
+    static constexpr int LOADS_PER_STAGE = TransLoader<C, C::BM>::IPW + WL::IPW;
     int e, i0, n0, ne, off, nk;
     Args a;
     __device__ int mvalid() const { return a.I - i0; }
@@ -465,11 +479,16 @@ struct WD {
         ne = args.v.counts[e];
         off = args.v.offsets[e];
         nk = (ne + C::BK - 1) / C::BK;
-        wl.init(args.v.ctok + off, ne, args.dy, args.H, args.v.T, n0);
+        if constexpr (CANON)
+            wl.init(args.dyc + (int64_t)off * args.H + n0, args.H, ne, args.H - n0);
+        else
+            wl.init(args.v.ctok + off, ne, args.dy, args.H, args.v.T, n0);
         xl.init(args.ga + (int64_t)off * args.I + i0, args.I, ne, args.I - i0);
         return true;
     }
-    __device__ void fetch(int kt) { wl.fetch(kt * C::BK); }
+    __device__ void fetch(int kt) {
+        if constexpr (!CANON) wl.fetch(kt * C::BK);
+    }
     __device__ void issue(int kt, uint32_t tile) {
         xl.issue(kt * C::BK, tile);
         wl.issue(kt * C::BK, tile + C::X_BYTES);
@@ -693,13 +712,13 @@ hipError_t bwd_round_gemms(const Plan &p, const DAArgs &aa, const DXArgs &xa, in
 
 // The weight-gradient GEMMs (dW_gate | dW_up, then dW_down), in the tile family C.
 // (Running dW_down beside dW_gate | dW_up on a second stream measured no faster.)
-template <class C>
+template <class C, bool CANON>
 hipError_t wgrad_gemms(const Plan &p, const WGUArgs &gu, const WDArgs &wda, hipStream_t st) {
-    const hipError_t e = launch_gemm<WGU<C>>(
+    const hipError_t e = launch_gemm<WGU<C, CANON>>(
         "wgrad_gate_up", dim3((unsigned)(ceil_div(2 * p.I, C::BN) * ceil_div(p.H, C::BM) * p.E)), gu, st,
         MOK_TRACE_WGRAD_GATE_UP);
     if (e != hipSuccess) return e;
-    return launch_gemm<WD<C>>(
+    return launch_gemm<WD<C, CANON>>(
         "wgrad_down", dim3((unsigned)(ceil_div(p.H, C::BN) * ceil_div(p.I, C::BM) * p.E)), wda, st,
         MOK_TRACE_WGRAD_DOWN);
 }
@@ -719,6 +738,8 @@ mok_status launch_forward(const Plan &p, const void *schedule, void *workspace, 
     uint16_t *aring = reinterpret_cast<uint16_t *>(ws + p.w_aring);
     uint16_t *stage = reinterpret_cast<uint16_t *>(ws + p.w_stage);
     uint16_t *h = reinterpret_cast<uint16_t *>(static_cast<char *>(fwd_ctx) + p.c_h);
+    // x rows saved in canonical order for the weight gradients (null when the plan keeps none)
+    uint16_t *xc = p.keep_canonical ? reinterpret_cast<uint16_t *>(static_cast<char *>(fwd_ctx) + p.c_xc) : nullptr;
     int *sync = reinterpret_cast<int *>(ws + p.w_sync);
     hipError_t err = hipSuccess;
     if (whole_pass(p) && !identity) {   // one launch for the pass, ring protocol in the kernel
@@ -735,13 +756,13 @@ mok_status launch_forward(const Plan &p, const void *schedule, void *workspace, 
     for (const Round r : make_rounds(p, false)) {
         const dim3 sgrid((unsigned)ceil_div(p.MB, kRowsPerBlock), (unsigned)(r.g1 - r.g0));
         if (mx) {
-            if ((err = mx_forward_round(p, v, r.g0, r.g1, mtile_bound(p, r), x, w, ws, h, topk_w, out, stage, st)) !=
+            if ((err = mx_forward_round(p, v, r.g0, r.g1, mtile_bound(p, r), x, w, ws, h, xc, topk_w, out, stage, st)) !=
                 hipSuccess)
                 break;
         } else {
             {
             KernelTimer tm("gather", st);
-            gather_rows<<<sgrid, 256, 0, st>>>(GatherBf16{v, p.n_slots, p.MB, p.H, p.k, x, ring}, r.g0);
+            gather_rows<<<sgrid, 256, 0, st>>>(GatherBf16{v, p.n_slots, p.MB, p.H, p.k, x, ring, xc}, r.g0);
         }
         if (identity) {
             KernelTimer tm("identity", st);
@@ -784,6 +805,12 @@ mok_status launch_backward(const Plan &p, const void *schedule, void *workspace,
     uint16_t *ga = reinterpret_cast<uint16_t *>(ws + p.w_ga);
     float *dgp = reinterpret_cast<float *>(ws + p.w_dgp);
     const uint16_t *h = reinterpret_cast<const uint16_t *>(static_cast<const char *>(fwd_ctx) + p.c_h);
+    const uint16_t *xc =
+        p.keep_canonical ? reinterpret_cast<const uint16_t *>(static_cast<const char *>(fwd_ctx) + p.c_xc) : nullptr;
+    // dy rows in canonical order for the weight gradients: the ring itself
+    // when it holds them so, else a copy the dy gather writes
+    uint16_t *dyc = !p.keep_canonical ? nullptr : p.dy_in_ring ? ring : reinterpret_cast<uint16_t *>(ws + p.w_dyc);
+    uint16_t *dyc_copy = p.keep_canonical && !p.dy_in_ring ? dyc : nullptr;
     const uint16_t *wg = static_cast<const uint16_t *>(w.w_gate);
     const uint16_t *wu = static_cast<const uint16_t *>(w.w_up);
     const uint16_t *wd = static_cast<const uint16_t *>(w.w_down);
@@ -806,13 +833,13 @@ mok_status launch_backward(const Plan &p, const void *schedule, void *workspace,
         for (const Round r : make_rounds(p, true)) {
             const dim3 sgrid((unsigned)ceil_div(p.MB, kRowsPerBlock), (unsigned)(r.g1 - r.g0));
             if (mx) {
-                if ((err = mx_backward_round(p, v, r.g0, r.g1, mtile_bound(p, r), dy, w, ws, h, topk_w, dx, stage,
+                if ((err = mx_backward_round(p, v, r.g0, r.g1, mtile_bound(p, r), dy, w, ws, h, dyc_copy, topk_w, dx, stage,
                                              st)) != hipSuccess)
                     break;
             } else {
             {
                 KernelTimer tm("gather_dy", st);
-                gather_rows<<<sgrid, 256, 0, st>>>(GatherBf16{v, p.n_slots, p.MB, p.H, p.k, dy, ring}, r.g0);
+                gather_rows<<<sgrid, 256, 0, st>>>(GatherBf16{v, p.n_slots, p.MB, p.H, p.k, dy, ring, dyc_copy}, r.g0);
             }
             const int64_t mt = mtile_bound(p, r);
             const int nta = (int)ceil_div(p.I, CfgA::BN), ntx = (int)ceil_div(p.H, CfgA::BN);
@@ -840,9 +867,15 @@ mok_status launch_backward(const Plan &p, const void *schedule, void *workspace,
         const hipError_t e2 = mx_wgrad_finish(p, v, ws, wq_side, err == hipSuccess, dw_gate, dw_up, dw_down, st);
         if (err == hipSuccess) err = e2;
     } else if (err == hipSuccess) {
-        const WGUArgs gu{v, p.H, p.I, x, dh, dw_gate, dw_up};
-        const WDArgs wda{v, p.H, p.I, ga, dy, dw_down};
-        err = p.tile.BM == CfgS::BM ? wgrad_gemms<CfgW>(p, gu, wda, st) : wgrad_gemms<CfgA>(p, gu, wda, st);
+        const WGUArgs gu{v, p.H, p.I, x, xc, dh, dw_gate, dw_up};
+        const WDArgs wda{v, p.H, p.I, ga, dy, dyc, dw_down};
+        if (p.keep_canonical && (!xc || !dyc)) return MOK_ERROR_INVALID_VALUE;   // not reachable: both derive from validated buffers
+        if (p.keep_canonical)
+            err = p.tile.BM == CfgS::BM ? wgrad_gemms<CfgW, true>(p, gu, wda, st)
+                                        : wgrad_gemms<CfgA, true>(p, gu, wda, st);
+        else
+            err = p.tile.BM == CfgS::BM ? wgrad_gemms<CfgW, false>(p, gu, wda, st)
+                                        : wgrad_gemms<CfgA, false>(p, gu, wda, st);
     }
     if (err == hipSuccess) err = hipGetLastError();
     return check_hip(err, "mok_backward");

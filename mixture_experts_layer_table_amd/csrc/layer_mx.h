@@ -9,17 +9,19 @@
 
 namespace mok {
 
-// Forward round g0 .. g1-1: gather + quantize x rows into the ring, gate/up
+// Forward round g0 .. g1-1: gather + quantize x rows into the ring (and, when
+// xc is not null, the bf16 rows at their canonical positions in xc), gate/up
 // GEMM (h -> fwd_ctx, a quantized along I -> the a-ring), down GEMM.
 hipError_t mx_forward_round(const Plan &p, const SchedView &v, int g0, int g1, int64_t mt_bound,
-                            const uint16_t *x, const mok_weights &w, char *ws, uint16_t *h, const float *topk_w,
-                            uint16_t *out, uint16_t *stage, hipStream_t st);
+                            const uint16_t *x, const mok_weights &w, char *ws, uint16_t *h, uint16_t *xc,
+                            const float *topk_w, uint16_t *out, uint16_t *stage, hipStream_t st);
 
-// Backward round g0 .. g1-1: gather + quantize dy rows, dA GEMM with the
-// SwiGLU backward (dh in bf16 and quantized along I), dX GEMM.
+// Backward round g0 .. g1-1: gather + quantize dy rows (and the bf16 rows at
+// their canonical positions in dyc, when not null), dA GEMM with the SwiGLU
+// backward (dh in bf16 and quantized along I), dX GEMM.
 hipError_t mx_backward_round(const Plan &p, const SchedView &v, int g0, int g1, int64_t mt_bound,
                              const uint16_t *dy, const mok_weights &w, char *ws, const uint16_t *h,
-                             const float *topk_w, uint16_t *dx, uint16_t *stage, hipStream_t st);
+                             uint16_t *dyc, const float *topk_w, uint16_t *dx, uint16_t *stage, hipStream_t st);
 
 // MXFP8 weight gradients (MOK_MXFP8_WGRAD). begin, before the backward
 // rounds: the padded expert offsets and x and dy quantized along the token

@@ -40,9 +40,12 @@ struct GatherMx {
     int MB, H, k;
     const uint16_t *src;
     uint8_t *ring;
+    uint16_t *canon;   // optional: the bf16 rows at their canonical positions, [R][H]
 
     __device__ __forceinline__ void row(int g, int r) const {
-        const int tok = v.perm[v.mb_start[g] + r] / k;
+        const int q = v.mb_start[g] + r;
+        const int tok = v.perm[q] / k;
+        uint4 *dc = canon ? reinterpret_cast<uint4 *>(canon + (int64_t)canon_pos(v, g, q) * H) : nullptr;
         const uint4 *s = reinterpret_cast<const uint4 *>(src + (int64_t)tok * H);
         uint8_t *slot = ring + (g % n_slots) * (int64_t)MB * (H + H / 32);
         uint8_t *el = slot + (int64_t)r * H;
@@ -55,6 +58,13 @@ struct GatherMx {
             for (int i = 0; i < 4; ++i) {
                 const int c = c0 + i * 64 + lane;
                 t[i] = c < n ? s[c] : make_uint4(0, 0, 0, 0);
+            }
+            if (dc) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int c = c0 + i * 64 + lane;
+                    if (c < n) dc[c] = t[i];
+                }
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -737,14 +747,14 @@ hipError_t launch_gemm8(const char *name, dim3 grid, const typename P::Args &arg
 }  // namespace
 
 hipError_t mx_forward_round(const Plan &p, const SchedView &v, int g0, int g1, int64_t mt_bound,
-                            const uint16_t *x, const mok_weights &w, char *ws, uint16_t *h, const float *topk_w,
-                            uint16_t *out, uint16_t *stage, hipStream_t st) {
+                            const uint16_t *x, const mok_weights &w, char *ws, uint16_t *h, uint16_t *xc,
+                            const float *topk_w, uint16_t *out, uint16_t *stage, hipStream_t st) {
     uint8_t *ring = reinterpret_cast<uint8_t *>(ws + p.w_ring);
     uint8_t *aring = reinterpret_cast<uint8_t *>(ws + p.w_aring);
     {
         const dim3 sgrid((unsigned)ceil_div(p.MB, kRowsPerBlock), (unsigned)(g1 - g0));
         KernelTimer tm("gather", st);
-        gather_rows_mx<<<sgrid, 256, 0, st>>>(GatherMx{v, p.n_slots, p.MB, p.H, p.k, x, ring}, g0);
+        gather_rows_mx<<<sgrid, 256, 0, st>>>(GatherMx{v, p.n_slots, p.MB, p.H, p.k, x, ring, xc}, g0);
     }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
@@ -761,7 +771,7 @@ hipError_t mx_forward_round(const Plan &p, const SchedView &v, int g0, int g1, i
 
 hipError_t mx_backward_round(const Plan &p, const SchedView &v, int g0, int g1, int64_t mt_bound,
                              const uint16_t *dy, const mok_weights &w, char *ws, const uint16_t *h,
-                             const float *topk_w, uint16_t *dx, uint16_t *stage, hipStream_t st) {
+                             uint16_t *dyc, const float *topk_w, uint16_t *dx, uint16_t *stage, hipStream_t st) {
     uint8_t *ring = reinterpret_cast<uint8_t *>(ws + p.w_ring);
     uint16_t *dh = reinterpret_cast<uint16_t *>(ws + p.w_dh);
     uint16_t *gav = reinterpret_cast<uint16_t *>(ws + p.w_ga);
@@ -771,7 +781,7 @@ hipError_t mx_backward_round(const Plan &p, const SchedView &v, int g0, int g1, 
     {
         const dim3 sgrid((unsigned)ceil_div(p.MB, kRowsPerBlock), (unsigned)(g1 - g0));
         KernelTimer tm("gather_dy", st);
-        gather_rows_mx<<<sgrid, 256, 0, st>>>(GatherMx{v, p.n_slots, p.MB, p.H, p.k, dy, ring}, g0);
+        gather_rows_mx<<<sgrid, 256, 0, st>>>(GatherMx{v, p.n_slots, p.MB, p.H, p.k, dy, ring, dyc}, g0);
     }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;

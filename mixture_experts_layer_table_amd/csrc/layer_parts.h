@@ -275,19 +275,40 @@ constexpr int kRowsPerBlock = 4;   // one 64-lane wave per row
 
 // Dispatch copy of one row (bf16 ring): one wave moves the row of processing
 // position q = mb_start[g] + r from token order into ring slot g % n_slots.
+// Canonical (expert, f) position of processing position q of mini-batch g:
+// the m-tiles of g are runs of consecutive positions in both orders, listed
+// with ascending q0, so a binary search over them finds q's run.
+__device__ __forceinline__ int canon_pos(const SchedView &v, int g, int q) {
+    int lo = v.mtfirst[g], hi = v.mtfirst[g + 1] - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (v.mtiles[mid].q0 <= q)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    const MTile t = v.mtiles[lo];
+    return t.c0 + (q - t.q0);
+}
+
 struct GatherBf16 {
     SchedView v;
     int64_t n_slots;
     int MB, H, k;
     const uint16_t *src;
     uint16_t *ring;
+    // optional second destination: the same rows at their canonical
+    // positions, [R][H] (the weight gradients read them from there)
+    uint16_t *canon = nullptr;
 
     // 8 loads in flight per lane before the stores: a wave moving rows one
     // after the other is otherwise bound by one memory round trip per 1 KiB.
     __device__ __forceinline__ void row(int g, int r) const {
-        const int tok = v.perm[v.mb_start[g] + r] / k;
+        const int q = v.mb_start[g] + r;
+        const int tok = v.perm[q] / k;
         const uint4 *s = reinterpret_cast<const uint4 *>(src + (int64_t)tok * H);
         uint4 *d = reinterpret_cast<uint4 *>(ring + ((g % n_slots) * MB + r) * (int64_t)H);
+        uint4 *dc = canon ? reinterpret_cast<uint4 *>(canon + (int64_t)canon_pos(v, g, q) * H) : nullptr;
         const int n = H / 8, lane = threadIdx.x & 63;
         for (int c0 = 0; c0 < n; c0 += 64 * 8) {
             uint4 t[8];
@@ -300,6 +321,13 @@ struct GatherBf16 {
             for (int i = 0; i < 8; ++i) {
                 const int c = c0 + i * 64 + lane;
                 if (c < n) d[c] = t[i];
+            }
+            if (dc) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int c = c0 + i * 64 + lane;
+                    if (c < n) dc[c] = t[i];
+                }
             }
         }
     }

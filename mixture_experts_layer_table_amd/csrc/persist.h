@@ -102,11 +102,15 @@ __device__ __forceinline__ void chunk_span(const QueueShape &q, int x, int nt, i
 }
 
 // Thread 0 of a workgroup: claim the next item. Returns its class (0: queue
-// drained or stalled) and sets id. Producer tiles go first, so that the tiles
-// an XCD runs together stay in the lockstep order of a separate launch (their
-// shared operand slices are then read from L2, not HBM); consumer tiles fill
-// the compute units that the producers' last partial wave leaves idle.
-__device__ int claim_item(const PairSync &s, const QueueShape &q, int xcd, uint32_t *status, int &id) {
+// drained) and sets id. Producer tiles go first, so that the tiles an XCD runs
+// together stay in the lockstep order of a separate launch (their shared
+// operand slices are then read from L2, not HBM); consumer tiles fill the
+// compute units that the producers' last partial wave leaves idle. A consumer
+// tile is claimed only once every producer tile is claimed, i.e. running on a
+// resident workgroup that will finish it; the wait for its m-tile is separate
+// (wait_consumer_inputs), so that a workgroup can claim its next item while it
+// still runs the current one.
+__device__ int claim_item(const PairSync &s, const QueueShape &q, int xcd, int &id) {
     for (int i = 0; i < kXcds; ++i) {
         const int x = (xcd + i) % kXcds;
         int start, len;
@@ -118,8 +122,6 @@ __device__ int claim_item(const PairSync &s, const QueueShape &q, int xcd, uint3
             return 1;
         }
     }
-    // Every producer tile is claimed, and each is running on a resident
-    // workgroup: take the next consumer tile and wait for its m-tile.
     for (int i = 0; i < kXcds; ++i) {
         const int x = (xcd + i) % kXcds;
         int start, len;
@@ -127,14 +129,21 @@ __device__ int claim_item(const PairSync &s, const QueueShape &q, int xcd, uint3
         if (load_relaxed(&s.head[kXcds + x]) >= len) continue;
         const int h = atomicAdd(&s.head[kXcds + x], 1);
         if (h >= len) continue;
-        int j, n;
-        item_tile(start + h, q.nt2, q.mtc, j, n);
-        if (!wait_at_least(&s.done[j], q.nt1, status, s.spin_limit)) return 0;
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         id = start + h;
         return 2;
     }
     return 0;
+}
+
+// Thread 0, before a consumer tile starts: wait until every producer tile of
+// its m-tile is done, then acquire what they wrote. False: the wait gave up
+// (stall flagged).
+__device__ bool wait_consumer_inputs(const PairSync &s, const QueueShape &q, int id, uint32_t *status) {
+    int j, n;
+    item_tile(id, q.nt2, q.mtc, j, n);
+    if (!wait_at_least(&s.done[j], q.nt1, status, s.spin_limit)) return false;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    return true;
 }
 
 // End of a work item: every wave waits for its own global stores to be
@@ -190,11 +199,34 @@ __global__ __launch_bounds__(P1::C::NT) void persist_pair_kernel(typename P1::Ar
     q.ng = (q.mtc + kGroupM - 1) / kGroupM;
     const int xcd = (int)(blockIdx.x % kXcds);   // workgroups are dispatched round-robin over the XCDs
     uint64_t t_claim = 0, t_start = 0;   // thread 0's item-trace times
+    // Thread 0 takes a ticket from its own XCD's chunk (producer chunk until
+    // claim_item has once handed it a consumer tile, consumer chunk after
+    // that) while the current item is in its epilogue: the atomic's round
+    // trip then overlaps the epilogue instead of following it. The ticket is
+    // checked at the top of the next iteration; an exhausted chunk falls back
+    // to claim_item's full search, which keeps the producers-first order
+    // (a consumer ticket is only ever taken once every producer tile has been
+    // claimed). The wait for a consumer tile's inputs comes after the current
+    // item is published: the current item may be one of the producer tiles it
+    // waits for.
+    int ticket = -1;   // thread 0: own-chunk ticket taken during the last epilogue (-1: none)
+    int phase = 1;     // thread 0: class of the chunk the ticket came from
     for (;;) {
         if (threadIdx.x == 0) {
-            if (s.trace.rec) t_claim = __builtin_amdgcn_s_memrealtime();
-            int id = 0;
-            const int cls = claim_item(s, q, xcd, v.status, id);
+            if (s.trace.rec && ticket < 0) t_claim = __builtin_amdgcn_s_memrealtime();
+            int cls = 0, id = 0;
+            if (ticket >= 0) {
+                int start, len;
+                if (phase == 1) chunk_span(q, xcd, q.nt1, q.n1, start, len);
+                else chunk_span(q, xcd, q.nt2, q.n2, start, len);
+                if (ticket < len) {
+                    cls = phase;
+                    id = start + ticket;
+                }
+            }
+            if (cls == 0) cls = claim_item(s, q, xcd, id);
+            if (cls != 0) phase = cls;
+            if (cls == 2 && !wait_consumer_inputs(s, q, id, v.status)) cls = 0;
             bcast[0] = cls;
             bcast[1] = id;
             if (s.trace.rec) t_start = __builtin_amdgcn_s_memrealtime();
@@ -202,22 +234,32 @@ __global__ __launch_bounds__(P1::C::NT) void persist_pair_kernel(typename P1::Ar
         __syncthreads();
         const int cls = bcast[0], id = bcast[1];
         if (cls == 0) return;
+        uint64_t t_next = 0;
+        auto take_ticket = [&]() {
+            if (threadIdx.x == 0) {
+                if (s.trace.rec) t_next = __builtin_amdgcn_s_memrealtime();
+                ticket = atomicAdd(&s.head[(phase == 1 ? 0 : kXcds) + xcd], 1);
+            }
+        };
         int j, n;
         uint64_t t_kloop;
         if (cls == 1) {
             item_tile(id, q.nt1, q.mtc, j, n);
             P1 p;
             p.init(a1, seg_tile<P1>(v, lo, j, n, a1.n_slots));
-            t_kloop = run_tile(p, lds);
+            t_kloop = gemm_tile(p, lds, take_ticket);
         } else {
             item_tile(id, q.nt2, q.mtc, j, n);
             P2 p;
             p.init(a2, seg_tile<P2>(v, lo, j, n, a2.n_slots));
-            t_kloop = run_tile(p, lds);
+            t_kloop = gemm_tile(p, lds, take_ticket);
         }
         item_done_barrier();
         if (cls == 1 && threadIdx.x == 0) __hip_atomic_fetch_add(&s.done[j], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-        if (threadIdx.x == 0) trace_item(s.trace, t_claim, t_start, t_kloop, cls, id);
+        if (threadIdx.x == 0) {
+            trace_item(s.trace, t_claim, t_start, t_kloop, cls, id);
+            t_claim = t_next;
+        }
     }
 }
 

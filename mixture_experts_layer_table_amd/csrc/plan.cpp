@@ -155,10 +155,26 @@ mok_status make_plan(const mok_config *cfg, const mok_shape *shape, Plan *p) {
         q.w_qdys = w.take((size_t)q.H * kp / 32);
         q.w_po = w.take(4 * (size_t)(q.E + 1));
     }
+    // With k = 1 every routed row is its own token, and the BF16 weight
+    // gradients read the x and dy rows of each expert in canonical order as
+    // contiguous rows saved by the gathers, instead of gathering them through
+    // the token index (measured 15% faster for both weight-gradient GEMMs at
+    // the EP-64 share). With k > 1 the token matrices are k times smaller than
+    // the routed rows and the indexed reads hit in cache, so the copies would
+    // cost more than they save (measured 0.9 ms slower at the full layer). The
+    // MXFP8 weight gradients quantize their own token-axis copies instead.
+    // One macro-batch whose mini-batches all fit the ring leaves the dy rows
+    // in the ring at their canonical positions (processing order equals
+    // canonical order then, and mini-batch g occupies slot g): the dy copy is
+    // then the ring itself.
+    q.keep_canonical = !q.mx_wgrad && q.k == 1;
+    q.dy_in_ring = q.keep_canonical && q.precision == MOK_BF16 && q.NM == 1 && (int64_t)q.G <= q.n_slots;
+    if (q.keep_canonical && !q.dy_in_ring) q.w_dyc = w.take((size_t)q.R * q.H * 2);
     q.w_total = w.off;
 
     Carver x;
     q.c_h = x.take((size_t)q.R * 2 * q.I * 2);
+    if (q.keep_canonical) q.c_xc = x.take((size_t)q.R * q.H * 2);
     q.c_total = x.off;
     q.fingerprint = schedule_fingerprint(q);
     *p = q;
@@ -173,7 +189,7 @@ Plan forward_only_workspace(const Plan &p, size_t *bytes) {
     q.w_stage = w.take((size_t)q.stage_rows * q.H * 2);
     q.w_sync = w.take(4 * (size_t)(kSyncHeads + q.max_mtiles));
     // backward-only regions: none in this layout (a forward never touches them)
-    q.w_dh = q.w_ga = q.w_dgp = q.w_dhq = q.w_dhq_scales = 0;
+    q.w_dh = q.w_ga = q.w_dgp = q.w_dhq = q.w_dhq_scales = q.w_dyc = 0;
     q.w_qx = q.w_qxs = q.w_qdh = q.w_qdhs = q.w_qga = q.w_qgas = q.w_qdy = q.w_qdys = q.w_po = 0;
     q.w_total = w.off;
     *bytes = w.off;

@@ -59,8 +59,16 @@ struct Plan {
     // po[e+1] - po[e] = its row count rounded up to 128; po [E+1] int32.
     int64_t Kp = 0;
     size_t w_qx = 0, w_qxs = 0, w_qdh = 0, w_qdhs = 0, w_qga = 0, w_qgas = 0, w_qdy = 0, w_qdys = 0, w_po = 0;
-    // fwd_ctx (byte offsets)
-    size_t c_h = 0, c_total = 0;
+    // BF16 weight gradients with k = 1 only: dy rows in canonical (expert, f)
+    // order, [R][H] bf16, written by the backward's dy gather (0 when unused,
+    // or when the ring already holds them so: dy_in_ring)
+    size_t w_dyc = 0;
+    bool dy_in_ring = false;
+    // fwd_ctx (byte offsets): h [R][2I] bf16 in processing order; with BF16
+    // weight gradients and k = 1 also the x rows in canonical order, [R][H]
+    // bf16, written by the forward's gather (c_xc 0 when unused)
+    size_t c_h = 0, c_xc = 0, c_total = 0;
+    bool keep_canonical = false;   // the two canonical copies above exist
 };
 
 mok_status make_plan(const mok_config *cfg, const mok_shape *shape, Plan *p);

@@ -79,6 +79,36 @@ def test_schedule_layout_matches_oracle_sizes():
         assert sc == lay.total_bytes and cx >= cfg.R * 2 * cfg.I * 2
 
 
+def test_canonical_row_copies_follow_k_and_mode():
+    """fwd_ctx holds h [R][2I] bf16, plus the x rows in canonical order [R][H]
+    bf16 exactly when every routed row is its own token (k = 1) and the weight
+    gradients run in BF16; the dy copy lives in the workspace, except when one
+    macro-batch fits the ring (the ring then holds the dy rows in canonical
+    order). With k > 1 the weight gradients read x and dy through the token
+    index, and neither copy exists: a kernel reading a copy the plan did not
+    make would read through a null pointer."""
+    def align(n):
+        return (n + 255) // 256 * 256
+    T, H, I, E = 256, 256, 128, 4
+    small_ring = 2 * 64 * 2 * H            # two 64-row slots: 4 mini-batches do not fit
+    for k, prec, canon in ((1, mok.MOK_BF16, True), (2, mok.MOK_BF16, False), (1, mok.MOK_MXFP8, True),
+                           (1, mok.MOK_MXFP8_WGRAD, False), (4, mok.MOK_MXFP8, False)):
+        R = T * k
+        big = mok.MoKConfig(minibatch_rows=64, ring_bytes=64 << 20, precision=prec)
+        small = mok.MoKConfig(minibatch_rows=64, ring_bytes=small_ring, precision=prec)
+        ws_big, _, cx = mok.query_sizes(big, T, H, I, E, k)
+        ws_small, _, cx_small = mok.query_sizes(small, T, H, I, E, k)
+        h_bytes = align(R * 2 * I * 2)
+        assert cx == cx_small == h_bytes + (align(R * H * 2) if canon else 0), (k, prec)
+        if prec == mok.MOK_BF16 and canon:
+            # one macro-batch in a ring that holds it: the dy rows stay in the
+            # ring; two macro-batches (same ring): a dy copy in the workspace
+            two_macro = mok.MoKConfig(minibatch_rows=64, ring_bytes=64 << 20, precision=prec,
+                                      macrobatch_tokens=T // 2)
+            ws_two, _, _ = mok.query_sizes(two_macro, T, H, I, E, k)
+            assert ws_two - ws_big == align(R * H * 2)
+
+
 def test_ring_slot_count_rule():
     from oracle import schedule as S
     # fewer than two mini-batches in the ring is rejected; exactly two is accepted
