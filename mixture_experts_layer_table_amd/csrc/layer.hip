@@ -740,6 +740,10 @@ mok_status launch_forward(const Plan &p, const void *schedule, void *workspace, 
     uint16_t *h = reinterpret_cast<uint16_t *>(static_cast<char *>(fwd_ctx) + p.c_h);
     // x rows saved in canonical order for the weight gradients (null when the plan keeps none)
     uint16_t *xc = p.keep_canonical ? reinterpret_cast<uint16_t *>(static_cast<char *>(fwd_ctx) + p.c_xc) : nullptr;
+    if (p.x_ring_is_copy && !identity) {   // the copy doubles as the ring: one write per x row
+        ring = xc;
+        xc = nullptr;
+    }
     int *sync = reinterpret_cast<int *>(ws + p.w_sync);
     hipError_t err = hipSuccess;
     if (whole_pass(p) && !identity) {   // one launch for the pass, ring protocol in the kernel

@@ -169,6 +169,7 @@ mok_status make_plan(const mok_config *cfg, const mok_shape *shape, Plan *p) {
     // then the ring itself.
     q.keep_canonical = !q.mx_wgrad && q.k == 1;
     q.dy_in_ring = q.keep_canonical && q.precision == MOK_BF16 && q.NM == 1 && (int64_t)q.G <= q.n_slots;
+    q.x_ring_is_copy = q.dy_in_ring;
     if (q.keep_canonical && !q.dy_in_ring) q.w_dyc = w.take((size_t)q.R * q.H * 2);
     q.w_total = w.off;
 

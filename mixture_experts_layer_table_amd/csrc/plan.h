@@ -64,6 +64,10 @@ struct Plan {
     // or when the ring already holds them so: dy_in_ring)
     size_t w_dyc = 0;
     bool dy_in_ring = false;
+    // the same condition in the forward (BF16, k = 1, one macro-batch, every
+    // mini-batch in its own slot): ring row q is canonical row q, so the
+    // forward uses fwd_ctx's x copy as its ring and writes each x row once
+    bool x_ring_is_copy = false;
     // fwd_ctx (byte offsets): h [R][2I] bf16 in processing order; with BF16
     // weight gradients and k = 1 also the x rows in canonical order, [R][H]
     // bf16, written by the forward's gather (c_xc 0 when unused)
