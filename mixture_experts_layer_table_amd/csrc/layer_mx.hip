@@ -59,11 +59,11 @@ struct GatherMx {
                 const int c = c0 + i * 64 + lane;
                 t[i] = c < n ? s[c] : make_uint4(0, 0, 0, 0);
             }
-            if (dc) {
+            if (dc) {   // read only by the weight gradients, much later: kept out of the caches
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int c = c0 + i * 64 + lane;
-                    if (c < n) dc[c] = t[i];
+                    if (c < n) store16_nt(dc + c, t[i]);
                 }
             }
 #pragma unroll

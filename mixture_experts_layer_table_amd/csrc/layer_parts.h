@@ -291,6 +291,17 @@ __device__ __forceinline__ int canon_pos(const SchedView &v, int g, int q) {
     return t.c0 + (q - t.q0);
 }
 
+// 16-byte store with the non-temporal hint (see store8_nt).
+__device__ __forceinline__ void store16_nt(uint4 *p, uint4 v) {
+    typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+    v4u w;
+    w.x = v.x;
+    w.y = v.y;
+    w.z = v.z;
+    w.w = v.w;
+    __builtin_nontemporal_store(w, reinterpret_cast<v4u *>(p));
+}
+
 struct GatherBf16 {
     SchedView v;
     int64_t n_slots;
@@ -322,11 +333,11 @@ struct GatherBf16 {
                 const int c = c0 + i * 64 + lane;
                 if (c < n) d[c] = t[i];
             }
-            if (dc) {
+            if (dc) {   // read only by the weight gradients, much later: kept out of the caches
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     const int c = c0 + i * 64 + lane;
-                    if (c < n) dc[c] = t[i];
+                    if (c < n) store16_nt(dc + c, t[i]);
                 }
             }
         }
