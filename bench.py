@@ -257,8 +257,11 @@ def item_trace_summary(rec, cfg):
     launch's first record to its last is split into claim and input wait, K
     loop, epilogue (stores and publication), idle before its first item and
     idle after its last; shares are over workgroups x launch span, averaged
-    over launches of the same kernel. Also microseconds per item and per K step
-    for each item class whose K is fixed (segment GEMMs)."""
+    over launches of the same kernel. A persistent workgroup takes its next
+    ticket during the current item's epilogue, so an item's claim time counts
+    from the later of its claim record and the end of the workgroup's
+    previous item. Also microseconds per item and per K step for each item
+    class whose K is fixed (segment GEMMs)."""
     import numpy as np
     H, I = cfg.H, cfg.I
     ksteps = {(0, 1): H // 32, (0, 2): I // 32, (1, 1): H // 32, (1, 2): 2 * I // 32}
@@ -267,8 +270,14 @@ def item_trace_summary(rec, cfg):
         rk = rec[rec["kernel"] == kern]
         shares, per_class = [], {}
         for launch in sorted(set(rk["launch"].tolist())):
-            r = rk[rk["launch"] == launch]
+            r = rk[rk["launch"] == launch].copy()
             t0, t1 = int(r["t_claim"].min()), int(r["t_end"].max())
+            # claim start: not before the workgroup's previous item ended
+            for wg in set(r["workgroup"].tolist()):
+                idx = np.flatnonzero(r["workgroup"] == wg)
+                idx = idx[np.argsort(r["t_start"][idx], kind="stable")]
+                prev_end = np.concatenate([[0], r["t_end"][idx][:-1]])
+                r["t_claim"][idx] = np.maximum(r["t_claim"][idx], prev_end)
             span = max(t1 - t0, 1)
             wgs = sorted(set(r["workgroup"].tolist()))
             tot = dict(claim=0, kloop=0, epilogue=0, idle_start=0, idle_end=0)

@@ -32,3 +32,18 @@ def test_shares_and_per_item_times_by_hand():
     assert c1["items_per_launch"] == 2 and c1["kloop_us"] == pytest.approx(0.55)
     assert c1["us_per_kstep"] == pytest.approx(0.55 / (128 // 32), abs=1e-3)
     assert s["classes"][2]["us_per_kstep"] == pytest.approx(0.10 / (64 // 32), abs=1e-3)
+
+
+def test_ticket_taken_during_the_previous_epilogue_counts_from_its_end():
+    # wg 0 takes its second item's ticket at 65, inside its first item's
+    # epilogue (60..70); the claim time of that item counts from 70
+    rec = np.array([
+        (0, 10, 60, 70, 0, 0, 1, 0, 0, 0),
+        (65, 80, 90, 100, 0, 0, 2, 0, 0, 0),
+    ], dtype=DT)
+    cfg = synth.small_config("t", T=64, H=128, I=64, E=2, k=1)
+    s = bench.item_trace_summary(rec, cfg)["fwd_gemms"]
+    sh = s["shares"]
+    assert sh["claim"] == pytest.approx((10 + 10) / 100)
+    assert sum(sh[k] for k in ("claim", "kloop", "epilogue", "idle_start", "idle_end")) == pytest.approx(1.0)
+    assert s["classes"][2]["claim_us"] == pytest.approx(0.10)
