@@ -254,8 +254,17 @@ __global__ __launch_bounds__(P1::C::NT) void persist_pair_kernel(typename P1::Ar
             p.init(a2, seg_tile<P2>(v, lo, j, n, a2.n_slots));
             t_kloop = gemm_tile(p, lds, take_ticket);
         }
-        item_done_barrier();
-        if (cls == 1 && threadIdx.x == 0) __hip_atomic_fetch_add(&s.done[j], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        if (cls == 1) {
+            item_done_barrier();   // the release below covers every wave's stores
+            if (threadIdx.x == 0) __hip_atomic_fetch_add(&s.done[j], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+            // Nothing in this launch reads a consumer tile's output: its stores
+            // drain while the next item starts. The barrier only frees the LDS
+            // (every wave's own LDS accesses done first); stores still in flight
+            // make the next item's load-counter waits stricter, never weaker.
+            wait_lgkm0();
+            lds_barrier();
+        }
         if (threadIdx.x == 0) {
             trace_item(s.trace, t_claim, t_start, t_kloop, cls, id);
             t_claim = t_next;
