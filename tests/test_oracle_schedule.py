@@ -176,3 +176,30 @@ def test_autosize_minibatch_by_enumeration(T, k, I, MT, units, tm):
         n += 1
     want = n * tm if n * tm <= macro_rows else -(-macro_rows // 16) * 16
     assert mb == max(16, want) and mb % 16 == 0
+
+
+@pytest.mark.parametrize("T,k,E,I,units,tm", [(16384, 1, 1, 2048, 256, 256), (16384, 1, 4, 2048, 256, 256),
+                                              (4096, 8, 1, 2048, 256, 128), (20480, 1, 8, 1024, 256, 256),
+                                              (2000, 2, 3, 512, 8, 128)])
+def test_autosize_minibatch_fills_two_waves_of_the_schedules_own_tiles(T, k, E, I, units, tm):
+    """The auto-sized mini-batch, counted through the schedule oracle's own
+    segments (not the closed form): every full mini-batch's gate/up GEMM has at
+    least two waves of output tiles (explainer 4 ②); with one expert, one m-tile
+    fewer would not (the size is the least such whole number of m-tiles)."""
+    tn = 256
+    rng = np.random.default_rng(T + k + E)
+    ids = np.stack([rng.permutation(E)[:k] if k <= E else rng.integers(0, E, k) for _ in range(T)]) \
+        if E > 1 else np.zeros((T, k), np.int64)
+    mb = S.autosize_minibatch(T, k, I, 0, units, tm, tn)
+    s = S.build(ids, E, mb, 0)
+    n_tiles_n = -(-2 * I // tn)
+    full = [g for g in range(s.G) if s.mb_start[g + 1] - s.mb_start[g] == mb]
+    assert full, "no full mini-batch"
+    for g in full:
+        segs = s.segments[s.segments[:, 0] == g]
+        tiles = sum(-(-int(length) // tm) for length in segs[:, 3]) * n_tiles_n
+        assert tiles >= 2 * units, (g, tiles)
+    if E == 1 and mb > tm:
+        fewer = S.build(ids, E, mb - tm, 0)
+        segs = fewer.segments[fewer.segments[:, 0] == 0]
+        assert sum(-(-int(length) // tm) for length in segs[:, 3]) * n_tiles_n < 2 * units
