@@ -161,6 +161,7 @@ struct Down {
     __device__ int mvalid() const { return t.mt.rows; }
     int n0, nk, H;
     Args a;
+    TokenRows<C> tr;
 
     __device__ bool setup(const Args &args, Blk b) {
         SegTile tt;
@@ -178,6 +179,7 @@ struct Down {
         xl.init(args.aring + row0 * args.I, args.I, t.mt.rows);
         wl.init(args.wd + (int64_t)t.mt.e * args.I * H + n0, H, args.I, H - n0);
         nk = args.I / C::BK;
+        tr.load(t, wave_id() / C::WAVES_N, args.v, args.k, args.topk_w, true);   // hidden behind the K loop
     }
     __device__ void issue(int kt, uint32_t tile) {
         xl.issue(kt * C::BK, tile);
@@ -185,7 +187,7 @@ struct Down {
     }
     __device__ int wrow(int wn, int fn) const { return wn * C::WN + fn * 32; }
     __device__ void epilogue(f32x16_t (&acc)[C::FM][C::FN], int wm, int wn) {
-        store_token_rows<C, C::LDS_BYTES>(acc, t, n0, wm, wn, a.v, H, a.k, a.MT, a.nb_full, a.topk_w, true, a.out, a.stage);
+        store_token_rows<C, C::LDS_BYTES>(acc, t, n0, wm, wn, tr, H, a.k, a.MT, a.nb_full, true, a.out, a.stage);
     }
 };
 
@@ -352,6 +354,7 @@ struct DX {
     __device__ int mvalid() const { return t.mt.rows; }
     int n0, nk, I;
     Args a;
+    TokenRows<C> tr;
 
     __device__ bool setup(const Args &args, Blk b) {
         SegTile tt;
@@ -370,6 +373,7 @@ struct DX {
         const int64_t wo = (int64_t)t.mt.e * H * I + (int64_t)n0 * I;
         wl.init(args.wg + wo, I, min(C::BN, H - n0), args.wu + wo, I);
         nk = 2 * I / C::BK;
+        tr.load(t, wave_id() / C::WAVES_N, args.v, args.k, nullptr, false);   // hidden behind the K loop
     }
     __device__ void issue(int kt, uint32_t tile) {
         xl.issue(kt * C::BK, tile);
@@ -377,7 +381,7 @@ struct DX {
     }
     __device__ int wrow(int wn, int fn) const { return wn * C::WN + fn * 32; }
     __device__ void epilogue(f32x16_t (&acc)[C::FM][C::FN], int wm, int wn) {
-        store_token_rows<C, C::LDS_BYTES>(acc, t, n0, wm, wn, a.v, a.H, a.k, a.MT, a.nb_full, nullptr, false, a.dx, a.stage);
+        store_token_rows<C, C::LDS_BYTES>(acc, t, n0, wm, wn, tr, a.H, a.k, a.MT, a.nb_full, false, a.dx, a.stage);
     }
 };
 

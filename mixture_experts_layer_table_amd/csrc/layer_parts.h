@@ -234,41 +234,62 @@ __device__ __forceinline__ float bf16_at(const uint2 &v, int j) {
 // towards token order. k == 1: straight to the token's row, the forward one
 // scaled by its gate weight after rounding y to bf16 (the weighted combine);
 // k > 1: into the macro-batch's staging rows, combined later in j order.
-template <class C, size_t LDS_END>
-__device__ __forceinline__ void store_token_rows(const f32x16_t (&acc)[C::FM][C::FN], const SegTile &t, int n0,
-                                                 int wm, int wn, const SchedView &v, int H, int k, int MT,
-                                                 int nb_full, const float *topk_w, bool weighted, uint16_t *dst_k1,
-                                                 uint16_t *stage) {
-    const int lane = epi_lane();
-    const int nb = n0 + wn * C::WN;
-    if (nb >= H) return;   // H % 64 == 0: the wave's columns are all valid or all past H
-    // k == 1: token (and gate weight) of the lane's fragment rows, row lane % 32
-    // of each fm, all loaded up front; the row passes take a row's token from
-    // the lane that holds it. (Loaded per pass, each fragment's index loads
-    // would wait behind the previous fragment's stores.)
+//
+// k == 1: token (and gate weight) of the lane's fragment rows, row lane % 32
+// of each fm. TokenRows::load issues these index loads; a tile calls it before
+// its K loop, so that their two dependent round trips (perm, then topk_w) are
+// hidden behind the K loop instead of opening the epilogue. (Loaded per pass,
+// each fragment's index loads would also wait behind the previous fragment's
+// stores.)
+template <class C>
+struct TokenRows {
     int tok[C::FM];
     float gw[C::FM];
+    __device__ __forceinline__ void load(const SegTile &t, int wm, const SchedView &v, int k, const float *topk_w,
+                                         bool weighted) {
+        const int lane = epi_lane();
 #pragma unroll
-    for (int fm = 0; fm < C::FM; ++fm) {
-        const int m = wm * C::WM + fm * 32 + (lane & 31);
-        tok[fm] = k == 1 ? v.perm[t.mt.q0 + (m < t.mt.rows ? m : 0)] : 0;
+        for (int fm = 0; fm < C::FM; ++fm) {
+            const int m = wm * C::WM + fm * 32 + (lane & 31);
+            tok[fm] = k == 1 ? v.perm[t.mt.q0 + (m < t.mt.rows ? m : 0)] : 0;
+        }
+#pragma unroll
+        for (int fm = 0; fm < C::FM; ++fm) gw[fm] = (weighted && k == 1) ? topk_w[tok[fm]] : 1.0f;
     }
-#pragma unroll
-    for (int fm = 0; fm < C::FM; ++fm) gw[fm] = (weighted && k == 1) ? topk_w[tok[fm]] : 1.0f;
+};
+
+template <class C, size_t LDS_END>
+__device__ __forceinline__ void store_token_rows(const f32x16_t (&acc)[C::FM][C::FN], const SegTile &t, int n0,
+                                                 int wm, int wn, const TokenRows<C> &tr, int H, int k, int MT,
+                                                 int nb_full, bool weighted, uint16_t *dst_k1, uint16_t *stage) {
+    const int nb = n0 + wn * C::WN;
+    if (nb >= H) return;   // H % 64 == 0: the wave's columns are all valid or all past H
     const int64_t sbase = (int64_t)k * ((t.mt.g / nb_full) * (int64_t)MT);
     staged_rows<C, LDS_END>(
         [&](int fm, int fn, int g4, int j) {
             const float y = acc[fm][fn][g4 * 4 + j];
-            return (weighted && k == 1) ? gw[fm] * bf16r(y) : y;   // y rows are bf16
+            return (weighted && k == 1) ? tr.gw[fm] * bf16r(y) : y;   // y rows are bf16
         },
         [&](int fm, int r) -> uint16_t * {
             // every lane takes part in the shuffle (before any lane leaves): lane r holds row r's token
-            const int tok_r = k == 1 ? __shfl(tok[fm], r) : 0;
+            const int tok_r = k == 1 ? __shfl(tr.tok[fm], r) : 0;
             const int m = wm * C::WM + fm * 32 + r;
             if (m >= t.mt.rows) return nullptr;
             const int q = t.mt.q0 + m;
             return (k == 1 ? dst_k1 + (int64_t)tok_r * H : stage + (q - sbase) * H) + nb;
         });
+}
+
+// The same, loading the token rows at the epilogue (tiles that do not prefetch them).
+template <class C, size_t LDS_END>
+__device__ __forceinline__ void store_token_rows(const f32x16_t (&acc)[C::FM][C::FN], const SegTile &t, int n0,
+                                                 int wm, int wn, const SchedView &v, int H, int k, int MT,
+                                                 int nb_full, const float *topk_w, bool weighted, uint16_t *dst_k1,
+                                                 uint16_t *stage) {
+    if (n0 + wn * C::WN >= H) return;
+    TokenRows<C> tr;
+    tr.load(t, wm, v, k, topk_w, weighted);
+    store_token_rows<C, LDS_END>(acc, t, n0, wm, wn, tr, H, k, MT, nb_full, weighted, dst_k1, stage);
 }
 
 constexpr int kRowsPerBlock = 4;   // one 64-lane wave per row
