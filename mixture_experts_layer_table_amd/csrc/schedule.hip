@@ -215,41 +215,66 @@ __global__ __launch_bounds__(kTableThreads) void sched_table(SchedView v) {
     }
 }
 
-// Stable scatter: perm, inv, canon, ctok.
+// Stable scatter: perm, inv, canon, ctok. A block ranks its chunk's rows in
+// row order, 256 rows (one per thread) at a time: inside a wave, the lanes
+// holding one expert are grouped with ballots (one pass per distinct expert
+// of the wave), which gives each row its rank among the wave's rows of its
+// expert and the group's size; the waves then take their turn, in order, at
+// a shared per-expert count of the rows already ranked in this chunk. With
+// the chunk's start count per expert (sched_bounds) that is the row's stable
+// rank among all rows of its expert.
 __global__ __launch_bounds__(kThreads) void sched_scatter(const int32_t *__restrict__ ids, SchedView v) {
     if (*v.status) return;
-    __shared__ int s_ids[kSchedChunk];
+    extern __shared__ int s_cnt[];   // [E] rows of each expert ranked so far in this chunk
     const int base = blockIdx.x * kSchedChunk;
     const int n = min(kSchedChunk, v.R - base);
-    for (int r = threadIdx.x; r < n; r += kThreads) s_ids[r] = ids[base + r];
+    for (int e = threadIdx.x; e < v.E; e += kThreads) s_cnt[e] = 0;
     __syncthreads();
-    const int r0 = threadIdx.x * 4;
-    if (r0 >= n) return;
-    int e4[4], cnt[4] = {0, 0, 0, 0};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) e4[j] = r0 + j < n ? s_ids[r0 + j] : -1;
-    for (int r = 0; r < r0; ++r) {
-        const int x = s_ids[r];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) cnt[j] += (x == e4[j]);
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int r = r0 + j;
-        if (r >= n) break;
-        for (int i = 0; i < j; ++i) cnt[j] += (e4[i] == e4[j]);
-        const int e = e4[j];
-        const int f = base + r;
-        const int rank = v.chunk[blockIdx.x * v.E + e] + cnt[j];
-        const int t = f / v.k;
-        const int m = t / v.MT;
-        const int q = v.moffsets[m * (v.E + 1) + e] + rank - v.bound[m * v.E + e];
-        const int c = v.offsets[e] + rank;
-        if ((unsigned)q >= (unsigned)v.R || (unsigned)c >= (unsigned)v.R) continue;  // unreachable
-        v.perm[q] = f;
-        v.inv[f] = q;
-        v.canon[c] = q;
-        v.ctok[c] = t;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint64_t lt = lane ? (~0ull >> (64 - lane)) : 0ull;   // lanes below this one
+    for (int r0 = 0; r0 < n; r0 += kThreads) {
+        const int r = r0 + (int)threadIdx.x;
+        const bool live = r < n;
+        const int e = live ? ids[base + r] : -1;
+        // group the wave's lanes by expert: each pass takes the lowest remaining lane's expert
+        uint64_t rest = __ballot(live);
+        int rank_w = 0, leader = 0, count = 0;
+        while (rest) {
+            const int l0 = __ffsll((unsigned long long)rest) - 1;
+            const int e0 = __shfl(e, l0);
+            const uint64_t grp = __ballot(live && e == e0) & rest;
+            if (live && e == e0) {
+                rank_w = __popcll(grp & lt);
+                leader = l0;
+                count = __popcll(grp);
+            }
+            rest &= ~grp;
+        }
+        // the waves of this step take their turn at the shared counts in row order
+        int start = 0;
+        for (int w = 0; w < kThreads / 64; ++w) {
+            __syncthreads();
+            if (wave == w && live && lane == leader) {
+                start = s_cnt[e];
+                s_cnt[e] = start + count;
+            }
+        }
+        start = __shfl(start, leader);
+        if (live) {
+            const int rank = v.chunk[blockIdx.x * v.E + e] + start + rank_w;
+            const int f = base + r;
+            const int t = f / v.k;
+            const int m = t / v.MT;
+            const int q = v.moffsets[m * (v.E + 1) + e] + rank - v.bound[m * v.E + e];
+            const int c = v.offsets[e] + rank;
+            if ((unsigned)q < (unsigned)v.R && (unsigned)c < (unsigned)v.R) {   // always (the ranks are a permutation)
+                v.perm[q] = f;
+                v.inv[f] = q;
+                v.canon[c] = q;
+                v.ctok[c] = t;
+            }
+        }
+        __syncthreads();   // this step's counts are complete before the next step reads them
     }
 }
 
@@ -282,7 +307,7 @@ mok_status launch_build_schedule(const Plan &p, const int32_t *ids, void *schedu
         sched_bounds<<<p.NM + 1, kThreads, hist_lds, st>>>(ids, v);
     }
     sched_table<<<1, kTableThreads, 0, st>>>(v);
-    if (p.nchunks > 0) sched_scatter<<<p.nchunks, kThreads, 0, st>>>(ids, v);
+    if (p.nchunks > 0) sched_scatter<<<p.nchunks, kThreads, (size_t)p.E * sizeof(int), st>>>(ids, v);
     return check_hip(hipGetLastError(), "mok_build_schedule");
 }
 
