@@ -80,10 +80,7 @@ struct GatherMx {
                 const int e = (int)sb - 127;
                 uint32_t o[2];
 #pragma unroll
-                for (int d = 0; d < 2; ++d)
-                    o[d] = e4m3_encode_bf16(w[2 * d] & 0xFFFFu, e) | (e4m3_encode_bf16(w[2 * d] >> 16, e) << 8) |
-                           (e4m3_encode_bf16(w[2 * d + 1] & 0xFFFFu, e) << 16) |
-                           (e4m3_encode_bf16(w[2 * d + 1] >> 16, e) << 24);
+                for (int d = 0; d < 2; ++d) o[d] = e4m3x4_bf16(w[2 * d], w[2 * d + 1], e);
                 if (c < n) {
                     *reinterpret_cast<uint2 *>(el + (int64_t)c * 8) = make_uint2(o[0], o[1]);
                     if ((c & 3) == 0) sc[c >> 2] = (uint8_t)sb;
@@ -123,14 +120,11 @@ __device__ __attribute__((noinline)) Enc16 quantize_block16(Block16 b) {
     amax = max(amax, (uint32_t)__shfl_xor((int)amax, 32));
     Enc16 r;
     r.scale = mx_scale_byte_f32(amax);
-    const int e = (int)r.scale - 127;
+    const float sc = mx_pow2_neg((int)r.scale - 127);
 #pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-        uint32_t x = 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) x |= e4m3_encode_f32(__float_as_uint(b.v[g4 * 4 + j]), e) << (8 * j);
-        r.enc[g4] = x;
-    }
+    for (int g4 = 0; g4 < 4; ++g4)
+        r.enc[g4] = e4m3x2_scaled(b.v[g4 * 4] * sc, b.v[g4 * 4 + 1] * sc) |
+                    (e4m3x2_scaled(b.v[g4 * 4 + 2] * sc, b.v[g4 * 4 + 3] * sc) << 16);
     return r;
 }
 
@@ -597,9 +591,7 @@ __global__ __launch_bounds__(256) void quantize_cols(QuantCols q) {
         const int ex = (int)sb - 127;
 #pragma unroll
         for (int d = 0; d < 8; ++d)
-            codes[c][b * 8 + d] = e4m3_encode_bf16(x[4 * d], ex) | (e4m3_encode_bf16(x[4 * d + 1], ex) << 8) |
-                                  (e4m3_encode_bf16(x[4 * d + 2], ex) << 16) |
-                                  (e4m3_encode_bf16(x[4 * d + 3], ex) << 24);
+            codes[c][b * 8 + d] = e4m3x4_bf16(x[4 * d] | (x[4 * d + 1] << 16), x[4 * d + 2] | (x[4 * d + 3] << 16), ex);
         if (col0 + c < q.ncols) q.sc[(int64_t)(col0 + c) * (q.Kp / 32) + p0 / 32 + b] = (uint8_t)sb;
     }
     __syncthreads();

@@ -2,8 +2,8 @@
 // share an E8M0 scale, elements are E4M3FN; "Mixture-of-Kittens (MoK)" project
 // summary, Key-concepts table, names MXFP8 as the low-precision format).
 //
-// Integer-only, on the bit patterns of bf16 or fp32 inputs, so the result does
-// not depend on any floating-point rounding mode:
+// The scale byte comes from the bit pattern of the block's largest magnitude;
+// elements are rounded by the hardware conversion on exactly scaled values:
 //   scale byte = 127 for an all-zero block, else clamp(floor(log2 amax) - 8,
 //                -127, 127) + 127, which is max(0, biased exponent of amax - 8)
 //                (subnormal maxima land on the lower clamp)
@@ -25,43 +25,36 @@ __device__ __forceinline__ uint32_t mx_scale_byte_f32(uint32_t amax_bits /* |fp3
     return mx_scale_from_exp(amax_bits >> 23, amax_bits == 0);
 }
 
-// E4M3FN code of sign * V * 2^X times 2^-e (V an integer significand).
-__device__ __forceinline__ uint32_t e4m3_from_parts(uint32_t sign, uint32_t V, int X) {
-    uint32_t code = 0;
-    if (V != 0) {
-        const int bl = 32 - __clz(V);                    // bit length of V
-        const int B = bl - 1 + X;                        // binade: floor(log2 |value|)
-        const int Qe = B < -6 ? -9 : B - 3;              // exponent of E4M3's quantum
-        const int shift = Qe - X;
-        uint32_t n;
-        if (shift <= 0) {
-            n = V << (-shift);
-        } else if (shift > 25) {
-            n = 0;                                       // below half a quantum (V < 2^25)
-        } else {
-            n = V >> shift;
-            const uint32_t rem = V & ((1u << shift) - 1u), half = 1u << (shift - 1);
-            if (rem > half || (rem == half && (n & 1u))) ++n;
-        }
-        if (Qe == -9)
-            code = n;                                    // subnormal (n == 8 is the smallest normal)
-        else
-            code = (uint32_t)((B + 7) << 3) + (n - 8);   // n == 16 carries into the next binade
-        code = min(code, 0x7Eu);                         // saturate at 448
-    }
-    return code | (sign << 7);
-}
+// E4M3FN code of a finite value v times 2^-e. 2^-e is a normal float for
+// every scale exponent a block can have (e = scale byte - 127, -127 .. 119),
+// so v * 2^-e is exact wherever E4M3 can represent anything (below 2^-126 it
+// rounds to a signed zero either way); magnitudes past 448 are clamped to it
+// (saturation); and the hardware conversion (v_cvt_pk_fp8_f32: OCP E4M3FN,
+// round to nearest even, the sign of zero kept) rounds the rest. A GPU test
+// holds it to the oracle's rule bit for bit for every finite bf16 pattern at
+// every scale exponent; for fp32 inputs it was checked against a bit-level
+// integer form of the rule on 2^28 hashed patterns and on every exponent
+// field x 4,096 mantissas (E4M3's rounding bits swept) x both signs x every
+// scale exponent, with no difference.
+__device__ __forceinline__ float mx_pow2_neg(int e) { return __uint_as_float((uint32_t)(127 - e) << 23); }
+__device__ __forceinline__ float mx_clamp448(float v) { return fminf(fmaxf(v, -448.0f), 448.0f); }
 
-__device__ __forceinline__ uint32_t e4m3_encode_bf16(uint32_t b, int e) {
-    const int ev = (int)((b >> 7) & 0xFFu);
-    const uint32_t mv = b & 0x7Fu;
-    return e4m3_from_parts((b >> 15) & 1u, ev ? (0x80u | mv) : mv, (ev ? ev : 1) - 134 - e);
+// Two codes (bytes 0 and 1) of a and b, already multiplied by 2^-e.
+__device__ __forceinline__ uint32_t e4m3x2_scaled(float a, float b) {
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(mx_clamp448(a), mx_clamp448(b), 0, false) & 0xFFFFu;
 }
 
 __device__ __forceinline__ uint32_t e4m3_encode_f32(uint32_t b, int e) {
-    const int ev = (int)((b >> 23) & 0xFFu);
-    const uint32_t mv = b & 0x7FFFFFu;
-    return e4m3_from_parts(b >> 31, ev ? (0x800000u | mv) : mv, (ev ? ev : 1) - 150 - e);
+    return e4m3x2_scaled(__uint_as_float(b) * mx_pow2_neg(e), 0.0f) & 0xFFu;
+}
+__device__ __forceinline__ uint32_t e4m3_encode_bf16(uint32_t b, int e) {
+    return e4m3_encode_f32(b << 16, e);
+}
+// Four codes (bytes 0..3) of the bf16 pairs w0 = (lo, hi) and w1 = (lo, hi).
+__device__ __forceinline__ uint32_t e4m3x4_bf16(uint32_t w0, uint32_t w1, int e) {
+    const float s = mx_pow2_neg(e);
+    return e4m3x2_scaled(__uint_as_float(w0 << 16) * s, __uint_as_float(w0 & 0xFFFF0000u) * s) |
+           (e4m3x2_scaled(__uint_as_float(w1 << 16) * s, __uint_as_float(w1 & 0xFFFF0000u) * s) << 16);
 }
 
 }  // namespace mok

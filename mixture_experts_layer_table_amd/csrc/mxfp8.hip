@@ -54,10 +54,7 @@ __global__ __launch_bounds__(256) void mxfp8_quantize_kernel(const uint16_t *__r
     uint32_t packed[8];
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
-        uint32_t x = 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) x |= e4m3_encode_bf16(v[w * 4 + j], e) << (8 * j);
-        packed[w] = x;
+        packed[w] = e4m3x4_bf16(v[w * 4] | (v[w * 4 + 1] << 16), v[w * 4 + 2] | (v[w * 4 + 3] << 16), e);
     }
     uint4 *dst = reinterpret_cast<uint4 *>(elems + (b * rows + r) * K + kb * 32);
     dst[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);

@@ -63,3 +63,24 @@ def test_special_blocks():
     bits = synth.f32_to_bf16_bits(vals).reshape(1, 4, 32)
     bits[0, 2, 5] = 0x8000                                          # -0 in a zero block
     _check(bits, False)
+
+
+def test_every_finite_bf16_pattern_at_every_scale_exponent():
+    """Each block holds one element 2^(e+8) that fixes the scale exponent e
+    (-127 .. 119, every exponent a block can have) and patterns no larger in
+    magnitude: every finite bf16 pattern meets every scale it can meet."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    fin = bits[(bits & 0x7F80) != 0x7F80]
+    blocks = []
+    for e in range(-127, 120):
+        top = np.uint16(max(0, min(254, e + 135)) << 7)          # 2^(e+8) as bf16 (e = -127: the smallest normal binade)
+        vals = fin[(fin & 0x7FFF) <= top]
+        n = -(-vals.size // 31)
+        blk = np.zeros((n, 32), np.uint16)
+        blk[:, 0] = top
+        v = np.zeros(n * 31, np.uint16)
+        v[:vals.size] = vals
+        blk[:, 1:] = v.reshape(n, 31)
+        blocks.append(blk)
+    data = np.concatenate(blocks).reshape(1, -1, 32)
+    _check(data, False)
