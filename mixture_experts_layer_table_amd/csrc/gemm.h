@@ -524,23 +524,38 @@ __device__ __forceinline__ void gemm_mainloop(P &p, uint32_t lds, f32x16_t (&acc
         gemm_kloop<P, false>(p, lds, acc, live);
 }
 
+// A tile pipeline whose epilogue takes a `publish` callable (P::SPLIT_EPILOGUE
+// true) stores first what consumer tiles of the same launch read, calls
+// publish() from every wave, then stores the rest.
+template <class P, class = void>
+struct split_epilogue : std::false_type {};
+template <class P>
+struct split_epilogue<P, std::void_t<decltype(P::SPLIT_EPILOGUE)>> : std::bool_constant<P::SPLIT_EPILOGUE> {};
+
 // One tile: prologue, K loop, `between()` (e.g. a persistent workgroup's
-// claim of its next item), epilogue. Returns the constant-clock time
-// (s_memrealtime, 100 MHz) at which the K loop ended, for the item trace.
-template <class P, class F>
-__device__ __forceinline__ uint64_t gemm_tile(P &p, uint32_t lds, F &&between) {
+// claim of its next item), epilogue, and `publish()` (a persistent producer's
+// completion: barrier and release), inside the epilogue for split epilogues,
+// after it otherwise. Returns the constant-clock time (s_memrealtime,
+// 100 MHz) at which the K loop ended, for the item trace.
+template <class P, class F, class G>
+__device__ __forceinline__ uint64_t gemm_tile(P &p, uint32_t lds, F &&between, G &&publish) {
     using C = typename P::C;
     f32x16_t acc[C::FM][C::FN];
     gemm_mainloop(p, lds, acc);
     const uint64_t t_kloop = __builtin_amdgcn_s_memrealtime();
     between();
     const int wave = wave_id();
-    p.epilogue(acc, wave / C::WAVES_N, wave % C::WAVES_N);
+    if constexpr (split_epilogue<P>::value) {
+        p.epilogue(acc, wave / C::WAVES_N, wave % C::WAVES_N, publish);
+    } else {
+        p.epilogue(acc, wave / C::WAVES_N, wave % C::WAVES_N);
+        publish();
+    }
     return t_kloop;
 }
 template <class P>
 __device__ __forceinline__ uint64_t gemm_tile(P &p, uint32_t lds) {
-    return gemm_tile(p, lds, [] {});
+    return gemm_tile(p, lds, [] {}, [] {});
 }
 
 // ----------------------------------------------------------------------------- item trace

@@ -3,7 +3,8 @@
 // Forward, per ring round of mini-batches ("Mixture-of-Kittens(MoK)란?"
 // explainer, section 4 ③: a fixed ring buffer consumed in mini-batches):
 //   gather   ring[slot(g)] <- x rows in processing order          (dispatch)
-//   gate/up  h = x W_gate | x W_up per segment, SwiGLU epilogue   (a -> ring-side buffer)
+//   gate/up  h = x W_gate | x W_up per segment, SwiGLU epilogue   (a -> ring-side buffer;
+//            h and g * a, the down weight gradient's operand, -> fwd_ctx)
 //   down     y = a W_down, then the weighted combine back to token order
 //            (fused into the epilogue when k = 1; staged per macro-batch and
 //            summed over j = 0..k-1 in fp32 otherwise)
@@ -14,7 +15,9 @@
 //            Mixture-of-Kittens (MoK)" digest, English abstract)
 //   dX       dx rows = dh_g W_gate^T + dh_u W_up^T, combined back to tokens
 //   then     router-weight partials summed in ascending order, and the weight
-//            gradients per expert over its rows in (expert, f) order.
+//            gradients per expert over its rows in (expert, f) order (dW_down
+//            on a side stream from the last dy gather on, beside the last
+//            dgrad GEMMs and dW_gate | dW_up).
 // Every output element is produced by one owner with a fixed reduction order
 // and no floating-point atomics, so results are bitwise reproducible and
 // independent of mini-batch, macro-batch, ring and capacity settings.
@@ -24,6 +27,7 @@
 #include "layer_mx.h"
 #include "layer_parts.h"
 #include "persist.h"
+#include "streams.h"
 
 namespace mok {
 namespace {
@@ -46,6 +50,8 @@ struct GateUpArgs {
     int MB, H, I;
     const uint16_t *ring, *wg, *wu;
     uint16_t *h, *aring;
+    const float *topk_w;
+    uint16_t *ga;   // fwd_ctx: g * a rows in canonical order, the down weight gradient's operand
 };
 
 template <class Cfg>
@@ -60,7 +66,8 @@ struct GateUp {
     SegTile t;
     __device__ int mvalid() const { return t.mt.rows; }
     int i0, nk, H, I, MB;
-    uint16_t *h, *aring;
+    uint16_t *h, *aring, *ga;
+    RowGates<C> rg;
 
     __device__ bool setup(const Args &a, Blk b) {
         SegTile tt;
@@ -81,7 +88,9 @@ struct GateUp {
         wl.init(a.wg + eoff + i0, I, H, I - i0, a.wu + eoff + i0);
         h = a.h;
         aring = a.aring;
+        ga = a.ga;
         nk = H / C::BK;
+        rg.load(t, wave_id() / C::WAVES_N, a.v, a.topk_w);   // hidden behind the K loop
     }
     __device__ void issue(int kt, uint32_t tile) {
         xl.issue(kt * C::BK, tile);
@@ -91,47 +100,66 @@ struct GateUp {
     __device__ int wrow(int wn, int fn) const {
         return fn < C::FN / 2 ? wn * (C::WN / 2) + fn * 32 : C::BN / 2 + wn * (C::WN / 2) + (fn - C::FN / 2) * 32;
     }
-    // h = [x W_gate | x W_up] rows and a = silu(h_gate) * h_up rows, staged
-    // through LDS (FragStage): the wave's columns are 32 gate then 32 up
-    // columns of the same 32 values of i.
-    __device__ void epilogue(f32x16_t (&acc)[C::FM][C::FN], int wm, int wn) {
-        const int ib = i0 + wn * (C::WN / 2);
-        if (ib >= I) return;   // I % 64 == 0: the wave's i are all valid or all past I
-        const int lane = epi_lane();
-        staged_rows<C, C::LDS_BYTES>([&](int fm, int fn, int g4, int j) { return acc[fm][fn][g4 * 4 + j]; },
-                       [&](int fm, int r) -> uint16_t * {
-                           const int m = wm * C::WM + fm * 32 + r;
-                           if (m >= t.mt.rows) return nullptr;
-                           // gate columns go to h[.., i], up columns to h[.., I + i]
-                           const bool up = FragStage<C, C::LDS_BYTES>::pass_col(lane) >= C::WN / 2;
-                           return h + (int64_t)(t.mt.q0 + m) * 2 * I + ib + (up ? I - C::WN / 2 : 0);
-                       });
-        // a: the first half of each staged row holds the 32 values of i
+    // a = silu(h_gate) * h_up rows for the down GEMM, then publish(), then
+    // h = [x W_gate | x W_up] rows and g * a rows (the gate weight times the
+    // bf16 a the down GEMM reads), which only the backward reads: all staged
+    // through LDS (FragStage). The wave's columns are 32 gate then 32 up
+    // columns of the same 32 values of i; every wave calls publish().
+    static constexpr bool SPLIT_EPILOGUE = true;
+    template <class G>
+    __device__ void epilogue(f32x16_t (&acc)[C::FM][C::FN], int wm, int wn, G &&publish) {
         using FS = FragStage<C, C::LDS_BYTES>;
+        const int ib = i0 + wn * (C::WN / 2);
+        const bool live = ib < I;   // I % 64 == 0: the wave's i are all valid or all past I
+        const int lane = epi_lane();
         const uint32_t area = FS::area(wave_id(), 1);
-#pragma unroll
-        for (int fm = 0; fm < C::FM; ++fm) {
+        // a (then g * a) for fragment fm in the first half of each staged row
+        auto stage_a = [&](int fm, bool weighted) {
 #pragma unroll
             for (int fn = 0; fn < C::FN / 2; ++fn)
 #pragma unroll
                 for (int g4 = 0; g4 < 4; ++g4) {
-                    float av[4];
+                    float v[4];
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const float hg = acc[fm][fn][g4 * 4 + j], hu = acc[fm][fn + C::FN / 2][g4 * 4 + j];
-                        av[j] = hg * sigmoidf_(hg) * hu;
+                        v[j] = hg * sigmoidf_(hg) * hu;
+                        if (weighted) v[j] = rg.gw[fm] * bf16r(v[j]);
                     }
                     FS::put(area + FS::frag_off(fn, g4, lane),
-                            make_uint2(pack_bf16x2(av[0], av[1]), pack_bf16x2(av[2], av[3])));
+                            make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])));
                 }
+        };
+        auto store_a = [&](int fm, uint16_t *base, int64_t row0) {
 #pragma unroll
             for (int p = 0; p < FS::PASSES; ++p) {
                 const int m = wm * C::WM + fm * 32 + FS::pass_row(p, lane);
                 const int cc = FS::pass_col(lane);
                 if (m < t.mt.rows && cc < C::WN / 2)
-                    store8_nt(aring + ((int64_t)t.slot * MB + t.rowoff + m) * I + ib + cc,
-                              FS::get(area + FS::pass_off(p, lane)));
+                    store8_nt(base + (row0 + m) * I + ib + cc, FS::get(area + FS::pass_off(p, lane)));
             }
+        };
+        if (live) {
+#pragma unroll
+            for (int fm = 0; fm < C::FM; ++fm) {
+                stage_a(fm, false);
+                store_a(fm, aring, (int64_t)t.slot * MB + t.rowoff);
+            }
+        }
+        publish();
+        if (!live) return;
+        // gate columns go to h[.., i], up columns to h[.., I + i]
+        staged_rows<C, C::LDS_BYTES>([&](int fm, int fn, int g4, int j) { return acc[fm][fn][g4 * 4 + j]; },
+                                     [&](int fm, int r) -> uint16_t * {
+                                         const int m = wm * C::WM + fm * 32 + r;
+                                         if (m >= t.mt.rows) return nullptr;
+                                         const bool up = FS::pass_col(lane) >= C::WN / 2;
+                                         return h + (int64_t)(t.mt.q0 + m) * 2 * I + ib + (up ? I - C::WN / 2 : 0);
+                                     });
+#pragma unroll
+        for (int fm = 0; fm < C::FM; ++fm) {
+            stage_a(fm, true);
+            store_a(fm, ga, (int64_t)t.mt.c0);   // g * a rows are kept in canonical order
         }
     }
 };
@@ -200,7 +228,7 @@ struct DAArgs {
     int MB, H, I, S;
     const uint16_t *ring, *wd, *h;
     const float *topk_w;
-    uint16_t *dh, *ga;
+    uint16_t *dh;
     float *dgp;
 };
 
@@ -241,7 +269,7 @@ struct DA {
     }
     __device__ int wrow(int wn, int fn) const { return wn * C::WN + fn * 32; }
     // SwiGLU backward of the tile, staged through LDS per 32-row fragment
-    // (FragStage): h rows come in and dh, g*a rows leave as whole row runs.
+    // (FragStage): h rows come in and dh rows leave as whole row runs.
     __device__ void epilogue(f32x16_t (&acc)[C::FM][C::FN], int wm, int wn) {
         using FS = FragStage<C, C::LDS_BYTES>;
         const int lane = epi_lane();
@@ -249,7 +277,7 @@ struct DA {
         const int slice = t.nt * C::WAVES_N + wn;
         const int ib = i0 + wn * C::WN;
         if (ib >= I) return;   // I % 64 == 0: this wave's columns are all valid or all past I
-        const uint32_t sg = FS::area(wave_id(), 3), su = sg + FS::BYTES, sa = su + FS::BYTES;
+        const uint32_t sg = FS::area(wave_id(), 2), su = sg + FS::BYTES;
         const int cc = FS::pass_col(lane);
         uint2 hg[FS::PASSES], hu[FS::PASSES];
         auto load_h = [&](int fm, uint2 (&g)[FS::PASSES], uint2 (&u)[FS::PASSES]) {
@@ -289,7 +317,7 @@ struct DA {
                 for (int g4 = 0; g4 < 4; ++g4) {
                     const uint32_t o = FS::frag_off(fn, g4, lane);
                     const uint2 hg2 = FS::get(sg + o), hu2 = FS::get(su + o);
-                    float dhg[4], dhu[4], gav[4];
+                    float dhg[4], dhu[4];
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const float G = acc[fm][fn][g4 * 4 + j];
@@ -301,11 +329,9 @@ struct DA {
                         const float da = gw * G;
                         dhu[j] = da * sl;
                         dhg[j] = da * huv * s * (1.0f + hgv * (1.0f - s));
-                        gav[j] = gw * av;
                     }
                     FS::put(sg + o, make_uint2(pack_bf16x2(dhg[0], dhg[1]), pack_bf16x2(dhg[2], dhg[3])));
                     FS::put(su + o, make_uint2(pack_bf16x2(dhu[0], dhu[1]), pack_bf16x2(dhu[2], dhu[3])));
-                    FS::put(sa + o, make_uint2(pack_bf16x2(gav[0], gav[1]), pack_bf16x2(gav[2], gav[3])));
                 }
             __builtin_amdgcn_sched_barrier(0);
             // next fragment's h in flight while this one's rows are stored (its accumulators are dead now)
@@ -315,11 +341,10 @@ struct DA {
             for (int p = 0; p < FS::PASSES; ++p) {
                 const int m = wm * C::WM + fm * 32 + FS::pass_row(p, lane);
                 if (m < t.mt.rows) {
-                    const int64_t c = t.mt.c0 + m;   // dh and g*a rows are kept in canonical order
+                    const int64_t c = t.mt.c0 + m;   // dh rows are kept in canonical order
                     const uint32_t o = FS::pass_off(p, lane);
                     store8_nt(a.dh + c * 2 * I + ib + cc, FS::get(sg + o));
                     store8_nt(a.dh + c * 2 * I + I + ib + cc, FS::get(su + o));
-                    store8_nt(a.ga + c * I + ib + cc, FS::get(sa + o));
                 }
             }
             // lanes l and l ^ 32 hold the same row: lower half + upper half, fixed order
@@ -714,17 +739,31 @@ hipError_t bwd_round_gemms(const Plan &p, const DAArgs &aa, const DXArgs &xa, in
                                                    persistent_grid(p), st, trace_args(MOK_TRACE_BWD_GEMMS));
 }
 
-// The weight-gradient GEMMs (dW_gate | dW_up, then dW_down), in the tile family C.
-// (Running dW_down beside dW_gate | dW_up on a second stream measured no faster.)
-template <class C, bool CANON>
-hipError_t wgrad_gemms(const Plan &p, const WGUArgs &gu, const WDArgs &wda, hipStream_t st) {
-    const hipError_t e = launch_gemm<WGU<C, CANON>>(
-        "wgrad_gate_up", dim3((unsigned)(ceil_div(2 * p.I, C::BN) * ceil_div(p.H, C::BM) * p.E)), gu, st,
-        MOK_TRACE_WGRAD_GATE_UP);
-    if (e != hipSuccess) return e;
-    return launch_gemm<WD<C, CANON>>(
-        "wgrad_down", dim3((unsigned)(ceil_div(p.H, C::BN) * ceil_div(p.I, C::BM) * p.E)), wda, st,
-        MOK_TRACE_WGRAD_DOWN);
+// The weight-gradient GEMMs, dW_gate | dW_up and dW_down, in the tile family
+// chosen by the plan; CANON: x and dy rows read from their canonical copies.
+hipError_t wgrad_gate_up(const Plan &p, const WGUArgs &gu, hipStream_t st) {
+    auto run = [&](auto c, auto canon) {
+        using C = decltype(c);
+        return launch_gemm<WGU<C, decltype(canon)::value>>(
+            "wgrad_gate_up", dim3((unsigned)(ceil_div(2 * p.I, C::BN) * ceil_div(p.H, C::BM) * p.E)), gu, st,
+            MOK_TRACE_WGRAD_GATE_UP);
+    };
+    if (p.keep_canonical && !gu.xc) return hipErrorInvalidValue;   // not reachable: derives from validated buffers
+    if (p.tile.BM == CfgS::BM)
+        return p.keep_canonical ? run(CfgW{}, std::true_type{}) : run(CfgW{}, std::false_type{});
+    return p.keep_canonical ? run(CfgA{}, std::true_type{}) : run(CfgA{}, std::false_type{});
+}
+hipError_t wgrad_down(const Plan &p, const WDArgs &wda, hipStream_t st) {
+    auto run = [&](auto c, auto canon) {
+        using C = decltype(c);
+        return launch_gemm<WD<C, decltype(canon)::value>>(
+            "wgrad_down", dim3((unsigned)(ceil_div(p.H, C::BN) * ceil_div(p.I, C::BM) * p.E)), wda, st,
+            MOK_TRACE_WGRAD_DOWN);
+    };
+    if (p.keep_canonical && !wda.dyc) return hipErrorInvalidValue;   // not reachable: derives from validated buffers
+    if (p.tile.BM == CfgS::BM)
+        return p.keep_canonical ? run(CfgW{}, std::true_type{}) : run(CfgW{}, std::false_type{});
+    return p.keep_canonical ? run(CfgA{}, std::true_type{}) : run(CfgA{}, std::false_type{});
 }
 
 }  // namespace
@@ -742,6 +781,7 @@ mok_status launch_forward(const Plan &p, const void *schedule, void *workspace, 
     uint16_t *aring = reinterpret_cast<uint16_t *>(ws + p.w_aring);
     uint16_t *stage = reinterpret_cast<uint16_t *>(ws + p.w_stage);
     uint16_t *h = reinterpret_cast<uint16_t *>(static_cast<char *>(fwd_ctx) + p.c_h);
+    uint16_t *ga_rows = reinterpret_cast<uint16_t *>(static_cast<char *>(fwd_ctx) + p.c_ga);
     // x rows saved in canonical order for the weight gradients (null when the plan keeps none)
     uint16_t *xc = p.keep_canonical ? reinterpret_cast<uint16_t *>(static_cast<char *>(fwd_ctx) + p.c_xc) : nullptr;
     if (p.x_ring_is_copy && !identity) {   // the copy doubles as the ring: one write per x row
@@ -752,8 +792,8 @@ mok_status launch_forward(const Plan &p, const void *schedule, void *workspace, 
     hipError_t err = hipSuccess;
     if (whole_pass(p) && !identity) {   // one launch for the pass, ring protocol in the kernel
         const int ntg = (int)ceil_div(p.I, CfgA::BN / 2), ntd = (int)ceil_div(p.H, CfgA::BN);
-        GateUpArgs ga{v, 0, p.G, ntg, p.n_slots, p.MB, p.H, p.I, ring,
-                      static_cast<const uint16_t *>(w.w_gate), static_cast<const uint16_t *>(w.w_up), h, aring};
+        GateUpArgs ga{v, 0, p.G, ntg, p.n_slots, p.MB, p.H, p.I, ring, static_cast<const uint16_t *>(w.w_gate),
+                      static_cast<const uint16_t *>(w.w_up), h, aring, topk_w, ga_rows};
         DownArgs da{v, 0, p.G, ntd, p.n_slots, p.MB, p.H, p.I, p.k, (int)p.MT, p.nb_full, aring,
                     static_cast<const uint16_t *>(w.w_down), topk_w, out, stage};
         err = launch_pass<GatherBf16, GateUp<CfgA>, Down<CfgA>, 3, CfgA::LDS_BYTES>(
@@ -764,8 +804,8 @@ mok_status launch_forward(const Plan &p, const void *schedule, void *workspace, 
     for (const Round r : make_rounds(p, false)) {
         const dim3 sgrid((unsigned)ceil_div(p.MB, kRowsPerBlock), (unsigned)(r.g1 - r.g0));
         if (mx) {
-            if ((err = mx_forward_round(p, v, r.g0, r.g1, mtile_bound(p, r), x, w, ws, h, xc, topk_w, out, stage, st)) !=
-                hipSuccess)
+            if ((err = mx_forward_round(p, v, r.g0, r.g1, mtile_bound(p, r), x, w, ws, h, ga_rows, xc, topk_w, out,
+                                        stage, st)) != hipSuccess)
                 break;
         } else {
             {
@@ -779,8 +819,8 @@ mok_status launch_forward(const Plan &p, const void *schedule, void *workspace, 
         } else {
             const int64_t mt = mtile_bound(p, r);
             const int ntg = (int)ceil_div(p.I, CfgA::BN / 2), ntd = (int)ceil_div(p.H, CfgA::BN);
-            GateUpArgs ga{v, r.g0, r.g1, ntg, p.n_slots, p.MB, p.H, p.I, ring,
-                          static_cast<const uint16_t *>(w.w_gate), static_cast<const uint16_t *>(w.w_up), h, aring};
+            GateUpArgs ga{v, r.g0, r.g1, ntg, p.n_slots, p.MB, p.H, p.I, ring, static_cast<const uint16_t *>(w.w_gate),
+                          static_cast<const uint16_t *>(w.w_up), h, aring, topk_w, ga_rows};
             DownArgs da{v, r.g0, r.g1, ntd, p.n_slots, p.MB, p.H, p.I, p.k, (int)p.MT, p.nb_full, aring,
                         static_cast<const uint16_t *>(w.w_down), topk_w, out, stage};
             err = p.tile.BM == CfgS::BM ? fwd_round_gemms<CfgS>(p, ga, da, mt, sync, st)
@@ -810,9 +850,9 @@ mok_status launch_backward(const Plan &p, const void *schedule, void *workspace,
     uint16_t *ring = reinterpret_cast<uint16_t *>(ws + p.w_ring);
     uint16_t *stage = reinterpret_cast<uint16_t *>(ws + p.w_stage);
     uint16_t *dh = reinterpret_cast<uint16_t *>(ws + p.w_dh);
-    uint16_t *ga = reinterpret_cast<uint16_t *>(ws + p.w_ga);
     float *dgp = reinterpret_cast<float *>(ws + p.w_dgp);
     const uint16_t *h = reinterpret_cast<const uint16_t *>(static_cast<const char *>(fwd_ctx) + p.c_h);
+    const uint16_t *ga = reinterpret_cast<const uint16_t *>(static_cast<const char *>(fwd_ctx) + p.c_ga);
     const uint16_t *xc =
         p.keep_canonical ? reinterpret_cast<const uint16_t *>(static_cast<const char *>(fwd_ctx) + p.c_xc) : nullptr;
     // dy rows in canonical order for the weight gradients: the ring itself
@@ -826,10 +866,21 @@ mok_status launch_backward(const Plan &p, const void *schedule, void *workspace,
     hipError_t err = hipSuccess;
     hipStream_t wq_side = st;   // MXFP8 weight gradients: x and dy quantizers forked to a side stream
     if (p.mx_wgrad) err = mx_wgrad_begin(p, v, ws, x, dy, st, &wq_side);
+    // BF16 dW_down needs only g * a (saved by the forward) and the dy rows: it
+    // starts on a side stream once the last round's dy gather is enqueued and
+    // runs beside the last dgrad GEMMs and dW_gate | dW_up, filling their tails.
+    const WDArgs wda{v, p.H, p.I, ga, dy, dyc, dw_down};
+    hipStream_t wd_side = st;
+    bool wd_launched = false;
+    auto launch_wd_beside = [&]() -> hipError_t {
+        wd_side = side_fork(st);
+        wd_launched = true;
+        return wgrad_down(p, wda, wd_side);
+    };
     if (err != hipSuccess) {
     } else if (p.R > 0 && whole_pass(p)) {   // one launch for the dgrad pass
         const int nta = (int)ceil_div(p.I, CfgA::BN), ntx = (int)ceil_div(p.H, CfgA::BN);
-        DAArgs aa{v, 0, p.G, nta, p.n_slots, p.MB, p.H, p.I, p.dg_slices, ring, wd, h, topk_w, dh, ga, dgp};
+        DAArgs aa{v, 0, p.G, nta, p.n_slots, p.MB, p.H, p.I, p.dg_slices, ring, wd, h, topk_w, dh, dgp};
         DXArgs xa{v, 0, p.G, ntx, p.n_slots, p.H, p.I, p.k, (int)p.MT, p.nb_full, dh, wg, wu, dx, stage};
         err = launch_pass<GatherBf16, DA<CfgA>, DX<CfgA>, 2, CfgA::LDS_BYTES>(
             "bwd_pass", p, GatherBf16{v, p.n_slots, p.MB, p.H, p.k, dy, ring}, aa, xa, true, sync, st);
@@ -838,25 +889,31 @@ mok_status launch_backward(const Plan &p, const void *schedule, void *workspace,
             reduce_router_grad<<<(unsigned)ceil_div(p.R, 256), 256, 0, st>>>(v, p.dg_slices, dgp, dtopk_w);
         }
     } else if (p.R > 0) {
-        for (const Round r : make_rounds(p, true)) {
+        const std::vector<Round> rounds = make_rounds(p, true);
+        for (size_t ri = 0; ri < rounds.size(); ++ri) {
+            const Round r = rounds[ri];
+            const bool last = ri + 1 == rounds.size();
             const dim3 sgrid((unsigned)ceil_div(p.MB, kRowsPerBlock), (unsigned)(r.g1 - r.g0));
             if (mx) {
-                if ((err = mx_backward_round(p, v, r.g0, r.g1, mtile_bound(p, r), dy, w, ws, h, dyc_copy, topk_w, dx, stage,
-                                             st)) != hipSuccess)
-                    break;
+                err = mx_gather_dy(p, v, r.g0, r.g1, dy, ws, dyc_copy, st);
             } else {
-            {
                 KernelTimer tm("gather_dy", st);
                 gather_rows<<<sgrid, 256, 0, st>>>(GatherBf16{v, p.n_slots, p.MB, p.H, p.k, dy, ring, dyc_copy}, r.g0);
+                err = hipGetLastError();
             }
-            const int64_t mt = mtile_bound(p, r);
-            const int nta = (int)ceil_div(p.I, CfgA::BN), ntx = (int)ceil_div(p.H, CfgA::BN);
-            DAArgs aa{v, r.g0, r.g1, nta, p.n_slots, p.MB, p.H, p.I, p.dg_slices, ring, wd, h, topk_w, dh, ga, dgp};
-            DXArgs xa{v, r.g0, r.g1, ntx, p.n_slots, p.H, p.I, p.k, (int)p.MT, p.nb_full, dh, wg, wu, dx, stage};
-            err = p.tile.BM == CfgS::BM ? bwd_round_gemms<CfgS>(p, aa, xa, mt, sync, st)
-                                        : bwd_round_gemms<CfgA>(p, aa, xa, mt, sync, st);
+            if (err == hipSuccess && last && !p.mx_wgrad) err = launch_wd_beside();
             if (err != hipSuccess) break;
+            const int64_t mt = mtile_bound(p, r);
+            if (mx) {
+                err = mx_backward_gemms(p, v, r.g0, r.g1, mt, w, ws, h, topk_w, dx, stage, st);
+            } else {
+                const int nta = (int)ceil_div(p.I, CfgA::BN), ntx = (int)ceil_div(p.H, CfgA::BN);
+                DAArgs aa{v, r.g0, r.g1, nta, p.n_slots, p.MB, p.H, p.I, p.dg_slices, ring, wd, h, topk_w, dh, dgp};
+                DXArgs xa{v, r.g0, r.g1, ntx, p.n_slots, p.H, p.I, p.k, (int)p.MT, p.nb_full, dh, wg, wu, dx, stage};
+                err = p.tile.BM == CfgS::BM ? bwd_round_gemms<CfgS>(p, aa, xa, mt, sync, st)
+                                            : bwd_round_gemms<CfgA>(p, aa, xa, mt, sync, st);
             }
+            if (err != hipSuccess) break;
             if (p.k > 1 && r.g0 == first_minibatch(p, macro_of_minibatch(p, r.g0))) {
                 const Macro mc = macro_info(p, macro_of_minibatch(p, r.g0));
                 KernelTimer tm("combine_dx", st);
@@ -872,18 +929,14 @@ mok_status launch_backward(const Plan &p, const void *schedule, void *workspace,
     }
     if (p.mx_wgrad) {
         // after an error only the join: no fork is left open
-        const hipError_t e2 = mx_wgrad_finish(p, v, ws, wq_side, err == hipSuccess, dw_gate, dw_up, dw_down, st);
+        const hipError_t e2 = mx_wgrad_finish(p, v, ws, ga, wq_side, err == hipSuccess, dw_gate, dw_up, dw_down, st);
         if (err == hipSuccess) err = e2;
-    } else if (err == hipSuccess) {
-        const WGUArgs gu{v, p.H, p.I, x, xc, dh, dw_gate, dw_up};
-        const WDArgs wda{v, p.H, p.I, ga, dy, dyc, dw_down};
-        if (p.keep_canonical && (!xc || !dyc)) return MOK_ERROR_INVALID_VALUE;   // not reachable: both derive from validated buffers
-        if (p.keep_canonical)
-            err = p.tile.BM == CfgS::BM ? wgrad_gemms<CfgW, true>(p, gu, wda, st)
-                                        : wgrad_gemms<CfgA, true>(p, gu, wda, st);
-        else
-            err = p.tile.BM == CfgS::BM ? wgrad_gemms<CfgW, false>(p, gu, wda, st)
-                                        : wgrad_gemms<CfgA, false>(p, gu, wda, st);
+    } else {
+        if (err == hipSuccess) err = wgrad_gate_up(p, WGUArgs{v, p.H, p.I, x, xc, dh, dw_gate, dw_up}, st);
+        if (err == hipSuccess && !wd_launched) err = wgrad_down(p, wda, st);
+        // the join also after an error: no fork is left open
+        const hipError_t e2 = side_join(st, wd_side);
+        if (err == hipSuccess) err = e2;
     }
     if (err == hipSuccess) err = hipGetLastError();
     return check_hip(err, "mok_backward");

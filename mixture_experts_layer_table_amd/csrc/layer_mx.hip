@@ -139,6 +139,8 @@ struct GateUp8Args {
     const uint8_t *wg, *wgs, *wu, *wus;        // W_gate^T, W_up^T [E][I][H] and scales [E][I][H/32]
     uint16_t *h;                               // fwd_ctx h [R][2I] bf16, processing order
     uint8_t *aring;                            // a quantized along I
+    const float *topk_w;
+    uint16_t *ga;                              // fwd_ctx g * a [R][I] bf16, canonical order
 };
 
 template <class Cfg>
@@ -153,6 +155,7 @@ struct GateUp8 {
     SegTile t;
     int i0, nk;
     Args a;
+    RowGates<C> rg;
 
     __device__ bool setup(const Args &args, Blk b) {
         SegTile tt;
@@ -166,6 +169,7 @@ struct GateUp8 {
         a = args;
         const int H = args.H, I = args.I;
         i0 = t.nt * (C::BN / 2);
+        rg.load(t, wave_id() / C::WAVES_N, args.v, args.topk_w);   // hidden behind the K loop
         const uint8_t *slot = args.ring + t.slot * (int64_t)args.MB * (H + H / 32);
         xl.init(as_pairs(slot + (int64_t)t.rowoff * H), H / 2, t.mt.rows);
         const int64_t eo = (int64_t)t.mt.e * I * H + (int64_t)i0 * H;
@@ -198,8 +202,13 @@ struct GateUp8 {
                                 const bool up = FragStage<C, END>::pass_col(epi_lane()) >= C::WN / 2;
                                 return a.h + (int64_t)(t.mt.q0 + m) * 2 * I + ib0 + (up ? I - C::WN / 2 : 0);
                             });
-        // a, quantized along i: fp8 codes and one scale per 32-block, stored directly
+        // a, quantized along i (fp8 codes and one scale per 32-block, stored
+        // directly), and g * a for the down weight gradient (the gate weight
+        // times a rounded to bf16, as the BF16 forward feeds a to its down
+        // GEMM), through the first half of each staged row
+        using FS = FragStage<C, END>;
         const int lane = epi_lane();
+        const uint32_t area = FS::area(wave_id(), 1);
         uint8_t *aslot = a.aring + t.slot * (int64_t)a.MB * I * 2;
 #pragma unroll
         for (int fm = 0; fm < C::FM; ++fm) {
@@ -212,12 +221,17 @@ struct GateUp8 {
                 const int ib = ib0 + fn * 32;   // one 32-block of i
                 Block16 av;
 #pragma unroll
-                for (int g4 = 0; g4 < 4; ++g4)
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    float gav[4];
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const float hg = acc[fm][fn][g4 * 4 + j], hu = acc[fm][fn + C::FN / 2][g4 * 4 + j];
                         av.v[g4 * 4 + j] = hg * sigmoidf_(hg) * hu;
+                        gav[j] = rg.gw[fm] * bf16r(av.v[g4 * 4 + j]);
                     }
+                    FS::put(area + FS::frag_off(fn, g4, lane),
+                            make_uint2(pack_bf16x2(gav[0], gav[1]), pack_bf16x2(gav[2], gav[3])));
+                }
                 const Enc16 q8 = quantize_block16(av);
                 if (ok) {
 #pragma unroll
@@ -225,6 +239,13 @@ struct GateUp8 {
                         *reinterpret_cast<uint32_t *>(ael + ib + g4 * 8 + (lane >> 5) * 4) = q8.enc[g4];
                     if (lane < 32) asc[ib / 32] = (uint8_t)q8.scale;
                 }
+            }
+#pragma unroll
+            for (int p = 0; p < FS::PASSES; ++p) {
+                const int mr = wm * C::WM + fm * 32 + FS::pass_row(p, lane);
+                const int cc = FS::pass_col(lane);
+                if (mr < t.mt.rows && cc < C::WN / 2)
+                    store8_nt(a.ga + (int64_t)(t.mt.c0 + mr) * I + ib0 + cc, FS::get(area + FS::pass_off(p, lane)));
             }
         }
     }
@@ -298,7 +319,7 @@ struct DA8Args {
     const uint8_t *wd, *wds;                   // W_down [E][I][H] and scales [E][I][H/32]
     const uint16_t *h;
     const float *topk_w;
-    uint16_t *dh, *ga;
+    uint16_t *dh;
     float *dgp;
     uint8_t *dhq, *dhqs;
 };
@@ -365,9 +386,8 @@ struct DA8 {
             HBatch<C> h;
             h.load(a.h + (int64_t)q[fm] * 2 * I, I, ib0, lane);
             const int m = wm * C::WM + fm * 32 + (lane & 31);
-            const int64_t c = t.mt.c0 + (ok[fm] ? m : 0);   // dh and g*a rows are kept in canonical order
+            const int64_t c = t.mt.c0 + (ok[fm] ? m : 0);   // dh rows are kept in canonical order
             uint16_t *dhrow = a.dh + c * 2 * I;
-            uint16_t *garow = a.ga + c * I;
             uint8_t *qrow = a.dhq + c * 2 * I;
             uint8_t *srow = a.dhqs + c * (2 * I / 32);
             float dg = 0.0f;
@@ -378,7 +398,6 @@ struct DA8 {
 #pragma unroll
                 for (int g4 = 0; g4 < 4; ++g4) {
                     const int i = ib + g4 * 8 + (lane >> 5) * 4;
-                    float gav[4];
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const float G = acc[fm][fn][g4 * 4 + j];
@@ -390,13 +409,11 @@ struct DA8 {
                         const float da = gw[fm] * G;
                         dhu.v[g4 * 4 + j] = da * sl_;
                         dhg.v[g4 * 4 + j] = da * hu * s * (1.0f + hg * (1.0f - s));
-                        gav[j] = gw[fm] * av;
                     }
                     if (ok[fm]) {
                         store4_bf16(dhrow + i, dhg.v[g4 * 4], dhg.v[g4 * 4 + 1], dhg.v[g4 * 4 + 2], dhg.v[g4 * 4 + 3]);
                         store4_bf16(dhrow + I + i, dhu.v[g4 * 4], dhu.v[g4 * 4 + 1], dhu.v[g4 * 4 + 2],
                                     dhu.v[g4 * 4 + 3]);
-                        store4_bf16(garow + i, gav[0], gav[1], gav[2], gav[3]);
                     }
                 }
                 const Enc16 qg = quantize_block16(dhg);
@@ -739,8 +756,8 @@ hipError_t launch_gemm8(const char *name, dim3 grid, const typename P::Args &arg
 }  // namespace
 
 hipError_t mx_forward_round(const Plan &p, const SchedView &v, int g0, int g1, int64_t mt_bound,
-                            const uint16_t *x, const mok_weights &w, char *ws, uint16_t *h, uint16_t *xc,
-                            const float *topk_w, uint16_t *out, uint16_t *stage, hipStream_t st) {
+                            const uint16_t *x, const mok_weights &w, char *ws, uint16_t *h, uint16_t *ga_rows,
+                            uint16_t *xc, const float *topk_w, uint16_t *out, uint16_t *stage, hipStream_t st) {
     uint8_t *ring = reinterpret_cast<uint8_t *>(ws + p.w_ring);
     uint8_t *aring = reinterpret_cast<uint8_t *>(ws + p.w_aring);
     {
@@ -752,7 +769,7 @@ hipError_t mx_forward_round(const Plan &p, const SchedView &v, int g0, int g1, i
     if (err != hipSuccess) return err;
     const int ntg = (int)ceil_div(p.I, CfgA::BN / 2), ntd = (int)ceil_div(p.H, CfgA::BN);
     GateUp8Args ga{v, g0, g1, ntg, p.n_slots, p.MB, p.H, p.I, ring, w.gate_elems, w.gate_scales,
-                   w.up_elems, w.up_scales, h, aring};
+                   w.up_elems, w.up_scales, h, aring, topk_w, ga_rows};
     Down8Args da{v, g0, g1, ntd, p.n_slots, p.MB, p.H, p.I, p.k, (int)p.MT, p.nb_full, aring,
                  w.down_elems, w.down_scales, topk_w, out, stage};
     // One launch per GEMM: the two block-scaled tiles do not fit one persistent
@@ -761,25 +778,27 @@ hipError_t mx_forward_round(const Plan &p, const SchedView &v, int g0, int g1, i
     return launch_gemm8<Down8<CfgA>>("down", seg_grid(ntd, mt_bound), da, st);
 }
 
-hipError_t mx_backward_round(const Plan &p, const SchedView &v, int g0, int g1, int64_t mt_bound,
-                             const uint16_t *dy, const mok_weights &w, char *ws, const uint16_t *h,
-                             uint16_t *dyc, const float *topk_w, uint16_t *dx, uint16_t *stage, hipStream_t st) {
+hipError_t mx_gather_dy(const Plan &p, const SchedView &v, int g0, int g1, const uint16_t *dy, char *ws,
+                        uint16_t *dyc, hipStream_t st) {
+    uint8_t *ring = reinterpret_cast<uint8_t *>(ws + p.w_ring);
+    const dim3 sgrid((unsigned)ceil_div(p.MB, kRowsPerBlock), (unsigned)(g1 - g0));
+    KernelTimer tm("gather_dy", st);
+    gather_rows_mx<<<sgrid, 256, 0, st>>>(GatherMx{v, p.n_slots, p.MB, p.H, p.k, dy, ring, dyc}, g0);
+    return hipGetLastError();
+}
+
+hipError_t mx_backward_gemms(const Plan &p, const SchedView &v, int g0, int g1, int64_t mt_bound,
+                             const mok_weights &w, char *ws, const uint16_t *h, const float *topk_w, uint16_t *dx,
+                             uint16_t *stage, hipStream_t st) {
     uint8_t *ring = reinterpret_cast<uint8_t *>(ws + p.w_ring);
     uint16_t *dh = reinterpret_cast<uint16_t *>(ws + p.w_dh);
-    uint16_t *gav = reinterpret_cast<uint16_t *>(ws + p.w_ga);
     float *dgp = reinterpret_cast<float *>(ws + p.w_dgp);
     uint8_t *dhq = reinterpret_cast<uint8_t *>(ws + p.w_dhq);
     uint8_t *dhqs = reinterpret_cast<uint8_t *>(ws + p.w_dhq_scales);
-    {
-        const dim3 sgrid((unsigned)ceil_div(p.MB, kRowsPerBlock), (unsigned)(g1 - g0));
-        KernelTimer tm("gather_dy", st);
-        gather_rows_mx<<<sgrid, 256, 0, st>>>(GatherMx{v, p.n_slots, p.MB, p.H, p.k, dy, ring, dyc}, g0);
-    }
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
+    hipError_t err;
     const int nta = (int)ceil_div(p.I, CfgA::BN), ntx = (int)ceil_div(p.H, CfgA::BN);
     DA8Args aa{v, g0, g1, nta, p.n_slots, p.MB, p.H, p.I, p.dg_slices, ring, w.down_elems, w.down_scales, h,
-               topk_w, dh, gav, dgp, dhq, dhqs};
+               topk_w, dh, dgp, dhq, dhqs};
     DX8Args xa{v, g0, g1, ntx, p.n_slots, p.H, p.I, p.k, (int)p.MT, p.nb_full, dhq, dhqs, w.gate_elems,
                w.gate_scales, w.up_elems, w.up_scales, dx, stage};
     if ((err = launch_gemm8<DA8<CfgA>>("dA", seg_grid(nta, mt_bound), aa, st)) != hipSuccess) return err;
@@ -788,16 +807,16 @@ hipError_t mx_backward_round(const Plan &p, const SchedView &v, int g0, int g1, 
 
 namespace {
 
+// which: 0 x, 1 dh, 2 g * a (ga), 3 dy
 QuantCols quant_cols(const Plan &p, const SchedView &v, char *ws, int which, const uint16_t *x,
-                     const uint16_t *dy) {
+                     const uint16_t *dy, const uint16_t *ga = nullptr) {
     int32_t *po = reinterpret_cast<int32_t *>(ws + p.w_po);
     auto B = [&](size_t off) { return reinterpret_cast<uint8_t *>(ws + off); };
     switch (which) {
     case 0: return QuantCols{v, po, x, p.H, p.H, true, p.Kp, B(p.w_qx), B(p.w_qxs)};
     case 1: return QuantCols{v, po, reinterpret_cast<const uint16_t *>(ws + p.w_dh), 2 * (int64_t)p.I, 2 * p.I,
                              false, p.Kp, B(p.w_qdh), B(p.w_qdhs)};
-    case 2: return QuantCols{v, po, reinterpret_cast<const uint16_t *>(ws + p.w_ga), p.I, p.I, false, p.Kp,
-                             B(p.w_qga), B(p.w_qgas)};
+    case 2: return QuantCols{v, po, ga, p.I, p.I, false, p.Kp, B(p.w_qga), B(p.w_qgas)};
     default: return QuantCols{v, po, dy, p.H, p.H, true, p.Kp, B(p.w_qdy), B(p.w_qdys)};
     }
 }
@@ -830,13 +849,13 @@ hipError_t mx_wgrad_begin(const Plan &p, const SchedView &v, char *ws, const uin
     return hipGetLastError();
 }
 
-hipError_t mx_wgrad_finish(const Plan &p, const SchedView &v, char *ws, hipStream_t side, bool compute,
-                           uint16_t *dw_gate, uint16_t *dw_up, uint16_t *dw_down, hipStream_t st) {
+hipError_t mx_wgrad_finish(const Plan &p, const SchedView &v, char *ws, const uint16_t *ga, hipStream_t side,
+                           bool compute, uint16_t *dw_gate, uint16_t *dw_up, uint16_t *dw_down, hipStream_t st) {
     hipError_t err = side_join(st, side);
     if (err != hipSuccess || !compute) return err;
     if (p.R > 0) {
         launch_quant(quant_cols(p, v, ws, 1, nullptr, nullptr), p, "wgrad_quantize_dh_ga", st);
-        launch_quant(quant_cols(p, v, ws, 2, nullptr, nullptr), p, "wgrad_quantize_dh_ga", st);
+        launch_quant(quant_cols(p, v, ws, 2, nullptr, nullptr, ga), p, "wgrad_quantize_dh_ga", st);
     }
     if ((err = hipGetLastError()) != hipSuccess) return err;
     auto B = [&](size_t off) { return reinterpret_cast<uint8_t *>(ws + off); };

@@ -183,12 +183,21 @@ struct FragStage {
     static __device__ __forceinline__ uint32_t pass_off(int p, int lane) { return at(pass_row(p, lane), lane % LPR); }
 };
 
-// One wave's share of a tile leaves as rows, through its FragStage area:
-// for each 32-row fragment fm, value(fm, fn, g4, j) is the element of
-// fragment row lane % 32 at wave column fn*32 + g4*8 + 4*(lane/32) + j, and
-// row_dst(fm, r) the destination of wave column 0 of fragment row r (nullptr:
-// row not stored). Every column of the wave is stored (callers return early
-// for waves whose columns lie past the output's width).
+// Gate weight of each fragment row the lane holds (row lane % 32 of each fm),
+// loaded when a tile is set up so that the loads hide behind its K loop.
+template <class C>
+struct RowGates {
+    float gw[C::FM];
+    __device__ __forceinline__ void load(const SegTile &t, int wm, const SchedView &v, const float *topk_w) {
+        const int lane = epi_lane();
+#pragma unroll
+        for (int fm = 0; fm < C::FM; ++fm) {
+            const int m = wm * C::WM + fm * 32 + (lane & 31);
+            gw[fm] = topk_w[v.perm[t.mt.q0 + (m < t.mt.rows ? m : 0)]];
+        }
+    }
+};
+
 // 8-byte row-run store of epilogue output with the non-temporal hint: output
 // rows are not read again by this kernel, and keeping them out of the L2's
 // retained lines leaves room for the operand slices that tiles share.
@@ -200,6 +209,12 @@ __device__ __forceinline__ void store8_nt(uint16_t *p, uint2 v) {
     __builtin_nontemporal_store(w, reinterpret_cast<v2u *>(p));
 }
 
+// One wave's share of a tile leaves as rows, through its FragStage area:
+// for each 32-row fragment fm, value(fm, fn, g4, j) is the element of
+// fragment row lane % 32 at wave column fn*32 + g4*8 + 4*(lane/32) + j, and
+// row_dst(fm, r) the destination of wave column 0 of fragment row r (nullptr:
+// row not stored). Every column of the wave is stored (callers return early
+// for waves whose columns lie past the output's width).
 template <class C, size_t LDS_END, class Val, class Dst>
 __device__ __forceinline__ void staged_rows(Val value, Dst row_dst) {
     using FS = FragStage<C, LDS_END>;

@@ -247,21 +247,25 @@ __global__ __launch_bounds__(P1::C::NT) void persist_pair_kernel(typename P1::Ar
             item_tile(id, q.nt1, q.mtc, j, n);
             P1 p;
             p.init(a1, seg_tile<P1>(v, lo, j, n, a1.n_slots));
-            t_kloop = gemm_tile(p, lds, take_ticket);
+            // the release covers every wave's stores issued before it: a split
+            // epilogue issues what consumer tiles read first, the rest after
+            t_kloop = gemm_tile(p, lds, take_ticket, [&] {
+                item_done_barrier();
+                if (threadIdx.x == 0)
+                    __hip_atomic_fetch_add(&s.done[j], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            });
         } else {
             item_tile(id, q.nt2, q.mtc, j, n);
             P2 p;
             p.init(a2, seg_tile<P2>(v, lo, j, n, a2.n_slots));
-            t_kloop = gemm_tile(p, lds, take_ticket);
+            t_kloop = gemm_tile(p, lds, take_ticket, [] {});
         }
-        if (cls == 1) {
-            item_done_barrier();   // the release below covers every wave's stores
-            if (threadIdx.x == 0) __hip_atomic_fetch_add(&s.done[j], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-        } else {
-            // Nothing in this launch reads a consumer tile's output: its stores
-            // drain while the next item starts. The barrier only frees the LDS
-            // (every wave's own LDS accesses done first); stores still in flight
-            // make the next item's load-counter waits stricter, never weaker.
+        if (cls == 2 || split_epilogue<P1>::value) {
+            // Stores that nothing in this launch reads (a consumer tile's
+            // output, a split producer's second part) drain while the next item
+            // starts. The barrier only frees the LDS (every wave's own LDS
+            // accesses done first); stores still in flight make the next
+            // item's load-counter waits stricter, never weaker.
             wait_lgkm0();
             lds_barrier();
         }

@@ -129,7 +129,6 @@ mok_status make_plan(const mok_config *cfg, const mok_shape *shape, Plan *p) {
     q.w_aring = w.take((size_t)q.n_slots * q.MB * q.I * 2);
     q.w_stage = w.take((size_t)q.stage_rows * q.H * 2);
     q.w_dh = w.take((size_t)q.R * 2 * q.I * 2);
-    q.w_ga = w.take((size_t)q.R * q.I * 2);
     q.w_dgp = w.take((size_t)q.R * q.dg_slices * 4);
     {   // persistent-kernel counters: the larger of the pair layout and the whole-pass layout
         const int64_t S = std::max<int64_t>(1, std::min<int64_t>(q.n_slots, (int64_t)q.G));
@@ -175,6 +174,7 @@ mok_status make_plan(const mok_config *cfg, const mok_shape *shape, Plan *p) {
 
     Carver x;
     q.c_h = x.take((size_t)q.R * 2 * q.I * 2);
+    q.c_ga = x.take((size_t)q.R * q.I * 2);
     if (q.keep_canonical) q.c_xc = x.take((size_t)q.R * q.H * 2);
     q.c_total = x.off;
     q.fingerprint = schedule_fingerprint(q);
@@ -190,7 +190,7 @@ Plan forward_only_workspace(const Plan &p, size_t *bytes) {
     q.w_stage = w.take((size_t)q.stage_rows * q.H * 2);
     q.w_sync = w.take(4 * (size_t)(kSyncHeads + q.max_mtiles));
     // backward-only regions: none in this layout (a forward never touches them)
-    q.w_dh = q.w_ga = q.w_dgp = q.w_dhq = q.w_dhq_scales = q.w_dyc = 0;
+    q.w_dh = q.w_dgp = q.w_dhq = q.w_dhq_scales = q.w_dyc = 0;
     q.w_qx = q.w_qxs = q.w_qdh = q.w_qdhs = q.w_qga = q.w_qgas = q.w_qdy = q.w_qdys = q.w_po = 0;
     q.w_total = w.off;
     *bytes = w.off;

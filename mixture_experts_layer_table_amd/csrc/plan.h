@@ -47,7 +47,7 @@ struct Plan {
            s_segments = 0, s_chunk = 0, s_bound = 0, s_segfirst = 0, s_mtfirst = 0,
            s_mtiles = 0, s_total = 0;
     // workspace (byte offsets)
-    size_t w_ring = 0, w_aring = 0, w_stage = 0, w_dh = 0, w_ga = 0, w_dgp = 0, w_total = 0;
+    size_t w_ring = 0, w_aring = 0, w_stage = 0, w_dh = 0, w_dgp = 0, w_total = 0;
     // persistent-kernel work queues: kSyncHeads claim counters, then one
     // completion counter per m-tile of a ring round
     size_t w_sync = 0;
@@ -68,10 +68,13 @@ struct Plan {
     // mini-batch in its own slot): ring row q is canonical row q, so the
     // forward uses fwd_ctx's x copy as its ring and writes each x row once
     bool x_ring_is_copy = false;
-    // fwd_ctx (byte offsets): h [R][2I] bf16 in processing order; with BF16
-    // weight gradients and k = 1 also the x rows in canonical order, [R][H]
-    // bf16, written by the forward's gather (c_xc 0 when unused)
-    size_t c_h = 0, c_xc = 0, c_total = 0;
+    // fwd_ctx (byte offsets): h [R][2I] bf16 in processing order; g * a
+    // [R][I] bf16 in canonical order (the down weight gradient's operand,
+    // written by the gate/up epilogue so that the backward can start that
+    // gradient as soon as its dy rows are in place); with BF16 weight
+    // gradients and k = 1 also the x rows in canonical order, [R][H] bf16,
+    // written by the forward's gather (c_xc 0 when unused)
+    size_t c_h = 0, c_ga = 0, c_xc = 0, c_total = 0;
     bool keep_canonical = false;   // the two canonical copies above exist
 };
 

@@ -80,9 +80,10 @@ def test_schedule_layout_matches_oracle_sizes():
 
 
 def test_canonical_row_copies_follow_k_and_mode():
-    """fwd_ctx holds h [R][2I] bf16, plus the x rows in canonical order [R][H]
-    bf16 exactly when every routed row is its own token (k = 1) and the weight
-    gradients run in BF16; the dy copy lives in the workspace, except when one
+    """fwd_ctx holds h [R][2I] bf16 and g * a [R][I] bf16 (the down weight
+    gradient's operand, written by the forward), plus the x rows in canonical
+    order [R][H] bf16 exactly when every routed row is its own token (k = 1)
+    and the weight gradients run in BF16; the dy copy lives in the workspace, except when one
     macro-batch fits the ring (the ring then holds the dy rows in canonical
     order). With k > 1 the weight gradients read x and dy through the token
     index, and neither copy exists: a kernel reading a copy the plan did not
@@ -98,8 +99,8 @@ def test_canonical_row_copies_follow_k_and_mode():
         small = mok.MoKConfig(minibatch_rows=64, ring_bytes=small_ring, precision=prec)
         ws_big, _, cx = mok.query_sizes(big, T, H, I, E, k)
         ws_small, _, cx_small = mok.query_sizes(small, T, H, I, E, k)
-        h_bytes = align(R * 2 * I * 2)
-        assert cx == cx_small == h_bytes + (align(R * H * 2) if canon else 0), (k, prec)
+        h_bytes, ga_bytes = align(R * 2 * I * 2), align(R * I * 2)
+        assert cx == cx_small == h_bytes + ga_bytes + (align(R * H * 2) if canon else 0), (k, prec)
         if prec == mok.MOK_BF16 and canon:
             # one macro-batch in a ring that holds it: the dy rows stay in the
             # ring; two macro-batches (same ring): a dy copy in the workspace
