@@ -269,7 +269,10 @@ struct DA {
     }
     __device__ int wrow(int wn, int fn) const { return wn * C::WN + fn * 32; }
     // SwiGLU backward of the tile, staged through LDS per 32-row fragment
-    // (FragStage): h rows come in and dh rows leave as whole row runs.
+    // (FragStage): h rows come in and dh rows leave as whole row runs, through
+    // buffer descriptors over the tile's valid rows (no branches: the next
+    // fragment's h loads, issued before this fragment's stores, are then
+    // waited for with an exact count instead of behind every store).
     __device__ void epilogue(f32x16_t (&acc)[C::FM][C::FN], int wm, int wn) {
         using FS = FragStage<C, C::LDS_BYTES>;
         const int lane = epi_lane();
@@ -278,15 +281,22 @@ struct DA {
         const int ib = i0 + wn * C::WN;
         if (ib >= I) return;   // I % 64 == 0: this wave's columns are all valid or all past I
         const uint32_t sg = FS::area(wave_id(), 2), su = sg + FS::BYTES;
-        const int cc = FS::pass_col(lane);
+        const uint32_t row_bytes = 4u * (uint32_t)I;   // one h or dh row: 2I bf16
+        // h rows in processing order, dh rows in canonical order, from the tile's first row
+        const brsrc_t hres = rows_rsrc(a.h + (int64_t)t.mt.q0 * 2 * I, (uint32_t)t.mt.rows * row_bytes);
+        const brsrc_t dres = rows_rsrc(a.dh + (int64_t)t.mt.c0 * 2 * I, (uint32_t)t.mt.rows * row_bytes);
+        const brsrc_t gres = rows_rsrc(a.dgp + (int64_t)t.mt.q0 * a.S, (uint32_t)t.mt.rows * (uint32_t)a.S * 4u);
+        const uint32_t up = 2u * (uint32_t)I;   // the up half of a row, in bytes
+        // byte offset of the lane's pass-0 element of fragment 0
+        const uint32_t voff0 = (uint32_t)(wm * C::WM + FS::pass_row(0, lane)) * row_bytes +
+                               2u * (uint32_t)(ib + FS::pass_col(lane));
+        auto voff = [&](int fm, int p) { return voff0 + (uint32_t)(fm * 32 + p * FS::RPP) * row_bytes; };
         uint2 hg[FS::PASSES], hu[FS::PASSES];
-        auto load_h = [&](int fm, uint2 (&g)[FS::PASSES], uint2 (&u)[FS::PASSES]) {
+        auto load_h = [&](int fm) {
 #pragma unroll
             for (int p = 0; p < FS::PASSES; ++p) {
-                const int m = wm * C::WM + fm * 32 + FS::pass_row(p, lane);
-                const uint16_t *hrow = a.h + (int64_t)(t.mt.q0 + (m < t.mt.rows ? m : 0)) * 2 * I + ib + cc;
-                g[p] = *reinterpret_cast<const uint2 *>(hrow);
-                u[p] = *reinterpret_cast<const uint2 *>(hrow + I);
+                hg[p] = bload8(hres, voff(fm, p), 0);
+                hu[p] = bload8(hres, voff(fm, p), up);
             }
         };
         // gate weights of the lane's fragment rows (row lane % 32 of each fm), in
@@ -297,7 +307,7 @@ struct DA {
             const int mrow = wm * C::WM + fm * 32 + (lane & 31);
             gws[fm] = a.topk_w[a.v.perm[t.mt.q0 + (mrow < t.mt.rows ? mrow : 0)]];
         }
-        load_h(0, hg, hu);
+        load_h(0);
 #pragma unroll
         for (int fm = 0; fm < C::FM; ++fm) {
 #pragma unroll
@@ -306,9 +316,6 @@ struct DA {
                 FS::put(su + FS::pass_off(p, lane), hu[p]);
             }
             __builtin_amdgcn_sched_barrier(0);   // phases stay in order: keeps live ranges short
-            const int mrow = wm * C::WM + fm * 32 + (lane & 31);
-            const bool ok = mrow < t.mt.rows;
-            const int q = t.mt.q0 + (ok ? mrow : 0);
             const float gw = gws[fm];
             float dg = 0.0f;
 #pragma unroll
@@ -335,22 +342,19 @@ struct DA {
                 }
             __builtin_amdgcn_sched_barrier(0);
             // next fragment's h in flight while this one's rows are stored (its accumulators are dead now)
-            if (fm + 1 < C::FM) load_h(fm + 1, hg, hu);
+            if (fm + 1 < C::FM) load_h(fm + 1);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int p = 0; p < FS::PASSES; ++p) {
-                const int m = wm * C::WM + fm * 32 + FS::pass_row(p, lane);
-                if (m < t.mt.rows) {
-                    const int64_t c = t.mt.c0 + m;   // dh rows are kept in canonical order
-                    const uint32_t o = FS::pass_off(p, lane);
-                    store8_nt(a.dh + c * 2 * I + ib + cc, FS::get(sg + o));
-                    store8_nt(a.dh + c * 2 * I + I + ib + cc, FS::get(su + o));
-                }
+                const uint32_t o = FS::pass_off(p, lane);
+                bstore8_nt(dres, voff(fm, p), 0, FS::get(sg + o));
+                bstore8_nt(dres, voff(fm, p), up, FS::get(su + o));
             }
             // lanes l and l ^ 32 hold the same row: lower half + upper half, fixed order
             const float other = __shfl_xor(dg, 32);
             const float tot = (lane < 32) ? dg + other : other + dg;
-            if (ok && lane < 32) a.dgp[(int64_t)q * a.S + slice] = tot;
+            const int mrow = wm * C::WM + fm * 32 + (lane & 31);
+            bstore4(gres, lane < 32 ? (uint32_t)(mrow * a.S + slice) * 4u : kOutOfRange, tot);
         }
     }
 };

@@ -97,6 +97,37 @@ __device__ __forceinline__ void store4_bf16(uint16_t *p, float a, float b, float
 
 __device__ __forceinline__ float bf16r(float x) { return bf16_to_f32(f32_to_bf16(x)); }
 
+// Epilogue rows through buffer descriptors: a descriptor covers the tile's
+// valid rows only, so loads of rows past them return zeros and stores to them
+// are dropped by the range check, with no branch. A branch around a store
+// leaves the number of stores in flight unknown to the compiler, and every
+// later wait for a load then waits for all stores (s_waitcnt vmcnt(0)): the
+// stores of one fragment would hold up the next fragment's loads. Offsets
+// are in bytes.
+typedef __amdgpu_buffer_rsrc_t brsrc_t;
+__device__ __forceinline__ brsrc_t rows_rsrc(const void *base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const uint64_t u = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a) |
+                       ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32)) << 32);
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(u), 0,
+                                             __builtin_amdgcn_readfirstlane((int)bytes), kBufWord3);
+}
+typedef uint32_t u32x2v_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint2 bload8(brsrc_t r, uint32_t voff, uint32_t soff) {
+    const u32x2v_t w = __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0);
+    return make_uint2(w.x, w.y);
+}
+// non-temporal (cache policy bit 1 on gfx950): see store8_nt
+__device__ __forceinline__ void bstore8_nt(brsrc_t r, uint32_t voff, uint32_t soff, uint2 v) {
+    u32x2v_t w;
+    w.x = v.x;
+    w.y = v.y;
+    __builtin_amdgcn_raw_buffer_store_b64(w, r, (int)voff, (int)soff, 2);
+}
+__device__ __forceinline__ void bstore4(brsrc_t r, uint32_t voff, float v) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, (int)voff, 0, 0);
+}
+
 // The saved pre-activations one lane needs for one 32-row fragment of the dA
 // epilogue: for each (fn, g4) block, 4 consecutive columns i of the gate half
 // and of the up half of its row (columns >= I read as zeros). The epilogue
