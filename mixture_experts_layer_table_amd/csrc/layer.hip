@@ -109,10 +109,14 @@ struct GateUp {
     template <class G>
     __device__ void epilogue(f32x16_t (&acc)[C::FM][C::FN], int wm, int wn, G &&publish) {
         using FS = FragStage<C, C::LDS_BYTES>;
-        const int ib = i0 + wn * (C::WN / 2);
-        const bool live = ib < I;   // I % 64 == 0: the wave's i are all valid or all past I
+        // I % 64 == 0: the wave's i are all valid or all past I. The publish
+        // below waits for every store anyway, so a wave past I may skip them.
+        const bool live = i0 + wn * (C::WN / 2) < I;
+        const int ib = live ? i0 + wn * (C::WN / 2) : 0;
+        const uint32_t rows = live ? (uint32_t)t.mt.rows : 0u;
         const int lane = epi_lane();
         const uint32_t area = FS::area(wave_id(), 1);
+        rg.settle();
         // a (then g * a) for fragment fm in the first half of each staged row
         auto stage_a = [&](int fm, bool weighted) {
 #pragma unroll
@@ -130,36 +134,41 @@ struct GateUp {
                             make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])));
                 }
         };
-        auto store_a = [&](int fm, uint16_t *base, int64_t row0) {
+        // rows of I values from the tile's first row (descriptors over its
+        // valid rows); lanes holding the unused second half store nothing
+        auto store_a = [&](int fm, brsrc_t dst) {
 #pragma unroll
             for (int p = 0; p < FS::PASSES; ++p) {
                 const int m = wm * C::WM + fm * 32 + FS::pass_row(p, lane);
                 const int cc = FS::pass_col(lane);
-                if (m < t.mt.rows && cc < C::WN / 2)
-                    store8_nt(base + (row0 + m) * I + ib + cc, FS::get(area + FS::pass_off(p, lane)));
+                bstore8_nt(dst, cc < C::WN / 2 ? 2u * (uint32_t)(m * I + ib + cc) : kOutOfRange, 0,
+                           FS::get(area + FS::pass_off(p, lane)));
             }
         };
+        const uint32_t a_bytes = rows * 2u * (uint32_t)I;
         if (live) {
+            const brsrc_t adst = rows_rsrc(aring + ((int64_t)t.slot * MB + t.rowoff) * I, a_bytes);
 #pragma unroll
             for (int fm = 0; fm < C::FM; ++fm) {
                 stage_a(fm, false);
-                store_a(fm, aring, (int64_t)t.slot * MB + t.rowoff);
+                store_a(fm, adst);
             }
         }
         publish();
         if (!live) return;
         // gate columns go to h[.., i], up columns to h[.., I + i]
+        const uint32_t h_row = 4u * (uint32_t)I;
+        const uint32_t h_col = 2u * (uint32_t)(ib + (FS::pass_col(lane) >= C::WN / 2 ? I - C::WN / 2 : 0));
         staged_rows<C, C::LDS_BYTES>([&](int fm, int fn, int g4, int j) { return acc[fm][fn][g4 * 4 + j]; },
-                                     [&](int fm, int r) -> uint16_t * {
-                                         const int m = wm * C::WM + fm * 32 + r;
-                                         if (m >= t.mt.rows) return nullptr;
-                                         const bool up = FS::pass_col(lane) >= C::WN / 2;
-                                         return h + (int64_t)(t.mt.q0 + m) * 2 * I + ib + (up ? I - C::WN / 2 : 0);
+                                     rows_rsrc(h + (int64_t)t.mt.q0 * 2 * I, rows * h_row),
+                                     [&](int fm, int r) -> uint32_t {
+                                         return (uint32_t)(wm * C::WM + fm * 32 + r) * h_row + h_col;
                                      });
+        const brsrc_t gdst = rows_rsrc(ga + (int64_t)t.mt.c0 * I, a_bytes);   // canonical order
 #pragma unroll
         for (int fm = 0; fm < C::FM; ++fm) {
             stage_a(fm, true);
-            store_a(fm, ga, (int64_t)t.mt.c0);   // g * a rows are kept in canonical order
+            store_a(fm, gdst);
         }
     }
 };
@@ -215,7 +224,7 @@ struct Down {
     }
     __device__ int wrow(int wn, int fn) const { return wn * C::WN + fn * 32; }
     __device__ void epilogue(f32x16_t (&acc)[C::FM][C::FN], int wm, int wn) {
-        store_token_rows<C, C::LDS_BYTES>(acc, t, n0, wm, wn, tr, H, a.k, a.MT, a.nb_full, true, a.out, a.stage);
+        store_token_rows<C, C::LDS_BYTES>(acc, t, n0, wm, wn, tr, a.v.T, H, a.k, a.MT, a.nb_full, true, a.out, a.stage);
     }
 };
 
@@ -278,14 +287,18 @@ struct DA {
         const int lane = epi_lane();
         const int I = a.I;
         const int slice = t.nt * C::WAVES_N + wn;
-        const int ib = i0 + wn * C::WN;
-        if (ib >= I) return;   // I % 64 == 0: this wave's columns are all valid or all past I
+        // I % 64 == 0: this wave's columns are all valid or all past I. A wave
+        // past I runs the same loads and stores on empty ranges (see
+        // store_token_rows: no early return).
+        const bool live = i0 + wn * C::WN < I;
+        const int ib = live ? i0 + wn * C::WN : 0;
+        const uint32_t rows = live ? (uint32_t)t.mt.rows : 0u;
         const uint32_t sg = FS::area(wave_id(), 2), su = sg + FS::BYTES;
         const uint32_t row_bytes = 4u * (uint32_t)I;   // one h or dh row: 2I bf16
         // h rows in processing order, dh rows in canonical order, from the tile's first row
-        const brsrc_t hres = rows_rsrc(a.h + (int64_t)t.mt.q0 * 2 * I, (uint32_t)t.mt.rows * row_bytes);
-        const brsrc_t dres = rows_rsrc(a.dh + (int64_t)t.mt.c0 * 2 * I, (uint32_t)t.mt.rows * row_bytes);
-        const brsrc_t gres = rows_rsrc(a.dgp + (int64_t)t.mt.q0 * a.S, (uint32_t)t.mt.rows * (uint32_t)a.S * 4u);
+        const brsrc_t hres = rows_rsrc(a.h + (int64_t)t.mt.q0 * 2 * I, rows * row_bytes);
+        const brsrc_t dres = rows_rsrc(a.dh + (int64_t)t.mt.c0 * 2 * I, rows * row_bytes);
+        const brsrc_t gres = rows_rsrc(a.dgp + (int64_t)t.mt.q0 * a.S, rows * (uint32_t)a.S * 4u);
         const uint32_t up = 2u * (uint32_t)I;   // the up half of a row, in bytes
         // byte offset of the lane's pass-0 element of fragment 0
         const uint32_t voff0 = (uint32_t)(wm * C::WM + FS::pass_row(0, lane)) * row_bytes +
@@ -410,7 +423,7 @@ struct DX {
     }
     __device__ int wrow(int wn, int fn) const { return wn * C::WN + fn * 32; }
     __device__ void epilogue(f32x16_t (&acc)[C::FM][C::FN], int wm, int wn) {
-        store_token_rows<C, C::LDS_BYTES>(acc, t, n0, wm, wn, tr, a.H, a.k, a.MT, a.nb_full, false, a.dx, a.stage);
+        store_token_rows<C, C::LDS_BYTES>(acc, t, n0, wm, wn, tr, a.v.T, a.H, a.k, a.MT, a.nb_full, false, a.dx, a.stage);
     }
 };
 
@@ -471,12 +484,11 @@ struct WGU {
         const int H = a.H, I = a.I;
         const int nb = n0 + wn * C::WN;
         if (nb >= 2 * I) return;   // I % 64 == 0: the wave's columns are all gate, all up or all past 2I
-        uint16_t *base = nb < I ? a.dwg + nb : a.dwu + (nb - I);
+        uint16_t *base = (nb < I ? a.dwg + nb : a.dwu + (nb - I)) + (int64_t)e * H * I;   // expert e's rows
         staged_rows<C, C::LDS_BYTES>([&](int fm, int fn, int g4, int j) { return acc[fm][fn][g4 * 4 + j]; },
-                       [&](int fm, int r) -> uint16_t * {
-                           const int hh = h0 + wm * C::WM + fm * 32 + r;
-                           return hh < H ? base + ((int64_t)e * H + hh) * I : nullptr;
-                       });
+                                     rows_rsrc(base, 2u * (uint32_t)H * (uint32_t)I), [&](int fm, int r) -> uint32_t {
+                                         return 2u * (uint32_t)(h0 + wm * C::WM + fm * 32 + r) * (uint32_t)I;
+                                     });
     }
 };
 
@@ -532,10 +544,10 @@ struct WD {
         const int nb = n0 + wn * C::WN;
         if (nb >= H) return;   // H % 64 == 0
         staged_rows<C, C::LDS_BYTES>([&](int fm, int fn, int g4, int j) { return acc[fm][fn][g4 * 4 + j]; },
-                       [&](int fm, int r) -> uint16_t * {
-                           const int ii = i0 + wm * C::WM + fm * 32 + r;
-                           return ii < I ? a.dwd + ((int64_t)e * I + ii) * H + nb : nullptr;
-                       });
+                                     rows_rsrc(a.dwd + (int64_t)e * I * H + nb, 2u * (uint32_t)I * (uint32_t)H),
+                                     [&](int fm, int r) -> uint32_t {
+                                         return 2u * (uint32_t)(i0 + wm * C::WM + fm * 32 + r) * (uint32_t)H;
+                                     });
     }
 };
 

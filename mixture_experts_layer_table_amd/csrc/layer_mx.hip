@@ -194,14 +194,14 @@ struct GateUp8 {
         const int I = a.I;
         const int ib0 = i0 + wn * (C::WN / 2);
         if (ib0 >= I) return;   // I % 128 == 0: the wave's i are all valid or all past I
+        rg.settle();
         // h rows (gate columns to h[.., i], up columns to h[.., I + i]) through LDS
+        const uint32_t h_row = 4u * (uint32_t)I;
+        const uint32_t h_col =
+            2u * (uint32_t)(ib0 + (FragStage<C, END>::pass_col(epi_lane()) >= C::WN / 2 ? I - C::WN / 2 : 0));
         staged_rows<C, END>([&](int fm, int fn, int g4, int j) { return acc[fm][fn][g4 * 4 + j]; },
-                            [&](int fm, int r) -> uint16_t * {
-                                const int m = wm * C::WM + fm * 32 + r;
-                                if (m >= t.mt.rows) return nullptr;
-                                const bool up = FragStage<C, END>::pass_col(epi_lane()) >= C::WN / 2;
-                                return a.h + (int64_t)(t.mt.q0 + m) * 2 * I + ib0 + (up ? I - C::WN / 2 : 0);
-                            });
+                            rows_rsrc(a.h + (int64_t)t.mt.q0 * 2 * I, (uint32_t)t.mt.rows * h_row),
+                            [&](int fm, int r) -> uint32_t { return (uint32_t)(wm * C::WM + fm * 32 + r) * h_row + h_col; });
         // a, quantized along i (fp8 codes and one scale per 32-block, stored
         // directly), and g * a for the down weight gradient (the gate weight
         // times a rounded to bf16, as the BF16 forward feeds a to its down
@@ -671,11 +671,11 @@ struct WGU8 {
         const int H = a.H, I = a.I;
         const int nb = n0 + wn * C::WN;
         if (nb >= 2 * I) return;   // I % 128 == 0: the wave's columns are all gate, all up or all past 2I
-        uint16_t *base = nb < I ? a.dwg + nb : a.dwu + (nb - I);
+        uint16_t *base = (nb < I ? a.dwg + nb : a.dwu + (nb - I)) + (int64_t)e * H * I;   // expert e's rows
         staged_rows<C, Fp8Stage<C>::LDS_BYTES>([&](int fm, int fn, int g4, int j) { return acc[fm][fn][g4 * 4 + j]; },
-                                               [&](int fm, int r) -> uint16_t * {
-                                                   const int hh = h0 + wm * C::WM + fm * 32 + r;
-                                                   return hh < H ? base + ((int64_t)e * H + hh) * I : nullptr;
+                                               rows_rsrc(base, 2u * (uint32_t)H * (uint32_t)I),
+                                               [&](int fm, int r) -> uint32_t {
+                                                   return 2u * (uint32_t)(h0 + wm * C::WM + fm * 32 + r) * (uint32_t)I;
                                                });
     }
 };
@@ -729,9 +729,9 @@ struct WD8 {
         const int nb = n0 + wn * C::WN;
         if (nb >= H) return;   // H % 128 == 0
         staged_rows<C, Fp8Stage<C>::LDS_BYTES>([&](int fm, int fn, int g4, int j) { return acc[fm][fn][g4 * 4 + j]; },
-                                               [&](int fm, int r) -> uint16_t * {
-                                                   const int ii = i0 + wm * C::WM + fm * 32 + r;
-                                                   return ii < I ? a.dwd + ((int64_t)e * I + ii) * H + nb : nullptr;
+                                               rows_rsrc(a.dwd + (int64_t)e * I * H + nb, 2u * (uint32_t)I * (uint32_t)H),
+                                               [&](int fm, int r) -> uint32_t {
+                                                   return 2u * (uint32_t)(i0 + wm * C::WM + fm * 32 + r) * (uint32_t)H;
                                                });
     }
 };

@@ -227,6 +227,11 @@ struct RowGates {
             gw[fm] = topk_w[v.perm[t.mt.q0 + (m < t.mt.rows ? m : 0)]];
         }
     }
+    // see TokenRows::settle
+    __device__ __forceinline__ void settle() {
+#pragma unroll
+        for (int fm = 0; fm < C::FM; ++fm) asm volatile("" : "+v"(gw[fm]));
+    }
 };
 
 // 8-byte row-run store of epilogue output with the non-temporal hint: output
@@ -243,11 +248,12 @@ __device__ __forceinline__ void store8_nt(uint16_t *p, uint2 v) {
 // One wave's share of a tile leaves as rows, through its FragStage area:
 // for each 32-row fragment fm, value(fm, fn, g4, j) is the element of
 // fragment row lane % 32 at wave column fn*32 + g4*8 + 4*(lane/32) + j, and
-// row_dst(fm, r) the destination of wave column 0 of fragment row r (nullptr:
-// row not stored). Every column of the wave is stored (callers return early
-// for waves whose columns lie past the output's width).
-template <class C, size_t LDS_END, class Val, class Dst>
-__device__ __forceinline__ void staged_rows(Val value, Dst row_dst) {
+// row_off(fm, r) the byte offset in dst of wave column 0 of fragment row r,
+// as this lane stores it (an offset past dst's range, e.g. kOutOfRange: row
+// not stored). Every column of the wave is stored (callers return early for
+// waves whose columns lie past the output's width).
+template <class C, size_t LDS_END, class Val, class Off>
+__device__ __forceinline__ void staged_rows(Val value, brsrc_t dst, Off row_off) {
     using FS = FragStage<C, LDS_END>;
     const int lane = epi_lane();
     const uint32_t area = FS::area(wave_id(), 1);
@@ -263,10 +269,9 @@ __device__ __forceinline__ void staged_rows(Val value, Dst row_dst) {
                 FS::put(area + FS::frag_off(fn, g4, lane), make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])));
             }
 #pragma unroll
-        for (int p = 0; p < FS::PASSES; ++p) {
-            uint16_t *d = row_dst(fm, FS::pass_row(p, lane));
-            if (d) store8_nt(d + FS::pass_col(lane), FS::get(area + FS::pass_off(p, lane)));
-        }
+        for (int p = 0; p < FS::PASSES; ++p)
+            bstore8_nt(dst, row_off(fm, FS::pass_row(p, lane)) + 2u * (uint32_t)FS::pass_col(lane), 0,
+                       FS::get(area + FS::pass_off(p, lane)));
     }
 }
 
@@ -302,27 +307,47 @@ struct TokenRows {
 #pragma unroll
         for (int fm = 0; fm < C::FM; ++fm) gw[fm] = (weighted && k == 1) ? topk_w[tok[fm]] : 1.0f;
     }
+    // The loads are long done when the epilogue starts. Waiting for them
+    // there, before any store, lets later uses go without a wait; a first use
+    // after the epilogue's first stores would wait for those stores as well.
+    __device__ __forceinline__ void settle() {
+#pragma unroll
+        for (int fm = 0; fm < C::FM; ++fm) asm volatile("" : "+v"(tok[fm]), "+v"(gw[fm]));
+    }
 };
 
 template <class C, size_t LDS_END>
 __device__ __forceinline__ void store_token_rows(const f32x16_t (&acc)[C::FM][C::FN], const SegTile &t, int n0,
-                                                 int wm, int wn, const TokenRows<C> &tr, int H, int k, int MT,
-                                                 int nb_full, bool weighted, uint16_t *dst_k1, uint16_t *stage) {
+                                                 int wm, int wn, const TokenRows<C> &tr, int T, int H, int k,
+                                                 int MT, int nb_full, bool weighted, uint16_t *dst_k1,
+                                                 uint16_t *stage) {
+    // H % 64 == 0: the wave's columns are all valid or all past H. A wave past
+    // H runs the same stores into an empty range (no early return: every wave
+    // then issues the same number of stores, which keeps the compiler's count
+    // of stores in flight exact for the waits that follow the tile).
     const int nb = n0 + wn * C::WN;
-    if (nb >= H) return;   // H % 64 == 0: the wave's columns are all valid or all past H
+    const bool live = nb < H;
+    TokenRows<C> trs = tr;
+    trs.settle();
+    const uint32_t row_bytes = 2u * (uint32_t)H;
+    // k == 1: the whole output [T][H], rows by token; k > 1: the macro-batch's
+    // staging rows, from the tile's first row (byte sizes stay below 2^31)
     const int64_t sbase = (int64_t)k * ((t.mt.g / nb_full) * (int64_t)MT);
+    const int cb = live ? nb : 0;
+    const brsrc_t dst = k == 1 ? rows_rsrc(dst_k1 + cb, live ? (uint32_t)T * row_bytes : 0u)
+                               : rows_rsrc(stage + (t.mt.q0 - sbase) * H + cb,
+                                           live ? (uint32_t)t.mt.rows * row_bytes : 0u);
     staged_rows<C, LDS_END>(
         [&](int fm, int fn, int g4, int j) {
             const float y = acc[fm][fn][g4 * 4 + j];
-            return (weighted && k == 1) ? tr.gw[fm] * bf16r(y) : y;   // y rows are bf16
+            return (weighted && k == 1) ? trs.gw[fm] * bf16r(y) : y;   // y rows are bf16
         },
-        [&](int fm, int r) -> uint16_t * {
-            // every lane takes part in the shuffle (before any lane leaves): lane r holds row r's token
-            const int tok_r = k == 1 ? __shfl(tr.tok[fm], r) : 0;
+        dst, [&](int fm, int r) -> uint32_t {
             const int m = wm * C::WM + fm * 32 + r;
-            if (m >= t.mt.rows) return nullptr;
-            const int q = t.mt.q0 + m;
-            return (k == 1 ? dst_k1 + (int64_t)tok_r * H : stage + (q - sbase) * H) + nb;
+            if (k != 1) return (uint32_t)m * row_bytes;   // rows past the tile lie past dst
+            // every lane takes part in the shuffle: lane r holds row r's token
+            const int tok_r = __shfl(trs.tok[fm], r);
+            return m < t.mt.rows ? (uint32_t)tok_r * row_bytes : kOutOfRange;
         });
 }
 
@@ -332,10 +357,9 @@ __device__ __forceinline__ void store_token_rows(const f32x16_t (&acc)[C::FM][C:
                                                  int wm, int wn, const SchedView &v, int H, int k, int MT,
                                                  int nb_full, const float *topk_w, bool weighted, uint16_t *dst_k1,
                                                  uint16_t *stage) {
-    if (n0 + wn * C::WN >= H) return;
     TokenRows<C> tr;
     tr.load(t, wm, v, k, topk_w, weighted);
-    store_token_rows<C, LDS_END>(acc, t, n0, wm, wn, tr, H, k, MT, nb_full, weighted, dst_k1, stage);
+    store_token_rows<C, LDS_END>(acc, t, n0, wm, wn, tr, v.T, H, k, MT, nb_full, weighted, dst_k1, stage);
 }
 
 constexpr int kRowsPerBlock = 4;   // one 64-lane wave per row

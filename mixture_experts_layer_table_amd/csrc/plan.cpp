@@ -51,6 +51,8 @@ mok_status make_plan(const mok_config *cfg, const mok_shape *shape, Plan *p) {
     // byte offsets: x / dy / out / dx [T,H] and h / dh [R,2I] stay below 2 GiB.
     if (s.T * (int64_t)s.H * 2 >= (int64_t(1) << 31)) return MOK_ERROR_INVALID_VALUE;
     if (s.T * (int64_t)s.k * s.I * 4 >= (int64_t(1) << 31)) return MOK_ERROR_INVALID_VALUE;
+    // so does one expert's weight gradient [H][I], rows of a partial last tile included
+    if ((s.H + 256) * (int64_t)s.I * 2 >= (int64_t(1) << 31)) return MOK_ERROR_INVALID_VALUE;
     if (cfg->minibatch_rows < 16 || cfg->minibatch_rows % 16) return MOK_ERROR_INVALID_VALUE;
     if (cfg->macrobatch_tokens < 0 || cfg->ring_bytes <= 0) return MOK_ERROR_INVALID_VALUE;
     if (!(cfg->capacity_multiplier > 0.0f && cfg->capacity_multiplier <= 4.0f))

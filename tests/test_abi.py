@@ -35,7 +35,8 @@ def test_config_default():
 
 BAD_SHAPES = [dict(T=-1), dict(H=100), dict(I=96), dict(E=0), dict(k=0), dict(k=9), dict(T=1 << 31),
               dict(T=1 << 17, H=8192),              # x [T,H] bf16 reaches 2 GiB
-              dict(T=1 << 18, I=1024, k=2)]         # h [R,2I] bf16 reaches 2 GiB
+              dict(T=1 << 18, I=1024, k=2),         # h [R,2I] bf16 reaches 2 GiB
+              dict(H=32768, I=32704)]               # one expert's weight gradient [H,I] bf16 near 2 GiB
 
 
 @pytest.mark.parametrize("bad", BAD_SHAPES)
