@@ -9,11 +9,14 @@
 // provides weights quantized along K in the orientation each GEMM needs.
 //
 // Scales: per stage each tile row needs the scale bytes of its two 32-blocks.
-// Scale rows are [rows][K/32] bytes with K a multiple of 128, so the 4 bytes
-// of blocks 4s .. 4s+3 of a row form one aligned dword; every stage loads that
-// dword for each of the 2 x 256 tile rows (waves 0-3: X rows, waves 4-7: W
-// rows, one direct-to-LDS dword load per wave and stage) into a [rows][4]
-// byte area after the operand tiles. Stage kt reads bytes 2*(kt%2) + 0/1.
+// Scale rows are [rows][K/32] bytes, so the bytes of consecutive blocks of a
+// row are contiguous: they are loaded a chunk of CB blocks at a time (16
+// bytes, 8 stages, where the rows allow 16-byte loads; else 4 bytes, K a
+// multiple of 128), one row per lane, into chunk buffers after the operand
+// stages (X rows by waves 0-3, W rows by waves 4-7, one load per wave on
+// the first stage of each chunk). Loading every stage's two bytes per row
+// would cost one memory request per row and stage, as many as the operand
+// rows themselves, for a 32nd of the bytes.
 //
 // MFMA operand layout (measured): lane l supplies 32 bytes of row l%32; its
 // bytes 0..15 belong to K-block 0 and bytes 16..31 to K-block 1 of the
@@ -33,20 +36,40 @@ typedef int i32x4_t __attribute__((ext_vector_type(4)));
 template <class C>
 struct Fp8Stage {
     static_assert(C::BM == 256 && C::BN == 256 && C::NW == 8, "scale loads assume 256 x 256 tiles, 8 waves");
-    static constexpr int SC_OFF = C::X_BYTES + C::W_BYTES;   // [BM][4] X scales, then [BN][4] W scales
-    static constexpr int SC_BYTES = (C::BM + C::BN) * 4;
-    static constexpr int BYTES = C::STAGE_BYTES + SC_BYTES;
-    static constexpr size_t LDS_BYTES = (size_t)C::NSTAGE * BYTES;
+    static constexpr int BYTES = C::STAGE_BYTES;
+    static constexpr int NSCBUF = 3;                         // scale chunk buffers per operand (see ScaleLoader)
+    static constexpr int SCBUF_BYTES = 256 * 16;             // one chunk: [256 rows][CB <= 16 bytes]
+    static constexpr int SC_OFF = C::NSTAGE * BYTES;         // X chunk buffers, then W chunk buffers
+    static constexpr size_t LDS_BYTES = (size_t)SC_OFF + 2 * NSCBUF * SCBUF_BYTES;
     static constexpr int BK8 = 64;                           // fp8 values per row and stage
 };
 
-// One direct-to-LDS dword load per wave and stage: the scale dwords of 64
-// tile rows. Waves 0-3 load X rows 64w .. 64w+63, waves 4-7 W rows.
+// Scale chunks of one operand's 256 tile rows. Blocks are counted from the
+// start of the source array they come from (a W operand may switch arrays at
+// K = ksplit); chunk q of a source holds its blocks [CB q, CB q + CB), and
+// chunks are numbered in K order across sources (seq), each in buffer
+// seq % NSCBUF. The chunk is loaded with the operand loads of its first
+// stage, ahead of them, so the wait for that stage covers it.
+//
+// Buffer reuse: chunk seq + NSCBUF overwrites chunk seq's buffer. Its load
+// goes out with the loads of stage y = (first stage of chunk seq + NSCBUF),
+// at the earliest after barrier y - 4 (group 1 issues stage y at the start of
+// iteration y - 3, group 0 after barrier y - 3), and every read of stage x
+// has landed before barrier x. So chunk seq's last stage must be at most
+// y - 4: the NSCBUF - 1 = 2 chunks in between must span at least 3 stages.
+// A full chunk spans CB / 2 >= 2 stages; only the last chunk of the first
+// source (a W operand switching arrays) can be shorter, at least 1 stage,
+// and never two of those in a row: 2 + 1 >= 3.
+struct ScaleChunk {
+    uint32_t seq, pos;   // chunk number, and block of the stage's first 32-block inside it
+};
 template <class C>
 struct ScaleLoader {
     rsrc_t res, res2;
-    uint32_t voff, lds0;
-    int ksplit;   // K (elements) from which res2 holds the blocks, at K - ksplit
+    uint32_t voff;   // byte offset of the lane's row in its source
+    int ksplit;      // K (elements) from which res2 holds the blocks, at K - ksplit
+    int cbx, cbw;    // blocks per chunk of the X and the W operand (16 or 4)
+    int nq0w;        // W chunks of source 0 (before ksplit)
 
     // x/w: scale rows of the X / W operand ([rows][kbx or kbw] bytes, kb = K/32
     // of that array), nx/nw valid rows. w_hi: W rows [BN/2, BN) come from w_hi
@@ -71,14 +94,46 @@ struct ScaleLoader {
         const uint32_t bytes = (uint32_t)((int64_t)max(n, 0) * kb);
         res = make_rsrc(base, bytes);
         res2 = make_rsrc(is_w && w2 ? w2 : base, bytes);
-        ksplit = is_w && w2 ? wsplit : (1 << 30);
+        ksplit = w2 ? wsplit : (1 << 30);
         voff = (uint32_t)r * (uint32_t)kb;
-        lds0 = (uint32_t)(Fp8Stage<C>::SC_OFF + (is_w ? C::BM * 4 : 0) + (wave & 3) * 256);
+        // 16-byte chunks where every row of every source starts 16-byte aligned
+        auto a16 = [](const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
+        cbx = (kbx % 16 == 0 && a16(x)) ? 16 : 4;
+        cbw = (kbw % 16 == 0 && a16(w) && (!w_hi || a16(w_hi)) && (!w2 || a16(w2))) ? 16 : 4;
+        nq0w = w2 ? (wsplit / 32 + cbw - 1) / cbw : 0;
     }
-    __device__ void issue(int k0, uint32_t stage) const {
-        const bool second = k0 >= ksplit;
-        const uint32_t soff = (uint32_t)(((second ? k0 - ksplit : k0) >> 7) << 2);
-        load_lds4(second ? res2 : res, voff, soff, stage + lds0);
+    __device__ __forceinline__ ScaleChunk chunk_x(int kt) const {
+        const uint32_t b = (uint32_t)kt * 2u;
+        return ScaleChunk{b / (uint32_t)cbx, b % (uint32_t)cbx};
+    }
+    __device__ __forceinline__ ScaleChunk chunk_w(int kt) const {
+        const int k0 = kt * Fp8Stage<C>::BK8;
+        if (k0 < ksplit) {
+            const uint32_t b = (uint32_t)k0 / 32u;
+            return ScaleChunk{b / (uint32_t)cbw, b % (uint32_t)cbw};
+        }
+        const uint32_t b = (uint32_t)(k0 - ksplit) / 32u;
+        return ScaleChunk{(uint32_t)nq0w + b / (uint32_t)cbw, b % (uint32_t)cbw};
+    }
+    // LDS address of chunk c's buffer for the X (w = false) or W operand
+    static __device__ __forceinline__ uint32_t buffer(uint32_t lds, bool w, uint32_t seq) {
+        return lds + (uint32_t)Fp8Stage<C>::SC_OFF +
+               ((w ? (uint32_t)Fp8Stage<C>::NSCBUF : 0u) + seq % (uint32_t)Fp8Stage<C>::NSCBUF) *
+                   (uint32_t)Fp8Stage<C>::SCBUF_BYTES;
+    }
+    // Before the operand loads of stage kt: this wave's rows of the chunk that
+    // starts at kt, if one does. lds: the tile's LDS base.
+    __device__ void issue(int kt, uint32_t lds) const {
+        const bool is_w = wave_id() >= 4;
+        const ScaleChunk c = is_w ? chunk_w(kt) : chunk_x(kt);
+        if (c.pos != 0) return;
+        const int cb = is_w ? cbw : cbx;
+        const int k0 = kt * Fp8Stage<C>::BK8;
+        const bool second = is_w && k0 >= ksplit;
+        const uint32_t soff = (uint32_t)((second ? k0 - ksplit : k0) >> 5);   // first block of the chunk
+        const uint32_t dst = buffer(lds, is_w, c.seq) + (uint32_t)((wave_id() & 3) * 64 * cb);
+        if (cb == 16) load_lds16(second ? res2 : res, voff, soff, dst);
+        else load_lds4(second ? res2 : res, voff, soff, dst);
     }
 };
 
@@ -91,16 +146,19 @@ __device__ __forceinline__ i32x8_t frag8(uint32_t tile, int row) {
     return i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-// Scale byte of (tile row `row` + l%32, block l/32) for stage kt.
-__device__ __forceinline__ int scale8(uint32_t area, int row, int kt) {
+// Scale byte of (tile row `row` + l%32, block l/32 of the stage) from the
+// chunk buffer `buf` of CB-byte rows, the stage's first block at `pos`.
+__device__ __forceinline__ int scale8(uint32_t buf, int cb, uint32_t pos, int row) {
     const int l = threadIdx.x & 63;
-    const uint32_t a = area + (uint32_t)((row + (l & 31)) * 4 + 2 * (kt & 1) + (l >> 5));
+    const uint32_t a = buf + (uint32_t)((row + (l & 31)) * cb) + pos + (uint32_t)(l >> 5);
     return (int)*(const __attribute__((address_space(3))) uint8_t *)(uintptr_t)a;
 }
 
 // Block-scaled tile. P provides what gemm_tile's problems provide (C, Args,
 // nk counted in 64-wide stages, issue(kt, stage) which also issues the scale
-// load, wrow, epilogue), with LOADS_PER_STAGE counting the scale load.
+// chunk a stage starts, ahead of its operand loads, wrow, epilogue) and a
+// ScaleLoader sl; LOADS_PER_STAGE counts the operand loads only (a stage
+// that also loads a scale chunk only makes the waits stricter).
 // Same ping-pong schedule as gemm_tile: the two waves of a SIMD (wm = 0, 1)
 // run half a stage apart around one barrier per stage, so one group's MFMAs
 // cover the other's barrier wait and fragment reads.
@@ -126,15 +184,17 @@ __device__ __forceinline__ void gemm8_tile(P &p, uint32_t lds) {
     int swa[FN], sxb[FM];
     auto read_stage = [&](int kt) {
         const uint32_t st = stage(kt);
+        const ScaleChunk cw = p.sl.chunk_w(kt), cx = p.sl.chunk_x(kt);
+        const uint32_t bw = ScaleLoader<C>::buffer(lds, true, cw.seq), bx = ScaleLoader<C>::buffer(lds, false, cx.seq);
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
             wa[fn] = frag8(st + C::X_BYTES, p.wrow(wn, fn));
-            swa[fn] = scale8(st + S::SC_OFF + C::BM * 4, p.wrow(wn, fn), kt);
+            swa[fn] = scale8(bw, p.sl.cbw, cw.pos, p.wrow(wn, fn));
         }
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm) {
             xb[fm] = frag8(st, wm * C::WM + fm * 32);
-            sxb[fm] = scale8(st + S::SC_OFF, wm * C::WM + fm * 32, kt);
+            sxb[fm] = scale8(bx, p.sl.cbx, cx.pos, wm * C::WM + fm * 32);
         }
     };
     auto mma_stage = [&]() {

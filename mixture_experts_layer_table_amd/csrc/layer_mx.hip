@@ -151,7 +151,7 @@ struct GateUp8 {
     RowLoader<C, C::BM> xl;
     RowLoader<C, C::BN> wl;
     ScaleLoader<C> sl;
-    static constexpr int LOADS_PER_STAGE = RowLoader<C, C::BM>::IPW + RowLoader<C, C::BN>::IPW + 1;
+    static constexpr int LOADS_PER_STAGE = RowLoader<C, C::BM>::IPW + RowLoader<C, C::BN>::IPW;
     SegTile t;
     int i0, nk;
     Args a;
@@ -181,9 +181,9 @@ struct GateUp8 {
         nk = H / S8::BK8;
     }
     __device__ void issue(int kt, uint32_t stage) {
+        sl.issue(kt, stage - (uint32_t)((kt % C::NSTAGE) * Fp8Stage<C>::BYTES));   // chunk first: see ScaleLoader
         xl.issue(kt * C::BK, stage);
         wl.issue(kt * C::BK, stage + C::X_BYTES);
-        sl.issue(kt * S8::BK8, stage);
     }
     // gate rows of the W tile pair with the up rows BN/2 further inside one wave
     __device__ int wrow(int wn, int fn) const {
@@ -272,7 +272,7 @@ struct Down8 {
     RowLoader<C, C::BM> xl;
     RowLoader<C, C::BN> wl;
     ScaleLoader<C> sl;
-    static constexpr int LOADS_PER_STAGE = RowLoader<C, C::BM>::IPW + RowLoader<C, C::BN>::IPW + 1;
+    static constexpr int LOADS_PER_STAGE = RowLoader<C, C::BM>::IPW + RowLoader<C, C::BN>::IPW;
     SegTile t;
     int n0, nk;
     Args a;
@@ -298,9 +298,9 @@ struct Down8 {
         nk = I / S8::BK8;
     }
     __device__ void issue(int kt, uint32_t stage) {
+        sl.issue(kt, stage - (uint32_t)((kt % C::NSTAGE) * Fp8Stage<C>::BYTES));   // chunk first: see ScaleLoader
         xl.issue(kt * C::BK, stage);
         wl.issue(kt * C::BK, stage + C::X_BYTES);
-        sl.issue(kt * S8::BK8, stage);
     }
     __device__ int wrow(int wn, int fn) const { return wn * C::WN + fn * 32; }
     __device__ void epilogue(f32x16_t (&acc)[C::FM][C::FN], int wm, int wn) {
@@ -332,7 +332,7 @@ struct DA8 {
     RowLoader<C, C::BM> xl;
     RowLoader<C, C::BN> wl;
     ScaleLoader<C> sl;
-    static constexpr int LOADS_PER_STAGE = RowLoader<C, C::BM>::IPW + RowLoader<C, C::BN>::IPW + 1;
+    static constexpr int LOADS_PER_STAGE = RowLoader<C, C::BM>::IPW + RowLoader<C, C::BN>::IPW;
     SegTile t;
     int i0, nk;
     Args a;
@@ -358,9 +358,9 @@ struct DA8 {
         nk = H / S8::BK8;
     }
     __device__ void issue(int kt, uint32_t stage) {
+        sl.issue(kt, stage - (uint32_t)((kt % C::NSTAGE) * Fp8Stage<C>::BYTES));   // chunk first: see ScaleLoader
         xl.issue(kt * C::BK, stage);
         wl.issue(kt * C::BK, stage + C::X_BYTES);
-        sl.issue(kt * S8::BK8, stage);
     }
     __device__ int wrow(int wn, int fn) const { return wn * C::WN + fn * 32; }
     __device__ void epilogue(f32x16_t (&acc)[C::FM][C::FN], int wm, int wn) {
@@ -459,7 +459,7 @@ struct DX8 {
     RowLoader<C, C::BM> xl;
     RowLoader<C, C::BN> wl;
     ScaleLoader<C> sl;
-    static constexpr int LOADS_PER_STAGE = RowLoader<C, C::BM>::IPW + RowLoader<C, C::BN>::IPW + 1;
+    static constexpr int LOADS_PER_STAGE = RowLoader<C, C::BM>::IPW + RowLoader<C, C::BN>::IPW;
     SegTile t;
     int n0, nk;
     Args a;
@@ -486,9 +486,9 @@ struct DX8 {
         nk = 2 * I / S8::BK8;
     }
     __device__ void issue(int kt, uint32_t stage) {
+        sl.issue(kt, stage - (uint32_t)((kt % C::NSTAGE) * Fp8Stage<C>::BYTES));   // chunk first: see ScaleLoader
         xl.issue(kt * C::BK, stage);
         wl.issue(kt * C::BK, stage + C::X_BYTES);
-        sl.issue(kt * S8::BK8, stage);
     }
     __device__ int wrow(int wn, int fn) const { return wn * C::WN + fn * 32; }
     __device__ void epilogue(f32x16_t (&acc)[C::FM][C::FN], int wm, int wn) {
@@ -641,7 +641,7 @@ struct WGU8 {
     RowLoader<C, C::BM> xl;
     RowLoader<C, C::BN> wl;
     ScaleLoader<C> sl;
-    static constexpr int LOADS_PER_STAGE = RowLoader<C, C::BM>::IPW + RowLoader<C, C::BN>::IPW + 1;
+    static constexpr int LOADS_PER_STAGE = RowLoader<C, C::BM>::IPW + RowLoader<C, C::BN>::IPW;
     int e, h0, n0, nk;
     Args a;
 
@@ -662,9 +662,9 @@ struct WGU8 {
         return true;
     }
     __device__ void issue(int kt, uint32_t stage) {
+        sl.issue(kt, stage - (uint32_t)((kt % C::NSTAGE) * Fp8Stage<C>::BYTES));   // chunk first: see ScaleLoader
         xl.issue(kt * C::BK, stage);
         wl.issue(kt * C::BK, stage + C::X_BYTES);
-        sl.issue(kt * Fp8Stage<C>::BK8, stage);
     }
     __device__ int wrow(int wn, int fn) const { return wn * C::WN + fn * 32; }
     __device__ void epilogue(f32x16_t (&acc)[C::FM][C::FN], int wm, int wn) {
@@ -698,7 +698,7 @@ struct WD8 {
     RowLoader<C, C::BM> xl;
     RowLoader<C, C::BN> wl;
     ScaleLoader<C> sl;
-    static constexpr int LOADS_PER_STAGE = RowLoader<C, C::BM>::IPW + RowLoader<C, C::BN>::IPW + 1;
+    static constexpr int LOADS_PER_STAGE = RowLoader<C, C::BM>::IPW + RowLoader<C, C::BN>::IPW;
     int e, i0, n0, nk;
     Args a;
 
@@ -719,9 +719,9 @@ struct WD8 {
         return true;
     }
     __device__ void issue(int kt, uint32_t stage) {
+        sl.issue(kt, stage - (uint32_t)((kt % C::NSTAGE) * Fp8Stage<C>::BYTES));   // chunk first: see ScaleLoader
         xl.issue(kt * C::BK, stage);
         wl.issue(kt * C::BK, stage + C::X_BYTES);
-        sl.issue(kt * Fp8Stage<C>::BK8, stage);
     }
     __device__ int wrow(int wn, int fn) const { return wn * C::WN + fn * 32; }
     __device__ void epilogue(f32x16_t (&acc)[C::FM][C::FN], int wm, int wn) {
