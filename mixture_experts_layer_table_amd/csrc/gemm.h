@@ -166,6 +166,11 @@ __device__ __forceinline__ uint32_t trans_off(int k, int col) {
 // starting at `base`, k-step columns [k0, k0 + 32). Optional second array for
 // k >= ksplit (at k - ksplit). Each wave issues ROWS / 16 / NW instructions of
 // 16 rows each.
+//
+// K-tiled arrays (init_tiled): blocks of 32 columns, each [rows][32] (64-byte
+// rows, rows contiguous), one block after the other. A stage's tile is then
+// one contiguous run of ROWS x 64 bytes: whole 128-byte lines, where rows of
+// a row-major array are 64-byte pieces of ROWS different lines.
 template <class C, int ROWS>
 struct RowLoader {
     static constexpr int IPW = ROWS / 16 / C::NW;     // instructions per wave per stage
@@ -173,6 +178,7 @@ struct RowLoader {
     rsrc_t res, res2;
     uint32_t voff, ldb, lds0;
     int ksplit;
+    uint32_t kblock = 0;   // K-tiled: bytes from one 32-column block to the next (0: row-major)
 
     __device__ void init(const uint16_t *base, int64_t ld, int nrows, const uint16_t *base2 = nullptr,
                          int ksplit_ = 1 << 30) {
@@ -186,6 +192,22 @@ struct RowLoader {
         voff = (uint32_t)r * ldb + (uint32_t)(c << 4);
         lds0 = (uint32_t)(wave * IPW * 1024);
         ksplit = ksplit_;
+    }
+    // K-tiled array: `base` is the tile's first row in the first block; rows
+    // past the tile's valid ones read the array's other rows (their outputs
+    // are discarded) or, past `bytes` (what the array holds from `base` on),
+    // zeros.
+    __device__ void init_tiled(const void *base, uint32_t block_bytes, uint32_t bytes) {
+        res = make_rsrc(base, bytes);
+        res2 = res;
+        ldb = 64;
+        kblock = block_bytes;
+        const int wave = wave_id(), L = threadIdx.x & 63;
+        const int r = wave * IPW * 16 + (L >> 2);
+        const int c = (L & 3) ^ ((L >> 4) & 3);
+        voff = (uint32_t)r * 64u + (uint32_t)(c << 4);
+        lds0 = (uint32_t)(wave * IPW * 1024);
+        ksplit = 1 << 30;
     }
     // Rows [0, ROWS/2) of the tile from `lo`, rows [ROWS/2, ROWS) from `hi`
     // (nrows_each valid rows in each; every wave's rows lie in one half).
@@ -207,6 +229,12 @@ struct RowLoader {
     __device__ void issue(int k0, uint32_t tile) const {
         const bool second = k0 >= ksplit;
         const rsrc_t r = second ? res2 : res;
+        if (kblock) {   // the whole offset in voffset: the range check leaves soffset out
+            const uint32_t kb = (uint32_t)(k0 >> 5) * kblock;
+#pragma unroll
+            for (int i = 0; i < IPW; ++i) load_lds16(res, voff + kb + (uint32_t)(i * 1024), 0, tile + lds0 + i * 1024);
+            return;
+        }
         const uint32_t kofs = (uint32_t)((second ? k0 - ksplit : k0) * 2);
 #pragma unroll
         for (int i = 0; i < IPW; ++i) load_lds16(r, voff, kofs + (uint32_t)(i * 16) * ldb, tile + lds0 + i * 1024);

@@ -134,24 +134,29 @@ struct GateUp {
                             make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])));
                 }
         };
-        // rows of I values from the tile's first row (descriptors over its
-        // valid rows); lanes holding the unused second half store nothing
-        auto store_a = [&](int fm, brsrc_t dst) {
+        // the first half of each staged row (32 values of i); off(m, cc): byte
+        // offset of column cc of tile row m, kOutOfRange for rows not stored;
+        // lanes holding the unused second half store nothing
+        auto store_a = [&](int fm, brsrc_t dst, auto off) {
 #pragma unroll
             for (int p = 0; p < FS::PASSES; ++p) {
                 const int m = wm * C::WM + fm * 32 + FS::pass_row(p, lane);
                 const int cc = FS::pass_col(lane);
-                bstore8_nt(dst, cc < C::WN / 2 ? 2u * (uint32_t)(m * I + ib + cc) : kOutOfRange, 0,
-                           FS::get(area + FS::pass_off(p, lane)));
+                bstore8_nt(dst, cc < C::WN / 2 ? off(m, cc) : kOutOfRange, 0, FS::get(area + FS::pass_off(p, lane)));
             }
         };
         const uint32_t a_bytes = rows * 2u * (uint32_t)I;
         if (live) {
-            const brsrc_t adst = rows_rsrc(aring + ((int64_t)t.slot * MB + t.rowoff) * I, a_bytes);
+            // a-ring slot, K-tiled for the down GEMM's loads: [I/32][MB][32]
+            // bf16, so that a K-step of 256 rows is one contiguous 16 KiB run
+            const brsrc_t adst = rows_rsrc(aring + (int64_t)t.slot * MB * I, (uint32_t)MB * 2u * (uint32_t)I);
+            const uint32_t a0 = (uint32_t)(ib / 32) * (uint32_t)MB * 64u + (uint32_t)t.rowoff * 64u;
 #pragma unroll
             for (int fm = 0; fm < C::FM; ++fm) {
                 stage_a(fm, false);
-                store_a(fm, adst);
+                store_a(fm, adst, [&](int m, int cc) {
+                    return m < t.mt.rows ? a0 + (uint32_t)m * 64u + 2u * (uint32_t)cc : kOutOfRange;
+                });
             }
         }
         publish();
@@ -168,7 +173,7 @@ struct GateUp {
 #pragma unroll
         for (int fm = 0; fm < C::FM; ++fm) {
             stage_a(fm, true);
-            store_a(fm, gdst);
+            store_a(fm, gdst, [&](int m, int cc) { return 2u * (uint32_t)(m * I + ib + cc); });
         }
     }
 };
@@ -212,8 +217,10 @@ struct Down {
         a = args;
         H = args.H;
         n0 = t.nt * C::BN;
-        const int64_t row0 = (int64_t)t.slot * args.MB + t.rowoff;
-        xl.init(args.aring + row0 * args.I, args.I, t.mt.rows);
+        // a-ring slot: K-tiled, [I/32][MB][32] bf16 (see GateUp's epilogue)
+        const uint32_t slot_bytes = (uint32_t)args.MB * (uint32_t)args.I * 2u;
+        xl.init_tiled(args.aring + (int64_t)t.slot * args.MB * args.I + (int64_t)t.rowoff * 32,
+                      (uint32_t)args.MB * 64u, slot_bytes - (uint32_t)t.rowoff * 64u);
         wl.init(args.wd + (int64_t)t.mt.e * args.I * H + n0, H, args.I, H - n0);
         nk = args.I / C::BK;
         tr.load(t, wave_id() / C::WAVES_N, args.v, args.k, args.topk_w, true);   // hidden behind the K loop
