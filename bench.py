@@ -9,9 +9,10 @@ weight-gradient GEMMs). Inputs are resident in HBM before timing starts.
 
 Prints one JSON line. `value` is tokens/s where a token is a pre-routing
 token of the GPU's share (the EP-64 share stands for 2,048 tokens per step).
-Also reports the dominant kernel's roofline (per-kernel durations from HIP
-events recorded by the library on its own stream) and the CPU oracle timed on
-a bounded sample of the same workload.
+Also reports the roofline of the dominant kernel among those that run alone
+(per-kernel durations from HIP events the library records on each launch's
+stream; dW_down, which runs beside other kernels on a side stream, gets no
+rate) and the CPU oracle timed on a bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME]
 """
@@ -469,12 +470,22 @@ def main():
     fp8_kernels = ("gateup", "down", "dA", "dX", "fwd_gemms", "bwd_gemms") if mx else ()
     if mx and args.mx_wgrad:
         fp8_kernels += ("wgrad_gate_up", "wgrad_down")
+    # With BF16 weight gradients, dW_down runs on a side stream beside the last
+    # dgrad GEMMs and dW_gate | dW_up: its span includes time it shares with
+    # them, so it gets no rate, and the roofline and the GEMM utilisation use
+    # the kernels that run alone.
+    side = () if (mx and args.mx_wgrad) else ("wgrad_down",)
     for n in kernels:
         if n in fpr:
             peak = PEAK_FP8_TFLOPS if n in fp8_kernels else PEAK_BF16_TFLOPS
             kernels[n]["mfma_dtype"] = "mxfp8" if n in fp8_kernels else "bf16"
-            kernels[n]["frac_of_peak"] = round(kernels[n]["tflops"] / peak, 4)
-    dominant = max((n for n in kernels if n in fpr), key=lambda n: kernels[n]["ms_per_step"])
+            if n in side:
+                kernels[n]["beside"] = True
+                del kernels[n]["tflops"]
+            else:
+                kernels[n]["frac_of_peak"] = round(kernels[n]["tflops"] / peak, 4)
+    alone = [n for n in kernels if n in fpr and n not in side]
+    dominant = max(alone, key=lambda n: kernels[n]["ms_per_step"])
     dk = kernels[dominant]
     ach = dk["tflops"]
     dpeak = PEAK_FP8_TFLOPS if dominant in fp8_kernels else PEAK_BF16_TFLOPS
@@ -505,8 +516,9 @@ def main():
         rows_per_s=round(R / (ms_per_step * 1e-3), 1),
         tflops=round(total_flops / (ms_per_step * 1e-3) / 1e12, 1),
         mfma_util=round(peak_time_s / (ms_per_step * 1e-3), 4),
-        # the grouped GEMMs alone: the same flops at peak over their summed kernel time
-        gemm_mfma_util=round(peak_time_s / (sum(kernels[n]["ms_per_step"] for n in kernels if n in fpr) * 1e-3), 4),
+        # the grouped GEMMs that run alone: their flops at peak over their summed kernel time
+        gemm_mfma_util=round(sum(fpr[n] * R * (PEAK_FP8_TFLOPS if n in fp8_kernels else PEAK_BF16_TFLOPS) ** -1
+                                 for n in alone) / 1e12 / (sum(kernels[n]["ms_per_step"] for n in alone) * 1e-3), 4),
         schedule_share=round(sched_ms / ms_per_step, 4) if sched_ms else None,
         weight_quantize_ms=round(quant_ms, 4) if quant_ms is not None else None,
         roofline=roofline, kernels=kernels, source_digest=source_digest(),
