@@ -382,7 +382,7 @@ struct DA8 {
         for (int fm = 0; fm < C::FM; ++fm) gw[fm] = a.topk_w[a.v.perm[q[fm]]];
 #pragma unroll
         for (int fm = 0; fm < C::FM; ++fm) {
-            // one batch per fragment (the quantizer's staging leaves no room to prefetch the next)
+            // one batch per fragment: loading the next one ahead of this fragment's stores measured slower
             HBatch<C> h;
             h.load(a.h + (int64_t)q[fm] * 2 * I, I, ib0, lane);
             const int m = wm * C::WM + fm * 32 + (lane & 31);

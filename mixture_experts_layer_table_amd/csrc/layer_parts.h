@@ -128,12 +128,11 @@ __device__ __forceinline__ void bstore4(brsrc_t r, uint32_t voff, float v) {
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, (int)voff, 0, 0);
 }
 
-// The saved pre-activations one lane needs for one 32-row fragment of the dA
-// epilogue: for each (fn, g4) block, 4 consecutive columns i of the gate half
-// and of the up half of its row (columns >= I read as zeros). The epilogue
-// loads the next fragment's batch before it stores the current one's
-// results: its stores may alias these loads for all the compiler knows, so
-// loads written after them would wait for every store before them.
+// The saved pre-activations one lane needs for one 32-row fragment of the
+// MXFP8 dA epilogue: for each (fn, g4) block, 4 consecutive columns i of the
+// gate half and of the up half of its row (columns >= I read as zeros). The
+// epilogue loads one fragment's batch at a time (loading the next one ahead
+// of the current one's stores measured slower there).
 template <class C>
 struct HBatch {
     uint2 g[C::FN][4], u[C::FN][4];
