@@ -273,8 +273,9 @@ struct TransLoader {
 #pragma unroll
         for (int i = 0; i < IPW; ++i) {
             const int inst = inst0 + i, sub = inst >> 3, kq = inst & 7;
-            const bool second = split && sub >= COLS / 256;
-            const uint32_t colb = split ? (uint32_t)((sub % (COLS / 256)) * 256) : (uint32_t)(sub * 256);
+            constexpr int SUBS = COLS >= 256 ? COLS / 256 : 1;   // 256-column sub-tiles per source
+            const bool second = split && sub >= SUBS;
+            const uint32_t colb = split ? (uint32_t)((sub % SUBS) * 256) : (uint32_t)(sub * 256);
             load_lds16(second ? res2 : res, voff, (uint32_t)(k0 + kq * 4) * ldb + colb, tile + lds0 + i * 1024);
         }
     }
@@ -289,6 +290,10 @@ struct TransLoader {
 // each fetch where no wait on LDS reads follows soon: scalar loads return out
 // of order, so while one is in flight every wait for an LDS fragment becomes
 // a wait for all of them, the scalar load's memory round trip included.
+// init loads the indices of the first two issues together, so that the
+// prologue's second issue does not wait for a round trip of its own (with a
+// few k-steps per tile, as for many small experts, that wait is a large part
+// of the tile).
 template <class C, int COLS>
 struct TransIdxLoader {
     static constexpr int NINST = COLS / 128 * 8;
@@ -299,6 +304,7 @@ struct TransIdxLoader {
     const int32_t *idx;
     int n, inst0, krow;
     sidx4_t nid[IPW];   // indices of the next issue's k-rows (loaded one issue ahead)
+    sidx4_t nid1[IPW];  // indices of the second issue (k0 = BK), loaded by init
 
     __device__ void init(const int32_t *idx_, int n_, const uint16_t *base, int64_t ld, int64_t total_rows,
                          int col0) {
@@ -312,15 +318,24 @@ struct TransIdxLoader {
         krow = L >> 4;
         inst0 = wave * IPW;
         lds0 = (uint32_t)(inst0 * 1024);
-        fetch(0);
+        load(0, nid);
+        load(C::BK, nid1);
     }
     // Scalar loads of the indices of k-rows [k0, k0 + 32) this wave issues;
     // reads at most 3 ints past the expert's rows (inside the index array's buffer).
-    __device__ void fetch(int k0) {
+    __device__ void load(int k0, sidx4_t (&dst)[IPW]) const {
 #pragma unroll
         for (int i = 0; i < IPW; ++i) {
             const int kb = min(k0 + ((inst0 + i) & 7) * 4, max(n - 1, 0));
-            nid[i] = sload4(idx + kb);
+            dst[i] = sload4(idx + kb);
+        }
+    }
+    __device__ void fetch(int k0) {
+        if (k0 == C::BK) {
+#pragma unroll
+            for (int i = 0; i < IPW; ++i) nid[i] = nid1[i];
+        } else {
+            load(k0, nid);
         }
     }
     // issue(k0) uses the indices fetched for k0 (init fetches those of k0 = 0).

@@ -463,13 +463,16 @@ struct WGU {
     __device__ int mvalid() const { return a.H - h0; }
 
     __device__ bool setup(const Args &args, Blk b) {
-        if (*args.v.status) return false;
+        // the status word is read together with the expert's count and offset
+        // (one round trip); both are in bounds whatever the status
+        const int bad = *args.v.status;
         a = args;
         wgrad_tile(args.v, b.x, (2 * args.I + C::BN - 1) / C::BN, (args.H + C::BM - 1) / C::BM, e, h0, n0);
         h0 *= C::BM;
         n0 *= C::BN;
         ne = args.v.counts[e];
         off = args.v.offsets[e];
+        if (bad) return false;
         nk = (ne + C::BK - 1) / C::BK;
         if constexpr (CANON)
             xl.init(args.xc + (int64_t)off * args.H + h0, args.H, ne, args.H - h0);
@@ -523,13 +526,14 @@ struct WD {
     __device__ int mvalid() const { return a.I - i0; }
 
     __device__ bool setup(const Args &args, Blk b) {
-        if (*args.v.status) return false;
+        const int bad = *args.v.status;   // read with the count and offset, as in WGU
         a = args;
         wgrad_tile(args.v, b.x, (args.H + C::BN - 1) / C::BN, (args.I + C::BM - 1) / C::BM, e, i0, n0);
         i0 *= C::BM;
         n0 *= C::BN;
         ne = args.v.counts[e];
         off = args.v.offsets[e];
+        if (bad) return false;
         nk = (ne + C::BK - 1) / C::BK;
         if constexpr (CANON)
             wl.init(args.dyc + (int64_t)off * args.H + n0, args.H, ne, args.H - n0);
