@@ -197,13 +197,22 @@ __device__ __forceinline__ void gemm8_tile(P &p, uint32_t lds) {
             sxb[fm] = scale8(bx, p.sl.cbx, cx.pos, wm * C::WM + fm * 32);
         }
     };
+    // The empty asm after each MFMA takes its accumulator as an operand, which
+    // pins the MFMA phase where the schedule puts it. Without it the compiler
+    // sank wave group 0's MFMAs past the barrier and the next stage's fragment
+    // reads (the MFMAs touch no memory, so neither the barrier's memory clobber
+    // nor s_setprio holds them), read those fragments into a second register
+    // set and copied it back after every stage: both groups then ran their
+    // MFMAs right after the same barrier, and the dense fp8 loop took 16% longer.
     auto mma_stage = [&]() {
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
-            for (int fn = 0; fn < FN; ++fn)
+            for (int fn = 0; fn < FN; ++fn) {
                 acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wa[fn], xb[fm], acc[fm][fn], 0, 0, 0,
                                                                               swa[fn], 0, sxb[fm]);
+                asm volatile("" : "+v"(acc[fm][fn]));
+            }
     };
 #pragma unroll
     for (int s = 0; s < 3; ++s)
