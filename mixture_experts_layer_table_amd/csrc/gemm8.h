@@ -162,8 +162,10 @@ __device__ __forceinline__ int scale8(uint32_t buf, int cb, uint32_t pos, int ro
 // Same ping-pong schedule as gemm_tile: the two waves of a SIMD (wm = 0, 1)
 // run half a stage apart around one barrier per stage, so one group's MFMAs
 // cover the other's barrier wait and fragment reads.
-template <class P>
-__device__ __forceinline__ void gemm8_tile(P &p, uint32_t lds) {
+// between() runs after the K loop and publish() after the epilogue, as in
+// gemm_tile (a persistent workgroup's ticket and a producer's release).
+template <class P, class F, class G>
+__device__ __forceinline__ void gemm8_tile(P &p, uint32_t lds, F &&between, G &&publish) {
     using C = typename P::C;
     using S = Fp8Stage<C>;
     constexpr int FM = C::FM, FN = C::FN, L = P::LOADS_PER_STAGE;
@@ -249,7 +251,13 @@ __device__ __forceinline__ void gemm8_tile(P &p, uint32_t lds) {
             __builtin_amdgcn_sched_barrier(0);
         }
     }
+    between();
     p.epilogue(acc, wm, wn);
+    publish();
+}
+template <class P>
+__device__ __forceinline__ void gemm8_tile(P &p, uint32_t lds) {
+    gemm8_tile(p, lds, [] {}, [] {});
 }
 
 template <class P>

@@ -18,6 +18,7 @@
 #include "layer_mx.h"
 #include "layer_parts.h"
 #include "mx_codec.h"
+#include "persist.h"
 #include "streams.h"
 
 namespace mok {
@@ -772,10 +773,17 @@ hipError_t mx_forward_round(const Plan &p, const SchedView &v, int g0, int g1, i
                    w.up_elems, w.up_scales, h, aring, topk_w, ga_rows};
     Down8Args da{v, g0, g1, ntd, p.n_slots, p.MB, p.H, p.I, p.k, (int)p.MT, p.nb_full, aring,
                  w.down_elems, w.down_scales, topk_w, out, stage};
-    // One launch per GEMM: the two block-scaled tiles do not fit one persistent
-    // kernel's register budget (two waves per SIMD) without spilling.
-    if ((err = launch_gemm8<GateUp8<CfgA>>("gateup", seg_grid(ntg, mt_bound), ga, st)) != hipSuccess) return err;
-    return launch_gemm8<Down8<CfgA>>("down", seg_grid(ntd, mt_bound), da, st);
+    if (p.debug & MOK_DEBUG_SEPARATE_LAUNCHES) {
+        if ((err = launch_gemm8<GateUp8<CfgA>>("gateup", seg_grid(ntg, mt_bound), ga, st)) != hipSuccess) return err;
+        return launch_gemm8<Down8<CfgA>>("down", seg_grid(ntd, mt_bound), da, st);
+    }
+    // The persistent pair kernel of the BF16 rounds, with block-scaled tiles
+    // (241 registers, no spills): down tiles fill the gate/up launch's last
+    // partial wave, which the ragged m-tiles of skewed loads leave large
+    // (EP-64 share, Zipf: 0.99 -> 0.87 ms for both GEMMs).
+    return launch_pair<GateUp8<CfgA>, Down8<CfgA>, S8::LDS_BYTES>(
+        "fwd_gemms", ga, da, reinterpret_cast<int *>(ws + p.w_sync), p.max_mtiles, spin_limit(p),
+        persistent_grid(p), st, TraceArgs{nullptr, nullptr, 0, 0, MOK_TRACE_FWD_GEMMS});
 }
 
 hipError_t mx_gather_dy(const Plan &p, const SchedView &v, int g0, int g1, const uint16_t *dy, char *ws,
@@ -801,6 +809,11 @@ hipError_t mx_backward_gemms(const Plan &p, const SchedView &v, int g0, int g1, 
                topk_w, dh, dgp, dhq, dhqs};
     DX8Args xa{v, g0, g1, ntx, p.n_slots, p.H, p.I, p.k, (int)p.MT, p.nb_full, dhq, dhqs, w.gate_elems,
                w.gate_scales, w.up_elems, w.up_scales, dx, stage};
+    // Separate launches: dW_down, on the side stream, fills dA's last partial
+    // wave (528 tiles are 2.06 waves at the EP-64 share). In the persistent
+    // pair (71 registers spilled around DA8's epilogue) dA + dX ran faster,
+    // 1.13 against 1.36 ms, but dW_down then ran beside dW_gate | dW_up
+    // instead: the step 2-6% slower.
     if ((err = launch_gemm8<DA8<CfgA>>("dA", seg_grid(nta, mt_bound), aa, st)) != hipSuccess) return err;
     return launch_gemm8<DX8<CfgA>>("dX", seg_grid(ntx, mt_bound), xa, st);
 }

@@ -180,6 +180,18 @@ __device__ __forceinline__ uint64_t run_tile(P &p, uint32_t lds) {
     }
 }
 
+// One item of a pair kernel: the block-scaled pipeline for fp8 problems.
+// Returns the K loop's end time where the pipeline reports it (0 otherwise).
+template <class P, class F, class G>
+__device__ __forceinline__ uint64_t pair_tile(P &p, uint32_t lds, F &&between, G &&publish) {
+    if constexpr (P::FP8) {
+        gemm8_tile(p, lds, between, publish);
+        return 0;
+    } else {
+        return gemm_tile(p, lds, between, publish);
+    }
+}
+
 template <class P>
 __device__ __forceinline__ SegTile seg_tile(const SchedView &v, int lo, int j, int n, int64_t n_slots) {
     SegTile t;
@@ -262,7 +274,7 @@ __global__ __launch_bounds__(P1::C::NT) void persist_pair_kernel(typename P1::Ar
             p.init(a1, seg_tile<P1>(v, lo, j, n, a1.n_slots));
             // the release covers every wave's stores issued before it: a split
             // epilogue issues what consumer tiles read first, the rest after
-            t_kloop = gemm_tile(p, lds, take_ticket, [&] {
+            t_kloop = pair_tile(p, lds, take_ticket, [&] {
                 item_done_barrier();
                 if (threadIdx.x == 0)
                     __hip_atomic_fetch_add(&s.done[j], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
@@ -271,7 +283,7 @@ __global__ __launch_bounds__(P1::C::NT) void persist_pair_kernel(typename P1::Ar
             item_tile(id, q.nt2, q.mtc, j, n, q.gsz);
             P2 p;
             p.init(a2, seg_tile<P2>(v, lo, j, n, a2.n_slots));
-            t_kloop = gemm_tile(p, lds, take_ticket, [] {});
+            t_kloop = pair_tile(p, lds, take_ticket, [] {});
         }
         if (cls == 2 || split_epilogue<P1>::value) {
             // Stores that nothing in this launch reads (a consumer tile's

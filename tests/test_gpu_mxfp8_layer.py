@@ -8,7 +8,7 @@ import torch
 
 import mixture_experts_layer_table_amd as mok
 import synth
-from gpu_support import (TOL_MXFP8, DeviceInputs, compare_full, host_f64, knobs, oracle_full, run_layer,
+from gpu_support import (DEV, TOL_MXFP8, DeviceInputs, compare_full, host_f64, knobs, oracle_full, run_layer,
                          same_bits, status_word)
 from oracle import layer as L
 from oracle import mxfp8 as M
@@ -65,6 +65,37 @@ def test_bitwise_deterministic_and_knob_invariant(name):
                  dict(debug_flags=mok.MOK_DEBUG_SEPARATE_LAUNCHES)):
         print(f"[mxfp8 layer] knobs {name} {over}", flush=True)
         same_bits(first, run_layer(d, knobs(cfg, **over)))
+
+
+@pytest.mark.parametrize("name", ["mx_k2_ragged", "mx_wide"])
+def test_persistent_grid_size_does_not_change_bits(name):
+    # the forward's two GEMMs run in the persistent pair kernel: one workgroup
+    # runs every tile in claim order, a few contend for them, more than the
+    # compute units queue behind the resident ones; every grid gives the same bits
+    cfg = SMALL[name]
+    d = DeviceInputs(synth.make_inputs(cfg))
+    first = run_layer(d, knobs(cfg))
+    for n in (1, 3, 64, 300):
+        print(f"[mxfp8 layer] grid {name} {n}", flush=True)
+        same_bits(first, run_layer(d, knobs(cfg, persistent_workgroups=n)))
+
+
+def test_forced_stall_ends_the_forward():
+    # the forward's down tiles wait for their m-tiles' gate/up tiles; with every
+    # wait giving up at once the launch must end, flag the stall and leave the
+    # output unwritten (the backward's GEMMs are separate launches: no waits)
+    cfg = SMALL["mx_k2_ragged"]
+    d = DeviceInputs(synth.make_inputs(cfg))
+    q = mok.MXFP8Weights(d.wg, d.wu, d.wd)
+    c = knobs(cfg, debug_flags=mok.MOK_DEBUG_FORCE_STALL)
+    ws = mok.get_workspace(c, device=DEV, num_local_tokens=cfg.T, hidden_size=cfg.H, intermediate_size=cfg.I,
+                           num_experts=cfg.E, topk=cfg.k)
+    sched = mok.build_schedule(ws, d.ids)
+    out = torch.full((cfg.T, cfg.H), 7.0, dtype=torch.bfloat16, device=DEV)
+    mok.forward(ws, sched, d.x, d.w, q.fwd, out=out)
+    torch.cuda.synchronize()
+    assert status_word(sched) == mok.MOK_SCHEDULER_STALLED
+    assert torch.all(out == 7.0)
 
 
 @pytest.mark.skip(reason="the whole-pass mode is switched off (MOK_ERROR_UNSUPPORTED): it was present in two "
