@@ -164,8 +164,9 @@ __device__ __forceinline__ int scale8(uint32_t buf, int cb, uint32_t pos, int ro
 // cover the other's barrier wait and fragment reads.
 // between() runs after the K loop and publish() after the epilogue, as in
 // gemm_tile (a persistent workgroup's ticket and a producer's release).
+// Returns the constant-clock time at which the K loop ended (item trace).
 template <class P, class F, class G>
-__device__ __forceinline__ void gemm8_tile(P &p, uint32_t lds, F &&between, G &&publish) {
+__device__ __forceinline__ uint64_t gemm8_tile(P &p, uint32_t lds, F &&between, G &&publish) {
     using C = typename P::C;
     using S = Fp8Stage<C>;
     constexpr int FM = C::FM, FN = C::FN, L = P::LOADS_PER_STAGE;
@@ -251,9 +252,11 @@ __device__ __forceinline__ void gemm8_tile(P &p, uint32_t lds, F &&between, G &&
             __builtin_amdgcn_sched_barrier(0);
         }
     }
+    const uint64_t t_kloop = __builtin_amdgcn_s_memrealtime();
     between();
     p.epilogue(acc, wm, wn);
     publish();
+    return t_kloop;
 }
 template <class P>
 __device__ __forceinline__ void gemm8_tile(P &p, uint32_t lds) {

@@ -795,6 +795,8 @@ hipError_t wgrad_down(const Plan &p, const WDArgs &wda, hipStream_t st) {
 
 }  // namespace
 
+TraceArgs item_trace_args(int kernel) { return trace_args(kernel); }
+
 mok_status launch_forward(const Plan &p, const void *schedule, void *workspace, const uint16_t *x,
                           const float *topk_w, const mok_weights &w, uint16_t *out, void *fwd_ctx,
                           hipStream_t st) {

@@ -9,6 +9,11 @@
 
 namespace mok {
 
+struct TraceArgs;
+// The per-item trace destination for the next launch of a GEMM kernel
+// (kernel: a MOK_TRACE_* value; all null while tracing is off).
+TraceArgs item_trace_args(int kernel);
+
 // Forward round g0 .. g1-1: gather + quantize x rows into the ring (and, when
 // xc is not null, the bf16 rows at their canonical positions in xc), gate/up
 // GEMM (h and g * a -> fwd_ctx, a quantized along I -> the a-ring), down GEMM.

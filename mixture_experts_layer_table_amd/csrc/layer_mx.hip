@@ -783,7 +783,7 @@ hipError_t mx_forward_round(const Plan &p, const SchedView &v, int g0, int g1, i
     // (EP-64 share, Zipf: 0.99 -> 0.87 ms for both GEMMs).
     return launch_pair<GateUp8<CfgA>, Down8<CfgA>, S8::LDS_BYTES>(
         "fwd_gemms", ga, da, reinterpret_cast<int *>(ws + p.w_sync), p.max_mtiles, spin_limit(p),
-        persistent_grid(p), st, TraceArgs{nullptr, nullptr, 0, 0, MOK_TRACE_FWD_GEMMS});
+        persistent_grid(p), st, item_trace_args(MOK_TRACE_FWD_GEMMS));
 }
 
 hipError_t mx_gather_dy(const Plan &p, const SchedView &v, int g0, int g1, const uint16_t *dy, char *ws,

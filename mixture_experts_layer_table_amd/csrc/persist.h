@@ -180,16 +180,14 @@ __device__ __forceinline__ uint64_t run_tile(P &p, uint32_t lds) {
     }
 }
 
-// One item of a pair kernel: the block-scaled pipeline for fp8 problems.
-// Returns the K loop's end time where the pipeline reports it (0 otherwise).
+// One item of a pair kernel (the block-scaled pipeline for fp8 problems).
+// Returns the K loop's end time.
 template <class P, class F, class G>
 __device__ __forceinline__ uint64_t pair_tile(P &p, uint32_t lds, F &&between, G &&publish) {
-    if constexpr (P::FP8) {
-        gemm8_tile(p, lds, between, publish);
-        return 0;
-    } else {
+    if constexpr (P::FP8)
+        return gemm8_tile(p, lds, between, publish);
+    else
         return gemm_tile(p, lds, between, publish);
-    }
 }
 
 template <class P>

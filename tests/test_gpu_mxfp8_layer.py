@@ -80,6 +80,30 @@ def test_persistent_grid_size_does_not_change_bits(name):
         same_bits(first, run_layer(d, knobs(cfg, persistent_workgroups=n)))
 
 
+def test_item_trace_records_every_forward_tile_without_changing_bits():
+    # the measurement aid on the block-scaled pair: one record per gate/up and
+    # down tile of each forward launch, times ordered, outputs unchanged
+    cfg = SMALL["mx_k2_ragged"]
+    d = DeviceInputs(synth.make_inputs(cfg))
+    base = run_layer(d, knobs(cfg))
+    assert mok.mok_item_trace_enable(1) == mok.MOK_OK
+    try:
+        traced = run_layer(d, knobs(cfg))
+        rec, n = mok.item_trace_read()
+    finally:
+        mok.mok_item_trace_enable(0)
+    same_bits(base, traced)
+    f = rec[rec["kernel"] == mok.MOK_TRACE_FWD_GEMMS]
+    assert len(f) > 0
+    assert np.all(f["t_claim"] <= f["t_start"]) and np.all(f["t_start"] <= f["t_kloop"])
+    assert np.all(f["t_kloop"] <= f["t_end"])
+    for launch in set(f["launch"].tolist()):
+        r = f[f["launch"] == launch]
+        for cls in (1, 2):
+            items = r["item"][r["item_class"] == cls]
+            assert len(items) == len(set(items.tolist())) > 0
+
+
 def test_forced_stall_ends_the_forward():
     # the forward's down tiles wait for their m-tiles' gate/up tiles; with every
     # wait giving up at once the launch must end, flag the stall and leave the
