@@ -53,27 +53,63 @@ __global__ __launch_bounds__(kThreads) void sched_hist(const int32_t *__restrict
     for (int e = threadIdx.x; e < v.E; e += kThreads) v.chunk[blockIdx.x * v.E + e] = hist[e];
 }
 
+constexpr int kTableThreads = 1024;
+
+// Exclusive scan of a[0, n) in place by one block of kTableThreads threads
+// (each thread a contiguous run, then a scan of the run totals); returns the
+// total. Every thread of the block must call it.
+__device__ int block_exclusive_scan1(int *a, int n) {
+    __shared__ int s[kTableThreads];
+    const int tid = threadIdx.x;
+    const int per = (n + kTableThreads - 1) / kTableThreads;
+    const int lo = min(n, tid * per), hi = min(n, lo + per);
+    int x = 0;
+    for (int i = lo; i < hi; ++i) x += a[i];
+    s[tid] = x;
+    __syncthreads();
+    for (int d = 1; d < kTableThreads; d <<= 1) {
+        const int y = tid >= d ? s[tid - d] : 0;
+        __syncthreads();
+        s[tid] += y;
+        __syncthreads();
+    }
+    int r = tid ? s[tid - 1] : 0;
+    for (int i = lo; i < hi; ++i) {
+        const int t = a[i];
+        a[i] = r;
+        r += t;
+    }
+    const int tot = s[kTableThreads - 1];
+    __syncthreads();
+    return tot;
+}
+
 // Exclusive scan of each expert's chunk histogram over chunks; counts, offsets.
-__global__ __launch_bounds__(kThreads) void sched_scan(SchedView v) {
+// The chunk counts are loaded a batch at a time and the offsets come from a
+// block scan: with hundreds of experts, one thread walking them (or a chunk
+// list one dependent load at a time) was most of the schedule's time.
+__global__ __launch_bounds__(kTableThreads) void sched_scan(SchedView v) {
     if (*v.status) return;
-    for (int e = threadIdx.x; e < v.E; e += kThreads) {
+    constexpr int B = 8;
+    for (int e = threadIdx.x; e < v.E; e += kTableThreads) {
         int run = 0;
-        for (int c = 0; c < v.nchunks; ++c) {
-            const int t = v.chunk[c * v.E + e];
-            v.chunk[c * v.E + e] = run;
-            run += t;
+        for (int c0 = 0; c0 < v.nchunks; c0 += B) {
+            int t[B];
+#pragma unroll
+            for (int i = 0; i < B; ++i) t[i] = c0 + i < v.nchunks ? v.chunk[(c0 + i) * v.E + e] : 0;
+#pragma unroll
+            for (int i = 0; i < B; ++i)
+                if (c0 + i < v.nchunks) {
+                    v.chunk[(c0 + i) * v.E + e] = run;
+                    run += t[i];
+                }
         }
         v.counts[e] = run;
+        v.offsets[e] = run;
     }
     __syncthreads();
-    if (threadIdx.x == 0) {
-        int run = 0;
-        for (int e = 0; e < v.E; ++e) {
-            v.offsets[e] = run;
-            run += v.counts[e];
-        }
-        v.offsets[v.E] = run;
-    }
+    const int tot = block_exclusive_scan1(v.offsets, v.E);
+    if (threadIdx.x == 0) v.offsets[v.E] = tot;
 }
 
 // rank_e at the first routed row of each macro-batch (and at R).
@@ -114,8 +150,6 @@ __device__ int expert_at(const int32_t *M, int E, int q) {
     return lo;
 }
 
-constexpr int kTableThreads = 1024;
-
 __device__ void block_exclusive_scan2(int *a, int *b, int G, int &tot_a, int &tot_b) {
     __shared__ int sa[kTableThreads], sb[kTableThreads];
     const int tid = threadIdx.x;
@@ -153,15 +187,30 @@ __device__ void block_exclusive_scan2(int *a, int *b, int G, int &tot_a, int &to
 __global__ __launch_bounds__(kTableThreads) void sched_table(SchedView v) {
     if (*v.status) return;
     const int tid = threadIdx.x;
-    for (int m = tid; m < v.NM; m += kTableThreads) {
-        int run = m * v.MT * v.k;
-        for (int e = 0; e < v.E; ++e) {
-            const int mc = v.bound[(m + 1) * v.E + e] - v.bound[m * v.E + e];
-            v.mcounts[m * v.E + e] = mc;
-            v.moffsets[m * (v.E + 1) + e] = run;
-            run += mc;
+    if (v.E > 64 && v.NM <= 64) {   // many experts, few macro-batches: a block scan per macro-batch
+        for (int m = 0; m < v.NM; ++m) {
+            int32_t *M = v.moffsets + m * (v.E + 1);
+            for (int e = tid; e < v.E; e += kTableThreads) {
+                const int mc = v.bound[(m + 1) * v.E + e] - v.bound[m * v.E + e];
+                v.mcounts[m * v.E + e] = mc;
+                M[e] = mc;
+            }
+            __syncthreads();
+            const int base = m * v.MT * v.k, tot = block_exclusive_scan1(M, v.E);
+            for (int e = tid; e < v.E; e += kTableThreads) M[e] += base;
+            if (tid == 0) M[v.E] = base + tot;
         }
-        v.moffsets[m * (v.E + 1) + v.E] = run;
+    } else {   // one thread per macro-batch walks its experts
+        for (int m = tid; m < v.NM; m += kTableThreads) {
+            int run = m * v.MT * v.k;
+            for (int e = 0; e < v.E; ++e) {
+                const int mc = v.bound[(m + 1) * v.E + e] - v.bound[m * v.E + e];
+                v.mcounts[m * v.E + e] = mc;
+                v.moffsets[m * (v.E + 1) + e] = run;
+                run += mc;
+            }
+            v.moffsets[m * (v.E + 1) + v.E] = run;
+        }
     }
     __syncthreads();
     for (int g = tid; g < v.G; g += kTableThreads) {
@@ -303,7 +352,7 @@ mok_status launch_build_schedule(const Plan &p, const int32_t *ids, void *schedu
     sched_init<<<1, kThreads, 0, st>>>(v);
     if (p.nchunks > 0) {
         sched_hist<<<p.nchunks, kThreads, hist_lds, st>>>(ids, v);
-        sched_scan<<<1, kThreads, 0, st>>>(v);
+        sched_scan<<<1, kTableThreads, 0, st>>>(v);
         sched_bounds<<<p.NM + 1, kThreads, hist_lds, st>>>(ids, v);
     }
     sched_table<<<1, kTableThreads, 0, st>>>(v);
