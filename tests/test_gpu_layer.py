@@ -24,6 +24,9 @@ SMALL = {
                                  ring_bytes=2 * 16 * 256),
     "wide": synth.small_config("wide", T=520, H=640, I=320, E=2, k=1, minibatch_rows=160,
                                ring_bytes=1 << 22, routing="zipf"),
+    # one token: two m-tiles of one row each, every other expert empty
+    "single_token": synth.small_config("single_token", T=1, H=128, I=64, E=4, k=2, minibatch_rows=16,
+                                       ring_bytes=2 * 16 * 256),
 }
 
 

@@ -29,6 +29,9 @@ SMALL = {
     "mx_wide": _mx("mx_wide", T=520, H=640, I=384, E=2, k=1, minibatch_rows=160, ring_bytes=1 << 22,
                    routing="zipf"),
     "mx_k_eq_E": _mx("mx_k_eq_E", T=70, H=128, I=128, E=4, k=4, minibatch_rows=16, ring_bytes=2 * 16 * 132),
+    # one token: two m-tiles of one row each, every other expert empty
+    "mx_single_token": _mx("mx_single_token", T=1, H=128, I=128, E=4, k=2, minibatch_rows=16,
+                           ring_bytes=2 * 16 * 132),
 }
 
 
@@ -138,7 +141,7 @@ def test_whole_pass_flag_in_mxfp8_mode(name):
 
 # ----------------------------------------------------------------------------- MXFP8 weight gradients
 
-@pytest.mark.parametrize("name", ["mx_k2_ragged", "mx_k1_macro", "mx_wide", "mx_k_eq_E"])
+@pytest.mark.parametrize("name", ["mx_k2_ragged", "mx_k1_macro", "mx_wide", "mx_k_eq_E", "mx_single_token"])
 def test_wgrad_parity_small(name):
     """MOK_MXFP8_WGRAD: weight gradients from operands quantized along the
     expert's rows (zero-padded tails) against the oracle with the same
