@@ -124,7 +124,11 @@ typedef struct mok_config {
  * Layer shape: T rows handed to the layer (tokens; for an expert-parallel
  * share, the received routed rows with k = 1), hidden size H, expert
  * intermediate size I, E local experts, k routed rows per token.
- * H and I are multiples of 64; 1 <= k <= E; T >= 0; T*k < 2^31.
+ * H and I are multiples of 64; 1 <= k <= E <= 4096; T >= 0;
+ * T*k < 2^31. Activations are addressed with 32-bit byte offsets, so also
+ * T*H*2 < 2^31 (x, dy, out, dx), T*k*I*4 < 2^31 (h, dh) and (H+256)*I*2 <
+ * 2^31 (one expert's weight gradient). A shape outside these bounds makes
+ * every call that takes it return MOK_ERROR_INVALID_VALUE.
  */
 typedef struct mok_shape {
     int64_t T;

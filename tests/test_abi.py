@@ -36,7 +36,8 @@ def test_config_default():
 BAD_SHAPES = [dict(T=-1), dict(H=100), dict(I=96), dict(E=0), dict(k=0), dict(k=9), dict(T=1 << 31),
               dict(T=1 << 17, H=8192),              # x [T,H] bf16 reaches 2 GiB
               dict(T=1 << 18, I=1024, k=2),         # h [R,2I] bf16 reaches 2 GiB
-              dict(H=32768, I=32704)]               # one expert's weight gradient [H,I] bf16 near 2 GiB
+              dict(H=32768, I=32704),               # one expert's weight gradient [H,I] bf16 near 2 GiB
+              dict(E=4097)]                         # past the expert limit
 
 
 @pytest.mark.parametrize("bad", BAD_SHAPES)
@@ -46,6 +47,21 @@ def test_bad_shapes_rejected(bad):
     with pytest.raises(mok.MokError) as e:
         mok.query_sizes(mok.MoKConfig(minibatch_rows=32, ring_bytes=1 << 20), **s)
     assert e.value.status == mok.MOK_ERROR_INVALID_VALUE
+
+
+# the largest shapes under each 2 GiB byte bound stay accepted
+EDGE_SHAPES = [dict(T=(1 << 17) - 1, H=8192),         # x [T,H] one row short of 2 GiB
+               dict(T=(1 << 18) - 1, I=1024, k=2),    # h [R,2I] one token short of 2 GiB
+               dict(H=32768, I=32448),                # (H + 256) * I * 2 just under 2 GiB
+               dict(E=4096, k=8)]
+
+
+@pytest.mark.parametrize("edge", EDGE_SHAPES)
+def test_shapes_at_the_bounds_accepted(edge):
+    s = dict(T=64, H=128, I=64, E=8, k=2)
+    s.update(edge)
+    sizes = mok.query_sizes(mok.MoKConfig(minibatch_rows=32, ring_bytes=1 << 26), **s)
+    assert all(v > 0 for v in sizes)
 
 
 BAD_CONFIGS = [dict(minibatch_rows=8), dict(minibatch_rows=40), dict(capacity_multiplier=0.0),
