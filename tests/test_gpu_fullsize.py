@@ -154,6 +154,15 @@ def test_ep64_share_mxfp8_wgrad():
     _check(synth.CONFIGS["ep64_share_mxfp8"], mx_wgrad=True)
 
 
+@pytest.mark.timeout(400)
+def test_largest_activation_under_the_byte_bound():
+    """x, dy, out and dx of (2^17 - 1) x 8192 bf16 each, 16 KiB short of 2 GiB:
+    the largest [T, H] the layer's 32-bit byte offsets take at H = 8192 (one
+    token more is refused). Eight ring rounds of 16,384 rows."""
+    _check(synth.small_config("x_byte_bound", T=(1 << 17) - 1, H=8192, I=64, E=8, k=1, minibatch_rows=512,
+                              ring_bytes=256 << 20))
+
+
 @pytest.mark.parametrize("name", ["ep64_share", "ep64_share_mxfp8"])
 def test_ten_runs_bitwise_at_full_size(name):
     """Ten runs of the benchmark's configuration (default knobs, the persistent
